@@ -1,0 +1,374 @@
+/*
+ * llsa_oracle.c -- plain fp64 CPU oracle for Log-linear Sparse Attention.
+ *
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline timing).  Every
+ * loop below follows the definition of the step it implements, in the order
+ * the method describes it; there is no blocking, fusion or reordering.  The
+ * sources are listed in llsa_oracle.h ([P1] LLSA README, [P2] LLSA skill
+ * summary "Core Technique", [P3] arXiv 2512.16615 abstract).
+ */
+#include "llsa_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int64_t ipow(int64_t b, int e)
+{
+    int64_t r = 1;
+    for (int i = 0; i < e; ++i) r *= b;
+    return r;
+}
+
+/* offset (in rows of width `w`) of level l (1-based) inside a pyramid */
+static int64_t lvl_off(int64_t G, int64_t N, int64_t bs, int l, int64_t w)
+{
+    int64_t off = 0;
+    for (int m = 1; m < l; ++m) off += G * (N / ipow(bs, m)) * w;
+    return off;
+}
+
+static double dot(const double* a, const double* b, int64_t d)
+{
+    double s = 0.0;
+    for (int64_t c = 0; c < d; ++c) s += a[c] * b[c];
+    return s;
+}
+
+/* ---------------------------------------------------------------- Z-order */
+
+/* [P1] quadtree reordering: at every scale the four quadrants are visited
+ * top-left, top-right, bottom-left, bottom-right, i.e. the row bit ranks above
+ * the column bit. */
+int64_t orc_morton(int64_t side, int64_t y, int64_t x)
+{
+    int64_t m = 0, w = 1;
+    for (int64_t s = 1; s < side; s <<= 1) {
+        int64_t yb = (y & s) ? 1 : 0, xb = (x & s) ? 1 : 0;
+        m += (2 * yb + xb) * w;
+        w *= 4;
+    }
+    return m;
+}
+
+void orc_zorder(const double* src, double* dst, int64_t outer, int64_t side,
+                int64_t inner, int inverse)
+{
+    int64_t n = side * side;
+    for (int64_t o = 0; o < outer; ++o)
+        for (int64_t r = 0; r < n; ++r) {
+            int64_t z = orc_morton(side, r / side, r % side);
+            const double* s = src + (o * n + (inverse ? z : r)) * inner;
+            double* t = dst + (o * n + (inverse ? r : z)) * inner;
+            memcpy(t, s, (size_t)inner * sizeof(double));
+        }
+}
+
+/* ------------------------------------------------------------------ pool */
+
+/* [P2] hierarchical compression: level l = block means of level l-1. */
+void orc_pool(const double* x, int64_t G, int64_t N, int64_t d, int64_t bs,
+              int L, double* pyr)
+{
+    for (int l = 1; l <= L; ++l) {
+        int64_t n_prev = N / ipow(bs, l - 1), n_l = N / ipow(bs, l);
+        const double* src = (l == 1) ? x : pyr + lvl_off(G, N, bs, l - 1, d);
+        double* dst = pyr + lvl_off(G, N, bs, l, d);
+        for (int64_t g = 0; g < G; ++g)
+            for (int64_t i = 0; i < n_l; ++i)
+                for (int64_t c = 0; c < d; ++c) {
+                    double s = 0.0;
+                    for (int64_t r = 0; r < bs; ++r)
+                        s += src[(g * n_prev + bs * i + r) * d + c];
+                    dst[(g * n_l + i) * d + c] = s / (double)bs;
+                }
+    }
+}
+
+/* --------------------------------------------------------------- select */
+
+typedef struct {
+    double score;
+    int32_t j;
+} cand_t;
+
+/* score descending, then block index ascending */
+static int cand_cmp(const void* a, const void* b)
+{
+    const cand_t* x = (const cand_t*)a;
+    const cand_t* y = (const cand_t*)b;
+    if (x->score > y->score) return -1;
+    if (x->score < y->score) return 1;
+    return (x->j < y->j) ? -1 : (x->j > y->j);
+}
+
+static int int_cmp(const void* a, const void* b)
+{
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x < y) ? -1 : (x > y);
+}
+
+void orc_select_level(const double* qbar, const double* kbar,
+                      const int32_t* parent, int64_t G, int64_t n_l, int64_t d,
+                      int64_t bs, int64_t K, double scale, int32_t* idx,
+                      double* gap)
+{
+    int64_t maxc = parent ? bs * K : n_l;
+    cand_t* c = (cand_t*)malloc((size_t)maxc * sizeof(cand_t));
+    for (int64_t g = 0; g < G; ++g)
+        for (int64_t i = 0; i < n_l; ++i) {
+            /* candidate blocks of row i */
+            int64_t nc = 0;
+            if (!parent) {
+                for (int64_t j = 0; j < n_l; ++j) c[nc++].j = (int32_t)j;
+            } else {
+                const int32_t* pr = parent + (g * (n_l / bs) + i / bs) * K;
+                for (int64_t p = 0; p < K; ++p)
+                    for (int64_t r = 0; r < bs; ++r)
+                        c[nc++].j = (int32_t)(bs * pr[p] + r);
+            }
+            const double* qi = qbar + (g * n_l + i) * d;
+            for (int64_t e = 0; e < nc; ++e)
+                c[e].score = scale * dot(qi, kbar + (g * n_l + c[e].j) * d, d);
+            qsort(c, (size_t)nc, sizeof(cand_t), cand_cmp);
+            int32_t* row = idx + (g * n_l + i) * K;
+            for (int64_t e = 0; e < K; ++e) row[e] = c[e].j;
+            qsort(row, (size_t)K, sizeof(int32_t), int_cmp);
+            if (gap) gap[g * n_l + i] = (nc > K) ? c[K - 1].score - c[K].score : INFINITY;
+        }
+    free(c);
+}
+
+void orc_select(const double* qpyr, const double* kpyr, int64_t G, int64_t N,
+                int64_t d, int64_t bs, int L, int64_t K, double scale,
+                int32_t* idx, double* gap)
+{
+    for (int l = L; l >= 1; --l) {
+        int64_t n_l = N / ipow(bs, l);
+        const int32_t* parent = (l == L) ? NULL : idx + lvl_off(G, N, bs, l + 1, K);
+        orc_select_level(qpyr + lvl_off(G, N, bs, l, d), kpyr + lvl_off(G, N, bs, l, d),
+                         parent, G, n_l, d, bs, K, scale,
+                         idx + lvl_off(G, N, bs, l, K),
+                         gap ? gap + lvl_off(G, N, bs, l, 1) : NULL);
+    }
+}
+
+/* ------------------------------------------------------------ KV set */
+
+/* Key/value rows of the set of token t (head g): the bs*K fine tokens of the
+ * selected level-1 blocks, then, unless disabled, the pooled pairs of the
+ * blocks selected at every level l for the token's level-l ancestor ([P2]
+ * hierarchical KV enrichment).  tag[e] = 0 for a fine entry (ref = token),
+ * tag[e] = l for a level-l pooled entry (ref = block). */
+static int64_t kv_set(const double* k, const double* v, const double* kpyr,
+                      const double* vpyr, const int32_t* idx, int64_t g,
+                      int64_t t, int64_t G, int64_t N, int64_t d, int64_t bs,
+                      int L, int64_t K, unsigned flags, const double** key,
+                      const double** val, int* tag, int64_t* ref)
+{
+    int64_t ne = 0;
+    int64_t n1 = N / bs;
+    const int32_t* sel1 = idx + (g * n1 + t / bs) * K;
+    for (int64_t p = 0; p < K; ++p)
+        for (int64_t r = 0; r < bs; ++r) {
+            int64_t u = bs * sel1[p] + r;
+            key[ne] = k + (g * N + u) * d;
+            val[ne] = v + (g * N + u) * d;
+            tag[ne] = 0;
+            ref[ne] = u;
+            ++ne;
+        }
+    if (!(flags & ORC_NO_ENRICH))
+        for (int l = 1; l <= L; ++l) {
+            int64_t n_l = N / ipow(bs, l), a = t / ipow(bs, l);
+            const int32_t* sel = idx + lvl_off(G, N, bs, l, K) + (g * n_l + a) * K;
+            for (int64_t p = 0; p < K; ++p) {
+                int64_t j = sel[p];
+                key[ne] = kpyr + lvl_off(G, N, bs, l, d) + (g * n_l + j) * d;
+                val[ne] = vpyr + lvl_off(G, N, bs, l, d) + (g * n_l + j) * d;
+                tag[ne] = l;
+                ref[ne] = j;
+                ++ne;
+            }
+        }
+    return ne;
+}
+
+/* ------------------------------------------------------------- forward */
+
+void orc_forward(const double* q, const double* k, const double* v,
+                 const double* kpyr, const double* vpyr, const int32_t* idx,
+                 int64_t G, int64_t N, int64_t d, int64_t bs, int L, int64_t K,
+                 double scale, unsigned flags, const int64_t* qblocks,
+                 int64_t nq, double* out, double* lse)
+{
+    int64_t n1 = N / bs, maxe = bs * K + (int64_t)L * K;
+    const double** key = (const double**)malloc((size_t)maxe * sizeof(double*));
+    const double** val = (const double**)malloc((size_t)maxe * sizeof(double*));
+    int* tag = (int*)malloc((size_t)maxe * sizeof(int));
+    int64_t* ref = (int64_t*)malloc((size_t)maxe * sizeof(int64_t));
+    double* z = (double*)malloc((size_t)maxe * sizeof(double));
+    int64_t nb = qblocks ? nq : n1;
+    for (int64_t g = 0; g < G; ++g)
+        for (int64_t b = 0; b < nb; ++b) {
+            int64_t i = qblocks ? qblocks[b] : b;
+            for (int64_t t = bs * i; t < bs * (i + 1); ++t) {
+                int64_t ne = kv_set(k, v, kpyr, vpyr, idx, g, t, G, N, d, bs, L, K,
+                                    flags, key, val, tag, ref);
+                const double* qt = q + (g * N + t) * d;
+                double m = -INFINITY;
+                for (int64_t e = 0; e < ne; ++e) {
+                    z[e] = scale * dot(qt, key[e], d);
+                    if (z[e] > m) m = z[e];
+                }
+                double l = 0.0;
+                for (int64_t e = 0; e < ne; ++e) l += exp(z[e] - m);
+                double* ot = out + (g * N + t) * d;
+                for (int64_t c = 0; c < d; ++c) {
+                    double s = 0.0;
+                    for (int64_t e = 0; e < ne; ++e) s += exp(z[e] - m) * val[e][c];
+                    ot[c] = s / l;
+                }
+                lse[g * N + t] = m + log(l);
+            }
+        }
+    free(key); free(val); free(tag); free(ref); free(z);
+}
+
+/* ------------------------------------------------------------ backward */
+
+void orc_backward(const double* q, const double* k, const double* v,
+                  const double* kpyr, const double* vpyr, const int32_t* idx,
+                  const double* o, const double* lse, const double* dout,
+                  int64_t G, int64_t N, int64_t d, int64_t bs, int L, int64_t K,
+                  double scale, unsigned flags, const int64_t* qblocks,
+                  int64_t nq, const int64_t* kblocks, int64_t nk, double* dq,
+                  double* dk, double* dv)
+{
+    int64_t n1 = N / bs, maxe = bs * K + (int64_t)L * K;
+    const double** key = (const double**)malloc((size_t)maxe * sizeof(double*));
+    const double** val = (const double**)malloc((size_t)maxe * sizeof(double*));
+    int* tag = (int*)malloc((size_t)maxe * sizeof(int));
+    int64_t* ref = (int64_t*)malloc((size_t)maxe * sizeof(int64_t));
+
+    /* which query blocks need dq; which key blocks need dk/dv; which pooled
+     * blocks (per level) feed a needed key block through the mean */
+    char* want_q = (char*)calloc((size_t)n1, 1);
+    char* want_k = (char*)calloc((size_t)n1, 1);
+    if (qblocks) for (int64_t b = 0; b < nq; ++b) want_q[qblocks[b]] = 1;
+    else memset(want_q, 1, (size_t)n1);
+    if (kblocks) for (int64_t b = 0; b < nk; ++b) want_k[kblocks[b]] = 1;
+    else memset(want_k, 1, (size_t)n1);
+    int64_t pyr_rows = lvl_off(1, N, bs, L + 1, 1); /* sum_l n_l */
+    char* want_p = (char*)calloc((size_t)pyr_rows, 1);
+    for (int l = 1; l <= L; ++l)
+        for (int64_t j = 0; j < n1; ++j)
+            if (want_k[j]) want_p[lvl_off(1, N, bs, l, 1) + j / ipow(bs, l - 1)] = 1;
+
+    /* gradients of the pooled keys / values of one head */
+    double* dkp = (double*)malloc((size_t)(pyr_rows * d) * sizeof(double));
+    double* dvp = (double*)malloc((size_t)(pyr_rows * d) * sizeof(double));
+
+    for (int64_t g = 0; g < G; ++g) {
+        memset(dkp, 0, (size_t)(pyr_rows * d) * sizeof(double));
+        memset(dvp, 0, (size_t)(pyr_rows * d) * sizeof(double));
+        for (int64_t b = 0; b < n1; ++b)
+            if (want_k[b])
+                for (int64_t x = bs * b; x < bs * (b + 1); ++x)
+                    for (int64_t c = 0; c < d; ++c) {
+                        dk[(g * N + x) * d + c] = 0.0;
+                        dv[(g * N + x) * d + c] = 0.0;
+                    }
+
+        for (int64_t i = 0; i < n1; ++i) {
+            /* skip query blocks that contribute to no requested output */
+            int need = want_q[i];
+            const int32_t* sel1 = idx + (g * n1 + i) * K;
+            for (int64_t p = 0; p < K && !need; ++p) need = want_k[sel1[p]];
+            if (!(flags & ORC_NO_ENRICH))
+                for (int l = 1; l <= L && !need; ++l) {
+                    int64_t n_l = N / ipow(bs, l), a = (bs * i) / ipow(bs, l);
+                    const int32_t* sel = idx + lvl_off(G, N, bs, l, K) + (g * n_l + a) * K;
+                    for (int64_t p = 0; p < K && !need; ++p)
+                        need = want_p[lvl_off(1, N, bs, l, 1) + sel[p]];
+                }
+            if (!need) continue;
+
+            for (int64_t t = bs * i; t < bs * (i + 1); ++t) {
+                int64_t ne = kv_set(k, v, kpyr, vpyr, idx, g, t, G, N, d, bs, L, K,
+                                    flags, key, val, tag, ref);
+                const double* qt = q + (g * N + t) * d;
+                const double* dot_ = dout + (g * N + t) * d;
+                double Dt = dot(dot_, o + (g * N + t) * d, d);
+                double lt = lse[g * N + t];
+                double* dqt = dq + (g * N + t) * d;
+                if (want_q[i])
+                    for (int64_t c = 0; c < d; ++c) dqt[c] = 0.0;
+                for (int64_t e = 0; e < ne; ++e) {
+                    double P = exp(scale * dot(qt, key[e], d) - lt);
+                    double dP = dot(dot_, val[e], d);
+                    double dS = P * (dP - Dt);
+                    if (want_q[i])
+                        for (int64_t c = 0; c < d; ++c) dqt[c] += scale * dS * key[e][c];
+                    double *gk, *gv;
+                    if (tag[e] == 0) {
+                        if (!want_k[ref[e] / bs]) continue;
+                        gk = dk + (g * N + ref[e]) * d;
+                        gv = dv + (g * N + ref[e]) * d;
+                    } else {
+                        int64_t row = lvl_off(1, N, bs, tag[e], 1) + ref[e];
+                        if (!want_p[row]) continue;
+                        gk = dkp + row * d;
+                        gv = dvp + row * d;
+                    }
+                    for (int64_t c = 0; c < d; ++c) {
+                        gk[c] += scale * dS * qt[c];
+                        gv[c] += P * dot_[c];
+                    }
+                }
+            }
+        }
+
+        /* a level-l pooled token is the mean of bs^l tokens: each of them
+         * receives 1/bs^l of its gradient */
+        for (int64_t b = 0; b < n1; ++b)
+            if (want_k[b])
+                for (int64_t x = bs * b; x < bs * (b + 1); ++x)
+                    for (int l = 1; l <= L; ++l) {
+                        int64_t row = lvl_off(1, N, bs, l, 1) + x / ipow(bs, l);
+                        double w = 1.0 / (double)ipow(bs, l);
+                        for (int64_t c = 0; c < d; ++c) {
+                            dk[(g * N + x) * d + c] += w * dkp[row * d + c];
+                            dv[(g * N + x) * d + c] += w * dvp[row * d + c];
+                        }
+                    }
+    }
+    free(key); free(val); free(tag); free(ref);
+    free(want_q); free(want_k); free(want_p); free(dkp); free(dvp);
+}
+
+/* ----------------------------------------------------------- transpose */
+
+/* [P2] technique 3: the key-block -> query-block lists are read off the
+ * query-block -> key-block lists; no dense mask.  Rows are visited in
+ * ascending order, so every output list comes out ascending. */
+void orc_transpose(const int32_t* idx, int64_t G, int64_t n, int64_t K,
+                   int32_t* rowptr, int32_t* col)
+{
+    int32_t* fill = (int32_t*)malloc((size_t)n * sizeof(int32_t));
+    for (int64_t g = 0; g < G; ++g) {
+        int32_t* rp = rowptr + g * (n + 1);
+        int32_t* cl = col + g * n * K;
+        const int32_t* I = idx + g * n * K;
+        for (int64_t j = 0; j <= n; ++j) rp[j] = 0;
+        for (int64_t e = 0; e < n * K; ++e) rp[I[e] + 1] += 1;
+        for (int64_t j = 0; j < n; ++j) rp[j + 1] += rp[j];
+        for (int64_t j = 0; j < n; ++j) fill[j] = 0;
+        for (int64_t i = 0; i < n; ++i)
+            for (int64_t p = 0; p < K; ++p) {
+                int32_t j = I[i * K + p];
+                cl[rp[j] + fill[j]++] = (int32_t)i;
+            }
+    }
+    free(fill);
+}
