@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""LLSA hot-path benchmark on one MI355X.
+
+One step = the whole hot path over one batch of seeded synthetic input already
+resident in HBM: Z-order gather of Q, K, V (raster -> quadtree order), the
+forward (pool pyramid, hierarchical Top-K, sparse attention with enrichment)
+and the backward (index transpose, dQ, pooled-token gradients, dK/dV), all
+through the C ABI of libllsa.so on one stream.  Prints ONE JSON line.
+
+The per-stage times come from HIP events recorded on the library's stream
+between the stage calls inside the timed region; the roofline object is
+computed for the stage kernel that takes the longest.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+FP32_PEAK_TFLOPS = 157.3
+METRIC = "LLSA fwd & fwd+bwd ms and TFLOP/s at N=65536 (256x256), d=64, bf16"
+DEFAULT_WORKLOAD = "grid256_bf16_l2_k16"
+
+
+def flops(w):
+    """Algorithmic FLOPs: attention fwd = 4*G*N*n_kv*d with n_kv = 16K + L*K
+    entries per query; bwd = 2.5 x fwd (five products, recomputation not
+    counted); selection = 2*d*G*(n_L^2 + sum_{l<L} n_l*16K)."""
+    n = [w.N // 16 ** l for l in range(w.levels + 1)]
+    n_kv = 16 * w.topk + w.levels * w.topk
+    attn_fwd = 4.0 * w.G * w.N * n_kv * w.d
+    sel = 2.0 * w.d * w.G * (n[w.levels] ** 2 + sum(n[l] * 16 * w.topk for l in range(1, w.levels)))
+    return {"attn_fwd": attn_fwd, "attn_bwd": 2.5 * attn_fwd, "select": sel,
+            "fwd": attn_fwd + sel, "fwdbwd": 3.5 * attn_fwd + sel, "n_kv": n_kv}
+
+
+def algo_bytes(w):
+    """Algorithmic (unique) HBM bytes per launch of each stage kernel: every
+    tensor the stage must read or write, counted once.  Per query block of 16
+    tokens the attention forward moves q, k, v, out (bf16: 4 x 16 x 128 B)
+    plus lse (64 B)."""
+    e = 2 if w.dtype == "bf16" else 4
+    tok = w.G * w.N * w.d * e
+    n = [w.N // 16 ** l for l in range(w.levels + 1)]
+    pyr = sum(w.G * n[l] * w.d * 4 for l in range(1, w.levels + 1))
+    idx = sum(w.G * n[l] * w.topk * 4 for l in range(1, w.levels + 1))
+    lse = w.G * w.N * 4
+    return {
+        "zorder": 2 * 3 * tok,
+        "pool": 3 * tok + 3 * pyr,
+        "select": 2 * pyr + idx,
+        "attn_fwd": 4 * tok + lse + idx,
+        "transpose": 3 * idx + sum(w.G * (n[l] + 1) * 4 for l in range(1, w.levels + 1)),
+        "dq": 5 * tok + 2 * lse + idx,           # q k v o dout in, dq out; lse in, delta out
+        "dkdv": 6 * tok + 2 * lse + 2 * idx,     # q k v dout in, dk dv out; lse, delta
+    }
+
+
+def sha_of_sources():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_attention_diffusion_order_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, w):
+    """Measured HBM bytes per launch from committed rocprofv3 --pmc counters,
+    if they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_%s_%s.json" % (kernel, w.name))
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha") != sha_of_sources():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s=30.0):
+    """The oracle (plain fp64 C, one thread) on a bounded sample of the same
+    workload: head 0 of B*H, whole path (pool, selection, forward, backward)."""
+    import oracle
+    G, N, d = w.G, w.N, w.d
+    head = lambda a: a.reshape(G, N, d)[:1]
+    q = oracle.zorder(head(inp["q64"]), w.side)
+    k = oracle.zorder(head(inp["k64"]), w.side)
+    v = oracle.zorder(head(inp["v64"]), w.side)
+    do = head(inp["do64"])
+    t0 = time.perf_counter()
+    oracle.run(q, k, v, 16, w.levels, w.topk, dout=do)
+    dt = time.perf_counter() - t0
+    f = flops(w)["fwdbwd"] / G
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": "head 0 of %d (1/%d of the workload): pool, selection, forward and "
+                      "backward, fp64 C oracle, single thread" % (G, G)}
+
+
+def dense_reference(w, q, k, v, do, reps=3):
+    """torch scaled_dot_product_attention, non-causal, same shapes and dtype."""
+    import torch
+    import torch.nn.functional as F
+    res = {}
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        ctx = sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION])
+    except Exception:  # pragma: no cover
+        import contextlib
+        ctx = contextlib.nullcontext()
+    with ctx:
+        qq, kk, vv = (x.detach().clone().requires_grad_(True) for x in (q, k, v))
+        for mode in ("fwd", "fwdbwd"):
+            times = []
+            for r in range(reps + 1):
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                s.record()
+                o = F.scaled_dot_product_attention(qq, kk, vv, dropout_p=0.0, is_causal=False)
+                if mode == "fwdbwd":
+                    o.backward(do)
+                e.record()
+                torch.cuda.synchronize()
+                if r:
+                    times.append(s.elapsed_time(e))
+            res[mode + "_ms"] = float(np.median(times))
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (for PMC scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the hot path shards over heads "
+              "with no communication); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_diffusion_order_amd as lib
+
+    w = synth.WORKLOADS[args.workload]
+    print("[bench] workload %s: generating inputs" % w.name, file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dcode = lib.BF16 if w.dtype == "bf16" else lib.F32
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    B, H, N, d, K, L = w.B, w.H, w.N, w.d, w.topk, w.levels
+    q_r, k_r, v_r, do = (up(inp[n]) for n in ("q", "k", "v", "do"))
+    q, k, v = (torch.empty_like(q_r) for _ in range(3))
+    out, dq, dk, dv = (torch.empty_like(q_r) for _ in range(4))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ws_bytes = lib.llsa_workspace_bytes(B, H, N, d, 16, K, L, dcode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    row_bytes = d * q_r.element_size()
+    shape = (B, H, N, d, 16, K, L, dcode, 0, ws, ws_bytes, sh)
+
+    stages = ["zorder", "pool", "select", "attn_fwd", "transpose", "dq", "enrich", "dkdv"]
+
+    def run_stage(name):
+        if name == "zorder":
+            for src, dst in ((q_r, q), (k_r, k), (v_r, v)):
+                lib.llsa_zorder(src, dst, B * H, w.side, row_bytes, 0, sh)
+        elif name in ("pool", "select", "attn_fwd"):
+            part = {"pool": lib.PART_POOL, "select": lib.PART_SELECT, "attn_fwd": lib.PART_ATTN}[name]
+            lib.llsa_forward_part(part, q, k, v, out, lse, *shape)
+        else:
+            part = {"transpose": lib.PART_TRANSPOSE, "dq": lib.PART_DQ,
+                    "enrich": lib.PART_ENRICH, "dkdv": lib.PART_DKDV}[name]
+            lib.llsa_backward_part(part, q, k, v, out, lse, do, dq, dk, dv, *shape)
+
+    def step(evs=None):
+        for si, name in enumerate(stages):
+            run_stage(name)
+            if evs is not None:
+                evs[si + 1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+               for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        all_evs[s][0].record(stream)
+        step(all_evs[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    stage_ms = {name: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in all_evs]))
+                for i, name in enumerate(stages)}
+
+    f = flops(w)
+    fwd_ms = stage_ms["pool"] + stage_ms["select"] + stage_ms["attn_fwd"]
+    bwd_ms = stage_ms["transpose"] + stage_ms["dq"] + stage_ms["enrich"] + stage_ms["dkdv"]
+    fwdbwd_ms = fwd_ms + bwd_ms
+    value = f["fwdbwd"] / (ms_per_step * 1e-3) / 1e12
+
+    # roofline of the longest single-kernel stage (attention fwd, dq or dkdv)
+    peak_mfma = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    abytes = algo_bytes(w)
+    kflops = {"attn_fwd": f["attn_fwd"], "dq": 2.0 * f["attn_fwd"], "dkdv": 2.0 * f["attn_fwd"]}
+    kname = max(("attn_fwd", "dq", "dkdv"), key=lambda s: stage_ms[s])
+    kms = stage_ms[kname]
+    achieved = abytes[kname] / (kms * 1e-3) / 1e9
+    traffic = load_traffic(kname, w)
+    roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "algo_bytes_per_launch": abytes[kname], "avg_launch_ms": round(kms, 5),
+                "mfma_tflops": round(kflops[kname] / (kms * 1e-3) / 1e12, 2),
+                "mfma_frac": round(kflops[kname] / (kms * 1e-3) / 1e12 / peak_mfma, 4)}
+
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "block_size": 16,
+                   "topk": K, "levels": L, "grid": "%dx%d" % (w.side, w.side),
+                   "sigma_px": w.sigma, "seed": w.seed},
+        "fwd_ms": round(fwd_ms, 5), "fwd_tflops": round(f["fwd"] / (fwd_ms * 1e-3) / 1e12, 3),
+        "fwdbwd_ms": round(fwdbwd_ms, 5),
+        "fwdbwd_tflops": round(f["fwdbwd"] / (fwdbwd_ms * 1e-3) / 1e12, 3),
+        "fwd_mfma_frac": round(f["fwd"] / (fwd_ms * 1e-3) / 1e12 / peak_mfma, 4),
+        "fwdbwd_mfma_frac": round(f["fwdbwd"] / (fwdbwd_ms * 1e-3) / 1e12 / peak_mfma, 4),
+        "stage_ms": {k_: round(v_, 5) for k_, v_ in stage_ms.items()},
+        "stage_gbs": {k_: round(abytes[k_] / (stage_ms[k_] * 1e-3) / 1e9, 1)
+                      for k_ in abytes if k_ in stage_ms},
+        "gflop": {k_: round(v_ / 1e9, 3) for k_, v_ in f.items() if k_ != "n_kv"},
+        "roofline": roofline,
+    }
+
+    if not args.no_dense:
+        print("[bench] dense SDPA reference", file=sys.stderr, flush=True)
+        try:
+            dense = dense_reference(w, q, k, v, do)
+            res["dense_sdpa"] = dict(dense, speedup_fwd=round(dense["fwd_ms"] / fwd_ms, 2),
+                                     speedup_fwdbwd=round(dense["fwdbwd_ms"] / fwdbwd_ms, 2),
+                                     pages_context="28.27x inference, 6.09x training at "
+                                                   "256x256 (hardware not stated)")
+        except Exception as ex:  # the comparison is context, not the product
+            res["dense_sdpa"] = {"error": repr(ex)[:200]}
+
+    if args.calib_copy_mib:
+        nb = args.calib_copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calib_copy_bytes"] = nb
+
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * llsa.h -- C ABI of libllsa.so, the MI355X (gfx950) implementation of the
+ * hot path of Log-linear Sparse Attention (LLSA).
+ *
+ * The method (pages: the LLSA GitHub README, "usage" and "reordering"
+ * sections; the LLSA skill summary, "Core Technique" 1-3; the arXiv 2512.16615
+ * abstract):
+ *   - tokens of a 2-D grid are put in Z-order (quadtree order) so that every
+ *     run of 16^l consecutive tokens is a square tile;
+ *   - queries and keys are block-mean-pooled into a pyramid (block_size 16);
+ *   - Top-K key blocks are chosen per query block: densely at the coarsest
+ *     level, and at every finer level only among the children of the blocks
+ *     chosen one level up;
+ *   - non-causal attention runs over the tokens of the chosen level-1 blocks,
+ *     enriched with the pooled key/value tokens of the blocks chosen at every
+ *     level;
+ *   - the backward pass turns the query->key block lists into key->query
+ *     lists (a sparse index transpose) instead of building a dense mask.
+ *
+ * Conventions shared by all entry points
+ *   Tensors q, k, v, out, dout, dq, dk, dv: contiguous [B][H][N][d] in the
+ *   element type `dtype` (LLSA_F32 or LLSA_BF16), tokens already in Z-order
+ *   (see llsa_zorder).  lse: contiguous [B][H][N] float32, natural log of the
+ *   softmax normaliser of each query row.
+ *   Pointers to tensors and to the workspace are DEVICE pointers owned by the
+ *   caller; the library never allocates, frees or keeps them.
+ *   stream: a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *   work on that stream and return; nothing synchronises the host.
+ *   The library holds no mutable global state: concurrent calls with
+ *   distinct workspaces are safe.
+ *   All argument validation happens before any HIP call, so every error code
+ *   except LLSA_ERR_HIP can be observed without a GPU.
+ */
+#ifndef LLSA_H
+#define LLSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define LLSA_F32 0
+#define LLSA_BF16 1
+
+/* flags */
+#define LLSA_NO_ENRICH 1u /* attend to the selected fine blocks only */
+
+/* error codes */
+#define LLSA_OK 0
+#define LLSA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define LLSA_ERR_SHAPE (-2)       /* N or topk not a power of two, levels < 1,
+                                     16^levels does not divide N,
+                                     topk > N / 16^levels, B or H < 1 */
+#define LLSA_ERR_UNSUPPORTED (-3) /* d != 64, block_size != 16, unknown dtype
+                                     or flags, levels > LLSA_MAX_LEVELS,
+                                     coarsest block count > 4096, topk > 64,
+                                     or B*H*N >= 2^31 */
+#define LLSA_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than
+                                     llsa_workspace_bytes() */
+#define LLSA_ERR_HIP (-5)         /* a HIP launch or runtime call failed */
+
+#define LLSA_MAX_LEVELS 6
+
+/* Byte offsets of the parts of the workspace (a test and profiling hook).
+ * Level arrays are indexed by l - 1 for level l = 1..levels.
+ *   qbar/kbar/vbar[l-1] : float32 [B*H][N/16^l][d]   block means (pyramid)
+ *   idx[l-1]            : int32   [B*H][N/16^l][topk] chosen blocks of each
+ *                         level-l query block, ascending
+ *   rowptr[l-1]         : int32   [B*H][N/16^l + 1]  key->query lists (CSR,
+ *   col[l-1]            : int32   [B*H][N/16^l*topk]  offsets per head from 0,
+ *                         each list ascending); written by llsa_backward
+ *   delta               : float32 [B*H][N]  rowsum(dout * out), backward
+ *   total               : bytes needed (== llsa_workspace_bytes) */
+typedef struct {
+    size_t qbar[LLSA_MAX_LEVELS];
+    size_t kbar[LLSA_MAX_LEVELS];
+    size_t vbar[LLSA_MAX_LEVELS];
+    size_t idx[LLSA_MAX_LEVELS];
+    size_t rowptr[LLSA_MAX_LEVELS];
+    size_t col[LLSA_MAX_LEVELS];
+    size_t delta;
+    size_t total;
+} llsa_ws_layout;
+
+/* Bytes of device workspace llsa_forward / llsa_backward need for this shape
+ * (O(B*H*N*d), never O(N^2): no dense mask).  Returns 0 for arguments that
+ * llsa_forward would reject. */
+size_t llsa_workspace_bytes(int B, int H, int N, int d, int block_size, int topk,
+                            int levels, int dtype);
+
+/* Fills *out with the workspace layout of this shape.  Returns LLSA_OK or the
+ * validation error llsa_forward would return (out untouched then). */
+int llsa_workspace_layout(int B, int H, int N, int d, int block_size, int topk,
+                          int levels, int dtype, llsa_ws_layout* out);
+
+/* Z-order (quadtree) token permutation (README, "reordering non-sequential
+ * data": quadrants top-left, top-right, bottom-left, bottom-right at every
+ * scale; Morton code with the row bit above the column bit).
+ * src, dst: device buffers [outer][side*side][inner_bytes], must not overlap.
+ * inverse == 0: raster -> Z-order, dst[o][morton(y,x)] = src[o][y*side+x];
+ * inverse != 0: Z-order -> raster.
+ * side must be a power of two in [1, 2^15]; inner_bytes a positive multiple
+ * of 4.  Errors: LLSA_ERR_NULL, LLSA_ERR_SHAPE, LLSA_ERR_HIP. */
+int llsa_zorder(const void* src, void* dst, long long outer, int side, int inner_bytes,
+                int inverse, void* stream);
+
+/* LLSA forward: pyramid, hierarchical Top-K (scores s*<qbar, kbar> in fp32,
+ * s = 1/sqrt(d), ties to the lower block index) and sparse attention with
+ * enrichment (unless LLSA_NO_ENRICH) writing out [B][H][N][d] and lse.
+ * The pyramid and the index lists are left in the workspace for
+ * llsa_backward, which must get the same workspace, shape, dtype and flags.
+ * levels = 1 corresponds to the README's llsa_l1, levels = 2 to llsa_l2. */
+int llsa_forward(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int H, int N, int d, int block_size, int topk, int levels,
+                 int dtype, unsigned flags, void* workspace, size_t ws_bytes,
+                 void* stream);
+
+/* LLSA backward (skill summary, "Core Technique" 3): given dout, writes dq,
+ * dk, dv ([B][H][N][d], dtype).  Reuses the forward's pyramid and index lists
+ * from the workspace (no re-selection; selection passes no gradient), builds
+ * the key->query lists by a counting sort, then computes dq query-major and
+ * dk, dv key-major.  A pooled token passes 1/16^l of its gradient to each of
+ * the 16^l tokens it averages.  Deterministic: no floating-point atomics. */
+int llsa_backward(const void* q, const void* k, const void* v, const void* out,
+                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                  int B, int H, int N, int d, int block_size, int topk, int levels,
+                  int dtype, unsigned flags, void* workspace, size_t ws_bytes,
+                  void* stream);
+
+/* Stages of llsa_forward / llsa_backward, for per-kernel timing and tests.
+ * llsa_forward == parts POOL, SELECT, ATTN in that order; llsa_backward ==
+ * parts TRANSPOSE, DQ, ENRICH, DKDV in that order (ENRICH: gradients of the
+ * pooled tokens, needed by DKDV).  Same arguments and errors as the full
+ * calls; an unknown part number gives LLSA_ERR_UNSUPPORTED. */
+#define LLSA_PART_POOL 0
+#define LLSA_PART_SELECT 1
+#define LLSA_PART_ATTN 2
+#define LLSA_PART_TRANSPOSE 3
+#define LLSA_PART_DQ 4
+#define LLSA_PART_DKDV 5
+#define LLSA_PART_ENRICH 6
+int llsa_forward_part(int part, const void* q, const void* k, const void* v, void* out,
+                      float* lse, int B, int H, int N, int d, int block_size, int topk,
+                      int levels, int dtype, unsigned flags, void* workspace,
+                      size_t ws_bytes, void* stream);
+int llsa_backward_part(int part, const void* q, const void* k, const void* v,
+                       const void* out, const float* lse, const void* dout, void* dq,
+                       void* dk, void* dv, int B, int H, int N, int d, int block_size,
+                       int topk, int levels, int dtype, unsigned flags, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/* Static description of an error code (never NULL). */
+const char* llsa_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,226 @@
+"""Python binding of libllsa.so (MI355X / gfx950 Log-linear Sparse Attention).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libllsa.so.  The C entry points are exposed under the same names
+(llsa_forward, llsa_backward, llsa_zorder, ...) and accept torch tensors (their
+device pointers are passed) or raw integer addresses.  `stream=None` means
+torch's current stream.  A nonzero return code raises LlsaError.
+
+The library must have been built in-tree (sparse_attention_diffusion_order_amd/
+libllsa.so, see build.py); there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "LlsaError", "F32", "BF16", "NO_ENRICH", "PART_POOL", "PART_SELECT", "PART_ATTN",
+    "PART_TRANSPOSE", "PART_DQ", "PART_ENRICH", "PART_DKDV", "library_path", "load", "exported_names",
+    "llsa_workspace_bytes", "llsa_workspace_layout", "llsa_zorder", "llsa_forward",
+    "llsa_backward", "llsa_forward_part", "llsa_backward_part", "llsa_strerror",
+    "forward", "backward", "zorder",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libllsa.so")
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "llsa.h")
+
+F32, BF16 = 0, 1
+NO_ENRICH = 1
+PART_POOL, PART_SELECT, PART_ATTN = 0, 1, 2
+PART_TRANSPOSE, PART_DQ, PART_DKDV, PART_ENRICH = 3, 4, 5, 6
+MAX_LEVELS = 6
+
+_lib = None
+
+
+class LlsaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %d (%s)" % (where, code, llsa_strerror(code)))
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_size_t * MAX_LEVELS)
+                for name in ("qbar", "kbar", "vbar", "idx", "rowptr", "col")] + \
+               [("delta", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libllsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libllsa.so is not built (run sparse_attention_diffusion_order_amd/"
+                          "build.py or __graft_entry__.build()); there is no fallback")
+    lib = ctypes.CDLL(_LIB_PATH)
+    I, P, U, S = ctypes.c_int, ctypes.c_void_p, ctypes.c_uint, ctypes.c_size_t
+    shape = [I] * 8  # B H N d block_size topk levels dtype
+    lib.llsa_workspace_bytes.argtypes = shape
+    lib.llsa_workspace_bytes.restype = S
+    lib.llsa_workspace_layout.argtypes = shape + [ctypes.POINTER(WsLayout)]
+    lib.llsa_workspace_layout.restype = I
+    lib.llsa_zorder.argtypes = [P, P, ctypes.c_longlong, I, I, I, P]
+    lib.llsa_zorder.restype = I
+    fwd = [P] * 5 + shape + [U, P, S, P]
+    bwd = [P] * 9 + shape + [U, P, S, P]
+    lib.llsa_forward.argtypes = fwd
+    lib.llsa_forward.restype = I
+    lib.llsa_backward.argtypes = bwd
+    lib.llsa_backward.restype = I
+    lib.llsa_forward_part.argtypes = [I] + fwd
+    lib.llsa_forward_part.restype = I
+    lib.llsa_backward_part.argtypes = [I] + bwd
+    lib.llsa_backward_part.restype = I
+    lib.llsa_strerror.argtypes = [I]
+    lib.llsa_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def exported_names():
+    """Function names declared in include/llsa.h."""
+    txt = open(_HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(llsa_\w+)\s*\(", txt,
+                                 flags=re.M)))
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise LlsaError(rc, where)
+
+
+def llsa_strerror(code: int) -> str:
+    return load().llsa_strerror(code).decode()
+
+
+def llsa_workspace_bytes(B, H, N, d, block_size, topk, levels, dtype) -> int:
+    return int(load().llsa_workspace_bytes(B, H, N, d, block_size, topk, levels, dtype))
+
+
+def llsa_workspace_layout(B, H, N, d, block_size, topk, levels, dtype) -> dict:
+    lay = WsLayout()
+    _check(load().llsa_workspace_layout(B, H, N, d, block_size, topk, levels, dtype,
+                                        ctypes.byref(lay)), "llsa_workspace_layout")
+    out = {name: list(getattr(lay, name))[:levels]
+           for name in ("qbar", "kbar", "vbar", "idx", "rowptr", "col")}
+    out["delta"], out["total"] = lay.delta, lay.total
+    return out
+
+
+def llsa_zorder(src, dst, outer, side, inner_bytes, inverse=0, stream=None):
+    _check(load().llsa_zorder(_ptr(src), _ptr(dst), outer, side, inner_bytes, int(inverse),
+                              _stream(stream)), "llsa_zorder")
+
+
+def llsa_forward(q, k, v, out, lse, B, H, N, d, block_size, topk, levels, dtype, flags,
+                 workspace, ws_bytes, stream=None):
+    _check(load().llsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                               block_size, topk, levels, dtype, flags, _ptr(workspace),
+                               ws_bytes, _stream(stream)), "llsa_forward")
+
+
+def llsa_backward(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, block_size, topk, levels,
+                  dtype, flags, workspace, ws_bytes, stream=None):
+    _check(load().llsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, block_size, topk,
+                                levels, dtype, flags, _ptr(workspace), ws_bytes,
+                                _stream(stream)), "llsa_backward")
+
+
+def llsa_forward_part(part, q, k, v, out, lse, B, H, N, d, block_size, topk, levels, dtype,
+                      flags, workspace, ws_bytes, stream=None):
+    _check(load().llsa_forward_part(part, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B,
+                                    H, N, d, block_size, topk, levels, dtype, flags,
+                                    _ptr(workspace), ws_bytes, _stream(stream)),
+           "llsa_forward_part")
+
+
+def llsa_backward_part(part, q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, block_size, topk,
+                       levels, dtype, flags, workspace, ws_bytes, stream=None):
+    _check(load().llsa_backward_part(part, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                     _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+                                     block_size, topk, levels, dtype, flags, _ptr(workspace),
+                                     ws_bytes, _stream(stream)), "llsa_backward_part")
+
+
+# ---------------------------------------------------------------- helpers
+# Convenience wrappers over the entry points above for torch tensors shaped
+# [B, H, N, d]; they allocate outputs and the workspace with torch.
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def forward(q, k, v, topk: int, levels: int, flags: int = 0, workspace=None, stream=None):
+    """Returns (out, lse, workspace); the workspace feeds `backward`."""
+    import torch
+    B, H, N, d = q.shape
+    dt = _dtype_code(q)
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous tensors of one shape and dtype")
+    nbytes = llsa_workspace_bytes(B, H, N, d, 16, topk, levels, dt)
+    if nbytes == 0:
+        raise LlsaError(-2, "llsa_workspace_bytes")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    llsa_forward(q, k, v, out, lse, B, H, N, d, 16, topk, levels, dt, flags, workspace,
+                 workspace.numel(), stream)
+    return out, lse, workspace
+
+
+def backward(q, k, v, out, lse, dout, topk: int, levels: int, workspace, flags: int = 0,
+             stream=None):
+    """Returns (dq, dk, dv); `workspace` must come from `forward`."""
+    import torch
+    B, H, N, d = q.shape
+    dt = _dtype_code(q)
+    if not dout.is_contiguous() or dout.shape != q.shape or dout.dtype != q.dtype:
+        raise ValueError("dout must be contiguous with the shape and dtype of q")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    llsa_backward(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, 16, topk, levels, dt, flags,
+                  workspace, workspace.numel(), stream)
+    return dq, dk, dv
+
+
+def zorder(x, side: int, inverse: bool = False, stream=None):
+    """x [..., side*side, C] (contiguous) -> Z-ordered copy (or its inverse)."""
+    import torch
+    if not x.is_contiguous() or x.shape[-2] != side * side:
+        raise ValueError("x must be contiguous with side*side tokens on dim -2")
+    y = torch.empty_like(x)
+    outer = x.numel() // (side * side * x.shape[-1])
+    llsa_zorder(x, y, outer, side, x.shape[-1] * x.element_size(), int(inverse), stream)
+    return y

@@ -1,0 +1,270 @@
+// api.hip -- C ABI of libllsa: validation, workspace layout and launch order.
+//
+// Every check happens before the first HIP call, so argument errors are
+// reported identically on a host without a GPU.
+#include <string.h>
+
+#include "common.h"
+
+using namespace llsa;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int validate(int B, int H, int N, int d, int block_size, int topk, int levels, int dtype,
+             unsigned flags)
+{
+    if (d != D || block_size != BS || (dtype != LLSA_F32 && dtype != LLSA_BF16) ||
+        (flags & ~LLSA_NO_ENRICH))
+        return LLSA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || N < BS || !pow2(N) || topk < 1 || !pow2(topk) || levels < 1)
+        return LLSA_ERR_SHAPE;
+    if (levels > MAX_L) return LLSA_ERR_UNSUPPORTED;
+    long long span = 1;
+    for (int l = 0; l < levels; ++l) span *= BS;
+    if (span > N || N % span) return LLSA_ERR_SHAPE;
+    long long nL = N / span;
+    if (topk > nL) return LLSA_ERR_SHAPE;
+    if (nL > 4096 || topk > 64) return LLSA_ERR_UNSUPPORTED;
+    if ((long long)B * H * N >= (1ll << 31)) return LLSA_ERR_UNSUPPORTED;
+    return LLSA_OK;
+}
+
+struct Layout {
+    llsa_ws_layout pub;
+    size_t part[MAX_L];
+    size_t dbar[MAX_L];
+};
+
+// Workspace: pyramid (float32), index lists, key->query CSR lists, delta,
+// enrichment gradient partials and sums.  Sizes are O(B*H*N*d): no part of
+// it grows with the square of the block count.
+void make_layout(int G, int N, int K, int L, Layout* lay)
+{
+    memset(lay, 0, sizeof(*lay));
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    long long n[MAX_L + 1];
+    n[0] = N;
+    for (int l = 1; l <= L; ++l) n[l] = n[l - 1] / BS;
+    for (int l = 1; l <= L; ++l) {
+        size_t pyr = (size_t)G * n[l] * D * sizeof(float);
+        lay->pub.qbar[l - 1] = take(pyr);
+        lay->pub.kbar[l - 1] = take(pyr);
+        lay->pub.vbar[l - 1] = take(pyr);
+        lay->pub.idx[l - 1] = take((size_t)G * n[l] * K * sizeof(int));
+    }
+    for (int l = 1; l <= L; ++l) {
+        lay->pub.rowptr[l - 1] = take((size_t)G * (n[l] + 1) * sizeof(int));
+        lay->pub.col[l - 1] = take((size_t)G * n[l] * K * sizeof(int));
+    }
+    lay->pub.delta = take((size_t)G * N * sizeof(float));
+    for (int l = 1; l <= L; ++l) {
+        lay->dbar[l - 1] = take((size_t)G * n[l] * 2 * D * sizeof(float));
+        if (l >= 2) lay->part[l - 1] = take((size_t)G * n[2] * K * 2 * D * sizeof(float));
+    }
+    lay->pub.total = off;
+}
+
+void make_geo(int B, int H, int N, int topk, int levels, unsigned flags, Geo* g)
+{
+    memset(g, 0, sizeof(*g));
+    g->G = B * H;
+    g->N = N;
+    g->K = topk;
+    g->L = levels;
+    g->n[0] = N;
+    for (int l = 1; l <= levels; ++l) g->n[l] = g->n[l - 1] / BS;
+    g->scale = 0.125f;  // 1/sqrt(64)
+    g->flags = flags;
+}
+
+void make_ws(void* base, const Layout& lay, int L, Ws* w)
+{
+    memset(w, 0, sizeof(*w));
+    char* b = (char*)base;
+    for (int l = 1; l <= L; ++l) {
+        w->qbar[l - 1] = (float*)(b + lay.pub.qbar[l - 1]);
+        w->kbar[l - 1] = (float*)(b + lay.pub.kbar[l - 1]);
+        w->vbar[l - 1] = (float*)(b + lay.pub.vbar[l - 1]);
+        w->idx[l - 1] = (int*)(b + lay.pub.idx[l - 1]);
+        w->rowptr[l - 1] = (int*)(b + lay.pub.rowptr[l - 1]);
+        w->col[l - 1] = (int*)(b + lay.pub.col[l - 1]);
+        w->dbar[l - 1] = (float*)(b + lay.dbar[l - 1]);
+        if (l >= 2) w->part[l - 1] = (float*)(b + lay.part[l - 1]);
+    }
+    w->delta = (float*)(b + lay.pub.delta);
+}
+
+struct Prep {
+    Geo geo;
+    Ws ws;
+    hipStream_t st;
+};
+
+int prepare(int B, int H, int N, int d, int block_size, int topk, int levels, int dtype,
+            unsigned flags, void* workspace, size_t ws_bytes, void* stream, Prep* p)
+{
+    int rc = validate(B, H, N, d, block_size, topk, levels, dtype, flags);
+    if (rc) return rc;
+    Layout lay;
+    make_layout(B * H, N, topk, levels, &lay);
+    if (!workspace || ws_bytes < lay.pub.total) return LLSA_ERR_WORKSPACE;
+    make_geo(B, H, N, topk, levels, flags, &p->geo);
+    make_ws(workspace, lay, levels, &p->ws);
+    p->st = (hipStream_t)stream;
+    return LLSA_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? LLSA_OK : LLSA_ERR_HIP; }
+
+int run_forward_part(int part, const void* q, const void* k, const void* v, void* out,
+                     float* lse, int dtype, const Prep& p)
+{
+    switch (part) {
+    case LLSA_PART_POOL: return hip_rc(launch_pool(q, k, v, dtype, p.geo, p.ws, p.st));
+    case LLSA_PART_SELECT: return hip_rc(launch_select(p.geo, p.ws, p.st));
+    case LLSA_PART_ATTN:
+        return hip_rc(launch_attn_fwd(q, k, v, out, lse, dtype, p.geo, p.ws, p.st));
+    default: return LLSA_ERR_UNSUPPORTED;
+    }
+}
+
+int run_backward_part(int part, const void* q, const void* k, const void* v, const void* out,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      int dtype, const Prep& p)
+{
+    switch (part) {
+    case LLSA_PART_TRANSPOSE: return hip_rc(launch_transpose(p.geo, p.ws, p.st));
+    case LLSA_PART_DQ:
+        return hip_rc(launch_attn_dq(q, k, v, out, lse, dout, dq, dtype, p.geo, p.ws, p.st));
+    case LLSA_PART_ENRICH:
+        return hip_rc(launch_attn_enrich(q, lse, dout, dtype, p.geo, p.ws, p.st));
+    case LLSA_PART_DKDV:
+        return hip_rc(launch_attn_dkdv(q, k, v, lse, dout, dk, dv, dtype, p.geo, p.ws, p.st));
+    default: return LLSA_ERR_UNSUPPORTED;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t llsa_workspace_bytes(int B, int H, int N, int d, int block_size, int topk, int levels,
+                            int dtype)
+{
+    if (validate(B, H, N, d, block_size, topk, levels, dtype, 0)) return 0;
+    Layout lay;
+    make_layout(B * H, N, topk, levels, &lay);
+    return lay.pub.total;
+}
+
+int llsa_workspace_layout(int B, int H, int N, int d, int block_size, int topk, int levels,
+                          int dtype, llsa_ws_layout* out)
+{
+    if (!out) return LLSA_ERR_NULL;
+    int rc = validate(B, H, N, d, block_size, topk, levels, dtype, 0);
+    if (rc) return rc;
+    Layout lay;
+    make_layout(B * H, N, topk, levels, &lay);
+    *out = lay.pub;
+    return LLSA_OK;
+}
+
+int llsa_zorder(const void* src, void* dst, long long outer, int side, int inner_bytes,
+                int inverse, void* stream)
+{
+    if (!src || !dst) return LLSA_ERR_NULL;
+    if (outer < 1 || side < 1 || side > (1 << 15) || !pow2(side) || inner_bytes < 4 ||
+        inner_bytes % 4)
+        return LLSA_ERR_SHAPE;
+    return hip_rc(launch_zorder(src, dst, outer, side, inner_bytes, inverse,
+                                (hipStream_t)stream));
+}
+
+int llsa_forward_part(int part, const void* q, const void* k, const void* v, void* out,
+                      float* lse, int B, int H, int N, int d, int block_size, int topk,
+                      int levels, int dtype, unsigned flags, void* workspace, size_t ws_bytes,
+                      void* stream)
+{
+    if (!q || !k || !v || !out || !lse) return LLSA_ERR_NULL;
+    Prep p;
+    int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
+                     stream, &p);
+    if (rc) return rc;
+    return run_forward_part(part, q, k, v, out, lse, dtype, p);
+}
+
+int llsa_forward(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                 int H, int N, int d, int block_size, int topk, int levels, int dtype,
+                 unsigned flags, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!q || !k || !v || !out || !lse) return LLSA_ERR_NULL;
+    Prep p;
+    int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
+                     stream, &p);
+    if (rc) return rc;
+    for (int part : {LLSA_PART_POOL, LLSA_PART_SELECT, LLSA_PART_ATTN}) {
+        rc = run_forward_part(part, q, k, v, out, lse, dtype, p);
+        if (rc) return rc;
+    }
+    return LLSA_OK;
+}
+
+int llsa_backward_part(int part, const void* q, const void* k, const void* v, const void* out,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                       int H, int N, int d, int block_size, int topk, int levels, int dtype,
+                       unsigned flags, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return LLSA_ERR_NULL;
+    Prep p;
+    int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
+                     stream, &p);
+    if (rc) return rc;
+    return run_backward_part(part, q, k, v, out, lse, dout, dq, dk, dv, dtype, p);
+}
+
+int llsa_backward(const void* q, const void* k, const void* v, const void* out,
+                  const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                  int H, int N, int d, int block_size, int topk, int levels, int dtype,
+                  unsigned flags, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return LLSA_ERR_NULL;
+    Prep p;
+    int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
+                     stream, &p);
+    if (rc) return rc;
+    for (int part : {LLSA_PART_TRANSPOSE, LLSA_PART_DQ, LLSA_PART_ENRICH, LLSA_PART_DKDV}) {
+        rc = run_backward_part(part, q, k, v, out, lse, dout, dq, dk, dv, dtype, p);
+        if (rc) return rc;
+    }
+    return LLSA_OK;
+}
+
+const char* llsa_strerror(int code)
+{
+    switch (code) {
+    case LLSA_OK: return "ok";
+    case LLSA_ERR_NULL: return "a required pointer is NULL";
+    case LLSA_ERR_SHAPE:
+        return "bad shape: N and topk must be powers of two, 16^levels must divide N and "
+               "topk <= N/16^levels";
+    case LLSA_ERR_UNSUPPORTED:
+        return "unsupported: needs d=64, block_size=16, dtype f32/bf16, known flags, "
+               "levels<=6, at most 4096 coarsest blocks, topk<=64, B*H*N<2^31";
+    case LLSA_ERR_WORKSPACE: return "workspace missing or smaller than llsa_workspace_bytes()";
+    case LLSA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

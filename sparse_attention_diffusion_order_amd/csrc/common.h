@@ -1,0 +1,124 @@
+// common.h -- internal definitions shared by the gfx950 kernels of libllsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "llsa.h"
+
+namespace llsa {
+
+constexpr int BS = 16;      // block size (tokens per level-1 block)
+constexpr int D = 64;       // head dimension supported by the kernels
+constexpr int MAX_L = LLSA_MAX_LEVELS;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+// Problem geometry derived once on the host and passed by value to kernels.
+struct Geo {
+    int G;                 // B * H
+    int N;                 // tokens per head
+    int K;                 // top-k per level
+    int L;                 // pooling levels
+    int n[MAX_L + 1];      // n[l] = N / 16^l blocks at level l (n[0] = N)
+    float scale;           // 1 / sqrt(d)
+    unsigned flags;
+};
+
+// Device pointers into the caller's workspace.
+struct Ws {
+    float* qbar[MAX_L];
+    float* kbar[MAX_L];
+    float* vbar[MAX_L];
+    int* idx[MAX_L];
+    int* rowptr[MAX_L];
+    int* col[MAX_L];
+    float* delta;            // [G][N]
+    float* part[MAX_L];      // level l>=2 partial enrichment grads [G][n2][K][2][D]
+    float* dbar[MAX_L];      // level l>=2 enrichment grads [G][n_l][2][D]
+};
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float bf2f(unsigned short u)
+{
+    return __uint_as_float(((unsigned)u) << 16);
+}
+
+__device__ __forceinline__ unsigned short f2bf(float f)
+{
+    bf16 b = (bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(unsigned short, b);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float get(const float* p, long i) { return p[i]; }
+};
+template <> struct Elem<unsigned short> {
+    static __device__ __forceinline__ float get(const unsigned short* p, long i) { return bf2f(p[i]); }
+};
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// LDS transposed read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j receives element (j & 3) of the 8-byte words read by lanes
+// 4r + (j >> 2), r = 0..3.  So if lane 4r + x of a group reads row r,
+// columns c0 + 4x .. c0 + 4x + 3 of a row-major bf16 matrix, lane j gets
+// column c0 + j of rows 0..3: a column slice, i.e. the transposed operand.
+__device__ __forceinline__ bf16x4 lds_read_tr(const void* lds_byte_ptr)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(__attribute__((address_space(3))) char*)(lds_byte_ptr));
+}
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// ------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.
+
+hipError_t launch_zorder(const void* src, void* dst, long long outer, int side, int inner_bytes,
+                         int inverse, hipStream_t st);
+hipError_t launch_pool(const void* q, const void* k, const void* v, int dtype, const Geo& g,
+                       const Ws& w, hipStream_t st);
+hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st);
+hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int dtype, const Geo& g, const Ws& w, hipStream_t st);
+hipError_t launch_transpose(const Geo& g, const Ws& w, hipStream_t st);
+hipError_t launch_attn_dq(const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, void* dq, int dtype, const Geo& g,
+                          const Ws& w, hipStream_t st);
+hipError_t launch_attn_enrich(const void* q, const float* lse, const void* dout, int dtype,
+                              const Geo& g, const Ws& w, hipStream_t st);
+hipError_t launch_attn_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                            const void* dout, void* dk, void* dv, int dtype, const Geo& g,
+                            const Ws& w, hipStream_t st);
+
+}  // namespace llsa

@@ -1,0 +1,120 @@
+// k_pool.hip -- block mean-pool pyramid of Q, K and V.
+//
+// LLSA skill summary, "Core Technique" 1 (hierarchical compression) and the
+// arXiv abstract (block-wise representation of tokens): the level-l token i
+// is the mean of the 16 level-(l-1) tokens 16i .. 16i+15.  Levels are
+// computed recursively, in float32.
+//
+// pool_l12: one workgroup per 256 consecutive tokens of one head and one
+// tensor.  Thread (blk, sub) sums the 16 tokens of level-1 block blk over the
+// channels 4*sub .. 4*sub+3, so each token row (128 B in bf16) is read whole
+// by 16 adjacent lanes.  Level 2 (one block per workgroup) is the mean of the
+// 16 level-1 means, formed in LDS.  pool_up forms levels >= 3 from level l-1.
+#include "common.h"
+
+namespace llsa {
+namespace {
+
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+    static __device__ __forceinline__ float4 load(const float* p)
+    {
+        return *(const float4*)p;
+    }
+};
+template <> struct Vec4<unsigned short> {
+    static __device__ __forceinline__ float4 load(const unsigned short* p)
+    {
+        uint2 u = *(const uint2*)p;
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T* __restrict__ k,
+                                                const T* __restrict__ v, Geo g, Ws w)
+{
+    __shared__ float m1[16][D];
+    const int tensor = blockIdx.y;
+    const T* x = tensor == 0 ? q : tensor == 1 ? k : v;
+    float* lv1 = tensor == 0 ? w.qbar[0] : tensor == 1 ? w.kbar[0] : w.vbar[0];
+    float* lv2 = g.L >= 2 ? (tensor == 0 ? w.qbar[1] : tensor == 1 ? w.kbar[1] : w.vbar[1])
+                          : nullptr;
+    const int n1 = g.n[1];
+    const int wg_per_head = (n1 + 15) / 16;
+    const int gh = blockIdx.x / wg_per_head;
+    const int b0 = (blockIdx.x % wg_per_head) * 16;  // first level-1 block
+    const int blk = threadIdx.x >> 4, sub = threadIdx.x & 15;
+    const bool live = b0 + blk < n1;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) {
+        const T* p = x + ((long)gh * g.N + (long)(b0 + blk) * BS) * D + 4 * sub;
+        float4 r[BS];
+#pragma unroll
+        for (int t = 0; t < BS; ++t) r[t] = Vec4<T>::load(p + (long)t * D);
+#pragma unroll
+        for (int t = 0; t < BS; ++t) {
+            s.x += r[t].x;
+            s.y += r[t].y;
+            s.z += r[t].z;
+            s.w += r[t].w;
+        }
+        const float inv = 1.0f / BS;
+        s = make_float4(s.x * inv, s.y * inv, s.z * inv, s.w * inv);
+        *(float4*)(lv1 + ((long)gh * n1 + b0 + blk) * D + 4 * sub) = s;
+    }
+    if (g.L >= 2) {  // b0 is a multiple of 16, so this workgroup is one level-2 block
+        m1[blk][4 * sub + 0] = s.x;
+        m1[blk][4 * sub + 1] = s.y;
+        m1[blk][4 * sub + 2] = s.z;
+        m1[blk][4 * sub + 3] = s.w;
+        __syncthreads();
+        if (threadIdx.x < D) {
+            float a = 0.f;
+#pragma unroll
+            for (int b = 0; b < 16; ++b) a += m1[b][threadIdx.x];
+            lv2[((long)gh * g.n[2] + b0 / 16) * D + threadIdx.x] = a * (1.0f / BS);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void pool_up(Geo g, Ws w, int l)
+{
+    const int tensor = blockIdx.y;
+    const float* src = (tensor == 0 ? w.qbar : tensor == 1 ? w.kbar : w.vbar)[l - 2];
+    float* dst = (tensor == 0 ? w.qbar : tensor == 1 ? w.kbar : w.vbar)[l - 1];
+    long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    long total = (long)g.G * g.n[l] * D;
+    if (id >= total) return;
+    long row = id / D;
+    int c = (int)(id % D);
+    float a = 0.f;
+    for (int t = 0; t < BS; ++t) a += src[(row * BS + t) * D + c];
+    dst[id] = a * (1.0f / BS);
+}
+
+}  // namespace
+
+hipError_t launch_pool(const void* q, const void* k, const void* v, int dtype, const Geo& g,
+                       const Ws& w, hipStream_t st)
+{
+    dim3 grid(g.G * ((g.n[1] + 15) / 16), 3);
+    if (dtype == LLSA_BF16)
+        hipLaunchKernelGGL(pool_l12<unsigned short>, grid, dim3(256), 0, st,
+                           (const unsigned short*)q, (const unsigned short*)k,
+                           (const unsigned short*)v, g, w);
+    else
+        hipLaunchKernelGGL(pool_l12<float>, grid, dim3(256), 0, st, (const float*)q,
+                           (const float*)k, (const float*)v, g, w);
+    hipError_t e = hipGetLastError();
+    for (int l = 3; l <= g.L && e == hipSuccess; ++l) {
+        long total = (long)g.G * g.n[l] * D;
+        hipLaunchKernelGGL(pool_up, dim3((unsigned)((total + 255) / 256), 3), dim3(256), 0, st,
+                           g, w, l);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace llsa

@@ -1,0 +1,159 @@
+// k_select.hip -- hierarchical Top-K block selection.
+//
+// LLSA skill summary, "Core Technique" 1: Top-K is dense only at the coarsest
+// level; every finer level scores only the children of the blocks chosen one
+// level up ("progressively adopting sparse Top-K selection with the indices
+// found at the previous level"), which makes selection log-linear instead of
+// quadratic (arXiv abstract: single-level selection is quadratic).
+//
+// Score of query block i and key block j: s * <qbar_l[i], kbar_l[j]> in
+// float32 (s = 1/sqrt(d)); order: score descending, then block index
+// ascending; the K winners are stored in ascending block order.
+//
+// One workgroup (4 waves) per group of R query rows that share a candidate
+// list: the 16 siblings of a parent below the coarsest level (candidates =
+// 16*K children of the parent's picks, ascending), or R rows of the coarsest
+// level (candidates = all blocks).  Scores of the R x M tile live in LDS.
+// Each wave then selects for its rows with an MSB-first radix search for the
+// K-th largest key (keys = order-preserving integer images of the scores),
+// ballots for ties (lowest candidate position first) and a ballot prefix
+// count to write the winners in ascending order.
+#include "common.h"
+
+namespace llsa {
+namespace {
+
+__device__ __forceinline__ unsigned order_key(float f)
+{
+    unsigned u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int KPL>
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ qbar,
+                                                     const float* __restrict__ kbar,
+                                                     const int* __restrict__ parent,
+                                                     int* __restrict__ idx, int n_l, int K,
+                                                     int R, int M, float scale)
+{
+    extern __shared__ float smem[];
+    float* qs = smem;                 // [R][D]
+    float* sc = qs + R * D;           // [R][M]
+    int* cand = (int*)(sc + R * M);   // [M]
+
+    const int groups_per_head = parent ? n_l / BS : (n_l + R - 1) / R;
+    const int gh = blockIdx.x / groups_per_head;
+    const int grp = blockIdx.x % groups_per_head;
+    const int row0 = grp * (parent ? BS : R);
+    const int rows = parent ? BS : min(R, n_l - row0);
+
+    // candidate list (ascending)
+    for (int c = threadIdx.x; c < M; c += blockDim.x) {
+        if (parent) {
+            const int* pr = parent + ((long)gh * (n_l / BS) + grp) * K;
+            cand[c] = BS * pr[c / BS] + (c % BS);
+        } else {
+            cand[c] = c;
+        }
+    }
+    for (int e = threadIdx.x; e < rows * D; e += blockDim.x)
+        qs[e] = qbar[((long)gh * n_l + row0) * D + e];
+    __syncthreads();
+
+    // score tile: thread per candidate, candidate row held in registers
+    for (int c = threadIdx.x; c < M; c += blockDim.x) {
+        const float4* kr = (const float4*)(kbar + ((long)gh * n_l + cand[c]) * D);
+        float4 kv[D / 4];
+#pragma unroll
+        for (int t = 0; t < D / 4; ++t) kv[t] = kr[t];
+        for (int r = 0; r < rows; ++r) {
+            const float4* qr = (const float4*)(qs + r * D);
+            float a = 0.f;
+#pragma unroll
+            for (int t = 0; t < D / 4; ++t) {
+                float4 qv = qr[t];
+                a = fmaf(qv.x, kv[t].x, a);
+                a = fmaf(qv.y, kv[t].y, a);
+                a = fmaf(qv.z, kv[t].z, a);
+                a = fmaf(qv.w, kv[t].w, a);
+            }
+            sc[r * M + c] = a * scale + 0.0f;  // + 0 turns -0 into +0
+        }
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int r = wv; r < rows; r += blockDim.x / 64) {
+        unsigned key[KPL];
+        bool ok[KPL];
+#pragma unroll
+        for (int s = 0; s < KPL; ++s) {
+            int p = s * 64 + lane;
+            ok[s] = p < M;
+            key[s] = ok[s] ? order_key(sc[r * M + p]) : 0u;
+        }
+        // largest T with #(key >= T) >= K: the K-th largest key
+        unsigned T = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            unsigned t = T | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int s = 0; s < KPL; ++s) cnt += __popcll(__ballot(ok[s] && key[s] >= t));
+            if (cnt >= K) T = t;
+        }
+        int gt = 0;
+#pragma unroll
+        for (int s = 0; s < KPL; ++s) gt += __popcll(__ballot(ok[s] && key[s] > T));
+        int need = K - gt;  // ties at T: lowest candidate positions win
+        int eq_before = 0, out_before = 0;
+        int* orow = idx + ((long)gh * n_l + row0 + r) * K;
+#pragma unroll
+        for (int s = 0; s < KPL; ++s) {
+            bool eq = ok[s] && key[s] == T;
+            unsigned long long beq = __ballot(eq);
+            bool take = (ok[s] && key[s] > T) || (eq && eq_before + __popcll(beq & below) < need);
+            unsigned long long bt = __ballot(take);
+            if (take) orow[out_before + __popcll(bt & below)] = cand[s * 64 + lane];
+            eq_before += __popcll(beq);
+            out_before += __popcll(bt);
+        }
+    }
+}
+
+template <int KPL>
+hipError_t launch_level(const float* qbar, const float* kbar, const int* parent, int* idx, int G,
+                  int n_l, int K, float scale, hipStream_t st)
+{
+    int M = parent ? BS * K : n_l;
+    int R = parent ? BS : min(16, min(n_l, max(1, 8192 / M)));
+    int groups = parent ? n_l / BS : (n_l + R - 1) / R;
+    size_t lds = (size_t)(R * D + R * M) * sizeof(float) + (size_t)M * sizeof(int);
+    if (lds > 65536) {  // 16 sibling rows x 1024 candidates (topk = 64)
+        hipError_t e = hipFuncSetAttribute((const void*)select_kernel<KPL>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(select_kernel<KPL>, dim3(G * groups), dim3(256), lds, st, qbar, kbar,
+                       parent, idx, n_l, K, R, M, scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
+{
+    for (int l = g.L; l >= 1; --l) {
+        const int* parent = (l == g.L) ? nullptr : w.idx[l];
+        int M = parent ? BS * g.K : g.n[l];
+        auto f = M <= 64 ? launch_level<1> : M <= 128 ? launch_level<2> : M <= 256 ? launch_level<4>
+               : M <= 512 ? launch_level<8> : M <= 1024 ? launch_level<16>
+               : M <= 2048 ? launch_level<32> : launch_level<64>;
+        hipError_t e = f(w.qbar[l - 1], w.kbar[l - 1], parent, w.idx[l - 1], g.G, g.n[l], g.K,
+                         g.scale, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace llsa

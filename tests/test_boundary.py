@@ -1,0 +1,114 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function declared in include/llsa.h, and
+reject bad arguments before any HIP call (README usage notes: non-causal only,
+power-of-two token count and top-k).
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import sparse_attention_diffusion_order_amd as L
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.library_path()),
+                                reason="libllsa.so not built")
+
+BAD = 16  # a non-null address that validation must never dereference
+
+
+def test_exports_every_declared_function():
+    names = L.exported_names()
+    assert {"llsa_forward", "llsa_backward", "llsa_zorder", "llsa_workspace_bytes",
+            "llsa_workspace_layout", "llsa_strerror", "llsa_forward_part",
+            "llsa_backward_part"} <= set(names)
+    lib = L.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    syms = subprocess.run(["nm", "-D", "--defined-only", L.library_path()], capture_output=True,
+                          text=True).stdout
+    exported = {line.split()[-1] for line in syms.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+
+
+def fwd(**kw):
+    a = dict(q=BAD, k=BAD, v=BAD, out=BAD, lse=BAD, B=1, H=2, N=4096, d=64, block_size=16,
+             topk=16, levels=1, dtype=L.BF16, flags=0, workspace=BAD, ws_bytes=1 << 40)
+    a.update(kw)
+    lib = L.load()
+    return lib.llsa_forward(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["N"],
+                            a["d"], a["block_size"], a["topk"], a["levels"], a["dtype"],
+                            a["flags"], a["workspace"], a["ws_bytes"], None)
+
+
+def bwd(**kw):
+    a = dict(B=1, H=2, N=4096, d=64, block_size=16, topk=16, levels=1, dtype=L.BF16, flags=0,
+             workspace=BAD, ws_bytes=1 << 40, dq=BAD)
+    a.update(kw)
+    lib = L.load()
+    return lib.llsa_backward(BAD, BAD, BAD, BAD, BAD, BAD, a["dq"], BAD, BAD, a["B"], a["H"],
+                             a["N"], a["d"], a["block_size"], a["topk"], a["levels"],
+                             a["dtype"], a["flags"], a["workspace"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lse=None), -1),
+    (dict(N=3000), -2), (dict(N=8), -2), (dict(topk=12), -2), (dict(topk=0), -2),
+    (dict(levels=0), -2), (dict(levels=4), -2), (dict(N=4096, levels=2, topk=32), -2),
+    (dict(B=0), -2), (dict(H=-1), -2),
+    (dict(d=128), -3), (dict(block_size=32), -3), (dict(dtype=7), -3), (dict(flags=2), -3),
+    (dict(levels=7, N=1 << 30), -3), (dict(N=131072, topk=16), -3), (dict(topk=128, N=65536, levels=2), -3),
+    (dict(B=1 << 16, H=1 << 4, N=4096), -3),
+    (dict(workspace=None), -4), (dict(ws_bytes=100), -4),
+])
+def test_forward_validation(kw, code):
+    assert fwd(**kw) == code
+    if "q" not in kw and "lse" not in kw:
+        assert bwd(**{k: v for k, v in kw.items()}) == code
+
+
+def test_backward_null_output():
+    assert bwd(dq=None) == -1
+
+
+def test_zorder_validation():
+    lib = L.load()
+    assert lib.llsa_zorder(None, BAD, 1, 16, 128, 0, None) == -1
+    assert lib.llsa_zorder(BAD, BAD, 1, 12, 128, 0, None) == -2
+    assert lib.llsa_zorder(BAD, BAD, 1, 16, 6, 0, None) == -2
+    assert lib.llsa_zorder(BAD, BAD, 0, 16, 128, 0, None) == -2
+
+
+def test_strerror():
+    for c in (0, -1, -2, -3, -4, -5, 99):
+        assert isinstance(L.llsa_strerror(c), str) and L.llsa_strerror(c)
+
+
+def test_workspace_is_log_linear_not_quadratic():
+    # the backward keeps sparse lists only: workspace grows linearly with N
+    small = L.llsa_workspace_bytes(1, 1, 65536, 64, 16, 16, 2, L.BF16)
+    big = L.llsa_workspace_bytes(1, 1, 262144, 64, 16, 16, 2, L.BF16)
+    assert 3.5 < big / small < 4.5
+    assert L.llsa_workspace_bytes(1, 1, 3000, 64, 16, 16, 1, L.BF16) == 0
+
+
+@pytest.mark.parametrize("B,H,N,K,Lv", [(1, 1, 1024, 8, 1), (1, 6, 65536, 16, 2),
+                                        (1, 6, 262144, 16, 3)])
+def test_layout_consistent(B, H, N, K, Lv):
+    lay = L.llsa_workspace_layout(B, H, N, 64, 16, K, Lv, L.BF16)
+    assert lay["total"] == L.llsa_workspace_bytes(B, H, N, 64, 16, K, Lv, L.BF16)
+    G = B * H
+    spans = []
+    for l in range(1, Lv + 1):
+        n = N // 16 ** l
+        for name, size in (("qbar", G * n * 64 * 4), ("kbar", G * n * 64 * 4),
+                           ("vbar", G * n * 64 * 4), ("idx", G * n * K * 4),
+                           ("rowptr", G * (n + 1) * 4), ("col", G * n * K * 4)):
+            spans.append((lay[name][l - 1], size))
+    spans.append((lay["delta"], G * N * 4))
+    spans.sort()
+    for (a, sa), (b, _) in zip(spans, spans[1:]):
+        assert a % 256 == 0 and a + sa <= b  # aligned and disjoint
+    assert spans[-1][0] + spans[-1][1] <= lay["total"]

@@ -1,0 +1,192 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Comparison rules are in llsa_check.py.
+
+Where the bf16 path legitimately picks a different block (oracle gap < 1e-3),
+the oracle's forward/backward is re-run on the GPU's index lists, so values
+are compared for the same key/value sets; the index lists themselves are
+checked separately against the oracle's selection.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from llsa_check import (BS, TOL, assert_close, check_selection, check_transpose, gpu_run,
+                        oracle_inputs)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.Workload
+
+
+def small(name, B, H, side, dtype, L, K, sigma=2.0, seed=0):
+    return W(name, B, H, side, 64, dtype, L, K, sigma, seed)
+
+
+SMALL = [
+    synth.WORKLOADS["grid32_f32_l1_k8"],
+    small("grid32_f32_l2_k2", 1, 2, 32, "f32", 2, 2),
+    small("grid16_bf16_l1_k4", 1, 3, 16, "bf16", 1, 4),
+    small("grid32_bf16_l2_k2", 2, 1, 32, "bf16", 2, 2),
+    small("grid64_bf16_l2_k4", 1, 2, 64, "bf16", 2, 4),
+    small("grid64_bf16_l3_k1", 1, 2, 64, "bf16", 3, 1),
+    small("grid64_bf16_l1_k32", 1, 1, 64, "bf16", 1, 32),
+    synth.WORKLOADS["grid64_bf16_l1_k16"],
+]
+
+
+def _full_check(w, flags=0):
+    inp = synth.make_inputs(w)
+    gpu = gpu_run(w, inp, flags=flags)
+    z = oracle_inputs(w, inp)
+    tol = TOL[w.dtype]
+    qp, kp, vp = (oracle.pool(z[n], BS, w.levels) for n in ("q", "k", "v"))
+    for l in range(w.levels):  # pyramid: fp32 sums of exact inputs
+        for name, ref in (("qbar", qp), ("kbar", kp), ("vbar", vp)):
+            assert_close(gpu[name][l], ref[l], 2e-6, what="%s level %d" % (name, l + 1))
+    check_selection(w, gpu, (qp, kp), exact=(w.dtype == "f32"))
+    check_transpose(gpu, w)
+    idx = gpu["idx"]
+    scale = 1.0 / np.sqrt(w.d)
+    o, lse = oracle.forward(z["q"], z["k"], z["v"], kp, vp, idx, BS, scale, flags)
+    assert_close(gpu["out"], o, tol["out_max"], tol["out_mean"], "out")
+    assert_close(gpu["lse"], lse, tol["out_max"], tol["out_mean"], "lse")
+    dq, dk, dv = oracle.backward(z["q"], z["k"], z["v"], kp, vp, idx, o, lse, z["do"], BS,
+                                 scale, flags)
+    for n_, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(gpu[n_], ref, tol["grad_max"], what=n_)
+    return gpu
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_workloads(w):
+    _full_check(w)
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[4]], ids=lambda w: w.name)
+def test_no_enrichment(w):
+    _full_check(w, flags=oracle.NO_ENRICH)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zorder_gather_bit_exact(dtype):
+    import torch
+    import sparse_attention_diffusion_order_amd as lib
+    from llsa_check import to_device
+    w = small("z", 2, 3, 64, dtype, 1, 1)
+    inp = synth.make_inputs(w, want_grad=False)
+    x = to_device(inp["q"], dtype)
+    z = lib.zorder(x, w.side)
+    back = lib.zorder(z, w.side, inverse=True)
+    torch.cuda.synchronize()
+    want = oracle.zorder(inp["q64"].reshape(w.G, w.N, w.d), w.side)
+    got = z.float().cpu().numpy().astype(np.float64).reshape(w.G, w.N, w.d)
+    np.testing.assert_array_equal(got, want)
+    assert torch.equal(back.view(torch.int16) if dtype == "bf16" else back,
+                       x.view(torch.int16) if dtype == "bf16" else x)
+    # odd row width (12 bytes) exercises the 4-byte path
+    y = torch.arange(4 * 16 * 3, dtype=torch.float32, device="cuda").reshape(4, 16, 3)
+    yz = lib.zorder(y, 4)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(yz.cpu().numpy(),
+                                  oracle.zorder(y.cpu().numpy(), 4).astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_blocks_no_enrichment_equals_dense(dtype):
+    w = small("dense", 1, 2, 32, dtype, 1, 64)  # K = n_1 = 64: every block
+    inp = synth.make_inputs(w, want_grad=False)
+    gpu = gpu_run(w, inp, flags=oracle.NO_ENRICH, backward=False)
+    z = oracle_inputs(w, inp)
+    s = 1.0 / np.sqrt(w.d)
+    logits = s * np.einsum("gtc,guc->gtu", z["q"], z["k"])
+    m = logits.max(2, keepdims=True)
+    p = np.exp(logits - m)
+    want = np.einsum("gtu,guc->gtc", p / p.sum(2, keepdims=True), z["v"])
+    lse = (m + np.log(p.sum(2, keepdims=True)))[..., 0]
+    tol = TOL[dtype]
+    assert_close(gpu["out"], want, tol["out_max"], tol["out_mean"], "out")
+    assert_close(gpu["lse"], lse, tol["out_max"], tol["out_mean"], "lse")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_query_ties_resolve_to_lowest_blocks(dtype):
+    w = small("zeroq", 1, 2, 64, dtype, 2, 4)
+    inp = synth.make_inputs(w)
+    inp["q"] = np.zeros_like(inp["q"])
+    inp["q64"] = np.zeros_like(inp["q64"])
+    gpu = gpu_run(w, inp)
+    for lvl in gpu["idx"]:
+        assert np.all(lvl == np.arange(w.topk)[None, None, :])
+    n_ent = BS * w.topk + w.levels * w.topk
+    np.testing.assert_allclose(gpu["lse"], np.log(n_ent), rtol=0, atol=1e-5)
+    check_transpose(gpu, w)  # degenerate lists: blocks 0..K-1 hold every row
+
+
+def test_runs_are_bit_identical():
+    import torch
+    w = small("det", 1, 2, 64, "bf16", 2, 4)
+    inp = synth.make_inputs(w)
+    a = gpu_run(w, inp)
+    b = gpu_run(w, inp)
+    for n_ in ("out_t", "lse_t", "dq_t", "dk_t", "dv_t"):
+        assert torch.equal(a[n_].view(torch.int16) if a[n_].dtype == torch.bfloat16 else a[n_],
+                           b[n_].view(torch.int16) if b[n_].dtype == torch.bfloat16 else b[n_]), n_
+    for l in range(w.levels):
+        np.testing.assert_array_equal(a["idx"][l], b["idx"][l])
+        np.testing.assert_array_equal(a["col"][l], b["col"][l])
+
+
+# ------------------------------------------------------- full-size workloads
+
+def _needed_qblocks(w, idx, kblocks):
+    """Query blocks whose tokens feed dk/dv of the given key blocks."""
+    need = set()
+    for l in range(1, w.levels + 1):
+        for j in kblocks:
+            a = j // BS ** (l - 1)
+            hits = np.nonzero(np.any(idx[l - 1][0] == a, axis=1))[0]
+            for b in hits:
+                need.update(range(b * BS ** (l - 1), (b + 1) * BS ** (l - 1)))
+    return np.array(sorted(need), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["grid128_bf16_l2_k16", "grid256_bf16_l2_k16",
+                                  "grid512_bf16_l3_k16"])
+def test_full_size_sampled(name):
+    """Full-size workloads in the benchmark's launch configuration: selection
+    and transposes checked in full, outputs and gradients on sampled blocks of
+    head 0 (the oracle computes them one by one)."""
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    gpu = gpu_run(w, inp)
+    z = oracle_inputs(w, inp)
+    qp, kp, vp = (oracle.pool(z[n], BS, w.levels) for n in ("q", "k", "v"))
+    for l in range(w.levels):
+        assert_close(gpu["kbar"][l], kp[l], 2e-6, what="kbar level %d" % (l + 1))
+    check_selection(w, gpu, (qp, kp), exact=False)
+    check_transpose(gpu, w)
+    tol = TOL[w.dtype]
+    n1 = w.N // BS
+    rng = np.random.default_rng(1)
+    head = slice(0, 1)
+    q0, k0, v0, do0 = (z[n][head] for n in ("q", "k", "v", "do"))
+    kp0, vp0 = [x[head] for x in kp], [x[head] for x in vp]
+    idx0 = [x[head] for x in gpu["idx"]]
+    scale = 1.0 / np.sqrt(w.d)
+    qbl = np.sort(rng.choice(n1, 48, replace=False))
+    # key blocks inside one top-level block keep the oracle's work bounded
+    top = BS ** (w.levels - 1)
+    j0 = int(rng.integers(0, n1 // top)) * top
+    kbl = np.sort(rng.choice(np.arange(j0, j0 + top), min(8, top), replace=False))
+    rows = np.union1d(qbl, _needed_qblocks(w, idx0, kbl))
+    o, lse = oracle.forward(q0, k0, v0, kp0, vp0, idx0, BS, scale, qblocks=rows)
+    tok = (qbl[:, None] * BS + np.arange(BS)).ravel()
+    assert_close(gpu["out"][0, tok], o[0, tok], tol["out_max"], tol["out_mean"], "out")
+    assert_close(gpu["lse"][0, tok], lse[0, tok], tol["out_max"], tol["out_mean"], "lse")
+    dq, dk, dv = oracle.backward(q0, k0, v0, kp0, vp0, idx0, o, lse, do0, BS, scale,
+                                 qblocks=qbl, kblocks=kbl)
+    assert_close(gpu["dq"][0, tok], dq[0, tok], tol["grad_max"], what="dq")
+    ktok = (kbl[:, None] * BS + np.arange(BS)).ravel()
+    assert_close(gpu["dk"][0, ktok], dk[0, ktok], tol["grad_max"], what="dk")
+    assert_close(gpu["dv"][0, ktok], dv[0, ktok], tol["grad_max"], what="dv")
