@@ -14,6 +14,10 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in arch VGPRs: the softmax reads them with VALU ops
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # no NaN inputs are supported: fmax needs no quieting
+    "-fno-honor-nans",
     "-Wno-unused-command-line-argument",
 ]
 

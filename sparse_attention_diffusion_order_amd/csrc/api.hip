@@ -37,6 +37,7 @@ int validate(int B, int H, int N, int d, int block_size, int topk, int levels, i
 
 struct Layout {
     llsa_ws_layout pub;
+    size_t slot[MAX_L];
     size_t part[MAX_L];
     size_t dbar[MAX_L];
 };
@@ -68,6 +69,7 @@ void make_layout(int G, int N, int K, int L, Layout* lay)
         lay->pub.col[l - 1] = take((size_t)G * n[l] * K * sizeof(int));
     }
     lay->pub.delta = take((size_t)G * N * sizeof(float));
+    for (int l = 1; l <= L; ++l) lay->slot[l - 1] = take((size_t)G * n[l] * K);
     for (int l = 1; l <= L; ++l) {
         lay->dbar[l - 1] = take((size_t)G * n[l] * 2 * D * sizeof(float));
         if (l >= 2) lay->part[l - 1] = take((size_t)G * n[2] * K * 2 * D * sizeof(float));
@@ -99,6 +101,7 @@ void make_ws(void* base, const Layout& lay, int L, Ws* w)
         w->idx[l - 1] = (int*)(b + lay.pub.idx[l - 1]);
         w->rowptr[l - 1] = (int*)(b + lay.pub.rowptr[l - 1]);
         w->col[l - 1] = (int*)(b + lay.pub.col[l - 1]);
+        w->slot[l - 1] = (unsigned char*)(b + lay.slot[l - 1]);
         w->dbar[l - 1] = (float*)(b + lay.dbar[l - 1]);
         if (l >= 2) w->part[l - 1] = (float*)(b + lay.part[l - 1]);
     }

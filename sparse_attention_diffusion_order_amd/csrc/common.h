@@ -40,6 +40,7 @@ struct Ws {
     int* idx[MAX_L];
     int* rowptr[MAX_L];
     int* col[MAX_L];
+    unsigned char* slot[MAX_L];  // position of j in idx_l[col[e]] for each CSR entry e
     float* delta;            // [G][N]
     float* part[MAX_L];      // level l>=2 partial enrichment grads [G][n2][K][2][D]
     float* dbar[MAX_L];      // level l>=2 enrichment grads [G][n_l][2][D]
@@ -100,6 +101,50 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Max / sum over the four lanes n, n+16, n+32, n+48 (one query row of an
+// S^T tile): gfx950 v_permlane16_swap / v_permlane32_swap leave each lane
+// holding its own value and its partner's, in some order; the result is the
+// same in all four lanes (max is exact, a + b == b + a).
+__device__ __forceinline__ float max_x4(float x)
+{
+    unsigned u = __float_as_uint(x);
+    auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_x4(float x)
+{
+    unsigned u = __float_as_uint(x);
+    auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Make all LDS writes of this wave visible to its later LDS reads, and keep
+// the compiler from moving memory accesses across this point.
+__device__ __forceinline__ void lds_fence()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on
+// XCD b % 8).  Renumber them so that consecutive logical workgroups -- which
+// work on neighbouring query or key blocks and gather the same candidate
+// blocks -- run on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_block(int b, int nb)
+{
+    const int full = nb & ~7;
+    if (b >= full) return b;
+    return (b & 7) * (full >> 3) + (b >> 3);
+}
 
 // ------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.

@@ -11,11 +11,8 @@
 //     j in idx_l[a_l] (unless LLSA_NO_ENRICH).
 // One softmax over the whole set, scale 1/sqrt(d); lse in natural log.
 //
-// Level-1 pooled tokens are folded into the fine tiles: kbar_1[j] is the mean
-// of the 16 keys of block j, so its logit is the mean of that tile's 16
-// logits and its value contributes P_e/16 to each of the tile's 16 values.
-// No extra loads or MFMAs are needed for them.  Levels >= 2 form extra tiles
-// of 16 pooled entries.
+// The pooled entries of all levels (L*K of them) form extra tiles of 16,
+// read from the float32 pyramid and rounded to bf16 for the MFMA.
 //
 // bf16 kernel (MFMA): one wave per query block, 4 waves per workgroup.
 //   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, A = key rows, B = query rows;
@@ -32,7 +29,12 @@
 namespace llsa {
 namespace {
 
-constexpr int LDS_ROW = 80;  // bf16 per staged row: 64 + 16 pad (160 B, spreads banks)
+// Staged 16-row tiles in LDS.  Rows read back transposed (ds_read_b64_tr_b16,
+// 4 rows x 32 B per 16 lanes) use a 160-byte stride; rows read as MFMA
+// operands (ds_read_b128, 8 rows x 16 B per 8 lanes) a 144-byte stride: both
+// spread their accesses over all 32 banks.
+constexpr int LDS_ROW = 80;   // transposed-read tiles
+constexpr int ROW_A = 72;     // operand-read tiles
 constexpr int TILE_ELEMS = BS * LDS_ROW;
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const unsigned short* p)
@@ -49,43 +51,30 @@ __device__ __forceinline__ bf16x8 ld_f32_as_bf16x8(const float* p)
     return r;
 }
 
-// Enrichment entry e (0 .. (L-1)*K-1) of query block i: level 2 + e / K,
-// slot e % K of the index list of the query's ancestor at that level.
+// Pooled entry e (0 .. L*K-1) of query block i: level 1 + e / K, slot e % K
+// of the index list of the query's ancestor at that level.
 __device__ __forceinline__ long enrich_row(const Geo& g, const Ws& w, int gh, int i, int e,
                                            int* level)
 {
-    int l = 2 + e / g.K, s = e % g.K;
+    int l = 1 + e / g.K, s = e % g.K;
     int a = i >> (4 * (l - 1));
     int j = w.idx[l - 1][((long)gh * g.n[l] + a) * g.K + s];
     *level = l;
     return ((long)gh * g.n[l] + j) * D;
 }
 
-// Fetch one 16-entry tile: the A operand of S^T (rows = entries) into k0/k1
-// and the value rows into LDS (row-major, zero rows for masked entries).
-// Returns the number of valid entries (16 for fine tiles).
-__device__ __forceinline__ int fetch_tile(const Geo& g, const Ws& w, const unsigned short* k,
-                                          const unsigned short* v, int gh, int i, int t,
-                                          int ntiles, unsigned short* lds, bf16x8& k0,
-                                          bf16x8& k1, int lane)
+// Pooled-entry tile t (entries 16t .. 16t+15): A operand of S^T (rows =
+// entries) into k0/k1, value rows into LDS (row-major, zero rows for masked
+// entries).  Returns the number of valid entries.
+__device__ __forceinline__ int fetch_enrich(const Geo& g, const Ws& w, int gh, int i, int t,
+                                            unsigned short* lds, bf16x8& k0, bf16x8& k1,
+                                            int lane)
 {
     const int gq = lane >> 4, nq = lane & 15;
-    const int vr = lane >> 3, vc = (lane & 7) * 8;  // staging: rows vr, vr+8; cols vc..vc+7
-    if (t < g.K) {  // fine tile: key block idx_1[i][t]
-        int j = w.idx[0][((long)gh * g.n[1] + i) * g.K + t];
-        long base = ((long)gh * g.N + (long)j * BS) * D;
-        k0 = ld_bf16x8(k + base + nq * D + 8 * gq);
-        k1 = ld_bf16x8(k + base + nq * D + 32 + 8 * gq);
-        bf16x8 v0 = ld_bf16x8(v + base + vr * D + vc);
-        bf16x8 v1 = ld_bf16x8(v + base + (vr + 8) * D + vc);
-        *(bf16x8*)(lds + vr * LDS_ROW + vc) = v0;
-        *(bf16x8*)(lds + (vr + 8) * LDS_ROW + vc) = v1;
-        return BS;
-    }
-    const int E = (t < ntiles && !(g.flags & LLSA_NO_ENRICH)) ? (g.L - 1) * g.K : 0;
-    const int e0 = (t - g.K) * BS;
-    const int nvalid = max(0, min(BS, E - e0));
-    bf16x8 z = {};
+    const int vr = lane >> 3, vc = (lane & 7) * 8;
+    const int e0 = t * BS;
+    const int nvalid = max(0, min(BS, g.L * g.K - e0));
+    const bf16x8 z = {};
     k0 = z;
     k1 = z;
     if (nq < nvalid) {
@@ -108,108 +97,200 @@ __device__ __forceinline__ int fetch_tile(const Geo& g, const Ws& w, const unsig
     return nvalid;
 }
 
+
+// Registers of one prefetched pair of fine tiles: rows vr and vr+8 (columns
+// vc .. vc+7) of the key and value tiles a and b.  Every load instruction
+// covers 8 whole 128-byte rows, the fast gather pattern of the vector L1.
+struct FinePair {
+    bf16x8 ka0, ka1, kb0, kb1;
+    bf16x8 va0, va1, vb0, vb1;
+};
+
+__device__ __forceinline__ void load_fine(FinePair& f, const unsigned short* k,
+                                          const unsigned short* v, long hbase, int ja, int jb,
+                                          int lane)
+{
+    const int vr = lane >> 3, vc = (lane & 7) * 8;
+    const long a = hbase + (long)ja * BS * D + vr * D + vc;
+    const long b = hbase + (long)max(jb, 0) * BS * D + vr * D + vc;
+    f.ka0 = ld_bf16x8(k + a);
+    f.ka1 = ld_bf16x8(k + a + 8 * D);
+    f.va0 = ld_bf16x8(v + a);
+    f.va1 = ld_bf16x8(v + a + 8 * D);
+    f.kb0 = ld_bf16x8(k + b);
+    f.kb1 = ld_bf16x8(k + b + 8 * D);
+    f.vb0 = ld_bf16x8(v + b);
+    f.vb1 = ld_bf16x8(v + b + 8 * D);
+}
+
+template <int ROW>
+__device__ __forceinline__ void stage_rows(unsigned short* lds, bf16x8 r0, bf16x8 r1, int lane)
+{
+    const int vr = lane >> 3, vc = (lane & 7) * 8;
+    *(bf16x8*)(lds + vr * ROW + vc) = r0;
+    *(bf16x8*)(lds + (vr + 8) * ROW + vc) = r1;
+}
+
+// A operand of S^T = K Q^T from a staged key tile: row lane%16, channels
+// 8(lane/16) .. +7 and 32 + 8(lane/16) .. +7.
+__device__ __forceinline__ void key_operand(const unsigned short* lds, bf16x8& k0, bf16x8& k1,
+                                            int lane)
+{
+    const int gq = lane >> 4, nq = lane & 15;
+    k0 = *(const bf16x8*)(lds + nq * ROW_A + 8 * gq);
+    k1 = *(const bf16x8*)(lds + nq * ROW_A + 32 + 8 * gq);
+}
+
+// Softmax state.  The exponentials use a reference max m that is raised only
+// when a new logit exceeds it by more than TAU (log2 units), so P <= 2^TAU and
+// the accumulators are rarely rescaled; the result is the same softmax.
+constexpr float TAU = 8.0f;
+
+struct Online {
+    f32x4 acc[4];  // O^T tiles: lane holds O^T[16d + 4(lane/16) + r][query lane%16]
+    float m;       // reference max (log2 units), equal in the 4 lanes of a query
+    float lsum;    // this lane's share of the softmax denominator
+};
+
+// One step over two 16-entry tiles whose values are staged in LDS at la / lb.
+// na / nb: valid entries (MASK == false: both tiles full).
+template <bool MASK>
+__device__ __forceinline__ void attend_pair(Online& st, bf16x8 bq0, bf16x8 bq1, bf16x8 ka0,
+                                            bf16x8 ka1, bf16x8 kb0, bf16x8 kb1,
+                                            const unsigned short* la, const unsigned short* lb,
+                                            int na, int nb, float c, int lane)
+{
+    const int gq = lane >> 4;
+    const int rr = (lane & 15) >> 2, xx = lane & 3;
+    const f32x4 zero = {};
+    const f32x4 sa = mfma32(ka1, bq1, mfma32(ka0, bq0, zero));
+    const f32x4 sb = mfma32(kb1, bq1, mfma32(kb0, bq0, zero));
+    float ya[4], yb[4];  // raw scores, masked entries at -inf
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        ya[r] = (!MASK || 4 * gq + r < na) ? sa[r] : -INFINITY;
+        yb[r] = (!MASK || 4 * gq + r < nb) ? sb[r] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(ya[0], ya[1]), fmaxf(ya[2], ya[3])),
+                     fmaxf(fmaxf(yb[0], yb[1]), fmaxf(yb[2], yb[3])));
+    mx = max_x4(mx) * c;
+    if (__ballot(mx > st.m + TAU)) {
+        const float mnew = fmaxf(st.m, mx);
+        const float alpha = fast_exp2(st.m - mnew);
+        st.lsum *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) st.acc[d] *= alpha;
+        st.m = mnew;
+    }
+    const float nm = -st.m;
+    bf16x8 pp;
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float pa = fast_exp2(fmaf(ya[r], c, nm));
+        const float pb = fast_exp2(fmaf(yb[r], c, nm));
+        ls += pa + pb;
+        pp[r] = (bf16)pa;
+        pp[4 + r] = (bf16)pb;
+    }
+    st.lsum += ls;
+    lds_fence();
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int off = (4 * gq + rr) * LDS_ROW + 16 * d + 4 * xx;
+        bf16x4 va = lds_read_tr(la + off), vb = lds_read_tr(lb + off);
+        bf16x8 av = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+        st.acc[d] = mfma32(av, pp, st.acc[d]);
+    }
+}
+
 __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __restrict__ q,
                                                      const unsigned short* __restrict__ k,
                                                      const unsigned short* __restrict__ v,
                                                      unsigned short* __restrict__ out,
                                                      float* __restrict__ lse, Geo g, Ws w)
 {
-    __shared__ __attribute__((aligned(16))) unsigned short smem[4][2][TILE_ELEMS];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) unsigned short smem[4][4][TILE_ELEMS];
+    const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, nq = lane & 15;
-    const long qblk = (long)blockIdx.x * 4 + wv;  // over G * n1
+    const long qblk = (long)xcd_block(blockIdx.x, gridDim.x) * 4 + wv;  // over G * n1
     if (qblk >= (long)g.G * g.n[1]) return;
     const int gh = (int)(qblk / g.n[1]), i = (int)(qblk % g.n[1]);
-    const bool enrich = !(g.flags & LLSA_NO_ENRICH);
     const float c = g.scale * LOG2E;  // logits in log2 units
-
-    const long qbase = ((long)gh * g.N + (long)i * BS) * D;
+    const long hbase = (long)gh * g.N * D;
+    const long qbase = hbase + (long)i * BS * D;
     const bf16x8 bq0 = ld_bf16x8(q + qbase + nq * D + 8 * gq);
     const bf16x8 bq1 = ld_bf16x8(q + qbase + nq * D + 32 + 8 * gq);
+    // the query block's K fine blocks, one per lane (K <= 64)
+    const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
+    const int myj = lane < g.K ? sel[lane] : -1;
 
-    const int ntiles = g.K + (enrich ? ((g.L - 1) * g.K + BS - 1) / BS : 0);
-    f32x4 acc[4] = {};
-    float m = -INFINITY, lsum = 0.f;
-    unsigned short* la = smem[wv][0];
+    Online st;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.lsum = 0.f;
+    unsigned short* la = smem[wv][0];  // value tiles (transposed reads)
     unsigned short* lb = smem[wv][1];
-    const int rr = (lane & 15) >> 2, xx = lane & 3;  // transposed-read coordinates
+    unsigned short* lka = smem[wv][2];  // key tiles (operand reads)
+    unsigned short* lkb = smem[wv][3];
 
-    for (int ta = 0; ta < ntiles; ta += 2) {
-        const int tb = ta + 1;
+    // fine tiles, two per step; the next pair's loads are in flight meanwhile.
+    // Two register sets alternate; prefetches are unconditional (indices
+    // clamped to the last block) so the compiler's wait counts stay exact.
+    auto jsel = [&](int t) { return __builtin_amdgcn_readlane(myj, min(t, g.K - 1)); };
+    auto step = [&](const FinePair& f, bool full) {
+        stage_rows<ROW_A>(lka, f.ka0, f.ka1, lane);
+        stage_rows<ROW_A>(lkb, f.kb0, f.kb1, lane);
+        stage_rows<LDS_ROW>(la, f.va0, f.va1, lane);
+        stage_rows<LDS_ROW>(lb, f.vb0, f.vb1, lane);
+        lds_fence();
         bf16x8 ka0, ka1, kb0, kb1;
-        int na = fetch_tile(g, w, k, v, gh, i, ta, ntiles, la, ka0, ka1, lane);
-        int nb = fetch_tile(g, w, k, v, gh, i, tb, ntiles, lb, kb0, kb1, lane);
-        const f32x4 zero = {};
-        f32x4 sa = mfma32(ka1, bq1, mfma32(ka0, bq0, zero));
-        f32x4 sb = mfma32(kb1, bq1, mfma32(kb0, bq0, zero));
-        float za[4], zb[4], mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            za[r] = (4 * gq + r < na) ? sa[r] * c : -INFINITY;
-            zb[r] = (4 * gq + r < nb) ? sb[r] * c : -INFINITY;
-            mx = fmaxf(mx, fmaxf(za[r], zb[r]));
+        key_operand(lka, ka0, ka1, lane);
+        key_operand(lkb, kb0, kb1, lane);
+        if (full)
+            attend_pair<false>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, BS, BS, c, lane);
+        else
+            attend_pair<true>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, BS, 0, c, lane);
+    };
+    if (g.K == 1) {
+        FinePair A;
+        load_fine(A, k, v, hbase, jsel(0), jsel(0), lane);
+        step(A, false);
+    } else {
+        const int npairs = g.K / 2;
+        FinePair A, B;
+        load_fine(A, k, v, hbase, jsel(0), jsel(1), lane);
+        for (int p = 0;; p += 2) {
+            load_fine(B, k, v, hbase, jsel(2 * p + 2), jsel(2 * p + 3), lane);
+            step(A, true);
+            if (p + 1 >= npairs) break;
+            load_fine(A, k, v, hbase, jsel(2 * p + 4), jsel(2 * p + 5), lane);
+            step(B, true);
+            if (p + 2 >= npairs) break;
         }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float mnew = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - mnew);
-        m = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) acc[d] *= alpha;
-        float pa[4], pb[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            pa[r] = fast_exp2(za[r] - m);
-            pb[r] = fast_exp2(zb[r] - m);
-        }
-        if (enrich) {  // level-1 pooled token of each fine tile, folded in
-            if (ta < g.K) {
-                float s = za[0] + za[1] + za[2] + za[3];
-                s += shfl_xor(s, 16);
-                s += shfl_xor(s, 32);
-                float pe = fast_exp2(s * (1.0f / BS) - m) * (1.0f / BS);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pa[r] += pe;
-            }
-            if (tb < g.K) {
-                float s = zb[0] + zb[1] + zb[2] + zb[3];
-                s += shfl_xor(s, 16);
-                s += shfl_xor(s, 32);
-                float pe = fast_exp2(s * (1.0f / BS) - m) * (1.0f / BS);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pb[r] += pe;
-            }
-        }
-        bf16x8 pp;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            lsum += pa[r] + pb[r];
-            pp[r] = (bf16)pa[r];
-            pp[4 + r] = (bf16)pb[r];
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const int off = (4 * gq + rr) * LDS_ROW + 16 * d + 4 * xx;
-            bf16x4 va = lds_read_tr(la + off), vb = lds_read_tr(lb + off);
-            bf16x8 av = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-            acc[d] = mfma32(av, pp, acc[d]);
-        }
-        wave_lds_sync();
     }
-    lsum += shfl_xor(lsum, 16);
-    lsum += shfl_xor(lsum, 32);
+    // pooled tokens of every level
+    if (!(g.flags & LLSA_NO_ENRICH)) {
+        const int nt = (g.L * g.K + BS - 1) / BS;
+        for (int t = 0; t < nt; t += 2) {
+            bf16x8 ka0, ka1, kb0, kb1;
+            int na = fetch_enrich(g, w, gh, i, t, la, ka0, ka1, lane);
+            int nb = fetch_enrich(g, w, gh, i, t + 1, lb, kb0, kb1, lane);
+            attend_pair<true>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, na, nb, c, lane);
+        }
+    }
+    const float lsum = sum_x4(st.lsum);
     const float inv = 1.0f / lsum;
     const long obase = qbase + nq * D + 4 * gq;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         u16x4 o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = f2bf(acc[d][r] * inv);
+        for (int r = 0; r < 4; ++r) o[r] = f2bf(st.acc[d][r] * inv);
         *(u16x4*)(out + obase + 16 * d) = o;
     }
-    if (gq == 0) lse[(long)gh * g.N + (long)i * BS + nq] = (m + fast_log2(lsum)) * LN2;
+    if (gq == 0) lse[(long)gh * g.N + (long)i * BS + nq] = (st.m + fast_log2(lsum)) * LN2;
 }
 
 // ------------------------------------------------------------ fp32 path

@@ -14,6 +14,8 @@
 // list: the 16 siblings of a parent below the coarsest level (candidates =
 // 16*K children of the parent's picks, ascending), or R rows of the coarsest
 // level (candidates = all blocks).  Scores of the R x M tile live in LDS.
+// Summation order of a score: four partial sums of 16 channels each, combined
+// pairwise -- fixed, so the result does not depend on the launch.
 // Each wave then selects for its rows with an MSB-first radix search for the
 // K-th largest key (keys = order-preserving integer images of the scores),
 // ballots for ties (lowest candidate position first) and a ballot prefix
@@ -60,24 +62,36 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
         qs[e] = qbar[((long)gh * n_l + row0) * D + e];
     __syncthreads();
 
-    // score tile: thread per candidate, candidate row held in registers
-    for (int c = threadIdx.x; c < M; c += blockDim.x) {
-        const float4* kr = (const float4*)(kbar + ((long)gh * n_l + cand[c]) * D);
-        float4 kv[D / 4];
+    // score tile: four adjacent threads per candidate, 16 channels each, so a
+    // wave reads 16 whole 256-byte candidate rows per load; the four partial
+    // dot products are summed within the quad (DPP), identically in all four.
+    const int sub = threadIdx.x & 3;
+    for (int c0 = 0; c0 < M; c0 += 64) {
+        const int c = c0 + (threadIdx.x >> 2);
+        const bool ok = c < M;
+        float4 kv[4];
+        if (ok) {
+            const float4* kr = (const float4*)(kbar + ((long)gh * n_l + cand[c]) * D + 16 * sub);
 #pragma unroll
-        for (int t = 0; t < D / 4; ++t) kv[t] = kr[t];
+            for (int t = 0; t < 4; ++t) kv[t] = kr[t];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) kv[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         for (int r = 0; r < rows; ++r) {
-            const float4* qr = (const float4*)(qs + r * D);
+            const float4* qr = (const float4*)(qs + r * D + 16 * sub);
             float a = 0.f;
 #pragma unroll
-            for (int t = 0; t < D / 4; ++t) {
-                float4 qv = qr[t];
+            for (int t = 0; t < 4; ++t) {
+                const float4 qv = qr[t];
                 a = fmaf(qv.x, kv[t].x, a);
                 a = fmaf(qv.y, kv[t].y, a);
                 a = fmaf(qv.z, kv[t].z, a);
                 a = fmaf(qv.w, kv[t].w, a);
             }
-            sc[r * M + c] = a * scale + 0.0f;  // + 0 turns -0 into +0
+            a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false));
+            a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false));
+            if (ok && sub == 0) sc[r * M + c] = a * scale + 0.0f;  // + 0 turns -0 into +0
         }
     }
     __syncthreads();
@@ -126,7 +140,9 @@ hipError_t launch_level(const float* qbar, const float* kbar, const int* parent,
                   int n_l, int K, float scale, hipStream_t st)
 {
     int M = parent ? BS * K : n_l;
-    int R = parent ? BS : min(16, min(n_l, max(1, 8192 / M)));
+    // coarsest level: few rows per workgroup, so that the dense n_L x n_L
+    // scoring spreads over many CUs
+    int R = parent ? BS : max(1, min(min(16, n_l / 64), 8192 / M));
     int groups = parent ? n_l / BS : (n_l + R - 1) / R;
     size_t lds = (size_t)(R * D + R * M) * sizeof(float) + (size_t)M * sizeof(int);
     if (lds > 65536) {  // 16 sibling rows x 1024 candidates (topk = 64)

@@ -6,7 +6,7 @@
 //
 // Levels are transposed coarsest first, each by count -> prefix scan -> fill
 // into CSR form (rowptr [G][n_l+1], col [G][n_l*K], every list ascending).
-// The count and fill kernels gather instead of scatter: one wave owns 16
+// The count and fill kernels gather instead of scatter: one workgroup owns 16
 // sibling key blocks 16p .. 16p+15 and walks the only query blocks that can
 // have chosen them -- at a finer level, the children of the query blocks in
 // the parent level's list of block p (hierarchical selection only offers
@@ -42,55 +42,103 @@ __device__ __forceinline__ Cands make_cands(const Geo& g, const Ws& w, int l, in
     return cs;
 }
 
-// 16-bit mask of which of the bins 16*grp .. 16*grp+15 query block i selected
+// 16-bit mask of which of the bins 16*grp .. 16*grp+15 query block i selected.
 __device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp)
 {
     unsigned m = 0;
-    for (int e = 0; e < K; ++e) {
-        int j = I[e];
-        if ((j >> 4) == grp) m |= 1u << (j & 15);
+    if ((K & 3) == 0) {
+        for (int e = 0; e < K; e += 4) {
+            const int4 j4 = *(const int4*)(I + e);
+            m |= ((j4.x >> 4) == grp) ? 1u << (j4.x & 15) : 0u;
+            m |= ((j4.y >> 4) == grp) ? 1u << (j4.y & 15) : 0u;
+            m |= ((j4.z >> 4) == grp) ? 1u << (j4.z & 15) : 0u;
+            m |= ((j4.w >> 4) == grp) ? 1u << (j4.w & 15) : 0u;
+        }
+    } else {
+        for (int e = 0; e < K; ++e) {
+            const int j = I[e];
+            m |= ((j >> 4) == grp) ? 1u << (j & 15) : 0u;
+        }
     }
     return m;
 }
 
-// FILL == false: rowptr[j + 1] = |T_l[j]|.   FILL == true: col lists.
+// Position of block j in the ascending list I[0..K-1] (j is present): the
+// number of entries below j; independent loads, no dependent search.
+__device__ __forceinline__ int list_pos(const int* I, int K, int j)
+{
+    int pos = 0;
+    if ((K & 3) == 0) {
+        for (int e = 0; e < K; e += 4) {
+            const int4 j4 = *(const int4*)(I + e);
+            pos += (j4.x < j) + (j4.y < j) + (j4.z < j) + (j4.w < j);
+        }
+    } else {
+        for (int e = 0; e < K; ++e) pos += I[e] < j;
+    }
+    return pos;
+}
+
+// One workgroup (4 waves) per 16 sibling key blocks; one candidate query
+// block per thread.  FILL == false: rowptr[j + 1] = |T_l[j]|.  FILL == true:
+// col lists (and, for the pooled-token gradients, the position of j in each
+// listed query block's index list).  Ranks: ballot within a wave, counts of
+// lower waves through LDS, counts of earlier rounds carried in registers.
 template <bool FILL>
 __global__ __launch_bounds__(256) void transpose_pass(Geo g, Ws w, int l)
 {
-    const int lane = threadIdx.x & 63;
+    __shared__ int wcnt[4][16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int groups = (g.n[l] + 15) / 16;
-    const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid >= (long)g.G * groups) return;
-    const int gh = (int)(wid / groups), grp = (int)(wid % groups);
+    const int gh = blockIdx.x / groups, grp = blockIdx.x % groups;
     const int* I = w.idx[l - 1] + (long)gh * g.n[l] * g.K;
     int* rowptr = w.rowptr[l - 1] + (long)gh * (g.n[l] + 1);
     int* col = w.col[l - 1] + (long)gh * g.n[l] * g.K;
+    unsigned char* slots = w.slot[l - 1] + (long)gh * g.n[l] * g.K;
     const Cands cs = make_cands(g, w, l, gh, grp);
     const unsigned long long below = (1ull << lane) - 1ull;
-    int base[16];
+    int run[16];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) base[b] = FILL ? rowptr[min(16 * grp + b, g.n[l])] : 0;
-    for (int c0 = 0; c0 < cs.n; c0 += 64) {
-        const int c = c0 + lane;
+    for (int b = 0; b < 16; ++b) run[b] = FILL ? rowptr[min(16 * grp + b, g.n[l])] : 0;
+    for (int c0 = 0; c0 < cs.n; c0 += 256) {
+        const int c = c0 + tid;
         int i = 0;
         unsigned m = 0;
         if (c < cs.n) {
             i = cs.row(c);
             m = hit_mask(I + (long)i * g.K, g.K, grp);
         }
+        unsigned long long bal[16];
 #pragma unroll
         for (int b = 0; b < 16; ++b) {
-            const bool hit = (m >> b) & 1u;
-            const unsigned long long bal = __ballot(hit);
-            if (FILL && hit) col[base[b] + __popcll(bal & below)] = i;
-            base[b] += __popcll(bal);
+            bal[b] = __ballot((m >> b) & 1u);
+            if (lane == b) wcnt[wv][b] = __popcll(bal[b]);
         }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+            int before = 0, total = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int cnt = wcnt[u][b];
+                before += (u < wv) ? cnt : 0;
+                total += cnt;
+            }
+            if (FILL && ((m >> b) & 1u)) {
+                const int pos = run[b] + before + __popcll(bal[b] & below);
+                col[pos] = i;
+                if (l >= 2)  // slots feed the pooled-token gradients of levels >= 2
+                    slots[pos] = (unsigned char)list_pos(I + (long)i * g.K, g.K, 16 * grp + b);
+            }
+            run[b] += total;
+        }
+        __syncthreads();
     }
-    if (!FILL && lane < 16 && 16 * grp + lane < g.n[l]) {
+    if (!FILL && tid < 16 && 16 * grp + tid < g.n[l]) {
         int cnt = 0;
 #pragma unroll
-        for (int b = 0; b < 16; ++b) cnt = (b == lane) ? base[b] : cnt;
-        rowptr[16 * grp + lane + 1] = cnt;
+        for (int b = 0; b < 16; ++b) cnt = (b == tid) ? run[b] : cnt;
+        rowptr[16 * grp + tid + 1] = cnt;
     }
 }
 
@@ -132,8 +180,7 @@ hipError_t launch_transpose(const Geo& g, const Ws& w, hipStream_t st)
     // level 1 feeds the key-major dk/dv pass; levels >= 2 feed the enrichment
     // gradients; finer levels need the coarser lists, so all are built.
     for (int l = g.L; l >= 1; --l) {
-        long waves = (long)g.G * ((g.n[l] + 15) / 16);
-        dim3 grid((unsigned)((waves + 3) / 4));
+        dim3 grid((unsigned)(g.G * ((g.n[l] + 15) / 16)));
         hipLaunchKernelGGL(transpose_pass<false>, grid, dim3(256), 0, st, g, w, l);
         hipLaunchKernelGGL(transpose_scan, dim3(g.G), dim3(1024), 0, st, g, w, l);
         hipLaunchKernelGGL(transpose_pass<true>, grid, dim3(256), 0, st, g, w, l);
