@@ -37,6 +37,7 @@ int validate(int B, int H, int N, int d, int block_size, int topk, int levels, i
 
 struct Layout {
     llsa_ws_layout pub;
+    size_t kb16, vb16, pe1;
     size_t slot[MAX_L];
     size_t part[MAX_L];
     size_t dbar[MAX_L];
@@ -68,7 +69,12 @@ void make_layout(int G, int N, int K, int L, Layout* lay)
         lay->pub.rowptr[l - 1] = take((size_t)G * (n[l] + 1) * sizeof(int));
         lay->pub.col[l - 1] = take((size_t)G * n[l] * K * sizeof(int));
     }
+    size_t prows = 0;
+    for (int l = 1; l <= L; ++l) prows += (size_t)G * n[l];
+    lay->kb16 = take(prows * D * 2);
+    lay->vb16 = take(prows * D * 2);
     lay->pub.delta = take((size_t)G * N * sizeof(float));
+    lay->pe1 = take((size_t)G * n[1] * K * 2 * BS * sizeof(float));
     for (int l = 1; l <= L; ++l) lay->slot[l - 1] = take((size_t)G * n[l] * K);
     for (int l = 1; l <= L; ++l) {
         lay->dbar[l - 1] = take((size_t)G * n[l] * 2 * D * sizeof(float));
@@ -106,6 +112,9 @@ void make_ws(void* base, const Layout& lay, int L, Ws* w)
         if (l >= 2) w->part[l - 1] = (float*)(b + lay.part[l - 1]);
     }
     w->delta = (float*)(b + lay.pub.delta);
+    w->pe1 = (float*)(b + lay.pe1);
+    w->kb16 = (unsigned short*)(b + lay.kb16);
+    w->vb16 = (unsigned short*)(b + lay.vb16);
 }
 
 struct Prep {
@@ -124,6 +133,11 @@ int prepare(int B, int H, int N, int d, int block_size, int topk, int levels, in
     if (!workspace || ws_bytes < lay.pub.total) return LLSA_ERR_WORKSPACE;
     make_geo(B, H, N, topk, levels, flags, &p->geo);
     make_ws(workspace, lay, levels, &p->ws);
+    long r = 0;
+    for (int l = 1; l <= levels; ++l) {
+        p->ws.prow[l - 1] = r;
+        r += (long)p->geo.G * p->geo.n[l];
+    }
     p->st = (hipStream_t)stream;
     return LLSA_OK;
 }

@@ -41,7 +41,11 @@ struct Ws {
     int* rowptr[MAX_L];
     int* col[MAX_L];
     unsigned char* slot[MAX_L];  // position of j in idx_l[col[e]] for each CSR entry e
+    unsigned short* kb16;    // bf16 copies of kbar / vbar, all levels in one array:
+    unsigned short* vb16;    //   row (prow[l] + gh * n_l + j) holds level l, head gh, block j
+    long prow[MAX_L];        // first row of each level in kb16 / vb16
     float* delta;            // [G][N]
+    float* pe1;              // [G][n1][K][2][16]: P and dS of the level-1 pooled entries
     float* part[MAX_L];      // level l>=2 partial enrichment grads [G][n2][K][2][D]
     float* dbar[MAX_L];      // level l>=2 enrichment grads [G][n_l][2][D]
 };

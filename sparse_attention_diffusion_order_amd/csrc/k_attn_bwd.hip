@@ -14,21 +14,19 @@
 // bf16 path:
 //   dq_bf16     one wave per query block; S^T = K Q^T and dP^T = V dO^T on
 //               MFMA, dQ^T += K^T dS^T with K^T read transposed from LDS;
-//               pooled entries of every level as extra tiles (bf16-rounded
-//               pyramid rows, as in the forward); also writes D.
+//               pooled entries of every level as extra tiles (the bf16
+//               pyramid copy, as in the forward); also writes D.
 //   enrich_bwd  one workgroup per level-2 block (256 query tokens): for each
 //               level >= 2 entry list (shared by all 256 tokens) the partial
 //               sums over the group, reduced across waves in fixed order.
 //   enrich_sum  per pooled block: sum of the partials of the query groups
 //               that chose it (found through that level's transpose).
-//   dkdv_bf16   one wave per key block over its list T_1[j] (pairs of query
-//               blocks form the 32-deep contraction); Q^T and dO^T read
-//               transposed from LDS.  The level-1 pooled token of block j is
-//               chosen by exactly the query blocks in T_1[j]: its logit and
-//               dP come from an MFMA against the pooled row broadcast to all
-//               16 columns, and since it averages the block's 16 keys its P/16
-//               and dS/16 are added to every key column.  The epilogue adds
-//               the pooled-level gradients of levels >= 2.
+//   dkdv_bf16   one wave per key block over its list T_1[j], one query block
+//               per step; Q^T and dO^T read transposed from LDS.  The level-1
+//               pooled token of block j is chosen by exactly the query blocks
+//               in T_1[j]; it averages the block's 16 keys, so its P/16 and
+//               dS/16 (stored by the dq pass) are added to every key column.
+//               The epilogue adds the pooled-level gradients of levels >= 2.
 // fp32 path: plain VALU kernels with explicit pooled tokens at every level.
 // No floating-point atomics anywhere: results are bit-identical run to run.
 #include "common.h"
@@ -54,51 +52,6 @@ __device__ __forceinline__ bf16x8 ld8f(const float* p)
     return r;
 }
 
-// Pooled entry e (0 .. L*K-1) of query block i: level 1 + e / K, slot e % K.
-__device__ __forceinline__ long enrich_row(const Geo& g, const Ws& w, int gh, int i, int e,
-                                           int* level)
-{
-    int l = 1 + e / g.K, s = e % g.K;
-    int a = i >> (4 * (l - 1));
-    int j = w.idx[l - 1][((long)gh * g.n[l] + a) * g.K + s];
-    *level = l;
-    return ((long)gh * g.n[l] + j) * D;
-}
-
-// Pooled-entry tile t for dq: pooled key rows staged row-major in LDS (for
-// the transposed K^T read), A operands of S^T (pooled keys) and dP^T (pooled
-// values) in registers; zeros for masked entries.
-__device__ __forceinline__ int dq_tile(const Geo& g, const Ws& w, int gh, int i, int t,
-                                       unsigned short* lds, bf16x8& k0, bf16x8& k1,
-                                       bf16x8& v0, bf16x8& v1, int lane)
-{
-    const int gq = lane >> 4, nq = lane & 15;
-    const int sr = lane >> 3, sc = (lane & 7) * 8;
-    const int e0 = t * BS;
-    const int nvalid = max(0, min(BS, g.L * g.K - e0));
-    const bf16x8 z = {};
-    k0 = k1 = v0 = v1 = z;
-    if (nq < nvalid) {
-        int lv;
-        long off = enrich_row(g, w, gh, i, e0 + nq, &lv);
-        k0 = ld8f(w.kbar[lv - 1] + off + 8 * gq);
-        k1 = ld8f(w.kbar[lv - 1] + off + 32 + 8 * gq);
-        v0 = ld8f(w.vbar[lv - 1] + off + 8 * gq);
-        v1 = ld8f(w.vbar[lv - 1] + off + 32 + 8 * gq);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        int row = sr + 8 * h;
-        bf16x8 val = z;
-        if (row < nvalid) {
-            int lv;
-            long off = enrich_row(g, w, gh, i, e0 + row, &lv);
-            val = ld8f(w.kbar[lv - 1] + off + sc);
-        }
-        *(bf16x8*)(lds + row * LDS_ROW + sc) = val;
-    }
-    return nvalid;
-}
 
 // Registers of one prefetched pair of fine tiles for dq: rows vr and vr+8
 // (columns vc .. vc+7) of the key and value tiles a and b -- 8 whole
@@ -107,23 +60,6 @@ struct DqPair {
     bf16x8 kra0, kra1, krb0, krb1;
     bf16x8 vra0, vra1, vrb0, vrb1;
 };
-
-__device__ __forceinline__ void load_dq_fine(DqPair& f, const unsigned short* k,
-                                             const unsigned short* v, long hbase, int ja, int jb,
-                                             int lane)
-{
-    const int sr = lane >> 3, sc = (lane & 7) * 8;
-    const long a = hbase + (long)ja * BS * D + sr * D + sc;
-    const long b = hbase + (long)max(jb, 0) * BS * D + sr * D + sc;
-    f.kra0 = ld8(k + a);
-    f.kra1 = ld8(k + a + 8 * D);
-    f.vra0 = ld8(v + a);
-    f.vra1 = ld8(v + a + 8 * D);
-    f.krb0 = ld8(k + b);
-    f.krb1 = ld8(k + b + 8 * D);
-    f.vrb0 = ld8(v + b);
-    f.vrb1 = ld8(v + b + 8 * D);
-}
 
 template <int ROW>
 __device__ __forceinline__ void put_rows_s(unsigned short* lds, bf16x8 r0, bf16x8 r1, int lane)
@@ -141,13 +77,16 @@ __device__ __forceinline__ void put_rows(unsigned short* lds, bf16x8 r0, bf16x8 
 // dQ^T += K^T dS^T over two 16-entry tiles.  Key rows are in LDS (la, lb);
 // ka*/kb* are the A operands of S^T (the same rows), va*/vb* those of dP^T.
 // na / nb: valid entries (MASK == false: both tiles full).
+// pe != nullptr (pooled tiles): entries ea + 4(lane/16) + r of tile a (and
+// ea + 16 + ... of tile b) below K are level-1 pooled tokens; their P and dS
+// are stored at pe[entry][0 | 1][query] for the key-major dk/dv pass.
 template <bool MASK>
 __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1, bf16x8 bd0,
                                         bf16x8 bd1, float nl2, float Dq, bf16x8 ka0, bf16x8 ka1,
                                         bf16x8 kb0, bf16x8 kb1, bf16x8 va0, bf16x8 va1,
                                         bf16x8 vb0, bf16x8 vb1, const unsigned short* la,
                                         const unsigned short* lb, int na, int nb, float c,
-                                        int lane)
+                                        int lane, float* pe = nullptr, int ea = 0, int K = 0)
 {
     const int gq = lane >> 4;
     const int rr = (lane & 15) >> 2, xx = lane & 3;
@@ -165,8 +104,21 @@ __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1,
             Pa = (4 * gq + r < na) ? Pa : 0.f;
             Pb = (4 * gq + r < nb) ? Pb : 0.f;
         }
-        bs[r] = (bf16)(Pa * (pa[r] - Dq));
-        bs[4 + r] = (bf16)(Pb * (pb[r] - Dq));
+        const float dSa = Pa * (pa[r] - Dq), dSb = Pb * (pb[r] - Dq);
+        if (pe) {
+            const int nq = lane & 15;
+            const int e_a = ea + 4 * gq + r, e_b = e_a + BS;
+            if (e_a < K) {
+                pe[e_a * 2 * BS + nq] = Pa;
+                pe[e_a * 2 * BS + BS + nq] = dSa;
+            }
+            if (e_b < K) {
+                pe[e_b * 2 * BS + nq] = Pb;
+                pe[e_b * 2 * BS + BS + nq] = dSb;
+            }
+        }
+        bs[r] = (bf16)dSa;
+        bs[4 + r] = (bf16)dSb;
     }
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -177,6 +129,18 @@ __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1,
     }
 }
 
+constexpr int MAX_E = MAX_L * 64;  // pooled entries per query block (L * K)
+
+// Per-wave LDS of dq: two key tiles (160-byte rows, read as operands and
+// transposed), two value tiles (144-byte rows) and the pooled-entry table.
+template <int ECAP>
+struct DqLds {
+    static constexpr int K_TILE = BS * LDS_ROW;
+    static constexpr int V_TILE = BS * ROW_A;
+    static constexpr int PER_WAVE = 2 * K_TILE + 2 * V_TILE + 2 * ECAP;
+};
+
+template <int ECAP>
 __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict__ q,
                                                const unsigned short* __restrict__ k,
                                                const unsigned short* __restrict__ v,
@@ -185,20 +149,20 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
                                                const unsigned short* __restrict__ dout,
                                                unsigned short* __restrict__ dq, Geo g, Ws w)
 {
-    __shared__ __attribute__((aligned(16))) unsigned short smem[4][4][TILE];
+    using Lay = DqLds<ECAP>;
+    __shared__ __attribute__((aligned(16))) unsigned short smem[4][Lay::PER_WAVE];
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, nq = lane & 15;
     const long qblk = (long)xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
     if (qblk >= (long)g.G * g.n[1]) return;
     const int gh = (int)(qblk / g.n[1]), i = (int)(qblk % g.n[1]);
-    const bool enrich = !(g.flags & LLSA_NO_ENRICH);
     const float c = g.scale * LOG2E;
     const long hbase = (long)gh * g.N * D;
     const long rowq = hbase + ((long)i * BS + nq) * D;
     const bf16x8 bq0 = ld8(q + rowq + 8 * gq), bq1 = ld8(q + rowq + 32 + 8 * gq);
     const bf16x8 bd0 = ld8(dout + rowq + 8 * gq), bd1 = ld8(dout + rowq + 32 + 8 * gq);
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
-    const int myj = lane < g.K ? sel[lane] : -1;
+    const int myj = lane < g.K ? sel[lane] : 0;
     float Dq;
     {
         const bf16x8 o0 = ld8(o + rowq + 8 * gq), o1 = ld8(o + rowq + 32 + 8 * gq);
@@ -210,14 +174,60 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
     const long tok = (long)gh * g.N + (long)i * BS + nq;
     if (gq == 0) w.delta[tok] = Dq;
     const float nl2 = -lse[tok] * LOG2E;
+    // pooled entries e = (l-1)*K + slot: their rows in the bf16 pooled arrays
+    const int E = (g.flags & LLSA_NO_ENRICH) ? 0 : g.L * g.K;
+    int* ent = (int*)(smem[wv] + 2 * Lay::K_TILE + 2 * Lay::V_TILE);
+    for (int l = 1; l <= (E ? g.L : 0); ++l) {
+        const long a = (long)gh * g.n[l] + (i >> (4 * (l - 1)));
+        for (int s0 = 0; s0 < g.K; s0 += 64)
+            if (s0 + lane < g.K)
+                ent[(l - 1) * g.K + s0 + lane] =
+                    (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * g.K + s0 + lane]);
+    }
+    lds_fence();
 
     f32x4 acc[4] = {};
-    unsigned short* la = smem[wv][0];
-    unsigned short* lb = smem[wv][1];
-    auto jsel = [&](int t) { return __builtin_amdgcn_readlane(myj, min(t, g.K - 1)); };
-    unsigned short* lva = smem[wv][2];  // value tiles, read as operands only
-    unsigned short* lvb = smem[wv][3];
-    auto step = [&](const DqPair& f, bool full) {
+    unsigned short* la = smem[wv];  // key tiles
+    unsigned short* lb = la + Lay::K_TILE;
+    unsigned short* lva = lb + Lay::K_TILE;  // value tiles, read as operands only
+    unsigned short* lvb = lva + Lay::V_TILE;
+    // one pipeline over NF fine pairs then the pooled pairs, next pair in
+    // flight; unconditional (clamped) loads keep the wait counts exact
+    const int NF = (g.K + 1) / 2;
+    const int NT = (E + BS - 1) / BS;
+    const int NP = NF + (NT + 1) / 2;
+    const int sr = lane >> 3, sc = (lane & 7) * 8;
+    auto load_pair = [&](DqPair& f, int p) {
+        long ka, kb, ka8, kb8;
+        const unsigned short *kp, *vp;
+        if (p < NF) {
+            const int ja = __builtin_amdgcn_readlane(myj, min(2 * p, g.K - 1));
+            const int jb = __builtin_amdgcn_readlane(myj, min(2 * p + 1, g.K - 1));
+            ka = hbase + ((long)ja * BS + sr) * D + sc;
+            kb = hbase + ((long)jb * BS + sr) * D + sc;
+            ka8 = ka + 8 * D;
+            kb8 = kb + 8 * D;
+            kp = k;
+            vp = v;
+        } else {
+            const int t = 2 * (p - NF);
+            ka = (long)ent[min(BS * t + sr, E - 1)] * D + sc;
+            ka8 = (long)ent[min(BS * t + sr + 8, E - 1)] * D + sc;
+            kb = (long)ent[min(BS * t + BS + sr, E - 1)] * D + sc;
+            kb8 = (long)ent[min(BS * t + BS + sr + 8, E - 1)] * D + sc;
+            kp = w.kb16;
+            vp = w.vb16;
+        }
+        f.kra0 = ld8(kp + ka);
+        f.kra1 = ld8(kp + ka8);
+        f.vra0 = ld8(vp + ka);
+        f.vra1 = ld8(vp + ka8);
+        f.krb0 = ld8(kp + kb);
+        f.krb1 = ld8(kp + kb8);
+        f.vrb0 = ld8(vp + kb);
+        f.vrb1 = ld8(vp + kb8);
+    };
+    auto step = [&](const DqPair& f, int p) {
         put_rows(la, f.kra0, f.kra1, lane);
         put_rows(lb, f.krb0, f.krb1, lane);
         put_rows_s<ROW_A>(lva, f.vra0, f.vra1, lane);
@@ -231,42 +241,28 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
         const bf16x8 va1 = *(const bf16x8*)(lva + nq * ROW_A + 32 + 8 * gq);
         const bf16x8 vb0 = *(const bf16x8*)(lvb + nq * ROW_A + 8 * gq);
         const bf16x8 vb1 = *(const bf16x8*)(lvb + nq * ROW_A + 32 + 8 * gq);
-        if (full)
+        if (p < NF && g.K > 1) {
             dq_pair<false>(acc, bq0, bq1, bd0, bd1, nl2, Dq, ka0, ka1, kb0, kb1, va0, va1, vb0,
                            vb1, la, lb, BS, BS, c, lane);
-        else
+        } else {
+            const int e0 = p < NF ? 0 : BS * 2 * (p - NF);
+            const int na = p < NF ? BS : max(0, min(BS, E - e0));
+            const int nb = p < NF ? 0 : max(0, min(BS, E - e0 - BS));
+            float* pe = (p >= NF && e0 < g.K)
+                            ? w.pe1 + ((long)gh * g.n[1] + i) * g.K * 2 * BS : nullptr;
             dq_pair<true>(acc, bq0, bq1, bd0, bd1, nl2, Dq, ka0, ka1, kb0, kb1, va0, va1, vb0,
-                          vb1, la, lb, BS, 0, c, lane);
+                          vb1, la, lb, na, nb, c, lane, pe, e0, g.K);
+        }
     };
-    // fine tiles two per step, next pair prefetched; unconditional (clamped)
-    // prefetches keep the compiler's wait counts exact
-    if (g.K == 1) {
-        DqPair A;
-        load_dq_fine(A, k, v, hbase, jsel(0), jsel(0), lane);
-        step(A, false);
-    } else {
-        const int npairs = g.K / 2;
-        DqPair A, B;
-        load_dq_fine(A, k, v, hbase, jsel(0), jsel(1), lane);
-        for (int p = 0;; p += 2) {
-            load_dq_fine(B, k, v, hbase, jsel(2 * p + 2), jsel(2 * p + 3), lane);
-            step(A, true);
-            if (p + 1 >= npairs) break;
-            load_dq_fine(A, k, v, hbase, jsel(2 * p + 4), jsel(2 * p + 5), lane);
-            step(B, true);
-            if (p + 2 >= npairs) break;
-        }
-    }
-    if (enrich) {  // pooled tokens of every level
-        const int nt = (g.L * g.K + BS - 1) / BS;
-        for (int t = 0; t < nt; t += 2) {
-            bf16x8 ka0, ka1, va0, va1, kb0, kb1, vb0, vb1;
-            int na = dq_tile(g, w, gh, i, t, la, ka0, ka1, va0, va1, lane);
-            int nb = dq_tile(g, w, gh, i, t + 1, lb, kb0, kb1, vb0, vb1, lane);
-            lds_fence();
-            dq_pair<true>(acc, bq0, bq1, bd0, bd1, nl2, Dq, ka0, ka1, kb0, kb1, va0, va1, vb0,
-                          vb1, la, lb, na, nb, c, lane);
-        }
+    DqPair A, B;
+    load_pair(A, 0);
+    for (int p = 0;; p += 2) {
+        load_pair(B, min(p + 1, NP - 1));
+        step(A, p);
+        if (p + 1 >= NP) break;
+        load_pair(A, min(p + 2, NP - 1));
+        step(B, p + 1);
+        if (p + 2 >= NP) break;
     }
     const long obase = rowq + 4 * gq;
 #pragma unroll
@@ -410,89 +406,51 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
     dst[D + dim] = sv;
 }
 
-// Registers of one prefetched pair of query blocks for dk/dv: the q and dout
-// rows this lane stages into LDS, and the per-row lse / delta of the rows
-// 4(lane/16) .. +3 it needs for P and dS.
-struct QPair {
-    bf16x8 qa0, qa1, da0, da1, qb0, qb1, db0, db1;
-    float4 la4, lb4, ea4, eb4;
+// dk/dv: one wave (and workgroup) per key block j, over the query blocks of
+// its list T_1[j], one block per step with the next one in flight.
+//   S  = Q K^T, dP = dO V^T   (16x16x32 MFMA; lane holds query 4(lane/16)+r,
+//                              key lane%16)
+//   P = exp(s S - lse), dS = P (dP - D); with enrichment, the level-1 pooled
+//   token of block j (chosen by exactly the blocks of T_1[j]) adds P_e/16 and
+//   dS_e/16 to every key column -- P_e and dS_e come from the dq pass
+//   dV^T += dO^T P, dK^T += Q^T dS   (16x16x16 MFMA over the 16 queries;
+//                                     Q^T, dO^T read transposed from LDS)
+struct QBlock {
+    bf16x8 q0, q1, d0, d1;  // rows sr and sr+8, channels sc .. sc+7
+    float4 l4, e4;          // lse and delta of rows 4(lane/16) .. +3
+    float4 p4, s4;          // level-1 pooled P and dS of those rows
 };
 
-__device__ __forceinline__ void load_qpair(QPair& f, const unsigned short* q,
-                                           const unsigned short* dout, const float* lse,
-                                           const float* delta, long hbase, long tbase, int ia,
-                                           int ib, int lane)
+__device__ __forceinline__ void load_qblock(QBlock& f, const unsigned short* q,
+                                            const unsigned short* dout, const float* lse,
+                                            const float* delta, const float* pe, long hbase,
+                                            long tbase, int i, int lane)
 {
     const int gq = lane >> 4;
     const int sr = lane >> 3, sc = (lane & 7) * 8;
-    const long a = hbase + (long)ia * BS * D;
-    const long b = hbase + (long)ib * BS * D;
-    f.qa0 = ld8(q + a + sr * D + sc);
-    f.qa1 = ld8(q + a + (sr + 8) * D + sc);
-    f.da0 = ld8(dout + a + sr * D + sc);
-    f.da1 = ld8(dout + a + (sr + 8) * D + sc);
-    f.qb0 = ld8(q + b + sr * D + sc);
-    f.qb1 = ld8(q + b + (sr + 8) * D + sc);
-    f.db0 = ld8(dout + b + sr * D + sc);
-    f.db1 = ld8(dout + b + (sr + 8) * D + sc);
-    f.la4 = *(const float4*)(lse + tbase + (long)ia * BS + 4 * gq);
-    f.ea4 = *(const float4*)(delta + tbase + (long)ia * BS + 4 * gq);
-    f.lb4 = *(const float4*)(lse + tbase + (long)ib * BS + 4 * gq);
-    f.eb4 = *(const float4*)(delta + tbase + (long)ib * BS + 4 * gq);
+    const long a = hbase + ((long)i * BS + sr) * D + sc;
+    f.q0 = ld8(q + a);
+    f.q1 = ld8(q + a + 8 * D);
+    f.d0 = ld8(dout + a);
+    f.d1 = ld8(dout + a + 8 * D);
+    f.l4 = *(const float4*)(lse + tbase + (long)i * BS + 4 * gq);
+    f.e4 = *(const float4*)(delta + tbase + (long)i * BS + 4 * gq);
+    f.p4 = *(const float4*)(pe + 4 * gq);
+    f.s4 = *(const float4*)(pe + BS + 4 * gq);
 }
 
-// P and dS of one query block (rows in LDS at lq / ld) against this wave's
-// key block; lane holds rows 4(lane/16)+r, key lane%16.  With enrichment the
-// block's level-1 pooled token (kp*, vp*: its row in every column) adds P/16
-// and dS/16 to each key.
-__device__ __forceinline__ void kv_block(const unsigned short* lq, const unsigned short* ld,
-                                         float4 l4, float4 d4, bool live, bf16x8 bk0,
-                                         bf16x8 bk1, bf16x8 bv0, bf16x8 bv1, bool enrich,
-                                         bf16x8 kp0, bf16x8 kp1, bf16x8 vp0, bf16x8 vp1,
-                                         float c, int lane, float (&P)[4], float (&S)[4])
+__global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict__ q,
+                                                const unsigned short* __restrict__ k,
+                                                const unsigned short* __restrict__ v,
+                                                const float* __restrict__ lse,
+                                                const unsigned short* __restrict__ dout,
+                                                unsigned short* __restrict__ dk,
+                                                unsigned short* __restrict__ dv, Geo g, Ws w)
 {
+    __shared__ __attribute__((aligned(16))) unsigned short lq[TILE], ld[TILE];
+    const int lane = threadIdx.x;
     const int gq = lane >> 4, nq = lane & 15;
-    const f32x4 zero = {};
-    const bf16x8 aq0 = *(const bf16x8*)(lq + nq * LDS_ROW + 8 * gq);
-    const bf16x8 aq1 = *(const bf16x8*)(lq + nq * LDS_ROW + 32 + 8 * gq);
-    const bf16x8 ad0 = *(const bf16x8*)(ld + nq * LDS_ROW + 8 * gq);
-    const bf16x8 ad1 = *(const bf16x8*)(ld + nq * LDS_ROW + 32 + 8 * gq);
-    const f32x4 s = mfma32(aq1, bk1, mfma32(aq0, bk0, zero));   // S[query 4gq+r][key nq]
-    const f32x4 dp = mfma32(ad1, bv1, mfma32(ad0, bv0, zero));  // dP[query][key]
-    f32x4 se = zero, dpe = zero;
-    if (enrich) {
-        se = mfma32(aq1, kp1, mfma32(aq0, kp0, zero));   // pooled logit, every column
-        dpe = mfma32(ad1, vp1, mfma32(ad0, vp0, zero));
-    }
-    const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, dr[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float nl2 = -lr[r] * LOG2E;
-        float p = live ? fast_exp2(fmaf(s[r], c, nl2)) : 0.f;
-        float ds = p * (dp[r] - dr[r]);
-        if (enrich) {
-            const float pe = live ? fast_exp2(fmaf(se[r], c, nl2)) : 0.f;
-            p += pe * (1.0f / BS);
-            ds += pe * (dpe[r] - dr[r]) * (1.0f / BS);
-        }
-        P[r] = p;
-        S[r] = ds;
-    }
-}
-
-__global__ __launch_bounds__(256, 2) void dkdv_bf16(const unsigned short* __restrict__ q,
-                                                 const unsigned short* __restrict__ k,
-                                                 const unsigned short* __restrict__ v,
-                                                 const float* __restrict__ lse,
-                                                 const unsigned short* __restrict__ dout,
-                                                 unsigned short* __restrict__ dk,
-                                                 unsigned short* __restrict__ dv, Geo g, Ws w)
-{
-    __shared__ __attribute__((aligned(16))) unsigned short smem[4][4][TILE];
-    const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
-    const int gq = lane >> 4, nq = lane & 15;
-    const long kblk = (long)xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
-    if (kblk >= (long)g.G * g.n[1]) return;
+    const long kblk = xcd_block(blockIdx.x, gridDim.x);
     const int gh = (int)(kblk / g.n[1]), j = (int)(kblk % g.n[1]);
     const bool enrich = !(g.flags & LLSA_NO_ENRICH);
     const float c = g.scale * LOG2E;
@@ -501,71 +459,70 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(const unsigned short* __rest
     const long kbase = hbase + (long)j * BS * D;
     const bf16x8 bk0 = ld8(k + kbase + nq * D + 8 * gq), bk1 = ld8(k + kbase + nq * D + 32 + 8 * gq);
     const bf16x8 bv0 = ld8(v + kbase + nq * D + 8 * gq), bv1 = ld8(v + kbase + nq * D + 32 + 8 * gq);
-    bf16x8 kp0 = {}, kp1 = {}, vp0 = {}, vp1 = {};  // level-1 pooled row, in every column
-    if (enrich) {
-        const long prow = ((long)gh * g.n[1] + j) * D;
-        kp0 = ld8f(w.kbar[0] + prow + 8 * gq);
-        kp1 = ld8f(w.kbar[0] + prow + 32 + 8 * gq);
-        vp0 = ld8f(w.vbar[0] + prow + 8 * gq);
-        vp1 = ld8f(w.vbar[0] + prow + 32 + 8 * gq);
-    }
     const int* rp = w.rowptr[0] + (long)gh * (g.n[1] + 1);
     const int* list = w.col[0] + (long)gh * g.n[1] * g.K;
+    const unsigned char* slots = w.slot[0] + (long)gh * g.n[1] * g.K;
     const int beg = uniform(rp[j]), end = uniform(rp[j + 1]);
-    unsigned short* lqa = smem[wv][0];
-    unsigned short* lda = smem[wv][1];
-    unsigned short* lqb = smem[wv][2];
-    unsigned short* ldb = smem[wv][3];
     const int rr = (lane & 15) >> 2, xx = lane & 3;
     const f32x4 zero = {};
     f32x4 accK[4] = {}, accV[4] = {};
-    // A missing second block of the last pair re-reads the first one (valid
-    // memory); its P and dS are zeroed, so it contributes nothing.  Two
-    // register sets alternate so the next pair's loads fly during this one.
-    auto step = [&](const QPair& f, bool hasb) {
-        put_rows(lqa, f.qa0, f.qa1, lane);
-        put_rows(lda, f.da0, f.da1, lane);
-        put_rows(lqb, f.qb0, f.qb1, lane);
-        put_rows(ldb, f.db0, f.db1, lane);
+    auto step = [&](const QBlock& f) {
+        put_rows(lq, f.q0, f.q1, lane);
+        put_rows(ld, f.d0, f.d1, lane);
         lds_fence();
-        float Pa[4], Sa[4], Pb[4], Sb[4];
-        kv_block(lqa, lda, f.la4, f.ea4, true, bk0, bk1, bv0, bv1, enrich, kp0, kp1, vp0, vp1,
-                 c, lane, Pa, Sa);
-        kv_block(lqb, ldb, f.lb4, f.eb4, hasb, bk0, bk1, bv0, bv1, enrich, kp0, kp1, vp0, vp1,
-                 c, lane, Pb, Sb);
-        bf16x8 bp, bs;
+        const bf16x8 aq0 = *(const bf16x8*)(lq + nq * LDS_ROW + 8 * gq);
+        const bf16x8 aq1 = *(const bf16x8*)(lq + nq * LDS_ROW + 32 + 8 * gq);
+        const bf16x8 ad0 = *(const bf16x8*)(ld + nq * LDS_ROW + 8 * gq);
+        const bf16x8 ad1 = *(const bf16x8*)(ld + nq * LDS_ROW + 32 + 8 * gq);
+        const f32x4 s = mfma32(aq1, bk1, mfma32(aq0, bk0, zero));   // S[query][key]
+        const f32x4 dp = mfma32(ad1, bv1, mfma32(ad0, bv0, zero));  // dP[query][key]
+        const float lr[4] = {f.l4.x, f.l4.y, f.l4.z, f.l4.w};
+        const float dr[4] = {f.e4.x, f.e4.y, f.e4.z, f.e4.w};
+        const float pr[4] = {f.p4.x, f.p4.y, f.p4.z, f.p4.w};
+        const float sr_[4] = {f.s4.x, f.s4.y, f.s4.z, f.s4.w};
+        bf16x4 bp, bs;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            bp[r] = (bf16)Pa[r];
-            bp[4 + r] = (bf16)Pb[r];
-            bs[r] = (bf16)Sa[r];
-            bs[4 + r] = (bf16)Sb[r];
+            float p = fast_exp2(fmaf(s[r], c, -lr[r] * LOG2E));
+            float ds = p * (dp[r] - dr[r]);
+            if (enrich) {
+                p = fmaf(pr[r], 1.0f / BS, p);
+                ds = fmaf(sr_[r], 1.0f / BS, ds);
+            }
+            bp[r] = (bf16)p;
+            bs[r] = (bf16)ds;
         }
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int off = (4 * gq + rr) * LDS_ROW + 16 * d + 4 * xx;
-            bf16x4 da = lds_read_tr(lda + off), db = lds_read_tr(ldb + off);
-            bf16x4 qa4 = lds_read_tr(lqa + off), qb4 = lds_read_tr(lqb + off);
-            bf16x8 adO = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3]};
-            bf16x8 aQ = {qa4[0], qa4[1], qa4[2], qa4[3], qb4[0], qb4[1], qb4[2], qb4[3]};
-            accV[d] = mfma32(adO, bp, accV[d]);
-            accK[d] = mfma32(aQ, bs, accK[d]);
+            accV[d] = mfma16(lds_read_tr(ld + off), bp, accV[d]);
+            accK[d] = mfma16(lds_read_tr(lq + off), bs, accK[d]);
         }
     };
-    auto fetch = [&](QPair& f, int e) {
-        load_qpair(f, q, dout, lse, w.delta, hbase, tbase, list[min(e, end - 1)],
-                   list[min(e + 1, end - 1)], lane);
+    // the list is read 64 entries at a time, one per lane, and each step takes
+    // its query block and slot with readlane, so no load waits on another
+    int myi = 0, mys = 0;
+    auto fetch = [&](QBlock& f, int t) {
+        const int i = __builtin_amdgcn_readlane(myi, t);
+        const int sl = __builtin_amdgcn_readlane(mys, t);
+        const float* pe = w.pe1 + (((long)gh * g.n[1] + i) * g.K + sl) * 2 * BS;
+        load_qblock(f, q, dout, lse, w.delta, pe, hbase, tbase, i, lane);
     };
-    QPair A, B;
-    if (beg < end) {
-        fetch(A, beg);
-        for (int e = beg;; e += 4) {
-            fetch(B, e + 2);  // unconditional (clamped): exact wait counts
-            step(A, e + 1 < end);
-            if (e + 2 >= end) break;
-            fetch(A, e + 4);
-            step(B, e + 3 < end);
-            if (e + 4 >= end) break;
+    // two register sets alternate; the prefetch past the end re-reads the
+    // last block (valid memory) and is simply not used
+    QBlock A, B;
+    for (int cb = beg; cb < end; cb += 64) {
+        const int n = min(64, end - cb);
+        myi = lane < n ? list[cb + lane] : 0;
+        mys = lane < n ? (int)slots[cb + lane] : 0;
+        fetch(A, 0);
+        for (int t = 0;; t += 2) {
+            fetch(B, min(t + 1, n - 1));
+            step(A);
+            if (t + 1 >= n) break;
+            fetch(A, min(t + 2, n - 1));
+            step(B);
+            if (t + 2 >= n) break;
         }
     }
     // epilogue: scale, add the pooled-level gradients (levels >= 2), store
@@ -756,7 +713,8 @@ hipError_t launch_attn_dq(const void* q, const void* k, const void* v, const voi
 {
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
-        hipLaunchKernelGGL(dq_bf16, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
+        auto kern = (g.L * g.K <= 64) ? dq_bf16<64> : dq_bf16<MAX_E>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
                            (const unsigned short*)q, (const unsigned short*)k,
                            (const unsigned short*)v, (const unsigned short*)out, lse,
                            (const unsigned short*)dout, (unsigned short*)dq, g, w);
@@ -804,7 +762,7 @@ hipError_t launch_attn_dkdv(const void* q, const void* k, const void* v, const f
 {
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
-        hipLaunchKernelGGL(dkdv_bf16, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
+        hipLaunchKernelGGL(dkdv_bf16, dim3((unsigned)nblk), dim3(64), 0, st,
                            (const unsigned short*)q, (const unsigned short*)k,
                            (const unsigned short*)v, lse, (const unsigned short*)dout,
                            (unsigned short*)dk, (unsigned short*)dv, g, w);

@@ -12,7 +12,7 @@
 // One softmax over the whole set, scale 1/sqrt(d); lse in natural log.
 //
 // The pooled entries of all levels (L*K of them) form extra tiles of 16,
-// read from the float32 pyramid and rounded to bf16 for the MFMA.
+// read from the bf16 copy of the pyramid that the pool pass writes.
 //
 // bf16 kernel (MFMA): one wave per query block, 4 waves per workgroup.
 //   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, A = key rows, B = query rows;
@@ -42,62 +42,6 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const unsigned short* p)
     return *(const bf16x8*)p;
 }
 
-__device__ __forceinline__ bf16x8 ld_f32_as_bf16x8(const float* p)
-{
-    float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
-    bf16x8 r;
-    r[0] = (bf16)a.x; r[1] = (bf16)a.y; r[2] = (bf16)a.z; r[3] = (bf16)a.w;
-    r[4] = (bf16)b.x; r[5] = (bf16)b.y; r[6] = (bf16)b.z; r[7] = (bf16)b.w;
-    return r;
-}
-
-// Pooled entry e (0 .. L*K-1) of query block i: level 1 + e / K, slot e % K
-// of the index list of the query's ancestor at that level.
-__device__ __forceinline__ long enrich_row(const Geo& g, const Ws& w, int gh, int i, int e,
-                                           int* level)
-{
-    int l = 1 + e / g.K, s = e % g.K;
-    int a = i >> (4 * (l - 1));
-    int j = w.idx[l - 1][((long)gh * g.n[l] + a) * g.K + s];
-    *level = l;
-    return ((long)gh * g.n[l] + j) * D;
-}
-
-// Pooled-entry tile t (entries 16t .. 16t+15): A operand of S^T (rows =
-// entries) into k0/k1, value rows into LDS (row-major, zero rows for masked
-// entries).  Returns the number of valid entries.
-__device__ __forceinline__ int fetch_enrich(const Geo& g, const Ws& w, int gh, int i, int t,
-                                            unsigned short* lds, bf16x8& k0, bf16x8& k1,
-                                            int lane)
-{
-    const int gq = lane >> 4, nq = lane & 15;
-    const int vr = lane >> 3, vc = (lane & 7) * 8;
-    const int e0 = t * BS;
-    const int nvalid = max(0, min(BS, g.L * g.K - e0));
-    const bf16x8 z = {};
-    k0 = z;
-    k1 = z;
-    if (nq < nvalid) {
-        int lv;
-        long off = enrich_row(g, w, gh, i, e0 + nq, &lv);
-        k0 = ld_f32_as_bf16x8(w.kbar[lv - 1] + off + 8 * gq);
-        k1 = ld_f32_as_bf16x8(w.kbar[lv - 1] + off + 32 + 8 * gq);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        int row = vr + 8 * h;
-        bf16x8 val = z;
-        if (row < nvalid) {
-            int lv;
-            long off = enrich_row(g, w, gh, i, e0 + row, &lv);
-            val = ld_f32_as_bf16x8(w.vbar[lv - 1] + off + vc);
-        }
-        *(bf16x8*)(lds + row * LDS_ROW + vc) = val;
-    }
-    return nvalid;
-}
-
-
 // Registers of one prefetched pair of fine tiles: rows vr and vr+8 (columns
 // vc .. vc+7) of the key and value tiles a and b.  Every load instruction
 // covers 8 whole 128-byte rows, the fast gather pattern of the vector L1.
@@ -105,23 +49,6 @@ struct FinePair {
     bf16x8 ka0, ka1, kb0, kb1;
     bf16x8 va0, va1, vb0, vb1;
 };
-
-__device__ __forceinline__ void load_fine(FinePair& f, const unsigned short* k,
-                                          const unsigned short* v, long hbase, int ja, int jb,
-                                          int lane)
-{
-    const int vr = lane >> 3, vc = (lane & 7) * 8;
-    const long a = hbase + (long)ja * BS * D + vr * D + vc;
-    const long b = hbase + (long)max(jb, 0) * BS * D + vr * D + vc;
-    f.ka0 = ld_bf16x8(k + a);
-    f.ka1 = ld_bf16x8(k + a + 8 * D);
-    f.va0 = ld_bf16x8(v + a);
-    f.va1 = ld_bf16x8(v + a + 8 * D);
-    f.kb0 = ld_bf16x8(k + b);
-    f.kb1 = ld_bf16x8(k + b + 8 * D);
-    f.vb0 = ld_bf16x8(v + b);
-    f.vb1 = ld_bf16x8(v + b + 8 * D);
-}
 
 template <int ROW>
 __device__ __forceinline__ void stage_rows(unsigned short* lds, bf16x8 r0, bf16x8 r1, int lane)
@@ -204,13 +131,27 @@ __device__ __forceinline__ void attend_pair(Online& st, bf16x8 bq0, bf16x8 bq1, 
     }
 }
 
+constexpr int MAX_E = MAX_L * 64;  // pooled entries per query block (L * K)
+
+// Per-wave LDS: two value tiles (160-byte rows), two key tiles (144-byte
+// rows) and the table of pooled-entry rows (ECAP ints).  With ECAP = 64 a
+// workgroup of 4 waves needs under 40 KB, so 4 workgroups share a CU.
+template <int ECAP>
+struct FwdLds {
+    static constexpr int V_TILE = BS * LDS_ROW;  // bf16 elements
+    static constexpr int K_TILE = BS * ROW_A;
+    static constexpr int PER_WAVE = 2 * V_TILE + 2 * K_TILE + 2 * ECAP;  // in bf16 units
+};
+
+template <int ECAP>
 __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __restrict__ q,
                                                      const unsigned short* __restrict__ k,
                                                      const unsigned short* __restrict__ v,
                                                      unsigned short* __restrict__ out,
                                                      float* __restrict__ lse, Geo g, Ws w)
 {
-    __shared__ __attribute__((aligned(16))) unsigned short smem[4][4][TILE_ELEMS];
+    using Lay = FwdLds<ECAP>;
+    __shared__ __attribute__((aligned(16))) unsigned short smem[4][Lay::PER_WAVE];
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, nq = lane & 15;
     const long qblk = (long)xcd_block(blockIdx.x, gridDim.x) * 4 + wv;  // over G * n1
@@ -223,23 +164,69 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
     const bf16x8 bq1 = ld_bf16x8(q + qbase + nq * D + 32 + 8 * gq);
     // the query block's K fine blocks, one per lane (K <= 64)
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
-    const int myj = lane < g.K ? sel[lane] : -1;
+    const int myj = lane < g.K ? sel[lane] : 0;
+    // pooled entries e = (l-1)*K + slot: their rows in the bf16 pooled arrays
+    const int E = (g.flags & LLSA_NO_ENRICH) ? 0 : g.L * g.K;
+    int* ent = (int*)(smem[wv] + 2 * Lay::V_TILE + 2 * Lay::K_TILE);
+    for (int l = 1; l <= (E ? g.L : 0); ++l) {
+        const long a = (long)gh * g.n[l] + (i >> (4 * (l - 1)));
+        for (int s0 = 0; s0 < g.K; s0 += 64)
+            if (s0 + lane < g.K)
+                ent[(l - 1) * g.K + s0 + lane] =
+                    (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * g.K + s0 + lane]);
+    }
+    lds_fence();
 
     Online st;
 #pragma unroll
     for (int d = 0; d < 4; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m = -INFINITY;
     st.lsum = 0.f;
-    unsigned short* la = smem[wv][0];  // value tiles (transposed reads)
-    unsigned short* lb = smem[wv][1];
-    unsigned short* lka = smem[wv][2];  // key tiles (operand reads)
-    unsigned short* lkb = smem[wv][3];
+    unsigned short* la = smem[wv];  // value tiles (transposed reads)
+    unsigned short* lb = la + Lay::V_TILE;
+    unsigned short* lka = lb + Lay::V_TILE;  // key tiles (operand reads)
+    unsigned short* lkb = lka + Lay::K_TILE;
 
-    // fine tiles, two per step; the next pair's loads are in flight meanwhile.
-    // Two register sets alternate; prefetches are unconditional (indices
-    // clamped to the last block) so the compiler's wait counts stay exact.
-    auto jsel = [&](int t) { return __builtin_amdgcn_readlane(myj, min(t, g.K - 1)); };
-    auto step = [&](const FinePair& f, bool full) {
+    // One pipeline over all tile pairs: NF pairs of fine tiles, then NP - NF
+    // pairs of pooled tiles.  The next pair's loads are in flight while this
+    // one is computed (two register sets alternate).  Loads are issued
+    // unconditionally -- out-of-range tiles re-read a valid row and are
+    // masked -- so the compiler's wait counts stay exact.
+    const int NF = (g.K + 1) / 2;
+    const int NT = (E + BS - 1) / BS;  // pooled tiles
+    const int NP = NF + (NT + 1) / 2;
+    const int vr = lane >> 3, vc = (lane & 7) * 8;
+    auto load_pair = [&](FinePair& f, int p) {
+        long ka, kb, ka8, kb8;  // element offsets of rows vr and vr + 8
+        const unsigned short *kp, *vp;
+        if (p < NF) {
+            const int ja = __builtin_amdgcn_readlane(myj, min(2 * p, g.K - 1));
+            const int jb = __builtin_amdgcn_readlane(myj, min(2 * p + 1, g.K - 1));
+            ka = hbase + ((long)ja * BS + vr) * D + vc;
+            kb = hbase + ((long)jb * BS + vr) * D + vc;
+            ka8 = ka + 8 * D;
+            kb8 = kb + 8 * D;
+            kp = k;
+            vp = v;
+        } else {
+            const int t = 2 * (p - NF);
+            ka = (long)ent[min(BS * t + vr, E - 1)] * D + vc;
+            ka8 = (long)ent[min(BS * t + vr + 8, E - 1)] * D + vc;
+            kb = (long)ent[min(BS * t + BS + vr, E - 1)] * D + vc;
+            kb8 = (long)ent[min(BS * t + BS + vr + 8, E - 1)] * D + vc;
+            kp = w.kb16;
+            vp = w.vb16;
+        }
+        f.ka0 = ld_bf16x8(kp + ka);
+        f.ka1 = ld_bf16x8(kp + ka8);
+        f.va0 = ld_bf16x8(vp + ka);
+        f.va1 = ld_bf16x8(vp + ka8);
+        f.kb0 = ld_bf16x8(kp + kb);
+        f.kb1 = ld_bf16x8(kp + kb8);
+        f.vb0 = ld_bf16x8(vp + kb);
+        f.vb1 = ld_bf16x8(vp + kb8);
+    };
+    auto step = [&](const FinePair& f, int p) {
         stage_rows<ROW_A>(lka, f.ka0, f.ka1, lane);
         stage_rows<ROW_A>(lkb, f.kb0, f.kb1, lane);
         stage_rows<LDS_ROW>(la, f.va0, f.va1, lane);
@@ -248,38 +235,26 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
         bf16x8 ka0, ka1, kb0, kb1;
         key_operand(lka, ka0, ka1, lane);
         key_operand(lkb, kb0, kb1, lane);
-        if (full)
+        if (p < NF && g.K > 1) {
             attend_pair<false>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, BS, BS, c, lane);
-        else
-            attend_pair<true>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, BS, 0, c, lane);
-    };
-    if (g.K == 1) {
-        FinePair A;
-        load_fine(A, k, v, hbase, jsel(0), jsel(0), lane);
-        step(A, false);
-    } else {
-        const int npairs = g.K / 2;
-        FinePair A, B;
-        load_fine(A, k, v, hbase, jsel(0), jsel(1), lane);
-        for (int p = 0;; p += 2) {
-            load_fine(B, k, v, hbase, jsel(2 * p + 2), jsel(2 * p + 3), lane);
-            step(A, true);
-            if (p + 1 >= npairs) break;
-            load_fine(A, k, v, hbase, jsel(2 * p + 4), jsel(2 * p + 5), lane);
-            step(B, true);
-            if (p + 2 >= npairs) break;
-        }
-    }
-    // pooled tokens of every level
-    if (!(g.flags & LLSA_NO_ENRICH)) {
-        const int nt = (g.L * g.K + BS - 1) / BS;
-        for (int t = 0; t < nt; t += 2) {
-            bf16x8 ka0, ka1, kb0, kb1;
-            int na = fetch_enrich(g, w, gh, i, t, la, ka0, ka1, lane);
-            int nb = fetch_enrich(g, w, gh, i, t + 1, lb, kb0, kb1, lane);
+        } else {
+            const int e0 = p < NF ? 0 : BS * 2 * (p - NF);
+            const int na = p < NF ? BS : max(0, min(BS, E - e0));
+            const int nb = p < NF ? 0 : max(0, min(BS, E - e0 - BS));
             attend_pair<true>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, na, nb, c, lane);
         }
+    };
+    FinePair A, B;
+    load_pair(A, 0);
+    for (int p = 0;; p += 2) {
+        load_pair(B, min(p + 1, NP - 1));
+        step(A, p);
+        if (p + 1 >= NP) break;
+        load_pair(A, min(p + 2, NP - 1));
+        step(B, p + 1);
+        if (p + 2 >= NP) break;
     }
+
     const float lsum = sum_x4(st.lsum);
     const float inv = 1.0f / lsum;
     const long obase = qbase + nq * D + 4 * gq;
@@ -356,7 +331,8 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* ou
 {
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
-        hipLaunchKernelGGL(attn_fwd_bf16, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
+        auto kern = (g.L * g.K <= 64) ? attn_fwd_bf16<64> : attn_fwd_bf16<MAX_E>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
                            (const unsigned short*)q, (const unsigned short*)k,
                            (const unsigned short*)v, (unsigned short*)out, lse, g, w);
     } else {

@@ -10,6 +10,8 @@
 // channels 4*sub .. 4*sub+3, so each token row (128 B in bf16) is read whole
 // by 16 adjacent lanes.  Level 2 (one block per workgroup) is the mean of the
 // 16 level-1 means, formed in LDS.  pool_up forms levels >= 3 from level l-1.
+// The pooled keys and values are also stored rounded to bf16 (the operands
+// the attention kernels feed to the MFMA).
 #include "common.h"
 
 namespace llsa {
@@ -30,6 +32,12 @@ template <> struct Vec4<unsigned short> {
                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
     }
 };
+
+__device__ __forceinline__ void put_bf16x4(unsigned short* dst, long off, float4 s)
+{
+    u16x4 o = {f2bf(s.x), f2bf(s.y), f2bf(s.z), f2bf(s.w)};
+    *(u16x4*)(dst + off) = o;
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T* __restrict__ k,
@@ -62,7 +70,9 @@ __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T
         }
         const float inv = 1.0f / BS;
         s = make_float4(s.x * inv, s.y * inv, s.z * inv, s.w * inv);
-        *(float4*)(lv1 + ((long)gh * n1 + b0 + blk) * D + 4 * sub) = s;
+        const long row = (long)gh * n1 + b0 + blk;
+        *(float4*)(lv1 + row * D + 4 * sub) = s;
+        if (tensor) put_bf16x4(tensor == 1 ? w.kb16 : w.vb16, (w.prow[0] + row) * D + 4 * sub, s);
     }
     if (g.L >= 2) {  // b0 is a multiple of 16, so this workgroup is one level-2 block
         m1[blk][4 * sub + 0] = s.x;
@@ -74,7 +84,11 @@ __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T
             float a = 0.f;
 #pragma unroll
             for (int b = 0; b < 16; ++b) a += m1[b][threadIdx.x];
-            lv2[((long)gh * g.n[2] + b0 / 16) * D + threadIdx.x] = a * (1.0f / BS);
+            const long row = (long)gh * g.n[2] + b0 / 16;
+            lv2[row * D + threadIdx.x] = a * (1.0f / BS);
+            if (tensor)
+                (tensor == 1 ? w.kb16 : w.vb16)[(w.prow[1] + row) * D + threadIdx.x] =
+                    f2bf(a * (1.0f / BS));
         }
     }
 }
@@ -92,6 +106,8 @@ __global__ __launch_bounds__(256) void pool_up(Geo g, Ws w, int l)
     float a = 0.f;
     for (int t = 0; t < BS; ++t) a += src[(row * BS + t) * D + c];
     dst[id] = a * (1.0f / BS);
+    if (tensor)
+        (tensor == 1 ? w.kb16 : w.vb16)[(w.prow[l - 1] + row) * D + c] = f2bf(a * (1.0f / BS));
 }
 
 }  // namespace

@@ -42,10 +42,15 @@ __device__ __forceinline__ Cands make_cands(const Geo& g, const Ws& w, int l, in
     return cs;
 }
 
-// 16-bit mask of which of the bins 16*grp .. 16*grp+15 query block i selected.
-__device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp)
+// 16-bit mask of which of the bins 16*grp .. 16*grp+15 query block i selected,
+// and in *first the number of its entries below bin 16*grp.  The list is
+// ascending, so the hits form one run starting at *first: the hit in bin b
+// sits at position *first + popcount(mask & ((1 << b) - 1)).
+__device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp, int* first)
 {
     unsigned m = 0;
+    int below = 0;
+    const int lo = BS * grp;
     if ((K & 3) == 0) {
         for (int e = 0; e < K; e += 4) {
             const int4 j4 = *(const int4*)(I + e);
@@ -53,30 +58,17 @@ __device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp)
             m |= ((j4.y >> 4) == grp) ? 1u << (j4.y & 15) : 0u;
             m |= ((j4.z >> 4) == grp) ? 1u << (j4.z & 15) : 0u;
             m |= ((j4.w >> 4) == grp) ? 1u << (j4.w & 15) : 0u;
+            below += (j4.x < lo) + (j4.y < lo) + (j4.z < lo) + (j4.w < lo);
         }
     } else {
         for (int e = 0; e < K; ++e) {
             const int j = I[e];
             m |= ((j >> 4) == grp) ? 1u << (j & 15) : 0u;
+            below += j < lo;
         }
     }
+    *first = below;
     return m;
-}
-
-// Position of block j in the ascending list I[0..K-1] (j is present): the
-// number of entries below j; independent loads, no dependent search.
-__device__ __forceinline__ int list_pos(const int* I, int K, int j)
-{
-    int pos = 0;
-    if ((K & 3) == 0) {
-        for (int e = 0; e < K; e += 4) {
-            const int4 j4 = *(const int4*)(I + e);
-            pos += (j4.x < j) + (j4.y < j) + (j4.z < j) + (j4.w < j);
-        }
-    } else {
-        for (int e = 0; e < K; ++e) pos += I[e] < j;
-    }
-    return pos;
 }
 
 // One workgroup (4 waves) per 16 sibling key blocks; one candidate query
@@ -102,11 +94,11 @@ __global__ __launch_bounds__(256) void transpose_pass(Geo g, Ws w, int l)
     for (int b = 0; b < 16; ++b) run[b] = FILL ? rowptr[min(16 * grp + b, g.n[l])] : 0;
     for (int c0 = 0; c0 < cs.n; c0 += 256) {
         const int c = c0 + tid;
-        int i = 0;
+        int i = 0, first = 0;
         unsigned m = 0;
         if (c < cs.n) {
             i = cs.row(c);
-            m = hit_mask(I + (long)i * g.K, g.K, grp);
+            m = hit_mask(I + (long)i * g.K, g.K, grp, &first);
         }
         unsigned long long bal[16];
 #pragma unroll
@@ -127,8 +119,7 @@ __global__ __launch_bounds__(256) void transpose_pass(Geo g, Ws w, int l)
             if (FILL && ((m >> b) & 1u)) {
                 const int pos = run[b] + before + __popcll(bal[b] & below);
                 col[pos] = i;
-                if (l >= 2)  // slots feed the pooled-token gradients of levels >= 2
-                    slots[pos] = (unsigned char)list_pos(I + (long)i * g.K, g.K, 16 * grp + b);
+                slots[pos] = (unsigned char)(first + __popc(m & ((1u << b) - 1u)));
             }
             run[b] += total;
         }
