@@ -77,10 +77,18 @@ def sha_of_sources():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, w):
-    """Measured HBM bytes per launch from committed rocprofv3 --pmc counters,
-    if they were taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "pmc_%s_%s.json" % (kernel, w.name))
+PMC_SUMMARY = "pmc_fetch_write_llsa_kernels_%s.json"
+TRACE_SUMMARY = "kernel_trace_llsa_kernels_%s.md"
+KERNEL_OF_STAGE = {"zorder": "zorder_kernel", "pool": "pool_l12", "select": "select_kernel",
+                   "attn_fwd": "attn_fwd_bf16", "transpose": "transpose_pass",
+                   "dq": "dq_bf16", "enrich": "enrich_bwd_bf16", "dkdv": "dkdv_bf16"}
+
+
+def load_traffic(stage, w):
+    """Measured HBM bytes per launch of a stage's kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this workload, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", PMC_SUMMARY % w.name)
     if not os.path.exists(path):
         return None
     try:
@@ -89,7 +97,84 @@ def load_traffic(kernel, w):
         return None
     if rec.get("sources_sha") != sha_of_sources():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    want = KERNEL_OF_STAGE.get(stage, stage)
+    for name, k in rec.get("kernels", {}).items():
+        if name.split("<")[0] == want:
+            return k.get("hbm_bytes_per_launch")
+    return None
+
+
+def _short_kernel(name):
+    n = name.replace("llsa::(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0].replace("HIP_vector_type<unsigned int, 4u> ", "uint4")
+
+
+def summarize_trace(db, out, cmd, bench_json=None):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats results database."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = list(c.execute("select name, total_calls, total_duration, average, percentage "
+                          "from top_kernels"))
+    with open(out, "w") as f:
+        f.write("# rocprofv3 kernel trace: LLSA kernels, workload %s\n\n" % os.path.basename(out)
+                .replace("kernel_trace_llsa_kernels_", "").replace(".md", ""))
+        f.write("Command (on the MI355X, from the repository root):\n\n    %s\n\n" % cmd)
+        f.write("Sources: csrc sha256 prefix %s\n\n" % sha_of_sources())
+        f.write("`top_kernels` view of the results database; durations in microseconds.\n\n")
+        f.write("| kernel | calls | total us | avg us | % |\n|---|---|---|---|---|\n")
+        for r in rows:
+            f.write("| %s | %d | %.0f | %.2f | %.2f |\n" % (_short_kernel(r[0]), r[1], r[2],
+                                                         r[3], r[4]))
+        if bench_json:
+            b = json.loads(open(bench_json).read().strip().splitlines()[-1])
+            f.write("\nHIP-event stage times of the same (profiled) bench run, ms per launch:\n\n")
+            f.write("    %s\n\nms_per_step %.4f, value %.2f TFLOP/s\n"
+                    % (json.dumps(b["stage_ms"]), b["ms_per_step"], b["value"]))
+
+
+def summarize_pmc(fetch_db, write_db, out, cmd, workload):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every kernel, scaled by what
+    the same counter reads for the plain device copy of known size that the
+    profiled bench run ends with (--calib-copy-mib)."""
+    import sqlite3
+
+    def per_kernel(db, counter):
+        c = sqlite3.connect(db)
+        acc = {}
+        for name, val in c.execute("select kernel_name, value from counters_collection "
+                                   "where counter_name = ?", (counter,)):
+            acc.setdefault(_short_kernel(name), []).append(val)
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fet, wri = per_kernel(fetch_db, "FETCH_SIZE"), per_kernel(write_db, "WRITE_SIZE")
+    copy = [k for k in fet if "copyBuffer" in k or "copy" in k.lower()]
+    if not copy:
+        raise SystemExit("no copy kernel in the FETCH_SIZE run (use --calib-copy-mib)")
+    ck = copy[0]
+    copy_kib = CALIB_COPY_MIB * 1024.0
+    f_fac = copy_kib / fet[ck]
+    w_fac = copy_kib / wri[ck]
+    kernels = {}
+    for k in sorted(set(fet) | set(wri)):
+        if k == ck:
+            continue
+        fb = fet.get(k, 0.0) * f_fac * 1024
+        wb = wri.get(k, 0.0) * w_fac * 1024
+        kernels[k] = {"fetch_kib_raw": round(fet.get(k, 0.0), 1),
+                      "write_kib_raw": round(wri.get(k, 0.0), 1),
+                      "hbm_bytes_per_launch": int(fb + wb),
+                      "fetch_bytes": int(fb), "write_bytes": int(wb)}
+    rec = {"workload": workload, "sources_sha": sha_of_sources(), "commands": cmd,
+           "calibration": {"kernel": ck, "copy_bytes": CALIB_COPY_MIB << 20,
+                           "fetch_kib_raw": round(fet[ck], 1), "write_kib_raw": round(wri[ck], 1),
+                           "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+           "kernels": kernels}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+
+
+CALIB_COPY_MIB = 256
 
 
 def cpu_baseline(w, inp, budget_s=30.0):
@@ -152,7 +237,23 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for PMC scaling)")
+    ap.add_argument("--summarize-trace", metavar="DB",
+                    help="write the markdown summary of a rocprofv3 --kernel-trace --stats "
+                         "database to --out and exit (no GPU)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write the JSON summary of rocprofv3 --pmc FETCH_SIZE and "
+                         "WRITE_SIZE databases to --out and exit (no GPU)")
+    ap.add_argument("--out")
+    ap.add_argument("--cmd", default="", help="the profiling command, recorded in the summary")
+    ap.add_argument("--bench-json", help="bench output of the profiled run (trace summary)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.cmd, args.bench_json)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.out, args.cmd,
+                      args.workload)
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the hot path shards over heads "
               "with no communication); --gpus %d is not supported" % args.gpus, file=sys.stderr)

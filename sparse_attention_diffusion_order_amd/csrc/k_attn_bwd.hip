@@ -417,26 +417,27 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
 //                                     Q^T, dO^T read transposed from LDS)
 struct QBlock {
     bf16x8 q0, q1, d0, d1;  // rows sr and sr+8, channels sc .. sc+7
-    float4 l4, e4;          // lse and delta of rows 4(lane/16) .. +3
-    float4 p4, s4;          // level-1 pooled P and dS of those rows
+    float x;                // lane < 16: lse of row lane; < 32: delta of row
+                            // lane - 16; else the level-1 pooled P (lanes 32..47)
+                            // and dS (48..63) of row lane % 16
 };
 
+// One dword per lane carries all per-row scalars of the block (a single
+// 256-byte load instead of four replicated 16-byte-per-lane loads).
 __device__ __forceinline__ void load_qblock(QBlock& f, const unsigned short* q,
                                             const unsigned short* dout, const float* lse,
                                             const float* delta, const float* pe, long hbase,
                                             long tbase, int i, int lane)
 {
-    const int gq = lane >> 4;
     const int sr = lane >> 3, sc = (lane & 7) * 8;
     const long a = hbase + ((long)i * BS + sr) * D + sc;
     f.q0 = ld8(q + a);
     f.q1 = ld8(q + a + 8 * D);
     f.d0 = ld8(dout + a);
     f.d1 = ld8(dout + a + 8 * D);
-    f.l4 = *(const float4*)(lse + tbase + (long)i * BS + 4 * gq);
-    f.e4 = *(const float4*)(delta + tbase + (long)i * BS + 4 * gq);
-    f.p4 = *(const float4*)(pe + 4 * gq);
-    f.s4 = *(const float4*)(pe + BS + 4 * gq);
+    const long t = tbase + (long)i * BS + (lane & 15);
+    const float* src = lane < 16 ? lse + t : lane < 32 ? delta + t : pe + (lane - 32);
+    f.x = *src;
 }
 
 __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict__ q,
@@ -448,6 +449,7 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
                                                 unsigned short* __restrict__ dv, Geo g, Ws w)
 {
     __shared__ __attribute__((aligned(16))) unsigned short lq[TILE], ld[TILE];
+    __shared__ __attribute__((aligned(16))) float aux[4 * BS];
     const int lane = threadIdx.x;
     const int gq = lane >> 4, nq = lane & 15;
     const long kblk = xcd_block(blockIdx.x, gridDim.x);
@@ -466,20 +468,27 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     const int rr = (lane & 15) >> 2, xx = lane & 3;
     const f32x4 zero = {};
     f32x4 accK[4] = {}, accV[4] = {};
-    auto step = [&](const QBlock& f) {
+    // live == false (the padding step of an odd-length chunk): the MFMAs run
+    // on valid data but contribute zero
+    auto step = [&](const QBlock& f, bool live) {
         put_rows(lq, f.q0, f.q1, lane);
         put_rows(ld, f.d0, f.d1, lane);
+        aux[lane] = f.x;
         lds_fence();
+        const float4 l4 = *(const float4*)(aux + 4 * gq);
+        const float4 e4 = *(const float4*)(aux + BS + 4 * gq);
+        const float4 p4 = *(const float4*)(aux + 2 * BS + 4 * gq);
+        const float4 s4 = *(const float4*)(aux + 3 * BS + 4 * gq);
         const bf16x8 aq0 = *(const bf16x8*)(lq + nq * LDS_ROW + 8 * gq);
         const bf16x8 aq1 = *(const bf16x8*)(lq + nq * LDS_ROW + 32 + 8 * gq);
         const bf16x8 ad0 = *(const bf16x8*)(ld + nq * LDS_ROW + 8 * gq);
         const bf16x8 ad1 = *(const bf16x8*)(ld + nq * LDS_ROW + 32 + 8 * gq);
         const f32x4 s = mfma32(aq1, bk1, mfma32(aq0, bk0, zero));   // S[query][key]
         const f32x4 dp = mfma32(ad1, bv1, mfma32(ad0, bv0, zero));  // dP[query][key]
-        const float lr[4] = {f.l4.x, f.l4.y, f.l4.z, f.l4.w};
-        const float dr[4] = {f.e4.x, f.e4.y, f.e4.z, f.e4.w};
-        const float pr[4] = {f.p4.x, f.p4.y, f.p4.z, f.p4.w};
-        const float sr_[4] = {f.s4.x, f.s4.y, f.s4.z, f.s4.w};
+        const float lr[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dr[4] = {e4.x, e4.y, e4.z, e4.w};
+        const float pr[4] = {p4.x, p4.y, p4.z, p4.w};
+        const float sr_[4] = {s4.x, s4.y, s4.z, s4.w};
         bf16x4 bp, bs;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -489,8 +498,8 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
                 p = fmaf(pr[r], 1.0f / BS, p);
                 ds = fmaf(sr_[r], 1.0f / BS, ds);
             }
-            bp[r] = (bf16)p;
-            bs[r] = (bf16)ds;
+            bp[r] = (bf16)(live ? p : 0.f);
+            bs[r] = (bf16)(live ? ds : 0.f);
         }
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -508,21 +517,21 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
         const float* pe = w.pe1 + (((long)gh * g.n[1] + i) * g.K + sl) * 2 * BS;
         load_qblock(f, q, dout, lse, w.delta, pe, hbase, tbase, i, lane);
     };
-    // two register sets alternate; the prefetch past the end re-reads the
-    // last block (valid memory) and is simply not used
+    // two register sets alternate, each filled one step before it is used.
+    // The loop body is one basic block: a conditional exit between a fetch
+    // and its use would let the compiler sink the loads down to the use.
+    // Fetches past the end re-read the last block (valid memory).
     QBlock A, B;
     for (int cb = beg; cb < end; cb += 64) {
         const int n = min(64, end - cb);
         myi = lane < n ? list[cb + lane] : 0;
         mys = lane < n ? (int)slots[cb + lane] : 0;
         fetch(A, 0);
-        for (int t = 0;; t += 2) {
+        for (int t = 0; t < n; t += 2) {
             fetch(B, min(t + 1, n - 1));
-            step(A);
-            if (t + 1 >= n) break;
+            step(A, true);
             fetch(A, min(t + 2, n - 1));
-            step(B);
-            if (t + 2 >= n) break;
+            step(B, t + 1 < n);
         }
     }
     // epilogue: scale, add the pooled-level gradients (levels >= 2), store
