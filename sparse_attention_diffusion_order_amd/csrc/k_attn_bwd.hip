@@ -289,16 +289,25 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
                                                        const unsigned short* __restrict__ dout,
                                                        Geo g, Ws w)
 {
+    // per-wave Q and dO tiles; after the last tile the same memory holds the
+    // four waves' partial sums for the cross-wave reduction
     __shared__ __attribute__((aligned(16))) unsigned short smem[4][2][TILE];
-    __shared__ float red[4][2][4][4][64];  // [wave][dk|dv][dtile][r][lane]
+    float* red = (float*)&smem[0][0][0];  // [wave][dtile][r][lane], one kind at a time
+    static_assert(sizeof(smem) >= 4 * 4 * 4 * 64 * sizeof(float), "reduction buffer");
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int gq = lane >> 4, nq = lane & 15;
     const int gh = blockIdx.x / g.n[2], a2 = blockIdx.x % g.n[2];
     const float c = g.scale * LOG2E;
     const int rr = (lane & 15) >> 2, xx = lane & 3;
+    const int sr = lane >> 3, sc = (lane & 7) * 8;
     unsigned short* lq = smem[wv][0];
     unsigned short* ld = smem[wv][1];
     const f32x4 zero = {};
+    // this wave's four query blocks i = 16 a2 + 4 wv + u (u < 4)
+    auto row_addr = [&](int u) {
+        const int i = 16 * a2 + 4 * wv + u;
+        return ((long)gh * g.N + (long)i * BS + sr) * D + sc;
+    };
     for (int l = 2; l <= g.L; ++l) {
         const int al = a2 >> (4 * (l - 2));
         const int* sel = w.idx[l - 1] + ((long)gh * g.n[l] + al) * g.K;
@@ -313,12 +322,19 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
                 bv1 = ld8f(w.vbar[l - 1] + off + 32 + 8 * gq);
             }
             f32x4 ak[4] = {}, av[4] = {};
+            // rows of block u + 1 are loaded while block u is computed
+            long a = row_addr(0);
+            bf16x8 q0 = ld8(q + a), q1 = ld8(q + a + 8 * D);
+            bf16x8 d0 = ld8(dout + a), d1 = ld8(dout + a + 8 * D);
+#pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i = 16 * a2 + 4 * wv + u;
-                const long qb = ((long)gh * g.N + (long)i * BS) * D;
-                stage_rows(lq, q, qb, true, lane);
-                stage_rows(ld, dout, qb, true, lane);
-                wave_lds_sync();
+                put_rows(lq, q0, q1, lane);
+                put_rows(ld, d0, d1, lane);
+                a = row_addr(min(u + 1, 3));
+                q0 = ld8(q + a); q1 = ld8(q + a + 8 * D);
+                d0 = ld8(dout + a); d1 = ld8(dout + a + 8 * D);
+                lds_fence();
                 const bf16x8 aq0 = *(const bf16x8*)(lq + nq * LDS_ROW + 8 * gq);
                 const bf16x8 aq1 = *(const bf16x8*)(lq + nq * LDS_ROW + 32 + 8 * gq);
                 const bf16x8 ad0 = *(const bf16x8*)(ld + nq * LDS_ROW + 8 * gq);
@@ -342,26 +358,25 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
                     ak[d] = mfma16(lds_read_tr(lq + off), pS, ak[d]);
                     av[d] = mfma16(lds_read_tr(ld + off), pP, av[d]);
                 }
-                wave_lds_sync();
             }
-            // reduce the four waves in a fixed order
+            // reduce the four waves in a fixed order, dk then dv
+            for (int kind = 0; kind < 2; ++kind) {
+                __syncthreads();  // tiles (or the previous kind) no longer read
 #pragma unroll
-            for (int d = 0; d < 4; ++d)
+                for (int d = 0; d < 4; ++d)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    red[wv][0][d][r][lane] = ak[d][r];
-                    red[wv][1][d][r][lane] = av[d][r];
-                }
-            __syncthreads();
-            for (int x = threadIdx.x; x < 2 * 4 * 4 * 64; x += blockDim.x) {
-                const int kind = x >> 10, d = (x >> 8) & 3, r = (x >> 6) & 3, ln = x & 63;
-                float s = red[0][kind][d][r][ln] + red[1][kind][d][r][ln] +
-                          red[2][kind][d][r][ln] + red[3][kind][d][r][ln];
-                const int ent = e0 + (ln & 15), dim = 16 * d + 4 * (ln >> 4) + r;
-                if (ent < g.K) {
-                    float* dst = w.part[l - 1] +
-                                 ((((long)gh * g.n[2] + a2) * g.K + ent) * 2 + kind) * D;
-                    dst[dim] = kind == 0 ? s * g.scale : s;
+                    for (int r = 0; r < 4; ++r)
+                        red[((wv * 4 + d) * 4 + r) * 64 + lane] = kind == 0 ? ak[d][r] : av[d][r];
+                __syncthreads();
+                for (int x = threadIdx.x; x < 4 * 4 * 64; x += blockDim.x) {
+                    const float s = red[x] + red[1024 + x] + red[2048 + x] + red[3072 + x];
+                    const int d = x >> 8, r = (x >> 6) & 3, ln = x & 63;
+                    const int ent = e0 + (ln & 15), dim = 16 * d + 4 * (ln >> 4) + r;
+                    if (ent < g.K) {
+                        float* dst = w.part[l - 1] +
+                                     ((((long)gh * g.n[2] + a2) * g.K + ent) * 2 + kind) * D;
+                        dst[dim] = kind == 0 ? s * g.scale : s;
+                    }
                 }
             }
             __syncthreads();
@@ -386,19 +401,30 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
     float sk = 0.f, sv = 0.f;
     const int beg = uniform(rp[j]), end = uniform(rp[j + 1]);
     // list entries in batches of 64: lane e holds entry beg + e (row offset
-    // into the partials); then the batch's partial rows are summed in order
+    // into the partials).  The batch's (entry, level-2 block) rows are summed
+    // in order, eight loads in flight at a time.
+    const int lane = threadIdx.x & 63;
     for (int e0 = beg; e0 < end; e0 += 64) {
         const int ne = min(64, end - e0);
-        const int lane = threadIdx.x & 63;
         int off = 0;  // in rows of 2*D floats
         if (lane < ne) off = cl[e0 + lane] * span * g.K + sl[e0 + lane];
-        for (int e = 0; e < ne; ++e) {
-            const long o = (long)__builtin_amdgcn_readlane(off, e) * 2 * D;
-            for (int a2 = 0; a2 < span; ++a2) {
-                const float* p = part + o + (long)a2 * g.K * 2 * D;
-                sk += p[0];
-                sv += p[D];
+        const int nrow = ne * span;
+        for (int q0 = 0; q0 < nrow; q0 += 8) {
+            float vk[8], vv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int qq = min(q0 + u, nrow - 1);
+                const int e = qq / span, a2 = qq % span;
+                const long o = ((long)__builtin_amdgcn_readlane(off, e) + (long)a2 * g.K) * 2 * D;
+                vk[u] = part[o];
+                vv[u] = part[o + D];
             }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q0 + u < nrow) {
+                    sk += vk[u];
+                    sv += vv[u];
+                }
         }
     }
     float* dst = w.dbar[l - 1] + blk * 2 * D;

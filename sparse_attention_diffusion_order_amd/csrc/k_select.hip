@@ -16,10 +16,11 @@
 // level (candidates = all blocks).  Scores of the R x M tile live in LDS.
 // Summation order of a score: four partial sums of 16 channels each, combined
 // pairwise -- fixed, so the result does not depend on the launch.
-// Each wave then selects for its rows with an MSB-first radix search for the
-// K-th largest key (keys = order-preserving integer images of the scores),
-// ballots for ties (lowest candidate position first) and a ballot prefix
-// count to write the winners in ascending order.
+// Each wave then selects for its rows with an MSB-first radix search on the
+// keys (order-preserving integer images of the scores) for a threshold that
+// admits exactly the K winners, ballots for ties at the K-th key (lowest
+// candidate position first) and a ballot prefix count to write the winners
+// in ascending order.
 #include "common.h"
 
 namespace llsa {
@@ -29,6 +30,57 @@ __device__ __forceinline__ unsigned order_key(float f)
 {
     unsigned u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Top-K of each of `rows` score rows (LDS, [rows][M]) written ascending to
+// out[r * K ..]; one wave per row at a time.
+template <int KPL>
+__device__ __forceinline__ void select_rows(const float* sc, const int* cand, int* out, int rows,
+                                            int M, int K)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int r = wv; r < rows; r += blockDim.x / 64) {
+        unsigned key[KPL];
+        bool ok[KPL];
+#pragma unroll
+        for (int s = 0; s < KPL; ++s) {
+            int p = s * 64 + lane;
+            ok[s] = p < M;
+            key[s] = ok[s] ? order_key(sc[r * M + p]) : 0u;
+        }
+        // MSB-first search for a threshold T with #(key >= T) >= K.  It ends
+        // at the K-th largest key, or earlier as soon as exactly K keys are
+        // >= T: those K keys are then the winners and T splits them from the
+        // rest (this is the common case; exact ties run to the last bit).
+        unsigned T = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            unsigned t = T | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int s = 0; s < KPL; ++s) cnt += __popcll(__ballot(ok[s] && key[s] >= t));
+            if (cnt >= K) {
+                T = t;
+                if (cnt == K) break;
+            }
+        }
+        int gt = 0;
+#pragma unroll
+        for (int s = 0; s < KPL; ++s) gt += __popcll(__ballot(ok[s] && key[s] > T));
+        int need = K - gt;  // ties at T: lowest candidate positions win
+        int eq_before = 0, out_before = 0;
+        int* orow = out + (long)r * K;
+#pragma unroll
+        for (int s = 0; s < KPL; ++s) {
+            bool eq = ok[s] && key[s] == T;
+            unsigned long long beq = __ballot(eq);
+            bool take = (ok[s] && key[s] > T) || (eq && eq_before + __popcll(beq & below) < need);
+            unsigned long long bt = __ballot(take);
+            if (take) orow[out_before + __popcll(bt & below)] = cand[s * 64 + lane];
+            eq_before += __popcll(beq);
+            out_before += __popcll(bt);
+        }
+    }
 }
 
 template <int KPL>
@@ -96,62 +148,180 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
     }
     __syncthreads();
 
+    select_rows<KPL>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K);
+}
+
+// Sum of x over the 16 lanes of each DPP row (every lane gets its row's sum).
+__device__ __forceinline__ int row16_sum(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false);  // row_ror 4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);  // row_ror 8
+    return x;
+}
+
+// Top-K of 16 score rows (LDS, [16][M]; rows >= `rows` ignored), written in
+// ascending candidate order to out[r * K ..].  Wave w takes rows 4w .. 4w+3,
+// one per 16-lane group; lane n of a group holds the keys of candidates
+// 16s + n (s < KPG), so all counting runs on the vector ALU with DPP row sums
+// and the four rows of a wave advance together.
+template <int KPG>
+__device__ __forceinline__ void select_rows16(const float* sc, const int* cand, int* out,
+                                              int rows, int M, int K)
+{
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const unsigned long long below = (1ull << lane) - 1ull;
-    for (int r = wv; r < rows; r += blockDim.x / 64) {
-        unsigned key[KPL];
-        bool ok[KPL];
+    const int g = lane >> 4, n = lane & 15;
+    const int r = 4 * wv + g;
+    const bool live = r < rows;
+    unsigned key[KPG];
 #pragma unroll
-        for (int s = 0; s < KPL; ++s) {
-            int p = s * 64 + lane;
-            ok[s] = p < M;
-            key[s] = ok[s] ? order_key(sc[r * M + p]) : 0u;
+    for (int s = 0; s < KPG; ++s) {
+        const int c = BS * s + n;
+        // invalid candidates get key 0, below every finite score's key
+        key[s] = (live && c < M) ? order_key(sc[r * M + c]) : 0u;
+    }
+    // per-row threshold search, stopped per row as soon as exactly K keys
+    // are >= T (see select_rows)
+    unsigned T = 0;
+    bool done = !live;
+    for (int bit = 31; bit >= 0; --bit) {
+        const unsigned t = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int s = 0; s < KPG; ++s) cnt += key[s] >= t ? 1 : 0;
+        cnt = row16_sum(cnt);
+        if (!done && cnt >= K) {
+            T = t;
+            done = cnt == K;
         }
-        // largest T with #(key >= T) >= K: the K-th largest key
-        unsigned T = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            unsigned t = T | (1u << bit);
-            int cnt = 0;
+        if (__all(done)) break;
+    }
+    int gt = 0;
 #pragma unroll
-            for (int s = 0; s < KPL; ++s) cnt += __popcll(__ballot(ok[s] && key[s] >= t));
-            if (cnt >= K) T = t;
-        }
-        int gt = 0;
+    for (int s = 0; s < KPG; ++s) gt += key[s] > T ? 1 : 0;
+    const int need = K - row16_sum(gt);  // ties at T: lowest candidate positions win
+    const unsigned below = (1u << n) - 1u;
+    const int sh = 16 * (g & 1);
+    int eq_before = 0, out_before = 0;
+    int* orow = out + (long)r * K;
 #pragma unroll
-        for (int s = 0; s < KPL; ++s) gt += __popcll(__ballot(ok[s] && key[s] > T));
-        int need = K - gt;  // ties at T: lowest candidate positions win
-        int eq_before = 0, out_before = 0;
-        int* orow = idx + ((long)gh * n_l + row0 + r) * K;
-#pragma unroll
-        for (int s = 0; s < KPL; ++s) {
-            bool eq = ok[s] && key[s] == T;
-            unsigned long long beq = __ballot(eq);
-            bool take = (ok[s] && key[s] > T) || (eq && eq_before + __popcll(beq & below) < need);
-            unsigned long long bt = __ballot(take);
-            if (take) orow[out_before + __popcll(bt & below)] = cand[s * 64 + lane];
-            eq_before += __popcll(beq);
-            out_before += __popcll(bt);
-        }
+    for (int s = 0; s < KPG; ++s) {
+        const bool eq = live && key[s] == T;
+        const unsigned long long beq = __ballot(eq);
+        const unsigned meq = ((unsigned)(g < 2 ? beq : beq >> 32) >> sh) & 0xFFFFu;
+        const bool take = (live && key[s] > T) || (eq && eq_before + __popc(meq & below) < need);
+        const unsigned long long bt = __ballot(take);
+        const unsigned mt = ((unsigned)(g < 2 ? bt : bt >> 32) >> sh) & 0xFFFFu;
+        if (take) orow[out_before + __popc(mt & below)] = cand[BS * s + n];
+        eq_before += __popc(meq);
+        out_before += __popc(mt);
     }
 }
 
-template <int KPL>
-hipError_t launch_level(const float* qbar, const float* kbar, const int* parent, int* idx, int G,
-                  int n_l, int K, float scale, hipStream_t st)
+// Scores on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): 16 query rows x
+// 16 candidates per tile; lane (g = lane/16, n = lane%16) feeds row n and
+// candidate n over channels 16g .. 16g+15, one channel per MFMA k-slot, so
+// every lane reads whole 64-byte pieces of the rows.  The channel sum order is
+// fixed by the instruction sequence.  Used for candidate lists of up to 1024.
+template <int KPG>
+__global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qbar,
+                                                   const float* __restrict__ kbar,
+                                                   const int* __restrict__ parent,
+                                                   int* __restrict__ idx, int n_l, int K, int M,
+                                                   float scale)
 {
-    int M = parent ? BS * K : n_l;
-    // coarsest level: few rows per workgroup, so that the dense n_L x n_L
-    // scoring spreads over many CUs
-    int R = parent ? BS : max(1, min(min(16, n_l / 64), 8192 / M));
-    int groups = parent ? n_l / BS : (n_l + R - 1) / R;
+    extern __shared__ float smem[];
+    float* sc = smem;                 // [16][M]
+    int* cand = (int*)(sc + BS * M);  // [M]
+    const int groups_per_head = (n_l + BS - 1) / BS;
+    const int gh = blockIdx.x / groups_per_head;
+    const int grp = blockIdx.x % groups_per_head;
+    const int row0 = grp * BS;
+    const int rows = min(BS, n_l - row0);
+    for (int c = threadIdx.x; c < M; c += blockDim.x) {
+        if (parent) {
+            const int* pr = parent + ((long)gh * (n_l / BS) + grp) * K;
+            cand[c] = BS * pr[c / BS] + (c % BS);
+        } else {
+            cand[c] = c;
+        }
+    }
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    float qa[16];
+    {
+        const float4* qr = (const float4*)(qbar + ((long)gh * n_l + row0 + min(n, rows - 1)) * D + 16 * g);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float4 v = qr[t];
+            qa[4 * t] = v.x; qa[4 * t + 1] = v.y; qa[4 * t + 2] = v.z; qa[4 * t + 3] = v.w;
+        }
+    }
+    __syncthreads();
+    const int tiles = (M + BS - 1) / BS;
+    const float* kh = kbar + (long)gh * n_l * D + 16 * g;
+    auto load_tile = [&](float (&kb)[16], int tile) {
+        const int c = cand[min(tile * BS + n, M - 1)];
+        const float4* kr = (const float4*)(kh + (long)c * D);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float4 v = kr[t];
+            kb[4 * t] = v.x; kb[4 * t + 1] = v.y; kb[4 * t + 2] = v.z; kb[4 * t + 3] = v.w;
+        }
+    };
+    float kb[16], kn[16];
+    load_tile(kb, min(wv, tiles - 1));
+    for (int tile = wv; tile < tiles; tile += 4) {
+        load_tile(kn, min(tile + 4, tiles - 1));
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[k], kb[k], acc, 0, 0, 0);
+        const int col = tile * BS + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (4 * g + r < rows && col < M) sc[(4 * g + r) * M + col] = acc[r] * scale + 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) kb[k] = kn[k];
+    }
+    __syncthreads();
+    select_rows16<KPG>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K);
+}
+
+template <int KPG>
+hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, int* idx, int G,
+                       int n_l, int K, int M, float scale, hipStream_t st)
+{
+    const int groups = (n_l + BS - 1) / BS;
+    const size_t lds = (size_t)BS * M * sizeof(float) + (size_t)M * sizeof(int);
+    if (lds > 65536) {  // 16 rows x 1024 candidates
+        hipError_t e = hipFuncSetAttribute((const void*)select_mfma<KPG>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(select_mfma<KPG>, dim3(G * groups), dim3(256), lds, st, qbar, kbar, parent,
+                       idx, n_l, K, M, scale);
+    return hipGetLastError();
+}
+
+// Coarsest level with more than 1024 blocks: few rows per workgroup, so that
+// the dense n_L x n_L scoring spreads over many CUs.
+template <int KPL>
+hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, int G, int n_l, int K,
+                       float scale, hipStream_t st)
+{
+    const int M = n_l;
+    int R = max(1, min(min(16, n_l / 64), 8192 / M));
+    int groups = (n_l + R - 1) / R;
     size_t lds = (size_t)(R * D + R * M) * sizeof(float) + (size_t)M * sizeof(int);
-    if (lds > 65536) {  // 16 sibling rows x 1024 candidates (topk = 64)
+    if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)select_kernel<KPL>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(select_kernel<KPL>, dim3(G * groups), dim3(256), lds, st, qbar, kbar,
-                       parent, idx, n_l, K, R, M, scale);
+                       nullptr, idx, n_l, K, R, M, scale);
     return hipGetLastError();
 }
 
@@ -161,12 +331,20 @@ hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
 {
     for (int l = g.L; l >= 1; --l) {
         const int* parent = (l == g.L) ? nullptr : w.idx[l];
-        int M = parent ? BS * g.K : g.n[l];
-        auto f = M <= 64 ? launch_level<1> : M <= 128 ? launch_level<2> : M <= 256 ? launch_level<4>
-               : M <= 512 ? launch_level<8> : M <= 1024 ? launch_level<16>
-               : M <= 2048 ? launch_level<32> : launch_level<64>;
-        hipError_t e = f(w.qbar[l - 1], w.kbar[l - 1], parent, w.idx[l - 1], g.G, g.n[l], g.K,
-                         g.scale, st);
+        const int M = parent ? BS * g.K : g.n[l];
+        const float* qb = w.qbar[l - 1];
+        const float* kb = w.kbar[l - 1];
+        int* out = w.idx[l - 1];
+        hipError_t e;
+        if (M <= 1024) {
+            auto f = M <= 16 ? launch_mfma<1> : M <= 32 ? launch_mfma<2> : M <= 64 ? launch_mfma<4>
+                   : M <= 128 ? launch_mfma<8> : M <= 256 ? launch_mfma<16>
+                   : M <= 512 ? launch_mfma<32> : launch_mfma<64>;
+            e = f(qb, kb, parent, out, g.G, g.n[l], g.K, M, g.scale, st);
+        } else {
+            auto f = M <= 2048 ? launch_wide<32> : launch_wide<64>;
+            e = f(qb, kb, out, g.G, g.n[l], g.K, g.scale, st);
+        }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
