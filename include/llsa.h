@@ -133,8 +133,11 @@ int llsa_backward(const void* q, const void* k, const void* v, const void* out,
 /* Stages of llsa_forward / llsa_backward, for per-kernel timing and tests.
  * llsa_forward == parts POOL, SELECT, ATTN in that order; llsa_backward ==
  * parts TRANSPOSE, DQ, ENRICH, DKDV in that order (ENRICH: gradients of the
- * pooled tokens, needed by DKDV).  Same arguments and errors as the full
- * calls; an unknown part number gives LLSA_ERR_UNSUPPORTED. */
+ * pooled tokens, needed by DKDV).  Each part expects the ones before it to
+ * have run on the same workspace since the last POOL: SELECT adds its picks
+ * to per-block counts that POOL clears and TRANSPOSE consumes.  Same
+ * arguments and errors as the full calls; an unknown part number gives
+ * LLSA_ERR_UNSUPPORTED. */
 #define LLSA_PART_POOL 0
 #define LLSA_PART_SELECT 1
 #define LLSA_PART_ATTN 2

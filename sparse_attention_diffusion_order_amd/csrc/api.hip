@@ -37,7 +37,7 @@ int validate(int B, int H, int N, int d, int block_size, int topk, int levels, i
 
 struct Layout {
     llsa_ws_layout pub;
-    size_t kb16, vb16, pe1;
+    size_t kb16, vb16, pe1, cnt;
     size_t slot[MAX_L];
     size_t part[MAX_L];
     size_t dbar[MAX_L];
@@ -76,6 +76,9 @@ void make_layout(int G, int N, int K, int L, Layout* lay)
     lay->pub.delta = take((size_t)G * N * sizeof(float));
     lay->pe1 = take((size_t)G * n[1] * K * 2 * BS * sizeof(float));
     for (int l = 1; l <= L; ++l) lay->slot[l - 1] = take((size_t)G * n[l] * K);
+    size_t blocks = 0;
+    for (int l = 1; l <= L; ++l) blocks += (size_t)G * n[l];
+    lay->cnt = take(blocks * sizeof(int));
     for (int l = 1; l <= L; ++l) {
         lay->dbar[l - 1] = take((size_t)G * n[l] * 2 * D * sizeof(float));
         if (l >= 2) lay->part[l - 1] = take((size_t)G * n[2] * K * 2 * D * sizeof(float));
@@ -113,6 +116,7 @@ void make_ws(void* base, const Layout& lay, int L, Ws* w)
     }
     w->delta = (float*)(b + lay.pub.delta);
     w->pe1 = (float*)(b + lay.pe1);
+    w->cnt_all = (int*)(b + lay.cnt);
     w->kb16 = (unsigned short*)(b + lay.kb16);
     w->vb16 = (unsigned short*)(b + lay.vb16);
 }
@@ -133,11 +137,15 @@ int prepare(int B, int H, int N, int d, int block_size, int topk, int levels, in
     if (!workspace || ws_bytes < lay.pub.total) return LLSA_ERR_WORKSPACE;
     make_geo(B, H, N, topk, levels, flags, &p->geo);
     make_ws(workspace, lay, levels, &p->ws);
+    // per-level block rows: the bf16 pyramid copies and the choice counts
+    // use the same level-by-level offsets
     long r = 0;
     for (int l = 1; l <= levels; ++l) {
         p->ws.prow[l - 1] = r;
+        p->ws.cnt[l - 1] = p->ws.cnt_all + r;
         r += (long)p->geo.G * p->geo.n[l];
     }
+    p->ws.cnt_len = r;
     p->st = (hipStream_t)stream;
     return LLSA_OK;
 }

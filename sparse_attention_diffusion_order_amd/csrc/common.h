@@ -41,6 +41,10 @@ struct Ws {
     int* rowptr[MAX_L];
     int* col[MAX_L];
     unsigned char* slot[MAX_L];  // position of j in idx_l[col[e]] for each CSR entry e
+    int* cnt[MAX_L];         // [G][n_l]: how many query blocks chose key block j (filled
+                             // by select, cleared by pool); feeds the transpose
+    int* cnt_all;            // all levels' cnt arrays, contiguous
+    long cnt_len;            // their total length
     unsigned short* kb16;    // bf16 copies of kbar / vbar, all levels in one array:
     unsigned short* vb16;    //   row (prow[l] + gh * n_l + j) holds level l, head gh, block j
     long prow[MAX_L];        // first row of each level in kb16 / vb16

@@ -20,7 +20,8 @@
 // keys (order-preserving integer images of the scores) for a threshold that
 // admits exactly the K winners, ballots for ties at the K-th key (lowest
 // candidate position first) and a ballot prefix count to write the winners
-// in ascending order.
+// in ascending order.  Every pick also increments the count of its key block
+// (integer atomics: exact, order-free), which the sparse transpose uses.
 #include "common.h"
 
 namespace llsa {
@@ -36,7 +37,7 @@ __device__ __forceinline__ unsigned order_key(float f)
 // out[r * K ..]; one wave per row at a time.
 template <int KPL>
 __device__ __forceinline__ void select_rows(const float* sc, const int* cand, int* out, int rows,
-                                            int M, int K)
+                                            int M, int K, int* cnt)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const unsigned long long below = (1ull << lane) - 1ull;
@@ -76,7 +77,11 @@ __device__ __forceinline__ void select_rows(const float* sc, const int* cand, in
             unsigned long long beq = __ballot(eq);
             bool take = (ok[s] && key[s] > T) || (eq && eq_before + __popcll(beq & below) < need);
             unsigned long long bt = __ballot(take);
-            if (take) orow[out_before + __popcll(bt & below)] = cand[s * 64 + lane];
+            if (take) {
+                const int j = cand[s * 64 + lane];
+                orow[out_before + __popcll(bt & below)] = j;
+                atomicAdd(cnt + j, 1);
+            }
             eq_before += __popcll(beq);
             out_before += __popcll(bt);
         }
@@ -87,7 +92,8 @@ template <int KPL>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ qbar,
                                                      const float* __restrict__ kbar,
                                                      const int* __restrict__ parent,
-                                                     int* __restrict__ idx, int n_l, int K,
+                                                     int* __restrict__ idx,
+                                                     int* __restrict__ cnt, int n_l, int K,
                                                      int R, int M, float scale)
 {
     extern __shared__ float smem[];
@@ -148,7 +154,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
     }
     __syncthreads();
 
-    select_rows<KPL>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K);
+    select_rows<KPL>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K,
+                     cnt + (long)gh * n_l);
 }
 
 // Sum of x over the 16 lanes of each DPP row (every lane gets its row's sum).
@@ -168,7 +175,7 @@ __device__ __forceinline__ int row16_sum(int x)
 // and the four rows of a wave advance together.
 template <int KPG>
 __device__ __forceinline__ void select_rows16(const float* sc, const int* cand, int* out,
-                                              int rows, int M, int K)
+                                              int rows, int M, int K, int* cnt)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
@@ -213,7 +220,11 @@ __device__ __forceinline__ void select_rows16(const float* sc, const int* cand, 
         const bool take = (live && key[s] > T) || (eq && eq_before + __popc(meq & below) < need);
         const unsigned long long bt = __ballot(take);
         const unsigned mt = ((unsigned)(g < 2 ? bt : bt >> 32) >> sh) & 0xFFFFu;
-        if (take) orow[out_before + __popc(mt & below)] = cand[BS * s + n];
+        if (take) {
+            const int j = cand[BS * s + n];
+            orow[out_before + __popc(mt & below)] = j;
+            atomicAdd(cnt + j, 1);
+        }
         eq_before += __popc(meq);
         out_before += __popc(mt);
     }
@@ -228,7 +239,8 @@ template <int KPG>
 __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qbar,
                                                    const float* __restrict__ kbar,
                                                    const int* __restrict__ parent,
-                                                   int* __restrict__ idx, int n_l, int K, int M,
+                                                   int* __restrict__ idx,
+                                                   int* __restrict__ cnt, int n_l, int K, int M,
                                                    float scale)
 {
     extern __shared__ float smem[];
@@ -286,12 +298,13 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
         for (int k = 0; k < 16; ++k) kb[k] = kn[k];
     }
     __syncthreads();
-    select_rows16<KPG>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K);
+    select_rows16<KPG>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K,
+                       cnt + (long)gh * n_l);
 }
 
 template <int KPG>
-hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, int* idx, int G,
-                       int n_l, int K, int M, float scale, hipStream_t st)
+hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, int* idx,
+                       int* cnt, int G, int n_l, int K, int M, float scale, hipStream_t st)
 {
     const int groups = (n_l + BS - 1) / BS;
     const size_t lds = (size_t)BS * M * sizeof(float) + (size_t)M * sizeof(int);
@@ -301,15 +314,15 @@ hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, 
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(select_mfma<KPG>, dim3(G * groups), dim3(256), lds, st, qbar, kbar, parent,
-                       idx, n_l, K, M, scale);
+                       idx, cnt, n_l, K, M, scale);
     return hipGetLastError();
 }
 
 // Coarsest level with more than 1024 blocks: few rows per workgroup, so that
 // the dense n_L x n_L scoring spreads over many CUs.
 template <int KPL>
-hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, int G, int n_l, int K,
-                       float scale, hipStream_t st)
+hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, int* cnt, int G, int n_l,
+                       int K, float scale, hipStream_t st)
 {
     const int M = n_l;
     int R = max(1, min(min(16, n_l / 64), 8192 / M));
@@ -321,7 +334,7 @@ hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, int G, in
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(select_kernel<KPL>, dim3(G * groups), dim3(256), lds, st, qbar, kbar,
-                       nullptr, idx, n_l, K, R, M, scale);
+                       nullptr, idx, cnt, n_l, K, R, M, scale);
     return hipGetLastError();
 }
 
@@ -340,10 +353,10 @@ hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
             auto f = M <= 16 ? launch_mfma<1> : M <= 32 ? launch_mfma<2> : M <= 64 ? launch_mfma<4>
                    : M <= 128 ? launch_mfma<8> : M <= 256 ? launch_mfma<16>
                    : M <= 512 ? launch_mfma<32> : launch_mfma<64>;
-            e = f(qb, kb, parent, out, g.G, g.n[l], g.K, M, g.scale, st);
+            e = f(qb, kb, parent, out, w.cnt[l - 1], g.G, g.n[l], g.K, M, g.scale, st);
         } else {
             auto f = M <= 2048 ? launch_wide<32> : launch_wide<64>;
-            e = f(qb, kb, out, g.G, g.n[l], g.K, g.scale, st);
+            e = f(qb, kb, out, w.cnt[l - 1], g.G, g.n[l], g.K, g.scale, st);
         }
         if (e != hipSuccess) return e;
     }

@@ -4,15 +4,17 @@
 // key block, the query blocks that selected it; the pages obtain these lists
 // directly from the sparse index lists instead of from a dense mask.
 //
-// Levels are transposed coarsest first, each by count -> prefix scan -> fill
-// into CSR form (rowptr [G][n_l+1], col [G][n_l*K], every list ascending).
-// The count and fill kernels gather instead of scatter: one workgroup owns 16
-// sibling key blocks 16p .. 16p+15 and walks the only query blocks that can
-// have chosen them -- at a finer level, the children of the query blocks in
-// the parent level's list of block p (hierarchical selection only offers
-// children of chosen parents); at the coarsest level, all query blocks.  The
-// candidates are walked in ascending order and ballots give each hit its rank,
-// so lists come out sorted and identical run to run, with no atomics.
+// A counting sort into CSR form (rowptr [G][n_l+1], col [G][n_l*K], every
+// list ascending), one launch per level, coarsest first.  The counts come
+// from the selection pass; the prefix over them is summed by each workgroup
+// for its own bins; the fill gathers instead of scattering: one workgroup
+// owns 16 sibling key blocks 16p .. 16p+15 and walks the only query blocks
+// that can have chosen them -- at a finer level, the children of the query
+// blocks in the parent level's list of block p (hierarchical selection only
+// offers children of chosen parents); at the coarsest level, all query
+// blocks.  The candidates are walked in ascending order and ballots give each
+// hit its rank, so lists come out sorted and identical run to run, with no
+// atomics.
 #include "common.h"
 
 namespace llsa {
@@ -71,27 +73,58 @@ __device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp, int* 
     return m;
 }
 
-// One workgroup (4 waves) per 16 sibling key blocks; one candidate query
-// block per thread.  FILL == false: rowptr[j + 1] = |T_l[j]|.  FILL == true:
-// col lists (and, for the pooled-token gradients, the position of j in each
-// listed query block's index list).  Ranks: ballot within a wave, counts of
-// lower waves through LDS, counts of earlier rounds carried in registers.
-template <bool FILL>
-__global__ __launch_bounds__(256) void transpose_pass(Geo g, Ws w, int l)
+// One workgroup (4 waves) per 16 sibling key blocks 16p .. 16p+15; one
+// candidate query block per thread.  The selection pass counted how often
+// each key block was chosen (cnt); the workgroup sums the counts of all key
+// blocks before its own to get its first CSR position (a few thousand ints
+// at most, read from L2), writes rowptr for its blocks, and fills their
+// lists.  Ranks: ballot within a wave, counts of lower waves through LDS,
+// counts of earlier rounds carried in registers.  Besides col it records, for
+// the pooled-token gradients and dk/dv, the position of j in each listed
+// query block's index list.
+__global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
 {
     __shared__ int wcnt[4][16];
+    __shared__ int wsum[4];
+    __shared__ int start[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int groups = (g.n[l] + 15) / 16;
+    const int n = g.n[l];
+    const int groups = (n + 15) / 16;
     const int gh = blockIdx.x / groups, grp = blockIdx.x % groups;
-    const int* I = w.idx[l - 1] + (long)gh * g.n[l] * g.K;
-    int* rowptr = w.rowptr[l - 1] + (long)gh * (g.n[l] + 1);
-    int* col = w.col[l - 1] + (long)gh * g.n[l] * g.K;
-    unsigned char* slots = w.slot[l - 1] + (long)gh * g.n[l] * g.K;
+    const int* I = w.idx[l - 1] + (long)gh * n * g.K;
+    const int* cnt = w.cnt[l - 1] + (long)gh * n;
+    int* rowptr = w.rowptr[l - 1] + (long)gh * (n + 1);
+    int* col = w.col[l - 1] + (long)gh * n * g.K;
+    unsigned char* slots = w.slot[l - 1] + (long)gh * n * g.K;
+
+    // first position of this group: sum of the counts of blocks 0 .. 16 grp - 1
+    int acc = 0;
+    for (int b = tid; b < 16 * grp; b += blockDim.x) acc += cnt[b];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) wsum[wv] = acc;
+    __syncthreads();
+    if (tid < 16) {
+        const int base = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        const int j = 16 * grp + tid;
+        const int c = j < n ? cnt[j] : 0;
+        int x = c;  // inclusive scan over the 16 bins
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int y = __shfl_up(x, o, 16);
+            if (tid >= o) x += y;
+        }
+        start[tid] = base + x - c;
+        if (j < n) rowptr[j] = base + x - c;
+        if (j == n - 1) rowptr[n] = base + x;
+    }
+    __syncthreads();
+
     const Cands cs = make_cands(g, w, l, gh, grp);
     const unsigned long long below = (1ull << lane) - 1ull;
     int run[16];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) run[b] = FILL ? rowptr[min(16 * grp + b, g.n[l])] : 0;
+    for (int b = 0; b < 16; ++b) run[b] = start[b];
     for (int c0 = 0; c0 < cs.n; c0 += 256) {
         const int c = c0 + tid;
         int i = 0, first = 0;
@@ -112,11 +145,11 @@ __global__ __launch_bounds__(256) void transpose_pass(Geo g, Ws w, int l)
             int before = 0, total = 0;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int cnt = wcnt[u][b];
-                before += (u < wv) ? cnt : 0;
-                total += cnt;
+                const int k = wcnt[u][b];
+                before += (u < wv) ? k : 0;
+                total += k;
             }
-            if (FILL && ((m >> b) & 1u)) {
+            if ((m >> b) & 1u) {
                 const int pos = run[b] + before + __popcll(bal[b] & below);
                 col[pos] = i;
                 slots[pos] = (unsigned char)(first + __popc(m & ((1u << b) - 1u)));
@@ -125,56 +158,18 @@ __global__ __launch_bounds__(256) void transpose_pass(Geo g, Ws w, int l)
         }
         __syncthreads();
     }
-    if (!FILL && tid < 16 && 16 * grp + tid < g.n[l]) {
-        int cnt = 0;
-#pragma unroll
-        for (int b = 0; b < 16; ++b) cnt = (b == tid) ? run[b] : cnt;
-        rowptr[16 * grp + tid + 1] = cnt;
-    }
-}
-
-// rowptr[1..n] holds counts; turn it into the exclusive prefix (rowptr[0] = 0).
-__global__ __launch_bounds__(1024) void transpose_scan(Geo g, Ws w, int l)
-{
-    __shared__ int wsum[16];
-    const int n = g.n[l];
-    int* rowptr = w.rowptr[l - 1] + (long)blockIdx.x * (n + 1);
-    const int per = (n + 1023) / 1024;
-    const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
-    int s = 0;
-    for (int j = lo; j < hi; ++j) s += rowptr[j + 1];
-    // inclusive scan of s over the block
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int x = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[wv] = x;
-    __syncthreads();
-    int off = 0;
-    for (int k = 0; k < wv; ++k) off += wsum[k];
-    int run = off + x - s;  // exclusive prefix of this thread's first bin
-    for (int j = lo; j < hi; ++j) {
-        int cnt = rowptr[j + 1];
-        run += cnt;
-        rowptr[j + 1] = run;
-    }
-    if (threadIdx.x == 0) rowptr[0] = 0;
 }
 
 }  // namespace
 
 hipError_t launch_transpose(const Geo& g, const Ws& w, hipStream_t st)
 {
-    // level 1 feeds the key-major dk/dv pass; levels >= 2 feed the enrichment
-    // gradients; finer levels need the coarser lists, so all are built.
+    // level 1 feeds the key-major dk/dv pass; levels >= 2 feed the pooled-
+    // token gradients; finer levels need the coarser lists, so all are built,
+    // coarsest first.
     for (int l = g.L; l >= 1; --l) {
         dim3 grid((unsigned)(g.G * ((g.n[l] + 15) / 16)));
-        hipLaunchKernelGGL(transpose_pass<false>, grid, dim3(256), 0, st, g, w, l);
-        hipLaunchKernelGGL(transpose_scan, dim3(g.G), dim3(1024), 0, st, g, w, l);
-        hipLaunchKernelGGL(transpose_pass<true>, grid, dim3(256), 0, st, g, w, l);
+        hipLaunchKernelGGL(transpose_fill, grid, dim3(256), 0, st, g, w, l);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
