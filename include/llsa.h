@@ -57,7 +57,7 @@ extern "C" {
 #define LLSA_ERR_UNSUPPORTED (-3) /* d != 64, block_size != 16, unknown dtype
                                      or flags, levels > LLSA_MAX_LEVELS,
                                      coarsest block count > 4096, topk > 64,
-                                     or B*H*N >= 2^31 */
+                                     N > 2^23, or B*H*N >= 2^31 */
 #define LLSA_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than
                                      llsa_workspace_bytes() */
 #define LLSA_ERR_HIP (-5)         /* a HIP launch or runtime call failed */
@@ -133,10 +133,10 @@ int llsa_backward(const void* q, const void* k, const void* v, const void* out,
 /* Stages of llsa_forward / llsa_backward, for per-kernel timing and tests.
  * llsa_forward == parts POOL, SELECT, ATTN in that order; llsa_backward ==
  * parts TRANSPOSE, DQ, ENRICH, DKDV in that order (ENRICH: gradients of the
- * pooled tokens, needed by DKDV).  Each part expects the ones before it to
- * have run on the same workspace since the last POOL: SELECT adds its picks
- * to per-block counts that POOL clears and TRANSPOSE consumes.  Same
- * arguments and errors as the full calls; an unknown part number gives
+ * pooled tokens, needed by DKDV).  Each part reads what the parts before it
+ * left in the workspace (SELECT also records how often each key block was
+ * chosen, which TRANSPOSE uses); any part may be repeated.  Same arguments
+ * and errors as the full calls; an unknown part number gives
  * LLSA_ERR_UNSUPPORTED. */
 #define LLSA_PART_POOL 0
 #define LLSA_PART_SELECT 1

@@ -32,6 +32,7 @@ int validate(int B, int H, int N, int d, int block_size, int topk, int levels, i
     if (topk > nL) return LLSA_ERR_SHAPE;
     if (nL > 4096 || topk > 64) return LLSA_ERR_UNSUPPORTED;
     if ((long long)B * H * N >= (1ll << 31)) return LLSA_ERR_UNSUPPORTED;
+    if (N > (1 << 23)) return LLSA_ERR_UNSUPPORTED;  // one head's tensor < 2 GiB (buffer offsets)
     return LLSA_OK;
 }
 

@@ -41,8 +41,8 @@ struct Ws {
     int* rowptr[MAX_L];
     int* col[MAX_L];
     unsigned char* slot[MAX_L];  // position of j in idx_l[col[e]] for each CSR entry e
-    int* cnt[MAX_L];         // [G][n_l]: how many query blocks chose key block j (filled
-                             // by select, cleared by pool); feeds the transpose
+    int* cnt[MAX_L];         // [G][n_l]: how many query blocks chose key block j
+                             // (cleared and filled by select); feeds the transpose
     int* cnt_all;            // all levels' cnt arrays, contiguous
     long cnt_len;            // their total length
     unsigned short* kb16;    // bf16 copies of kbar / vbar, all levels in one array:
@@ -136,6 +136,21 @@ __device__ __forceinline__ float sum_x4(float x)
 
 // Make all LDS writes of this wave visible to its later LDS reads, and keep
 // the compiler from moving memory accesses across this point.
+// Buffer loads: a resource per tensor (or per head) in scalar registers; the
+// per-lane byte offset is loop-invariant and the row offset a scalar, so a
+// gathered 16-row tile costs no vector address arithmetic.  Out-of-range
+// offsets read zeros (hardware range check against num_bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned num_bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 __device__ __forceinline__ void lds_fence()
 {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

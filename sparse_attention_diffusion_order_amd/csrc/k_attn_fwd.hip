@@ -14,7 +14,9 @@
 // The pooled entries of all levels (L*K of them) form extra tiles of 16,
 // read from the bf16 copy of the pyramid that the pool pass writes.
 //
-// bf16 kernel (MFMA): one wave per query block, 4 waves per workgroup.
+// bf16 kernels (MFMA): attn_fwd_u4 (below; K <= 16) gives a wave four
+// sibling query blocks and loads each tile they share once;
+// attn_fwd_bf16 (any K) gives a wave one query block:
 //   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, A = key rows, B = query rows;
 //                    lane (g = lane/16, n = lane%16) holds S^T[4g + r][n]:
 //                    four keys of query n, so softmax statistics of query n
@@ -75,8 +77,10 @@ constexpr float TAU = 8.0f;
 
 struct Online {
     f32x4 acc[4];  // O^T tiles: lane holds O^T[16d + 4(lane/16) + r][query lane%16]
+    f32x4 den;     // softmax denominator of query lane%16 (all four equal): the
+                   // same MFMA as O^T with an all-ones value tile, so it sums
+                   // exactly the bf16 weights that multiply the values
     float m;       // reference max (log2 units), equal in the 4 lanes of a query
-    float lsum;    // this lane's share of the softmax denominator
 };
 
 // One step over two 16-entry tiles whose values are staged in LDS at la / lb.
@@ -98,29 +102,25 @@ __device__ __forceinline__ void attend_pair(Online& st, bf16x8 bq0, bf16x8 bq1, 
         ya[r] = (!MASK || 4 * gq + r < na) ? sa[r] : -INFINITY;
         yb[r] = (!MASK || 4 * gq + r < nb) ? sb[r] : -INFINITY;
     }
-    float mx = fmaxf(fmaxf(fmaxf(ya[0], ya[1]), fmaxf(ya[2], ya[3])),
-                     fmaxf(fmaxf(yb[0], yb[1]), fmaxf(yb[2], yb[3])));
-    mx = max_x4(mx) * c;
-    if (__ballot(mx > st.m + TAU)) {
-        const float mnew = fmaxf(st.m, mx);
+    // this lane's max; the 4-lane reduction is only needed when the
+    // reference max must move (rarely, after the first pair)
+    const float lm = fmaxf(fmaxf(fmaxf(ya[0], ya[1]), fmaxf(ya[2], ya[3])),
+                           fmaxf(fmaxf(yb[0], yb[1]), fmaxf(yb[2], yb[3])));
+    if (__ballot(lm * c > st.m + TAU)) {
+        const float mnew = fmaxf(st.m, max_x4(lm) * c);
         const float alpha = fast_exp2(st.m - mnew);
-        st.lsum *= alpha;
 #pragma unroll
         for (int d = 0; d < 4; ++d) st.acc[d] *= alpha;
+        st.den *= alpha;
         st.m = mnew;
     }
     const float nm = -st.m;
     bf16x8 pp;
-    float ls = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const float pa = fast_exp2(fmaf(ya[r], c, nm));
-        const float pb = fast_exp2(fmaf(yb[r], c, nm));
-        ls += pa + pb;
-        pp[r] = (bf16)pa;
-        pp[4 + r] = (bf16)pb;
+        pp[r] = (bf16)fast_exp2(fmaf(ya[r], c, nm));
+        pp[4 + r] = (bf16)fast_exp2(fmaf(yb[r], c, nm));
     }
-    st.lsum += ls;
     lds_fence();
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -129,6 +129,9 @@ __device__ __forceinline__ void attend_pair(Online& st, bf16x8 bq0, bf16x8 bq1, 
         bf16x8 av = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
         st.acc[d] = mfma32(av, pp, st.acc[d]);
     }
+    const bf16 one = (bf16)1.0f;
+    const bf16x8 ones = {one, one, one, one, one, one, one, one};
+    st.den = mfma32(ones, pp, st.den);
 }
 
 constexpr int MAX_E = MAX_L * 64;  // pooled entries per query block (L * K)
@@ -180,82 +183,101 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
     Online st;
 #pragma unroll
     for (int d = 0; d < 4; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.den = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m = -INFINITY;
-    st.lsum = 0.f;
     unsigned short* la = smem[wv];  // value tiles (transposed reads)
     unsigned short* lb = la + Lay::V_TILE;
     unsigned short* lka = lb + Lay::V_TILE;  // key tiles (operand reads)
     unsigned short* lkb = lka + Lay::K_TILE;
 
-    // One pipeline over all tile pairs: NF pairs of fine tiles, then NP - NF
-    // pairs of pooled tiles.  The next pair's loads are in flight while this
-    // one is computed (two register sets alternate).  Loads are issued
-    // unconditionally -- out-of-range tiles re-read a valid row and are
-    // masked -- so the compiler's wait counts stay exact.
-    const int NF = (g.K + 1) / 2;
-    const int NT = (E + BS - 1) / BS;  // pooled tiles
-    const int NP = NF + (NT + 1) / 2;
+    // Fine tiles first: K/2 full pairs in a loop whose body is one basic
+    // block (prefetch of the next pair, then this pair), so the compiler
+    // keeps every load a full step ahead of its use.  Buffer loads: lane
+    // offset of row vr (row vr + 8 is 1024 bytes on), tile offset j * 2048.
+    // Then the masked tail: a lone fine tile (K = 1) and the pooled tiles.
     const int vr = lane >> 3, vc = (lane & 7) * 8;
-    auto load_pair = [&](FinePair& f, int p) {
-        long ka, kb, ka8, kb8;  // element offsets of rows vr and vr + 8
-        const unsigned short *kp, *vp;
-        if (p < NF) {
-            const int ja = __builtin_amdgcn_readlane(myj, min(2 * p, g.K - 1));
-            const int jb = __builtin_amdgcn_readlane(myj, min(2 * p + 1, g.K - 1));
-            ka = hbase + ((long)ja * BS + vr) * D + vc;
-            kb = hbase + ((long)jb * BS + vr) * D + vc;
-            ka8 = ka + 8 * D;
-            kb8 = kb + 8 * D;
-            kp = k;
-            vp = v;
-        } else {
-            const int t = 2 * (p - NF);
-            ka = (long)ent[min(BS * t + vr, E - 1)] * D + vc;
-            ka8 = (long)ent[min(BS * t + vr + 8, E - 1)] * D + vc;
-            kb = (long)ent[min(BS * t + BS + vr, E - 1)] * D + vc;
-            kb8 = (long)ent[min(BS * t + BS + vr + 8, E - 1)] * D + vc;
-            kp = w.kb16;
-            vp = w.vb16;
-        }
-        f.ka0 = ld_bf16x8(kp + ka);
-        f.ka1 = ld_bf16x8(kp + ka8);
-        f.va0 = ld_bf16x8(vp + ka);
-        f.va1 = ld_bf16x8(vp + ka8);
-        f.kb0 = ld_bf16x8(kp + kb);
-        f.kb1 = ld_bf16x8(kp + kb8);
-        f.vb0 = ld_bf16x8(vp + kb);
-        f.vb1 = ld_bf16x8(vp + kb8);
+    const unsigned head_bytes = (unsigned)g.N * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + hbase, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + hbase, head_bytes);
+    const int voff = (vr * D + vc) * 2;
+    const int NF = g.K / 2;  // full fine pairs
+    auto load_fine = [&](FinePair& f, int p) {
+        const int sa = __builtin_amdgcn_readlane(myj, 2 * p) * (BS * D * 2);
+        const int sb = __builtin_amdgcn_readlane(myj, 2 * p + 1) * (BS * D * 2);
+        f.ka0 = bload8(rk, voff, sa);
+        f.ka1 = bload8(rk, voff + 8 * D * 2, sa);
+        f.va0 = bload8(rv, voff, sa);
+        f.va1 = bload8(rv, voff + 8 * D * 2, sa);
+        f.kb0 = bload8(rk, voff, sb);
+        f.kb1 = bload8(rk, voff + 8 * D * 2, sb);
+        f.vb0 = bload8(rv, voff, sb);
+        f.vb1 = bload8(rv, voff + 8 * D * 2, sb);
     };
-    auto step = [&](const FinePair& f, int p) {
+    auto stage = [&](const FinePair& f, bf16x8& ka0, bf16x8& ka1, bf16x8& kb0, bf16x8& kb1) {
         stage_rows<ROW_A>(lka, f.ka0, f.ka1, lane);
         stage_rows<ROW_A>(lkb, f.kb0, f.kb1, lane);
         stage_rows<LDS_ROW>(la, f.va0, f.va1, lane);
         stage_rows<LDS_ROW>(lb, f.vb0, f.vb1, lane);
         lds_fence();
-        bf16x8 ka0, ka1, kb0, kb1;
         key_operand(lka, ka0, ka1, lane);
         key_operand(lkb, kb0, kb1, lane);
-        if (p < NF && g.K > 1) {
-            attend_pair<false>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, BS, BS, c, lane);
-        } else {
-            const int e0 = p < NF ? 0 : BS * 2 * (p - NF);
-            const int na = p < NF ? BS : max(0, min(BS, E - e0));
-            const int nb = p < NF ? 0 : max(0, min(BS, E - e0 - BS));
-            attend_pair<true>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, na, nb, c, lane);
-        }
+    };
+    auto step_fine = [&](const FinePair& f) {
+        bf16x8 ka0, ka1, kb0, kb1;
+        stage(f, ka0, ka1, kb0, kb1);
+        attend_pair<false>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, BS, BS, c, lane);
     };
     FinePair A, B;
-    load_pair(A, 0);
-    for (int p = 0;; p += 2) {
-        load_pair(B, min(p + 1, NP - 1));
-        step(A, p);
-        if (p + 1 >= NP) break;
-        load_pair(A, min(p + 2, NP - 1));
-        step(B, p + 1);
-        if (p + 2 >= NP) break;
+    if (NF > 0) {
+        load_fine(A, 0);
+        int p = 0;
+        for (; p + 2 <= NF; p += 2) {
+            load_fine(B, p + 1);
+            step_fine(A);
+            load_fine(A, min(p + 2, NF - 1));
+            step_fine(B);
+        }
+        if (p < NF) step_fine(A);  // odd number of pairs: the last one is in A
+    }
+    // masked tail: tile t < NFT is the lone fine tile (K odd), then the
+    // pooled tiles; pairs of tiles, rows read through per-lane pointers
+    const int NFT = g.K & 1;
+    const int NT = NFT + (E + BS - 1) / BS;
+    const int jlast = __builtin_amdgcn_readlane(myj, g.K - 1);
+    auto tail_off = [&](int t, int r) -> long {
+        // element offset of row r (0..15) of tail tile t in k / v (the lone
+        // fine tile) or in the pooled copies; rows past the last entry
+        // repeat a valid one (they are masked)
+        if (t < NFT) return hbase + ((long)jlast * BS + r) * D;
+        return (long)ent[min(BS * (t - NFT) + r, E - 1)] * D;
+    };
+    for (int t = 0; t < NT; t += 2) {
+        const int tb = min(t + 1, NT - 1);
+        const bool fa = t < NFT, fb = tb < NFT;
+        const long oa = tail_off(t, vr), oa8 = tail_off(t, vr + 8);
+        const long ob = tail_off(tb, vr), ob8 = tail_off(tb, vr + 8);
+        const unsigned short* kpa = fa ? k : w.kb16;
+        const unsigned short* vpa = fa ? v : w.vb16;
+        const unsigned short* kpb = fb ? k : w.kb16;
+        const unsigned short* vpb = fb ? v : w.vb16;
+        FinePair f;
+        f.ka0 = ld_bf16x8(kpa + oa + vc);
+        f.ka1 = ld_bf16x8(kpa + oa8 + vc);
+        f.va0 = ld_bf16x8(vpa + oa + vc);
+        f.va1 = ld_bf16x8(vpa + oa8 + vc);
+        f.kb0 = ld_bf16x8(kpb + ob + vc);
+        f.kb1 = ld_bf16x8(kpb + ob8 + vc);
+        f.vb0 = ld_bf16x8(vpb + ob + vc);
+        f.vb1 = ld_bf16x8(vpb + ob8 + vc);
+        bf16x8 ka0, ka1, kb0, kb1;
+        stage(f, ka0, ka1, kb0, kb1);
+        // valid entries of the two tiles
+        const int na = t < NFT ? BS : max(0, min(BS, E - BS * (t - NFT)));
+        const int nb = t + 1 >= NT ? 0 : (t + 1 < NFT ? BS : max(0, min(BS, E - BS * (t + 1 - NFT))));
+        attend_pair<true>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, na, nb, c, lane);
     }
 
-    const float lsum = sum_x4(st.lsum);
+    const float lsum = st.den[0];
     const float inv = 1.0f / lsum;
     const long obase = qbase + nq * D + 4 * gq;
 #pragma unroll
@@ -266,6 +288,246 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
         *(u16x4*)(out + obase + 16 * d) = o;
     }
     if (gq == 0) lse[(long)gh * g.N + (long)i * BS + nq] = (st.m + fast_log2(lsum)) * LN2;
+}
+
+// --------------------------------------------- four sibling blocks per wave
+//
+// attn_fwd_u4 (K <= 16): a wave owns four consecutive query blocks.  They
+// are siblings (the same parent at every coarser level), so their fine picks
+// overlap: the wave forms the ascending union of the 4 K picks (about 37 of
+// 64 at 256x256, K = 16), loads every union tile once and applies it to each
+// of its blocks that picked it.  The vector-memory traffic per unit of work
+// drops by that overlap, and the four blocks' independent softmax chains
+// give the wave more to issue while MFMA results are pending.  One 16-key
+// tile per step: S^T = K Q^T (16x16x32 MFMA over the channels), then
+// O^T += V^T P^T and the denominator with 16x16x16 MFMAs over the 16 keys.
+// Pooled tiles follow: one level-1 tile per block (its picks' pooled rows),
+// one tile per coarser level shared by all four (same ancestor).
+
+struct Tile {
+    bf16x8 k0, k1, v0, v1;  // rows vr and vr+8, channels vc .. vc+7
+};
+
+struct Q4 {
+    f32x4 acc[4];
+    f32x4 den;
+    float m;
+};
+
+template <bool MASK>
+__device__ __forceinline__ void tile_step(Q4& st, bf16x8 bq0, bf16x8 bq1, bf16x8 ka0, bf16x8 ka1,
+                                          const bf16x4 (&vt)[4], int na, float c, int lane)
+{
+    const int gq = lane >> 4;
+    const f32x4 zero = {};
+    const f32x4 sa = mfma32(ka1, bq1, mfma32(ka0, bq0, zero));
+    float y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = (!MASK || 4 * gq + r < na) ? sa[r] : -INFINITY;
+    const float lm = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+    if (__ballot(lm * c > st.m + TAU)) {
+        const float mnew = fmaxf(st.m, max_x4(lm) * c);
+        const float alpha = fast_exp2(st.m - mnew);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) st.acc[d] *= alpha;
+        st.den *= alpha;
+        st.m = mnew;
+    }
+    const float nm = -st.m;
+    bf16x4 pp;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pp[r] = (bf16)fast_exp2(fmaf(y[r], c, nm));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) st.acc[d] = mfma16(vt[d], pp, st.acc[d]);
+    const bf16 one = (bf16)1.0f;
+    const bf16x4 ones = {one, one, one, one};
+    st.den = mfma16(ones, pp, st.den);
+}
+
+constexpr int U4_PT = 4 + MAX_L - 1;  // pooled tiles per wave (4 level-1 + one per coarser level)
+
+struct U4Lds {
+    unsigned short k[BS * ROW_A];
+    unsigned short v[BS * LDS_ROW];
+    int arr[64];                  // the 4 x 16 picks (lane order), INT_MAX if unused
+    int first[64];                // pick value if it is the first occurrence, else INT_MAX
+    int tab[64];                  // union tile j
+    int tmask[64];                // which of the 4 blocks picked it
+    int pent[U4_PT * BS];         // pooled tile rows (row index into kb16 / vb16)
+};
+
+__global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restrict__ q,
+                                                   const unsigned short* __restrict__ k,
+                                                   const unsigned short* __restrict__ v,
+                                                   unsigned short* __restrict__ out,
+                                                   float* __restrict__ lse, Geo g, Ws w)
+{
+    __shared__ __attribute__((aligned(16))) U4Lds sm[4];
+    const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
+    const int gq = lane >> 4, nq = lane & 15;
+    const int rr = (lane & 15) >> 2, xx = lane & 3;
+    const long qb0 = ((long)xcd_block(blockIdx.x, gridDim.x) * 4 + wv) * 4;  // over G * n1
+    if (qb0 >= (long)g.G * g.n[1]) return;
+    const int gh = (int)(qb0 / g.n[1]), i0 = (int)(qb0 % g.n[1]);
+    U4Lds& L = sm[wv];
+    const float c = g.scale * LOG2E;
+    const long hbase = (long)gh * g.N * D;
+    const int K = g.K;
+    const int E = (g.flags & LLSA_NO_ENRICH) ? 0 : g.L * K;
+
+    // query operands of the four blocks
+    bf16x8 bq0[4], bq1[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const long qb = hbase + ((long)(i0 + b) * BS + nq) * D + 8 * gq;
+        bq0[b] = ld_bf16x8(q + qb);
+        bq1[b] = ld_bf16x8(q + qb + 32);
+    }
+    // the 4 pick lists, lane 16 b + s holds pick s of block i0 + b
+    const int* sel = w.idx[0] + ((long)gh * g.n[1] + i0) * K;
+    const int my = (nq < K) ? sel[gq * K + nq] : INT_MAX;
+    L.arr[lane] = my;
+    lds_fence();
+    // union: first occurrences in lane order, their rank among distinct picks,
+    // and the set of blocks that share each pick
+    int dup = 0, mask = 0;
+    for (int m = 0; m < 64; m += 4) {
+        const int4 a4 = *(const int4*)&L.arr[m];
+        const int av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bool eq = av[t] == my;
+            dup |= (eq && m + t < lane) ? 1 : 0;
+            mask |= eq ? 1 << ((m + t) >> 4) : 0;
+        }
+    }
+    const bool first = my != INT_MAX && !dup;
+    L.first[lane] = first ? my : INT_MAX;
+    lds_fence();
+    int upos = 0;
+    for (int m = 0; m < 64; m += 4) {
+        const int4 f4 = *(const int4*)&L.first[m];
+        upos += (f4.x < my) + (f4.y < my) + (f4.z < my) + (f4.w < my);
+    }
+    const int U = __popcll(__ballot(first));
+    if (first) {
+        L.tab[upos] = my;
+        L.tmask[upos] = mask;
+    }
+    // pooled tile rows: tile b < 4 = level-1 pooled rows of block i0 + b's
+    // picks; tile 4 + (l - 2) = level-l pooled rows of the common ancestor
+    const int NPT = E ? 4 + (g.L - 1) : 0;
+    if (E) {
+        for (int t = 0; t < NPT; ++t) {
+            if (lane < BS) {
+                const int r = min(lane, K - 1);
+                int row;
+                if (t < 4) {
+                    row = (int)(w.prow[0] + (long)gh * g.n[1] + L.arr[t * 16 + r]);
+                } else {
+                    const int l = t - 2;
+                    const long a = (long)gh * g.n[l] + (i0 >> (4 * (l - 1)));
+                    row = (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * K + r]);
+                }
+                L.pent[t * BS + lane] = row;
+            }
+        }
+    }
+    lds_fence();
+    const int tj = L.tab[lane], tm = L.tmask[lane];
+
+    Q4 st[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) st[b].acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st[b].den = f32x4{0.f, 0.f, 0.f, 0.f};
+        st[b].m = -INFINITY;
+    }
+
+    const int vr = lane >> 3, vc = (lane & 7) * 8;
+    const unsigned head_bytes = (unsigned)g.N * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + hbase, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + hbase, head_bytes);
+    const int voff = (vr * D + vc) * 2;
+    auto load_union = [&](Tile& T, int u) {
+        const int so = __builtin_amdgcn_readlane(tj, u) * (BS * D * 2);
+        T.k0 = bload8(rk, voff, so);
+        T.k1 = bload8(rk, voff + 8 * D * 2, so);
+        T.v0 = bload8(rv, voff, so);
+        T.v1 = bload8(rv, voff + 8 * D * 2, so);
+    };
+    auto load_pooled = [&](Tile& T, int t) {
+        const long ra = (long)L.pent[t * BS + vr] * D + vc;
+        const long rb = (long)L.pent[t * BS + vr + 8] * D + vc;
+        T.k0 = ld_bf16x8(w.kb16 + ra);
+        T.k1 = ld_bf16x8(w.kb16 + rb);
+        T.v0 = ld_bf16x8(w.vb16 + ra);
+        T.v1 = ld_bf16x8(w.vb16 + rb);
+    };
+    // stage a tile, then run it for the blocks in `members`
+    auto run = [&](const Tile& T, int members, int na, auto masked) {
+        stage_rows<ROW_A>(L.k, T.k0, T.k1, lane);
+        stage_rows<LDS_ROW>(L.v, T.v0, T.v1, lane);
+        lds_fence();
+        bf16x8 ka0, ka1;
+        key_operand(L.k, ka0, ka1, lane);
+        bf16x4 vt[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            vt[d] = lds_read_tr(L.v + (4 * gq + rr) * LDS_ROW + 16 * d + 4 * xx);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if ((members >> b) & 1) {
+                if (masked)
+                    tile_step<true>(st[b], bq0[b], bq1[b], ka0, ka1, vt, na, c, lane);
+                else
+                    tile_step<false>(st[b], bq0[b], bq1[b], ka0, ka1, vt, BS, c, lane);
+            }
+    };
+    // union tiles, the next one in flight; the loop body has no conditional
+    // exit between a load and its use.  A load past the end re-reads the
+    // last tile (valid memory) and is not used.
+    Tile A, B;
+    if (U > 0) {
+        load_union(A, 0);
+        int u = 0;
+        for (; u + 2 <= U; u += 2) {
+            load_union(B, u + 1);
+            run(A, __builtin_amdgcn_readlane(tm, u), BS, false);
+            load_union(A, min(u + 2, U - 1));
+            run(B, __builtin_amdgcn_readlane(tm, u + 1), BS, false);
+        }
+        if (u < U) run(A, __builtin_amdgcn_readlane(tm, u), BS, false);
+    }
+    if (NPT > 0) {
+        const bool part = K < BS;
+        load_pooled(A, 0);
+        int t = 0;
+        for (; t + 2 <= NPT; t += 2) {
+            load_pooled(B, t + 1);
+            run(A, t < 4 ? 1 << t : 0xF, K, part);
+            load_pooled(A, min(t + 2, NPT - 1));
+            run(B, t + 1 < 4 ? 1 << (t + 1) : 0xF, K, part);
+        }
+        if (t < NPT) run(A, t < 4 ? 1 << t : 0xF, K, part);
+    }
+
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const float lsum = st[b].den[0];
+        const float inv = 1.0f / lsum;
+        const long obase = hbase + ((long)(i0 + b) * BS + nq) * D + 4 * gq;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            u16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = f2bf(st[b].acc[d][r] * inv);
+            *(u16x4*)(out + obase + 16 * d) = o;
+        }
+        if (gq == 0)
+            lse[(long)gh * g.N + (long)(i0 + b) * BS + nq] = (st[b].m + fast_log2(lsum)) * LN2;
+    }
 }
 
 // ------------------------------------------------------------ fp32 path
@@ -331,10 +593,16 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* ou
 {
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
-        auto kern = (g.L * g.K <= 64) ? attn_fwd_bf16<64> : attn_fwd_bf16<MAX_E>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
-                           (const unsigned short*)q, (const unsigned short*)k,
-                           (const unsigned short*)v, (unsigned short*)out, lse, g, w);
+        if (g.K <= BS && g.n[1] % 4 == 0) {
+            hipLaunchKernelGGL(attn_fwd_u4, dim3((unsigned)((nblk + 15) / 16)), dim3(256), 0, st,
+                               (const unsigned short*)q, (const unsigned short*)k,
+                               (const unsigned short*)v, (unsigned short*)out, lse, g, w);
+        } else {
+            auto kern = (g.L * g.K <= 64) ? attn_fwd_bf16<64> : attn_fwd_bf16<MAX_E>;
+            hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
+                               (const unsigned short*)q, (const unsigned short*)k,
+                               (const unsigned short*)v, (unsigned short*)out, lse, g, w);
+        }
     } else {
         long ntok = (long)g.G * g.N;
         hipLaunchKernelGGL(attn_fwd_f32, dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, st,

@@ -11,8 +11,7 @@
 // by 16 adjacent lanes.  Level 2 (one block per workgroup) is the mean of the
 // 16 level-1 means, formed in LDS.  pool_up forms levels >= 3 from level l-1.
 // The pooled keys and values are also stored rounded to bf16 (the operands
-// the attention kernels feed to the MFMA).  pool_l12 also clears the choice
-// counts that the selection pass then accumulates.
+// the attention kernels feed to the MFMA).
 #include "common.h"
 
 namespace llsa {
@@ -45,10 +44,6 @@ __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T
                                                 const T* __restrict__ v, Geo g, Ws w)
 {
     __shared__ float m1[16][D];
-    // clear the per-level choice counts that the selection pass accumulates
-    for (long t = ((long)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-         t < w.cnt_len; t += (long)gridDim.x * gridDim.y * blockDim.x)
-        w.cnt_all[t] = 0;
     const int tensor = blockIdx.y;
     const T* x = tensor == 0 ? q : tensor == 1 ? k : v;
     float* lv1 = tensor == 0 ? w.qbar[0] : tensor == 1 ? w.kbar[0] : w.vbar[0];

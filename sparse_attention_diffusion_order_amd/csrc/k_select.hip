@@ -27,6 +27,15 @@
 namespace llsa {
 namespace {
 
+// Zero the choice counts of every level (the selection launches that follow
+// on the same stream add to them), so each selection pass counts afresh.
+__global__ __launch_bounds__(256) void clear_counts(int* __restrict__ cnt, long n)
+{
+    for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < n;
+         t += (long)gridDim.x * blockDim.x)
+        cnt[t] = 0;
+}
+
 __device__ __forceinline__ unsigned order_key(float f)
 {
     unsigned u = __float_as_uint(f);
@@ -342,6 +351,8 @@ hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, int* cnt,
 
 hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
 {
+    const unsigned cgrid = (unsigned)min((w.cnt_len + 255) / 256, 1024L);
+    hipLaunchKernelGGL(clear_counts, dim3(cgrid), dim3(256), 0, st, w.cnt_all, w.cnt_len);
     for (int l = g.L; l >= 1; --l) {
         const int* parent = (l == g.L) ? nullptr : w.idx[l];
         const int M = parent ? BS * g.K : g.n[l];

@@ -149,8 +149,11 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
                 before += (u < wv) ? k : 0;
                 total += k;
             }
-            if ((m >> b) & 1u) {
-                const int pos = run[b] + before + __popcll(bal[b] & below);
+            const int pos = run[b] + before + __popcll(bal[b] & below);
+            // pos < n K whenever the counts match the index lists (both come
+            // from the same selection pass); the test only keeps a workspace
+            // that was not filled by one from being written out of bounds
+            if (((m >> b) & 1u) && pos < n * g.K) {
                 col[pos] = i;
                 slots[pos] = (unsigned char)(first + __popc(m & ((1u << b) - 1u)));
             }

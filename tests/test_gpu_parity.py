@@ -12,7 +12,7 @@ import pytest
 import oracle
 import synth
 from llsa_check import (BS, TOL, assert_close, check_selection, check_transpose, gpu_run,
-                        oracle_inputs)
+                        oracle_inputs, to_device, ws_array)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +135,41 @@ def test_runs_are_bit_identical():
     for l in range(w.levels):
         np.testing.assert_array_equal(a["idx"][l], b["idx"][l])
         np.testing.assert_array_equal(a["col"][l], b["col"][l])
+
+
+def test_repeated_parts_keep_the_transpose_exact():
+    """Stages may be re-run on the same workspace (here: selection three times,
+    transpose twice): the key->query lists stay the exact transpose of the
+    index lists and the gradients do not change."""
+    import torch
+    import sparse_attention_diffusion_order_amd as lib
+    w = small("rep", 1, 2, 64, "bf16", 2, 4)
+    inp = synth.make_inputs(w)
+    a = gpu_run(w, inp)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    ws = a["ws"]
+    do = to_device(inp["do"], w.dtype)
+    dq, dk, dv = (torch.empty_like(a["q"]) for _ in range(3))
+    args = (B, H, N, d, BS, w.topk, w.levels, lib.BF16, 0, ws, ws.numel())
+    for _ in range(3):
+        lib.llsa_forward_part(lib.PART_SELECT, a["q"], a["k"], a["v"], a["out_t"], a["lse_t"], *args)
+    for _ in range(2):
+        lib.llsa_backward_part(lib.PART_TRANSPOSE, a["q"], a["k"], a["v"], a["out_t"], a["lse_t"],
+                               do, dq, dk, dv, *args)
+    for part in (lib.PART_DQ, lib.PART_ENRICH, lib.PART_DKDV):
+        lib.llsa_backward_part(part, a["q"], a["k"], a["v"], a["out_t"], a["lse_t"], do, dq, dk, dv,
+                               *args)
+    torch.cuda.synchronize()
+    G = B * H
+    for l in range(w.levels):
+        n = N // BS ** (l + 1)
+        rp = ws_array(ws, a["lay"]["rowptr"][l], G * (n + 1), np.int32).reshape(G, n + 1)
+        col = ws_array(ws, a["lay"]["col"][l], G * n * w.topk, np.int32).reshape(G, n * w.topk)
+        want_rp, want_col = oracle.transpose(a["idx"][l])
+        np.testing.assert_array_equal(rp, want_rp)
+        np.testing.assert_array_equal(col, want_col)
+    for got, ref in ((dq, a["dq_t"]), (dk, a["dk_t"]), (dv, a["dv_t"])):
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
 
 
 # ------------------------------------------------------- full-size workloads
