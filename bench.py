@@ -7,9 +7,10 @@ forward (pool pyramid, hierarchical Top-K, sparse attention with enrichment)
 and the backward (index transpose, dQ, pooled-token gradients, dK/dV), all
 through the C ABI of libllsa.so on one stream.  Prints ONE JSON line.
 
-The per-stage times come from HIP events recorded on the library's stream
-between the stage calls inside the timed region; the roofline object is
-computed for the stage kernel that takes the longest.
+The headline times K whole steps between two HIP events on the library's
+stream.  A second pass of K steps records an event after every stage for the
+per-stage times; the roofline object is computed from it for the stage kernel
+that takes the longest.
 """
 from __future__ import annotations
 
@@ -311,26 +312,42 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    def timed(body):
+        """ms per call of body over K calls, one start and one end event"""
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for _ in range(args.steps):
+            body()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / args.steps
+
+    def run_list(names):
+        for name in names:
+            run_stage(name)
+
+    # headline: K whole steps
+    ms_per_step = timed(step)
+    # the forward (llsa_forward's parts) and forward + backward, same protocol
+    fwd_ms = timed(lambda: run_list(["pool", "select", "attn_fwd"]))
+    fwdbwd_ms = timed(lambda: run_list(stages[1:]))
+
+    # breakdown: K more steps with an event after every stage (each record
+    # adds a few microseconds between stages, so these are not summed into
+    # the headline); each stage's time is that of its kernel launches
     all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
                for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record(stream)
     for s in range(args.steps):
         all_evs[s][0].record(stream)
         step(all_evs[s])
-    t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
     stage_ms = {name: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in all_evs]))
                 for i, name in enumerate(stages)}
 
     f = flops(w)
-    fwd_ms = stage_ms["pool"] + stage_ms["select"] + stage_ms["attn_fwd"]
-    bwd_ms = stage_ms["transpose"] + stage_ms["dq"] + stage_ms["enrich"] + stage_ms["dkdv"]
-    fwdbwd_ms = fwd_ms + bwd_ms
     value = f["fwdbwd"] / (ms_per_step * 1e-3) / 1e12
 
     # roofline of the longest single-kernel stage (attention fwd, dq or dkdv)

@@ -255,11 +255,14 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
     extern __shared__ float smem[];
     float* sc = smem;                 // [16][M]
     int* cand = (int*)(sc + BS * M);  // [M]
-    const int groups_per_head = (n_l + BS - 1) / BS;
+    // R rows per workgroup: the 16 siblings of a parent (they share their
+    // candidates), or 4 rows of the coarsest level (more workgroups)
+    const int R = parent ? BS : 4;
+    const int groups_per_head = (n_l + R - 1) / R;
     const int gh = blockIdx.x / groups_per_head;
     const int grp = blockIdx.x % groups_per_head;
-    const int row0 = grp * BS;
-    const int rows = min(BS, n_l - row0);
+    const int row0 = grp * R;
+    const int rows = min(R, n_l - row0);
     for (int c = threadIdx.x; c < M; c += blockDim.x) {
         if (parent) {
             const int* pr = parent + ((long)gh * (n_l / BS) + grp) * K;
@@ -315,7 +318,7 @@ template <int KPG>
 hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, int* idx,
                        int* cnt, int G, int n_l, int K, int M, float scale, hipStream_t st)
 {
-    const int groups = (n_l + BS - 1) / BS;
+    const int groups = (n_l + (parent ? BS : 4) - 1) / (parent ? BS : 4);
     const size_t lds = (size_t)BS * M * sizeof(float) + (size_t)M * sizeof(int);
     if (lds > 65536) {  // 16 rows x 1024 candidates
         hipError_t e = hipFuncSetAttribute((const void*)select_mfma<KPG>,

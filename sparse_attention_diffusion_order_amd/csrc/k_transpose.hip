@@ -97,6 +97,23 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
     int* col = w.col[l - 1] + (long)gh * n * g.K;
     unsigned char* slots = w.slot[l - 1] + (long)gh * n * g.K;
 
+    // the candidate walk (parent list -> candidate rows -> their picks) and
+    // the prefix over earlier bins are independent: both go out before the
+    // first barrier
+    const Cands cs = make_cands(g, w, l, gh, grp);
+    int ci = 0, cfirst = 0;
+    unsigned cm = 0;
+    auto probe = [&](int c0) {
+        const int c = c0 + tid;
+        ci = 0;
+        cfirst = 0;
+        cm = 0;
+        if (c < cs.n) {
+            ci = cs.row(c);
+            cm = hit_mask(I + (long)ci * g.K, g.K, grp, &cfirst);
+        }
+    };
+    probe(0);
     // first position of this group: sum of the counts of blocks 0 .. 16 grp - 1
     int acc = 0;
     for (int b = tid; b < 16 * grp; b += blockDim.x) acc += cnt[b];
@@ -120,19 +137,13 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
     }
     __syncthreads();
 
-    const Cands cs = make_cands(g, w, l, gh, grp);
     const unsigned long long below = (1ull << lane) - 1ull;
     int run[16];
 #pragma unroll
     for (int b = 0; b < 16; ++b) run[b] = start[b];
     for (int c0 = 0; c0 < cs.n; c0 += 256) {
-        const int c = c0 + tid;
-        int i = 0, first = 0;
-        unsigned m = 0;
-        if (c < cs.n) {
-            i = cs.row(c);
-            m = hit_mask(I + (long)i * g.K, g.K, grp, &first);
-        }
+        const int i = ci, first = cfirst;
+        const unsigned m = cm;
         unsigned long long bal[16];
 #pragma unroll
         for (int b = 0; b < 16; ++b) {
@@ -159,6 +170,7 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
             }
             run[b] += total;
         }
+        probe(c0 + 256);
         __syncthreads();
     }
 }
