@@ -151,6 +151,15 @@ __device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, int voff, int
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+__device__ __forceinline__ float bloadf(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+// A per-lane buffer offset that is out of range for any resource here: the
+// load returns 0 (used to switch a lane's load off without a branch).
+constexpr int OFF_NONE = 0x7ffffff0;
+
 __device__ __forceinline__ void lds_fence()
 {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

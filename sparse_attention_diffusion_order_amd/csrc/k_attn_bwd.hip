@@ -448,24 +448,6 @@ struct QBlock {
                             // and dS (48..63) of row lane % 16
 };
 
-// One dword per lane carries all per-row scalars of the block (a single
-// 256-byte load instead of four replicated 16-byte-per-lane loads).
-__device__ __forceinline__ void load_qblock(QBlock& f, const unsigned short* q,
-                                            const unsigned short* dout, const float* lse,
-                                            const float* delta, const float* pe, long hbase,
-                                            long tbase, int i, int lane)
-{
-    const int sr = lane >> 3, sc = (lane & 7) * 8;
-    const long a = hbase + ((long)i * BS + sr) * D + sc;
-    f.q0 = ld8(q + a);
-    f.q1 = ld8(q + a + 8 * D);
-    f.d0 = ld8(dout + a);
-    f.d1 = ld8(dout + a + 8 * D);
-    const long t = tbase + (long)i * BS + (lane & 15);
-    const float* src = lane < 16 ? lse + t : lane < 32 ? delta + t : pe + (lane - 32);
-    f.x = *src;
-}
-
 __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict__ q,
                                                 const unsigned short* __restrict__ k,
                                                 const unsigned short* __restrict__ v,
@@ -537,11 +519,33 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     // the list is read 64 entries at a time, one per lane, and each step takes
     // its query block and slot with readlane, so no load waits on another
     int myi = 0, mys = 0;
+    // buffer loads: rows sr and sr + 8 of block i at lane offset voff (+1024),
+    // block offset i * 2048 bytes; one dword per lane carries the block's
+    // per-row scalars (lse, delta, pooled P and dS), each lane reading from
+    // one of three resources -- the other two give 0 for an out-of-range
+    // offset -- so there is no divergent branch
+    const unsigned head_bytes = (unsigned)g.N * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + hbase, head_bytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + hbase, head_bytes);
+    const __amdgpu_buffer_rsrc_t rlse = make_rsrc(lse + tbase, (unsigned)g.N * 4);
+    const __amdgpu_buffer_rsrc_t rdel = make_rsrc(w.delta + tbase, (unsigned)g.N * 4);
+    const int sr = lane >> 3, sc = (lane & 7) * 8;
+    const int voff = (sr * D + sc) * 2;
+    const int off_lse = lane < 16 ? 4 * lane : OFF_NONE;
+    const int off_del = (lane >= 16 && lane < 32) ? 4 * (lane - 16) : OFF_NONE;
+    const int off_pe = lane >= 32 ? 4 * (lane - 32) : OFF_NONE;
     auto fetch = [&](QBlock& f, int t) {
         const int i = __builtin_amdgcn_readlane(myi, t);
         const int sl = __builtin_amdgcn_readlane(mys, t);
-        const float* pe = w.pe1 + (((long)gh * g.n[1] + i) * g.K + sl) * 2 * BS;
-        load_qblock(f, q, dout, lse, w.delta, pe, hbase, tbase, i, lane);
+        const int so = i * (BS * D * 2);
+        f.q0 = bload8(rq, voff, so);
+        f.q1 = bload8(rq, voff + 8 * D * 2, so);
+        f.d0 = bload8(rdo, voff, so);
+        f.d1 = bload8(rdo, voff + 8 * D * 2, so);
+        const __amdgpu_buffer_rsrc_t rpe =
+            make_rsrc(w.pe1 + (((long)gh * g.n[1] + i) * g.K + sl) * 2 * BS, 2 * BS * 4);
+        f.x = bloadf(rlse, off_lse, i * BS * 4) + bloadf(rdel, off_del, i * BS * 4) +
+              bloadf(rpe, off_pe, 0);
     };
     // two register sets alternate, each filled one step before it is used.
     // The loop body is one basic block: a conditional exit between a fetch
