@@ -80,9 +80,11 @@ def sha_of_sources():
 
 PMC_SUMMARY = "pmc_fetch_write_llsa_kernels_%s.json"
 TRACE_SUMMARY = "kernel_trace_llsa_kernels_%s.md"
-KERNEL_OF_STAGE = {"zorder": "zorder_kernel", "pool": "pool_l12", "select": "select_kernel",
-                   "attn_fwd": "attn_fwd_bf16", "transpose": "transpose_pass",
-                   "dq": "dq_bf16", "enrich": "enrich_bwd_bf16", "dkdv": "dkdv_bf16"}
+KERNEL_OF_STAGE = {"zorder": ("zorder_kernel",), "pool": ("pool_l12",),
+                   "select": ("select_mfma", "select_kernel"),
+                   "attn_fwd": ("attn_fwd_u4", "attn_fwd_bf16"),
+                   "transpose": ("transpose_fill",), "dq": ("dq_bf16",),
+                   "enrich": ("enrich_bwd_bf16",), "dkdv": ("dkdv_bf16",)}
 
 
 def load_traffic(stage, w):
@@ -98,10 +100,10 @@ def load_traffic(stage, w):
         return None
     if rec.get("sources_sha") != sha_of_sources():
         return None
-    want = KERNEL_OF_STAGE.get(stage, stage)
-    for name, k in rec.get("kernels", {}).items():
-        if name.split("<")[0] == want:
-            return k.get("hbm_bytes_per_launch")
+    for want in KERNEL_OF_STAGE.get(stage, (stage,)):
+        for name, k in rec.get("kernels", {}).items():
+            if name.split("<")[0] == want:
+                return k.get("hbm_bytes_per_launch")
     return None
 
 
@@ -382,6 +384,10 @@ def main():
         "stage_gbs": {k_: round(abytes[k_] / (stage_ms[k_] * 1e-3) / 1e9, 1)
                       for k_ in abytes if k_ in stage_ms},
         "gflop": {k_: round(v_ / 1e9, 3) for k_, v_ in f.items() if k_ != "n_kv"},
+        # measured HBM bytes per launch (committed rocprofv3 FETCH_SIZE +
+        # WRITE_SIZE summary of the current kernel sources), where available
+        "stage_hbm_mb": {k_: round(t_ / 1e6, 1) for k_, t_ in
+                         ((k_, load_traffic(k_, w)) for k_ in stages) if t_ is not None},
         "roofline": roofline,
     }
 

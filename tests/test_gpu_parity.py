@@ -63,6 +63,18 @@ def test_small_workloads(w):
     _full_check(w)
 
 
+@pytest.mark.parametrize("w", [
+    # topk = 64 at a 1024-block coarsest level: the selection's score tile
+    # needs more than 64 KiB of LDS; the attention uses the one-block kernels
+    small("grid128_bf16_l1_k64", 1, 1, 128, "bf16", 1, 64),
+    # a 4096-block coarsest level: the dense selection with few rows per
+    # workgroup
+    small("grid256_bf16_l1_k16", 1, 1, 256, "bf16", 1, 16),
+], ids=lambda w: w.name)
+def test_large_candidate_lists(w):
+    _full_check(w)
+
+
 @pytest.mark.parametrize("w", [SMALL[0], SMALL[4]], ids=lambda w: w.name)
 def test_no_enrichment(w):
     _full_check(w, flags=oracle.NO_ENRICH)
