@@ -78,7 +78,8 @@ void make_layout(int G, int N, int K, int L, Layout* lay)
     lay->pe1 = take((size_t)G * n[1] * K * 2 * BS * sizeof(float));
     for (int l = 1; l <= L; ++l) lay->slot[l - 1] = take((size_t)G * n[l] * K);
     size_t blocks = 0;
-    for (int l = 1; l <= L; ++l) blocks += (size_t)G * n[l];
+    for (int l = 1; l <= L; ++l)
+        blocks += (size_t)G * (n[l] + (n[l] + 15) / 16);
     lay->cnt = take(blocks * sizeof(int));
     for (int l = 1; l <= L; ++l) {
         lay->dbar[l - 1] = take((size_t)G * n[l] * 2 * D * sizeof(float));
@@ -138,15 +139,20 @@ int prepare(int B, int H, int N, int d, int block_size, int topk, int levels, in
     if (!workspace || ws_bytes < lay.pub.total) return LLSA_ERR_WORKSPACE;
     make_geo(B, H, N, topk, levels, flags, &p->geo);
     make_ws(workspace, lay, levels, &p->ws);
-    // per-level block rows: the bf16 pyramid copies and the choice counts
-    // use the same level-by-level offsets
-    long r = 0;
+    // per-level block rows of the bf16 pyramid copies; the choice counts
+    // (per block and per 16 blocks) of every level
+    long r = 0, c = 0;
+    const long G = p->geo.G;
     for (int l = 1; l <= levels; ++l) {
+        const long nl = p->geo.n[l];
         p->ws.prow[l - 1] = r;
-        p->ws.cnt[l - 1] = p->ws.cnt_all + r;
-        r += (long)p->geo.G * p->geo.n[l];
+        r += G * nl;
+        p->ws.cnt[l - 1] = p->ws.cnt_all + c;
+        c += G * nl;
+        p->ws.c16[l - 1] = p->ws.cnt_all + c;
+        c += G * ((nl + 15) / 16);
     }
-    p->ws.cnt_len = r;
+    p->ws.cnt_len = c;
     p->st = (hipStream_t)stream;
     return LLSA_OK;
 }

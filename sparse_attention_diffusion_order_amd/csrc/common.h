@@ -43,6 +43,7 @@ struct Ws {
     unsigned char* slot[MAX_L];  // position of j in idx_l[col[e]] for each CSR entry e
     int* cnt[MAX_L];         // [G][n_l]: how many query blocks chose key block j
                              // (cleared and filled by select); feeds the transpose
+    int* c16[MAX_L];         // [G][ceil(n_l/16)]: the same summed over 16 blocks
     int* cnt_all;            // all levels' cnt arrays, contiguous
     long cnt_len;            // their total length
     unsigned short* kb16;    // bf16 copies of kbar / vbar, all levels in one array:
@@ -159,6 +160,25 @@ __device__ __forceinline__ float bloadf(__amdgpu_buffer_rsrc_t r, int voff, int 
 // A per-lane buffer offset that is out of range for any resource here: the
 // load returns 0 (used to switch a lane's load off without a branch).
 constexpr int OFF_NONE = 0x7ffffff0;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave: DPP sums within each 16-lane row, the
+// four rows through permlane swaps, and lane 0's total broadcast so that
+// every lane holds the identical value.
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += dpp_f<0xB1>(x);   // quad_perm 1,0,3,2
+    x += dpp_f<0x4E>(x);   // quad_perm 2,3,0,1
+    x += dpp_f<0x124>(x);  // row_ror 4
+    x += dpp_f<0x128>(x);  // row_ror 8
+    x = sum_x4(x);
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
 
 __device__ __forceinline__ void lds_fence()
 {

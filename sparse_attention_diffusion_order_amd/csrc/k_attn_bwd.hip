@@ -27,7 +27,8 @@
 //               in T_1[j]; it averages the block's 16 keys, so its P/16 and
 //               dS/16 (stored by the dq pass) are added to every key column.
 //               The epilogue adds the pooled-level gradients of levels >= 2.
-// fp32 path: plain VALU kernels with explicit pooled tokens at every level.
+// fp32 path: plain VALU kernels, one wave per row (lane = channel), with
+// explicit pooled tokens at every level.
 // No floating-point atomics anywhere: results are bit-identical run to run.
 #include "common.h"
 
@@ -596,6 +597,8 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
 
 // ------------------------------------------------------------ fp32 path
 
+// One wave per row, lane = channel: every dot product is a wave sum.
+
 template <typename F>
 __device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const float* k,
                                                const float* v, int gh, int t, F f)
@@ -617,6 +620,7 @@ __device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const 
         }
 }
 
+// dq and delta: one wave per query token
 __global__ __launch_bounds__(256) void dq_f32(const float* __restrict__ q,
                                               const float* __restrict__ k,
                                               const float* __restrict__ v,
@@ -625,72 +629,61 @@ __global__ __launch_bounds__(256) void dq_f32(const float* __restrict__ q,
                                               const float* __restrict__ dout,
                                               float* __restrict__ dq, Geo g, Ws w)
 {
-    const long tg = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long tg = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (tg >= (long)g.G * g.N) return;
+    const int lane = threadIdx.x & 63;
     const int gh = (int)(tg / g.N), t = (int)(tg % g.N);
-    const float* qr = q + tg * D;
-    const float* dr = dout + tg * D;
-    float Dt = 0.f;
-    for (int c = 0; c < D; ++c) Dt = fmaf(dr[c], o[tg * D + c], Dt);
-    w.delta[tg] = Dt;
+    const float qc = q[tg * D + lane], dc = dout[tg * D + lane];
+    const float Dt = wave_sum(dc * o[tg * D + lane]);
+    if (lane == 0) w.delta[tg] = Dt;
     const float lt = lse[tg];
-    float acc[D];
-#pragma unroll
-    for (int c = 0; c < D; ++c) acc[c] = 0.f;
+    float acc = 0.f;
     for_each_entry(g, w, k, v, gh, t, [&](const float* kr, const float* vr) {
-        float z = 0.f, dp = 0.f;
-        for (int c = 0; c < D; ++c) {
-            z = fmaf(qr[c], kr[c], z);
-            dp = fmaf(dr[c], vr[c], dp);
-        }
+        const float kc = kr[lane];
+        const float z = wave_sum(qc * kc);
+        const float dp = wave_sum(dc * vr[lane]);
         const float P = expf(z * g.scale - lt);
         const float ds = P * (dp - Dt) * g.scale;
-#pragma unroll
-        for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, kr[c], acc[c]);
+        acc = fmaf(ds, kc, acc);
     });
-#pragma unroll
-    for (int c = 0; c < D; ++c) dq[tg * D + c] = acc[c];
+    dq[tg * D + lane] = acc;
 }
 
-// pooled-token gradients, every level: thread per (level block, channel)
+// pooled-token gradients, every level: one wave per level-l block
 __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
                                                   const float* __restrict__ lse,
                                                   const float* __restrict__ dout, Geo g, Ws w,
                                                   int l)
 {
-    const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (id >= (long)g.G * g.n[l] * D) return;
-    const int dim = (int)(id % D);
-    const long blk = id / D;
+    const long blk = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    if (blk >= (long)g.G * g.n[l]) return;
+    const int lane = threadIdx.x & 63;
     const int gh = (int)(blk / g.n[l]), j = (int)(blk % g.n[l]);
-    const float* kb = w.kbar[l - 1] + blk * D;
-    const float* vb = w.vbar[l - 1] + blk * D;
+    const float kb = w.kbar[l - 1][blk * D + lane];
+    const float vb = w.vbar[l - 1][blk * D + lane];
     const int* rp = w.rowptr[l - 1] + (long)gh * (g.n[l] + 1);
     const int* cl = w.col[l - 1] + (long)gh * g.n[l] * g.K;
-    const int span = 1 << (4 * l);
+    const long span = 1l << (4 * l);
     float sk = 0.f, sv = 0.f;
     for (int e = rp[j]; e < rp[j + 1]; ++e) {
-        const int a = cl[e];
-        for (long t = (long)a * span; t < (long)(a + 1) * span; ++t) {
+        const long a = cl[e];
+        for (long t = a * span; t < (a + 1) * span; ++t) {
             const long tg = (long)gh * g.N + t;
-            const float* qr = q + tg * D;
-            const float* dr = dout + tg * D;
-            float z = 0.f, dp = 0.f;
-            for (int c = 0; c < D; ++c) {
-                z = fmaf(qr[c], kb[c], z);
-                dp = fmaf(dr[c], vb[c], dp);
-            }
+            const float qc = q[tg * D + lane], dc = dout[tg * D + lane];
+            const float z = wave_sum(qc * kb);
+            const float dp = wave_sum(dc * vb);
             const float P = expf(z * g.scale - lse[tg]);
             const float ds = P * (dp - w.delta[tg]);
-            sk = fmaf(ds * g.scale, qr[dim], sk);
-            sv = fmaf(P, dr[dim], sv);
+            sk = fmaf(ds * g.scale, qc, sk);
+            sv = fmaf(P, dc, sv);
         }
     }
     float* dst = w.dbar[l - 1] + blk * 2 * D;
-    dst[dim] = sk;
-    dst[D + dim] = sv;
+    dst[lane] = sk;
+    dst[D + lane] = sv;
 }
 
+// dk, dv: one wave per key token
 __global__ __launch_bounds__(256) void dkdv_f32(const float* __restrict__ q,
                                                 const float* __restrict__ k,
                                                 const float* __restrict__ v,
@@ -699,49 +692,34 @@ __global__ __launch_bounds__(256) void dkdv_f32(const float* __restrict__ q,
                                                 float* __restrict__ dk, float* __restrict__ dv,
                                                 Geo g, Ws w)
 {
-    const long xg = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long xg = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (xg >= (long)g.G * g.N) return;
+    const int lane = threadIdx.x & 63;
     const int gh = (int)(xg / g.N), x = (int)(xg % g.N), j = x / BS;
-    const float* kr = k + xg * D;
-    const float* vr = v + xg * D;
-    float ak[D], av[D];
-#pragma unroll
-    for (int c = 0; c < D; ++c) ak[c] = av[c] = 0.f;
+    const float kc = k[xg * D + lane], vc = v[xg * D + lane];
+    float ak = 0.f, av = 0.f;
     const int* rp = w.rowptr[0] + (long)gh * (g.n[1] + 1);
     const int* cl = w.col[0] + (long)gh * g.n[1] * g.K;
     for (int e = rp[j]; e < rp[j + 1]; ++e)
         for (int r = 0; r < BS; ++r) {
             const long tg = (long)gh * g.N + (long)cl[e] * BS + r;
-            const float* qr = q + tg * D;
-            const float* dr = dout + tg * D;
-            float z = 0.f, dp = 0.f;
-            for (int c = 0; c < D; ++c) {
-                z = fmaf(qr[c], kr[c], z);
-                dp = fmaf(dr[c], vr[c], dp);
-            }
+            const float qc = q[tg * D + lane], dc = dout[tg * D + lane];
+            const float z = wave_sum(qc * kc);
+            const float dp = wave_sum(dc * vc);
             const float P = expf(z * g.scale - lse[tg]);
             const float ds = P * (dp - w.delta[tg]) * g.scale;
-#pragma unroll
-            for (int c = 0; c < D; ++c) {
-                ak[c] = fmaf(ds, qr[c], ak[c]);
-                av[c] = fmaf(P, dr[c], av[c]);
-            }
+            ak = fmaf(ds, qc, ak);
+            av = fmaf(P, dc, av);
         }
     if (!(g.flags & LLSA_NO_ENRICH))
         for (int l = 1; l <= g.L; ++l) {
             const float wgt = 1.0f / (float)(1 << (4 * l));
             const float* db = w.dbar[l - 1] + ((long)gh * g.n[l] + (x >> (4 * l))) * 2 * D;
-#pragma unroll
-            for (int c = 0; c < D; ++c) {
-                ak[c] += db[c] * wgt;
-                av[c] += db[D + c] * wgt;
-            }
+            ak += db[lane] * wgt;
+            av += db[D + lane] * wgt;
         }
-#pragma unroll
-    for (int c = 0; c < D; ++c) {
-        dk[xg * D + c] = ak[c];
-        dv[xg * D + c] = av[c];
-    }
+    dk[xg * D + lane] = ak;
+    dv[xg * D + lane] = av;
 }
 
 }  // namespace
@@ -758,8 +736,8 @@ hipError_t launch_attn_dq(const void* q, const void* k, const void* v, const voi
                            (const unsigned short*)v, (const unsigned short*)out, lse,
                            (const unsigned short*)dout, (unsigned short*)dq, g, w);
     } else {
-        long ntok = (long)g.G * g.N;
-        hipLaunchKernelGGL(dq_f32, dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, st,
+        long ntok = (long)g.G * g.N;  // one wave each
+        hipLaunchKernelGGL(dq_f32, dim3((unsigned)((ntok + 3) / 4)), dim3(256), 0, st,
                            (const float*)q, (const float*)k, (const float*)v, (const float*)out,
                            lse, (const float*)dout, (float*)dq, g, w);
     }
@@ -787,8 +765,8 @@ hipError_t launch_attn_enrich(const void* q, const float* lse, const void* dout,
     }
     hipError_t e = hipSuccess;
     for (int l = 1; l <= g.L && e == hipSuccess; ++l) {
-        long n = (long)g.G * g.n[l] * D;
-        hipLaunchKernelGGL(enrich_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+        long n = (long)g.G * g.n[l];  // one wave per pooled block
+        hipLaunchKernelGGL(enrich_f32, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st,
                            (const float*)q, lse, (const float*)dout, g, w, l);
         e = hipGetLastError();
     }
@@ -806,8 +784,8 @@ hipError_t launch_attn_dkdv(const void* q, const void* k, const void* v, const f
                            (const unsigned short*)v, lse, (const unsigned short*)dout,
                            (unsigned short*)dk, (unsigned short*)dv, g, w);
     } else {
-        long ntok = (long)g.G * g.N;
-        hipLaunchKernelGGL(dkdv_f32, dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, st,
+        long ntok = (long)g.G * g.N;  // one wave per key token
+        hipLaunchKernelGGL(dkdv_f32, dim3((unsigned)((ntok + 3) / 4)), dim3(256), 0, st,
                            (const float*)q, (const float*)k, (const float*)v, lse,
                            (const float*)dout, (float*)dk, (float*)dv, g, w);
     }

@@ -25,7 +25,8 @@
 //                    staged row-major, read back transposed), B = P^T taken
 //                    straight from the S^T accumulator layout: two 16-key
 //                    tiles form the 32-deep contraction.
-// fp32 kernel (VALU): one thread per query token, explicit pooled tokens.
+// fp32 kernel (VALU): one wave per query token (lane = channel), explicit
+// pooled tokens.
 #include "common.h"
 
 namespace llsa {
@@ -532,43 +533,35 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
 
 // ------------------------------------------------------------ fp32 path
 
+// one wave per query token, lane = channel: every logit is a wave sum
 __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
                                                     const float* __restrict__ k,
                                                     const float* __restrict__ v,
                                                     float* __restrict__ out,
                                                     float* __restrict__ lse, Geo g, Ws w)
 {
-    const long tg = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long tg = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (tg >= (long)g.G * g.N) return;
+    const int lane = threadIdx.x & 63;
     const int gh = (int)(tg / g.N), t = (int)(tg % g.N);
-    float qr[D], o[D];
-#pragma unroll
-    for (int c = 0; c < D; ++c) {
-        qr[c] = q[tg * D + c];
-        o[c] = 0.f;
-    }
-    float m = -INFINITY, l = 0.f;
+    const float qc = q[tg * D + lane];
+    float m = -INFINITY, l = 0.f, o = 0.f;
     auto visit = [&](const float* kr, const float* vr) {
-        float z = 0.f;
-#pragma unroll
-        for (int c = 0; c < D; ++c) z = fmaf(qr[c], kr[c], z);
-        z *= g.scale;
+        const float z = wave_sum(qc * kr[lane]) * g.scale;
         if (z > m) {
-            float a = expf(m - z);
+            const float a = expf(m - z);
             l *= a;
-#pragma unroll
-            for (int c = 0; c < D; ++c) o[c] *= a;
+            o *= a;
             m = z;
         }
-        float p = expf(z - m);
+        const float p = expf(z - m);
         l += p;
-#pragma unroll
-        for (int c = 0; c < D; ++c) o[c] = fmaf(p, vr[c], o[c]);
+        o = fmaf(p, vr[lane], o);
     };
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + t / BS) * g.K;
     for (int s = 0; s < g.K; ++s)
         for (int r = 0; r < BS; ++r) {
-            long row = ((long)gh * g.N + (long)sel[s] * BS + r) * D;
+            const long row = ((long)gh * g.N + (long)sel[s] * BS + r) * D;
             visit(k + row, v + row);
         }
     if (!(g.flags & LLSA_NO_ENRICH))
@@ -576,14 +569,12 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
             const int a = t >> (4 * lv);
             const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.K;
             for (int s = 0; s < g.K; ++s) {
-                long row = ((long)gh * g.n[lv] + sl[s]) * D;
+                const long row = ((long)gh * g.n[lv] + sl[s]) * D;
                 visit(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row);
             }
         }
-    const float inv = 1.0f / l;
-#pragma unroll
-    for (int c = 0; c < D; ++c) out[tg * D + c] = o[c] * inv;
-    lse[tg] = m + logf(l);
+    out[tg * D + lane] = o / l;
+    if (lane == 0) lse[tg] = m + logf(l);
 }
 
 }  // namespace
@@ -604,8 +595,8 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* ou
                                (const unsigned short*)v, (unsigned short*)out, lse, g, w);
         }
     } else {
-        long ntok = (long)g.G * g.N;
-        hipLaunchKernelGGL(attn_fwd_f32, dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, st,
+        long ntok = (long)g.G * g.N;  // one wave each
+        hipLaunchKernelGGL(attn_fwd_f32, dim3((unsigned)((ntok + 3) / 4)), dim3(256), 0, st,
                            (const float*)q, (const float*)k, (const float*)v, (float*)out, lse,
                            g, w);
     }

@@ -20,8 +20,8 @@
 // keys (order-preserving integer images of the scores) for a threshold that
 // admits exactly the K winners, ballots for ties at the K-th key (lowest
 // candidate position first) and a ballot prefix count to write the winners
-// in ascending order.  Every pick also increments the count of its key block
-// (integer atomics: exact, order-free), which the sparse transpose uses.
+// in ascending order.  The picks are also counted per key block and per 16
+// key blocks (see flush_counts), which the sparse transpose uses.
 #include "common.h"
 
 namespace llsa {
@@ -44,9 +44,31 @@ __device__ __forceinline__ unsigned order_key(float f)
 
 // Top-K of each of `rows` score rows (LDS, [rows][M]) written ascending to
 // out[r * K ..]; one wave per row at a time.
+// Pick counts of one head: per key block and per 16 key blocks.  A
+// workgroup first counts its picks per candidate in LDS (pc), then adds them
+// with one global atomic per picked block and one per group of 16
+// candidates (16 consecutive candidates are always the 16 children of one
+// block, or 16 consecutive blocks at the coarsest level).  Integer atomics:
+// exact whatever the order.
+struct Counts {
+    int* c1;
+    int* c16;
+};
+
+__device__ __forceinline__ void flush_counts(const int* pc, const int* cand, int M, Counts cnt)
+{
+    for (int c = threadIdx.x; c < M; c += blockDim.x)
+        if (pc[c]) atomicAdd(cnt.c1 + cand[c], pc[c]);
+    for (int gi = threadIdx.x; gi * BS < M; gi += blockDim.x) {
+        int sum = 0;
+        for (int u = 0; u < BS && gi * BS + u < M; ++u) sum += pc[gi * BS + u];
+        if (sum) atomicAdd(cnt.c16 + (cand[gi * BS] >> 4), sum);
+    }
+}
+
 template <int KPL>
 __device__ __forceinline__ void select_rows(const float* sc, const int* cand, int* out, int rows,
-                                            int M, int K, int* cnt)
+                                            int M, int K, int* pc)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const unsigned long long below = (1ull << lane) - 1ull;
@@ -87,9 +109,8 @@ __device__ __forceinline__ void select_rows(const float* sc, const int* cand, in
             bool take = (ok[s] && key[s] > T) || (eq && eq_before + __popcll(beq & below) < need);
             unsigned long long bt = __ballot(take);
             if (take) {
-                const int j = cand[s * 64 + lane];
-                orow[out_before + __popcll(bt & below)] = j;
-                atomicAdd(cnt + j, 1);
+                orow[out_before + __popcll(bt & below)] = cand[s * 64 + lane];
+                atomicAdd(pc + s * 64 + lane, 1);
             }
             eq_before += __popcll(beq);
             out_before += __popcll(bt);
@@ -101,14 +122,14 @@ template <int KPL>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ qbar,
                                                      const float* __restrict__ kbar,
                                                      const int* __restrict__ parent,
-                                                     int* __restrict__ idx,
-                                                     int* __restrict__ cnt, int n_l, int K,
-                                                     int R, int M, float scale)
+                                                     int* __restrict__ idx, Counts cnt,
+                                                     int n_l, int K, int R, int M, float scale)
 {
     extern __shared__ float smem[];
     float* qs = smem;                 // [R][D]
     float* sc = qs + R * D;           // [R][M]
     int* cand = (int*)(sc + R * M);   // [M]
+    int* pc = cand + M;               // [M] picks per candidate
 
     const int groups_per_head = parent ? n_l / BS : (n_l + R - 1) / R;
     const int gh = blockIdx.x / groups_per_head;
@@ -124,6 +145,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
         } else {
             cand[c] = c;
         }
+        pc[c] = 0;
     }
     for (int e = threadIdx.x; e < rows * D; e += blockDim.x)
         qs[e] = qbar[((long)gh * n_l + row0) * D + e];
@@ -163,8 +185,9 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
     }
     __syncthreads();
 
-    select_rows<KPL>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K,
-                     cnt + (long)gh * n_l);
+    select_rows<KPL>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K, pc);
+    __syncthreads();
+    flush_counts(pc, cand, M, {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)});
 }
 
 // Sum of x over the 16 lanes of each DPP row (every lane gets its row's sum).
@@ -184,7 +207,7 @@ __device__ __forceinline__ int row16_sum(int x)
 // and the four rows of a wave advance together.
 template <int KPG>
 __device__ __forceinline__ void select_rows16(const float* sc, const int* cand, int* out,
-                                              int rows, int M, int K, int* cnt)
+                                              int rows, int M, int K, int* pc)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
@@ -230,9 +253,8 @@ __device__ __forceinline__ void select_rows16(const float* sc, const int* cand, 
         const unsigned long long bt = __ballot(take);
         const unsigned mt = ((unsigned)(g < 2 ? bt : bt >> 32) >> sh) & 0xFFFFu;
         if (take) {
-            const int j = cand[BS * s + n];
-            orow[out_before + __popc(mt & below)] = j;
-            atomicAdd(cnt + j, 1);
+            orow[out_before + __popc(mt & below)] = cand[BS * s + n];
+            atomicAdd(pc + BS * s + n, 1);
         }
         eq_before += __popc(meq);
         out_before += __popc(mt);
@@ -248,13 +270,13 @@ template <int KPG>
 __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qbar,
                                                    const float* __restrict__ kbar,
                                                    const int* __restrict__ parent,
-                                                   int* __restrict__ idx,
-                                                   int* __restrict__ cnt, int n_l, int K, int M,
-                                                   float scale)
+                                                   int* __restrict__ idx, Counts cnt,
+                                                   int n_l, int K, int M, float scale)
 {
     extern __shared__ float smem[];
     float* sc = smem;                 // [16][M]
     int* cand = (int*)(sc + BS * M);  // [M]
+    int* pc = cand + M;               // [M] picks per candidate
     // R rows per workgroup: the 16 siblings of a parent (they share their
     // candidates), or 4 rows of the coarsest level (more workgroups)
     const int R = parent ? BS : 4;
@@ -270,6 +292,7 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
         } else {
             cand[c] = c;
         }
+        pc[c] = 0;
     }
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
@@ -310,16 +333,17 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
         for (int k = 0; k < 16; ++k) kb[k] = kn[k];
     }
     __syncthreads();
-    select_rows16<KPG>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K,
-                       cnt + (long)gh * n_l);
+    select_rows16<KPG>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K, pc);
+    __syncthreads();
+    flush_counts(pc, cand, M, {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)});
 }
 
 template <int KPG>
 hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, int* idx,
-                       int* cnt, int G, int n_l, int K, int M, float scale, hipStream_t st)
+                       Counts cnt, int G, int n_l, int K, int M, float scale, hipStream_t st)
 {
     const int groups = (n_l + (parent ? BS : 4) - 1) / (parent ? BS : 4);
-    const size_t lds = (size_t)BS * M * sizeof(float) + (size_t)M * sizeof(int);
+    const size_t lds = (size_t)BS * M * sizeof(float) + 2 * (size_t)M * sizeof(int);
     if (lds > 65536) {  // 16 rows x 1024 candidates
         hipError_t e = hipFuncSetAttribute((const void*)select_mfma<KPG>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -333,13 +357,13 @@ hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, 
 // Coarsest level with more than 1024 blocks: few rows per workgroup, so that
 // the dense n_L x n_L scoring spreads over many CUs.
 template <int KPL>
-hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, int* cnt, int G, int n_l,
+hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, Counts cnt, int G, int n_l,
                        int K, float scale, hipStream_t st)
 {
     const int M = n_l;
     int R = max(1, min(min(16, n_l / 64), 8192 / M));
     int groups = (n_l + R - 1) / R;
-    size_t lds = (size_t)(R * D + R * M) * sizeof(float) + (size_t)M * sizeof(int);
+    size_t lds = (size_t)(R * D + R * M) * sizeof(float) + 2 * (size_t)M * sizeof(int);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)select_kernel<KPL>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -362,15 +386,16 @@ hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
         const float* qb = w.qbar[l - 1];
         const float* kb = w.kbar[l - 1];
         int* out = w.idx[l - 1];
+        const Counts cnt = {w.cnt[l - 1], w.c16[l - 1]};
         hipError_t e;
         if (M <= 1024) {
             auto f = M <= 16 ? launch_mfma<1> : M <= 32 ? launch_mfma<2> : M <= 64 ? launch_mfma<4>
                    : M <= 128 ? launch_mfma<8> : M <= 256 ? launch_mfma<16>
                    : M <= 512 ? launch_mfma<32> : launch_mfma<64>;
-            e = f(qb, kb, parent, out, w.cnt[l - 1], g.G, g.n[l], g.K, M, g.scale, st);
+            e = f(qb, kb, parent, out, cnt, g.G, g.n[l], g.K, M, g.scale, st);
         } else {
             auto f = M <= 2048 ? launch_wide<32> : launch_wide<64>;
-            e = f(qb, kb, out, w.cnt[l - 1], g.G, g.n[l], g.K, g.scale, st);
+            e = f(qb, kb, out, cnt, g.G, g.n[l], g.K, g.scale, st);
         }
         if (e != hipSuccess) return e;
     }

@@ -6,8 +6,9 @@
 //
 // A counting sort into CSR form (rowptr [G][n_l+1], col [G][n_l*K], every
 // list ascending), one launch per level, coarsest first.  The counts come
-// from the selection pass; the prefix over them is summed by each workgroup
-// for its own bins; the fill gathers instead of scattering: one workgroup
+// from the selection pass (per block and per 16 blocks); each workgroup sums
+// the prefix before its own bins from the group counts; the fill gathers
+// instead of scattering: one workgroup
 // owns 16 sibling key blocks 16p .. 16p+15 and walks the only query blocks
 // that can have chosen them -- at a finer level, the children of the query
 // blocks in the parent level's list of block p (hierarchical selection only
@@ -75,10 +76,9 @@ __device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp, int* 
 
 // One workgroup (4 waves) per 16 sibling key blocks 16p .. 16p+15; one
 // candidate query block per thread.  The selection pass counted how often
-// each key block was chosen (cnt); the workgroup sums the counts of all key
-// blocks before its own to get its first CSR position (a few thousand ints
-// at most, read from L2), writes rowptr for its blocks, and fills their
-// lists.  Ranks: ballot within a wave, counts of lower waves through LDS,
+// each key block was chosen (per block and per 16 blocks); the workgroup
+// sums the group counts before its own blocks (n_l / 16 at most) to get its
+// first CSR position, writes rowptr for its blocks, and fills their lists.  Ranks: ballot within a wave, counts of lower waves through LDS,
 // counts of earlier rounds carried in registers.  Besides col it records, for
 // the pooled-token gradients and dk/dv, the position of j in each listed
 // query block's index list.
@@ -93,6 +93,7 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
     const int gh = blockIdx.x / groups, grp = blockIdx.x % groups;
     const int* I = w.idx[l - 1] + (long)gh * n * g.K;
     const int* cnt = w.cnt[l - 1] + (long)gh * n;
+    const int* c16 = w.c16[l - 1] + (long)gh * ((n + 15) / 16);
     int* rowptr = w.rowptr[l - 1] + (long)gh * (n + 1);
     int* col = w.col[l - 1] + (long)gh * n * g.K;
     unsigned char* slots = w.slot[l - 1] + (long)gh * n * g.K;
@@ -114,9 +115,10 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
         }
     };
     probe(0);
-    // first position of this group: sum of the counts of blocks 0 .. 16 grp - 1
+    // first position of this group: the counts of blocks 0 .. 16 grp - 1,
+    // summed as 16-block groups
     int acc = 0;
-    for (int b = tid; b < 16 * grp; b += blockDim.x) acc += cnt[b];
+    for (int b = tid; b < grp; b += blockDim.x) acc += c16[b];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if (lane == 0) wsum[wv] = acc;
