@@ -180,24 +180,28 @@ def summarize_pmc(fetch_db, write_db, out, cmd, workload):
 CALIB_COPY_MIB = 256
 
 
-def cpu_baseline(w, inp, budget_s=30.0):
+def cpu_baseline(w, inp, min_s=10.0):
     """The oracle (plain fp64 C, one thread) on a bounded sample of the same
-    workload: head 0 of B*H, whole path (pool, selection, forward, backward)."""
+    workload: whole heads (pool, selection, forward, backward), one after the
+    other, until at least min_s seconds of CPU work have run."""
     import oracle
     G, N, d = w.G, w.N, w.d
-    head = lambda a: a.reshape(G, N, d)[:1]
-    q = oracle.zorder(head(inp["q64"]), w.side)
-    k = oracle.zorder(head(inp["k64"]), w.side)
-    v = oracle.zorder(head(inp["v64"]), w.side)
-    do = head(inp["do64"])
-    t0 = time.perf_counter()
-    oracle.run(q, k, v, 16, w.levels, w.topk, dout=do)
-    dt = time.perf_counter() - t0
-    f = flops(w)["fwdbwd"] / G
+    head = lambda a, h: a.reshape(G, N, d)[h:h + 1]
+    done, dt = 0, 0.0
+    while done < G and dt < min_s:
+        q = oracle.zorder(head(inp["q64"], done), w.side)
+        k = oracle.zorder(head(inp["k64"], done), w.side)
+        v = oracle.zorder(head(inp["v64"], done), w.side)
+        do = head(inp["do64"], done)
+        t0 = time.perf_counter()
+        oracle.run(q, k, v, 16, w.levels, w.topk, dout=do)
+        dt += time.perf_counter() - t0
+        done += 1
+    f = flops(w)["fwdbwd"] * done / G
     return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 3),
-            "sample": "head 0 of %d (1/%d of the workload): pool, selection, forward and "
-                      "backward, fp64 C oracle, single thread" % (G, G)}
+            "sample": "heads 0..%d of %d (%d/%d of the workload): pool, selection, forward "
+                      "and backward, fp64 C oracle, single thread" % (done - 1, G, done, G)}
 
 
 def dense_reference(w, q, k, v, do, reps=3):
