@@ -478,11 +478,17 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     const f32x4 zero = {};
     f32x4 accK[4] = {}, accV[4] = {};
     // live == false (the padding step of an odd-length chunk): the MFMAs run
-    // on valid data but contribute zero
+    // on valid rows but every P and dS is 0
+    // per-row scalars as the step uses them: -lse * log2(e) (lanes < 16), so
+    // that P = exp2(S c - lse log2 e) is one fma and one exp2; in the padding
+    // step (live == false) -inf there and 0 for the pooled P and dS, which
+    // makes every P and dS of the step exactly 0
+    const bool lse_lane = lane < 16, pe_lane = lane >= 32;
     auto step = [&](const QBlock& f, bool live) {
         put_rows(lq, f.q0, f.q1, lane);
         put_rows(ld, f.d0, f.d1, lane);
-        aux[lane] = f.x;
+        const float nls = live ? -LOG2E * f.x : -INFINITY;
+        aux[lane] = lse_lane ? nls : (pe_lane && !live) ? 0.f : f.x;
         lds_fence();
         const float4 l4 = *(const float4*)(aux + 4 * gq);
         const float4 e4 = *(const float4*)(aux + BS + 4 * gq);
@@ -501,14 +507,14 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
         bf16x4 bp, bs;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float p = fast_exp2(fmaf(s[r], c, -lr[r] * LOG2E));
+            float p = fast_exp2(fmaf(s[r], c, lr[r]));
             float ds = p * (dp[r] - dr[r]);
             if (enrich) {
                 p = fmaf(pr[r], 1.0f / BS, p);
                 ds = fmaf(sr_[r], 1.0f / BS, ds);
             }
-            bp[r] = (bf16)(live ? p : 0.f);
-            bs[r] = (bf16)(live ? ds : 0.f);
+            bp[r] = (bf16)p;
+            bs[r] = (bf16)ds;
         }
 #pragma unroll
         for (int d = 0; d < 4; ++d) {

@@ -31,20 +31,30 @@ __device__ __forceinline__ unsigned gather_bits(unsigned x)  // inverse of sprea
     return x;
 }
 
-template <typename V>
+// CPR_LOG2 >= 0: chunks per row is 2^CPR_LOG2 and every index splits with
+// shifts; CPR_LOG2 < 0: any chunk count (divisions).
+template <typename V, int CPR_LOG2>
 __global__ __launch_bounds__(256) void zorder_kernel(const V* __restrict__ src,
                                                      V* __restrict__ dst, long long total,
                                                      int chunks_per_row, int side_log2,
-                                                     long long n, int inverse)
+                                                     int inverse)
 {
     const unsigned side_mask = (1u << side_log2) - 1u;
+    const unsigned n_mask = (1u << (2 * side_log2)) - 1u;
     for (long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x; id < total;
          id += (long long)gridDim.x * blockDim.x) {
-        long long row = id / chunks_per_row;
-        int c = (int)(id - row * chunks_per_row);
-        long long o = row / n;
-        unsigned p = (unsigned)(row - o * n);  // destination position
-        unsigned s;                             // source position
+        long long row;
+        int c;
+        if (CPR_LOG2 >= 0) {
+            row = id >> CPR_LOG2;
+            c = (int)(id & ((1 << CPR_LOG2) - 1));
+        } else {
+            row = id / chunks_per_row;
+            c = (int)(id - row * chunks_per_row);
+        }
+        const long long o = row >> (2 * side_log2);
+        const unsigned p = (unsigned)row & n_mask;  // destination position
+        unsigned s;                                   // source position
         if (!inverse) {  // p is a Morton code; read the raster cell it names
             unsigned x = gather_bits(p), y = gather_bits(p >> 1);
             s = (y << side_log2) | x;
@@ -52,7 +62,8 @@ __global__ __launch_bounds__(256) void zorder_kernel(const V* __restrict__ src,
             unsigned y = p >> side_log2, x = p & side_mask;
             s = (spread_bits(y) << 1) | spread_bits(x);
         }
-        dst[id] = src[(o * n + s) * chunks_per_row + c];
+        const long long srow = (o << (2 * side_log2)) | s;
+        dst[id] = src[CPR_LOG2 >= 0 ? (srow << CPR_LOG2) | c : srow * chunks_per_row + c];
     }
 }
 
@@ -63,22 +74,27 @@ hipError_t launch_zorder(const void* src, void* dst, long long outer, int side, 
 {
     int lg = 0;
     while ((1 << lg) < side) ++lg;
-    long long n = (long long)side * side;
     int vw = (inner_bytes % 16 == 0) ? 16 : (inner_bytes % 8 == 0) ? 8 : 4;
     int cpr = inner_bytes / vw;
-    long long total = outer * n * cpr;
+    long long total = outer * ((long long)side * side) * cpr;
     long long blocks = (total + 255) / 256;
     if (blocks > (1ll << 20)) blocks = 1ll << 20;
     dim3 grid((unsigned)blocks);
-    if (vw == 16)
-        hipLaunchKernelGGL(zorder_kernel<uint4>, grid, dim3(256), 0, st, (const uint4*)src,
-                           (uint4*)dst, total, cpr, lg, n, inverse);
-    else if (vw == 8)
-        hipLaunchKernelGGL(zorder_kernel<uint2>, grid, dim3(256), 0, st, (const uint2*)src,
-                           (uint2*)dst, total, cpr, lg, n, inverse);
-    else
-        hipLaunchKernelGGL(zorder_kernel<unsigned>, grid, dim3(256), 0, st,
-                           (const unsigned*)src, (unsigned*)dst, total, cpr, lg, n, inverse);
+    const int pl = (cpr & (cpr - 1)) == 0 ? __builtin_ctz(cpr) : -1;
+#define LLSA_ZLAUNCH(V, L)                                                                  \
+    hipLaunchKernelGGL((zorder_kernel<V, L>), grid, dim3(256), 0, st, (const V*)src, (V*)dst, \
+                       total, cpr, lg, inverse)
+    if (vw == 16) {
+        if (pl == 3) LLSA_ZLAUNCH(uint4, 3);
+        else if (pl == 2) LLSA_ZLAUNCH(uint4, 2);
+        else if (pl == 4) LLSA_ZLAUNCH(uint4, 4);
+        else LLSA_ZLAUNCH(uint4, -1);
+    } else if (vw == 8) {
+        LLSA_ZLAUNCH(uint2, -1);
+    } else {
+        LLSA_ZLAUNCH(unsigned, -1);
+    }
+#undef LLSA_ZLAUNCH
     return hipGetLastError();
 }
 
