@@ -16,6 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "llsa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 NO_ENRICH = 1
+ENRICH_COARSE = 2
+SIZE_BIAS = 4
 
 _lib = None
 

@@ -158,8 +158,18 @@ void orc_select(const double* qpyr, const double* kpyr, int64_t G, int64_t N,
 /* Key/value rows of the set of token t (head g): the bs*K fine tokens of the
  * selected level-1 blocks, then, unless disabled, the pooled pairs of the
  * blocks selected at every level l for the token's level-l ancestor ([P2]
- * hierarchical KV enrichment).  tag[e] = 0 for a fine entry (ref = token),
- * tag[e] = l for a level-l pooled entry (ref = block). */
+ * hierarchical KV enrichment; with ORC_ENRICH_COARSE only levels 2..L).
+ * tag[e] = 0 for a fine entry (ref = token), tag[e] = l for a level-l pooled
+ * entry (ref = block). */
+
+/* Additive logit of entry e: with ORC_SIZE_BIAS a level-l pooled token, the
+ * mean of bs^l tokens, counts as bs^l copies of itself in the softmax
+ * (logit + ln bs^l); otherwise 0. */
+static double entry_bias(int tag, int64_t bs, unsigned flags)
+{
+    return (tag > 0 && (flags & ORC_SIZE_BIAS)) ? (double)tag * log((double)bs) : 0.0;
+}
+
 static int64_t kv_set(const double* k, const double* v, const double* kpyr,
                       const double* vpyr, const int32_t* idx, int64_t g,
                       int64_t t, int64_t G, int64_t N, int64_t d, int64_t bs,
@@ -179,7 +189,7 @@ static int64_t kv_set(const double* k, const double* v, const double* kpyr,
             ++ne;
         }
     if (!(flags & ORC_NO_ENRICH))
-        for (int l = 1; l <= L; ++l) {
+        for (int l = (flags & ORC_ENRICH_COARSE) ? 2 : 1; l <= L; ++l) {
             int64_t n_l = N / ipow(bs, l), a = t / ipow(bs, l);
             const int32_t* sel = idx + lvl_off(G, N, bs, l, K) + (g * n_l + a) * K;
             for (int64_t p = 0; p < K; ++p) {
@@ -218,7 +228,7 @@ void orc_forward(const double* q, const double* k, const double* v,
                 const double* qt = q + (g * N + t) * d;
                 double m = -INFINITY;
                 for (int64_t e = 0; e < ne; ++e) {
-                    z[e] = scale * dot(qt, key[e], d);
+                    z[e] = scale * dot(qt, key[e], d) + entry_bias(tag[e], bs, flags);
                     if (z[e] > m) m = z[e];
                 }
                 double l = 0.0;
@@ -305,7 +315,7 @@ void orc_backward(const double* q, const double* k, const double* v,
                 if (want_q[i])
                     for (int64_t c = 0; c < d; ++c) dqt[c] = 0.0;
                 for (int64_t e = 0; e < ne; ++e) {
-                    double P = exp(scale * dot(qt, key[e], d) - lt);
+                    double P = exp(scale * dot(qt, key[e], d) + entry_bias(tag[e], bs, flags) - lt);
                     double dP = dot(dot_, val[e], d);
                     double dS = P * (dP - Dt);
                     if (want_q[i])

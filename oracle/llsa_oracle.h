@@ -42,7 +42,10 @@
 extern "C" {
 #endif
 
-#define ORC_NO_ENRICH 1u
+/* enrichment variants (flags) */
+#define ORC_NO_ENRICH 1u     /* fine tokens only */
+#define ORC_ENRICH_COARSE 2u /* pooled tokens of levels 2..L only */
+#define ORC_SIZE_BIAS 4u     /* a level-l pooled logit gets + ln bs^l */
 
 /* Morton (Z-order) position of raster cell (y, x) on a side x side grid,
  * side a power of two: bits of y and x interleaved, the y bit above the x

@@ -25,7 +25,9 @@ def _loss_and_idx(q, k, v, dout, L, K, flags):
 
 
 @pytest.mark.parametrize("N,L,K,flags", [(256, 1, 4, 0), (256, 1, 4, oracle.NO_ENRICH),
-                                         (1024, 2, 2, 0)])
+                                         (1024, 2, 2, 0), (256, 1, 4, oracle.SIZE_BIAS),
+                                         (1024, 2, 2, oracle.ENRICH_COARSE),
+                                         (1024, 2, 2, oracle.ENRICH_COARSE | oracle.SIZE_BIAS)])
 def test_finite_differences(N, L, K, flags):
     G, d = 1, 8
     rng = np.random.default_rng(N + K + flags)

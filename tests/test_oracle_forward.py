@@ -21,10 +21,12 @@ def dense_attention(q, k, v, scale):
     return np.einsum("gtu,guc->gtc", p / l, v), (m + np.log(l))[..., 0]
 
 
-def dense_mask_reference(q, k, v, idx, scale, enrich=True):
+def dense_mask_reference(q, k, v, idx, scale, enrich=True, first_level=1, size_bias=False):
     """Independent formulation: one masked softmax per token over all fine
     tokens plus all pooled tokens of every level, the mask built densely from
-    the index lists."""
+    the index lists.  first_level = 2: pooled tokens of levels 2..L only;
+    size_bias: the logit of a level-l pooled token gets + ln(16^l) (it stands
+    for 16^l tokens)."""
     G, N, d = q.shape
     L = len(idx)
     n1 = N // BS
@@ -38,6 +40,13 @@ def dense_mask_reference(q, k, v, idx, scale, enrich=True):
             cols_v.append(v[g].reshape(N // BS ** l, BS ** l, d).mean(axis=1))
         Kc, Vc = np.concatenate(cols_k), np.concatenate(cols_v)
         mask = np.zeros((N, Kc.shape[0]), bool)
+        bias = np.zeros(Kc.shape[0])
+        off = N
+        for l in range(1, L + 1):
+            n = N // BS ** l
+            if size_bias:
+                bias[off:off + n] = l * np.log(BS)
+            off += n
         for t in range(N):
             i = t // BS
             blk = np.zeros(n1, bool)
@@ -47,9 +56,10 @@ def dense_mask_reference(q, k, v, idx, scale, enrich=True):
                 off = N
                 for l in range(1, L + 1):
                     n = N // BS ** l
-                    mask[t, off + idx[l - 1][g, t // BS ** l]] = True
+                    if l >= first_level:
+                        mask[t, off + idx[l - 1][g, t // BS ** l]] = True
                     off += n
-        z = scale * (q[g] @ Kc.T)
+        z = scale * (q[g] @ Kc.T) + bias[None, :]
         z = np.where(mask, z, -np.inf)
         m = z.max(axis=1, keepdims=True)
         p = np.exp(z - m)
@@ -86,14 +96,21 @@ def test_all_blocks_with_enrichment_is_dense_over_concatenation():
     np.testing.assert_allclose(r["lse"], lse, rtol=0, atol=1e-12)
 
 
+VARIANTS = {"enrich": 0, "no_enrich": oracle.NO_ENRICH, "coarse": oracle.ENRICH_COARSE,
+            "size_bias": oracle.SIZE_BIAS, "coarse_size_bias": oracle.ENRICH_COARSE | oracle.SIZE_BIAS}
+
+
 @pytest.mark.parametrize("N,L,K", [(1024, 2, 2), (4096, 2, 4), (256, 1, 4)])
-@pytest.mark.parametrize("enrich", [True, False])
-def test_matches_dense_mask_formulation(N, L, K, enrich):
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_matches_dense_mask_formulation(N, L, K, variant):
     G, d = 2, 8
     q, k, v = (_rand((G, N, d), s + N) for s in (7, 8, 9))
-    flags = 0 if enrich else oracle.NO_ENRICH
+    flags = VARIANTS[variant]
     r = oracle.run(q, k, v, BS, L, K, flags=flags)
-    o, lse = dense_mask_reference(q, k, v, r["idx"], r["scale"], enrich)
+    o, lse = dense_mask_reference(q, k, v, r["idx"], r["scale"],
+                                  enrich=not (flags & oracle.NO_ENRICH),
+                                  first_level=2 if flags & oracle.ENRICH_COARSE else 1,
+                                  size_bias=bool(flags & oracle.SIZE_BIAS))
     np.testing.assert_allclose(r["out"], o, rtol=0, atol=1e-12)
     np.testing.assert_allclose(r["lse"], lse, rtol=0, atol=1e-12)
 
@@ -134,3 +151,33 @@ def test_query_block_subset_matches_full():
         np.testing.assert_array_equal(o[:, BS * i:BS * (i + 1)], r["out"][:, BS * i:BS * (i + 1)])
         np.testing.assert_array_equal(lse[:, BS * i:BS * (i + 1)],
                                       r["lse"][:, BS * i:BS * (i + 1)])
+
+
+@pytest.mark.parametrize("coarse", [False, True])
+def test_zero_query_size_bias_weights_pooled_tokens_by_their_size(coarse):
+    """Q = 0 with size-weighted pooled logits: every fine token has weight 1 and a
+    level-l pooled token weight 16^l, so out is the weighted mean in closed form
+    and lse = ln(16 K + K sum_l 16^l)."""
+    G, N, d, L, K = 1, 4096, 8, 2, 4
+    q = np.zeros((G, N, d))
+    k, v = _rand((G, N, d), 20), _rand((G, N, d), 21)
+    flags = oracle.SIZE_BIAS | (oracle.ENRICH_COARSE if coarse else 0)
+    r = oracle.run(q, k, v, BS, L, K, flags=flags)
+    levels = range(2 if coarse else 1, L + 1)
+    total = BS * K + sum(K * BS ** l for l in levels)
+    np.testing.assert_allclose(r["lse"], np.log(total), rtol=0, atol=1e-12)
+    fine = v[0, :BS * K].sum(axis=0)
+    pooled = sum(BS ** l * v[0, :BS ** l * K].reshape(K, BS ** l, d).mean(axis=1).sum(axis=0)
+                 for l in levels)
+    want = (fine + pooled) / total
+    np.testing.assert_allclose(r["out"][0], np.broadcast_to(want, (N, d)), rtol=0, atol=1e-12)
+
+
+def test_coarse_enrichment_with_one_level_is_no_enrichment():
+    """Levels 2..L only, with L = 1, leaves the fine tokens alone."""
+    G, N, d = 2, 512, 8
+    q, k, v = (_rand((G, N, d), s) for s in (22, 23, 24))
+    a = oracle.run(q, k, v, BS, 1, 4, flags=oracle.ENRICH_COARSE)
+    b = oracle.run(q, k, v, BS, 1, 4, flags=oracle.NO_ENRICH)
+    np.testing.assert_array_equal(a["out"], b["out"])
+    np.testing.assert_array_equal(a["lse"], b["lse"])
