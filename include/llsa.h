@@ -45,8 +45,14 @@ extern "C" {
 #define LLSA_F32 0
 #define LLSA_BF16 1
 
-/* flags */
-#define LLSA_NO_ENRICH 1u /* attend to the selected fine blocks only */
+/* flags: which pooled tokens enrich the key/value set (skill summary, "Core
+ * Technique" 2, leaves the levels and the weighting open).  Default (0): the
+ * pooled keys/values of the blocks chosen at every level, plain logits. */
+#define LLSA_NO_ENRICH 1u     /* attend to the selected fine blocks only */
+#define LLSA_ENRICH_COARSE 2u /* pooled tokens of levels 2..levels only */
+#define LLSA_SIZE_BIAS 4u     /* a level-l pooled token, the mean of 16^l tokens,
+                                 counts as 16^l copies (logit + ln 16^l) */
+#define LLSA_KNOWN_FLAGS 7u
 
 /* error codes */
 #define LLSA_OK 0

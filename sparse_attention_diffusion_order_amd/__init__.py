@@ -16,7 +16,7 @@ import os
 import re
 
 __all__ = [
-    "LlsaError", "F32", "BF16", "NO_ENRICH", "PART_POOL", "PART_SELECT", "PART_ATTN",
+    "LlsaError", "F32", "BF16", "NO_ENRICH", "ENRICH_COARSE", "SIZE_BIAS", "PART_POOL", "PART_SELECT", "PART_ATTN",
     "PART_TRANSPOSE", "PART_DQ", "PART_ENRICH", "PART_DKDV", "library_path", "load", "exported_names",
     "llsa_workspace_bytes", "llsa_workspace_layout", "llsa_zorder", "llsa_forward",
     "llsa_backward", "llsa_forward_part", "llsa_backward_part", "llsa_strerror",
@@ -29,6 +29,8 @@ _HEADER = os.path.join(os.path.dirname(_HERE), "include", "llsa.h")
 
 F32, BF16 = 0, 1
 NO_ENRICH = 1
+ENRICH_COARSE = 2
+SIZE_BIAS = 4
 PART_POOL, PART_SELECT, PART_ATTN = 0, 1, 2
 PART_TRANSPOSE, PART_DQ, PART_DKDV, PART_ENRICH = 3, 4, 5, 6
 MAX_LEVELS = 6

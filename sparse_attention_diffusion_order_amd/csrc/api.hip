@@ -20,7 +20,7 @@ int validate(int B, int H, int N, int d, int block_size, int topk, int levels, i
              unsigned flags)
 {
     if (d != D || block_size != BS || (dtype != LLSA_F32 && dtype != LLSA_BF16) ||
-        (flags & ~LLSA_NO_ENRICH))
+        (flags & ~LLSA_KNOWN_FLAGS))
         return LLSA_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || N < BS || !pow2(N) || topk < 1 || !pow2(topk) || levels < 1)
         return LLSA_ERR_SHAPE;
@@ -99,6 +99,8 @@ void make_geo(int B, int H, int N, int topk, int levels, unsigned flags, Geo* g)
     for (int l = 1; l <= levels; ++l) g->n[l] = g->n[l - 1] / BS;
     g->scale = 0.125f;  // 1/sqrt(64)
     g->flags = flags;
+    g->l0 = (flags & LLSA_NO_ENRICH) ? levels + 1 : (flags & LLSA_ENRICH_COARSE) ? 2 : 1;
+    g->lb2 = (flags & LLSA_SIZE_BIAS) ? 4.0f : 0.0f;  // log2(16^l) = 4 l
 }
 
 void make_ws(void* base, const Layout& lay, int L, Ws* w)

@@ -30,6 +30,10 @@ struct Geo {
     int n[MAX_L + 1];      // n[l] = N / 16^l blocks at level l (n[0] = N)
     float scale;           // 1 / sqrt(d)
     unsigned flags;
+    int l0;                // first level whose pooled tokens enrich (L + 1: none)
+    float lb2;             // logit bias of a level-l pooled token: l * lb2 (log2 units)
+    // pooled entries per query block: levels l0..L, K each
+    __host__ __device__ int n_pooled() const { return l0 <= L ? (L - l0 + 1) * K : 0; }
 };
 
 // Device pointers into the caller's workspace.

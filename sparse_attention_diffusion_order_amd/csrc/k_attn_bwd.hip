@@ -78,16 +78,19 @@ __device__ __forceinline__ void put_rows(unsigned short* lds, bf16x8 r0, bf16x8 
 // dQ^T += K^T dS^T over two 16-entry tiles.  Key rows are in LDS (la, lb);
 // ka*/kb* are the A operands of S^T (the same rows), va*/vb* those of dP^T.
 // na / nb: valid entries (MASK == false: both tiles full).
-// pe != nullptr (pooled tiles): entries ea + 4(lane/16) + r of tile a (and
-// ea + 16 + ... of tile b) below K are level-1 pooled tokens; their P and dS
-// are stored at pe[entry][0 | 1][query] for the key-major dk/dv pass.
+// Pooled tiles: entry ea + 4(lane/16) + r of tile a (ea + 16 + ... of tile b)
+// is a level l0 + entry / K token and its logit gets lb2 times that level
+// (lb2 = 0: no bias; fine tiles pass 0).  pe != nullptr: the entries below K
+// are level-1 pooled tokens; their P and dS are stored at
+// pe[entry][0 | 1][query] for the key-major dk/dv pass.
 template <bool MASK>
 __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1, bf16x8 bd0,
                                         bf16x8 bd1, float nl2, float Dq, bf16x8 ka0, bf16x8 ka1,
                                         bf16x8 kb0, bf16x8 kb1, bf16x8 va0, bf16x8 va1,
                                         bf16x8 vb0, bf16x8 vb1, const unsigned short* la,
                                         const unsigned short* lb, int na, int nb, float c,
-                                        int lane, float* pe = nullptr, int ea = 0, int K = 0)
+                                        int lane, float* pe = nullptr, int ea = 0, int K = 1,
+                                        float lb2 = 0.f, int l0 = 1)
 {
     const int gq = lane >> 4;
     const int rr = (lane & 15) >> 2, xx = lane & 3;
@@ -99,8 +102,14 @@ __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1,
     bf16x8 bs;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        float Pa = fast_exp2(fmaf(sa[r], c, nl2));
-        float Pb = fast_exp2(fmaf(sb[r], c, nl2));
+        float ba = 0.f, bb = 0.f;
+        if (MASK) {
+            const int e_a = ea + 4 * gq + r;
+            ba = lb2 * (float)(l0 + e_a / K);
+            bb = lb2 * (float)(l0 + (e_a + BS) / K);
+        }
+        float Pa = fast_exp2(fmaf(sa[r], c, nl2 + ba));
+        float Pb = fast_exp2(fmaf(sb[r], c, nl2 + bb));
         if (MASK) {
             Pa = (4 * gq + r < na) ? Pa : 0.f;
             Pb = (4 * gq + r < nb) ? Pb : 0.f;
@@ -175,14 +184,15 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
     const long tok = (long)gh * g.N + (long)i * BS + nq;
     if (gq == 0) w.delta[tok] = Dq;
     const float nl2 = -lse[tok] * LOG2E;
-    // pooled entries e = (l-1)*K + slot: their rows in the bf16 pooled arrays
-    const int E = (g.flags & LLSA_NO_ENRICH) ? 0 : g.L * g.K;
+    // pooled entries e = (l - l0) * K + slot of the enriching levels l0..L:
+    // their rows in the bf16 pooled arrays
+    const int E = g.n_pooled();
     int* ent = (int*)(smem[wv] + 2 * Lay::K_TILE + 2 * Lay::V_TILE);
-    for (int l = 1; l <= (E ? g.L : 0); ++l) {
+    for (int l = g.l0; l <= g.L; ++l) {
         const long a = (long)gh * g.n[l] + (i >> (4 * (l - 1)));
         for (int s0 = 0; s0 < g.K; s0 += 64)
             if (s0 + lane < g.K)
-                ent[(l - 1) * g.K + s0 + lane] =
+                ent[(l - g.l0) * g.K + s0 + lane] =
                     (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * g.K + s0 + lane]);
     }
     lds_fence();
@@ -249,10 +259,12 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
             const int e0 = p < NF ? 0 : BS * 2 * (p - NF);
             const int na = p < NF ? BS : max(0, min(BS, E - e0));
             const int nb = p < NF ? 0 : max(0, min(BS, E - e0 - BS));
-            float* pe = (p >= NF && e0 < g.K)
+            const bool pooled = p >= NF;
+            float* pe = (pooled && g.l0 == 1 && e0 < g.K)
                             ? w.pe1 + ((long)gh * g.n[1] + i) * g.K * 2 * BS : nullptr;
             dq_pair<true>(acc, bq0, bq1, bd0, bd1, nl2, Dq, ka0, ka1, kb0, kb1, va0, va1, vb0,
-                          vb1, la, lb, na, nb, c, lane, pe, e0, g.K);
+                          vb1, la, lb, na, nb, c, lane, pe, e0, g.K, pooled ? g.lb2 : 0.f,
+                          g.l0);
         }
     };
     DqPair A, B;
@@ -312,6 +324,7 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
     for (int l = 2; l <= g.L; ++l) {
         const int al = a2 >> (4 * (l - 2));
         const int* sel = w.idx[l - 1] + ((long)gh * g.n[l] + al) * g.K;
+        const float lb = g.lb2 * (float)l;  // size bias of a level-l token (log2)
         for (int e0 = 0; e0 < g.K; e0 += BS) {
             const bool ev = e0 + nq < g.K;
             bf16x8 bk0 = {}, bk1 = {}, bv0 = {}, bv1 = {};
@@ -349,7 +362,7 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
                 bf16x4 pP, pS;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float P = ev ? fast_exp2(s[r] * c - lr[r] * LOG2E) : 0.f;
+                    float P = ev ? fast_exp2(s[r] * c - lr[r] * LOG2E + lb) : 0.f;
                     pP[r] = (bf16)P;
                     pS[r] = (bf16)(P * (dp[r] - dr[r]));
                 }
@@ -437,7 +450,7 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
 // its list T_1[j], one block per step with the next one in flight.
 //   S  = Q K^T, dP = dO V^T   (16x16x32 MFMA; lane holds query 4(lane/16)+r,
 //                              key lane%16)
-//   P = exp(s S - lse), dS = P (dP - D); with enrichment, the level-1 pooled
+//   P = exp(s S - lse), dS = P (dP - D); when level 1 enriches, the level-1 pooled
 //   token of block j (chosen by exactly the blocks of T_1[j]) adds P_e/16 and
 //   dS_e/16 to every key column -- P_e and dS_e come from the dq pass
 //   dV^T += dO^T P, dK^T += Q^T dS   (16x16x16 MFMA over the 16 queries;
@@ -463,7 +476,7 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     const int gq = lane >> 4, nq = lane & 15;
     const long kblk = xcd_block(blockIdx.x, gridDim.x);
     const int gh = (int)(kblk / g.n[1]), j = (int)(kblk % g.n[1]);
-    const bool enrich = !(g.flags & LLSA_NO_ENRICH);
+    const bool enrich1 = g.l0 == 1;  // level-1 pooled tokens enrich
     const float c = g.scale * LOG2E;
     const long hbase = (long)gh * g.N * D;
     const long tbase = (long)gh * g.N;
@@ -509,7 +522,7 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
         for (int r = 0; r < 4; ++r) {
             float p = fast_exp2(fmaf(s[r], c, lr[r]));
             float ds = p * (dp[r] - dr[r]);
-            if (enrich) {
+            if (enrich1) {
                 p = fmaf(pr[r], 1.0f / BS, p);
                 ds = fmaf(sr_[r], 1.0f / BS, ds);
             }
@@ -581,15 +594,14 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
             xk[r] = accK[d][r] * g.scale;
             xv[r] = accV[d][r];
         }
-        if (enrich)
-            for (int l = 2; l <= g.L; ++l) {
-                const int a = j >> (4 * (l - 1));
-                const float wgt = 1.0f / (float)(1 << (4 * l));
-                const float* db = w.dbar[l - 1] + ((long)gh * g.n[l] + a) * 2 * D + 16 * d + 4 * gq;
-                const float4 gk = *(const float4*)db, gv = *(const float4*)(db + D);
-                xk[0] += gk.x * wgt; xk[1] += gk.y * wgt; xk[2] += gk.z * wgt; xk[3] += gk.w * wgt;
-                xv[0] += gv.x * wgt; xv[1] += gv.y * wgt; xv[2] += gv.z * wgt; xv[3] += gv.w * wgt;
-            }
+        for (int l = max(2, g.l0); l <= g.L; ++l) {
+            const int a = j >> (4 * (l - 1));
+            const float wgt = 1.0f / (float)(1 << (4 * l));
+            const float* db = w.dbar[l - 1] + ((long)gh * g.n[l] + a) * 2 * D + 16 * d + 4 * gq;
+            const float4 gk = *(const float4*)db, gv = *(const float4*)(db + D);
+            xk[0] += gk.x * wgt; xk[1] += gk.y * wgt; xk[2] += gk.z * wgt; xk[3] += gk.w * wgt;
+            xv[0] += gv.x * wgt; xv[1] += gv.y * wgt; xv[2] += gv.z * wgt; xv[3] += gv.w * wgt;
+        }
         u16x4 ok, ov;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -613,17 +625,18 @@ __device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const 
     for (int s = 0; s < g.K; ++s)
         for (int r = 0; r < BS; ++r) {
             long row = ((long)gh * g.N + (long)sel[s] * BS + r) * D;
-            f(k + row, v + row);
+            f(k + row, v + row, 0.f);
         }
-    if (!(g.flags & LLSA_NO_ENRICH))
-        for (int lv = 1; lv <= g.L; ++lv) {
-            const int a = t >> (4 * lv);
-            const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.K;
-            for (int s = 0; s < g.K; ++s) {
-                long row = ((long)gh * g.n[lv] + sl[s]) * D;
-                f(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row);
-            }
+    // enriching levels l0..L; a level-lv token's logit gets lb2 * lv * ln 2
+    for (int lv = g.l0; lv <= g.L; ++lv) {
+        const int a = t >> (4 * lv);
+        const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.K;
+        const float bias = g.lb2 * (float)lv * LN2;
+        for (int s = 0; s < g.K; ++s) {
+            long row = ((long)gh * g.n[lv] + sl[s]) * D;
+            f(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, bias);
         }
+    }
 }
 
 // dq and delta: one wave per query token
@@ -644,11 +657,11 @@ __global__ __launch_bounds__(256) void dq_f32(const float* __restrict__ q,
     if (lane == 0) w.delta[tg] = Dt;
     const float lt = lse[tg];
     float acc = 0.f;
-    for_each_entry(g, w, k, v, gh, t, [&](const float* kr, const float* vr) {
+    for_each_entry(g, w, k, v, gh, t, [&](const float* kr, const float* vr, float bias) {
         const float kc = kr[lane];
         const float z = wave_sum(qc * kc);
         const float dp = wave_sum(dc * vr[lane]);
-        const float P = expf(z * g.scale - lt);
+        const float P = expf(z * g.scale + bias - lt);
         const float ds = P * (dp - Dt) * g.scale;
         acc = fmaf(ds, kc, acc);
     });
@@ -670,6 +683,7 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
     const int* rp = w.rowptr[l - 1] + (long)gh * (g.n[l] + 1);
     const int* cl = w.col[l - 1] + (long)gh * g.n[l] * g.K;
     const long span = 1l << (4 * l);
+    const float bias = g.lb2 * (float)l * LN2;  // size bias of a level-l token
     float sk = 0.f, sv = 0.f;
     for (int e = rp[j]; e < rp[j + 1]; ++e) {
         const long a = cl[e];
@@ -678,7 +692,7 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
             const float qc = q[tg * D + lane], dc = dout[tg * D + lane];
             const float z = wave_sum(qc * kb);
             const float dp = wave_sum(dc * vb);
-            const float P = expf(z * g.scale - lse[tg]);
+            const float P = expf(z * g.scale + bias - lse[tg]);
             const float ds = P * (dp - w.delta[tg]);
             sk = fmaf(ds * g.scale, qc, sk);
             sv = fmaf(P, dc, sv);
@@ -717,13 +731,12 @@ __global__ __launch_bounds__(256) void dkdv_f32(const float* __restrict__ q,
             ak = fmaf(ds, qc, ak);
             av = fmaf(P, dc, av);
         }
-    if (!(g.flags & LLSA_NO_ENRICH))
-        for (int l = 1; l <= g.L; ++l) {
-            const float wgt = 1.0f / (float)(1 << (4 * l));
-            const float* db = w.dbar[l - 1] + ((long)gh * g.n[l] + (x >> (4 * l))) * 2 * D;
-            ak += db[lane] * wgt;
-            av += db[D + lane] * wgt;
-        }
+    for (int l = g.l0; l <= g.L; ++l) {
+        const float wgt = 1.0f / (float)(1 << (4 * l));
+        const float* db = w.dbar[l - 1] + ((long)gh * g.n[l] + (x >> (4 * l))) * 2 * D;
+        ak += db[lane] * wgt;
+        av += db[D + lane] * wgt;
+    }
     dk[xg * D + lane] = ak;
     dv[xg * D + lane] = av;
 }
@@ -736,7 +749,7 @@ hipError_t launch_attn_dq(const void* q, const void* k, const void* v, const voi
 {
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
-        auto kern = (g.L * g.K <= 64) ? dq_bf16<64> : dq_bf16<MAX_E>;
+        auto kern = (g.n_pooled() <= 64) ? dq_bf16<64> : dq_bf16<MAX_E>;
         hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
                            (const unsigned short*)q, (const unsigned short*)k,
                            (const unsigned short*)v, (const unsigned short*)out, lse,
@@ -750,12 +763,13 @@ hipError_t launch_attn_dq(const void* q, const void* k, const void* v, const voi
     return hipGetLastError();
 }
 
-// Gradients of the pooled tokens (bf16: levels >= 2, level 1 being handled in
-// the dk/dv pass; fp32: every level).  Needs delta from the dq pass.
+// Gradients of the enriching pooled tokens (bf16: levels >= 2, level 1 being
+// handled in the dk/dv pass; fp32: every enriching level).  Needs delta from
+// the dq pass.
 hipError_t launch_attn_enrich(const void* q, const float* lse, const void* dout, int dtype,
                               const Geo& g, const Ws& w, hipStream_t st)
 {
-    if (g.flags & LLSA_NO_ENRICH) return hipSuccess;
+    if (g.l0 > g.L) return hipSuccess;
     if (dtype == LLSA_BF16) {
         if (g.L < 2) return hipSuccess;
         hipLaunchKernelGGL(enrich_bwd_bf16, dim3(g.G * g.n[2]), dim3(256), 0, st,
@@ -770,7 +784,7 @@ hipError_t launch_attn_enrich(const void* q, const float* lse, const void* dout,
         return e;
     }
     hipError_t e = hipSuccess;
-    for (int l = 1; l <= g.L && e == hipSuccess; ++l) {
+    for (int l = g.l0; l <= g.L && e == hipSuccess; ++l) {
         long n = (long)g.G * g.n[l];  // one wave per pooled block
         hipLaunchKernelGGL(enrich_f32, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st,
                            (const float*)q, lse, (const float*)dout, g, w, l);

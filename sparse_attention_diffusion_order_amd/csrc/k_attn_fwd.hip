@@ -7,12 +7,16 @@
 // Key/value set of the 16 tokens of query block i (level-l ancestor
 // a_l = i / 16^(l-1)):
 //   - the 16*K tokens of the key blocks idx_1[i] (fine tiles, 16 keys each);
-//   - for every level l = 1..L the pooled pairs (kbar_l[j], vbar_l[j]) for
-//     j in idx_l[a_l] (unless LLSA_NO_ENRICH).
-// One softmax over the whole set, scale 1/sqrt(d); lse in natural log.
+//   - for every enriching level l = l0..L the pooled pairs (kbar_l[j],
+//     vbar_l[j]) for j in idx_l[a_l]; l0 = 1 by default, 2 with
+//     LLSA_ENRICH_COARSE, none with LLSA_NO_ENRICH.
+// One softmax over the whole set, scale 1/sqrt(d); lse in natural log.  With
+// LLSA_SIZE_BIAS a level-l pooled logit gets + ln 16^l, as if the token stood
+// for its 16^l keys.
 //
-// The pooled entries of all levels (L*K of them) form extra tiles of 16,
-// read from the bf16 copy of the pyramid that the pool pass writes.
+// The pooled entries of the enriching levels ((L - l0 + 1)*K of them) form
+// extra tiles of 16, read from the bf16 copy of the pyramid that the pool
+// pass writes.
 //
 // bf16 kernels (MFMA): attn_fwd_u4 (below; K <= 16) gives a wave four
 // sibling query blocks and loads each tile they share once;
@@ -86,41 +90,44 @@ struct Online {
 
 // One step over two 16-entry tiles whose values are staged in LDS at la / lb.
 // na / nb: valid entries (MASK == false: both tiles full).
+// MASK == true (the masked tail): entries of tile a at or past na (b: nb)
+// are masked, and ba / bb add a logit bias to rows 4(lane/16) + r (log2
+// units; pooled tokens under the size-weighted variant).
 template <bool MASK>
 __device__ __forceinline__ void attend_pair(Online& st, bf16x8 bq0, bf16x8 bq1, bf16x8 ka0,
                                             bf16x8 ka1, bf16x8 kb0, bf16x8 kb1,
                                             const unsigned short* la, const unsigned short* lb,
-                                            int na, int nb, float c, int lane)
+                                            int na, int nb, float c, int lane,
+                                            const float* ba = nullptr, const float* bb = nullptr)
 {
     const int gq = lane >> 4;
     const int rr = (lane & 15) >> 2, xx = lane & 3;
     const f32x4 zero = {};
     const f32x4 sa = mfma32(ka1, bq1, mfma32(ka0, bq0, zero));
     const f32x4 sb = mfma32(kb1, bq1, mfma32(kb0, bq0, zero));
-    float ya[4], yb[4];  // raw scores, masked entries at -inf
+    float ya[4], yb[4];  // logits in log2 units, masked entries at -inf
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        ya[r] = (!MASK || 4 * gq + r < na) ? sa[r] : -INFINITY;
-        yb[r] = (!MASK || 4 * gq + r < nb) ? sb[r] : -INFINITY;
+        ya[r] = (!MASK || 4 * gq + r < na) ? (MASK ? fmaf(sa[r], c, ba[r]) : sa[r] * c) : -INFINITY;
+        yb[r] = (!MASK || 4 * gq + r < nb) ? (MASK ? fmaf(sb[r], c, bb[r]) : sb[r] * c) : -INFINITY;
     }
     // this lane's max; the 4-lane reduction is only needed when the
     // reference max must move (rarely, after the first pair)
     const float lm = fmaxf(fmaxf(fmaxf(ya[0], ya[1]), fmaxf(ya[2], ya[3])),
                            fmaxf(fmaxf(yb[0], yb[1]), fmaxf(yb[2], yb[3])));
-    if (__ballot(lm * c > st.m + TAU)) {
-        const float mnew = fmaxf(st.m, max_x4(lm) * c);
+    if (__ballot(lm > st.m + TAU)) {
+        const float mnew = fmaxf(st.m, max_x4(lm));
         const float alpha = fast_exp2(st.m - mnew);
 #pragma unroll
         for (int d = 0; d < 4; ++d) st.acc[d] *= alpha;
         st.den *= alpha;
         st.m = mnew;
     }
-    const float nm = -st.m;
     bf16x8 pp;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        pp[r] = (bf16)fast_exp2(fmaf(ya[r], c, nm));
-        pp[4 + r] = (bf16)fast_exp2(fmaf(yb[r], c, nm));
+        pp[r] = (bf16)fast_exp2(ya[r] - st.m);
+        pp[4 + r] = (bf16)fast_exp2(yb[r] - st.m);
     }
     lds_fence();
 #pragma unroll
@@ -170,13 +177,14 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
     const int myj = lane < g.K ? sel[lane] : 0;
     // pooled entries e = (l-1)*K + slot: their rows in the bf16 pooled arrays
-    const int E = (g.flags & LLSA_NO_ENRICH) ? 0 : g.L * g.K;
+    // pooled entries e = (l - l0) * K + slot for the enriching levels l0..L
+    const int E = g.n_pooled();
     int* ent = (int*)(smem[wv] + 2 * Lay::V_TILE + 2 * Lay::K_TILE);
-    for (int l = 1; l <= (E ? g.L : 0); ++l) {
+    for (int l = g.l0; l <= g.L; ++l) {
         const long a = (long)gh * g.n[l] + (i >> (4 * (l - 1)));
         for (int s0 = 0; s0 < g.K; s0 += 64)
             if (s0 + lane < g.K)
-                ent[(l - 1) * g.K + s0 + lane] =
+                ent[(l - g.l0) * g.K + s0 + lane] =
                     (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * g.K + s0 + lane]);
     }
     lds_fence();
@@ -272,10 +280,18 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
         f.vb1 = ld_bf16x8(vpb + ob8 + vc);
         bf16x8 ka0, ka1, kb0, kb1;
         stage(f, ka0, ka1, kb0, kb1);
-        // valid entries of the two tiles
+        // valid entries of the two tiles, and each row's logit bias: a
+        // pooled entry e is a level l0 + e / K token
         const int na = t < NFT ? BS : max(0, min(BS, E - BS * (t - NFT)));
         const int nb = t + 1 >= NT ? 0 : (t + 1 < NFT ? BS : max(0, min(BS, E - BS * (t + 1 - NFT))));
-        attend_pair<true>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, na, nb, c, lane);
+        float ba[4], bb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ea = BS * (t - NFT) + 4 * gq + r, eb = ea + BS;
+            ba[r] = t < NFT ? 0.f : g.lb2 * (float)(g.l0 + ea / g.K);
+            bb[r] = t + 1 < NFT ? 0.f : g.lb2 * (float)(g.l0 + eb / g.K);
+        }
+        attend_pair<true>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, na, nb, c, lane, ba, bb);
     }
 
     const float lsum = st.den[0];
@@ -315,29 +331,32 @@ struct Q4 {
     float m;
 };
 
+// MASK == true: rows at or past na are masked and every logit gets the
+// tile's bias b2 (log2 units; pooled tiles under the size-weighted variant)
 template <bool MASK>
 __device__ __forceinline__ void tile_step(Q4& st, bf16x8 bq0, bf16x8 bq1, bf16x8 ka0, bf16x8 ka1,
-                                          const bf16x4 (&vt)[4], int na, float c, int lane)
+                                          const bf16x4 (&vt)[4], int na, float c, int lane,
+                                          float b2 = 0.f)
 {
     const int gq = lane >> 4;
     const f32x4 zero = {};
     const f32x4 sa = mfma32(ka1, bq1, mfma32(ka0, bq0, zero));
-    float y[4];
+    float y[4];  // logits in log2 units, masked at -inf
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] = (!MASK || 4 * gq + r < na) ? sa[r] : -INFINITY;
+    for (int r = 0; r < 4; ++r)
+        y[r] = (!MASK || 4 * gq + r < na) ? (MASK ? fmaf(sa[r], c, b2) : sa[r] * c) : -INFINITY;
     const float lm = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
-    if (__ballot(lm * c > st.m + TAU)) {
-        const float mnew = fmaxf(st.m, max_x4(lm) * c);
+    if (__ballot(lm > st.m + TAU)) {
+        const float mnew = fmaxf(st.m, max_x4(lm));
         const float alpha = fast_exp2(st.m - mnew);
 #pragma unroll
         for (int d = 0; d < 4; ++d) st.acc[d] *= alpha;
         st.den *= alpha;
         st.m = mnew;
     }
-    const float nm = -st.m;
     bf16x4 pp;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pp[r] = (bf16)fast_exp2(fmaf(y[r], c, nm));
+    for (int r = 0; r < 4; ++r) pp[r] = (bf16)fast_exp2(y[r] - st.m);
 #pragma unroll
     for (int d = 0; d < 4; ++d) st.acc[d] = mfma16(vt[d], pp, st.acc[d]);
     const bf16 one = (bf16)1.0f;
@@ -374,7 +393,7 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
     const float c = g.scale * LOG2E;
     const long hbase = (long)gh * g.N * D;
     const int K = g.K;
-    const int E = (g.flags & LLSA_NO_ENRICH) ? 0 : g.L * K;
+    const int E = g.n_pooled();
 
     // query operands of the four blocks
     bf16x8 bq0[4], bq1[4];
@@ -415,18 +434,21 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
         L.tab[upos] = my;
         L.tmask[upos] = mask;
     }
-    // pooled tile rows: tile b < 4 = level-1 pooled rows of block i0 + b's
-    // picks; tile 4 + (l - 2) = level-l pooled rows of the common ancestor
-    const int NPT = E ? 4 + (g.L - 1) : 0;
+    // pooled tile rows: when level 1 enriches, tiles 0..3 hold the level-1
+    // pooled rows of blocks i0 + b's picks; then one tile per coarser level
+    // l = 2..L (the common ancestor's picks)
+    const int NT1 = (E && g.l0 == 1) ? 4 : 0;
+    const int NPT = E ? NT1 + (g.L - max(g.l0, 2) + 1) : 0;
+    auto tile_level = [&](int t) { return t < NT1 ? 1 : max(g.l0, 2) + (t - NT1); };
     if (E) {
         for (int t = 0; t < NPT; ++t) {
             if (lane < BS) {
                 const int r = min(lane, K - 1);
                 int row;
-                if (t < 4) {
+                if (t < NT1) {
                     row = (int)(w.prow[0] + (long)gh * g.n[1] + L.arr[t * 16 + r]);
                 } else {
-                    const int l = t - 2;
+                    const int l = tile_level(t);
                     const long a = (long)gh * g.n[l] + (i0 >> (4 * (l - 1)));
                     row = (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * K + r]);
                 }
@@ -467,7 +489,7 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
         T.v1 = ld_bf16x8(w.vb16 + rb);
     };
     // stage a tile, then run it for the blocks in `members`
-    auto run = [&](const Tile& T, int members, int na, auto masked) {
+    auto run = [&](const Tile& T, int members, int na, auto masked, float b2 = 0.f) {
         stage_rows<ROW_A>(L.k, T.k0, T.k1, lane);
         stage_rows<LDS_ROW>(L.v, T.v0, T.v1, lane);
         lds_fence();
@@ -481,7 +503,7 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
         for (int b = 0; b < 4; ++b)
             if ((members >> b) & 1) {
                 if (masked)
-                    tile_step<true>(st[b], bq0[b], bq1[b], ka0, ka1, vt, na, c, lane);
+                    tile_step<true>(st[b], bq0[b], bq1[b], ka0, ka1, vt, na, c, lane, b2);
                 else
                     tile_step<false>(st[b], bq0[b], bq1[b], ka0, ka1, vt, BS, c, lane);
             }
@@ -502,16 +524,18 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
         if (u < U) run(A, __builtin_amdgcn_readlane(tm, u), BS, false);
     }
     if (NPT > 0) {
-        const bool part = K < BS;
+        // masked runs (rows >= K, logit bias of the tile's level)
+        auto members = [&](int t) { return t < NT1 ? 1 << t : 0xF; };
+        auto bias = [&](int t) { return g.lb2 * (float)tile_level(t); };
         load_pooled(A, 0);
         int t = 0;
         for (; t + 2 <= NPT; t += 2) {
             load_pooled(B, t + 1);
-            run(A, t < 4 ? 1 << t : 0xF, K, part);
+            run(A, members(t), K, true, bias(t));
             load_pooled(A, min(t + 2, NPT - 1));
-            run(B, t + 1 < 4 ? 1 << (t + 1) : 0xF, K, part);
+            run(B, members(t + 1), K, true, bias(t + 1));
         }
-        if (t < NPT) run(A, t < 4 ? 1 << t : 0xF, K, part);
+        if (t < NPT) run(A, members(t), K, true, bias(t));
     }
 
 #pragma unroll
@@ -546,8 +570,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
     const int gh = (int)(tg / g.N), t = (int)(tg % g.N);
     const float qc = q[tg * D + lane];
     float m = -INFINITY, l = 0.f, o = 0.f;
-    auto visit = [&](const float* kr, const float* vr) {
-        const float z = wave_sum(qc * kr[lane]) * g.scale;
+    auto visit = [&](const float* kr, const float* vr, float bias) {
+        const float z = wave_sum(qc * kr[lane]) * g.scale + bias;
         if (z > m) {
             const float a = expf(m - z);
             l *= a;
@@ -562,17 +586,17 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
     for (int s = 0; s < g.K; ++s)
         for (int r = 0; r < BS; ++r) {
             const long row = ((long)gh * g.N + (long)sel[s] * BS + r) * D;
-            visit(k + row, v + row);
+            visit(k + row, v + row, 0.f);
         }
-    if (!(g.flags & LLSA_NO_ENRICH))
-        for (int lv = 1; lv <= g.L; ++lv) {
-            const int a = t >> (4 * lv);
-            const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.K;
-            for (int s = 0; s < g.K; ++s) {
-                const long row = ((long)gh * g.n[lv] + sl[s]) * D;
-                visit(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row);
-            }
+    for (int lv = g.l0; lv <= g.L; ++lv) {  // pooled tokens of the enriching levels
+        const int a = t >> (4 * lv);
+        const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.K;
+        const float bias = g.lb2 * (float)lv * LN2;
+        for (int s = 0; s < g.K; ++s) {
+            const long row = ((long)gh * g.n[lv] + sl[s]) * D;
+            visit(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, bias);
         }
+    }
     out[tg * D + lane] = o / l;
     if (lane == 0) lse[tg] = m + logf(l);
 }
@@ -589,7 +613,7 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* ou
                                (const unsigned short*)q, (const unsigned short*)k,
                                (const unsigned short*)v, (unsigned short*)out, lse, g, w);
         } else {
-            auto kern = (g.L * g.K <= 64) ? attn_fwd_bf16<64> : attn_fwd_bf16<MAX_E>;
+            auto kern = (g.n_pooled() <= 64) ? attn_fwd_bf16<64> : attn_fwd_bf16<MAX_E>;
             hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
                                (const unsigned short*)q, (const unsigned short*)k,
                                (const unsigned short*)v, (unsigned short*)out, lse, g, w);

@@ -58,7 +58,7 @@ def bwd(**kw):
     (dict(N=3000), -2), (dict(N=8), -2), (dict(topk=12), -2), (dict(topk=0), -2),
     (dict(levels=0), -2), (dict(levels=4), -2), (dict(N=4096, levels=2, topk=32), -2),
     (dict(B=0), -2), (dict(H=-1), -2),
-    (dict(d=128), -3), (dict(block_size=32), -3), (dict(dtype=7), -3), (dict(flags=2), -3),
+    (dict(d=128), -3), (dict(block_size=32), -3), (dict(dtype=7), -3), (dict(flags=8), -3),
     (dict(levels=7, N=1 << 30), -3), (dict(N=131072, topk=16), -3), (dict(topk=128, N=65536, levels=2), -3),
     (dict(B=1 << 16, H=1 << 4, N=4096), -3), (dict(N=1 << 24, levels=3, topk=16), -3),
     (dict(workspace=None), -4), (dict(ws_bytes=100), -4),

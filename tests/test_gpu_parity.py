@@ -80,6 +80,26 @@ def test_no_enrichment(w):
     _full_check(w, flags=oracle.NO_ENRICH)
 
 
+_COARSE, _SIZE = oracle.ENRICH_COARSE, oracle.SIZE_BIAS
+_VARIANT_CASES = [
+    (SMALL[0], _SIZE),  # fp32, one level
+    (SMALL[2], _SIZE),  # bf16, one level (four-block kernel)
+    (SMALL[1], _COARSE), (SMALL[1], _SIZE), (SMALL[1], _COARSE | _SIZE),
+    (SMALL[4], _COARSE), (SMALL[4], _SIZE), (SMALL[4], _COARSE | _SIZE),
+    (SMALL[5], _COARSE | _SIZE),  # three levels, topk 1
+    (SMALL[6], _COARSE),  # one level: coarse enrichment adds nothing
+    # topk 32 over two levels: the one-block bf16 kernels
+    (small("grid128_bf16_l2_k32", 1, 1, 128, "bf16", 2, 32), _COARSE | _SIZE),
+    (small("grid128_bf16_l2_k32", 1, 1, 128, "bf16", 2, 32), _SIZE),
+]
+
+
+@pytest.mark.parametrize("w,flags", _VARIANT_CASES,
+                         ids=["%s_f%d" % (w.name, f) for w, f in _VARIANT_CASES])
+def test_enrichment_variants(w, flags):
+    _full_check(w, flags=flags)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_zorder_gather_bit_exact(dtype):
     import torch
