@@ -44,6 +44,9 @@ def _load():
         lib.orc_morton.argtypes = [I, I, I]
         lib.orc_morton.restype = I
         lib.orc_zorder.argtypes = [P, P, I, I, I, ctypes.c_int]
+        lib.orc_grid_index.argtypes = [I] * 6
+        lib.orc_grid_index.restype = I
+        lib.orc_grid_order.argtypes = [P, P, I, I, I, I, I, ctypes.c_int]
         lib.orc_pool.argtypes = [P, I, I, I, I, ctypes.c_int, P]
         lib.orc_select_level.argtypes = [P, P, P, I, I, I, I, I, D, P, P]
         lib.orc_select.argtypes = [P, P, I, I, I, I, ctypes.c_int, I, D, P, P]
@@ -52,7 +55,7 @@ def _load():
         lib.orc_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, ctypes.c_int,
                                      I, D, ctypes.c_uint, P, I, P, I, P, P, P]
         lib.orc_transpose.argtypes = [P, I, I, I, P, P]
-        for f in ("orc_zorder", "orc_pool", "orc_select_level", "orc_select",
+        for f in ("orc_zorder", "orc_grid_order", "orc_pool", "orc_select_level", "orc_select",
                   "orc_forward", "orc_backward", "orc_transpose"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -101,6 +104,20 @@ def zorder(x, side: int, inverse: bool = False):
     assert n == side * side
     y = np.empty_like(x)
     _load().orc_zorder(_p(x), _p(y), outer, side, inner, int(inverse))
+    return y
+
+
+def grid_index(frames: int, height: int, width: int, t: int, y: int, x: int) -> int:
+    return int(_load().orc_grid_index(frames, height, width, t, y, x))
+
+
+def grid_order(x, frames: int, height: int, width: int, inverse: bool = False):
+    """x [outer, frames*height*width, inner] (raster order) -> grid order (or back)."""
+    x = _f64(x)
+    outer, n, inner = x.shape
+    assert n == frames * height * width
+    y = np.empty_like(x)
+    _load().orc_grid_order(_p(x), _p(y), outer, frames, height, width, inner, int(inverse))
     return y
 
 

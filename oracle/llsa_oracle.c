@@ -64,6 +64,50 @@ void orc_zorder(const double* src, double* dst, int64_t outer, int64_t side,
         }
 }
 
+/* Grid order for images that are not square powers of two and for video
+ * ([P1] reorders images "or videos" by a quadtree; the same rule in three
+ * dimensions is an octree).  A grid of T frames of H x W cells is cut into
+ * tiles of S x S cells (S x S x S cells when T > 1), S the largest power of
+ * two that divides every side; tiles come in raster order (frame, row,
+ * column), and inside a tile the cells come in Morton order with, at every
+ * scale, the frame bit above the row bit above the column bit.  A square
+ * power-of-two image is a single tile, so the order is orc_morton's. */
+static int64_t pow2_part(int64_t n) { return n & -n; }
+
+int64_t orc_grid_index(int64_t T, int64_t H, int64_t W, int64_t t, int64_t y, int64_t x)
+{
+    int64_t S = pow2_part(H) < pow2_part(W) ? pow2_part(H) : pow2_part(W);
+    const int video = T > 1;
+    if (video && pow2_part(T) < S) S = pow2_part(T);
+    const int64_t tile = ((video ? t / S : 0) * (H / S) + y / S) * (W / S) + x / S;
+    const int64_t cells = video ? S * S * S : S * S;
+    int64_t code = 0, w = 1;
+    for (int64_t s = 1; s < S; s <<= 1) {
+        const int64_t tb = (t & s) ? 1 : 0, yb = (y & s) ? 1 : 0, xb = (x & s) ? 1 : 0;
+        if (video) {
+            code += (4 * tb + 2 * yb + xb) * w;
+            w *= 8;
+        } else {
+            code += (2 * yb + xb) * w;
+            w *= 4;
+        }
+    }
+    return tile * cells + code;
+}
+
+void orc_grid_order(const double* src, double* dst, int64_t outer, int64_t T, int64_t H,
+                    int64_t W, int64_t inner, int inverse)
+{
+    const int64_t n = T * H * W;
+    for (int64_t o = 0; o < outer; ++o)
+        for (int64_t r = 0; r < n; ++r) {  /* r: raster cell (frame, row, column) */
+            const int64_t z = orc_grid_index(T, H, W, r / (H * W), (r / W) % H, r % W);
+            const double* s = src + (o * n + (inverse ? z : r)) * inner;
+            double* t = dst + (o * n + (inverse ? r : z)) * inner;
+            memcpy(t, s, (size_t)inner * sizeof(double));
+        }
+}
+
 /* ------------------------------------------------------------------ pool */
 
 /* [P2] hierarchical compression: level l = block means of level l-1. */

@@ -57,6 +57,19 @@ int64_t orc_morton(int64_t side, int64_t y, int64_t x);
 void orc_zorder(const double* src, double* dst, int64_t outer, int64_t side,
                 int64_t inner, int inverse);
 
+/* Grid order of T frames of H x W cells (T = 1: an image): tiles of the
+ * largest power-of-two square (cube when T > 1) dividing every side, in raster
+ * order; Morton order inside a tile, frame bit above row bit above column bit
+ * ([P1], quadtree reordering, extended to rectangles and video).  Returns the
+ * position of cell (t, y, x); for a square power-of-two image it equals
+ * orc_morton. */
+int64_t orc_grid_index(int64_t T, int64_t H, int64_t W, int64_t t, int64_t y, int64_t x);
+
+/* Gather src [outer][T*H*W][inner] (raster order) into dst in grid order;
+ * inverse != 0 undoes it. */
+void orc_grid_order(const double* src, double* dst, int64_t outer, int64_t T, int64_t H,
+                    int64_t W, int64_t inner, int inverse);
+
 /* Block mean-pool pyramid of x [G][N][d]: level l token i is the mean of the
  * bs level-(l-1) tokens bs*i .. bs*i+bs-1 ([P2] hierarchical compression,
  * [P3] block-wise representation). */
