@@ -2,7 +2,7 @@
 """LLSA hot-path benchmark on one MI355X.
 
 One step = the whole hot path over one batch of seeded synthetic input already
-resident in HBM: Z-order gather of Q, K, V (raster -> quadtree order), the
+resident in HBM: grid-order gather of Q, K, V (raster -> quadtree order), the
 forward (pool pyramid, hierarchical Top-K, sparse attention with enrichment)
 and the backward (index transpose, dQ, pooled-token gradients, dK/dV), all
 through the C ABI of libllsa.so on one stream.  Prints ONE JSON line.
@@ -31,8 +31,19 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 FP32_PEAK_TFLOPS = 157.3
-METRIC = "LLSA fwd & fwd+bwd ms and TFLOP/s at N=65536 (256x256), d=64, bf16"
 DEFAULT_WORKLOAD = "grid256_bf16_l2_k16"
+
+
+def grid_name(w):
+    return ("%dx%dx%d" % (w.frames, w.rows, w.side) if w.frames > 1
+            else "%dx%d" % (w.rows, w.side))
+
+
+def metric(w):
+    """The headline metric, named for the workload's size (for the default
+    workload: 'LLSA fwd & fwd+bwd ms and TFLOP/s at N=65536 (256x256), d=64, bf16')."""
+    return "LLSA fwd & fwd+bwd ms and TFLOP/s at N=%d (%s), d=%d, %s" % (
+        w.N, grid_name(w), w.d, w.dtype)
 
 
 def flops(w):
@@ -189,9 +200,8 @@ def cpu_baseline(w, inp, min_s=10.0):
     head = lambda a, h: a.reshape(G, N, d)[h:h + 1]
     done, dt = 0, 0.0
     while done < G and dt < min_s:
-        q = oracle.zorder(head(inp["q64"], done), w.side)
-        k = oracle.zorder(head(inp["k64"], done), w.side)
-        v = oracle.zorder(head(inp["v64"], done), w.side)
+        q, k, v = (oracle.grid_order(head(inp[n + "64"], done), w.frames, w.rows, w.side)
+                   for n in ("q", "k", "v"))
         do = head(inp["do64"], done)
         t0 = time.perf_counter()
         oracle.run(q, k, v, 16, w.levels, w.topk, dout=do)
@@ -299,7 +309,7 @@ def main():
     def run_stage(name):
         if name == "zorder":
             for src, dst in ((q_r, q), (k_r, k), (v_r, v)):
-                lib.llsa_zorder(src, dst, B * H, w.side, row_bytes, 0, sh)
+                lib.llsa_grid_order(src, dst, B * H, w.frames, w.rows, w.side, row_bytes, 0, sh)
         elif name in ("pool", "select", "attn_fwd"):
             part = {"pool": lib.PART_POOL, "select": lib.PART_SELECT, "attn_fwd": lib.PART_ATTN}[name]
             lib.llsa_forward_part(part, q, k, v, out, lse, *shape)
@@ -372,12 +382,12 @@ def main():
                 "mfma_frac": round(kflops[kname] / (kms * 1e-3) / 1e12 / peak_mfma, 4)}
 
     res = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": metric(w), "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "block_size": 16,
-                   "topk": K, "levels": L, "grid": "%dx%d" % (w.side, w.side),
+                   "topk": K, "levels": L, "grid": grid_name(w),
                    "sigma_px": w.sigma, "seed": w.seed},
         "fwd_ms": round(fwd_ms, 5), "fwd_tflops": round(f["fwd"] / (fwd_ms * 1e-3) / 1e12, 3),
         "fwdbwd_ms": round(fwdbwd_ms, 5),

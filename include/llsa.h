@@ -57,9 +57,10 @@ extern "C" {
 /* error codes */
 #define LLSA_OK 0
 #define LLSA_ERR_NULL (-1)        /* a required pointer is NULL */
-#define LLSA_ERR_SHAPE (-2)       /* N or topk not a power of two, levels < 1,
-                                     16^levels does not divide N,
-                                     topk > N / 16^levels, B or H < 1 */
+#define LLSA_ERR_SHAPE (-2)       /* levels < 1, 16^levels does not divide N,
+                                     topk < 1 or topk > N / 16^levels,
+                                     B or H < 1 (N and topk need not be
+                                     powers of two) */
 #define LLSA_ERR_UNSUPPORTED (-3) /* d != 64, block_size != 16, unknown dtype
                                      or flags, levels > LLSA_MAX_LEVELS,
                                      coarsest block count > 4096, topk > 64,
@@ -112,6 +113,23 @@ int llsa_workspace_layout(int B, int H, int N, int d, int block_size, int topk,
  * of 4.  Errors: LLSA_ERR_NULL, LLSA_ERR_SHAPE, LLSA_ERR_HIP. */
 int llsa_zorder(const void* src, void* dst, long long outer, int side, int inner_bytes,
                 int inverse, void* stream);
+
+/* Grid order: the quadtree permutation extended to images whose sides are not
+ * equal powers of two and, as an octree, to video (README: images or videos
+ * are reordered so that nearby cells share blocks).  The grid of `frames`
+ * frames of height x width cells (frames == 1: an image) is cut into tiles of
+ * S x S cells (S x S x S when frames > 1), S the largest power of two that
+ * divides every side; tiles are taken in raster order (frame, row, column)
+ * and the cells of a tile in Morton order with, at every scale, the frame bit
+ * above the row bit above the column bit.  A square power-of-two image gives
+ * llsa_zorder's order.  With 4^l dividing the tile side, every aligned run of
+ * 16^l tokens of an image is a 4^l x 4^l patch.
+ * src, dst: device buffers [outer][frames*height*width][inner_bytes], not
+ * overlapping; inverse == 0: raster -> grid order, else the inverse.
+ * Each side in [1, 2^15], frames*height*width <= 2^30, inner_bytes a positive
+ * multiple of 4.  Errors: LLSA_ERR_NULL, LLSA_ERR_SHAPE, LLSA_ERR_HIP. */
+int llsa_grid_order(const void* src, void* dst, long long outer, int frames, int height,
+                    int width, int inner_bytes, int inverse, void* stream);
 
 /* LLSA forward: pyramid, hierarchical Top-K (scores s*<qbar, kbar> in fp32,
  * s = 1/sqrt(d), ties to the lower block index) and sparse attention with

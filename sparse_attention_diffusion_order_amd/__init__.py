@@ -18,9 +18,10 @@ import re
 __all__ = [
     "LlsaError", "F32", "BF16", "NO_ENRICH", "ENRICH_COARSE", "SIZE_BIAS", "PART_POOL", "PART_SELECT", "PART_ATTN",
     "PART_TRANSPOSE", "PART_DQ", "PART_ENRICH", "PART_DKDV", "library_path", "load", "exported_names",
-    "llsa_workspace_bytes", "llsa_workspace_layout", "llsa_zorder", "llsa_forward",
+    "llsa_workspace_bytes", "llsa_workspace_layout", "llsa_zorder", "llsa_grid_order",
+    "llsa_forward",
     "llsa_backward", "llsa_forward_part", "llsa_backward_part", "llsa_strerror",
-    "forward", "backward", "zorder",
+    "forward", "backward", "zorder", "grid_order",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +72,8 @@ def load():
     lib.llsa_workspace_layout.restype = I
     lib.llsa_zorder.argtypes = [P, P, ctypes.c_longlong, I, I, I, P]
     lib.llsa_zorder.restype = I
+    lib.llsa_grid_order.argtypes = [P, P, ctypes.c_longlong, I, I, I, I, I, P]
+    lib.llsa_grid_order.restype = I
     fwd = [P] * 5 + shape + [U, P, S, P]
     bwd = [P] * 9 + shape + [U, P, S, P]
     lib.llsa_forward.argtypes = fwd
@@ -137,6 +140,11 @@ def llsa_workspace_layout(B, H, N, d, block_size, topk, levels, dtype) -> dict:
 def llsa_zorder(src, dst, outer, side, inner_bytes, inverse=0, stream=None):
     _check(load().llsa_zorder(_ptr(src), _ptr(dst), outer, side, inner_bytes, int(inverse),
                               _stream(stream)), "llsa_zorder")
+
+
+def llsa_grid_order(src, dst, outer, frames, height, width, inner_bytes, inverse=0, stream=None):
+    _check(load().llsa_grid_order(_ptr(src), _ptr(dst), outer, frames, height, width,
+                                  inner_bytes, int(inverse), _stream(stream)), "llsa_grid_order")
 
 
 def llsa_forward(q, k, v, out, lse, B, H, N, d, block_size, topk, levels, dtype, flags,
@@ -225,4 +233,18 @@ def zorder(x, side: int, inverse: bool = False, stream=None):
     y = torch.empty_like(x)
     outer = x.numel() // (side * side * x.shape[-1])
     llsa_zorder(x, y, outer, side, x.shape[-1] * x.element_size(), int(inverse), stream)
+    return y
+
+
+def grid_order(x, frames: int, height: int, width: int, inverse: bool = False, stream=None):
+    """x [..., frames*height*width, C] (contiguous, raster order) -> grid-ordered copy
+    (or its inverse); frames == 1 for an image."""
+    import torch
+    n = frames * height * width
+    if not x.is_contiguous() or x.shape[-2] != n:
+        raise ValueError("x must be contiguous with frames*height*width tokens on dim -2")
+    y = torch.empty_like(x)
+    outer = x.numel() // (n * x.shape[-1])
+    llsa_grid_order(x, y, outer, frames, height, width, x.shape[-1] * x.element_size(),
+                    int(inverse), stream)
     return y

@@ -22,8 +22,7 @@ int validate(int B, int H, int N, int d, int block_size, int topk, int levels, i
     if (d != D || block_size != BS || (dtype != LLSA_F32 && dtype != LLSA_BF16) ||
         (flags & ~LLSA_KNOWN_FLAGS))
         return LLSA_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || N < BS || !pow2(N) || topk < 1 || !pow2(topk) || levels < 1)
-        return LLSA_ERR_SHAPE;
+    if (B < 1 || H < 1 || N < BS || topk < 1 || levels < 1) return LLSA_ERR_SHAPE;
     if (levels > MAX_L) return LLSA_ERR_UNSUPPORTED;
     long long span = 1;
     for (int l = 0; l < levels; ++l) span *= BS;
@@ -225,6 +224,19 @@ int llsa_zorder(const void* src, void* dst, long long outer, int side, int inner
                                 (hipStream_t)stream));
 }
 
+int llsa_grid_order(const void* src, void* dst, long long outer, int frames, int height,
+                    int width, int inner_bytes, int inverse, void* stream)
+{
+    if (!src || !dst) return LLSA_ERR_NULL;
+    const int lim = 1 << 15;
+    if (outer < 1 || frames < 1 || height < 1 || width < 1 || frames > lim || height > lim ||
+        width > lim || (long long)frames * height * width > (1ll << 30) || inner_bytes < 4 ||
+        inner_bytes % 4)
+        return LLSA_ERR_SHAPE;
+    return hip_rc(launch_grid_order(src, dst, outer, frames, height, width, inner_bytes, inverse,
+                                    (hipStream_t)stream));
+}
+
 int llsa_forward_part(int part, const void* q, const void* k, const void* v, void* out,
                       float* lse, int B, int H, int N, int d, int block_size, int topk,
                       int levels, int dtype, unsigned flags, void* workspace, size_t ws_bytes,
@@ -290,8 +302,9 @@ const char* llsa_strerror(int code)
     case LLSA_OK: return "ok";
     case LLSA_ERR_NULL: return "a required pointer is NULL";
     case LLSA_ERR_SHAPE:
-        return "bad shape: N and topk must be powers of two, 16^levels must divide N and "
-               "topk <= N/16^levels";
+        return "bad shape: 16^levels must divide N, 1 <= topk <= N/16^levels, B, H, "
+               "levels >= 1 (grid order: sides in [1, 2^15], at most 2^30 cells, "
+               "inner_bytes a positive multiple of 4)";
     case LLSA_ERR_UNSUPPORTED:
         return "unsupported: needs d=64, block_size=16, dtype f32/bf16, known flags, "
                "levels<=6, at most 4096 coarsest blocks, topk<=64, B*H*N<2^31";

@@ -205,6 +205,8 @@ __device__ __forceinline__ int xcd_block(int b, int nb)
 // ------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 
+hipError_t launch_grid_order(const void* src, void* dst, long long outer, int frames, int height,
+                             int width, int inner_bytes, int inverse, hipStream_t st);
 hipError_t launch_zorder(const void* src, void* dst, long long outer, int side, int inner_bytes,
                          int inverse, hipStream_t st);
 hipError_t launch_pool(const void* q, const void* k, const void* v, int dtype, const Geo& g,

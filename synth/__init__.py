@@ -9,10 +9,11 @@ side applies its own Z-order permutation.
 Recipe (stand-in for the pixel-space DiT activations of the LLSA README, page 1
 "experiments", whose FFHQ data and checkpoints are not available here):
   1. rng = numpy.random.default_rng(seed)
-  2. float64 standard normals [B, H, side, side, d] for Q, then K, then V,
-     then dO with shape [B, H, N, d] (dO is not smoothed)
-  3. Q, K, V: separable normalised Gaussian blur over the two grid axes,
-     sigma px, radius ceil(4 sigma), periodic boundary
+  2. float64 standard normals [B, H, rows, side, d] for Q, then K, then V
+     ([B, H, frames, rows, side, d] for video), then dO with shape [B, H, N, d]
+     (dO is not smoothed); rows = side unless the grid is a rectangle
+  3. Q, K, V: separable normalised Gaussian blur over the grid axes (frames
+     too, for video), sigma cells, radius ceil(4 sigma), periodic boundary
   4. each of Q, K, V divided by its own standard deviation
   5. rounding to the storage dtype (fp32, or bf16 round-to-nearest-even)
 """
@@ -41,18 +42,25 @@ class Workload:
     sigma: float
     seed: int = 0
     block_size: int = 16
+    frames: int = 1     # > 1: video of `frames` frames
+    height: int = 0     # rows of the grid; 0: square (rows = side)
+
+    @property
+    def rows(self) -> int:
+        return self.height or self.side
 
     @property
     def N(self) -> int:
-        return self.side * self.side
+        return self.frames * self.rows * self.side
 
     @property
     def G(self) -> int:
         return self.B * self.H
 
 
-# The five workloads of the LLSA hot path: a small fp32 correctness case, then
-# bf16 pixel grids of 64^2, 128^2, 256^2 (headline) and 512^2 tokens.
+# The workloads of the LLSA hot path: a small fp32 correctness case, bf16 pixel
+# grids of 64^2, 128^2, 256^2 (headline) and 512^2 tokens, and two grids the
+# README's power-of-two limits exclude (video, a rectangle).
 WORKLOADS = {
     w.name: w for w in [
         Workload("grid32_f32_l1_k8", 1, 1, 32, 64, "f32", 1, 8, 2.0),
@@ -60,6 +68,10 @@ WORKLOADS = {
         Workload("grid128_bf16_l2_k16", 2, 6, 128, 64, "bf16", 2, 16, 2.0),
         Workload("grid256_bf16_l2_k16", 1, 6, 256, 64, "bf16", 2, 16, 4.0),
         Workload("grid512_bf16_l3_k16", 1, 6, 512, 64, "bf16", 3, 16, 2.0),
+        # the same token budget as 256^2 as 16 frames of 64^2 (octree order),
+        # and a 192 x 320 image (N = 61440, not a power of two)
+        Workload("video16x64x64_bf16_l2_k16", 1, 6, 64, 64, "bf16", 2, 16, 2.0, frames=16),
+        Workload("rect192x320_bf16_l2_k16", 1, 6, 320, 64, "bf16", 2, 16, 4.0, height=192),
     ]
 }
 
@@ -73,7 +85,7 @@ def gaussian_kernel_1d(sigma: float) -> np.ndarray:
 
 
 def blur_periodic(x: np.ndarray, sigma: float, axes=(-3, -2)) -> np.ndarray:
-    """Separable periodic Gaussian blur over two grid axes (via FFT).
+    """Separable periodic Gaussian blur over the given grid axes (via FFT).
 
     The taps are wrapped onto the periodic grid, so this is an exact circular
     convolution (up to FFT rounding) even when the grid is smaller than the
@@ -129,11 +141,14 @@ def make_inputs(w: Workload, want_grad: bool = True) -> dict:
     ("q64" etc.).
     """
     rng = np.random.default_rng(w.seed)
-    shape = (w.B, w.H, w.side, w.side, w.d)
+    if w.frames > 1:
+        shape, axes = (w.B, w.H, w.frames, w.rows, w.side, w.d), (-4, -3, -2)
+    else:
+        shape, axes = (w.B, w.H, w.rows, w.side, w.d), (-3, -2)
     out = {}
     for name in ("q", "k", "v"):
         x = rng.standard_normal(shape)
-        x = blur_periodic(x, w.sigma)
+        x = blur_periodic(x, w.sigma, axes)
         x = x / x.std()
         x = x.reshape(w.B, w.H, w.N, w.d)
         out[name], out[name + "64"] = _cast(x, w.dtype)

@@ -40,14 +40,14 @@ def ws_array(ws, off, count, np_dtype):
 
 
 def gpu_run(w, inp, flags=0, backward=True, q64=None):
-    """HIP path on raster-order inputs: Z-order gather, forward, backward.
+    """HIP path on raster-order inputs: grid-order gather, forward, backward.
     Returns numpy float64 results in Z-order plus workspace contents."""
     import torch
     import sparse_attention_diffusion_order_amd as lib
     B, H, N, d = w.B, w.H, w.N, w.d
     dt = lib.BF16 if w.dtype == "bf16" else lib.F32
     q_r, k_r, v_r = (to_device(inp[n], w.dtype) for n in ("q", "k", "v"))
-    q, k, v = (lib.zorder(x, w.side) for x in (q_r, k_r, v_r))
+    q, k, v = (lib.grid_order(x, w.frames, w.rows, w.side) for x in (q_r, k_r, v_r))
     out, lse, ws = lib.forward(q, k, v, w.topk, w.levels, flags)
     res = {"q": q, "k": k, "v": v, "out_t": out, "lse_t": lse, "ws": ws}
     if backward:
@@ -81,11 +81,11 @@ def gpu_run(w, inp, flags=0, backward=True, q64=None):
 
 
 def oracle_inputs(w, inp):
-    """Exact float64 values of the stored inputs, Z-ordered by the oracle."""
+    """Exact float64 values of the stored inputs, grid-ordered by the oracle."""
     G, N, d = w.G, w.N, w.d
     z = {}
     for n in ("q", "k", "v"):
-        z[n] = oracle.zorder(inp[n + "64"].reshape(G, N, d), w.side)
+        z[n] = oracle.grid_order(inp[n + "64"].reshape(G, N, d), w.frames, w.rows, w.side)
     z["do"] = inp["do64"].reshape(G, N, d) if "do64" in inp else None
     return z
 

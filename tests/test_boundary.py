@@ -1,8 +1,9 @@
 """Host-side tests of the C ABI (no GPU needed).
 
 The library must load, export every function declared in include/llsa.h, and
-reject bad arguments before any HIP call (README usage notes: non-causal only,
-power-of-two token count and top-k).
+reject bad arguments before any HIP call.  The README's usage notes limit the
+token count and top-k to powers of two; this library accepts any N that
+16^levels divides and any topk up to the coarsest block count.
 """
 import ctypes
 import os
@@ -20,7 +21,8 @@ BAD = 16  # a non-null address that validation must never dereference
 
 def test_exports_every_declared_function():
     names = L.exported_names()
-    assert {"llsa_forward", "llsa_backward", "llsa_zorder", "llsa_workspace_bytes",
+    assert {"llsa_forward", "llsa_backward", "llsa_zorder", "llsa_grid_order",
+            "llsa_workspace_bytes",
             "llsa_workspace_layout", "llsa_strerror", "llsa_forward_part",
             "llsa_backward_part"} <= set(names)
     lib = L.load()
@@ -55,7 +57,8 @@ def bwd(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(lse=None), -1),
-    (dict(N=3000), -2), (dict(N=8), -2), (dict(topk=12), -2), (dict(topk=0), -2),
+    (dict(N=3000), -2), (dict(N=8), -2), (dict(topk=257), -2), (dict(topk=0), -2),
+    (dict(N=48 * 80, levels=2, topk=16), -2),
     (dict(levels=0), -2), (dict(levels=4), -2), (dict(N=4096, levels=2, topk=32), -2),
     (dict(B=0), -2), (dict(H=-1), -2),
     (dict(d=128), -3), (dict(block_size=32), -3), (dict(dtype=7), -3), (dict(flags=8), -3),
@@ -79,6 +82,25 @@ def test_zorder_validation():
     assert lib.llsa_zorder(BAD, BAD, 1, 12, 128, 0, None) == -2
     assert lib.llsa_zorder(BAD, BAD, 1, 16, 6, 0, None) == -2
     assert lib.llsa_zorder(BAD, BAD, 0, 16, 128, 0, None) == -2
+
+
+def test_grid_order_validation():
+    lib = L.load()
+    g = lib.llsa_grid_order
+    assert g(None, BAD, 1, 1, 16, 16, 128, 0, None) == -1
+    assert g(BAD, None, 1, 1, 16, 16, 128, 0, None) == -1
+    assert g(BAD, BAD, 0, 1, 16, 16, 128, 0, None) == -2
+    assert g(BAD, BAD, 1, 0, 16, 16, 128, 0, None) == -2
+    assert g(BAD, BAD, 1, 1, 0, 16, 128, 0, None) == -2
+    assert g(BAD, BAD, 1, 1, 16, 1 << 16, 128, 0, None) == -2
+    assert g(BAD, BAD, 1, 1 << 10, 1 << 11, 1 << 10, 128, 0, None) == -2  # > 2^30 cells
+    assert g(BAD, BAD, 1, 1, 16, 16, 6, 0, None) == -2
+
+
+@pytest.mark.parametrize("N,K,Lv", [(48 * 80, 8, 2), (3 * 256, 3, 1), (15 * 256, 5, 2),
+                                    (4 * 32 * 32, 12, 2), (3 * 4096, 3, 3)])
+def test_shapes_beyond_powers_of_two_are_accepted(N, K, Lv):
+    assert L.llsa_workspace_bytes(1, 2, N, 64, 16, K, Lv, L.BF16) > 0
 
 
 def test_strerror():

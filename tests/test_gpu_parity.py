@@ -124,6 +124,50 @@ def test_zorder_gather_bit_exact(dtype):
                                   oracle.zorder(y.cpu().numpy(), 4).astype(np.float32))
 
 
+@pytest.mark.parametrize("T,Hh,Ww", [(1, 48, 80), (1, 16, 64), (1, 12, 20), (1, 3, 5),
+                                     (4, 32, 32), (3, 8, 24), (2, 16, 16), (8, 4, 4)])
+@pytest.mark.parametrize("dtype,width", [("f32", 64), ("bf16", 64), ("f32", 3), ("f32", 2),
+                                         ("bf16", 2)])  # rows of 256, 128, 12, 8, 4 bytes
+def test_grid_order_bit_exact(T, Hh, Ww, dtype, width):
+    import torch
+    import sparse_attention_diffusion_order_amd as lib
+    n = T * Hh * Ww
+    rng = np.random.default_rng(n + width)
+    for dt in ((torch.float32,) if dtype == "f32" else (torch.bfloat16,)):
+        x = torch.from_numpy(rng.standard_normal((2, n, width))).to(dt).cuda()
+        z = lib.grid_order(x, T, Hh, Ww)
+        back = lib.grid_order(z, T, Hh, Ww, inverse=True)
+        torch.cuda.synchronize()
+        x64 = x.float().cpu().numpy().astype(np.float64)
+        np.testing.assert_array_equal(z.float().cpu().numpy(), oracle.grid_order(x64, T, Hh, Ww))
+        assert torch.equal(back.view(torch.int16) if dt == torch.bfloat16 else back,
+                           x.view(torch.int16) if dt == torch.bfloat16 else x)
+
+
+def _grid(name, dtype, L, K, side, height=0, frames=1, B=1, H=2, sigma=2.0):
+    return W(name, B, H, side, 64, dtype, L, K, sigma, 0, 16, frames, height)
+
+
+# shapes the README's power-of-two limits exclude: rectangles, odd top-k,
+# block counts that are not multiples of 4 or 16, and video in octree order
+_BEYOND = [
+    _grid("rect48x80_bf16_l2_k8", "bf16", 2, 8, 80, height=48),     # N = 3840, 15 coarse blocks
+    _grid("rect12x20_bf16_l1_k4", "bf16", 1, 4, 20, height=12),     # 15 blocks: one-block kernels
+    _grid("rect12x20_f32_l1_k3", "f32", 1, 3, 20, height=12),
+    _grid("grid64_bf16_l1_k12", "bf16", 1, 12, 64),                 # topk 12
+    _grid("grid32_f32_l2_k3", "f32", 2, 3, 32),                     # topk 3 of 4 coarse blocks
+    _grid("rect96x128_bf16_l3_k2", "bf16", 3, 2, 128, height=96, H=1),  # N = 12288, 3 coarse
+    _grid("video4x32x32_bf16_l2_k8", "bf16", 2, 8, 32, frames=4),   # octree, N = 4096
+    _grid("video2x16x16_f32_l1_k4", "f32", 1, 4, 16, frames=2, H=1),
+    _grid("video3x16x16_bf16_l2_k2", "bf16", 2, 2, 16, frames=3),   # 3 coarse blocks
+]
+
+
+@pytest.mark.parametrize("w", _BEYOND, ids=lambda w: w.name)
+def test_shapes_beyond_powers_of_two(w):
+    _full_check(w)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_all_blocks_no_enrichment_equals_dense(dtype):
     w = small("dense", 1, 2, 32, dtype, 1, 64)  # K = n_1 = 64: every block
@@ -219,7 +263,8 @@ def _needed_qblocks(w, idx, kblocks):
 
 
 @pytest.mark.parametrize("name", ["grid128_bf16_l2_k16", "grid256_bf16_l2_k16",
-                                  "grid512_bf16_l3_k16"])
+                                  "grid512_bf16_l3_k16", "video16x64x64_bf16_l2_k16",
+                                  "rect192x320_bf16_l2_k16"])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration: selection
     and transposes checked in full, outputs and gradients on sampled blocks of
