@@ -13,7 +13,8 @@ Recipe (stand-in for the pixel-space DiT activations of the LLSA README, page 1
      ([B, H, frames, rows, side, d] for video), then dO with shape [B, H, N, d]
      (dO is not smoothed); rows = side unless the grid is a rectangle
   3. Q, K, V: separable normalised Gaussian blur over the grid axes (frames
-     too, for video), sigma cells, radius ceil(4 sigma), periodic boundary
+     too, for video), sigma cells, radius ceil(4 sigma), periodic boundary;
+     sigma 0 leaves them white
   4. each of Q, K, V divided by its own standard deviation
   5. rounding to the storage dtype (fp32, or bf16 round-to-nearest-even)
 """
@@ -148,7 +149,8 @@ def make_inputs(w: Workload, want_grad: bool = True) -> dict:
     out = {}
     for name in ("q", "k", "v"):
         x = rng.standard_normal(shape)
-        x = blur_periodic(x, w.sigma, axes)
+        if w.sigma > 0:  # sigma 0: white noise (the largest shapes, where a blur is costly)
+            x = blur_periodic(x, w.sigma, axes)
         x = x / x.std()
         x = x.reshape(w.B, w.H, w.N, w.d)
         out[name], out[name + "64"] = _cast(x, w.dtype)

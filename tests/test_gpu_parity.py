@@ -262,14 +262,23 @@ def _needed_qblocks(w, idx, kblocks):
     return np.array(sorted(need), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["grid128_bf16_l2_k16", "grid256_bf16_l2_k16",
-                                  "grid512_bf16_l3_k16", "video16x64x64_bf16_l2_k16",
-                                  "rect192x320_bf16_l2_k16"])
-def test_full_size_sampled(name):
+_SAMPLED = [synth.WORKLOADS[n] for n in (
+    "grid128_bf16_l2_k16", "grid256_bf16_l2_k16", "grid512_bf16_l3_k16",
+    "video16x64x64_bf16_l2_k16", "rect192x320_bf16_l2_k16")] + [
+    # the deepest pyramids N <= 2^23 allows: 4 and 5 levels down to one block
+    _grid("grid256_bf16_l4_k1", "bf16", 4, 1, 256, H=1),
+    _grid("grid1024_bf16_l5_k1", "bf16", 5, 1, 1024, H=1),
+    # the largest N the boundary accepts (2^23 tokens, 1 GiB per head and
+    # tensor), two heads; white inputs keep the generator fast
+    _grid("rect2048x4096_bf16_l3_k16", "bf16", 3, 16, 4096, height=2048, H=2, sigma=0.0),
+]
+
+
+@pytest.mark.parametrize("w", _SAMPLED, ids=lambda w: w.name)
+def test_full_size_sampled(w):
     """Full-size workloads in the benchmark's launch configuration: selection
     and transposes checked in full, outputs and gradients on sampled blocks of
     head 0 (the oracle computes them one by one)."""
-    w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w)
     gpu = gpu_run(w, inp)
     z = oracle_inputs(w, inp)
