@@ -48,12 +48,12 @@ def _load():
         lib.orc_grid_index.restype = I
         lib.orc_grid_order.argtypes = [P, P, I, I, I, I, I, ctypes.c_int]
         lib.orc_pool.argtypes = [P, I, I, I, I, ctypes.c_int, P]
-        lib.orc_select_level.argtypes = [P, P, P, I, I, I, I, I, D, P, P]
-        lib.orc_select.argtypes = [P, P, I, I, I, I, ctypes.c_int, I, D, P, P]
-        lib.orc_forward.argtypes = [P, P, P, P, P, P, I, I, I, I, ctypes.c_int, I, D,
+        lib.orc_select_level.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P]
+        lib.orc_select.argtypes = [P, P, I, I, I, I, ctypes.c_int, P, D, P, P]
+        lib.orc_forward.argtypes = [P, P, P, P, P, P, I, I, I, I, ctypes.c_int, P, D,
                                     ctypes.c_uint, P, I, P, P]
         lib.orc_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, ctypes.c_int,
-                                     I, D, ctypes.c_uint, P, I, P, I, P, P, P]
+                                     P, D, ctypes.c_uint, P, I, P, I, P, P, P]
         lib.orc_transpose.argtypes = [P, I, I, I, P, P]
         for f in ("orc_zorder", "orc_grid_order", "orc_pool", "orc_select_level", "orc_select",
                   "orc_forward", "orc_backward", "orc_transpose"):
@@ -131,31 +131,52 @@ def pool(x, bs: int, L: int):
     return _split_levels(buf, G, sizes, d)
 
 
+def level_topk(K, L: int):
+    """K as an int (every level) or a sequence of L values (level 1 first)."""
+    ks = [int(K)] * L if np.isscalar(K) else [int(x) for x in K]
+    assert len(ks) == L
+    return ks
+
+
+def _ks(idx):
+    """per-level K of an index pyramid, as the C array the oracle takes"""
+    return np.ascontiguousarray([x.shape[2] for x in idx], dtype=np.int64)
+
+
 def select_level(qbar, kbar, parent, K: int, bs: int, scale: float):
-    """One level of Top-K; returns (idx [G, n, K] int32, gap [G, n])."""
+    """One level of Top-K; returns (idx [G, n, K] int32, gap [G, n]).  The
+    parent rows may hold another count of picks than K."""
     qbar, kbar = _f64(qbar), _f64(kbar)
     G, n, d = qbar.shape
     par = None if parent is None else _i32(parent)
+    Kp = 0 if par is None else par.shape[2]
     if par is not None:
-        assert par.shape == (G, n // bs, K)
+        assert par.shape[:2] == (G, n // bs)
     idx = np.zeros((G, n, K), np.int32)
     gap = np.zeros((G, n))
-    _load().orc_select_level(_p(qbar), _p(kbar), _p(par), G, n, d, bs, K, scale,
+    _load().orc_select_level(_p(qbar), _p(kbar), _p(par), G, n, d, bs, K, Kp, scale,
                              _p(idx), _p(gap))
     return idx, gap
 
 
-def select(qpyr, kpyr, K: int, bs: int, scale: float):
-    """All levels; returns (idx list per level 1..L, gap list per level)."""
+def select(qpyr, kpyr, K, bs: int, scale: float):
+    """All levels; K an int or one value per level (level 1 first).  Returns
+    (idx list per level 1..L, gap list per level)."""
     G, n1, d = qpyr[0].shape
     L = len(qpyr)
     N = n1 * bs
+    ks = level_topk(K, L)
     sizes = level_sizes(N, bs, L)
-    idx = np.zeros(G * K * sum(sizes), np.int32)
+    idx = np.zeros(G * sum(n * k for n, k in zip(sizes, ks)), np.int32)
     gap = np.zeros(G * sum(sizes))
-    _load().orc_select(_p(_flat_levels(qpyr)), _p(_flat_levels(kpyr)), G, N, d, bs, L, K,
+    ka = np.ascontiguousarray(ks, dtype=np.int64)
+    _load().orc_select(_p(_flat_levels(qpyr)), _p(_flat_levels(kpyr)), G, N, d, bs, L, _p(ka),
                        scale, _p(idx), _p(gap))
-    return _split_levels(idx, G, sizes, K), _split_levels(gap, G, sizes, 1, squeeze=True)
+    out, off = [], 0
+    for n, k in zip(sizes, ks):
+        out.append(idx[off:off + G * n * k].reshape(G, n, k))
+        off += G * n * k
+    return out, _split_levels(gap, G, sizes, 1, squeeze=True)
 
 
 def forward(q, k, v, kpyr, vpyr, idx, bs: int, scale: float, flags: int = 0,
@@ -163,13 +184,13 @@ def forward(q, k, v, kpyr, vpyr, idx, bs: int, scale: float, flags: int = 0,
     """Sparse attention forward; returns (out [G, N, d], lse [G, N])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     G, N, d = q.shape
-    L, K = len(idx), idx[0].shape[2]
+    L, K = len(idx), _ks(idx)
     out = np.zeros((G, N, d)) if out is None else out
     lse = np.zeros((G, N)) if lse is None else lse
     qb = None if qblocks is None else np.ascontiguousarray(qblocks, dtype=np.int64)
     _load().orc_forward(_p(q), _p(k), _p(v), _p(_flat_levels(kpyr)), _p(_flat_levels(vpyr)),
-                        _p(_flat_levels([_i32(x) for x in idx])), G, N, d, bs, L, K, scale,
-                        flags, _p(qb), 0 if qb is None else len(qb), _p(out), _p(lse))
+                        _p(_flat_levels([_i32(x) for x in idx])), G, N, d, bs, L, _p(K),
+                        scale, flags, _p(qb), 0 if qb is None else len(qb), _p(out), _p(lse))
     return out, lse
 
 
@@ -178,13 +199,13 @@ def backward(q, k, v, kpyr, vpyr, idx, o, lse, dout, bs: int, scale: float,
     """Backward; returns (dq, dk, dv), each [G, N, d] (only requested rows set)."""
     q, k, v, o, lse, dout = (_f64(a) for a in (q, k, v, o, lse, dout))
     G, N, d = q.shape
-    L, K = len(idx), idx[0].shape[2]
+    L, K = len(idx), _ks(idx)
     dq, dk, dv = (np.zeros((G, N, d)) for _ in range(3))
     qb = None if qblocks is None else np.ascontiguousarray(qblocks, dtype=np.int64)
     kb = None if kblocks is None else np.ascontiguousarray(kblocks, dtype=np.int64)
     _load().orc_backward(_p(q), _p(k), _p(v), _p(_flat_levels(kpyr)), _p(_flat_levels(vpyr)),
                          _p(_flat_levels([_i32(x) for x in idx])), _p(o), _p(lse), _p(dout),
-                         G, N, d, bs, L, K, scale, flags, _p(qb), 0 if qb is None else len(qb),
+                         G, N, d, bs, L, _p(K), scale, flags, _p(qb), 0 if qb is None else len(qb),
                          _p(kb), 0 if kb is None else len(kb), _p(dq), _p(dk), _p(dv))
     return dq, dk, dv
 
@@ -199,10 +220,11 @@ def transpose(idx):
     return rowptr, col
 
 
-def run(q, k, v, bs: int, L: int, K: int, flags: int = 0, dout=None, scale=None,
+def run(q, k, v, bs: int, L: int, K, flags: int = 0, dout=None, scale=None,
         idx=None, qblocks=None):
     """Whole path on Z-ordered [G, N, d] inputs: pyramid, selection (unless
-    `idx` is given), forward and, with `dout`, backward.  Returns a dict."""
+    `idx` is given; K an int or one value per level), forward and, with `dout`,
+    backward.  Returns a dict."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     d = q.shape[2]
     scale = 1.0 / np.sqrt(d) if scale is None else scale

@@ -28,6 +28,15 @@ static int64_t lvl_off(int64_t G, int64_t N, int64_t bs, int l, int64_t w)
     return off;
 }
 
+/* offset of level l (1-based) inside an index pyramid whose level-m rows hold
+ * K[m-1] entries */
+static int64_t idx_off(int64_t G, int64_t N, int64_t bs, int l, const int64_t* K)
+{
+    int64_t off = 0;
+    for (int m = 1; m < l; ++m) off += G * (N / ipow(bs, m)) * K[m - 1];
+    return off;
+}
+
 static double dot(const double* a, const double* b, int64_t d)
 {
     double s = 0.0;
@@ -154,10 +163,10 @@ static int int_cmp(const void* a, const void* b)
 
 void orc_select_level(const double* qbar, const double* kbar,
                       const int32_t* parent, int64_t G, int64_t n_l, int64_t d,
-                      int64_t bs, int64_t K, double scale, int32_t* idx,
+                      int64_t bs, int64_t K, int64_t Kp, double scale, int32_t* idx,
                       double* gap)
 {
-    int64_t maxc = parent ? bs * K : n_l;
+    int64_t maxc = parent ? bs * Kp : n_l;
     cand_t* c = (cand_t*)malloc((size_t)maxc * sizeof(cand_t));
     for (int64_t g = 0; g < G; ++g)
         for (int64_t i = 0; i < n_l; ++i) {
@@ -166,8 +175,8 @@ void orc_select_level(const double* qbar, const double* kbar,
             if (!parent) {
                 for (int64_t j = 0; j < n_l; ++j) c[nc++].j = (int32_t)j;
             } else {
-                const int32_t* pr = parent + (g * (n_l / bs) + i / bs) * K;
-                for (int64_t p = 0; p < K; ++p)
+                const int32_t* pr = parent + (g * (n_l / bs) + i / bs) * Kp;
+                for (int64_t p = 0; p < Kp; ++p)
                     for (int64_t r = 0; r < bs; ++r)
                         c[nc++].j = (int32_t)(bs * pr[p] + r);
             }
@@ -184,15 +193,15 @@ void orc_select_level(const double* qbar, const double* kbar,
 }
 
 void orc_select(const double* qpyr, const double* kpyr, int64_t G, int64_t N,
-                int64_t d, int64_t bs, int L, int64_t K, double scale,
+                int64_t d, int64_t bs, int L, const int64_t* K, double scale,
                 int32_t* idx, double* gap)
 {
     for (int l = L; l >= 1; --l) {
         int64_t n_l = N / ipow(bs, l);
-        const int32_t* parent = (l == L) ? NULL : idx + lvl_off(G, N, bs, l + 1, K);
+        const int32_t* parent = (l == L) ? NULL : idx + idx_off(G, N, bs, l + 1, K);
         orc_select_level(qpyr + lvl_off(G, N, bs, l, d), kpyr + lvl_off(G, N, bs, l, d),
-                         parent, G, n_l, d, bs, K, scale,
-                         idx + lvl_off(G, N, bs, l, K),
+                         parent, G, n_l, d, bs, K[l - 1], l == L ? 0 : K[l], scale,
+                         idx + idx_off(G, N, bs, l, K),
                          gap ? gap + lvl_off(G, N, bs, l, 1) : NULL);
     }
 }
@@ -217,13 +226,13 @@ static double entry_bias(int tag, int64_t bs, unsigned flags)
 static int64_t kv_set(const double* k, const double* v, const double* kpyr,
                       const double* vpyr, const int32_t* idx, int64_t g,
                       int64_t t, int64_t G, int64_t N, int64_t d, int64_t bs,
-                      int L, int64_t K, unsigned flags, const double** key,
+                      int L, const int64_t* K, unsigned flags, const double** key,
                       const double** val, int* tag, int64_t* ref)
 {
     int64_t ne = 0;
     int64_t n1 = N / bs;
-    const int32_t* sel1 = idx + (g * n1 + t / bs) * K;
-    for (int64_t p = 0; p < K; ++p)
+    const int32_t* sel1 = idx + (g * n1 + t / bs) * K[0];
+    for (int64_t p = 0; p < K[0]; ++p)
         for (int64_t r = 0; r < bs; ++r) {
             int64_t u = bs * sel1[p] + r;
             key[ne] = k + (g * N + u) * d;
@@ -235,8 +244,8 @@ static int64_t kv_set(const double* k, const double* v, const double* kpyr,
     if (!(flags & ORC_NO_ENRICH))
         for (int l = (flags & ORC_ENRICH_COARSE) ? 2 : 1; l <= L; ++l) {
             int64_t n_l = N / ipow(bs, l), a = t / ipow(bs, l);
-            const int32_t* sel = idx + lvl_off(G, N, bs, l, K) + (g * n_l + a) * K;
-            for (int64_t p = 0; p < K; ++p) {
+            const int32_t* sel = idx + idx_off(G, N, bs, l, K) + (g * n_l + a) * K[l - 1];
+            for (int64_t p = 0; p < K[l - 1]; ++p) {
                 int64_t j = sel[p];
                 key[ne] = kpyr + lvl_off(G, N, bs, l, d) + (g * n_l + j) * d;
                 val[ne] = vpyr + lvl_off(G, N, bs, l, d) + (g * n_l + j) * d;
@@ -252,11 +261,12 @@ static int64_t kv_set(const double* k, const double* v, const double* kpyr,
 
 void orc_forward(const double* q, const double* k, const double* v,
                  const double* kpyr, const double* vpyr, const int32_t* idx,
-                 int64_t G, int64_t N, int64_t d, int64_t bs, int L, int64_t K,
+                 int64_t G, int64_t N, int64_t d, int64_t bs, int L, const int64_t* K,
                  double scale, unsigned flags, const int64_t* qblocks,
                  int64_t nq, double* out, double* lse)
 {
-    int64_t n1 = N / bs, maxe = bs * K + (int64_t)L * K;
+    int64_t n1 = N / bs, maxe = bs * K[0];
+    for (int l = 1; l <= L; ++l) maxe += K[l - 1];
     const double** key = (const double**)malloc((size_t)maxe * sizeof(double*));
     const double** val = (const double**)malloc((size_t)maxe * sizeof(double*));
     int* tag = (int*)malloc((size_t)maxe * sizeof(int));
@@ -294,12 +304,13 @@ void orc_forward(const double* q, const double* k, const double* v,
 void orc_backward(const double* q, const double* k, const double* v,
                   const double* kpyr, const double* vpyr, const int32_t* idx,
                   const double* o, const double* lse, const double* dout,
-                  int64_t G, int64_t N, int64_t d, int64_t bs, int L, int64_t K,
+                  int64_t G, int64_t N, int64_t d, int64_t bs, int L, const int64_t* K,
                   double scale, unsigned flags, const int64_t* qblocks,
                   int64_t nq, const int64_t* kblocks, int64_t nk, double* dq,
                   double* dk, double* dv)
 {
-    int64_t n1 = N / bs, maxe = bs * K + (int64_t)L * K;
+    int64_t n1 = N / bs, maxe = bs * K[0];
+    for (int l = 1; l <= L; ++l) maxe += K[l - 1];
     const double** key = (const double**)malloc((size_t)maxe * sizeof(double*));
     const double** val = (const double**)malloc((size_t)maxe * sizeof(double*));
     int* tag = (int*)malloc((size_t)maxe * sizeof(int));
@@ -337,13 +348,13 @@ void orc_backward(const double* q, const double* k, const double* v,
         for (int64_t i = 0; i < n1; ++i) {
             /* skip query blocks that contribute to no requested output */
             int need = want_q[i];
-            const int32_t* sel1 = idx + (g * n1 + i) * K;
-            for (int64_t p = 0; p < K && !need; ++p) need = want_k[sel1[p]];
+            const int32_t* sel1 = idx + (g * n1 + i) * K[0];
+            for (int64_t p = 0; p < K[0] && !need; ++p) need = want_k[sel1[p]];
             if (!(flags & ORC_NO_ENRICH))
                 for (int l = 1; l <= L && !need; ++l) {
                     int64_t n_l = N / ipow(bs, l), a = (bs * i) / ipow(bs, l);
-                    const int32_t* sel = idx + lvl_off(G, N, bs, l, K) + (g * n_l + a) * K;
-                    for (int64_t p = 0; p < K && !need; ++p)
+                    const int32_t* sel = idx + idx_off(G, N, bs, l, K) + (g * n_l + a) * K[l - 1];
+                    for (int64_t p = 0; p < K[l - 1] && !need; ++p)
                         need = want_p[lvl_off(1, N, bs, l, 1) + sel[p]];
                 }
             if (!need) continue;

@@ -19,13 +19,14 @@
  *
  * Conventions (all arrays contiguous, row-major):
  *   G = B*H independent heads, N tokens, d channels, bs = block size,
- *   L = number of pooling levels, K = top-k per level,
+ *   L = number of pooling levels, K[l-1] = top-k of level l (all equal in the
+ *   README's usage; a per-level K is an extension),
  *   n_l = N / bs^l blocks at level l (l = 1..L).
  *   token tensors  : [G][N][d]            double
  *   pyramid        : level l (1..L) stored at offset G*d*sum_{l'<l} n_{l'},
  *                    each level [G][n_l][d]
- *   index pyramid  : level l stored at offset G*K*sum_{l'<l} n_{l'},
- *                    each level [G][n_l][K], ascending within a row
+ *   index pyramid  : level l stored at offset G*sum_{l'<l} n_{l'}*K[l'-1],
+ *                    each level [G][n_l][K[l-1]], ascending within a row
  *   gap pyramid    : level l at offset G*sum_{l'<l} n_{l'}, each [G][n_l]
  *   lse            : [G][N], natural logarithm
  *
@@ -78,24 +79,25 @@ void orc_pool(const double* x, int64_t G, int64_t N, int64_t d, int64_t bs,
 
 /* Top-K selection at one level ([P2] hierarchical Top-K).
  * parent == NULL: coarsest level, candidates are all n_l blocks.
- * otherwise parent is [G][n_l/bs][K] (ascending) and the candidates of row i
- * are the children bs*c + r of the parent row i/bs.
+ * otherwise parent is [G][n_l/bs][Kp] (ascending) and the candidates of row i
+ * are the bs*Kp children bs*c + r of the parent row i/bs.
  * Score = scale * <qbar_l[i], kbar_l[j]>; order = score descending, then
  * block index ascending; the first K are kept and stored ascending.
  * gap[i] = score of K-th kept - score of best rejected (+inf if none). */
 void orc_select_level(const double* qbar, const double* kbar,
                       const int32_t* parent, int64_t G, int64_t n_l, int64_t d,
-                      int64_t bs, int64_t K, double scale, int32_t* idx,
+                      int64_t bs, int64_t K, int64_t Kp, double scale, int32_t* idx,
                       double* gap);
 
-/* All levels, coarsest first (idx, gap in pyramid layouts). */
+/* All levels, coarsest first (idx, gap in pyramid layouts); K[l-1] picks at
+ * level l. */
 void orc_select(const double* qpyr, const double* kpyr, int64_t G, int64_t N,
-                int64_t d, int64_t bs, int L, int64_t K, double scale,
+                int64_t d, int64_t bs, int L, const int64_t* K, double scale,
                 int32_t* idx, double* gap);
 
 /* Sparse attention forward with hierarchical KV enrichment.
  * For token t with query block i = t/bs and level-l ancestor a_l = t/bs^l the
- * key/value set is the bs*K tokens of the blocks idx_1[i] plus (unless
+ * key/value set is the bs*K[0] tokens of the blocks idx_1[i] plus (unless
  * ORC_NO_ENRICH) the pooled pairs (kbar_l[j], vbar_l[j]) for l = 1..L and
  * j in idx_l[a_l].  One softmax over that set with the given scale;
  * lse = m + ln(sum exp(z - m)).
@@ -103,7 +105,7 @@ void orc_select(const double* qpyr, const double* kpyr, int64_t G, int64_t N,
  * which case nq is ignored); rows not listed are left untouched. */
 void orc_forward(const double* q, const double* k, const double* v,
                  const double* kpyr, const double* vpyr, const int32_t* idx,
-                 int64_t G, int64_t N, int64_t d, int64_t bs, int L, int64_t K,
+                 int64_t G, int64_t N, int64_t d, int64_t bs, int L, const int64_t* K,
                  double scale, unsigned flags, const int64_t* qblocks,
                  int64_t nq, double* out, double* lse);
 
@@ -115,7 +117,7 @@ void orc_forward(const double* q, const double* k, const double* v,
 void orc_backward(const double* q, const double* k, const double* v,
                   const double* kpyr, const double* vpyr, const int32_t* idx,
                   const double* o, const double* lse, const double* dout,
-                  int64_t G, int64_t N, int64_t d, int64_t bs, int L, int64_t K,
+                  int64_t G, int64_t N, int64_t d, int64_t bs, int L, const int64_t* K,
                   double scale, unsigned flags, const int64_t* qblocks,
                   int64_t nq, const int64_t* kblocks, int64_t nk, double* dq,
                   double* dk, double* dv);

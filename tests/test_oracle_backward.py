@@ -27,10 +27,12 @@ def _loss_and_idx(q, k, v, dout, L, K, flags):
 @pytest.mark.parametrize("N,L,K,flags", [(256, 1, 4, 0), (256, 1, 4, oracle.NO_ENRICH),
                                          (1024, 2, 2, 0), (256, 1, 4, oracle.SIZE_BIAS),
                                          (1024, 2, 2, oracle.ENRICH_COARSE),
-                                         (1024, 2, 2, oracle.ENRICH_COARSE | oracle.SIZE_BIAS)])
+                                         (1024, 2, 2, oracle.ENRICH_COARSE | oracle.SIZE_BIAS),
+                                         (1024, 2, (3, 2), 0),
+                                         (1024, 2, (5, 1), oracle.SIZE_BIAS)])
 def test_finite_differences(N, L, K, flags):
     G, d = 1, 8
-    rng = np.random.default_rng(N + K + flags)
+    rng = np.random.default_rng(N + int(np.sum(K)) + flags)
     q, k, v, dout = (rng.standard_normal((G, N, d)) for _ in range(4))
     r = oracle.run(q, k, v, BS, L, K, flags=flags, dout=dout)
     grads = {"q": r["dq"], "k": r["dk"], "v": r["dv"]}

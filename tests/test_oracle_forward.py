@@ -100,7 +100,8 @@ VARIANTS = {"enrich": 0, "no_enrich": oracle.NO_ENRICH, "coarse": oracle.ENRICH_
             "size_bias": oracle.SIZE_BIAS, "coarse_size_bias": oracle.ENRICH_COARSE | oracle.SIZE_BIAS}
 
 
-@pytest.mark.parametrize("N,L,K", [(1024, 2, 2), (4096, 2, 4), (256, 1, 4)])
+@pytest.mark.parametrize("N,L,K", [(1024, 2, 2), (4096, 2, 4), (256, 1, 4),
+                                   (1024, 2, (4, 2)), (4096, 3, (2, 5, 1))])
 @pytest.mark.parametrize("variant", list(VARIANTS))
 def test_matches_dense_mask_formulation(N, L, K, variant):
     G, d = 2, 8

@@ -23,10 +23,14 @@ def brute_topk(qbar, kbar, cands, K, scale):
 
 
 def check_hierarchy(qpyr, kpyr, idx, gap, K, scale):
+    """K: one top-k for every level, or one per level (level 1 first)."""
     G = qpyr[0].shape[0]
     L = len(qpyr)
+    ks = [K] * L if np.isscalar(K) else list(K)
     for l in range(L, 0, -1):
         n = qpyr[l - 1].shape[1]
+        Kl = ks[l - 1]
+        assert idx[l - 1].shape == (G, n, Kl)
         for g in range(G):
             for i in range(n):
                 if l == L:
@@ -34,7 +38,7 @@ def check_hierarchy(qpyr, kpyr, idx, gap, K, scale):
                 else:
                     par = idx[l][g, i // BS]
                     cands = (BS * par[:, None] + np.arange(BS)[None, :]).ravel()
-                keep, gp = brute_topk(qpyr[l - 1][g, i], kpyr[l - 1][g], cands, K, scale)
+                keep, gp = brute_topk(qpyr[l - 1][g, i], kpyr[l - 1][g], cands, Kl, scale)
                 np.testing.assert_array_equal(idx[l - 1][g, i], keep)
                 if np.isinf(gp):
                     assert np.isinf(gap[l - 1][g, i])
@@ -43,9 +47,12 @@ def check_hierarchy(qpyr, kpyr, idx, gap, K, scale):
 
 
 @pytest.mark.parametrize("N,L,K", [(256, 1, 4), (1024, 1, 8), (1024, 2, 2), (4096, 2, 4),
-                                   (4096, 3, 1)])
+                                   (4096, 3, 1),
+                                   # a top-k per level (level 1 first)
+                                   (1024, 2, (4, 2)), (4096, 2, (3, 8)), (1024, 2, (32, 3)),
+                                   (4096, 3, (2, 5, 1)), (65536, 3, (6, 3, 9))])
 def test_select_matches_brute_force(N, L, K):
-    rng = np.random.default_rng(N + L + K)
+    rng = np.random.default_rng(N + L + int(np.sum(K)))
     G, d = 2, 8
     q, k = rng.standard_normal((G, N, d)), rng.standard_normal((G, N, d))
     qp, kp = oracle.pool(q, BS, L), oracle.pool(k, BS, L)
