@@ -75,6 +75,7 @@ extern "C" {
  * Level arrays are indexed by l - 1 for level l = 1..levels.
  *   qbar/kbar/vbar[l-1] : float32 [B*H][N/16^l][d]   block means (pyramid)
  *   idx[l-1]            : int32   [B*H][N/16^l][topk] chosen blocks of each
+ *                         (topk: that level's count with the _lk calls)
  *                         level-l query block, ascending
  *   rowptr[l-1]         : int32   [B*H][N/16^l + 1]  key->query lists (CSR,
  *   col[l-1]            : int32   [B*H][N/16^l*topk]  offsets per head from 0,
@@ -153,6 +154,29 @@ int llsa_backward(const void* q, const void* k, const void* v, const void* out,
                   int B, int H, int N, int d, int block_size, int topk, int levels,
                   int dtype, unsigned flags, void* workspace, size_t ws_bytes,
                   void* stream);
+
+/* A top-k per level (the README's usage takes one top-k for every level; the
+ * hierarchical selection of the skill summary, "Core Technique" 1, works the
+ * same with a different count at each level).  topk: HOST array of `levels`
+ * ints, topk[l-1] the picks of every level-l row, level 1 (the fine blocks)
+ * first; read during the call only.  Level l < levels chooses among the
+ * 16*topk[l] children of its parent's picks, so 1 <= topk[l-1] <=
+ * 16*topk[l]; the coarsest level among N/16^levels blocks.  Every other
+ * argument, the layout and the errors are those of the uniform calls (a NULL
+ * topk gives LLSA_ERR_NULL); with equal values the results are identical to
+ * them.  The workspace must be sized by llsa_workspace_bytes_lk with the same
+ * array, and the backward given the forward's array. */
+size_t llsa_workspace_bytes_lk(int B, int H, int N, int d, int block_size, const int* topk,
+                               int levels, int dtype);
+int llsa_workspace_layout_lk(int B, int H, int N, int d, int block_size, const int* topk,
+                             int levels, int dtype, llsa_ws_layout* out);
+int llsa_forward_lk(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                    int H, int N, int d, int block_size, const int* topk, int levels, int dtype,
+                    unsigned flags, void* workspace, size_t ws_bytes, void* stream);
+int llsa_backward_lk(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                     int H, int N, int d, int block_size, const int* topk, int levels,
+                     int dtype, unsigned flags, void* workspace, size_t ws_bytes, void* stream);
 
 /* Stages of llsa_forward / llsa_backward, for per-kernel timing and tests.
  * llsa_forward == parts POOL, SELECT, ATTN in that order; llsa_backward ==

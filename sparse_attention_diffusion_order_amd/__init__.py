@@ -21,6 +21,7 @@ __all__ = [
     "llsa_workspace_bytes", "llsa_workspace_layout", "llsa_zorder", "llsa_grid_order",
     "llsa_forward",
     "llsa_backward", "llsa_forward_part", "llsa_backward_part", "llsa_strerror",
+    "llsa_workspace_bytes_lk", "llsa_workspace_layout_lk", "llsa_forward_lk", "llsa_backward_lk",
     "forward", "backward", "zorder", "grid_order",
 ]
 
@@ -84,6 +85,16 @@ def load():
     lib.llsa_forward_part.restype = I
     lib.llsa_backward_part.argtypes = [I] + bwd
     lib.llsa_backward_part.restype = I
+    IP = ctypes.POINTER(ctypes.c_int)
+    lk = [I] * 5 + [IP, I, I]  # B H N d block_size topk[] levels dtype
+    lib.llsa_workspace_bytes_lk.argtypes = lk
+    lib.llsa_workspace_bytes_lk.restype = S
+    lib.llsa_workspace_layout_lk.argtypes = lk + [ctypes.POINTER(WsLayout)]
+    lib.llsa_workspace_layout_lk.restype = I
+    lib.llsa_forward_lk.argtypes = [P] * 5 + lk + [U, P, S, P]
+    lib.llsa_forward_lk.restype = I
+    lib.llsa_backward_lk.argtypes = [P] * 9 + lk + [U, P, S, P]
+    lib.llsa_backward_lk.restype = I
     lib.llsa_strerror.argtypes = [I]
     lib.llsa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -147,6 +158,42 @@ def llsa_grid_order(src, dst, outer, frames, height, width, inner_bytes, inverse
                                   inner_bytes, int(inverse), _stream(stream)), "llsa_grid_order")
 
 
+def _karr(topk):
+    """a per-level top-k sequence (level 1 first) as a C int array"""
+    ks = [int(x) for x in topk]
+    return (ctypes.c_int * max(1, len(ks)))(*ks)
+
+
+def llsa_workspace_bytes_lk(B, H, N, d, block_size, topk, levels, dtype) -> int:
+    return int(load().llsa_workspace_bytes_lk(B, H, N, d, block_size, _karr(topk), levels,
+                                              dtype))
+
+
+def llsa_workspace_layout_lk(B, H, N, d, block_size, topk, levels, dtype) -> dict:
+    lay = WsLayout()
+    _check(load().llsa_workspace_layout_lk(B, H, N, d, block_size, _karr(topk), levels, dtype,
+                                           ctypes.byref(lay)), "llsa_workspace_layout_lk")
+    out = {name: list(getattr(lay, name))[:levels]
+           for name in ("qbar", "kbar", "vbar", "idx", "rowptr", "col")}
+    out["delta"], out["total"] = lay.delta, lay.total
+    return out
+
+
+def llsa_forward_lk(q, k, v, out, lse, B, H, N, d, block_size, topk, levels, dtype, flags,
+                    workspace, ws_bytes, stream=None):
+    _check(load().llsa_forward_lk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                  block_size, _karr(topk), levels, dtype, flags,
+                                  _ptr(workspace), ws_bytes, _stream(stream)), "llsa_forward_lk")
+
+
+def llsa_backward_lk(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, block_size, topk, levels,
+                     dtype, flags, workspace, ws_bytes, stream=None):
+    _check(load().llsa_backward_lk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, block_size,
+                                   _karr(topk), levels, dtype, flags, _ptr(workspace),
+                                   ws_bytes, _stream(stream)), "llsa_backward_lk")
+
+
 def llsa_forward(q, k, v, out, lse, B, H, N, d, block_size, topk, levels, dtype, flags,
                  workspace, ws_bytes, stream=None):
     _check(load().llsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
@@ -191,27 +238,31 @@ def _dtype_code(t) -> int:
     raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
 
 
-def forward(q, k, v, topk: int, levels: int, flags: int = 0, workspace=None, stream=None):
-    """Returns (out, lse, workspace); the workspace feeds `backward`."""
+def forward(q, k, v, topk, levels: int, flags: int = 0, workspace=None, stream=None):
+    """Returns (out, lse, workspace); the workspace feeds `backward`.  topk: an
+    int for every level, or one value per level (level 1 first)."""
     import torch
     B, H, N, d = q.shape
     dt = _dtype_code(q)
     for t in (q, k, v):
         if not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError("q, k, v must be contiguous tensors of one shape and dtype")
-    nbytes = llsa_workspace_bytes(B, H, N, d, 16, topk, levels, dt)
+    per_level = not isinstance(topk, int)
+    nbytes = (llsa_workspace_bytes_lk if per_level else llsa_workspace_bytes)(
+        B, H, N, d, 16, topk, levels, dt)
     if nbytes == 0:
         raise LlsaError(-2, "llsa_workspace_bytes")
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     out = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    llsa_forward(q, k, v, out, lse, B, H, N, d, 16, topk, levels, dt, flags, workspace,
-                 workspace.numel(), stream)
+    (llsa_forward_lk if per_level else llsa_forward)(
+        q, k, v, out, lse, B, H, N, d, 16, topk, levels, dt, flags, workspace,
+        workspace.numel(), stream)
     return out, lse, workspace
 
 
-def backward(q, k, v, out, lse, dout, topk: int, levels: int, workspace, flags: int = 0,
+def backward(q, k, v, out, lse, dout, topk, levels: int, workspace, flags: int = 0,
              stream=None):
     """Returns (dq, dk, dv); `workspace` must come from `forward`."""
     import torch
@@ -220,8 +271,9 @@ def backward(q, k, v, out, lse, dout, topk: int, levels: int, workspace, flags: 
     if not dout.is_contiguous() or dout.shape != q.shape or dout.dtype != q.dtype:
         raise ValueError("dout must be contiguous with the shape and dtype of q")
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    llsa_backward(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, 16, topk, levels, dt, flags,
-                  workspace, workspace.numel(), stream)
+    (llsa_backward if isinstance(topk, int) else llsa_backward_lk)(
+        q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, 16, topk, levels, dt, flags,
+        workspace, workspace.numel(), stream)
     return dq, dk, dv
 
 

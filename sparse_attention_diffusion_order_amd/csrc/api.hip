@@ -16,20 +16,29 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
 
-int validate(int B, int H, int N, int d, int block_size, int topk, int levels, int dtype,
+// ks[l - 1]: picks per level-l row (l = 1..levels)
+int validate(int B, int H, int N, int d, int block_size, const int* ks, int levels, int dtype,
              unsigned flags)
 {
+    if (!ks) return LLSA_ERR_NULL;
     if (d != D || block_size != BS || (dtype != LLSA_F32 && dtype != LLSA_BF16) ||
         (flags & ~LLSA_KNOWN_FLAGS))
         return LLSA_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || N < BS || topk < 1 || levels < 1) return LLSA_ERR_SHAPE;
+    if (B < 1 || H < 1 || N < BS || levels < 1) return LLSA_ERR_SHAPE;
     if (levels > MAX_L) return LLSA_ERR_UNSUPPORTED;
     long long span = 1;
     for (int l = 0; l < levels; ++l) span *= BS;
     if (span > N || N % span) return LLSA_ERR_SHAPE;
     long long nL = N / span;
-    if (topk > nL) return LLSA_ERR_SHAPE;
-    if (nL > 4096 || topk > 64) return LLSA_ERR_UNSUPPORTED;
+    // level l chooses among n_L blocks (coarsest) or the 16 K_{l+1} children
+    // of its parent's picks
+    for (int l = levels; l >= 1; --l) {
+        const long long cands = l == levels ? nL : (long long)BS * ks[l];
+        if (ks[l - 1] < 1 || ks[l - 1] > cands) return LLSA_ERR_SHAPE;
+    }
+    for (int l = 0; l < levels; ++l)
+        if (ks[l] > 64) return LLSA_ERR_UNSUPPORTED;
+    if (nL > 4096) return LLSA_ERR_UNSUPPORTED;
     if ((long long)B * H * N >= (1ll << 31)) return LLSA_ERR_UNSUPPORTED;
     if (N > (1 << 23)) return LLSA_ERR_UNSUPPORTED;  // one head's tensor < 2 GiB (buffer offsets)
     return LLSA_OK;
@@ -46,7 +55,7 @@ struct Layout {
 // Workspace: pyramid (float32), index lists, key->query CSR lists, delta,
 // enrichment gradient partials and sums.  Sizes are O(B*H*N*d): no part of
 // it grows with the square of the block count.
-void make_layout(int G, int N, int K, int L, Layout* lay)
+void make_layout(int G, int N, const int* ks, int L, Layout* lay)
 {
     memset(lay, 0, sizeof(*lay));
     size_t off = 0;
@@ -63,43 +72,52 @@ void make_layout(int G, int N, int K, int L, Layout* lay)
         lay->pub.qbar[l - 1] = take(pyr);
         lay->pub.kbar[l - 1] = take(pyr);
         lay->pub.vbar[l - 1] = take(pyr);
-        lay->pub.idx[l - 1] = take((size_t)G * n[l] * K * sizeof(int));
+        lay->pub.idx[l - 1] = take((size_t)G * n[l] * ks[l - 1] * sizeof(int));
     }
     for (int l = 1; l <= L; ++l) {
         lay->pub.rowptr[l - 1] = take((size_t)G * (n[l] + 1) * sizeof(int));
-        lay->pub.col[l - 1] = take((size_t)G * n[l] * K * sizeof(int));
+        lay->pub.col[l - 1] = take((size_t)G * n[l] * ks[l - 1] * sizeof(int));
     }
     size_t prows = 0;
     for (int l = 1; l <= L; ++l) prows += (size_t)G * n[l];
     lay->kb16 = take(prows * D * 2);
     lay->vb16 = take(prows * D * 2);
     lay->pub.delta = take((size_t)G * N * sizeof(float));
-    lay->pe1 = take((size_t)G * n[1] * K * 2 * BS * sizeof(float));
-    for (int l = 1; l <= L; ++l) lay->slot[l - 1] = take((size_t)G * n[l] * K);
+    lay->pe1 = take((size_t)G * n[1] * ks[0] * 2 * BS * sizeof(float));
+    for (int l = 1; l <= L; ++l) lay->slot[l - 1] = take((size_t)G * n[l] * ks[l - 1]);
     size_t blocks = 0;
     for (int l = 1; l <= L; ++l)
         blocks += (size_t)G * (n[l] + (n[l] + 15) / 16);
     lay->cnt = take(blocks * sizeof(int));
     for (int l = 1; l <= L; ++l) {
         lay->dbar[l - 1] = take((size_t)G * n[l] * 2 * D * sizeof(float));
-        if (l >= 2) lay->part[l - 1] = take((size_t)G * n[2] * K * 2 * D * sizeof(float));
+        if (l >= 2) lay->part[l - 1] = take((size_t)G * n[2] * ks[l - 1] * 2 * D * sizeof(float));
     }
     lay->pub.total = off;
 }
 
-void make_geo(int B, int H, int N, int topk, int levels, unsigned flags, Geo* g)
+void make_geo(int B, int H, int N, const int* ks, int levels, unsigned flags, Geo* g)
 {
     memset(g, 0, sizeof(*g));
     g->G = B * H;
     g->N = N;
-    g->K = topk;
+    g->K = ks[0];
     g->L = levels;
     g->n[0] = N;
-    for (int l = 1; l <= levels; ++l) g->n[l] = g->n[l - 1] / BS;
+    for (int l = 1; l <= levels; ++l) {
+        g->n[l] = g->n[l - 1] / BS;
+        g->Kl[l] = ks[l - 1];
+    }
     g->scale = 0.125f;  // 1/sqrt(64)
     g->flags = flags;
     g->l0 = (flags & LLSA_NO_ENRICH) ? levels + 1 : (flags & LLSA_ENRICH_COARSE) ? 2 : 1;
     g->lb2 = (flags & LLSA_SIZE_BIAS) ? 4.0f : 0.0f;  // log2(16^l) = 4 l
+    int e = 0;  // pooled entry offsets of the enriching levels
+    for (int l = g->l0; l <= levels; ++l) {
+        g->eoff[l] = e;
+        e += ks[l - 1];
+    }
+    g->eoff[levels + 1] = e;
 }
 
 void make_ws(void* base, const Layout& lay, int L, Ws* w)
@@ -130,15 +148,15 @@ struct Prep {
     hipStream_t st;
 };
 
-int prepare(int B, int H, int N, int d, int block_size, int topk, int levels, int dtype,
+int prepare(int B, int H, int N, int d, int block_size, const int* ks, int levels, int dtype,
             unsigned flags, void* workspace, size_t ws_bytes, void* stream, Prep* p)
 {
-    int rc = validate(B, H, N, d, block_size, topk, levels, dtype, flags);
+    int rc = validate(B, H, N, d, block_size, ks, levels, dtype, flags);
     if (rc) return rc;
     Layout lay;
-    make_layout(B * H, N, topk, levels, &lay);
+    make_layout(B * H, N, ks, levels, &lay);
     if (!workspace || ws_bytes < lay.pub.total) return LLSA_ERR_WORKSPACE;
-    make_geo(B, H, N, topk, levels, flags, &p->geo);
+    make_geo(B, H, N, ks, levels, flags, &p->geo);
     make_ws(workspace, lay, levels, &p->ws);
     // per-level block rows of the bf16 pyramid copies; the choice counts
     // (per block and per 16 blocks) of every level
@@ -188,12 +206,22 @@ int run_backward_part(int part, const void* q, const void* k, const void* v, con
     }
 }
 
+// the same top-k at every level, as an array (levels outside 1..MAX_L are
+// rejected by validate before the array is read)
+struct UniformK {
+    int ks[MAX_L];
+    UniformK(int topk, int levels)
+    {
+        for (int l = 0; l < MAX_L; ++l) ks[l] = l < levels ? topk : 0;
+    }
+};
+
 }  // namespace
 
 extern "C" {
 
-size_t llsa_workspace_bytes(int B, int H, int N, int d, int block_size, int topk, int levels,
-                            int dtype)
+size_t llsa_workspace_bytes_lk(int B, int H, int N, int d, int block_size, const int* topk,
+                               int levels, int dtype)
 {
     if (validate(B, H, N, d, block_size, topk, levels, dtype, 0)) return 0;
     Layout lay;
@@ -201,8 +229,15 @@ size_t llsa_workspace_bytes(int B, int H, int N, int d, int block_size, int topk
     return lay.pub.total;
 }
 
-int llsa_workspace_layout(int B, int H, int N, int d, int block_size, int topk, int levels,
-                          int dtype, llsa_ws_layout* out)
+size_t llsa_workspace_bytes(int B, int H, int N, int d, int block_size, int topk, int levels,
+                            int dtype)
+{
+    return llsa_workspace_bytes_lk(B, H, N, d, block_size, UniformK(topk, levels).ks, levels,
+                                   dtype);
+}
+
+int llsa_workspace_layout_lk(int B, int H, int N, int d, int block_size, const int* topk,
+                             int levels, int dtype, llsa_ws_layout* out)
 {
     if (!out) return LLSA_ERR_NULL;
     int rc = validate(B, H, N, d, block_size, topk, levels, dtype, 0);
@@ -211,6 +246,13 @@ int llsa_workspace_layout(int B, int H, int N, int d, int block_size, int topk, 
     make_layout(B * H, N, topk, levels, &lay);
     *out = lay.pub;
     return LLSA_OK;
+}
+
+int llsa_workspace_layout(int B, int H, int N, int d, int block_size, int topk, int levels,
+                          int dtype, llsa_ws_layout* out)
+{
+    return llsa_workspace_layout_lk(B, H, N, d, block_size, UniformK(topk, levels).ks, levels,
+                                    dtype, out);
 }
 
 int llsa_zorder(const void* src, void* dst, long long outer, int side, int inner_bytes,
@@ -244,15 +286,15 @@ int llsa_forward_part(int part, const void* q, const void* k, const void* v, voi
 {
     if (!q || !k || !v || !out || !lse) return LLSA_ERR_NULL;
     Prep p;
-    int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
-                     stream, &p);
+    int rc = prepare(B, H, N, d, block_size, UniformK(topk, levels).ks, levels, dtype, flags,
+                     workspace, ws_bytes, stream, &p);
     if (rc) return rc;
     return run_forward_part(part, q, k, v, out, lse, dtype, p);
 }
 
-int llsa_forward(const void* q, const void* k, const void* v, void* out, float* lse, int B,
-                 int H, int N, int d, int block_size, int topk, int levels, int dtype,
-                 unsigned flags, void* workspace, size_t ws_bytes, void* stream)
+int llsa_forward_lk(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                    int H, int N, int d, int block_size, const int* topk, int levels, int dtype,
+                    unsigned flags, void* workspace, size_t ws_bytes, void* stream)
 {
     if (!q || !k || !v || !out || !lse) return LLSA_ERR_NULL;
     Prep p;
@@ -266,6 +308,15 @@ int llsa_forward(const void* q, const void* k, const void* v, void* out, float* 
     return LLSA_OK;
 }
 
+int llsa_forward(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                 int H, int N, int d, int block_size, int topk, int levels, int dtype,
+                 unsigned flags, void* workspace, size_t ws_bytes, void* stream)
+{
+    return llsa_forward_lk(q, k, v, out, lse, B, H, N, d, block_size,
+                           UniformK(topk, levels).ks, levels, dtype, flags, workspace, ws_bytes,
+                           stream);
+}
+
 int llsa_backward_part(int part, const void* q, const void* k, const void* v, const void* out,
                        const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
                        int H, int N, int d, int block_size, int topk, int levels, int dtype,
@@ -273,16 +324,16 @@ int llsa_backward_part(int part, const void* q, const void* k, const void* v, co
 {
     if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return LLSA_ERR_NULL;
     Prep p;
-    int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
-                     stream, &p);
+    int rc = prepare(B, H, N, d, block_size, UniformK(topk, levels).ks, levels, dtype, flags,
+                     workspace, ws_bytes, stream, &p);
     if (rc) return rc;
     return run_backward_part(part, q, k, v, out, lse, dout, dq, dk, dv, dtype, p);
 }
 
-int llsa_backward(const void* q, const void* k, const void* v, const void* out,
-                  const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
-                  int H, int N, int d, int block_size, int topk, int levels, int dtype,
-                  unsigned flags, void* workspace, size_t ws_bytes, void* stream)
+int llsa_backward_lk(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                     int H, int N, int d, int block_size, const int* topk, int levels,
+                     int dtype, unsigned flags, void* workspace, size_t ws_bytes, void* stream)
 {
     if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return LLSA_ERR_NULL;
     Prep p;
@@ -296,15 +347,26 @@ int llsa_backward(const void* q, const void* k, const void* v, const void* out,
     return LLSA_OK;
 }
 
+int llsa_backward(const void* q, const void* k, const void* v, const void* out,
+                  const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                  int H, int N, int d, int block_size, int topk, int levels, int dtype,
+                  unsigned flags, void* workspace, size_t ws_bytes, void* stream)
+{
+    return llsa_backward_lk(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, block_size,
+                            UniformK(topk, levels).ks, levels, dtype, flags, workspace,
+                            ws_bytes, stream);
+}
+
 const char* llsa_strerror(int code)
 {
     switch (code) {
     case LLSA_OK: return "ok";
     case LLSA_ERR_NULL: return "a required pointer is NULL";
     case LLSA_ERR_SHAPE:
-        return "bad shape: 16^levels must divide N, 1 <= topk <= N/16^levels, B, H, "
-               "levels >= 1 (grid order: sides in [1, 2^15], at most 2^30 cells, "
-               "inner_bytes a positive multiple of 4)";
+        return "bad shape: 16^levels must divide N; B, H, levels >= 1; every top-k >= 1 and "
+               "at most its level's candidates (N/16^levels at the coarsest level, 16 times "
+               "the parent level's top-k below it); grid order: sides in [1, 2^15], at most "
+               "2^30 cells, inner_bytes a positive multiple of 4";
     case LLSA_ERR_UNSUPPORTED:
         return "unsupported: needs d=64, block_size=16, dtype f32/bf16, known flags, "
                "levels<=6, at most 4096 coarsest blocks, topk<=64, B*H*N<2^31";

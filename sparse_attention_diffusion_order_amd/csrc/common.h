@@ -25,15 +25,25 @@ typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 struct Geo {
     int G;                 // B * H
     int N;                 // tokens per head
-    int K;                 // top-k per level
+    int K;                 // top-k of level 1 (the fine blocks), == Kl[1]
     int L;                 // pooling levels
     int n[MAX_L + 1];      // n[l] = N / 16^l blocks at level l (n[0] = N)
+    int Kl[MAX_L + 2];     // Kl[l]: picks per level-l row, l = 1..L
+    // pooled entries of a query block: those of level l (l0 <= l <= L) are
+    // entries eoff[l] .. eoff[l + 1] - 1; eoff[l0] = 0
+    int eoff[MAX_L + 2];
     float scale;           // 1 / sqrt(d)
     unsigned flags;
     int l0;                // first level whose pooled tokens enrich (L + 1: none)
     float lb2;             // logit bias of a level-l pooled token: l * lb2 (log2 units)
-    // pooled entries per query block: levels l0..L, K each
-    __host__ __device__ int n_pooled() const { return l0 <= L ? (L - l0 + 1) * K : 0; }
+    __host__ __device__ int n_pooled() const { return l0 <= L ? eoff[L + 1] : 0; }
+    // level of pooled entry e (0 <= e < n_pooled())
+    __host__ __device__ int entry_level(int e) const
+    {
+        int l = l0;
+        while (l < L && e >= eoff[l + 1]) ++l;
+        return l;
+    }
 };
 
 // Device pointers into the caller's workspace.

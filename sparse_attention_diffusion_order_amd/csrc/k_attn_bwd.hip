@@ -78,10 +78,10 @@ __device__ __forceinline__ void put_rows(unsigned short* lds, bf16x8 r0, bf16x8 
 // dQ^T += K^T dS^T over two 16-entry tiles.  Key rows are in LDS (la, lb);
 // ka*/kb* are the A operands of S^T (the same rows), va*/vb* those of dP^T.
 // na / nb: valid entries (MASK == false: both tiles full).
-// Pooled tiles: entry ea + 4(lane/16) + r of tile a (ea + 16 + ... of tile b)
-// is a level l0 + entry / K token and its logit gets lb2 times that level
-// (lb2 = 0: no bias; fine tiles pass 0).  pe != nullptr: the entries below K
-// are level-1 pooled tokens; their P and dS are stored at
+// ba / bb (MASK only, may be null): logit bias of rows 4(lane/16) + r of
+// tiles a and b (log2 units; pooled entries under the size-weighted variant).
+// pe != nullptr: entries ea + 4(lane/16) + r (tile a) and ea + 16 + ... (tile
+// b) below K1 are level-1 pooled tokens; their P and dS are stored at
 // pe[entry][0 | 1][query] for the key-major dk/dv pass.
 template <bool MASK>
 __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1, bf16x8 bd0,
@@ -89,8 +89,8 @@ __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1,
                                         bf16x8 kb0, bf16x8 kb1, bf16x8 va0, bf16x8 va1,
                                         bf16x8 vb0, bf16x8 vb1, const unsigned short* la,
                                         const unsigned short* lb, int na, int nb, float c,
-                                        int lane, float* pe = nullptr, int ea = 0, int K = 1,
-                                        float lb2 = 0.f, int l0 = 1)
+                                        int lane, float* pe = nullptr, int ea = 0, int K1 = 0,
+                                        const float* ba = nullptr, const float* bb = nullptr)
 {
     const int gq = lane >> 4;
     const int rr = (lane & 15) >> 2, xx = lane & 3;
@@ -102,14 +102,9 @@ __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1,
     bf16x8 bs;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        float ba = 0.f, bb = 0.f;
-        if (MASK) {
-            const int e_a = ea + 4 * gq + r;
-            ba = lb2 * (float)(l0 + e_a / K);
-            bb = lb2 * (float)(l0 + (e_a + BS) / K);
-        }
-        float Pa = fast_exp2(fmaf(sa[r], c, nl2 + ba));
-        float Pb = fast_exp2(fmaf(sb[r], c, nl2 + bb));
+        const float xa = (MASK && ba) ? ba[r] : 0.f, xb = (MASK && bb) ? bb[r] : 0.f;
+        float Pa = fast_exp2(fmaf(sa[r], c, nl2 + xa));
+        float Pb = fast_exp2(fmaf(sb[r], c, nl2 + xb));
         if (MASK) {
             Pa = (4 * gq + r < na) ? Pa : 0.f;
             Pb = (4 * gq + r < nb) ? Pb : 0.f;
@@ -118,11 +113,11 @@ __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1,
         if (pe) {
             const int nq = lane & 15;
             const int e_a = ea + 4 * gq + r, e_b = e_a + BS;
-            if (e_a < K) {
+            if (e_a < K1) {
                 pe[e_a * 2 * BS + nq] = Pa;
                 pe[e_a * 2 * BS + BS + nq] = dSa;
             }
-            if (e_b < K) {
+            if (e_b < K1) {
                 pe[e_b * 2 * BS + nq] = Pb;
                 pe[e_b * 2 * BS + BS + nq] = dSb;
             }
@@ -139,7 +134,7 @@ __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1,
     }
 }
 
-constexpr int MAX_E = MAX_L * 64;  // pooled entries per query block (L * K)
+constexpr int MAX_E = MAX_L * 64;  // pooled entries per query block (sum of the levels' K)
 
 // Per-wave LDS of dq: two key tiles (160-byte rows, read as operands and
 // transposed), two value tiles (144-byte rows) and the pooled-entry table.
@@ -189,11 +184,12 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
     const int E = g.n_pooled();
     int* ent = (int*)(smem[wv] + 2 * Lay::K_TILE + 2 * Lay::V_TILE);
     for (int l = g.l0; l <= g.L; ++l) {
+        const int Kl = g.Kl[l];
         const long a = (long)gh * g.n[l] + (i >> (4 * (l - 1)));
-        for (int s0 = 0; s0 < g.K; s0 += 64)
-            if (s0 + lane < g.K)
-                ent[(l - g.l0) * g.K + s0 + lane] =
-                    (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * g.K + s0 + lane]);
+        for (int s0 = 0; s0 < Kl; s0 += 64)
+            if (s0 + lane < Kl)
+                ent[g.eoff[l] + s0 + lane] =
+                    (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * Kl + s0 + lane]);
     }
     lds_fence();
 
@@ -262,9 +258,15 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
             const bool pooled = p >= NF;
             float* pe = (pooled && g.l0 == 1 && e0 < g.K)
                             ? w.pe1 + ((long)gh * g.n[1] + i) * g.K * 2 * BS : nullptr;
+            float ba[4], bb[4];  // pooled rows: the logit bias of the entry's level
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ea = e0 + 4 * gq + r;
+                ba[r] = pooled ? g.lb2 * (float)g.entry_level(ea) : 0.f;
+                bb[r] = pooled ? g.lb2 * (float)g.entry_level(ea + BS) : 0.f;
+            }
             dq_pair<true>(acc, bq0, bq1, bd0, bd1, nl2, Dq, ka0, ka1, kb0, kb1, va0, va1, vb0,
-                          vb1, la, lb, na, nb, c, lane, pe, e0, g.K, pooled ? g.lb2 : 0.f,
-                          g.l0);
+                          vb1, la, lb, na, nb, c, lane, pe, e0, g.K, ba, bb);
         }
     };
     DqPair A, B;
@@ -323,10 +325,11 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
     };
     for (int l = 2; l <= g.L; ++l) {
         const int al = a2 >> (4 * (l - 2));
-        const int* sel = w.idx[l - 1] + ((long)gh * g.n[l] + al) * g.K;
+        const int Kl = g.Kl[l];
+        const int* sel = w.idx[l - 1] + ((long)gh * g.n[l] + al) * Kl;
         const float lb = g.lb2 * (float)l;  // size bias of a level-l token (log2)
-        for (int e0 = 0; e0 < g.K; e0 += BS) {
-            const bool ev = e0 + nq < g.K;
+        for (int e0 = 0; e0 < Kl; e0 += BS) {
+            const bool ev = e0 + nq < Kl;
             bf16x8 bk0 = {}, bk1 = {}, bv0 = {}, bv1 = {};
             if (ev) {
                 long off = ((long)gh * g.n[l] + sel[e0 + nq]) * D;
@@ -386,9 +389,9 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
                     const float s = red[x] + red[1024 + x] + red[2048 + x] + red[3072 + x];
                     const int d = x >> 8, r = (x >> 6) & 3, ln = x & 63;
                     const int ent = e0 + (ln & 15), dim = 16 * d + 4 * (ln >> 4) + r;
-                    if (ent < g.K) {
+                    if (ent < Kl) {
                         float* dst = w.part[l - 1] +
-                                     ((((long)gh * g.n[2] + a2) * g.K + ent) * 2 + kind) * D;
+                                     ((((long)gh * g.n[2] + a2) * Kl + ent) * 2 + kind) * D;
                         dst[dim] = kind == 0 ? s * g.scale : s;
                     }
                 }
@@ -408,10 +411,11 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
     const int dim = threadIdx.x & 63;
     const int gh = (int)(blk / g.n[l]), j = (int)(blk % g.n[l]);
     const int* rp = w.rowptr[l - 1] + (long)gh * (g.n[l] + 1);
-    const int* cl = w.col[l - 1] + (long)gh * g.n[l] * g.K;
-    const unsigned char* sl = w.slot[l - 1] + (long)gh * g.n[l] * g.K;
+    const int Kl = g.Kl[l];
+    const int* cl = w.col[l - 1] + (long)gh * g.n[l] * Kl;
+    const unsigned char* sl = w.slot[l - 1] + (long)gh * g.n[l] * Kl;
     const int span = 1 << (4 * (l - 2));  // level-2 blocks per level-l block
-    const float* part = w.part[l - 1] + (long)gh * g.n[2] * g.K * 2 * D + dim;
+    const float* part = w.part[l - 1] + (long)gh * g.n[2] * Kl * 2 * D + dim;
     float sk = 0.f, sv = 0.f;
     const int beg = uniform(rp[j]), end = uniform(rp[j + 1]);
     // list entries in batches of 64: lane e holds entry beg + e (row offset
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
     for (int e0 = beg; e0 < end; e0 += 64) {
         const int ne = min(64, end - e0);
         int off = 0;  // in rows of 2*D floats
-        if (lane < ne) off = cl[e0 + lane] * span * g.K + sl[e0 + lane];
+        if (lane < ne) off = cl[e0 + lane] * span * Kl + sl[e0 + lane];
         const int nrow = ne * span;
         for (int q0 = 0; q0 < nrow; q0 += 8) {
             float vk[8], vv[8];
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
             for (int u = 0; u < 8; ++u) {
                 const int qq = min(q0 + u, nrow - 1);
                 const int e = qq / span, a2 = qq % span;
-                const long o = ((long)__builtin_amdgcn_readlane(off, e) + (long)a2 * g.K) * 2 * D;
+                const long o = ((long)__builtin_amdgcn_readlane(off, e) + (long)a2 * Kl) * 2 * D;
                 vk[u] = part[o];
                 vv[u] = part[o + D];
             }
@@ -630,9 +634,9 @@ __device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const 
     // enriching levels l0..L; a level-lv token's logit gets lb2 * lv * ln 2
     for (int lv = g.l0; lv <= g.L; ++lv) {
         const int a = t >> (4 * lv);
-        const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.K;
+        const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.Kl[lv];
         const float bias = g.lb2 * (float)lv * LN2;
-        for (int s = 0; s < g.K; ++s) {
+        for (int s = 0; s < g.Kl[lv]; ++s) {
             long row = ((long)gh * g.n[lv] + sl[s]) * D;
             f(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, bias);
         }
@@ -681,7 +685,7 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
     const float kb = w.kbar[l - 1][blk * D + lane];
     const float vb = w.vbar[l - 1][blk * D + lane];
     const int* rp = w.rowptr[l - 1] + (long)gh * (g.n[l] + 1);
-    const int* cl = w.col[l - 1] + (long)gh * g.n[l] * g.K;
+    const int* cl = w.col[l - 1] + (long)gh * g.n[l] * g.Kl[l];
     const long span = 1l << (4 * l);
     const float bias = g.lb2 * (float)l * LN2;  // size bias of a level-l token
     float sk = 0.f, sv = 0.f;

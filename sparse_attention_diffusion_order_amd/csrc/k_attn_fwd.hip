@@ -14,7 +14,7 @@
 // LLSA_SIZE_BIAS a level-l pooled logit gets + ln 16^l, as if the token stood
 // for its 16^l keys.
 //
-// The pooled entries of the enriching levels ((L - l0 + 1)*K of them) form
+// The pooled entries of the enriching levels (the sum of their top-k) form
 // extra tiles of 16, read from the bf16 copy of the pyramid that the pool
 // pass writes.
 //
@@ -176,16 +176,17 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
     // the query block's K fine blocks, one per lane (K <= 64)
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
     const int myj = lane < g.K ? sel[lane] : 0;
-    // pooled entries e = (l-1)*K + slot: their rows in the bf16 pooled arrays
-    // pooled entries e = (l - l0) * K + slot for the enriching levels l0..L
+    // pooled entries e = eoff[l] + slot of the enriching levels l0..L: their
+    // rows in the bf16 pooled arrays
     const int E = g.n_pooled();
     int* ent = (int*)(smem[wv] + 2 * Lay::V_TILE + 2 * Lay::K_TILE);
     for (int l = g.l0; l <= g.L; ++l) {
+        const int Kl = g.Kl[l];
         const long a = (long)gh * g.n[l] + (i >> (4 * (l - 1)));
-        for (int s0 = 0; s0 < g.K; s0 += 64)
-            if (s0 + lane < g.K)
-                ent[(l - g.l0) * g.K + s0 + lane] =
-                    (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * g.K + s0 + lane]);
+        for (int s0 = 0; s0 < Kl; s0 += 64)
+            if (s0 + lane < Kl)
+                ent[g.eoff[l] + s0 + lane] =
+                    (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * Kl + s0 + lane]);
     }
     lds_fence();
 
@@ -280,16 +281,16 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
         f.vb1 = ld_bf16x8(vpb + ob8 + vc);
         bf16x8 ka0, ka1, kb0, kb1;
         stage(f, ka0, ka1, kb0, kb1);
-        // valid entries of the two tiles, and each row's logit bias: a
-        // pooled entry e is a level l0 + e / K token
+        // valid entries of the two tiles, and each row's logit bias (that
+        // of the level of pooled entry e)
         const int na = t < NFT ? BS : max(0, min(BS, E - BS * (t - NFT)));
         const int nb = t + 1 >= NT ? 0 : (t + 1 < NFT ? BS : max(0, min(BS, E - BS * (t + 1 - NFT))));
         float ba[4], bb[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int ea = BS * (t - NFT) + 4 * gq + r, eb = ea + BS;
-            ba[r] = t < NFT ? 0.f : g.lb2 * (float)(g.l0 + ea / g.K);
-            bb[r] = t + 1 < NFT ? 0.f : g.lb2 * (float)(g.l0 + eb / g.K);
+            ba[r] = t < NFT ? 0.f : g.lb2 * (float)g.entry_level(ea);
+            bb[r] = t + 1 < NFT ? 0.f : g.lb2 * (float)g.entry_level(eb);
         }
         attend_pair<true>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, na, nb, c, lane, ba, bb);
     }
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
 
 // --------------------------------------------- four sibling blocks per wave
 //
-// attn_fwd_u4 (K <= 16): a wave owns four consecutive query blocks.  They
+// attn_fwd_u4 (every top-k <= 16): a wave owns four consecutive query blocks.  They
 // are siblings (the same parent at every coarser level), so their fine picks
 // overlap: the wave forms the ascending union of the 4 K picks (about 37 of
 // 64 at 256x256, K = 16), loads every union tile once and applies it to each
@@ -443,14 +444,14 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
     if (E) {
         for (int t = 0; t < NPT; ++t) {
             if (lane < BS) {
-                const int r = min(lane, K - 1);
                 int row;
                 if (t < NT1) {
-                    row = (int)(w.prow[0] + (long)gh * g.n[1] + L.arr[t * 16 + r]);
+                    row = (int)(w.prow[0] + (long)gh * g.n[1] + L.arr[t * 16 + min(lane, K - 1)]);
                 } else {
-                    const int l = tile_level(t);
+                    const int l = tile_level(t), Kl = g.Kl[l];
                     const long a = (long)gh * g.n[l] + (i0 >> (4 * (l - 1)));
-                    row = (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * K + r]);
+                    row = (int)(w.prow[l - 1] + (long)gh * g.n[l] +
+                                w.idx[l - 1][a * Kl + min(lane, Kl - 1)]);
                 }
                 L.pent[t * BS + lane] = row;
             }
@@ -524,18 +525,20 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
         if (u < U) run(A, __builtin_amdgcn_readlane(tm, u), BS, false);
     }
     if (NPT > 0) {
-        // masked runs (rows >= K, logit bias of the tile's level)
+        // masked runs (rows at or past the tile level's K, logit bias of
+        // the tile's level)
         auto members = [&](int t) { return t < NT1 ? 1 << t : 0xF; };
         auto bias = [&](int t) { return g.lb2 * (float)tile_level(t); };
+        auto rows = [&](int t) { return g.Kl[tile_level(t)]; };
         load_pooled(A, 0);
         int t = 0;
         for (; t + 2 <= NPT; t += 2) {
             load_pooled(B, t + 1);
-            run(A, members(t), K, true, bias(t));
+            run(A, members(t), rows(t), true, bias(t));
             load_pooled(A, min(t + 2, NPT - 1));
-            run(B, members(t + 1), K, true, bias(t + 1));
+            run(B, members(t + 1), rows(t + 1), true, bias(t + 1));
         }
-        if (t < NPT) run(A, members(t), K, true, bias(t));
+        if (t < NPT) run(A, members(t), rows(t), true, bias(t));
     }
 
 #pragma unroll
@@ -590,9 +593,9 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
         }
     for (int lv = g.l0; lv <= g.L; ++lv) {  // pooled tokens of the enriching levels
         const int a = t >> (4 * lv);
-        const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.K;
+        const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.Kl[lv];
         const float bias = g.lb2 * (float)lv * LN2;
-        for (int s = 0; s < g.K; ++s) {
+        for (int s = 0; s < g.Kl[lv]; ++s) {
             const long row = ((long)gh * g.n[lv] + sl[s]) * D;
             visit(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, bias);
         }
@@ -608,7 +611,11 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* ou
 {
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
-        if (g.K <= BS && g.n[1] % 4 == 0) {
+        // the four-block kernel: every fine list and every pooled list fit
+        // one 16-entry tile
+        bool fits = g.K <= BS && g.n[1] % 4 == 0;
+        for (int l = g.l0; l <= g.L; ++l) fits = fits && g.Kl[l] <= BS;
+        if (fits) {
             hipLaunchKernelGGL(attn_fwd_u4, dim3((unsigned)((nblk + 15) / 16)), dim3(256), 0, st,
                                (const unsigned short*)q, (const unsigned short*)k,
                                (const unsigned short*)v, (unsigned short*)out, lse, g, w);

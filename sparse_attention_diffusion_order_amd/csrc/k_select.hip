@@ -12,7 +12,7 @@
 //
 // One workgroup (4 waves) per group of R query rows that share a candidate
 // list: the 16 siblings of a parent below the coarsest level (candidates =
-// 16*K children of the parent's picks, ascending), or R rows of the coarsest
+// the 16 K' children of the parent's K' picks, ascending), or R rows of the coarsest
 // level (candidates = all blocks).  Scores of the R x M tile live in LDS.
 // Summation order of a score: four partial sums of 16 channels each, combined
 // pairwise -- fixed, so the result does not depend on the launch.
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
     // candidate list (ascending)
     for (int c = threadIdx.x; c < M; c += blockDim.x) {
         if (parent) {
-            const int* pr = parent + ((long)gh * (n_l / BS) + grp) * K;
+            const int* pr = parent + ((long)gh * (n_l / BS) + grp) * (M / BS);  // parent row: M/16 picks
             cand[c] = BS * pr[c / BS] + (c % BS);
         } else {
             cand[c] = c;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
     const int rows = min(R, n_l - row0);
     for (int c = threadIdx.x; c < M; c += blockDim.x) {
         if (parent) {
-            const int* pr = parent + ((long)gh * (n_l / BS) + grp) * K;
+            const int* pr = parent + ((long)gh * (n_l / BS) + grp) * (M / BS);  // parent row: M/16 picks
             cand[c] = BS * pr[c / BS] + (c % BS);
         } else {
             cand[c] = c;
@@ -382,7 +382,8 @@ hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
     hipLaunchKernelGGL(clear_counts, dim3(cgrid), dim3(256), 0, st, w.cnt_all, w.cnt_len);
     for (int l = g.L; l >= 1; --l) {
         const int* parent = (l == g.L) ? nullptr : w.idx[l];
-        const int M = parent ? BS * g.K : g.n[l];
+        const int K = g.Kl[l];  // picks of a level-l row
+        const int M = parent ? BS * g.Kl[l + 1] : g.n[l];  // its candidates
         const float* qb = w.qbar[l - 1];
         const float* kb = w.kbar[l - 1];
         int* out = w.idx[l - 1];
@@ -392,10 +393,10 @@ hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
             auto f = M <= 16 ? launch_mfma<1> : M <= 32 ? launch_mfma<2> : M <= 64 ? launch_mfma<4>
                    : M <= 128 ? launch_mfma<8> : M <= 256 ? launch_mfma<16>
                    : M <= 512 ? launch_mfma<32> : launch_mfma<64>;
-            e = f(qb, kb, parent, out, cnt, g.G, g.n[l], g.K, M, g.scale, st);
+            e = f(qb, kb, parent, out, cnt, g.G, g.n[l], K, M, g.scale, st);
         } else {
             auto f = M <= 2048 ? launch_wide<32> : launch_wide<64>;
-            e = f(qb, kb, out, cnt, g.G, g.n[l], g.K, g.scale, st);
+            e = f(qb, kb, out, cnt, g.G, g.n[l], K, g.scale, st);
         }
         if (e != hipSuccess) return e;
     }

@@ -39,7 +39,7 @@ __device__ __forceinline__ Cands make_cands(const Geo& g, const Ws& w, int l, in
         cs.n = g.n[l];
     } else {
         const int* rp = w.rowptr[l] + (long)gh * (g.n[l + 1] + 1);
-        cs.plist = w.col[l] + (long)gh * g.n[l + 1] * g.K + rp[grp];
+        cs.plist = w.col[l] + (long)gh * g.n[l + 1] * g.Kl[l + 1] + rp[grp];
         cs.n = BS * (rp[grp + 1] - rp[grp]);
     }
     return cs;
@@ -91,12 +91,13 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
     const int n = g.n[l];
     const int groups = (n + 15) / 16;
     const int gh = blockIdx.x / groups, grp = blockIdx.x % groups;
-    const int* I = w.idx[l - 1] + (long)gh * n * g.K;
+    const int K = g.Kl[l];  // picks per level-l row
+    const int* I = w.idx[l - 1] + (long)gh * n * K;
     const int* cnt = w.cnt[l - 1] + (long)gh * n;
     const int* c16 = w.c16[l - 1] + (long)gh * ((n + 15) / 16);
     int* rowptr = w.rowptr[l - 1] + (long)gh * (n + 1);
-    int* col = w.col[l - 1] + (long)gh * n * g.K;
-    unsigned char* slots = w.slot[l - 1] + (long)gh * n * g.K;
+    int* col = w.col[l - 1] + (long)gh * n * K;
+    unsigned char* slots = w.slot[l - 1] + (long)gh * n * K;
 
     // the candidate walk (parent list -> candidate rows -> their picks) and
     // the prefix over earlier bins are independent: both go out before the
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
         cm = 0;
         if (c < cs.n) {
             ci = cs.row(c);
-            cm = hit_mask(I + (long)ci * g.K, g.K, grp, &cfirst);
+            cm = hit_mask(I + (long)ci * K, K, grp, &cfirst);
         }
     };
     probe(0);
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
             // pos < n K whenever the counts match the index lists (both come
             // from the same selection pass); the test only keeps a workspace
             // that was not filled by one from being written out of bounds
-            if (((m >> b) & 1u) && pos < n * g.K) {
+            if (((m >> b) & 1u) && pos < n * K) {
                 col[pos] = i;
                 slots[pos] = (unsigned char)(first + __popc(m & ((1u << b) - 1u)));
             }

@@ -22,6 +22,11 @@ TOL = {"bf16": dict(out_max=2e-2, out_mean=2e-3, grad_max=5e-2),
        "f32": dict(out_max=1e-5, out_mean=1e-5, grad_max=1e-4)}
 
 
+def level_k(w, l):
+    """top-k of level l (1-based): w.topk is an int or one value per level"""
+    return w.topk if isinstance(w.topk, int) else w.topk[l - 1]
+
+
 def to_device(arr, dtype):
     import torch
     if dtype == "bf16":
@@ -55,23 +60,26 @@ def gpu_run(w, inp, flags=0, backward=True, q64=None):
         dq, dk, dv = lib.backward(q, k, v, out, lse, do, w.topk, w.levels, ws, flags)
         res.update(dq_t=dq, dk_t=dk, dv_t=dv)
     torch.cuda.synchronize()
-    lay = lib.llsa_workspace_layout(B, H, N, d, BS, w.topk, w.levels, dt)
+    lay = (lib.llsa_workspace_layout(B, H, N, d, BS, w.topk, w.levels, dt)
+           if isinstance(w.topk, int) else
+           lib.llsa_workspace_layout_lk(B, H, N, d, BS, w.topk, w.levels, dt))
     G = B * H
     res["lay"] = lay
     res["idx"], res["qbar"], res["kbar"], res["vbar"] = [], [], [], []
     res["rowptr"], res["col"] = [], []
     for l in range(1, w.levels + 1):
         n = N // BS ** l
-        res["idx"].append(ws_array(ws, lay["idx"][l - 1], G * n * w.topk, np.int32)
-                          .reshape(G, n, w.topk))
+        K = level_k(w, l)
+        res["idx"].append(ws_array(ws, lay["idx"][l - 1], G * n * K, np.int32)
+                          .reshape(G, n, K))
         for name in ("qbar", "kbar", "vbar"):
             res[name].append(ws_array(ws, lay[name][l - 1], G * n * d, np.float32)
                              .reshape(G, n, d).astype(np.float64))
         if backward:
             res["rowptr"].append(ws_array(ws, lay["rowptr"][l - 1], G * (n + 1), np.int32)
                                  .reshape(G, n + 1))
-            res["col"].append(ws_array(ws, lay["col"][l - 1], G * n * w.topk, np.int32)
-                              .reshape(G, n * w.topk))
+            res["col"].append(ws_array(ws, lay["col"][l - 1], G * n * K, np.int32)
+                              .reshape(G, n * K))
     res["out"] = to_f64(out).reshape(G, N, d)
     res["lse"] = lse.cpu().numpy().astype(np.float64).reshape(G, N)
     if backward:
@@ -97,7 +105,7 @@ def check_selection(w, gpu, orc_pyr, exact: bool):
     diffs = 0
     for l in range(w.levels, 0, -1):
         parent = None if l == w.levels else gpu["idx"][l]
-        want, gap = oracle.select_level(qp[l - 1], kp[l - 1], parent, w.topk, BS, scale)
+        want, gap = oracle.select_level(qp[l - 1], kp[l - 1], parent, level_k(w, l), BS, scale)
         got = gpu["idx"][l - 1]
         bad = np.any(got != want, axis=2)
         if exact:

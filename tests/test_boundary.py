@@ -103,6 +103,33 @@ def test_shapes_beyond_powers_of_two_are_accepted(N, K, Lv):
     assert L.llsa_workspace_bytes(1, 2, N, 64, 16, K, Lv, L.BF16) > 0
 
 
+def test_per_level_top_k_validation():
+    lib = L.load()
+    arr = lambda *ks: (ctypes.c_int * len(ks))(*ks)
+    wb = lambda ks, N=4096, Lv=2: lib.llsa_workspace_bytes_lk(1, 2, N, 64, 16, ks, Lv, L.BF16)
+    lay = L.WsLayout()
+    assert lib.llsa_workspace_layout_lk(1, 2, 4096, 64, 16, None, 2, L.BF16,
+                                        ctypes.byref(lay)) == -1
+    assert wb(arr(8, 4)) > 0
+    assert wb(arr(16, 16)) == L.llsa_workspace_bytes(1, 2, 4096, 64, 16, 16, 2, L.BF16)
+    assert wb(arr(8, 17)) == 0          # coarsest: 16 blocks
+    assert wb(arr(65, 4)) == 0          # level 1: at most 16 * 4 = 64 candidates
+    assert wb(arr(0, 4)) == 0
+    assert wb(arr(2, 3, 1), N=4096, Lv=3) > 0
+    assert wb(arr(2, 17, 1), N=4096, Lv=3) == 0  # 16 * 1 level-2 candidates
+    args = [BAD] * 5 + [1, 2, 4096, 64, 16]
+    assert lib.llsa_forward_lk(*args, None, 2, L.BF16, 0, BAD, 1 << 40, None) == -1
+    assert lib.llsa_forward_lk(*args, arr(8, 17), 2, L.BF16, 0, BAD, 1 << 40, None) == -2
+    assert lib.llsa_forward_lk(*args, arr(128, 16), 2, L.BF16, 0, BAD, 1 << 40, None) == -3
+    assert lib.llsa_forward_lk(*args, arr(8, 4), 2, L.BF16, 0, BAD, 100, None) == -4
+    bargs = [BAD] * 9 + [1, 2, 4096, 64, 16]
+    assert lib.llsa_backward_lk(*bargs, arr(8, 17), 2, L.BF16, 0, BAD, 1 << 40, None) == -2
+    # each level's lists take that level's top-k
+    lk = L.llsa_workspace_layout_lk(1, 2, 4096, 64, 16, [8, 4], 2, L.BF16)
+    assert lk["idx"][1] - lk["idx"][0] >= 2 * 256 * 8 * 4
+    assert lk["col"][1] - lk["col"][0] >= 2 * 256 * 8 * 4
+
+
 def test_strerror():
     for c in (0, -1, -2, -3, -4, -5, 99):
         assert isinstance(L.llsa_strerror(c), str) and L.llsa_strerror(c)

@@ -168,6 +168,26 @@ def test_shapes_beyond_powers_of_two(w):
     _full_check(w)
 
 
+# a top-k per level (level 1 first), through the _lk entry points
+_PER_LEVEL = [
+    (_grid("grid64_bf16_l2_k8x4", "bf16", 2, (8, 4), 64), 0),           # four-block kernels
+    (_grid("grid128_bf16_l2_k32x8", "bf16", 2, (32, 8), 128), 0),       # one-block kernels
+    (_grid("grid32_f32_l2_k4x2", "f32", 2, (4, 2), 32), 0),
+    (_grid("grid64_bf16_l3_k2x3x1", "bf16", 3, (2, 3, 1), 64), 0),
+    (_grid("grid128_bf16_l2_k32x8", "bf16", 2, (32, 8), 128),
+     oracle.ENRICH_COARSE | oracle.SIZE_BIAS),
+    (_grid("grid64_bf16_l2_k8x4", "bf16", 2, (8, 4), 64), oracle.SIZE_BIAS),
+    (_grid("grid32_f32_l2_k4x2", "f32", 2, (4, 2), 32), oracle.SIZE_BIAS),
+    (_grid("grid64_bf16_l2_k2x16", "bf16", 2, (2, 16), 64), 0),         # fewer fine picks
+]
+
+
+@pytest.mark.parametrize("w,flags", _PER_LEVEL,
+                         ids=["%s_f%d" % (w.name, f) for w, f in _PER_LEVEL])
+def test_top_k_per_level(w, flags):
+    _full_check(w, flags=flags)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_all_blocks_no_enrichment_equals_dense(dtype):
     w = small("dense", 1, 2, 32, dtype, 1, 64)  # K = n_1 = 64: every block
