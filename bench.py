@@ -10,7 +10,9 @@ through the C ABI of libllsa.so on one stream.  Prints ONE JSON line.
 The headline times K whole steps between two HIP events on the library's
 stream.  A second pass of K steps records an event after every stage for the
 per-stage times; the roofline object is computed from it for the stage kernel
-that takes the longest.
+that takes the longest.  Then per-rep distributions (median, p10, p90) of the
+forward, forward+backward and grid-order gather: warm, and cold with a
+512 MiB write before each rep so that nothing stays in the 256 MB MALL.
 """
 from __future__ import annotations
 
@@ -208,8 +210,14 @@ def cpu_baseline(w, inp, min_s=10.0):
         dt += time.perf_counter() - t0
         done += 1
     f = flops(w)["fwdbwd"] * done / G
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 3),
+            "seconds": round(dt, 3), "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": "heads 0..%d of %d (%d/%d of the workload): pool, selection, forward "
                       "and backward, fp64 C oracle, single thread" % (done - 1, G, done, G)}
 
@@ -219,12 +227,21 @@ def dense_reference(w, q, k, v, do, reps=3):
     import torch
     import torch.nn.functional as F
     res = {}
-    try:
-        from torch.nn.attention import SDPBackend, sdpa_kernel
-        ctx = sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION])
-    except Exception:  # pragma: no cover
-        import contextlib
-        ctx = contextlib.nullcontext()
+    import contextlib
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    # the fused backend that takes these shapes: flash attention, else the
+    # memory-efficient kernel (recorded, as the comparison depends on it)
+    ctx, res["backend"] = contextlib.nullcontext(), "default"
+    for name, be in (("flash", SDPBackend.FLASH_ATTENTION),
+                     ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([be]):
+                F.scaled_dot_product_attention(q[:, :1, :256], k[:, :1, :256], v[:, :1, :256])
+            torch.cuda.synchronize()
+            ctx, res["backend"] = sdpa_kernel([be]), name
+            break
+        except Exception:
+            continue
     with ctx:
         qq, kk, vv = (x.detach().clone().requires_grad_(True) for x in (q, k, v))
         for mode in ("fwd", "fwdbwd"):
@@ -363,6 +380,35 @@ def main():
     stage_ms = {name: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in all_evs]))
                 for i, name in enumerate(stages)}
 
+    # per-rep distributions: warm (inputs and workspace may sit in the 256 MB
+    # MALL from the previous rep) and cold (a 512 MiB write before each rep
+    # evicts them); one event pair around each rep on the library's stream
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def reps(body, cold, n):
+        out_ms = []
+        for _ in range(n):
+            if cold:
+                flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            body()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out_ms.append(e0.elapsed_time(e1))
+        p10, p50, p90 = np.percentile(out_ms, [10, 50, 90])
+        return {"p50": round(float(p50), 5), "p10": round(float(p10), 5),
+                "p90": round(float(p90), 5)}
+
+    nrep = max(args.steps, 20)
+    timing = {"reps": nrep}
+    for cold in (False, True):
+        tag = "cold" if cold else "warm"
+        timing["fwd_ms_" + tag] = reps(lambda: run_list(["pool", "select", "attn_fwd"]), cold, nrep)
+        timing["fwdbwd_ms_" + tag] = reps(lambda: run_list(stages[1:]), cold, nrep)
+        timing["grid_order_ms_" + tag] = reps(lambda: run_stage("zorder"), cold, nrep)
+    del flush
+
     f = flops(w)
     value = f["fwdbwd"] / (ms_per_step * 1e-3) / 1e12
 
@@ -403,6 +449,20 @@ def main():
         "stage_hbm_mb": {k_: round(t_ / 1e6, 1) for k_, t_ in
                          ((k_, load_traffic(k_, w)) for k_ in stages) if t_ is not None},
         "roofline": roofline,
+        "timing": timing,
+        # each attention kernel against its own algorithmic roofline,
+        # min(MFMA peak, intensity x HBM peak) with intensity = FLOP / unique bytes
+        "attained_vs_roofline": {
+            k_: {"tflops": round(kflops[k_] / (stage_ms[k_] * 1e-3) / 1e12, 2),
+                 "roof_tflops": round(min(peak_mfma, kflops[k_] / abytes[k_] * HBM_PEAK_GBS / 1e3), 1),
+                 "frac": round(kflops[k_] / (stage_ms[k_] * 1e-3) / 1e12 /
+                               min(peak_mfma, kflops[k_] / abytes[k_] * HBM_PEAK_GBS / 1e3), 4)}
+            for k_ in ("attn_fwd", "dq", "dkdv")},
+        # selection: fp32 dot products (ALU) and its unique bytes (HBM)
+        "select_frac": {"alu": round(f["select"] / (stage_ms["select"] * 1e-3) / 1e12 /
+                                     FP32_PEAK_TFLOPS, 4),
+                        "hbm": round(abytes["select"] / (stage_ms["select"] * 1e-3) / 1e9 /
+                                     HBM_PEAK_GBS, 4)},
     }
 
     if not args.no_dense:
