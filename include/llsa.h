@@ -61,7 +61,7 @@ extern "C" {
                                      topk < 1 or topk > N / 16^levels,
                                      B or H < 1 (N and topk need not be
                                      powers of two) */
-#define LLSA_ERR_UNSUPPORTED (-3) /* d != 64, block_size != 16, unknown dtype
+#define LLSA_ERR_UNSUPPORTED (-3) /* d not 64 or 128, block_size != 16, unknown dtype
                                      or flags, levels > LLSA_MAX_LEVELS,
                                      coarsest block count > 4096, topk > 64,
                                      N > 2^23, or B*H*N >= 2^31 */

@@ -21,7 +21,7 @@ int validate(int B, int H, int N, int d, int block_size, const int* ks, int leve
              unsigned flags)
 {
     if (!ks) return LLSA_ERR_NULL;
-    if (d != D || block_size != BS || (dtype != LLSA_F32 && dtype != LLSA_BF16) ||
+    if ((d != D64 && d != D128) || block_size != BS || (dtype != LLSA_F32 && dtype != LLSA_BF16) ||
         (flags & ~LLSA_KNOWN_FLAGS))
         return LLSA_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || N < BS || levels < 1) return LLSA_ERR_SHAPE;
@@ -55,7 +55,7 @@ struct Layout {
 // Workspace: pyramid (float32), index lists, key->query CSR lists, delta,
 // enrichment gradient partials and sums.  Sizes are O(B*H*N*d): no part of
 // it grows with the square of the block count.
-void make_layout(int G, int N, const int* ks, int L, Layout* lay)
+void make_layout(int G, int N, int D, const int* ks, int L, Layout* lay)
 {
     memset(lay, 0, sizeof(*lay));
     size_t off = 0;
@@ -96,11 +96,12 @@ void make_layout(int G, int N, const int* ks, int L, Layout* lay)
     lay->pub.total = off;
 }
 
-void make_geo(int B, int H, int N, const int* ks, int levels, unsigned flags, Geo* g)
+void make_geo(int B, int H, int N, int d, const int* ks, int levels, unsigned flags, Geo* g)
 {
     memset(g, 0, sizeof(*g));
     g->G = B * H;
     g->N = N;
+    g->d = d;
     g->K = ks[0];
     g->L = levels;
     g->n[0] = N;
@@ -108,7 +109,7 @@ void make_geo(int B, int H, int N, const int* ks, int levels, unsigned flags, Ge
         g->n[l] = g->n[l - 1] / BS;
         g->Kl[l] = ks[l - 1];
     }
-    g->scale = 0.125f;  // 1/sqrt(64)
+    g->scale = 1.0f / sqrtf((float)d);  // SDPA's default scale
     g->flags = flags;
     g->l0 = (flags & LLSA_NO_ENRICH) ? levels + 1 : (flags & LLSA_ENRICH_COARSE) ? 2 : 1;
     g->lb2 = (flags & LLSA_SIZE_BIAS) ? 4.0f : 0.0f;  // log2(16^l) = 4 l
@@ -154,9 +155,9 @@ int prepare(int B, int H, int N, int d, int block_size, const int* ks, int level
     int rc = validate(B, H, N, d, block_size, ks, levels, dtype, flags);
     if (rc) return rc;
     Layout lay;
-    make_layout(B * H, N, ks, levels, &lay);
+    make_layout(B * H, N, d, ks, levels, &lay);
     if (!workspace || ws_bytes < lay.pub.total) return LLSA_ERR_WORKSPACE;
-    make_geo(B, H, N, ks, levels, flags, &p->geo);
+    make_geo(B, H, N, d, ks, levels, flags, &p->geo);
     make_ws(workspace, lay, levels, &p->ws);
     // per-level block rows of the bf16 pyramid copies; the choice counts
     // (per block and per 16 blocks) of every level
@@ -225,7 +226,7 @@ size_t llsa_workspace_bytes_lk(int B, int H, int N, int d, int block_size, const
 {
     if (validate(B, H, N, d, block_size, topk, levels, dtype, 0)) return 0;
     Layout lay;
-    make_layout(B * H, N, topk, levels, &lay);
+    make_layout(B * H, N, d, topk, levels, &lay);
     return lay.pub.total;
 }
 
@@ -243,7 +244,7 @@ int llsa_workspace_layout_lk(int B, int H, int N, int d, int block_size, const i
     int rc = validate(B, H, N, d, block_size, topk, levels, dtype, 0);
     if (rc) return rc;
     Layout lay;
-    make_layout(B * H, N, topk, levels, &lay);
+    make_layout(B * H, N, d, topk, levels, &lay);
     *out = lay.pub;
     return LLSA_OK;
 }
@@ -368,7 +369,7 @@ const char* llsa_strerror(int code)
                "the parent level's top-k below it); grid order: sides in [1, 2^15], at most "
                "2^30 cells, inner_bytes a positive multiple of 4";
     case LLSA_ERR_UNSUPPORTED:
-        return "unsupported: needs d=64, block_size=16, dtype f32/bf16, known flags, "
+        return "unsupported: needs d=64 or 128, block_size=16, dtype f32/bf16, known flags, "
                "levels<=6, at most 4096 coarsest blocks, topk<=64, B*H*N<2^31";
     case LLSA_ERR_WORKSPACE: return "workspace missing or smaller than llsa_workspace_bytes()";
     case LLSA_ERR_HIP: return "HIP launch or runtime error";

@@ -9,7 +9,8 @@
 namespace llsa {
 
 constexpr int BS = 16;      // block size (tokens per level-1 block)
-constexpr int D = 64;       // head dimension supported by the kernels
+constexpr int D64 = 64;     // head dimensions supported by the kernels: 64 and 128
+constexpr int D128 = 128;
 constexpr int MAX_L = LLSA_MAX_LEVELS;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -28,6 +29,7 @@ struct Geo {
     int K;                 // top-k of level 1 (the fine blocks), == Kl[1]
     int L;                 // pooling levels
     int n[MAX_L + 1];      // n[l] = N / 16^l blocks at level l (n[0] = N)
+    int d;                 // head dimension (64 or 128)
     int Kl[MAX_L + 2];     // Kl[l]: picks per level-l row, l = 1..L
     // pooled entries of a query block: those of level l (l0 <= l <= L) are
     // entries eoff[l] .. eoff[l + 1] - 1; eoff[l0] = 0
@@ -65,8 +67,8 @@ struct Ws {
     long prow[MAX_L];        // first row of each level in kb16 / vb16
     float* delta;            // [G][N]
     float* pe1;              // [G][n1][K][2][16]: P and dS of the level-1 pooled entries
-    float* part[MAX_L];      // level l>=2 partial enrichment grads [G][n2][K][2][D]
-    float* dbar[MAX_L];      // level l>=2 enrichment grads [G][n_l][2][D]
+    float* part[MAX_L];      // level l>=2 partial enrichment grads [G][n2][K][2][d]
+    float* dbar[MAX_L];      // level l>=2 enrichment grads [G][n_l][2][d]
 };
 
 // ---------------------------------------------------------------- helpers
@@ -210,6 +212,56 @@ __device__ __forceinline__ int xcd_block(int b, int nb)
     const int full = nb & ~7;
     if (b >= full) return b;
     return (b & 7) * (full >> 3) + (b >> 3);
+}
+
+// A 16-row bf16 tile of D channels loaded by one wave in 16-byte chunks: a
+// row is D/8 chunks; one load instruction covers 1024 bytes (RPI rows), so a
+// tile takes NI = D/32 loads per lane.  LDS row strides: ROW_T for tiles read
+// back transposed (ds_read_b64_tr_b16), ROW_A for tiles read as MFMA operands;
+// both shift successive rows by 8 or 4 banks, so the reads spread over all banks.
+template <int D>
+struct TileShape {
+    static constexpr int LPR = D / 8;     // lanes per row
+    static constexpr int RPI = 64 / LPR;  // rows per load instruction
+    static constexpr int NI = BS / RPI;   // load instructions per tile
+    static constexpr int ROW_T = D + 16;
+    static constexpr int ROW_A = D + 8;
+    static_assert(D == D64 || D == D128, "head dimension");
+};
+
+// Store a tile loaded as TileShape<D> chunks (load u: row lane/LPR + RPI u,
+// columns 8 (lane % LPR) ..) into LDS rows of stride ROW.
+template <int D, int ROW>
+__device__ __forceinline__ void stage_rows(unsigned short* lds, const bf16x8 (&r)[TileShape<D>::NI],
+                                           int lane)
+{
+    using TS = TileShape<D>;
+    const int vr = lane / TS::LPR, vc = (lane % TS::LPR) * 8;
+#pragma unroll
+    for (int u = 0; u < TS::NI; ++u) *(bf16x8*)(lds + (vr + TS::RPI * u) * ROW + vc) = r[u];
+}
+
+// MFMA operand rows of a staged tile: row lane%16, channels 32u + 8(lane/16)
+// .. +7 for u < D/32 (the A or B operand of a 16x16x32 product over D).
+template <int D, int ROW>
+__device__ __forceinline__ void operand_rows(const unsigned short* lds,
+                                             bf16x8 (&x)[TileShape<D>::NI], int lane)
+{
+    const int gq = lane >> 4, nq = lane & 15;
+#pragma unroll
+    for (int u = 0; u < TileShape<D>::NI; ++u)
+        x[u] = *(const bf16x8*)(lds + nq * ROW + 32 * u + 8 * gq);
+}
+
+// 16x16 product over D channels: D/32 chained 16x16x32 MFMAs
+template <int D>
+__device__ __forceinline__ f32x4 scores(const bf16x8 (&a)[TileShape<D>::NI],
+                                        const bf16x8 (&b)[TileShape<D>::NI])
+{
+    f32x4 s = {};
+#pragma unroll
+    for (int u = 0; u < TileShape<D>::NI; ++u) s = mfma32(a[u], b[u], s);
+    return s;
 }
 
 // ------------------------------------------------------------ launchers

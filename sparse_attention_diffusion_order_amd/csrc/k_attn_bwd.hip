@@ -35,12 +35,12 @@
 namespace llsa {
 namespace {
 
-// Staged 16-row tiles in LDS: 160-byte rows where a tile is read back
-// transposed (ds_read_b64_tr_b16), 144-byte rows where it is only read as an
-// MFMA operand (ds_read_b128); either way the accesses spread over all banks.
-constexpr int LDS_ROW = 80;
-constexpr int ROW_A = 72;
-constexpr int TILE = BS * LDS_ROW;
+// Staged 16-row tiles in LDS (TileShape<D>): rows of D + 16 elements where a
+// tile is read back transposed (ds_read_b64_tr_b16), D + 8 where it is only
+// read as an MFMA operand (ds_read_b128); either way the accesses spread over
+// all banks.
+template <int D>
+constexpr int TILE = BS * TileShape<D>::ROW_T;
 
 __device__ __forceinline__ bf16x8 ld8(const unsigned short* p) { return *(const bf16x8*)p; }
 
@@ -54,25 +54,21 @@ __device__ __forceinline__ bf16x8 ld8f(const float* p)
 }
 
 
-// Registers of one prefetched pair of fine tiles for dq: rows vr and vr+8
-// (columns vc .. vc+7) of the key and value tiles a and b -- 8 whole
-// 128-byte rows per load instruction.
+// Registers of one prefetched pair of fine tiles for dq: load u holds row
+// sr + RPI u (columns sc .. sc+7) of the key and value tiles a and b -- whole
+// rows, 1024 bytes per load instruction.
+template <int D>
 struct DqPair {
-    bf16x8 kra0, kra1, krb0, krb1;
-    bf16x8 vra0, vra1, vrb0, vrb1;
+    static constexpr int NI = TileShape<D>::NI;
+    bf16x8 kra[NI], krb[NI], vra[NI], vrb[NI];
 };
 
-template <int ROW>
-__device__ __forceinline__ void put_rows_s(unsigned short* lds, bf16x8 r0, bf16x8 r1, int lane)
+// a tile (TileShape<D> chunks) into LDS rows read back transposed
+template <int D>
+__device__ __forceinline__ void put_rows(unsigned short* lds, const bf16x8 (&r)[TileShape<D>::NI],
+                                         int lane)
 {
-    const int sr = lane >> 3, sc = (lane & 7) * 8;
-    *(bf16x8*)(lds + sr * ROW + sc) = r0;
-    *(bf16x8*)(lds + (sr + 8) * ROW + sc) = r1;
-}
-
-__device__ __forceinline__ void put_rows(unsigned short* lds, bf16x8 r0, bf16x8 r1, int lane)
-{
-    put_rows_s<LDS_ROW>(lds, r0, r1, lane);
+    stage_rows<D, TileShape<D>::ROW_T>(lds, r, lane);
 }
 
 // dQ^T += K^T dS^T over two 16-entry tiles.  Key rows are in LDS (la, lb);
@@ -83,22 +79,22 @@ __device__ __forceinline__ void put_rows(unsigned short* lds, bf16x8 r0, bf16x8 
 // pe != nullptr: entries ea + 4(lane/16) + r (tile a) and ea + 16 + ... (tile
 // b) below K1 are level-1 pooled tokens; their P and dS are stored at
 // pe[entry][0 | 1][query] for the key-major dk/dv pass.
-template <bool MASK>
-__device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1, bf16x8 bd0,
-                                        bf16x8 bd1, float nl2, float Dq, bf16x8 ka0, bf16x8 ka1,
-                                        bf16x8 kb0, bf16x8 kb1, bf16x8 va0, bf16x8 va1,
-                                        bf16x8 vb0, bf16x8 vb1, const unsigned short* la,
-                                        const unsigned short* lb, int na, int nb, float c,
-                                        int lane, float* pe = nullptr, int ea = 0, int K1 = 0,
-                                        const float* ba = nullptr, const float* bb = nullptr)
+template <bool MASK, int D>
+__device__ __forceinline__ void dq_pair(f32x4 (&acc)[D / 16], const bf16x8 (&bq)[D / 32],
+                                        const bf16x8 (&bd)[D / 32], float nl2, float Dq,
+                                        const bf16x8 (&ka)[D / 32], const bf16x8 (&kb)[D / 32],
+                                        const bf16x8 (&va)[D / 32], const bf16x8 (&vb)[D / 32],
+                                        const unsigned short* la, const unsigned short* lb,
+                                        int na, int nb, float c, int lane, float* pe = nullptr,
+                                        int ea = 0, int K1 = 0, const float* ba = nullptr,
+                                        const float* bb = nullptr)
 {
     const int gq = lane >> 4;
     const int rr = (lane & 15) >> 2, xx = lane & 3;
-    const f32x4 zero = {};
-    const f32x4 sa = mfma32(ka1, bq1, mfma32(ka0, bq0, zero));
-    const f32x4 sb = mfma32(kb1, bq1, mfma32(kb0, bq0, zero));
-    const f32x4 pa = mfma32(va1, bd1, mfma32(va0, bd0, zero));  // dP^T
-    const f32x4 pb = mfma32(vb1, bd1, mfma32(vb0, bd0, zero));
+    const f32x4 sa = scores<D>(ka, bq);
+    const f32x4 sb = scores<D>(kb, bq);
+    const f32x4 pa = scores<D>(va, bd);  // dP^T
+    const f32x4 pb = scores<D>(vb, bd);
     bf16x8 bs;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -126,8 +122,8 @@ __device__ __forceinline__ void dq_pair(f32x4 (&acc)[4], bf16x8 bq0, bf16x8 bq1,
         bs[4 + r] = (bf16)dSb;
     }
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const int off = (4 * gq + rr) * LDS_ROW + 16 * d + 4 * xx;
+    for (int d = 0; d < D / 16; ++d) {
+        const int off = (4 * gq + rr) * TileShape<D>::ROW_T + 16 * d + 4 * xx;
         bf16x4 x0 = lds_read_tr(la + off), x1 = lds_read_tr(lb + off);
         bf16x8 ak = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
         acc[d] = mfma32(ak, bs, acc[d]);
@@ -138,14 +134,14 @@ constexpr int MAX_E = MAX_L * 64;  // pooled entries per query block (sum of the
 
 // Per-wave LDS of dq: two key tiles (160-byte rows, read as operands and
 // transposed), two value tiles (144-byte rows) and the pooled-entry table.
-template <int ECAP>
+template <int ECAP, int D>
 struct DqLds {
-    static constexpr int K_TILE = BS * LDS_ROW;
-    static constexpr int V_TILE = BS * ROW_A;
+    static constexpr int K_TILE = BS * TileShape<D>::ROW_T;
+    static constexpr int V_TILE = BS * TileShape<D>::ROW_A;
     static constexpr int PER_WAVE = 2 * K_TILE + 2 * V_TILE + 2 * ECAP;
 };
 
-template <int ECAP>
+template <int ECAP, int D>
 __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict__ q,
                                                const unsigned short* __restrict__ k,
                                                const unsigned short* __restrict__ v,
@@ -154,7 +150,9 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
                                                const unsigned short* __restrict__ dout,
                                                unsigned short* __restrict__ dq, Geo g, Ws w)
 {
-    using Lay = DqLds<ECAP>;
+    using Lay = DqLds<ECAP, D>;
+    using TS = TileShape<D>;
+    constexpr int NI = TS::NI;
     __shared__ __attribute__((aligned(16))) unsigned short smem[4][Lay::PER_WAVE];
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, nq = lane & 15;
@@ -164,16 +162,23 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
     const float c = g.scale * LOG2E;
     const long hbase = (long)gh * g.N * D;
     const long rowq = hbase + ((long)i * BS + nq) * D;
-    const bf16x8 bq0 = ld8(q + rowq + 8 * gq), bq1 = ld8(q + rowq + 32 + 8 * gq);
-    const bf16x8 bd0 = ld8(dout + rowq + 8 * gq), bd1 = ld8(dout + rowq + 32 + 8 * gq);
+    bf16x8 bq[NI], bd[NI];  // query and dO rows lane%16, channels 32u + 8(lane/16) ..
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+        bq[u] = ld8(q + rowq + 32 * u + 8 * gq);
+        bd[u] = ld8(dout + rowq + 32 * u + 8 * gq);
+    }
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
     const int myj = lane < g.K ? sel[lane] : 0;
     float Dq;
     {
-        const bf16x8 o0 = ld8(o + rowq + 8 * gq), o1 = ld8(o + rowq + 32 + 8 * gq);
         float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += (float)bd0[e] * (float)o0[e] + (float)bd1[e] * (float)o1[e];
+        for (int u = 0; u < NI; ++u) {
+            const bf16x8 ou = ld8(o + rowq + 32 * u + 8 * gq);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += (float)bd[u][e] * (float)ou[e];
+        }
         Dq = sum_x4(s);
     }
     const long tok = (long)gh * g.N + (long)i * BS + nq;
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
     }
     lds_fence();
 
-    f32x4 acc[4] = {};
+    f32x4 acc[D / 16] = {};
     unsigned short* la = smem[wv];  // key tiles
     unsigned short* lb = la + Lay::K_TILE;
     unsigned short* lva = lb + Lay::K_TILE;  // value tiles, read as operands only
@@ -203,54 +208,53 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
     const int NF = (g.K + 1) / 2;
     const int NT = (E + BS - 1) / BS;
     const int NP = NF + (NT + 1) / 2;
-    const int sr = lane >> 3, sc = (lane & 7) * 8;
-    auto load_pair = [&](DqPair& f, int p) {
-        long ka, kb, ka8, kb8;
+    const int sr = lane / TS::LPR, sc = (lane % TS::LPR) * 8;
+    auto load_pair = [&](DqPair<D>& f, int p) {
+        long ka[NI], kb[NI];  // element offsets of row sr + RPI u of tiles a and b
         const unsigned short *kp, *vp;
         if (p < NF) {
             const int ja = __builtin_amdgcn_readlane(myj, min(2 * p, g.K - 1));
             const int jb = __builtin_amdgcn_readlane(myj, min(2 * p + 1, g.K - 1));
-            ka = hbase + ((long)ja * BS + sr) * D + sc;
-            kb = hbase + ((long)jb * BS + sr) * D + sc;
-            ka8 = ka + 8 * D;
-            kb8 = kb + 8 * D;
+#pragma unroll
+            for (int u = 0; u < NI; ++u) {
+                ka[u] = hbase + ((long)ja * BS + sr + TS::RPI * u) * D + sc;
+                kb[u] = hbase + ((long)jb * BS + sr + TS::RPI * u) * D + sc;
+            }
             kp = k;
             vp = v;
-        } else {
+        } else {  // pooled pairs exist only when E > 0
             const int t = 2 * (p - NF);
-            ka = (long)ent[min(BS * t + sr, E - 1)] * D + sc;
-            ka8 = (long)ent[min(BS * t + sr + 8, E - 1)] * D + sc;
-            kb = (long)ent[min(BS * t + BS + sr, E - 1)] * D + sc;
-            kb8 = (long)ent[min(BS * t + BS + sr + 8, E - 1)] * D + sc;
+#pragma unroll
+            for (int u = 0; u < NI; ++u) {
+                ka[u] = (long)ent[min(BS * t + sr + TS::RPI * u, E - 1)] * D + sc;
+                kb[u] = (long)ent[min(BS * t + BS + sr + TS::RPI * u, E - 1)] * D + sc;
+            }
             kp = w.kb16;
             vp = w.vb16;
         }
-        f.kra0 = ld8(kp + ka);
-        f.kra1 = ld8(kp + ka8);
-        f.vra0 = ld8(vp + ka);
-        f.vra1 = ld8(vp + ka8);
-        f.krb0 = ld8(kp + kb);
-        f.krb1 = ld8(kp + kb8);
-        f.vrb0 = ld8(vp + kb);
-        f.vrb1 = ld8(vp + kb8);
+        // issue order: key rows, then value rows, of tile a, then of tile b
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.kra[u] = ld8(kp + ka[u]);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.vra[u] = ld8(vp + ka[u]);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.krb[u] = ld8(kp + kb[u]);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.vrb[u] = ld8(vp + kb[u]);
     };
-    auto step = [&](const DqPair& f, int p) {
-        put_rows(la, f.kra0, f.kra1, lane);
-        put_rows(lb, f.krb0, f.krb1, lane);
-        put_rows_s<ROW_A>(lva, f.vra0, f.vra1, lane);
-        put_rows_s<ROW_A>(lvb, f.vrb0, f.vrb1, lane);
+    auto step = [&](const DqPair<D>& f, int p) {
+        put_rows<D>(la, f.kra, lane);
+        put_rows<D>(lb, f.krb, lane);
+        stage_rows<D, TS::ROW_A>(lva, f.vra, lane);
+        stage_rows<D, TS::ROW_A>(lvb, f.vrb, lane);
         lds_fence();
-        const bf16x8 ka0 = *(const bf16x8*)(la + nq * LDS_ROW + 8 * gq);
-        const bf16x8 ka1 = *(const bf16x8*)(la + nq * LDS_ROW + 32 + 8 * gq);
-        const bf16x8 kb0 = *(const bf16x8*)(lb + nq * LDS_ROW + 8 * gq);
-        const bf16x8 kb1 = *(const bf16x8*)(lb + nq * LDS_ROW + 32 + 8 * gq);
-        const bf16x8 va0 = *(const bf16x8*)(lva + nq * ROW_A + 8 * gq);
-        const bf16x8 va1 = *(const bf16x8*)(lva + nq * ROW_A + 32 + 8 * gq);
-        const bf16x8 vb0 = *(const bf16x8*)(lvb + nq * ROW_A + 8 * gq);
-        const bf16x8 vb1 = *(const bf16x8*)(lvb + nq * ROW_A + 32 + 8 * gq);
+        bf16x8 ka[NI], kb[NI], va[NI], vb[NI];
+        operand_rows<D, TS::ROW_T>(la, ka, lane);
+        operand_rows<D, TS::ROW_T>(lb, kb, lane);
+        operand_rows<D, TS::ROW_A>(lva, va, lane);
+        operand_rows<D, TS::ROW_A>(lvb, vb, lane);
         if (p < NF && g.K > 1) {
-            dq_pair<false>(acc, bq0, bq1, bd0, bd1, nl2, Dq, ka0, ka1, kb0, kb1, va0, va1, vb0,
-                           vb1, la, lb, BS, BS, c, lane);
+            dq_pair<false, D>(acc, bq, bd, nl2, Dq, ka, kb, va, vb, la, lb, BS, BS, c, lane);
         } else {
             const int e0 = p < NF ? 0 : BS * 2 * (p - NF);
             const int na = p < NF ? BS : max(0, min(BS, E - e0));
@@ -265,11 +269,11 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
                 ba[r] = pooled ? g.lb2 * (float)g.entry_level(ea) : 0.f;
                 bb[r] = pooled ? g.lb2 * (float)g.entry_level(ea + BS) : 0.f;
             }
-            dq_pair<true>(acc, bq0, bq1, bd0, bd1, nl2, Dq, ka0, ka1, kb0, kb1, va0, va1, vb0,
-                          vb1, la, lb, na, nb, c, lane, pe, e0, g.K, ba, bb);
+            dq_pair<true, D>(acc, bq, bd, nl2, Dq, ka, kb, va, vb, la, lb, na, nb, c, lane, pe,
+                             e0, g.K, ba, bb);
         }
     };
-    DqPair A, B;
+    DqPair<D> A, B;
     load_pair(A, 0);
     for (int p = 0;; p += 2) {
         load_pair(B, min(p + 1, NP - 1));
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
     }
     const long obase = rowq + 4 * gq;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < D / 16; ++d) {
         u16x4 r4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) r4[r] = f2bf(acc[d][r] * g.scale);
@@ -289,39 +293,38 @@ __global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict_
     }
 }
 
-// Stage a 16-token query-side tile (rows of x) into LDS, zeros if !live.
-__device__ __forceinline__ void stage_rows(unsigned short* lds, const unsigned short* x, long base,
-                                           bool live, int lane)
-{
-    const int sr = lane >> 3, sc = (lane & 7) * 8;
-    const bf16x8 z = {};
-    *(bf16x8*)(lds + sr * LDS_ROW + sc) = live ? ld8(x + base + sr * D + sc) : z;
-    *(bf16x8*)(lds + (sr + 8) * LDS_ROW + sc) = live ? ld8(x + base + (sr + 8) * D + sc) : z;
-}
-
+template <int D>
 __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __restrict__ q,
                                                        const float* __restrict__ lse,
                                                        const unsigned short* __restrict__ dout,
                                                        Geo g, Ws w)
 {
+    using TS = TileShape<D>;
+    constexpr int NI = TS::NI, ND = D / 16;
     // per-wave Q and dO tiles; after the last tile the same memory holds the
     // four waves' partial sums for the cross-wave reduction
-    __shared__ __attribute__((aligned(16))) unsigned short smem[4][2][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned short smem[4][2][TILE<D>];
     float* red = (float*)&smem[0][0][0];  // [wave][dtile][r][lane], one kind at a time
-    static_assert(sizeof(smem) >= 4 * 4 * 4 * 64 * sizeof(float), "reduction buffer");
+    static_assert(sizeof(smem) >= 4 * ND * 4 * 64 * sizeof(float), "reduction buffer");
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int gq = lane >> 4, nq = lane & 15;
     const int gh = blockIdx.x / g.n[2], a2 = blockIdx.x % g.n[2];
     const float c = g.scale * LOG2E;
     const int rr = (lane & 15) >> 2, xx = lane & 3;
-    const int sr = lane >> 3, sc = (lane & 7) * 8;
+    const int sr = lane / TS::LPR, sc = (lane % TS::LPR) * 8;
     unsigned short* lq = smem[wv][0];
     unsigned short* ld = smem[wv][1];
-    const f32x4 zero = {};
-    // this wave's four query blocks i = 16 a2 + 4 wv + u (u < 4)
+    // this wave's four query blocks i = 16 a2 + 4 wv + u (u < 4); load v of
+    // a block covers its row sr + RPI v
     auto row_addr = [&](int u) {
         const int i = 16 * a2 + 4 * wv + u;
         return ((long)gh * g.N + (long)i * BS + sr) * D + sc;
+    };
+    auto load_rows = [&](bf16x8 (&xq)[NI], bf16x8 (&xd)[NI], long a) {
+#pragma unroll
+        for (int v = 0; v < NI; ++v) xq[v] = ld8(q + a + (long)TS::RPI * v * D);
+#pragma unroll
+        for (int v = 0; v < NI; ++v) xd[v] = ld8(dout + a + (long)TS::RPI * v * D);
     };
     for (int l = 2; l <= g.L; ++l) {
         const int al = a2 >> (4 * (l - 2));
@@ -330,34 +333,33 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
         const float lb = g.lb2 * (float)l;  // size bias of a level-l token (log2)
         for (int e0 = 0; e0 < Kl; e0 += BS) {
             const bool ev = e0 + nq < Kl;
-            bf16x8 bk0 = {}, bk1 = {}, bv0 = {}, bv1 = {};
+            bf16x8 bk[NI], bv[NI];  // entry rows lane%16, channels 32u + 8(lane/16) ..
+#pragma unroll
+            for (int u = 0; u < NI; ++u) bk[u] = bv[u] = bf16x8{};
             if (ev) {
                 long off = ((long)gh * g.n[l] + sel[e0 + nq]) * D;
-                bk0 = ld8f(w.kbar[l - 1] + off + 8 * gq);
-                bk1 = ld8f(w.kbar[l - 1] + off + 32 + 8 * gq);
-                bv0 = ld8f(w.vbar[l - 1] + off + 8 * gq);
-                bv1 = ld8f(w.vbar[l - 1] + off + 32 + 8 * gq);
+#pragma unroll
+                for (int u = 0; u < NI; ++u) {
+                    bk[u] = ld8f(w.kbar[l - 1] + off + 32 * u + 8 * gq);
+                    bv[u] = ld8f(w.vbar[l - 1] + off + 32 * u + 8 * gq);
+                }
             }
-            f32x4 ak[4] = {}, av[4] = {};
+            f32x4 ak[ND] = {}, av[ND] = {};
             // rows of block u + 1 are loaded while block u is computed
-            long a = row_addr(0);
-            bf16x8 q0 = ld8(q + a), q1 = ld8(q + a + 8 * D);
-            bf16x8 d0 = ld8(dout + a), d1 = ld8(dout + a + 8 * D);
+            bf16x8 xq[NI], xd[NI];
+            load_rows(xq, xd, row_addr(0));
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i = 16 * a2 + 4 * wv + u;
-                put_rows(lq, q0, q1, lane);
-                put_rows(ld, d0, d1, lane);
-                a = row_addr(min(u + 1, 3));
-                q0 = ld8(q + a); q1 = ld8(q + a + 8 * D);
-                d0 = ld8(dout + a); d1 = ld8(dout + a + 8 * D);
+                put_rows<D>(lq, xq, lane);
+                put_rows<D>(ld, xd, lane);
+                load_rows(xq, xd, row_addr(min(u + 1, 3)));
                 lds_fence();
-                const bf16x8 aq0 = *(const bf16x8*)(lq + nq * LDS_ROW + 8 * gq);
-                const bf16x8 aq1 = *(const bf16x8*)(lq + nq * LDS_ROW + 32 + 8 * gq);
-                const bf16x8 ad0 = *(const bf16x8*)(ld + nq * LDS_ROW + 8 * gq);
-                const bf16x8 ad1 = *(const bf16x8*)(ld + nq * LDS_ROW + 32 + 8 * gq);
-                f32x4 s = mfma32(aq1, bk1, mfma32(aq0, bk0, zero));  // S[query][entry]
-                f32x4 dp = mfma32(ad1, bv1, mfma32(ad0, bv0, zero));
+                bf16x8 aq[NI], ad[NI];
+                operand_rows<D, TS::ROW_T>(lq, aq, lane);
+                operand_rows<D, TS::ROW_T>(ld, ad, lane);
+                f32x4 s = scores<D>(aq, bk);  // S[query][entry]
+                f32x4 dp = scores<D>(ad, bv);
                 const long tq = (long)gh * g.N + (long)i * BS + 4 * gq;
                 const float4 l4 = *(const float4*)(lse + tq);
                 const float4 d4 = *(const float4*)(w.delta + tq);
@@ -370,8 +372,8 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
                     pS[r] = (bf16)(P * (dp[r] - dr[r]));
                 }
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const int off = (4 * gq + rr) * LDS_ROW + 16 * d + 4 * xx;
+                for (int d = 0; d < ND; ++d) {
+                    const int off = (4 * gq + rr) * TS::ROW_T + 16 * d + 4 * xx;
                     ak[d] = mfma16(lds_read_tr(lq + off), pS, ak[d]);
                     av[d] = mfma16(lds_read_tr(ld + off), pP, av[d]);
                 }
@@ -380,13 +382,14 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
             for (int kind = 0; kind < 2; ++kind) {
                 __syncthreads();  // tiles (or the previous kind) no longer read
 #pragma unroll
-                for (int d = 0; d < 4; ++d)
+                for (int d = 0; d < ND; ++d)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        red[((wv * 4 + d) * 4 + r) * 64 + lane] = kind == 0 ? ak[d][r] : av[d][r];
+                        red[((wv * ND + d) * 4 + r) * 64 + lane] = kind == 0 ? ak[d][r] : av[d][r];
                 __syncthreads();
-                for (int x = threadIdx.x; x < 4 * 4 * 64; x += blockDim.x) {
-                    const float s = red[x] + red[1024 + x] + red[2048 + x] + red[3072 + x];
+                for (int x = threadIdx.x; x < ND * 4 * 64; x += blockDim.x) {
+                    const float s = red[x] + red[ND * 256 + x] + red[2 * ND * 256 + x] +
+                                    red[3 * ND * 256 + x];
                     const int d = x >> 8, r = (x >> 6) & 3, ln = x & 63;
                     const int ent = e0 + (ln & 15), dim = 16 * d + 4 * (ln >> 4) + r;
                     if (ent < Kl) {
@@ -403,9 +406,12 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
 
 // dbar_l[j] = sum over level-l query blocks a that chose j, and over the
 // level-2 blocks under a, of the partial sums at j's slot in a's list.  One
-// wave per pooled block, lane = channel; list entries in ascending order.
+// wave per pooled block, lane = channels lane + 64 c; list entries in
+// ascending order.
+template <int D>
 __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
 {
+    constexpr int NC = D / 64;  // channels dim + 64 c per lane
     const long blk = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (blk >= (long)g.G * g.n[l]) return;
     const int dim = threadIdx.x & 63;
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
     const unsigned char* sl = w.slot[l - 1] + (long)gh * g.n[l] * Kl;
     const int span = 1 << (4 * (l - 2));  // level-2 blocks per level-l block
     const float* part = w.part[l - 1] + (long)gh * g.n[2] * Kl * 2 * D + dim;
-    float sk = 0.f, sv = 0.f;
+    float sk[NC] = {}, sv[NC] = {};
     const int beg = uniform(rp[j]), end = uniform(rp[j + 1]);
     // list entries in batches of 64: lane e holds entry beg + e (row offset
     // into the partials).  The batch's (entry, level-2 block) rows are summed
@@ -428,26 +434,34 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
         if (lane < ne) off = cl[e0 + lane] * span * Kl + sl[e0 + lane];
         const int nrow = ne * span;
         for (int q0 = 0; q0 < nrow; q0 += 8) {
-            float vk[8], vv[8];
+            float vk[8][NC], vv[8][NC];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int qq = min(q0 + u, nrow - 1);
                 const int e = qq / span, a2 = qq % span;
                 const long o = ((long)__builtin_amdgcn_readlane(off, e) + (long)a2 * Kl) * 2 * D;
-                vk[u] = part[o];
-                vv[u] = part[o + D];
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    vk[u][c] = part[o + 64 * c];
+                    vv[u][c] = part[o + D + 64 * c];
+                }
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (q0 + u < nrow) {
-                    sk += vk[u];
-                    sv += vv[u];
-                }
+                if (q0 + u < nrow)
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        sk[c] += vk[u][c];
+                        sv[c] += vv[u][c];
+                    }
         }
     }
     float* dst = w.dbar[l - 1] + blk * 2 * D;
-    dst[dim] = sk;
-    dst[D + dim] = sv;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        dst[dim + 64 * c] = sk[c];
+        dst[D + dim + 64 * c] = sv[c];
+    }
 }
 
 // dk/dv: one wave (and workgroup) per key block j, over the query blocks of
@@ -459,13 +473,14 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
 //   dS_e/16 to every key column -- P_e and dS_e come from the dq pass
 //   dV^T += dO^T P, dK^T += Q^T dS   (16x16x16 MFMA over the 16 queries;
 //                                     Q^T, dO^T read transposed from LDS)
+template <int D>
 struct QBlock {
-    bf16x8 q0, q1, d0, d1;  // rows sr and sr+8, channels sc .. sc+7
-    float x;                // lane < 16: lse of row lane; < 32: delta of row
-                            // lane - 16; else the level-1 pooled P (lanes 32..47)
-                            // and dS (48..63) of row lane % 16
+    bf16x8 q[D / 32], d[D / 32];  // load u: row sr + RPI u, channels sc .. sc+7
+    float x;  // lane < 16: lse of row lane; < 32: delta of row lane - 16; else the
+              // level-1 pooled P (lanes 32..47) and dS (48..63) of row lane % 16
 };
 
+template <int D>
 __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict__ q,
                                                 const unsigned short* __restrict__ k,
                                                 const unsigned short* __restrict__ v,
@@ -474,7 +489,9 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
                                                 unsigned short* __restrict__ dk,
                                                 unsigned short* __restrict__ dv, Geo g, Ws w)
 {
-    __shared__ __attribute__((aligned(16))) unsigned short lq[TILE], ld[TILE];
+    using TS = TileShape<D>;
+    constexpr int NI = TS::NI, ND = D / 16;
+    __shared__ __attribute__((aligned(16))) unsigned short lq[TILE<D>], ld[TILE<D>];
     __shared__ __attribute__((aligned(16))) float aux[4 * BS];
     const int lane = threadIdx.x;
     const int gq = lane >> 4, nq = lane & 15;
@@ -485,15 +502,18 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     const long hbase = (long)gh * g.N * D;
     const long tbase = (long)gh * g.N;
     const long kbase = hbase + (long)j * BS * D;
-    const bf16x8 bk0 = ld8(k + kbase + nq * D + 8 * gq), bk1 = ld8(k + kbase + nq * D + 32 + 8 * gq);
-    const bf16x8 bv0 = ld8(v + kbase + nq * D + 8 * gq), bv1 = ld8(v + kbase + nq * D + 32 + 8 * gq);
+    bf16x8 bk[NI], bv[NI];  // the key block's rows lane%16, channels 32u + 8(lane/16) ..
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+        bk[u] = ld8(k + kbase + nq * D + 32 * u + 8 * gq);
+        bv[u] = ld8(v + kbase + nq * D + 32 * u + 8 * gq);
+    }
     const int* rp = w.rowptr[0] + (long)gh * (g.n[1] + 1);
     const int* list = w.col[0] + (long)gh * g.n[1] * g.K;
     const unsigned char* slots = w.slot[0] + (long)gh * g.n[1] * g.K;
     const int beg = uniform(rp[j]), end = uniform(rp[j + 1]);
     const int rr = (lane & 15) >> 2, xx = lane & 3;
-    const f32x4 zero = {};
-    f32x4 accK[4] = {}, accV[4] = {};
+    f32x4 accK[ND] = {}, accV[ND] = {};
     // live == false (the padding step of an odd-length chunk): the MFMAs run
     // on valid rows but every P and dS is 0
     // per-row scalars as the step uses them: -lse * log2(e) (lanes < 16), so
@@ -501,9 +521,9 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     // step (live == false) -inf there and 0 for the pooled P and dS, which
     // makes every P and dS of the step exactly 0
     const bool lse_lane = lane < 16, pe_lane = lane >= 32;
-    auto step = [&](const QBlock& f, bool live) {
-        put_rows(lq, f.q0, f.q1, lane);
-        put_rows(ld, f.d0, f.d1, lane);
+    auto step = [&](const QBlock<D>& f, bool live) {
+        put_rows<D>(lq, f.q, lane);
+        put_rows<D>(ld, f.d, lane);
         const float nls = live ? -LOG2E * f.x : -INFINITY;
         aux[lane] = lse_lane ? nls : (pe_lane && !live) ? 0.f : f.x;
         lds_fence();
@@ -511,12 +531,11 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
         const float4 e4 = *(const float4*)(aux + BS + 4 * gq);
         const float4 p4 = *(const float4*)(aux + 2 * BS + 4 * gq);
         const float4 s4 = *(const float4*)(aux + 3 * BS + 4 * gq);
-        const bf16x8 aq0 = *(const bf16x8*)(lq + nq * LDS_ROW + 8 * gq);
-        const bf16x8 aq1 = *(const bf16x8*)(lq + nq * LDS_ROW + 32 + 8 * gq);
-        const bf16x8 ad0 = *(const bf16x8*)(ld + nq * LDS_ROW + 8 * gq);
-        const bf16x8 ad1 = *(const bf16x8*)(ld + nq * LDS_ROW + 32 + 8 * gq);
-        const f32x4 s = mfma32(aq1, bk1, mfma32(aq0, bk0, zero));   // S[query][key]
-        const f32x4 dp = mfma32(ad1, bv1, mfma32(ad0, bv0, zero));  // dP[query][key]
+        bf16x8 aq[NI], ad[NI];
+        operand_rows<D, TS::ROW_T>(lq, aq, lane);
+        operand_rows<D, TS::ROW_T>(ld, ad, lane);
+        const f32x4 s = scores<D>(aq, bk);   // S[query][key]
+        const f32x4 dp = scores<D>(ad, bv);  // dP[query][key]
         const float lr[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dr[4] = {e4.x, e4.y, e4.z, e4.w};
         const float pr[4] = {p4.x, p4.y, p4.z, p4.w};
@@ -534,8 +553,8 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
             bs[r] = (bf16)ds;
         }
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const int off = (4 * gq + rr) * LDS_ROW + 16 * d + 4 * xx;
+        for (int d = 0; d < ND; ++d) {
+            const int off = (4 * gq + rr) * TS::ROW_T + 16 * d + 4 * xx;
             accV[d] = mfma16(lds_read_tr(ld + off), bp, accV[d]);
             accK[d] = mfma16(lds_read_tr(lq + off), bs, accK[d]);
         }
@@ -543,8 +562,8 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     // the list is read 64 entries at a time, one per lane, and each step takes
     // its query block and slot with readlane, so no load waits on another
     int myi = 0, mys = 0;
-    // buffer loads: rows sr and sr + 8 of block i at lane offset voff (+1024),
-    // block offset i * 2048 bytes; one dword per lane carries the block's
+    // buffer loads: rows sr + RPI u of block i at lane offset voff + 1024 u,
+    // block offset i * 32 D bytes; one dword per lane carries the block's
     // per-row scalars (lse, delta, pooled P and dS), each lane reading from
     // one of three resources -- the other two give 0 for an out-of-range
     // offset -- so there is no divergent branch
@@ -553,19 +572,19 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + hbase, head_bytes);
     const __amdgpu_buffer_rsrc_t rlse = make_rsrc(lse + tbase, (unsigned)g.N * 4);
     const __amdgpu_buffer_rsrc_t rdel = make_rsrc(w.delta + tbase, (unsigned)g.N * 4);
-    const int sr = lane >> 3, sc = (lane & 7) * 8;
+    const int sr = lane / TS::LPR, sc = (lane % TS::LPR) * 8;
     const int voff = (sr * D + sc) * 2;
     const int off_lse = lane < 16 ? 4 * lane : OFF_NONE;
     const int off_del = (lane >= 16 && lane < 32) ? 4 * (lane - 16) : OFF_NONE;
     const int off_pe = lane >= 32 ? 4 * (lane - 32) : OFF_NONE;
-    auto fetch = [&](QBlock& f, int t) {
+    auto fetch = [&](QBlock<D>& f, int t) {
         const int i = __builtin_amdgcn_readlane(myi, t);
         const int sl = __builtin_amdgcn_readlane(mys, t);
         const int so = i * (BS * D * 2);
-        f.q0 = bload8(rq, voff, so);
-        f.q1 = bload8(rq, voff + 8 * D * 2, so);
-        f.d0 = bload8(rdo, voff, so);
-        f.d1 = bload8(rdo, voff + 8 * D * 2, so);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.q[u] = bload8(rq, voff + 1024 * u, so);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.d[u] = bload8(rdo, voff + 1024 * u, so);
         const __amdgpu_buffer_rsrc_t rpe =
             make_rsrc(w.pe1 + (((long)gh * g.n[1] + i) * g.K + sl) * 2 * BS, 2 * BS * 4);
         f.x = bloadf(rlse, off_lse, i * BS * 4) + bloadf(rdel, off_del, i * BS * 4) +
@@ -575,7 +594,7 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     // The loop body is one basic block: a conditional exit between a fetch
     // and its use would let the compiler sink the loads down to the use.
     // Fetches past the end re-read the last block (valid memory).
-    QBlock A, B;
+    QBlock<D> A, B;
     for (int cb = beg; cb < end; cb += 64) {
         const int n = min(64, end - cb);
         myi = lane < n ? list[cb + lane] : 0;
@@ -591,7 +610,7 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     // epilogue: scale, add the pooled-level gradients (levels >= 2), store
     const long obase = kbase + nq * D + 4 * gq;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < ND; ++d) {
         float xk[4], xv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -619,9 +638,27 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
 
 // ------------------------------------------------------------ fp32 path
 
-// One wave per row, lane = channel: every dot product is a wave sum.
+// One wave per row, lane = channels lane + 64 c: every dot product is a wave
+// sum.
 
-template <typename F>
+// <a, row> over the D channels, a held as the lane's channels
+template <int D>
+__device__ __forceinline__ float row_dot(const float (&a)[D / 64], const float* row, int lane)
+{
+    float part = a[0] * row[lane];
+#pragma unroll
+    for (int c = 1; c < D / 64; ++c) part = fmaf(a[c], row[lane + 64 * c], part);
+    return wave_sum(part);
+}
+
+template <int D>
+__device__ __forceinline__ void lane_channels(float (&x)[D / 64], const float* row, int lane)
+{
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) x[c] = row[lane + 64 * c];
+}
+
+template <int D, typename F>
 __device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const float* k,
                                                const float* v, int gh, int t, F f)
 {
@@ -644,6 +681,7 @@ __device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const 
 }
 
 // dq and delta: one wave per query token
+template <int D>
 __global__ __launch_bounds__(256) void dq_f32(const float* __restrict__ q,
                                               const float* __restrict__ k,
                                               const float* __restrict__ v,
@@ -652,62 +690,82 @@ __global__ __launch_bounds__(256) void dq_f32(const float* __restrict__ q,
                                               const float* __restrict__ dout,
                                               float* __restrict__ dq, Geo g, Ws w)
 {
+    constexpr int NC = D / 64;
     const long tg = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (tg >= (long)g.G * g.N) return;
     const int lane = threadIdx.x & 63;
     const int gh = (int)(tg / g.N), t = (int)(tg % g.N);
-    const float qc = q[tg * D + lane], dc = dout[tg * D + lane];
-    const float Dt = wave_sum(dc * o[tg * D + lane]);
+    float qc[NC], dc[NC], acc[NC];
+    lane_channels<D>(qc, q + tg * D, lane);
+    lane_channels<D>(dc, dout + tg * D, lane);
+    const float Dt = row_dot<D>(dc, o + tg * D, lane);
     if (lane == 0) w.delta[tg] = Dt;
     const float lt = lse[tg];
-    float acc = 0.f;
-    for_each_entry(g, w, k, v, gh, t, [&](const float* kr, const float* vr, float bias) {
-        const float kc = kr[lane];
-        const float z = wave_sum(qc * kc);
-        const float dp = wave_sum(dc * vr[lane]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = 0.f;
+    for_each_entry<D>(g, w, k, v, gh, t, [&](const float* kr, const float* vr, float bias) {
+        float kc[NC];
+        lane_channels<D>(kc, kr, lane);
+        const float z = row_dot<D>(qc, kr, lane);
+        const float dp = row_dot<D>(dc, vr, lane);
         const float P = expf(z * g.scale + bias - lt);
         const float ds = P * (dp - Dt) * g.scale;
-        acc = fmaf(ds, kc, acc);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] = fmaf(ds, kc[c], acc[c]);
     });
-    dq[tg * D + lane] = acc;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) dq[tg * D + lane + 64 * c] = acc[c];
 }
 
 // pooled-token gradients, every level: one wave per level-l block
+template <int D>
 __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
                                                   const float* __restrict__ lse,
                                                   const float* __restrict__ dout, Geo g, Ws w,
                                                   int l)
 {
+    constexpr int NC = D / 64;
     const long blk = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (blk >= (long)g.G * g.n[l]) return;
     const int lane = threadIdx.x & 63;
     const int gh = (int)(blk / g.n[l]), j = (int)(blk % g.n[l]);
-    const float kb = w.kbar[l - 1][blk * D + lane];
-    const float vb = w.vbar[l - 1][blk * D + lane];
+    float kb[NC], vb[NC], sk[NC], sv[NC];
+    lane_channels<D>(kb, w.kbar[l - 1] + blk * D, lane);
+    lane_channels<D>(vb, w.vbar[l - 1] + blk * D, lane);
     const int* rp = w.rowptr[l - 1] + (long)gh * (g.n[l] + 1);
     const int* cl = w.col[l - 1] + (long)gh * g.n[l] * g.Kl[l];
     const long span = 1l << (4 * l);
     const float bias = g.lb2 * (float)l * LN2;  // size bias of a level-l token
-    float sk = 0.f, sv = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sk[c] = sv[c] = 0.f;
     for (int e = rp[j]; e < rp[j + 1]; ++e) {
         const long a = cl[e];
         for (long t = a * span; t < (a + 1) * span; ++t) {
             const long tg = (long)gh * g.N + t;
-            const float qc = q[tg * D + lane], dc = dout[tg * D + lane];
-            const float z = wave_sum(qc * kb);
-            const float dp = wave_sum(dc * vb);
+            float qc[NC], dc[NC];
+            lane_channels<D>(qc, q + tg * D, lane);
+            lane_channels<D>(dc, dout + tg * D, lane);
+            const float z = row_dot<D>(kb, q + tg * D, lane);
+            const float dp = row_dot<D>(vb, dout + tg * D, lane);
             const float P = expf(z * g.scale + bias - lse[tg]);
             const float ds = P * (dp - w.delta[tg]);
-            sk = fmaf(ds * g.scale, qc, sk);
-            sv = fmaf(P, dc, sv);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                sk[c] = fmaf(ds * g.scale, qc[c], sk[c]);
+                sv[c] = fmaf(P, dc[c], sv[c]);
+            }
         }
     }
     float* dst = w.dbar[l - 1] + blk * 2 * D;
-    dst[lane] = sk;
-    dst[D + lane] = sv;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        dst[lane + 64 * c] = sk[c];
+        dst[D + lane + 64 * c] = sv[c];
+    }
 }
 
 // dk, dv: one wave per key token
+template <int D>
 __global__ __launch_bounds__(256) void dkdv_f32(const float* __restrict__ q,
                                                 const float* __restrict__ k,
                                                 const float* __restrict__ v,
@@ -716,33 +774,117 @@ __global__ __launch_bounds__(256) void dkdv_f32(const float* __restrict__ q,
                                                 float* __restrict__ dk, float* __restrict__ dv,
                                                 Geo g, Ws w)
 {
+    constexpr int NC = D / 64;
     const long xg = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (xg >= (long)g.G * g.N) return;
     const int lane = threadIdx.x & 63;
     const int gh = (int)(xg / g.N), x = (int)(xg % g.N), j = x / BS;
-    const float kc = k[xg * D + lane], vc = v[xg * D + lane];
-    float ak = 0.f, av = 0.f;
+    float kc[NC], vc[NC], ak[NC], av[NC];
+    lane_channels<D>(kc, k + xg * D, lane);
+    lane_channels<D>(vc, v + xg * D, lane);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) ak[c] = av[c] = 0.f;
     const int* rp = w.rowptr[0] + (long)gh * (g.n[1] + 1);
     const int* cl = w.col[0] + (long)gh * g.n[1] * g.K;
     for (int e = rp[j]; e < rp[j + 1]; ++e)
         for (int r = 0; r < BS; ++r) {
             const long tg = (long)gh * g.N + (long)cl[e] * BS + r;
-            const float qc = q[tg * D + lane], dc = dout[tg * D + lane];
-            const float z = wave_sum(qc * kc);
-            const float dp = wave_sum(dc * vc);
+            float qc[NC], dc[NC];
+            lane_channels<D>(qc, q + tg * D, lane);
+            lane_channels<D>(dc, dout + tg * D, lane);
+            const float z = row_dot<D>(kc, q + tg * D, lane);
+            const float dp = row_dot<D>(vc, dout + tg * D, lane);
             const float P = expf(z * g.scale - lse[tg]);
             const float ds = P * (dp - w.delta[tg]) * g.scale;
-            ak = fmaf(ds, qc, ak);
-            av = fmaf(P, dc, av);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                ak[c] = fmaf(ds, qc[c], ak[c]);
+                av[c] = fmaf(P, dc[c], av[c]);
+            }
         }
     for (int l = g.l0; l <= g.L; ++l) {
         const float wgt = 1.0f / (float)(1 << (4 * l));
         const float* db = w.dbar[l - 1] + ((long)gh * g.n[l] + (x >> (4 * l))) * 2 * D;
-        ak += db[lane] * wgt;
-        av += db[D + lane] * wgt;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            ak[c] += db[lane + 64 * c] * wgt;
+            av[c] += db[D + lane + 64 * c] * wgt;
+        }
     }
-    dk[xg * D + lane] = ak;
-    dv[xg * D + lane] = av;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        dk[xg * D + lane + 64 * c] = ak[c];
+        dv[xg * D + lane + 64 * c] = av[c];
+    }
+}
+
+template <int D>
+hipError_t launch_attn_dq_d(const void* q, const void* k, const void* v, const void* out,
+                            const float* lse, const void* dout, void* dq, int dtype,
+                            const Geo& g, const Ws& w, hipStream_t st)
+{
+    if (dtype == LLSA_BF16) {
+        long nblk = (long)g.G * g.n[1];
+        auto kern = (g.n_pooled() <= 64) ? dq_bf16<64, D> : dq_bf16<MAX_E, D>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
+                           (const unsigned short*)q, (const unsigned short*)k,
+                           (const unsigned short*)v, (const unsigned short*)out, lse,
+                           (const unsigned short*)dout, (unsigned short*)dq, g, w);
+    } else {
+        long ntok = (long)g.G * g.N;  // one wave each
+        hipLaunchKernelGGL(dq_f32<D>, dim3((unsigned)((ntok + 3) / 4)), dim3(256), 0, st,
+                           (const float*)q, (const float*)k, (const float*)v, (const float*)out,
+                           lse, (const float*)dout, (float*)dq, g, w);
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_attn_enrich_d(const void* q, const float* lse, const void* dout, int dtype,
+                                const Geo& g, const Ws& w, hipStream_t st)
+{
+    if (g.l0 > g.L) return hipSuccess;
+    if (dtype == LLSA_BF16) {
+        if (g.L < 2) return hipSuccess;
+        hipLaunchKernelGGL(enrich_bwd_bf16<D>, dim3(g.G * g.n[2]), dim3(256), 0, st,
+                           (const unsigned short*)q, lse, (const unsigned short*)dout, g, w);
+        hipError_t e = hipGetLastError();
+        for (int l = 2; l <= g.L && e == hipSuccess; ++l) {
+            long n = (long)g.G * g.n[l];
+            hipLaunchKernelGGL(enrich_sum<D>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, g,
+                               w, l);
+            e = hipGetLastError();
+        }
+        return e;
+    }
+    hipError_t e = hipSuccess;
+    for (int l = g.l0; l <= g.L && e == hipSuccess; ++l) {
+        long n = (long)g.G * g.n[l];  // one wave per pooled block
+        hipLaunchKernelGGL(enrich_f32<D>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st,
+                           (const float*)q, lse, (const float*)dout, g, w, l);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+template <int D>
+hipError_t launch_attn_dkdv_d(const void* q, const void* k, const void* v, const float* lse,
+                              const void* dout, void* dk, void* dv, int dtype, const Geo& g,
+                              const Ws& w, hipStream_t st)
+{
+    if (dtype == LLSA_BF16) {
+        long nblk = (long)g.G * g.n[1];
+        hipLaunchKernelGGL(dkdv_bf16<D>, dim3((unsigned)nblk), dim3(64), 0, st,
+                           (const unsigned short*)q, (const unsigned short*)k,
+                           (const unsigned short*)v, lse, (const unsigned short*)dout,
+                           (unsigned short*)dk, (unsigned short*)dv, g, w);
+    } else {
+        long ntok = (long)g.G * g.N;  // one wave per key token
+        hipLaunchKernelGGL(dkdv_f32<D>, dim3((unsigned)((ntok + 3) / 4)), dim3(256), 0, st,
+                           (const float*)q, (const float*)k, (const float*)v, lse,
+                           (const float*)dout, (float*)dk, (float*)dv, g, w);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -751,20 +893,8 @@ hipError_t launch_attn_dq(const void* q, const void* k, const void* v, const voi
                           const float* lse, const void* dout, void* dq, int dtype, const Geo& g,
                           const Ws& w, hipStream_t st)
 {
-    if (dtype == LLSA_BF16) {
-        long nblk = (long)g.G * g.n[1];
-        auto kern = (g.n_pooled() <= 64) ? dq_bf16<64> : dq_bf16<MAX_E>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
-                           (const unsigned short*)q, (const unsigned short*)k,
-                           (const unsigned short*)v, (const unsigned short*)out, lse,
-                           (const unsigned short*)dout, (unsigned short*)dq, g, w);
-    } else {
-        long ntok = (long)g.G * g.N;  // one wave each
-        hipLaunchKernelGGL(dq_f32, dim3((unsigned)((ntok + 3) / 4)), dim3(256), 0, st,
-                           (const float*)q, (const float*)k, (const float*)v, (const float*)out,
-                           lse, (const float*)dout, (float*)dq, g, w);
-    }
-    return hipGetLastError();
+    return g.d == D128 ? launch_attn_dq_d<D128>(q, k, v, out, lse, dout, dq, dtype, g, w, st)
+                       : launch_attn_dq_d<D64>(q, k, v, out, lse, dout, dq, dtype, g, w, st);
 }
 
 // Gradients of the enriching pooled tokens (bf16: levels >= 2, level 1 being
@@ -773,47 +903,16 @@ hipError_t launch_attn_dq(const void* q, const void* k, const void* v, const voi
 hipError_t launch_attn_enrich(const void* q, const float* lse, const void* dout, int dtype,
                               const Geo& g, const Ws& w, hipStream_t st)
 {
-    if (g.l0 > g.L) return hipSuccess;
-    if (dtype == LLSA_BF16) {
-        if (g.L < 2) return hipSuccess;
-        hipLaunchKernelGGL(enrich_bwd_bf16, dim3(g.G * g.n[2]), dim3(256), 0, st,
-                           (const unsigned short*)q, lse, (const unsigned short*)dout, g, w);
-        hipError_t e = hipGetLastError();
-        for (int l = 2; l <= g.L && e == hipSuccess; ++l) {
-            long n = (long)g.G * g.n[l];
-            hipLaunchKernelGGL(enrich_sum, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, g, w,
-                               l);
-            e = hipGetLastError();
-        }
-        return e;
-    }
-    hipError_t e = hipSuccess;
-    for (int l = g.l0; l <= g.L && e == hipSuccess; ++l) {
-        long n = (long)g.G * g.n[l];  // one wave per pooled block
-        hipLaunchKernelGGL(enrich_f32, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st,
-                           (const float*)q, lse, (const float*)dout, g, w, l);
-        e = hipGetLastError();
-    }
-    return e;
+    return g.d == D128 ? launch_attn_enrich_d<D128>(q, lse, dout, dtype, g, w, st)
+                       : launch_attn_enrich_d<D64>(q, lse, dout, dtype, g, w, st);
 }
 
 hipError_t launch_attn_dkdv(const void* q, const void* k, const void* v, const float* lse,
                             const void* dout, void* dk, void* dv, int dtype, const Geo& g,
                             const Ws& w, hipStream_t st)
 {
-    if (dtype == LLSA_BF16) {
-        long nblk = (long)g.G * g.n[1];
-        hipLaunchKernelGGL(dkdv_bf16, dim3((unsigned)nblk), dim3(64), 0, st,
-                           (const unsigned short*)q, (const unsigned short*)k,
-                           (const unsigned short*)v, lse, (const unsigned short*)dout,
-                           (unsigned short*)dk, (unsigned short*)dv, g, w);
-    } else {
-        long ntok = (long)g.G * g.N;  // one wave per key token
-        hipLaunchKernelGGL(dkdv_f32, dim3((unsigned)((ntok + 3) / 4)), dim3(256), 0, st,
-                           (const float*)q, (const float*)k, (const float*)v, lse,
-                           (const float*)dout, (float*)dk, (float*)dv, g, w);
-    }
-    return hipGetLastError();
+    return g.d == D128 ? launch_attn_dkdv_d<D128>(q, k, v, lse, dout, dk, dv, dtype, g, w, st)
+                       : launch_attn_dkdv_d<D64>(q, k, v, lse, dout, dk, dv, dtype, g, w, st);
 }
 
 }  // namespace llsa

@@ -36,43 +36,33 @@
 namespace llsa {
 namespace {
 
-// Staged 16-row tiles in LDS.  Rows read back transposed (ds_read_b64_tr_b16,
-// 4 rows x 32 B per 16 lanes) use a 160-byte stride; rows read as MFMA
-// operands (ds_read_b128, 8 rows x 16 B per 8 lanes) a 144-byte stride: both
-// spread their accesses over all 32 banks.
-constexpr int LDS_ROW = 80;   // transposed-read tiles
-constexpr int ROW_A = 72;     // operand-read tiles
-constexpr int TILE_ELEMS = BS * LDS_ROW;
+// Staged 16-row tiles in LDS (TileShape<D>): rows read back transposed
+// (ds_read_b64_tr_b16, 4 rows x 32 B per 16 lanes) use a stride of D + 16
+// elements, rows read as MFMA operands (ds_read_b128) D + 8; both spread their
+// accesses over all banks.
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const unsigned short* p)
 {
     return *(const bf16x8*)p;
 }
 
-// Registers of one prefetched pair of fine tiles: rows vr and vr+8 (columns
-// vc .. vc+7) of the key and value tiles a and b.  Every load instruction
-// covers 8 whole 128-byte rows, the fast gather pattern of the vector L1.
+// Registers of one prefetched pair of fine tiles: load u of a tile holds row
+// vr + RPI u (vr = lane / LPR), columns vc .. vc + 7 (vc = 8 (lane % LPR)) of
+// the key and value tiles a and b.  Every load instruction covers whole rows,
+// 1024 bytes, the fast gather pattern of the vector L1.
+template <int D>
 struct FinePair {
-    bf16x8 ka0, ka1, kb0, kb1;
-    bf16x8 va0, va1, vb0, vb1;
+    static constexpr int NI = TileShape<D>::NI;
+    bf16x8 ka[NI], kb[NI], va[NI], vb[NI];
 };
 
-template <int ROW>
-__device__ __forceinline__ void stage_rows(unsigned short* lds, bf16x8 r0, bf16x8 r1, int lane)
-{
-    const int vr = lane >> 3, vc = (lane & 7) * 8;
-    *(bf16x8*)(lds + vr * ROW + vc) = r0;
-    *(bf16x8*)(lds + (vr + 8) * ROW + vc) = r1;
-}
-
 // A operand of S^T = K Q^T from a staged key tile: row lane%16, channels
-// 8(lane/16) .. +7 and 32 + 8(lane/16) .. +7.
-__device__ __forceinline__ void key_operand(const unsigned short* lds, bf16x8& k0, bf16x8& k1,
-                                            int lane)
+// 32u + 8(lane/16) .. +7 for u < D/32.
+template <int D>
+__device__ __forceinline__ void key_operand(const unsigned short* lds,
+                                            bf16x8 (&k)[TileShape<D>::NI], int lane)
 {
-    const int gq = lane >> 4, nq = lane & 15;
-    k0 = *(const bf16x8*)(lds + nq * ROW_A + 8 * gq);
-    k1 = *(const bf16x8*)(lds + nq * ROW_A + 32 + 8 * gq);
+    operand_rows<D, TileShape<D>::ROW_A>(lds, k, lane);
 }
 
 // Softmax state.  The exponentials use a reference max m that is raised only
@@ -80,12 +70,13 @@ __device__ __forceinline__ void key_operand(const unsigned short* lds, bf16x8& k
 // the accumulators are rarely rescaled; the result is the same softmax.
 constexpr float TAU = 8.0f;
 
+template <int D>
 struct Online {
-    f32x4 acc[4];  // O^T tiles: lane holds O^T[16d + 4(lane/16) + r][query lane%16]
-    f32x4 den;     // softmax denominator of query lane%16 (all four equal): the
-                   // same MFMA as O^T with an all-ones value tile, so it sums
-                   // exactly the bf16 weights that multiply the values
-    float m;       // reference max (log2 units), equal in the 4 lanes of a query
+    f32x4 acc[D / 16];  // O^T tiles: lane holds O^T[16d + 4(lane/16) + r][query lane%16]
+    f32x4 den;          // softmax denominator of query lane%16 (all four equal): the
+                        // same MFMA as O^T with an all-ones value tile, so it sums
+                        // exactly the bf16 weights that multiply the values
+    float m;            // reference max (log2 units), equal in the 4 lanes of a query
 };
 
 // One step over two 16-entry tiles whose values are staged in LDS at la / lb.
@@ -93,18 +84,18 @@ struct Online {
 // MASK == true (the masked tail): entries of tile a at or past na (b: nb)
 // are masked, and ba / bb add a logit bias to rows 4(lane/16) + r (log2
 // units; pooled tokens under the size-weighted variant).
-template <bool MASK>
-__device__ __forceinline__ void attend_pair(Online& st, bf16x8 bq0, bf16x8 bq1, bf16x8 ka0,
-                                            bf16x8 ka1, bf16x8 kb0, bf16x8 kb1,
+template <bool MASK, int D>
+__device__ __forceinline__ void attend_pair(Online<D>& st, const bf16x8 (&bq)[TileShape<D>::NI],
+                                            const bf16x8 (&ka)[TileShape<D>::NI],
+                                            const bf16x8 (&kb)[TileShape<D>::NI],
                                             const unsigned short* la, const unsigned short* lb,
                                             int na, int nb, float c, int lane,
                                             const float* ba = nullptr, const float* bb = nullptr)
 {
     const int gq = lane >> 4;
     const int rr = (lane & 15) >> 2, xx = lane & 3;
-    const f32x4 zero = {};
-    const f32x4 sa = mfma32(ka1, bq1, mfma32(ka0, bq0, zero));
-    const f32x4 sb = mfma32(kb1, bq1, mfma32(kb0, bq0, zero));
+    const f32x4 sa = scores<D>(ka, bq);
+    const f32x4 sb = scores<D>(kb, bq);
     float ya[4], yb[4];  // logits in log2 units, masked entries at -inf
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -119,7 +110,7 @@ __device__ __forceinline__ void attend_pair(Online& st, bf16x8 bq0, bf16x8 bq1, 
         const float mnew = fmaxf(st.m, max_x4(lm));
         const float alpha = fast_exp2(st.m - mnew);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) st.acc[d] *= alpha;
+        for (int d = 0; d < D / 16; ++d) st.acc[d] *= alpha;
         st.den *= alpha;
         st.m = mnew;
     }
@@ -131,8 +122,8 @@ __device__ __forceinline__ void attend_pair(Online& st, bf16x8 bq0, bf16x8 bq1, 
     }
     lds_fence();
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const int off = (4 * gq + rr) * LDS_ROW + 16 * d + 4 * xx;
+    for (int d = 0; d < D / 16; ++d) {
+        const int off = (4 * gq + rr) * TileShape<D>::ROW_T + 16 * d + 4 * xx;
         bf16x4 va = lds_read_tr(la + off), vb = lds_read_tr(lb + off);
         bf16x8 av = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
         st.acc[d] = mfma32(av, pp, st.acc[d]);
@@ -147,21 +138,23 @@ constexpr int MAX_E = MAX_L * 64;  // pooled entries per query block (L * K)
 // Per-wave LDS: two value tiles (160-byte rows), two key tiles (144-byte
 // rows) and the table of pooled-entry rows (ECAP ints).  With ECAP = 64 a
 // workgroup of 4 waves needs under 40 KB, so 4 workgroups share a CU.
-template <int ECAP>
+template <int ECAP, int D>
 struct FwdLds {
-    static constexpr int V_TILE = BS * LDS_ROW;  // bf16 elements
-    static constexpr int K_TILE = BS * ROW_A;
+    static constexpr int V_TILE = BS * TileShape<D>::ROW_T;  // bf16 elements
+    static constexpr int K_TILE = BS * TileShape<D>::ROW_A;
     static constexpr int PER_WAVE = 2 * V_TILE + 2 * K_TILE + 2 * ECAP;  // in bf16 units
 };
 
-template <int ECAP>
+template <int ECAP, int D>
 __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __restrict__ q,
                                                      const unsigned short* __restrict__ k,
                                                      const unsigned short* __restrict__ v,
                                                      unsigned short* __restrict__ out,
                                                      float* __restrict__ lse, Geo g, Ws w)
 {
-    using Lay = FwdLds<ECAP>;
+    using Lay = FwdLds<ECAP, D>;
+    using TS = TileShape<D>;
+    constexpr int NI = TS::NI;
     __shared__ __attribute__((aligned(16))) unsigned short smem[4][Lay::PER_WAVE];
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, nq = lane & 15;
@@ -171,8 +164,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
     const float c = g.scale * LOG2E;  // logits in log2 units
     const long hbase = (long)gh * g.N * D;
     const long qbase = hbase + (long)i * BS * D;
-    const bf16x8 bq0 = ld_bf16x8(q + qbase + nq * D + 8 * gq);
-    const bf16x8 bq1 = ld_bf16x8(q + qbase + nq * D + 32 + 8 * gq);
+    bf16x8 bq[NI];  // B operand of S^T: query row lane%16, channels 32u + 8(lane/16) ..
+#pragma unroll
+    for (int u = 0; u < NI; ++u) bq[u] = ld_bf16x8(q + qbase + nq * D + 32 * u + 8 * gq);
     // the query block's K fine blocks, one per lane (K <= 64)
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
     const int myj = lane < g.K ? sel[lane] : 0;
@@ -190,9 +184,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
     }
     lds_fence();
 
-    Online st;
+    Online<D> st;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < D / 16; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.den = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m = -INFINITY;
     unsigned short* la = smem[wv];  // value tiles (transposed reads)
@@ -203,41 +197,43 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
     // Fine tiles first: K/2 full pairs in a loop whose body is one basic
     // block (prefetch of the next pair, then this pair), so the compiler
     // keeps every load a full step ahead of its use.  Buffer loads: lane
-    // offset of row vr (row vr + 8 is 1024 bytes on), tile offset j * 2048.
-    // Then the masked tail: a lone fine tile (K = 1) and the pooled tiles.
-    const int vr = lane >> 3, vc = (lane & 7) * 8;
+    // offset of row vr (row vr + RPI u is 1024 u bytes on), tile offset
+    // j * 32 D.  Then the masked tail: a lone fine tile (K odd) and the
+    // pooled tiles.
+    const int vr = lane / TS::LPR, vc = (lane % TS::LPR) * 8;
     const unsigned head_bytes = (unsigned)g.N * D * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + hbase, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + hbase, head_bytes);
     const int voff = (vr * D + vc) * 2;
     const int NF = g.K / 2;  // full fine pairs
-    auto load_fine = [&](FinePair& f, int p) {
+    auto load_fine = [&](FinePair<D>& f, int p) {
         const int sa = __builtin_amdgcn_readlane(myj, 2 * p) * (BS * D * 2);
         const int sb = __builtin_amdgcn_readlane(myj, 2 * p + 1) * (BS * D * 2);
-        f.ka0 = bload8(rk, voff, sa);
-        f.ka1 = bload8(rk, voff + 8 * D * 2, sa);
-        f.va0 = bload8(rv, voff, sa);
-        f.va1 = bload8(rv, voff + 8 * D * 2, sa);
-        f.kb0 = bload8(rk, voff, sb);
-        f.kb1 = bload8(rk, voff + 8 * D * 2, sb);
-        f.vb0 = bload8(rv, voff, sb);
-        f.vb1 = bload8(rv, voff + 8 * D * 2, sb);
+        // issue order: key rows, then value rows, of tile a, then of tile b
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.ka[u] = bload8(rk, voff + 1024 * u, sa);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.va[u] = bload8(rv, voff + 1024 * u, sa);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.kb[u] = bload8(rk, voff + 1024 * u, sb);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.vb[u] = bload8(rv, voff + 1024 * u, sb);
     };
-    auto stage = [&](const FinePair& f, bf16x8& ka0, bf16x8& ka1, bf16x8& kb0, bf16x8& kb1) {
-        stage_rows<ROW_A>(lka, f.ka0, f.ka1, lane);
-        stage_rows<ROW_A>(lkb, f.kb0, f.kb1, lane);
-        stage_rows<LDS_ROW>(la, f.va0, f.va1, lane);
-        stage_rows<LDS_ROW>(lb, f.vb0, f.vb1, lane);
+    auto stage = [&](const FinePair<D>& f, bf16x8 (&ka)[NI], bf16x8 (&kb)[NI]) {
+        stage_rows<D, TS::ROW_A>(lka, f.ka, lane);
+        stage_rows<D, TS::ROW_A>(lkb, f.kb, lane);
+        stage_rows<D, TS::ROW_T>(la, f.va, lane);
+        stage_rows<D, TS::ROW_T>(lb, f.vb, lane);
         lds_fence();
-        key_operand(lka, ka0, ka1, lane);
-        key_operand(lkb, kb0, kb1, lane);
+        key_operand<D>(lka, ka, lane);
+        key_operand<D>(lkb, kb, lane);
     };
-    auto step_fine = [&](const FinePair& f) {
-        bf16x8 ka0, ka1, kb0, kb1;
-        stage(f, ka0, ka1, kb0, kb1);
-        attend_pair<false>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, BS, BS, c, lane);
+    auto step_fine = [&](const FinePair<D>& f) {
+        bf16x8 ka[NI], kb[NI];
+        stage(f, ka, kb);
+        attend_pair<false, D>(st, bq, ka, kb, la, lb, BS, BS, c, lane);
     };
-    FinePair A, B;
+    FinePair<D> A, B;
     if (NF > 0) {
         load_fine(A, 0);
         int p = 0;
@@ -264,23 +260,27 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
     for (int t = 0; t < NT; t += 2) {
         const int tb = min(t + 1, NT - 1);
         const bool fa = t < NFT, fb = tb < NFT;
-        const long oa = tail_off(t, vr), oa8 = tail_off(t, vr + 8);
-        const long ob = tail_off(tb, vr), ob8 = tail_off(tb, vr + 8);
         const unsigned short* kpa = fa ? k : w.kb16;
         const unsigned short* vpa = fa ? v : w.vb16;
         const unsigned short* kpb = fb ? k : w.kb16;
         const unsigned short* vpb = fb ? v : w.vb16;
-        FinePair f;
-        f.ka0 = ld_bf16x8(kpa + oa + vc);
-        f.ka1 = ld_bf16x8(kpa + oa8 + vc);
-        f.va0 = ld_bf16x8(vpa + oa + vc);
-        f.va1 = ld_bf16x8(vpa + oa8 + vc);
-        f.kb0 = ld_bf16x8(kpb + ob + vc);
-        f.kb1 = ld_bf16x8(kpb + ob8 + vc);
-        f.vb0 = ld_bf16x8(vpb + ob + vc);
-        f.vb1 = ld_bf16x8(vpb + ob8 + vc);
-        bf16x8 ka0, ka1, kb0, kb1;
-        stage(f, ka0, ka1, kb0, kb1);
+        FinePair<D> f;
+        long oa[NI], ob[NI];
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+            oa[u] = tail_off(t, vr + TS::RPI * u);
+            ob[u] = tail_off(tb, vr + TS::RPI * u);
+        }
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.ka[u] = ld_bf16x8(kpa + oa[u] + vc);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.va[u] = ld_bf16x8(vpa + oa[u] + vc);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.kb[u] = ld_bf16x8(kpb + ob[u] + vc);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) f.vb[u] = ld_bf16x8(vpb + ob[u] + vc);
+        bf16x8 ka[NI], kb[NI];
+        stage(f, ka, kb);
         // valid entries of the two tiles, and each row's logit bias (that
         // of the level of pooled entry e)
         const int na = t < NFT ? BS : max(0, min(BS, E - BS * (t - NFT)));
@@ -292,14 +292,14 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
             ba[r] = t < NFT ? 0.f : g.lb2 * (float)g.entry_level(ea);
             bb[r] = t + 1 < NFT ? 0.f : g.lb2 * (float)g.entry_level(eb);
         }
-        attend_pair<true>(st, bq0, bq1, ka0, ka1, kb0, kb1, la, lb, na, nb, c, lane, ba, bb);
+        attend_pair<true, D>(st, bq, ka, kb, la, lb, na, nb, c, lane, ba, bb);
     }
 
     const float lsum = st.den[0];
     const float inv = 1.0f / lsum;
     const long obase = qbase + nq * D + 4 * gq;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < D / 16; ++d) {
         u16x4 o;
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[r] = f2bf(st.acc[d][r] * inv);
@@ -322,8 +322,11 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
 // Pooled tiles follow: one level-1 tile per block (its picks' pooled rows),
 // one tile per coarser level shared by all four (same ancestor).
 
+// (d = 64 only: the four blocks' state fills the register file)
+using TS64 = TileShape<D64>;
+
 struct Tile {
-    bf16x8 k0, k1, v0, v1;  // rows vr and vr+8, channels vc .. vc+7
+    bf16x8 k[2], v[2];  // rows vr and vr+8, channels vc .. vc+7
 };
 
 struct Q4 {
@@ -368,8 +371,8 @@ __device__ __forceinline__ void tile_step(Q4& st, bf16x8 bq0, bf16x8 bq1, bf16x8
 constexpr int U4_PT = 4 + MAX_L - 1;  // pooled tiles per wave (4 level-1 + one per coarser level)
 
 struct U4Lds {
-    unsigned short k[BS * ROW_A];
-    unsigned short v[BS * LDS_ROW];
+    unsigned short k[BS * TS64::ROW_A];
+    unsigned short v[BS * TS64::ROW_T];
     int arr[64];                  // the 4 x 16 picks (lane order), INT_MAX if unused
     int first[64];                // pick value if it is the first occurrence, else INT_MAX
     int tab[64];                  // union tile j
@@ -383,6 +386,7 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
                                                    unsigned short* __restrict__ out,
                                                    float* __restrict__ lse, Geo g, Ws w)
 {
+    constexpr int D = D64;
     __shared__ __attribute__((aligned(16))) U4Lds sm[4];
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, nq = lane & 15;
@@ -476,37 +480,37 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
     const int voff = (vr * D + vc) * 2;
     auto load_union = [&](Tile& T, int u) {
         const int so = __builtin_amdgcn_readlane(tj, u) * (BS * D * 2);
-        T.k0 = bload8(rk, voff, so);
-        T.k1 = bload8(rk, voff + 8 * D * 2, so);
-        T.v0 = bload8(rv, voff, so);
-        T.v1 = bload8(rv, voff + 8 * D * 2, so);
+        T.k[0] = bload8(rk, voff, so);
+        T.k[1] = bload8(rk, voff + 8 * D * 2, so);
+        T.v[0] = bload8(rv, voff, so);
+        T.v[1] = bload8(rv, voff + 8 * D * 2, so);
     };
     auto load_pooled = [&](Tile& T, int t) {
         const long ra = (long)L.pent[t * BS + vr] * D + vc;
         const long rb = (long)L.pent[t * BS + vr + 8] * D + vc;
-        T.k0 = ld_bf16x8(w.kb16 + ra);
-        T.k1 = ld_bf16x8(w.kb16 + rb);
-        T.v0 = ld_bf16x8(w.vb16 + ra);
-        T.v1 = ld_bf16x8(w.vb16 + rb);
+        T.k[0] = ld_bf16x8(w.kb16 + ra);
+        T.k[1] = ld_bf16x8(w.kb16 + rb);
+        T.v[0] = ld_bf16x8(w.vb16 + ra);
+        T.v[1] = ld_bf16x8(w.vb16 + rb);
     };
     // stage a tile, then run it for the blocks in `members`
     auto run = [&](const Tile& T, int members, int na, auto masked, float b2 = 0.f) {
-        stage_rows<ROW_A>(L.k, T.k0, T.k1, lane);
-        stage_rows<LDS_ROW>(L.v, T.v0, T.v1, lane);
+        stage_rows<D64, TS64::ROW_A>(L.k, T.k, lane);
+        stage_rows<D64, TS64::ROW_T>(L.v, T.v, lane);
         lds_fence();
-        bf16x8 ka0, ka1;
-        key_operand(L.k, ka0, ka1, lane);
+        bf16x8 ka[2];
+        key_operand<D64>(L.k, ka, lane);
         bf16x4 vt[4];
 #pragma unroll
         for (int d = 0; d < 4; ++d)
-            vt[d] = lds_read_tr(L.v + (4 * gq + rr) * LDS_ROW + 16 * d + 4 * xx);
+            vt[d] = lds_read_tr(L.v + (4 * gq + rr) * TS64::ROW_T + 16 * d + 4 * xx);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             if ((members >> b) & 1) {
                 if (masked)
-                    tile_step<true>(st[b], bq0[b], bq1[b], ka0, ka1, vt, na, c, lane, b2);
+                    tile_step<true>(st[b], bq0[b], bq1[b], ka[0], ka[1], vt, na, c, lane, b2);
                 else
-                    tile_step<false>(st[b], bq0[b], bq1[b], ka0, ka1, vt, BS, c, lane);
+                    tile_step<false>(st[b], bq0[b], bq1[b], ka[0], ka[1], vt, BS, c, lane);
             }
     };
     // union tiles, the next one in flight; the loop body has no conditional
@@ -560,30 +564,43 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
 
 // ------------------------------------------------------------ fp32 path
 
-// one wave per query token, lane = channel: every logit is a wave sum
+// one wave per query token, lane = channels lane + 64 c: every logit is a
+// wave sum
+template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
                                                     const float* __restrict__ k,
                                                     const float* __restrict__ v,
                                                     float* __restrict__ out,
                                                     float* __restrict__ lse, Geo g, Ws w)
 {
+    constexpr int NC = D / 64;
     const long tg = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (tg >= (long)g.G * g.N) return;
     const int lane = threadIdx.x & 63;
     const int gh = (int)(tg / g.N), t = (int)(tg % g.N);
-    const float qc = q[tg * D + lane];
-    float m = -INFINITY, l = 0.f, o = 0.f;
+    float qc[NC], o[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        qc[c] = q[tg * D + lane + 64 * c];
+        o[c] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
     auto visit = [&](const float* kr, const float* vr, float bias) {
-        const float z = wave_sum(qc * kr[lane]) * g.scale + bias;
+        float part = qc[0] * kr[lane];
+#pragma unroll
+        for (int c = 1; c < NC; ++c) part = fmaf(qc[c], kr[lane + 64 * c], part);
+        const float z = wave_sum(part) * g.scale + bias;
         if (z > m) {
             const float a = expf(m - z);
             l *= a;
-            o *= a;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) o[c] *= a;
             m = z;
         }
         const float p = expf(z - m);
         l += p;
-        o = fmaf(p, vr[lane], o);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) o[c] = fmaf(p, vr[lane + 64 * c], o[c]);
     };
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + t / BS) * g.K;
     for (int s = 0; s < g.K; ++s)
@@ -600,8 +617,38 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
             visit(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, bias);
         }
     }
-    out[tg * D + lane] = o / l;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) out[tg * D + lane + 64 * c] = o[c] / l;
     if (lane == 0) lse[tg] = m + logf(l);
+}
+
+template <int D>
+hipError_t launch_attn_fwd_d(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int dtype, const Geo& g, const Ws& w, hipStream_t st)
+{
+    if (dtype == LLSA_BF16) {
+        long nblk = (long)g.G * g.n[1];
+        // the four-block kernel (d = 64): every fine list and every pooled
+        // list fit one 16-entry tile
+        bool fits = D == D64 && g.K <= BS && g.n[1] % 4 == 0;
+        for (int l = g.l0; l <= g.L; ++l) fits = fits && g.Kl[l] <= BS;
+        if (fits) {
+            hipLaunchKernelGGL(attn_fwd_u4, dim3((unsigned)((nblk + 15) / 16)), dim3(256), 0, st,
+                               (const unsigned short*)q, (const unsigned short*)k,
+                               (const unsigned short*)v, (unsigned short*)out, lse, g, w);
+        } else {
+            auto kern = (g.n_pooled() <= 64) ? attn_fwd_bf16<64, D> : attn_fwd_bf16<MAX_E, D>;
+            hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
+                               (const unsigned short*)q, (const unsigned short*)k,
+                               (const unsigned short*)v, (unsigned short*)out, lse, g, w);
+        }
+    } else {
+        long ntok = (long)g.G * g.N;  // one wave each
+        hipLaunchKernelGGL(attn_fwd_f32<D>, dim3((unsigned)((ntok + 3) / 4)), dim3(256), 0, st,
+                           (const float*)q, (const float*)k, (const float*)v, (float*)out, lse,
+                           g, w);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -609,29 +656,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                            int dtype, const Geo& g, const Ws& w, hipStream_t st)
 {
-    if (dtype == LLSA_BF16) {
-        long nblk = (long)g.G * g.n[1];
-        // the four-block kernel: every fine list and every pooled list fit
-        // one 16-entry tile
-        bool fits = g.K <= BS && g.n[1] % 4 == 0;
-        for (int l = g.l0; l <= g.L; ++l) fits = fits && g.Kl[l] <= BS;
-        if (fits) {
-            hipLaunchKernelGGL(attn_fwd_u4, dim3((unsigned)((nblk + 15) / 16)), dim3(256), 0, st,
-                               (const unsigned short*)q, (const unsigned short*)k,
-                               (const unsigned short*)v, (unsigned short*)out, lse, g, w);
-        } else {
-            auto kern = (g.n_pooled() <= 64) ? attn_fwd_bf16<64> : attn_fwd_bf16<MAX_E>;
-            hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
-                               (const unsigned short*)q, (const unsigned short*)k,
-                               (const unsigned short*)v, (unsigned short*)out, lse, g, w);
-        }
-    } else {
-        long ntok = (long)g.G * g.N;  // one wave each
-        hipLaunchKernelGGL(attn_fwd_f32, dim3((unsigned)((ntok + 3) / 4)), dim3(256), 0, st,
-                           (const float*)q, (const float*)k, (const float*)v, (float*)out, lse,
-                           g, w);
-    }
-    return hipGetLastError();
+    return g.d == D128 ? launch_attn_fwd_d<D128>(q, k, v, out, lse, dtype, g, w, st)
+                       : launch_attn_fwd_d<D64>(q, k, v, out, lse, dtype, g, w, st);
 }
 
 }  // namespace llsa

@@ -7,8 +7,8 @@
 //
 // pool_l12: one workgroup per 256 consecutive tokens of one head and one
 // tensor.  Thread (blk, sub) sums the 16 tokens of level-1 block blk over the
-// channels 4*sub .. 4*sub+3, so each token row (128 B in bf16) is read whole
-// by 16 adjacent lanes.  Level 2 (one block per workgroup) is the mean of the
+// channels 4*sub .. 4*sub+3 (and 64 + 4*sub .. when d = 128), so each 64-channel
+// part of a token row is read whole by 16 adjacent lanes.  Level 2 (one block per workgroup) is the mean of the
 // 16 level-1 means, formed in LDS.  pool_up forms levels >= 3 from level l-1.
 // The pooled keys and values are also stored rounded to bf16 (the operands
 // the attention kernels feed to the MFMA).
@@ -39,10 +39,11 @@ __device__ __forceinline__ void put_bf16x4(unsigned short* dst, long off, float4
     *(u16x4*)(dst + off) = o;
 }
 
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T* __restrict__ k,
                                                 const T* __restrict__ v, Geo g, Ws w)
 {
+    constexpr int NC = D / 64;  // 4-channel groups per thread: channels 4 sub + 64 c
     __shared__ float m1[16][D];
     const int tensor = blockIdx.y;
     const T* x = tensor == 0 ? q : tensor == 1 ? k : v;
@@ -55,30 +56,43 @@ __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T
     const int b0 = (blockIdx.x % wg_per_head) * 16;  // first level-1 block
     const int blk = threadIdx.x >> 4, sub = threadIdx.x & 15;
     const bool live = b0 + blk < n1;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 s[NC];
+#pragma unroll
+    for (int cg = 0; cg < NC; ++cg) s[cg] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live) {
         const T* p = x + ((long)gh * g.N + (long)(b0 + blk) * BS) * D + 4 * sub;
-        float4 r[BS];
 #pragma unroll
-        for (int t = 0; t < BS; ++t) r[t] = Vec4<T>::load(p + (long)t * D);
+        for (int cg = 0; cg < NC; ++cg) {
+            float4 r[BS];
 #pragma unroll
-        for (int t = 0; t < BS; ++t) {
-            s.x += r[t].x;
-            s.y += r[t].y;
-            s.z += r[t].z;
-            s.w += r[t].w;
+            for (int t = 0; t < BS; ++t) r[t] = Vec4<T>::load(p + (long)t * D + 64 * cg);
+#pragma unroll
+            for (int t = 0; t < BS; ++t) {
+                s[cg].x += r[t].x;
+                s[cg].y += r[t].y;
+                s[cg].z += r[t].z;
+                s[cg].w += r[t].w;
+            }
         }
         const float inv = 1.0f / BS;
-        s = make_float4(s.x * inv, s.y * inv, s.z * inv, s.w * inv);
         const long row = (long)gh * n1 + b0 + blk;
-        *(float4*)(lv1 + row * D + 4 * sub) = s;
-        if (tensor) put_bf16x4(tensor == 1 ? w.kb16 : w.vb16, (w.prow[0] + row) * D + 4 * sub, s);
+#pragma unroll
+        for (int cg = 0; cg < NC; ++cg) {
+            s[cg] = make_float4(s[cg].x * inv, s[cg].y * inv, s[cg].z * inv, s[cg].w * inv);
+            *(float4*)(lv1 + row * D + 4 * sub + 64 * cg) = s[cg];
+            if (tensor)
+                put_bf16x4(tensor == 1 ? w.kb16 : w.vb16, (w.prow[0] + row) * D + 4 * sub + 64 * cg,
+                           s[cg]);
+        }
     }
     if (g.L >= 2) {  // b0 is a multiple of 16, so this workgroup is one level-2 block
-        m1[blk][4 * sub + 0] = s.x;
-        m1[blk][4 * sub + 1] = s.y;
-        m1[blk][4 * sub + 2] = s.z;
-        m1[blk][4 * sub + 3] = s.w;
+#pragma unroll
+        for (int cg = 0; cg < NC; ++cg) {
+            m1[blk][4 * sub + 64 * cg + 0] = s[cg].x;
+            m1[blk][4 * sub + 64 * cg + 1] = s[cg].y;
+            m1[blk][4 * sub + 64 * cg + 2] = s[cg].z;
+            m1[blk][4 * sub + 64 * cg + 3] = s[cg].w;
+        }
         __syncthreads();
         if (threadIdx.x < D) {
             float a = 0.f;
@@ -93,6 +107,7 @@ __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T
     }
 }
 
+template <int D>
 __global__ __launch_bounds__(256) void pool_up(Geo g, Ws w, int l)
 {
     const int tensor = blockIdx.y;
@@ -110,27 +125,35 @@ __global__ __launch_bounds__(256) void pool_up(Geo g, Ws w, int l)
         (tensor == 1 ? w.kb16 : w.vb16)[(w.prow[l - 1] + row) * D + c] = f2bf(a * (1.0f / BS));
 }
 
+template <int D>
+hipError_t launch_pool_d(const void* q, const void* k, const void* v, int dtype, const Geo& g,
+                         const Ws& w, hipStream_t st)
+{
+    dim3 grid(g.G * ((g.n[1] + 15) / 16), 3);
+    if (dtype == LLSA_BF16)
+        hipLaunchKernelGGL((pool_l12<unsigned short, D>), grid, dim3(256), 0, st,
+                           (const unsigned short*)q, (const unsigned short*)k,
+                           (const unsigned short*)v, g, w);
+    else
+        hipLaunchKernelGGL((pool_l12<float, D>), grid, dim3(256), 0, st, (const float*)q,
+                           (const float*)k, (const float*)v, g, w);
+    hipError_t e = hipGetLastError();
+    for (int l = 3; l <= g.L && e == hipSuccess; ++l) {
+        long total = (long)g.G * g.n[l] * D;
+        hipLaunchKernelGGL(pool_up<D>, dim3((unsigned)((total + 255) / 256), 3), dim3(256), 0, st,
+                           g, w, l);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
 }  // namespace
 
 hipError_t launch_pool(const void* q, const void* k, const void* v, int dtype, const Geo& g,
                        const Ws& w, hipStream_t st)
 {
-    dim3 grid(g.G * ((g.n[1] + 15) / 16), 3);
-    if (dtype == LLSA_BF16)
-        hipLaunchKernelGGL(pool_l12<unsigned short>, grid, dim3(256), 0, st,
-                           (const unsigned short*)q, (const unsigned short*)k,
-                           (const unsigned short*)v, g, w);
-    else
-        hipLaunchKernelGGL(pool_l12<float>, grid, dim3(256), 0, st, (const float*)q,
-                           (const float*)k, (const float*)v, g, w);
-    hipError_t e = hipGetLastError();
-    for (int l = 3; l <= g.L && e == hipSuccess; ++l) {
-        long total = (long)g.G * g.n[l] * D;
-        hipLaunchKernelGGL(pool_up, dim3((unsigned)((total + 255) / 256), 3), dim3(256), 0, st,
-                           g, w, l);
-        e = hipGetLastError();
-    }
-    return e;
+    return g.d == D128 ? launch_pool_d<D128>(q, k, v, dtype, g, w, st)
+                       : launch_pool_d<D64>(q, k, v, dtype, g, w, st);
 }
 
 }  // namespace llsa

@@ -118,7 +118,7 @@ __device__ __forceinline__ void select_rows(const float* sc, const int* cand, in
     }
 }
 
-template <int KPL>
+template <int KPL, int D>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ qbar,
                                                      const float* __restrict__ kbar,
                                                      const int* __restrict__ parent,
@@ -151,27 +151,28 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
         qs[e] = qbar[((long)gh * n_l + row0) * D + e];
     __syncthreads();
 
-    // score tile: four adjacent threads per candidate, 16 channels each, so a
-    // wave reads 16 whole 256-byte candidate rows per load; the four partial
-    // dot products are summed within the quad (DPP), identically in all four.
+    // score tile: four adjacent threads per candidate, D/4 channels each, so a
+    // wave reads 16 whole candidate rows per load; the four partial dot
+    // products are summed within the quad (DPP), identically in all four.
+    constexpr int NV = D / 16;  // float4 per thread and row
     const int sub = threadIdx.x & 3;
     for (int c0 = 0; c0 < M; c0 += 64) {
         const int c = c0 + (threadIdx.x >> 2);
         const bool ok = c < M;
-        float4 kv[4];
+        float4 kv[NV];
         if (ok) {
-            const float4* kr = (const float4*)(kbar + ((long)gh * n_l + cand[c]) * D + 16 * sub);
+            const float4* kr = (const float4*)(kbar + ((long)gh * n_l + cand[c]) * D + (D / 4) * sub);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) kv[t] = kr[t];
+            for (int t = 0; t < NV; ++t) kv[t] = kr[t];
         } else {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) kv[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int t = 0; t < NV; ++t) kv[t] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
         for (int r = 0; r < rows; ++r) {
-            const float4* qr = (const float4*)(qs + r * D + 16 * sub);
+            const float4* qr = (const float4*)(qs + r * D + (D / 4) * sub);
             float a = 0.f;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < NV; ++t) {
                 const float4 qv = qr[t];
                 a = fmaf(qv.x, kv[t].x, a);
                 a = fmaf(qv.y, kv[t].y, a);
@@ -263,10 +264,10 @@ __device__ __forceinline__ void select_rows16(const float* sc, const int* cand, 
 
 // Scores on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): 16 query rows x
 // 16 candidates per tile; lane (g = lane/16, n = lane%16) feeds row n and
-// candidate n over channels 16g .. 16g+15, one channel per MFMA k-slot, so
-// every lane reads whole 64-byte pieces of the rows.  The channel sum order is
+// candidate n over channels (d/4)g .. (d/4)(g+1) - 1, one channel per MFMA
+// k-slot, so every lane reads whole 64-byte pieces of the rows.  The channel sum order is
 // fixed by the instruction sequence.  Used for candidate lists of up to 1024.
-template <int KPG>
+template <int KPG, int D>
 __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qbar,
                                                    const float* __restrict__ kbar,
                                                    const int* __restrict__ parent,
@@ -296,41 +297,42 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
     }
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
-    float qa[16];
+    constexpr int CG = D / 4;  // channels of lane group g: CG g .. CG g + CG - 1
+    float qa[CG];
     {
-        const float4* qr = (const float4*)(qbar + ((long)gh * n_l + row0 + min(n, rows - 1)) * D + 16 * g);
+        const float4* qr = (const float4*)(qbar + ((long)gh * n_l + row0 + min(n, rows - 1)) * D + CG * g);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < CG / 4; ++t) {
             const float4 v = qr[t];
             qa[4 * t] = v.x; qa[4 * t + 1] = v.y; qa[4 * t + 2] = v.z; qa[4 * t + 3] = v.w;
         }
     }
     __syncthreads();
     const int tiles = (M + BS - 1) / BS;
-    const float* kh = kbar + (long)gh * n_l * D + 16 * g;
-    auto load_tile = [&](float (&kb)[16], int tile) {
+    const float* kh = kbar + (long)gh * n_l * D + CG * g;
+    auto load_tile = [&](float (&kb)[CG], int tile) {
         const int c = cand[min(tile * BS + n, M - 1)];
         const float4* kr = (const float4*)(kh + (long)c * D);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < CG / 4; ++t) {
             const float4 v = kr[t];
             kb[4 * t] = v.x; kb[4 * t + 1] = v.y; kb[4 * t + 2] = v.z; kb[4 * t + 3] = v.w;
         }
     };
-    float kb[16], kn[16];
+    float kb[CG], kn[CG];
     load_tile(kb, min(wv, tiles - 1));
     for (int tile = wv; tile < tiles; tile += 4) {
         load_tile(kn, min(tile + 4, tiles - 1));
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
+        for (int k = 0; k < CG; ++k)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[k], kb[k], acc, 0, 0, 0);
         const int col = tile * BS + n;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (4 * g + r < rows && col < M) sc[(4 * g + r) * M + col] = acc[r] * scale + 0.0f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) kb[k] = kn[k];
+        for (int k = 0; k < CG; ++k) kb[k] = kn[k];
     }
     __syncthreads();
     select_rows16<KPG>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K, pc);
@@ -338,25 +340,25 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
     flush_counts(pc, cand, M, {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)});
 }
 
-template <int KPG>
+template <int KPG, int D>
 hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, int* idx,
                        Counts cnt, int G, int n_l, int K, int M, float scale, hipStream_t st)
 {
     const int groups = (n_l + (parent ? BS : 4) - 1) / (parent ? BS : 4);
     const size_t lds = (size_t)BS * M * sizeof(float) + 2 * (size_t)M * sizeof(int);
     if (lds > 65536) {  // 16 rows x 1024 candidates
-        hipError_t e = hipFuncSetAttribute((const void*)select_mfma<KPG>,
+        hipError_t e = hipFuncSetAttribute((const void*)select_mfma<KPG, D>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(select_mfma<KPG>, dim3(G * groups), dim3(256), lds, st, qbar, kbar, parent,
+    hipLaunchKernelGGL((select_mfma<KPG, D>), dim3(G * groups), dim3(256), lds, st, qbar, kbar, parent,
                        idx, cnt, n_l, K, M, scale);
     return hipGetLastError();
 }
 
 // Coarsest level with more than 1024 blocks: few rows per workgroup, so that
 // the dense n_L x n_L scoring spreads over many CUs.
-template <int KPL>
+template <int KPL, int D>
 hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, Counts cnt, int G, int n_l,
                        int K, float scale, hipStream_t st)
 {
@@ -365,18 +367,17 @@ hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, Counts cn
     int groups = (n_l + R - 1) / R;
     size_t lds = (size_t)(R * D + R * M) * sizeof(float) + 2 * (size_t)M * sizeof(int);
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)select_kernel<KPL>,
+        hipError_t e = hipFuncSetAttribute((const void*)select_kernel<KPL, D>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(select_kernel<KPL>, dim3(G * groups), dim3(256), lds, st, qbar, kbar,
+    hipLaunchKernelGGL((select_kernel<KPL, D>), dim3(G * groups), dim3(256), lds, st, qbar, kbar,
                        nullptr, idx, cnt, n_l, K, R, M, scale);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
+template <int D>
+hipError_t launch_select_d(const Geo& g, const Ws& w, hipStream_t st)
 {
     const unsigned cgrid = (unsigned)min((w.cnt_len + 255) / 256, 1024L);
     hipLaunchKernelGGL(clear_counts, dim3(cgrid), dim3(256), 0, st, w.cnt_all, w.cnt_len);
@@ -390,17 +391,25 @@ hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
         const Counts cnt = {w.cnt[l - 1], w.c16[l - 1]};
         hipError_t e;
         if (M <= 1024) {
-            auto f = M <= 16 ? launch_mfma<1> : M <= 32 ? launch_mfma<2> : M <= 64 ? launch_mfma<4>
-                   : M <= 128 ? launch_mfma<8> : M <= 256 ? launch_mfma<16>
-                   : M <= 512 ? launch_mfma<32> : launch_mfma<64>;
+            auto f = M <= 16 ? launch_mfma<1, D> : M <= 32 ? launch_mfma<2, D>
+                   : M <= 64 ? launch_mfma<4, D> : M <= 128 ? launch_mfma<8, D>
+                   : M <= 256 ? launch_mfma<16, D> : M <= 512 ? launch_mfma<32, D>
+                   : launch_mfma<64, D>;
             e = f(qb, kb, parent, out, cnt, g.G, g.n[l], K, M, g.scale, st);
         } else {
-            auto f = M <= 2048 ? launch_wide<32> : launch_wide<64>;
+            auto f = M <= 2048 ? launch_wide<32, D> : launch_wide<64, D>;
             e = f(qb, kb, out, cnt, g.G, g.n[l], K, g.scale, st);
         }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
+{
+    return g.d == D128 ? launch_select_d<D128>(g, w, st) : launch_select_d<D64>(g, w, st);
 }
 
 }  // namespace llsa

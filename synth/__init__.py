@@ -60,8 +60,8 @@ class Workload:
 
 
 # The workloads of the LLSA hot path: a small fp32 correctness case, bf16 pixel
-# grids of 64^2, 128^2, 256^2 (headline) and 512^2 tokens, and two grids the
-# README's power-of-two limits exclude (video, a rectangle).
+# grids of 64^2, 128^2, 256^2 (headline) and 512^2 tokens, two grids the
+# README's power-of-two limits exclude (video, a rectangle), and d = 128.
 WORKLOADS = {
     w.name: w for w in [
         Workload("grid32_f32_l1_k8", 1, 1, 32, 64, "f32", 1, 8, 2.0),
@@ -73,6 +73,8 @@ WORKLOADS = {
         # and a 192 x 320 image (N = 61440, not a power of two)
         Workload("video16x64x64_bf16_l2_k16", 1, 6, 64, 64, "bf16", 2, 16, 2.0, frames=16),
         Workload("rect192x320_bf16_l2_k16", 1, 6, 320, 64, "bf16", 2, 16, 4.0, height=192),
+        # head dimension 128 at the headline grid
+        Workload("grid256_d128_bf16_l2_k16", 1, 6, 256, 128, "bf16", 2, 16, 4.0),
     ]
 }
 

@@ -61,7 +61,7 @@ def bwd(**kw):
     (dict(N=48 * 80, levels=2, topk=16), -2),
     (dict(levels=0), -2), (dict(levels=4), -2), (dict(N=4096, levels=2, topk=32), -2),
     (dict(B=0), -2), (dict(H=-1), -2),
-    (dict(d=128), -3), (dict(block_size=32), -3), (dict(dtype=7), -3), (dict(flags=8), -3),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(block_size=32), -3), (dict(dtype=7), -3), (dict(flags=8), -3),
     (dict(levels=7, N=1 << 30), -3), (dict(N=131072, topk=16), -3), (dict(topk=128, N=65536, levels=2), -3),
     (dict(B=1 << 16, H=1 << 4, N=4096), -3), (dict(N=1 << 24, levels=3, topk=16), -3),
     (dict(workspace=None), -4), (dict(ws_bytes=100), -4),
@@ -101,6 +101,11 @@ def test_grid_order_validation():
                                     (4 * 32 * 32, 12, 2), (3 * 4096, 3, 3)])
 def test_shapes_beyond_powers_of_two_are_accepted(N, K, Lv):
     assert L.llsa_workspace_bytes(1, 2, N, 64, 16, K, Lv, L.BF16) > 0
+
+
+def test_head_dimension_128_is_accepted():
+    assert L.llsa_workspace_bytes(1, 2, 4096, 128, 16, 16, 2, L.BF16) > \
+        L.llsa_workspace_bytes(1, 2, 4096, 64, 16, 16, 2, L.BF16) > 0
 
 
 def test_per_level_top_k_validation():

@@ -144,8 +144,8 @@ def test_grid_order_bit_exact(T, Hh, Ww, dtype, width):
                            x.view(torch.int16) if dt == torch.bfloat16 else x)
 
 
-def _grid(name, dtype, L, K, side, height=0, frames=1, B=1, H=2, sigma=2.0):
-    return W(name, B, H, side, 64, dtype, L, K, sigma, 0, 16, frames, height)
+def _grid(name, dtype, L, K, side, height=0, frames=1, B=1, H=2, sigma=2.0, d=64):
+    return W(name, B, H, side, d, dtype, L, K, sigma, 0, 16, frames, height)
 
 
 # shapes the README's power-of-two limits exclude: rectangles, odd top-k,
@@ -185,6 +185,25 @@ _PER_LEVEL = [
 @pytest.mark.parametrize("w,flags", _PER_LEVEL,
                          ids=["%s_f%d" % (w.name, f) for w, f in _PER_LEVEL])
 def test_top_k_per_level(w, flags):
+    _full_check(w, flags=flags)
+
+
+# head dimension 128 (the one-block bf16 kernels and the fp32 kernels)
+_D128 = [
+    (_grid("grid32_f32_l1_k8_d128", "f32", 1, 8, 32, H=1, d=128), 0),
+    (_grid("grid32_f32_l2_k2_d128", "f32", 2, 2, 32, d=128), oracle.SIZE_BIAS),
+    (_grid("grid64_bf16_l1_k16_d128", "bf16", 1, 16, 64, d=128), 0),
+    (_grid("grid64_bf16_l2_k4_d128", "bf16", 2, 4, 64, d=128), 0),
+    (_grid("grid64_bf16_l2_k4_d128", "bf16", 2, 4, 64, d=128),
+     oracle.ENRICH_COARSE | oracle.SIZE_BIAS),
+    (_grid("grid64_bf16_l3_k1_d128", "bf16", 3, 1, 64, d=128), 0),
+    (_grid("grid64_bf16_l2_k8x4_d128", "bf16", 2, (8, 4), 64, d=128), 0),
+    (_grid("rect48x80_bf16_l2_k8_d128", "bf16", 2, 8, 80, height=48, d=128), oracle.NO_ENRICH),
+]
+
+
+@pytest.mark.parametrize("w,flags", _D128, ids=["%s_f%d" % (w.name, f) for w, f in _D128])
+def test_head_dim_128(w, flags):
     _full_check(w, flags=flags)
 
 
@@ -284,7 +303,8 @@ def _needed_qblocks(w, idx, kblocks):
 
 _SAMPLED = [synth.WORKLOADS[n] for n in (
     "grid128_bf16_l2_k16", "grid256_bf16_l2_k16", "grid512_bf16_l3_k16",
-    "video16x64x64_bf16_l2_k16", "rect192x320_bf16_l2_k16")] + [
+    "video16x64x64_bf16_l2_k16", "rect192x320_bf16_l2_k16",
+    "grid256_d128_bf16_l2_k16")] + [
     # the deepest pyramids N <= 2^23 allows: 4 and 5 levels down to one block
     _grid("grid256_bf16_l4_k1", "bf16", 4, 1, 256, H=1),
     _grid("grid1024_bf16_l5_k1", "bf16", 5, 1, 1024, H=1),
