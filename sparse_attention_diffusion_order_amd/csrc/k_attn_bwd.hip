@@ -141,8 +141,9 @@ struct DqLds {
     static constexpr int PER_WAVE = 2 * K_TILE + 2 * V_TILE + 2 * ECAP;
 };
 
+// at least two waves per SIMD at d = 128 (d = 64 has three without a bound)
 template <int ECAP, int D>
-__global__ __launch_bounds__(256) void dq_bf16(const unsigned short* __restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ? 2 : 1))) void dq_bf16(const unsigned short* __restrict__ q,
                                                const unsigned short* __restrict__ k,
                                                const unsigned short* __restrict__ v,
                                                const unsigned short* __restrict__ o,
