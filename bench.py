@@ -191,6 +191,31 @@ def summarize_pmc(fetch_db, write_db, out, cmd, workload):
 
 
 CALIB_COPY_MIB = 256
+N_CU = 256
+
+
+def summarize_counters(db, out, cmd, workload):
+    """Per-kernel averages of the counters of one rocprofv3 --pmc pass; with
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE also the MFMA-busy fraction
+    busy / (active cycles x 256 CUs)."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    acc = {}
+    for name, ctr, val in c.execute("select kernel_name, counter_name, value "
+                                    "from counters_collection"):
+        acc.setdefault(_short_kernel(name), {}).setdefault(ctr, []).append(val)
+    kernels = {}
+    for k, ctrs in sorted(acc.items()):
+        row = {ctr: round(sum(v) / len(v), 1) for ctr, v in sorted(ctrs.items())}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in row and row.get("GRBM_GUI_ACTIVE"):
+            row["mfma_busy_frac"] = round(row["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                          (row["GRBM_GUI_ACTIVE"] * N_CU), 4)
+        kernels[k] = row
+    rec = {"workload": workload, "sources_sha": sha_of_sources(), "commands": cmd,
+           "kernels": kernels}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
 
 
 def cpu_baseline(w, inp, min_s=10.0):
@@ -269,6 +294,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-dist", action="store_true",
+                    help="skip the per-rep warm/cold distributions (for profiled runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for PMC scaling)")
     ap.add_argument("--summarize-trace", metavar="DB",
@@ -277,12 +304,17 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write the JSON summary of rocprofv3 --pmc FETCH_SIZE and "
                          "WRITE_SIZE databases to --out and exit (no GPU)")
+    ap.add_argument("--summarize-counters", metavar="DB",
+                    help="per-kernel averages of one rocprofv3 --pmc pass")
     ap.add_argument("--out")
     ap.add_argument("--cmd", default="", help="the profiling command, recorded in the summary")
     ap.add_argument("--bench-json", help="bench output of the profiled run (trace summary)")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.cmd, args.bench_json)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.out, args.cmd, args.workload)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.out, args.cmd,
@@ -402,7 +434,7 @@ def main():
 
     nrep = max(args.steps, 20)
     timing = {"reps": nrep}
-    for cold in (False, True):
+    for cold in (() if args.no_dist else (False, True)):
         tag = "cold" if cold else "warm"
         timing["fwd_ms_" + tag] = reps(lambda: run_list(["pool", "select", "attn_fwd"]), cold, nrep)
         timing["fwdbwd_ms_" + tag] = reps(lambda: run_list(stages[1:]), cold, nrep)
