@@ -5,12 +5,16 @@ One step = the whole hot path over one batch of seeded synthetic input already
 resident in HBM: grid-order gather of Q, K, V (raster -> quadtree order), the
 forward (pool pyramid, hierarchical Top-K, sparse attention with enrichment)
 and the backward (index transpose, dQ, pooled-token gradients, dK/dV), all
-through the C ABI of libllsa.so on one stream.  Prints ONE JSON line.
+through the C ABI of libllsa.so: llsa_grid_order, llsa_forward and
+llsa_backward on the caller's stream (the backward runs the index transpose on
+a stream of its own beside dQ and joins it before the pooled-token
+gradients).  Prints ONE JSON line.
 
-The headline times K whole steps between two HIP events on the library's
-stream.  A second pass of K steps records an event after every stage for the
-per-stage times; the roofline object is computed from it for the stage kernel
-that takes the longest.  Then per-rep distributions (median, p10, p90) of the
+The headline times K whole steps between two HIP events on the caller's
+stream.  A second pass of K steps runs the same work stage by stage
+(llsa_forward_part / llsa_backward_part, one stream) and records an event
+after every stage for the per-stage times; the roofline object is computed
+from it for the stage kernel that takes the longest.  Then per-rep distributions (median, p10, p90) of the
 forward, forward+backward and grid-order gather: warm, and cold with a
 512 MiB write before each rep so that nothing stays in the 256 MB MALL.
 """
@@ -367,11 +371,24 @@ def main():
                     "enrich": lib.PART_ENRICH, "dkdv": lib.PART_DKDV}[name]
             lib.llsa_backward_part(part, q, k, v, out, lse, do, dq, dk, dv, *shape)
 
-    def step(evs=None):
+    def fwd():
+        lib.llsa_forward(q, k, v, out, lse, *shape)
+
+    def fwdbwd():
+        lib.llsa_forward(q, k, v, out, lse, *shape)
+        lib.llsa_backward(q, k, v, out, lse, do, dq, dk, dv, *shape)
+
+    def step():
+        """one pass of the whole path through the public entry points (the
+        backward runs its sparse transpose beside the dq pass)"""
+        run_stage("zorder")
+        fwdbwd()
+
+    def step_parts(evs):
+        """the same work stage by stage, one stream, an event after each"""
         for si, name in enumerate(stages):
             run_stage(name)
-            if evs is not None:
-                evs[si + 1].record(stream)
+            evs[si + 1].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -389,15 +406,11 @@ def main():
         torch.cuda.synchronize()
         return t_start.elapsed_time(t_end) / args.steps
 
-    def run_list(names):
-        for name in names:
-            run_stage(name)
-
     # headline: K whole steps
     ms_per_step = timed(step)
-    # the forward (llsa_forward's parts) and forward + backward, same protocol
-    fwd_ms = timed(lambda: run_list(["pool", "select", "attn_fwd"]))
-    fwdbwd_ms = timed(lambda: run_list(stages[1:]))
+    # the forward (llsa_forward) and forward + backward, same protocol
+    fwd_ms = timed(fwd)
+    fwdbwd_ms = timed(fwdbwd)
 
     # breakdown: K more steps with an event after every stage (each record
     # adds a few microseconds between stages, so these are not summed into
@@ -407,7 +420,7 @@ def main():
     torch.cuda.synchronize()
     for s in range(args.steps):
         all_evs[s][0].record(stream)
-        step(all_evs[s])
+        step_parts(all_evs[s])
     torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in all_evs]))
                 for i, name in enumerate(stages)}
@@ -436,8 +449,8 @@ def main():
     timing = {"reps": nrep}
     for cold in (() if args.no_dist else (False, True)):
         tag = "cold" if cold else "warm"
-        timing["fwd_ms_" + tag] = reps(lambda: run_list(["pool", "select", "attn_fwd"]), cold, nrep)
-        timing["fwdbwd_ms_" + tag] = reps(lambda: run_list(stages[1:]), cold, nrep)
+        timing["fwd_ms_" + tag] = reps(fwd, cold, nrep)
+        timing["fwdbwd_ms_" + tag] = reps(fwdbwd, cold, nrep)
         timing["grid_order_ms_" + tag] = reps(lambda: run_stage("zorder"), cold, nrep)
     del flush
 

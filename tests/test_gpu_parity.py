@@ -287,6 +287,54 @@ def test_repeated_parts_keep_the_transpose_exact():
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
 
 
+def test_backward_transpose_beside_dq_matches_stage_order():
+    """llsa_backward runs the index transpose on a stream of its own while dq
+    runs on the caller's, and joins it before the pooled-token gradients.  On a
+    caller stream other than the default one, two back-to-back forward +
+    backward calls with different inputs and workspaces (no host sync between
+    them) give, bit for bit, the gradients and key->query lists of the
+    one-stream stage-by-stage sequence."""
+    import torch
+    import sparse_attention_diffusion_order_amd as lib
+    ws_ = [small("side%d" % s_, 1, 3, 128, "bf16", 2, 8, seed=s_) for s_ in (1, 2)]
+    dev = []
+    for w in ws_:
+        inp = synth.make_inputs(w)
+        q, k, v = (to_device(inp[n_], "bf16").reshape(w.B, w.H, w.N, w.d) for n_ in "qkv")
+        do = to_device(inp["do"], "bf16").reshape(w.B, w.H, w.N, w.d)
+        dev.append((w, q, k, v, do))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = []
+    with torch.cuda.stream(side):
+        for w, q, k, v, do in dev:
+            out, lse, ws = lib.forward(q, k, v, w.topk, w.levels)
+            got.append((out, lse, ws) + lib.backward(q, k, v, out, lse, do, w.topk, w.levels, ws))
+    side.synchronize()
+    for (w, q, k, v, do), (out, lse, ws, dq, dk, dv) in zip(dev, got):
+        args = (w.B, w.H, w.N, w.d, BS, w.topk, w.levels, lib.BF16, 0)
+        ws2 = torch.empty_like(ws)
+        out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+        dq2, dk2, dv2 = (torch.empty_like(q) for _ in range(3))
+        for part in (lib.PART_POOL, lib.PART_SELECT, lib.PART_ATTN):
+            lib.llsa_forward_part(part, q, k, v, out2, lse2, *args, ws2, ws2.numel())
+        for part in (lib.PART_TRANSPOSE, lib.PART_DQ, lib.PART_ENRICH, lib.PART_DKDV):
+            lib.llsa_backward_part(part, q, k, v, out2, lse2, do, dq2, dk2, dv2, *args, ws2,
+                                   ws2.numel())
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+        for a_, b_ in ((dq, dq2), (dk, dk2), (dv, dv2)):
+            assert torch.equal(a_.view(torch.int16), b_.view(torch.int16))
+        lay = lib.llsa_workspace_layout_lk(w.B, w.H, w.N, w.d, BS, [w.topk] * w.levels,
+                                           w.levels, lib.BF16)
+        G = w.B * w.H
+        for l in range(w.levels):
+            n = w.N // BS ** (l + 1)
+            for off, cnt in ((lay["rowptr"][l], G * (n + 1)), (lay["col"][l], G * n * w.topk)):
+                np.testing.assert_array_equal(ws_array(ws, off, cnt, np.int32),
+                                              ws_array(ws2, off, cnt, np.int32))
+
+
 # ------------------------------------------------------- full-size workloads
 
 def _needed_qblocks(w, idx, kblocks):
