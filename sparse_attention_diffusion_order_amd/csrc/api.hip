@@ -185,8 +185,8 @@ int run_forward_part(int part, const void* q, const void* k, const void* v, void
                      float* lse, int dtype, const Prep& p)
 {
     switch (part) {
-    case LLSA_PART_POOL: return hip_rc(launch_pool(q, k, v, dtype, p.geo, p.ws, p.st));
-    case LLSA_PART_SELECT: return hip_rc(launch_select(p.geo, p.ws, p.st));
+    case LLSA_PART_POOL: return hip_rc(launch_pool(q, k, v, dtype, p.geo, p.ws, false, p.st));
+    case LLSA_PART_SELECT: return hip_rc(launch_select(p.geo, p.ws, true, p.st));
     case LLSA_PART_ATTN:
         return hip_rc(launch_attn_fwd(q, k, v, out, lse, dtype, p.geo, p.ws, p.st));
     default: return LLSA_ERR_UNSUPPORTED;
@@ -346,11 +346,13 @@ int llsa_forward_lk(const void* q, const void* k, const void* v, void* out, floa
     int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
                      stream, &p);
     if (rc) return rc;
-    for (int part : {LLSA_PART_POOL, LLSA_PART_SELECT, LLSA_PART_ATTN}) {
-        rc = run_forward_part(part, q, k, v, out, lse, dtype, p);
-        if (rc) return rc;
-    }
-    return LLSA_OK;
+    // pool zeroes the pick counters the selection adds to (one launch fewer
+    // than the selection part on its own, which zeroes them itself)
+    rc = hip_rc(launch_pool(q, k, v, dtype, p.geo, p.ws, true, p.st));
+    if (rc) return rc;
+    rc = hip_rc(launch_select(p.geo, p.ws, false, p.st));
+    if (rc) return rc;
+    return run_forward_part(LLSA_PART_ATTN, q, k, v, out, lse, dtype, p);
 }
 
 int llsa_forward(const void* q, const void* k, const void* v, void* out, float* lse, int B,

@@ -271,9 +271,11 @@ hipError_t launch_grid_order(const void* src, void* dst, long long outer, int fr
                              int width, int inner_bytes, int inverse, hipStream_t st);
 hipError_t launch_zorder(const void* src, void* dst, long long outer, int side, int inner_bytes,
                          int inverse, hipStream_t st);
+// zero_counts: pool zeroes the selection's pick counters (llsa_forward);
+// select zeroes them itself (the selection part on its own)
 hipError_t launch_pool(const void* q, const void* k, const void* v, int dtype, const Geo& g,
-                       const Ws& w, hipStream_t st);
-hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st);
+                       const Ws& w, bool zero_counts, hipStream_t st);
+hipError_t launch_select(const Geo& g, const Ws& w, bool zero_counts, hipStream_t st);
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                            int dtype, const Geo& g, const Ws& w, hipStream_t st);
 hipError_t launch_transpose(const Geo& g, const Ws& w, hipStream_t st);

@@ -11,7 +11,9 @@
 // part of a token row is read whole by 16 adjacent lanes.  Level 2 (one block per workgroup) is the mean of the
 // 16 level-1 means, formed in LDS.  pool_up forms levels >= 3 from level l-1.
 // The pooled keys and values are also stored rounded to bf16 (the operands
-// the attention kernels feed to the MFMA).
+// the attention kernels feed to the MFMA).  pool_l12 also zeroes the
+// selection's pick counters when given them (llsa_forward), which saves the
+// selection pass a launch.
 #include "common.h"
 
 namespace llsa {
@@ -45,6 +47,14 @@ __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T
 {
     constexpr int NC = D / 64;  // 4-channel groups per thread: channels 4 sub + 64 c
     __shared__ float m1[16][D];
+    if (w.cnt_all) {
+        // zero the selection's pick counters (the selection pass that follows
+        // adds to them); far fewer counters than threads
+        const long nth = (long)gridDim.x * gridDim.y * blockDim.x;
+        for (long t = ((long)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+             t < w.cnt_len; t += nth)
+            w.cnt_all[t] = 0;
+    }
     const int tensor = blockIdx.y;
     const T* x = tensor == 0 ? q : tensor == 1 ? k : v;
     float* lv1 = tensor == 0 ? w.qbar[0] : tensor == 1 ? w.kbar[0] : w.vbar[0];
@@ -150,10 +160,12 @@ hipError_t launch_pool_d(const void* q, const void* k, const void* v, int dtype,
 }  // namespace
 
 hipError_t launch_pool(const void* q, const void* k, const void* v, int dtype, const Geo& g,
-                       const Ws& w, hipStream_t st)
+                       const Ws& w, bool zero_counts, hipStream_t st)
 {
-    return g.d == D128 ? launch_pool_d<D128>(q, k, v, dtype, g, w, st)
-                       : launch_pool_d<D64>(q, k, v, dtype, g, w, st);
+    Ws wz = w;
+    if (!zero_counts) wz.cnt_all = nullptr;
+    return g.d == D128 ? launch_pool_d<D128>(q, k, v, dtype, g, wz, st)
+                       : launch_pool_d<D64>(q, k, v, dtype, g, wz, st);
 }
 
 }  // namespace llsa

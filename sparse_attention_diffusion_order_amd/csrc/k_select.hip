@@ -20,8 +20,10 @@
 // keys (order-preserving integer images of the scores) for a threshold that
 // admits exactly the K winners, ballots for ties at the K-th key (lowest
 // candidate position first) and a ballot prefix count to write the winners
-// in ascending order.  The picks are also counted per key block and per 16
-// key blocks (see flush_counts), which the sparse transpose uses.
+// in ascending order.  Below the coarsest level the picks are also counted
+// per key block and per 16 key blocks (see flush_counts), which the sparse
+// transpose uses.  When both fit, the two coarsest levels run in one launch
+// (select_top2).
 #include "common.h"
 
 namespace llsa {
@@ -42,9 +44,8 @@ __device__ __forceinline__ unsigned order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Top-K of each of `rows` score rows (LDS, [rows][M]) written ascending to
-// out[r * K ..]; one wave per row at a time.
-// Pick counts of one head: per key block and per 16 key blocks.  A
+// Pick counts of one head below the coarsest level: per key block and per
+// 16 key blocks.  A
 // workgroup first counts its picks per candidate in LDS (pc), then adds them
 // with one global atomic per picked block and one per group of 16
 // candidates (16 consecutive candidates are always the 16 children of one
@@ -57,6 +58,7 @@ struct Counts {
 
 __device__ __forceinline__ void flush_counts(const int* pc, const int* cand, int M, Counts cnt)
 {
+    if (!cnt.c1) return;  // the coarsest level is not counted (its transpose counts itself)
     for (int c = threadIdx.x; c < M; c += blockDim.x)
         if (pc[c]) atomicAdd(cnt.c1 + cand[c], pc[c]);
     for (int gi = threadIdx.x; gi * BS < M; gi += blockDim.x) {
@@ -66,9 +68,13 @@ __device__ __forceinline__ void flush_counts(const int* pc, const int* cand, int
     }
 }
 
+// Top-K of each of `rows` score rows (LDS, [rows][M]) written ascending to
+// out[r * K ..]; one wave per row at a time.  cand: the candidates' block
+// numbers (LDS), or nullptr for 0 .. M-1; pc: per-candidate pick counts
+// (LDS) to add to, or nullptr; lout: an LDS copy of the output, or nullptr.
 template <int KPL>
 __device__ __forceinline__ void select_rows(const float* sc, const int* cand, int* out, int rows,
-                                            int M, int K, int* pc)
+                                            int M, int K, int* pc, int* lout = nullptr)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const unsigned long long below = (1ull << lane) - 1ull;
@@ -109,8 +115,11 @@ __device__ __forceinline__ void select_rows(const float* sc, const int* cand, in
             bool take = (ok[s] && key[s] > T) || (eq && eq_before + __popcll(beq & below) < need);
             unsigned long long bt = __ballot(take);
             if (take) {
-                orow[out_before + __popcll(bt & below)] = cand[s * 64 + lane];
-                atomicAdd(pc + s * 64 + lane, 1);
+                const int pos = out_before + __popcll(bt & below);
+                const int blk = cand ? cand[s * 64 + lane] : s * 64 + lane;
+                orow[pos] = blk;
+                if (lout) lout[r * K + pos] = blk;
+                if (pc) atomicAdd(pc + s * 64 + lane, 1);
             }
             eq_before += __popcll(beq);
             out_before += __popcll(bt);
@@ -262,11 +271,71 @@ __device__ __forceinline__ void select_rows16(const float* sc, const int* cand, 
     }
 }
 
+// Query operand of the fp32 matrix-core scores: lane (g = lane/16, n =
+// lane%16) holds channels (d/4)g .. (d/4)(g+1) - 1 of query row row0 + n
+// (the last valid row repeated past `rows`).
+template <int D>
+__device__ __forceinline__ void load_query_operand(float (&qa)[D / 4], const float* qbar, long row0,
+                                                   int rows)
+{
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+    constexpr int CG = D / 4;
+    const float4* qr = (const float4*)(qbar + (row0 + min(n, rows - 1)) * D + CG * g);
+#pragma unroll
+    for (int t = 0; t < CG / 4; ++t) {
+        const float4 v = qr[t];
+        qa[4 * t] = v.x; qa[4 * t + 1] = v.y; qa[4 * t + 2] = v.z; qa[4 * t + 3] = v.w;
+    }
+}
+
 // Scores on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): 16 query rows x
 // 16 candidates per tile; lane (g = lane/16, n = lane%16) feeds row n and
 // candidate n over channels (d/4)g .. (d/4)(g+1) - 1, one channel per MFMA
 // k-slot, so every lane reads whole 64-byte pieces of the rows.  The channel sum order is
-// fixed by the instruction sequence.  Used for candidate lists of up to 1024.
+// fixed by the instruction sequence.  Then the top-K of the `rows` rows
+// (select_rows16) and the pick counts.  On entry cand and pc (LDS, M each)
+// are filled and zeroed and a barrier has passed; kh = the head's key rows.
+template <int KPG, int D>
+__device__ __forceinline__ void score_select16(const float (&qa)[D / 4], const float* kh, int* out,
+                                               int rows, int M, int K, float scale, float* sc,
+                                               const int* cand, int* pc, Counts cnt)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    constexpr int CG = D / 4;  // channels of lane group g: CG g .. CG g + CG - 1
+    const int tiles = (M + BS - 1) / BS;
+    kh += CG * g;
+    auto load_tile = [&](float (&kb)[CG], int tile) {
+        const int c = cand[min(tile * BS + n, M - 1)];
+        const float4* kr = (const float4*)(kh + (long)c * D);
+#pragma unroll
+        for (int t = 0; t < CG / 4; ++t) {
+            const float4 v = kr[t];
+            kb[4 * t] = v.x; kb[4 * t + 1] = v.y; kb[4 * t + 2] = v.z; kb[4 * t + 3] = v.w;
+        }
+    };
+    float kb[CG], kn[CG];
+    load_tile(kb, min(wv, tiles - 1));
+    for (int tile = wv; tile < tiles; tile += 4) {
+        load_tile(kn, min(tile + 4, tiles - 1));
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < CG; ++k)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[k], kb[k], acc, 0, 0, 0);
+        const int col = tile * BS + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (4 * g + r < rows && col < M) sc[(4 * g + r) * M + col] = acc[r] * scale + 0.0f;
+#pragma unroll
+        for (int k = 0; k < CG; ++k) kb[k] = kn[k];
+    }
+    __syncthreads();
+    select_rows16<KPG>(sc, cand, out, rows, M, K, pc);
+    __syncthreads();
+    flush_counts(pc, cand, M, cnt);
+}
+
+// Used for candidate lists of up to 1024.
 template <int KPG, int D>
 __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qbar,
                                                    const float* __restrict__ kbar,
@@ -295,49 +364,96 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
         }
         pc[c] = 0;
     }
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int g = lane >> 4, n = lane & 15;
-    constexpr int CG = D / 4;  // channels of lane group g: CG g .. CG g + CG - 1
-    float qa[CG];
-    {
-        const float4* qr = (const float4*)(qbar + ((long)gh * n_l + row0 + min(n, rows - 1)) * D + CG * g);
+    float qa[D / 4];
+    load_query_operand<D>(qa, qbar, (long)gh * n_l + row0, rows);
+    __syncthreads();
+    score_select16<KPG, D>(qa, kbar + (long)gh * n_l * D, idx + ((long)gh * n_l + row0) * K, rows,
+                           M, K, scale, sc, cand, pc,
+                           {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)});
+}
+
+// The two coarsest levels in one launch.  Workgroup p (of a head) first
+// chooses the top K_L of level-L row p among all n_L blocks, then -- with
+// those picks kept in LDS as its candidate list -- the top K_{L-1} of the 16
+// level-(L-1) rows 16p .. 16p+15 (the children of row p) exactly as
+// select_mfma does.  Row p's scores are fp32 dot products, eight lanes per
+// candidate (fixed order: each lane's channels in turn, then the lane sums
+// pairwise); its top K_L is taken by one wave (select_rows).  Saves the coarsest level's launch and its write /
+// read of the picks.  The coarsest level's picks are not counted (its
+// transpose counts them itself): one count per workgroup and pick would put
+// every workgroup's atomics on the same few addresses.  n_L <= 64 KPL.
+template <int KPL, int KPG, int D>
+__global__ __launch_bounds__(256) void select_top2(const float* __restrict__ qtop,
+                                                   const float* __restrict__ ktop,
+                                                   const float* __restrict__ qbar,
+                                                   const float* __restrict__ kbar,
+                                                   int* __restrict__ idx_top,
+                                                   int* __restrict__ idx, Counts cnt,
+                                                   int nL, int Ktop, int K,
+                                                   float scale)
+{
+    extern __shared__ float smem[];
+    const int M = BS * Ktop;          // candidates of a level-(L-1) row
+    float* sc = smem;                 // [16][M]
+    int* cand = (int*)(sc + BS * M);  // [M]
+    int* pc = cand + M;               // [M]
+    float* st = (float*)(pc + M);     // [nL] scores of row p
+    int* picks = (int*)(st + nL);     // [Ktop]
+    const int gh = blockIdx.x / nL, p = blockIdx.x % nL;
+    const int n_l = BS * nL;
+    for (int c = threadIdx.x; c < M; c += blockDim.x) pc[c] = 0;
+    // row p's scores: eight lanes per candidate, lane u reading 16-byte
+    // pieces u, u + 8, ... of the rows (query row p and key rows), so each
+    // load instruction takes whole 128-byte lines of 8 key rows; PA rows per
+    // lane group are loaded before the first is used
+    constexpr int NT = D / 32;               // 16-byte pieces per lane and row
+    constexpr int PA = D == D64 ? 4 : 2;     // rows in flight per lane group
+    const int u = threadIdx.x & 7, rg = threadIdx.x >> 3;  // 32 lane groups
+    float4 qv[NT];
+    const float4* qrow = (const float4*)(qtop + ((long)gh * nL + p) * D);
 #pragma unroll
-        for (int t = 0; t < CG / 4; ++t) {
-            const float4 v = qr[t];
-            qa[4 * t] = v.x; qa[4 * t + 1] = v.y; qa[4 * t + 2] = v.z; qa[4 * t + 3] = v.w;
+    for (int t = 0; t < NT; ++t) qv[t] = qrow[u + 8 * t];
+    const float* kt = ktop + (long)gh * nL * D;
+    for (int c0 = 0; c0 < nL; c0 += 32 * PA) {
+        float4 kv[PA][NT];
+#pragma unroll
+        for (int a = 0; a < PA; ++a) {
+            const int c = min(c0 + 32 * a + rg, nL - 1);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) kv[a][t] = ((const float4*)(kt + (long)c * D))[u + 8 * t];
+        }
+#pragma unroll
+        for (int a = 0; a < PA; ++a) {
+            float x = 0.f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                x = fmaf(qv[t].x, kv[a][t].x, x);
+                x = fmaf(qv[t].y, kv[a][t].y, x);
+                x = fmaf(qv[t].z, kv[a][t].z, x);
+                x = fmaf(qv[t].w, kv[a][t].w, x);
+            }
+            // sum over the 8 lanes: within quads, then the two quads (half-row mirror)
+            x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+            x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+            x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+            const int c = c0 + 32 * a + rg;
+            if (u == 0 && c < nL) st[c] = x * scale + 0.0f;  // + 0 turns -0 into +0
         }
     }
     __syncthreads();
-    const int tiles = (M + BS - 1) / BS;
-    const float* kh = kbar + (long)gh * n_l * D + CG * g;
-    auto load_tile = [&](float (&kb)[CG], int tile) {
-        const int c = cand[min(tile * BS + n, M - 1)];
-        const float4* kr = (const float4*)(kh + (long)c * D);
-#pragma unroll
-        for (int t = 0; t < CG / 4; ++t) {
-            const float4 v = kr[t];
-            kb[4 * t] = v.x; kb[4 * t + 1] = v.y; kb[4 * t + 2] = v.z; kb[4 * t + 3] = v.w;
-        }
-    };
-    float kb[CG], kn[CG];
-    load_tile(kb, min(wv, tiles - 1));
-    for (int tile = wv; tile < tiles; tile += 4) {
-        load_tile(kn, min(tile + 4, tiles - 1));
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < CG; ++k)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[k], kb[k], acc, 0, 0, 0);
-        const int col = tile * BS + n;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * g + r < rows && col < M) sc[(4 * g + r) * M + col] = acc[r] * scale + 0.0f;
-#pragma unroll
-        for (int k = 0; k < CG; ++k) kb[k] = kn[k];
-    }
+    if (threadIdx.x < 64)
+        select_rows<KPL>(st, nullptr, idx_top + ((long)gh * nL + p) * Ktop, 1, nL, Ktop, nullptr,
+                         picks);
     __syncthreads();
-    select_rows16<KPG>(sc, cand, idx + ((long)gh * n_l + row0) * K, rows, M, K, pc);
+    // the children's query operand (loaded only now: phase-A registers are
+    // free again, and its latency overlaps the first key tile's)
+    float qa[D / 4];
+    load_query_operand<D>(qa, qbar, (long)gh * n_l + BS * p, BS);
+    for (int c = threadIdx.x; c < M; c += blockDim.x) cand[c] = BS * picks[c / BS] + (c % BS);
     __syncthreads();
-    flush_counts(pc, cand, M, {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)});
+    score_select16<KPG, D>(qa, kbar + (long)gh * n_l * D, idx + ((long)gh * n_l + BS * p) * K, BS,
+                           M, K, scale, sc, cand, pc,
+                           {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)});
 }
 
 template <int KPG, int D>
@@ -354,6 +470,35 @@ hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, 
     hipLaunchKernelGGL((select_mfma<KPG, D>), dim3(G * groups), dim3(256), lds, st, qbar, kbar, parent,
                        idx, cnt, n_l, K, M, scale);
     return hipGetLastError();
+}
+
+template <int KPL, int KPG, int D>
+hipError_t launch_top2(const Geo& g, const Ws& w, hipStream_t st)
+{
+    const int L = g.L, nL = g.n[L];
+    const int M = BS * g.Kl[L];
+    const size_t lds = (size_t)(BS * M + 2 * M + nL + g.Kl[L]) * sizeof(float);
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)select_top2<KPL, KPG, D>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((select_top2<KPL, KPG, D>), dim3(g.G * nL), dim3(256), lds, st,
+                       w.qbar[L - 1], w.kbar[L - 1], w.qbar[L - 2], w.kbar[L - 2], w.idx[L - 1],
+                       w.idx[L - 2], Counts{w.cnt[L - 2], w.c16[L - 2]}, nL, g.Kl[L],
+                       g.Kl[L - 1], g.scale);
+    return hipGetLastError();
+}
+
+template <int KPL, int D>
+hipError_t launch_top2_k(const Geo& g, const Ws& w, hipStream_t st)
+{
+    const int M = BS * g.Kl[g.L];
+    auto f = M <= 16 ? launch_top2<KPL, 1, D> : M <= 32 ? launch_top2<KPL, 2, D>
+           : M <= 64 ? launch_top2<KPL, 4, D> : M <= 128 ? launch_top2<KPL, 8, D>
+           : M <= 256 ? launch_top2<KPL, 16, D> : M <= 512 ? launch_top2<KPL, 32, D>
+           : launch_top2<KPL, 64, D>;
+    return f(g, w, st);
 }
 
 // Coarsest level with more than 1024 blocks: few rows per workgroup, so that
@@ -377,18 +522,28 @@ hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, Counts cn
 }
 
 template <int D>
-hipError_t launch_select_d(const Geo& g, const Ws& w, hipStream_t st)
+hipError_t launch_select_d(const Geo& g, const Ws& w, bool zero_counts, hipStream_t st)
 {
-    const unsigned cgrid = (unsigned)min((w.cnt_len + 255) / 256, 1024L);
-    hipLaunchKernelGGL(clear_counts, dim3(cgrid), dim3(256), 0, st, w.cnt_all, w.cnt_len);
-    for (int l = g.L; l >= 1; --l) {
+    if (zero_counts) {
+        const unsigned cgrid = (unsigned)min((w.cnt_len + 255) / 256, 1024L);
+        hipLaunchKernelGGL(clear_counts, dim3(cgrid), dim3(256), 0, st, w.cnt_all, w.cnt_len);
+    }
+    int l = g.L;
+    // levels L and L-1 together when both fit the matrix-core path
+    if (g.L >= 2 && g.n[g.L] <= 1024 && BS * g.Kl[g.L] <= 1024) {
+        hipError_t e = g.n[g.L] <= 256 ? launch_top2_k<4, D>(g, w, st)
+                                       : launch_top2_k<16, D>(g, w, st);
+        if (e != hipSuccess) return e;
+        l = g.L - 2;
+    }
+    for (; l >= 1; --l) {
         const int* parent = (l == g.L) ? nullptr : w.idx[l];
         const int K = g.Kl[l];  // picks of a level-l row
         const int M = parent ? BS * g.Kl[l + 1] : g.n[l];  // its candidates
         const float* qb = w.qbar[l - 1];
         const float* kb = w.kbar[l - 1];
         int* out = w.idx[l - 1];
-        const Counts cnt = {w.cnt[l - 1], w.c16[l - 1]};
+        const Counts cnt = parent ? Counts{w.cnt[l - 1], w.c16[l - 1]} : Counts{nullptr, nullptr};
         hipError_t e;
         if (M <= 1024) {
             auto f = M <= 16 ? launch_mfma<1, D> : M <= 32 ? launch_mfma<2, D>
@@ -407,9 +562,10 @@ hipError_t launch_select_d(const Geo& g, const Ws& w, hipStream_t st)
 
 }  // namespace
 
-hipError_t launch_select(const Geo& g, const Ws& w, hipStream_t st)
+hipError_t launch_select(const Geo& g, const Ws& w, bool zero_counts, hipStream_t st)
 {
-    return g.d == D128 ? launch_select_d<D128>(g, w, st) : launch_select_d<D64>(g, w, st);
+    return g.d == D128 ? launch_select_d<D128>(g, w, zero_counts, st)
+                       : launch_select_d<D64>(g, w, zero_counts, st);
 }
 
 }  // namespace llsa

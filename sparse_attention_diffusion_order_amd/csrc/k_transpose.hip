@@ -5,17 +5,18 @@
 // directly from the sparse index lists instead of from a dense mask.
 //
 // A counting sort into CSR form (rowptr [G][n_l+1], col [G][n_l*K], every
-// list ascending), one launch per level, coarsest first.  The counts come
-// from the selection pass (per block and per 16 blocks); each workgroup sums
-// the prefix before its own bins from the group counts; the fill gathers
-// instead of scattering: one workgroup
-// owns 16 sibling key blocks 16p .. 16p+15 and walks the only query blocks
-// that can have chosen them -- at a finer level, the children of the query
-// blocks in the parent level's list of block p (hierarchical selection only
-// offers children of chosen parents); at the coarsest level, all query
-// blocks.  The candidates are walked in ascending order and ballots give each
-// hit its rank, so lists come out sorted and identical run to run, with no
-// atomics.
+// list ascending), one launch per level, coarsest first.  Below the coarsest
+// level the counts come from the selection pass (per block and per 16
+// blocks) and each workgroup sums the prefix before its own bins from the
+// group counts; at the coarsest level, where every query block is a
+// candidate, each workgroup counts the (short) index lists itself.  The fill
+// gathers instead of scattering: one workgroup owns 16 sibling key blocks
+// 16p .. 16p+15 and walks the only query blocks that can have chosen them --
+// at a finer level, the children of the query blocks in the parent level's
+// list of block p (hierarchical selection only offers children of chosen
+// parents); at the coarsest level, all query blocks.  The candidates are
+// walked in ascending order and ballots give each hit its rank, so lists come
+// out sorted and identical run to run; the fill uses no atomics.
 #include "common.h"
 
 namespace llsa {
@@ -75,10 +76,12 @@ __device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp, int* 
 }
 
 // One workgroup (4 waves) per 16 sibling key blocks 16p .. 16p+15; one
-// candidate query block per thread.  The selection pass counted how often
-// each key block was chosen (per block and per 16 blocks); the workgroup
-// sums the group counts before its own blocks (n_l / 16 at most) to get its
-// first CSR position, writes rowptr for its blocks, and fills their lists.  Ranks: ballot within a wave, counts of lower waves through LDS,
+// candidate query block per thread.  Below the coarsest level the selection
+// pass counted how often each key block was chosen (per block and per 16
+// blocks); the workgroup sums the group counts before its own blocks (n_l / 16
+// at most) to get its first CSR position (at the coarsest level it counts
+// from the index lists), writes rowptr for its blocks, and fills their
+// lists.  Ranks: ballot within a wave, counts of lower waves through LDS,
 // counts of earlier rounds carried in registers.  Besides col it records, for
 // the pooled-token gradients and dk/dv, the position of j in each listed
 // query block's index list.
@@ -87,6 +90,7 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
     __shared__ int wcnt[4][16];
     __shared__ int wsum[4];
     __shared__ int start[16];
+    __shared__ int lcnt[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = g.n[l];
     const int groups = (n + 15) / 16;
@@ -116,10 +120,25 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
         }
     };
     probe(0);
-    // first position of this group: the counts of blocks 0 .. 16 grp - 1,
-    // summed as 16-block groups
+    // first position of this group: the counts of blocks 0 .. 16 grp - 1.
+    // Below the coarsest level they come from the selection pass, summed as
+    // 16-block groups.  At the coarsest level every query block is a
+    // candidate, so the workgroup counts them from the (short) index lists:
+    // the entries below bin 16 grp, and the hits of each of its 16 bins.
+    const bool top = l == g.L;
     int acc = 0;
-    for (int b = tid; b < grp; b += blockDim.x) acc += c16[b];
+    if (top) {
+        if (tid < 16) lcnt[tid] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += blockDim.x) {
+            int below;
+            unsigned m = hit_mask(I + (long)i * K, K, grp, &below);
+            acc += below;
+            for (; m; m &= m - 1) atomicAdd(&lcnt[__ffs(m) - 1], 1);
+        }
+    } else {
+        for (int b = tid; b < grp; b += blockDim.x) acc += c16[b];
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if (lane == 0) wsum[wv] = acc;
@@ -127,7 +146,7 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
     if (tid < 16) {
         const int base = wsum[0] + wsum[1] + wsum[2] + wsum[3];
         const int j = 16 * grp + tid;
-        const int c = j < n ? cnt[j] : 0;
+        const int c = top ? lcnt[tid] : j < n ? cnt[j] : 0;
         int x = c;  // inclusive scan over the 16 bins
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) {
