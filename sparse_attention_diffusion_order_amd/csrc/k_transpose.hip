@@ -82,14 +82,15 @@ __device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp, int* 
 // at most) to get its first CSR position (at the coarsest level it counts
 // from the index lists), writes rowptr for its blocks, and fills their
 // lists.  Ranks: ballot within a wave, counts of lower waves through LDS,
-// counts of earlier rounds carried in registers.  Besides col it records, for
+// counts of earlier rounds in LDS.  Besides col it records, for
 // the pooled-token gradients and dk/dv, the position of j in each listed
 // query block's index list.
 __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
 {
-    __shared__ int wcnt[4][16];
+    __shared__ int wcnt[2][4][16];                   // per round parity, wave, bin
+    __shared__ unsigned long long wbal[2][4][16];    // the wave's ballot of each bin
     __shared__ int wsum[4];
-    __shared__ int start[16];
+    __shared__ int run[16];                          // next free position of each bin
     __shared__ int lcnt[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = g.n[l];
@@ -153,47 +154,48 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
             const int y = __shfl_up(x, o, 16);
             if (tid >= o) x += y;
         }
-        start[tid] = base + x - c;
+        run[tid] = base + x - c;
         if (j < n) rowptr[j] = base + x - c;
         if (j == n - 1) rowptr[n] = base + x;
     }
     __syncthreads();
 
+    // Fill, 256 candidates a round.  Every bin's hits are ranked by ballot
+    // (candidate order = thread order); a lane then places only its own hits
+    // (about one per round): position = the bin's next free slot + the hits
+    // of lower waves + the lower lanes of its own wave.  The counts and
+    // ballots alternate between two buffers, so the bins' running positions
+    // can be advanced after the round while the next round's ballots go in.
     const unsigned long long below = (1ull << lane) - 1ull;
-    int run[16];
-#pragma unroll
-    for (int b = 0; b < 16; ++b) run[b] = start[b];
-    for (int c0 = 0; c0 < cs.n; c0 += 256) {
+    for (int c0 = 0, par = 0; c0 < cs.n; c0 += 256, par ^= 1) {
         const int i = ci, first = cfirst;
         const unsigned m = cm;
-        unsigned long long bal[16];
 #pragma unroll
         for (int b = 0; b < 16; ++b) {
-            bal[b] = __ballot((m >> b) & 1u);
-            if (lane == b) wcnt[wv][b] = __popcll(bal[b]);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            int before = 0, total = 0;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int k = wcnt[u][b];
-                before += (u < wv) ? k : 0;
-                total += k;
+            const unsigned long long bal = __ballot((m >> b) & 1u);
+            if (lane == b) {
+                wcnt[par][wv][b] = __popcll(bal);
+                wbal[par][wv][b] = bal;
             }
-            const int pos = run[b] + before + __popcll(bal[b] & below);
+        }
+        probe(c0 + 256);  // the next round's candidates, in flight meanwhile
+        __syncthreads();
+        for (unsigned mm = m; mm; mm &= mm - 1) {
+            const int b = __ffs(mm) - 1;
+            int pos = run[b] + __popcll(wbal[par][wv][b] & below);
+            for (int u = 0; u < wv; ++u) pos += wcnt[par][u][b];
             // pos < n K whenever the counts match the index lists (both come
             // from the same selection pass); the test only keeps a workspace
             // that was not filled by one from being written out of bounds
-            if (((m >> b) & 1u) && pos < n * K) {
+            if (pos < n * K) {
                 col[pos] = i;
                 slots[pos] = (unsigned char)(first + __popc(m & ((1u << b) - 1u)));
             }
-            run[b] += total;
         }
-        probe(c0 + 256);
-        __syncthreads();
+        __syncthreads();  // every lane has read run[] for this round
+        if (tid < 16)
+            run[tid] += wcnt[par][0][tid] + wcnt[par][1][tid] + wcnt[par][2][tid] +
+                        wcnt[par][3][tid];
     }
 }
 
