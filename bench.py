@@ -98,7 +98,7 @@ def sha_of_sources():
 PMC_SUMMARY = "pmc_fetch_write_llsa_kernels_%s.json"
 TRACE_SUMMARY = "kernel_trace_llsa_kernels_%s.md"
 KERNEL_OF_STAGE = {"zorder": ("zorder_kernel",), "pool": ("pool_l12",),
-                   "select": ("select_mfma", "select_kernel"),
+                   "select": ("select_top2", "select_mfma", "select_kernel"),
                    "attn_fwd": ("attn_fwd_u4", "attn_fwd_bf16"),
                    "transpose": ("transpose_fill",), "dq": ("dq_bf16",),
                    "enrich": ("enrich_bwd_bf16",), "dkdv": ("dkdv_bf16",)}
