@@ -6,9 +6,7 @@ resident in HBM: grid-order gather of Q, K, V (raster -> quadtree order), the
 forward (pool pyramid, hierarchical Top-K, sparse attention with enrichment)
 and the backward (index transpose, dQ, pooled-token gradients, dK/dV), all
 through the C ABI of libllsa.so: llsa_grid_order, llsa_forward and
-llsa_backward on the caller's stream (the backward runs the index transpose on
-a stream of its own beside dQ and joins it before the pooled-token
-gradients).  Prints ONE JSON line.
+llsa_backward on one stream.  Prints ONE JSON line.
 
 The headline times K whole steps between two HIP events on the caller's
 stream.  A second pass of K steps runs the same work stage by stage
@@ -379,8 +377,7 @@ def main():
         lib.llsa_backward(q, k, v, out, lse, do, dq, dk, dv, *shape)
 
     def step():
-        """one pass of the whole path through the public entry points (the
-        backward runs its sparse transpose beside the dq pass)"""
+        """one pass of the whole path through the public entry points"""
         run_stage("zorder")
         fwdbwd()
 

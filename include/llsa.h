@@ -148,14 +148,7 @@ int llsa_forward(const void* q, const void* k, const void* v, void* out, float* 
  * from the workspace (no re-selection; selection passes no gradient), builds
  * the key->query lists by a counting sort, then computes dq query-major and
  * dk, dv key-major.  A pooled token passes 1/16^l of its gradient to each of
- * the 16^l tokens it averages.  Deterministic: no floating-point atomics.
- * Streams: the key->query lists are built on a second stream of the library's
- * own (one per device, default priority, made on the first call outside
- * stream capture and kept until the process ends) while dq runs on `stream`;
- * `stream` waits for that work before the pooled-token gradients, so all of
- * the call's work is ordered before what the caller enqueues on `stream`
- * afterwards.  Calls from several host threads are serialised while they
- * enqueue this fork and join. */
+ * the 16^l tokens it averages.  Deterministic: no floating-point atomics. */
 int llsa_backward(const void* q, const void* k, const void* v, const void* out,
                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
                   int B, int H, int N, int d, int block_size, int topk, int levels,
@@ -188,8 +181,7 @@ int llsa_backward_lk(const void* q, const void* k, const void* v, const void* ou
 /* Stages of llsa_forward / llsa_backward, for per-kernel timing and tests.
  * llsa_forward == parts POOL, SELECT, ATTN in that order; llsa_backward ==
  * parts TRANSPOSE, DQ, ENRICH, DKDV in that order (ENRICH: gradients of the
- * pooled tokens, needed by DKDV; llsa_backward runs TRANSPOSE beside DQ, the
- * parts all run on `stream`).  Each part reads what the parts before it
+ * pooled tokens, needed by DKDV).  Each part reads what the parts before it
  * left in the workspace (SELECT also records how often each key block was
  * chosen, which TRANSPOSE uses); any part may be repeated.  Same arguments
  * and errors as the full calls; an unknown part number gives

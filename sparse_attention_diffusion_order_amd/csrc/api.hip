@@ -4,8 +4,6 @@
 // reported identically on a host without a GPU.
 #include <string.h>
 
-#include <mutex>
-
 #include "common.h"
 
 using namespace llsa;
@@ -209,48 +207,6 @@ int run_backward_part(int part, const void* q, const void* k, const void* v, con
     }
 }
 
-// A second stream per device: llsa_backward runs the sparse transpose on it
-// while the dq pass runs on the caller's stream.  The two passes read the
-// index lists and write disjoint workspace regions (CSR lists and slots vs.
-// delta, pooled-gradient partials and dq); the enrichment pass needs both, so
-// the caller's stream waits for the transpose before it.  Made on first use
-// outside stream capture, default priority, kept until the process ends.
-struct Side {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    bool tried = false;
-};
-constexpr int MAX_DEV = 64;
-std::mutex side_mu;
-Side side_tab[MAX_DEV];
-
-// With side_mu held: the current device's side stream, or nullptr (then the
-// two passes run one after the other on the caller's stream).
-Side* side_stream(hipStream_t caller)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    Side& sd = side_tab[dev];
-    if (!sd.tried) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-            (void)hipGetLastError();
-            return nullptr;  // no stream or event creation during capture
-        }
-        sd.tried = true;
-        if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess ||
-            hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
-            (void)hipGetLastError();
-            sd.s = nullptr;
-        }
-    }
-    return sd.s ? &sd : nullptr;
-}
-
 // the same top-k at every level, as an array (levels outside 1..MAX_L are
 // rejected by validate before the array is read)
 struct UniformK {
@@ -387,32 +343,7 @@ int llsa_backward_lk(const void* q, const void* k, const void* v, const void* ou
     int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
                      stream, &p);
     if (rc) return rc;
-    {
-        // transpose (side stream) alongside dq (caller's stream); the mutex
-        // keeps each call's record / wait / record / wait sequence whole
-        std::lock_guard<std::mutex> lock(side_mu);
-        Side* sd = side_stream(p.st);
-        if (sd) {
-            Prep ps = p;
-            ps.st = sd->s;
-            if (hipEventRecord(sd->fork, p.st) != hipSuccess ||
-                hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
-                return LLSA_ERR_HIP;
-            rc = run_backward_part(LLSA_PART_TRANSPOSE, q, k, v, out, lse, dout, dq, dk, dv,
-                                   dtype, ps);
-            if (rc) return rc;
-            if (hipEventRecord(sd->join, sd->s) != hipSuccess) return LLSA_ERR_HIP;
-            rc = run_backward_part(LLSA_PART_DQ, q, k, v, out, lse, dout, dq, dk, dv, dtype, p);
-            if (rc) return rc;
-            if (hipStreamWaitEvent(p.st, sd->join, 0) != hipSuccess) return LLSA_ERR_HIP;
-        } else {
-            for (int part : {LLSA_PART_TRANSPOSE, LLSA_PART_DQ}) {
-                rc = run_backward_part(part, q, k, v, out, lse, dout, dq, dk, dv, dtype, p);
-                if (rc) return rc;
-            }
-        }
-    }
-    for (int part : {LLSA_PART_ENRICH, LLSA_PART_DKDV}) {
+    for (int part : {LLSA_PART_TRANSPOSE, LLSA_PART_DQ, LLSA_PART_ENRICH, LLSA_PART_DKDV}) {
         rc = run_backward_part(part, q, k, v, out, lse, dout, dq, dk, dv, dtype, p);
         if (rc) return rc;
     }

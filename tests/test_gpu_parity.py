@@ -287,13 +287,13 @@ def test_repeated_parts_keep_the_transpose_exact():
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
 
 
-def test_backward_transpose_beside_dq_matches_stage_order():
-    """llsa_backward runs the index transpose on a stream of its own while dq
-    runs on the caller's, and joins it before the pooled-token gradients.  On a
-    caller stream other than the default one, two back-to-back forward +
-    backward calls with different inputs and workspaces (no host sync between
-    them) give, bit for bit, the gradients and key->query lists of the
-    one-stream stage-by-stage sequence."""
+def test_whole_calls_on_a_side_stream_match_stage_order():
+    """On a caller stream other than the default one, two back-to-back
+    llsa_forward + llsa_backward calls with different inputs and workspaces
+    (no host sync between them) give, bit for bit, the output, gradients and
+    key->query lists of the stage-by-stage part sequence on the default stream
+    (llsa_forward lets its pool launch zero the pick counters; the selection
+    part on its own zeroes them itself)."""
     import torch
     import sparse_attention_diffusion_order_amd as lib
     ws_ = [small("side%d" % s_, 1, 3, 128, "bf16", 2, 8, seed=s_) for s_ in (1, 2)]
