@@ -353,6 +353,10 @@ _SAMPLED = [synth.WORKLOADS[n] for n in (
     "grid128_bf16_l2_k16", "grid256_bf16_l2_k16", "grid512_bf16_l3_k16",
     "video16x64x64_bf16_l2_k16", "rect192x320_bf16_l2_k16",
     "grid256_d128_bf16_l2_k16")] + [
+    # coarsest levels of 1024 and 480 blocks under a finer level: the fused
+    # two-level selection with 16 keys per lane in its first phase
+    _grid("grid512_bf16_l2_k16", "bf16", 2, 16, 512, H=2),
+    _grid("rect384x320_bf16_l2_k24", "bf16", 2, 24, 320, height=384, H=1, d=128),
     # the deepest pyramids N <= 2^23 allows: 4 and 5 levels down to one block
     _grid("grid256_bf16_l4_k1", "bf16", 4, 1, 256, H=1),
     _grid("grid1024_bf16_l5_k1", "bf16", 5, 1, 1024, H=1),
