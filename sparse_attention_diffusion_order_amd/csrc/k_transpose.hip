@@ -85,17 +85,32 @@ __device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp, int* 
 // counts of earlier rounds in LDS.  Besides col it records, for
 // the pooled-token gradients and dk/dv, the position of j in each listed
 // query block's index list.
-__global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
+//
+// pair != 0: one launch builds the two coarsest levels.  The first
+// G * ceil(n_L / 16) workgroups take level L; the others take level L-1 and
+// find the level-L blocks that chose their group's parent by scanning the
+// level-L index lists (at most TOP2_MAX rows, read from L2) instead of
+// reading level L's key->query lists, which the same launch is building.
+constexpr int TOP2_MAX = 1024;
+
+__global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l, int pair)
 {
     __shared__ int wcnt[2][4][16];                   // per round parity, wave, bin
     __shared__ unsigned long long wbal[2][4][16];    // the wave's ballot of each bin
     __shared__ int wsum[4];
     __shared__ int run[16];                          // next free position of each bin
     __shared__ int lcnt[16];
+    __shared__ int pickers[TOP2_MAX];                // pair mode: level-L choosers of the parent
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int bid = blockIdx.x;
+    if (pair) {
+        const int top_wgs = g.G * ((g.n[g.L] + 15) / 16);
+        l = bid < top_wgs ? g.L : g.L - 1;
+        if (bid >= top_wgs) bid -= top_wgs;
+    }
     const int n = g.n[l];
     const int groups = (n + 15) / 16;
-    const int gh = blockIdx.x / groups, grp = blockIdx.x % groups;
+    const int gh = bid / groups, grp = bid % groups;
     const int K = g.Kl[l];  // picks per level-l row
     const int* I = w.idx[l - 1] + (long)gh * n * K;
     const int* cnt = w.cnt[l - 1] + (long)gh * n;
@@ -107,7 +122,41 @@ __global__ __launch_bounds__(256) void transpose_fill(Geo g, Ws w, int l)
     // the candidate walk (parent list -> candidate rows -> their picks) and
     // the prefix over earlier bins are independent: both go out before the
     // first barrier
-    const Cands cs = make_cands(g, w, l, gh, grp);
+    Cands cs;
+    if (pair && l == g.L - 1) {
+        // the level-L rows whose lists hold block grp, ascending
+        const int nT = g.n[g.L], KT = g.Kl[g.L];
+        const int* IT = w.idx[g.L - 1] + (long)gh * nT * KT;
+        const unsigned long long lower = (1ull << lane) - 1ull;
+        int total = 0;
+        for (int a0 = 0; a0 < nT; a0 += 256) {
+            const int a = a0 + tid;
+            bool hit = false;
+            if (a < nT) {
+                const int* row = IT + (long)a * KT;
+                if ((KT & 3) == 0) {
+                    for (int e = 0; e < KT; e += 4) {
+                        const int4 j4 = *(const int4*)(row + e);
+                        hit |= (j4.x == grp) | (j4.y == grp) | (j4.z == grp) | (j4.w == grp);
+                    }
+                } else {
+                    for (int e = 0; e < KT; ++e) hit |= row[e] == grp;
+                }
+            }
+            const unsigned long long bal = __ballot(hit);
+            if (lane == 0) wsum[wv] = __popcll(bal);
+            __syncthreads();
+            int pos = total + __popcll(bal & lower);
+            for (int u = 0; u < wv; ++u) pos += wsum[u];
+            if (hit) pickers[pos] = a;
+            total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+            __syncthreads();
+        }
+        cs.plist = pickers;
+        cs.n = BS * total;
+    } else {
+        cs = make_cands(g, w, l, gh, grp);
+    }
     int ci = 0, cfirst = 0;
     unsigned cm = 0;
     auto probe = [&](int c0) {
@@ -206,9 +255,17 @@ hipError_t launch_transpose(const Geo& g, const Ws& w, hipStream_t st)
     // level 1 feeds the key-major dk/dv pass; levels >= 2 feed the pooled-
     // token gradients; finer levels need the coarser lists, so all are built,
     // coarsest first.
-    for (int l = g.L; l >= 1; --l) {
+    int l = g.L;
+    if (g.L >= 2 && g.n[g.L] <= TOP2_MAX) {  // the two coarsest levels in one launch
+        dim3 grid((unsigned)(g.G * ((g.n[l] + 15) / 16 + (g.n[l - 1] + 15) / 16)));
+        hipLaunchKernelGGL(transpose_fill, grid, dim3(256), 0, st, g, w, l - 1, 1);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        l -= 2;
+    }
+    for (; l >= 1; --l) {
         dim3 grid((unsigned)(g.G * ((g.n[l] + 15) / 16)));
-        hipLaunchKernelGGL(transpose_fill, grid, dim3(256), 0, st, g, w, l);
+        hipLaunchKernelGGL(transpose_fill, grid, dim3(256), 0, st, g, w, l, 0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
