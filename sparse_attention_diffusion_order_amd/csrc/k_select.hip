@@ -12,10 +12,10 @@
 //
 // One workgroup (4 waves) per group of R query rows that share a candidate
 // list: the 16 siblings of a parent below the coarsest level (candidates =
-// the 16 K' children of the parent's K' picks, ascending), or R rows of the coarsest
-// level (candidates = all blocks).  Scores of the R x M tile live in LDS.
-// Summation order of a score: four partial sums of 16 channels each, combined
-// pairwise -- fixed, so the result does not depend on the launch.
+// the 16 K' children of the parent's K' picks, ascending), or R rows of the
+// coarsest level (candidates = all blocks).  Scores of the R x M tile live in
+// LDS.  Each kernel sums a score's channels in one fixed order (stated at the
+// kernel), so the result does not depend on the launch.
 // Each wave then selects for its rows with an MSB-first radix search on the
 // keys (order-preserving integer images of the scores) for a threshold that
 // admits exactly the K winners, ballots for ties at the K-th key (lowest
@@ -30,7 +30,8 @@ namespace llsa {
 namespace {
 
 // Zero the choice counts of every level (the selection launches that follow
-// on the same stream add to them), so each selection pass counts afresh.
+// on the same stream add to them), so each selection pass counts afresh; used
+// by the selection part on its own (llsa_forward's pool launch zeroes them).
 __global__ __launch_bounds__(256) void clear_counts(int* __restrict__ cnt, long n)
 {
     for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < n;
@@ -45,12 +46,10 @@ __device__ __forceinline__ unsigned order_key(float f)
 }
 
 // Pick counts of one head below the coarsest level: per key block and per
-// 16 key blocks.  A
-// workgroup first counts its picks per candidate in LDS (pc), then adds them
-// with one global atomic per picked block and one per group of 16
-// candidates (16 consecutive candidates are always the 16 children of one
-// block, or 16 consecutive blocks at the coarsest level).  Integer atomics:
-// exact whatever the order.
+// 16 key blocks.  A workgroup first counts its picks per candidate in LDS
+// (pc), then adds them with one global atomic per picked block and one per
+// group of 16 candidates (16 consecutive candidates are always the 16
+// children of one block).  Integer atomics: exact whatever the order.
 struct Counts {
     int* c1;
     int* c16;
