@@ -335,6 +335,38 @@ def test_whole_calls_on_a_side_stream_match_stage_order():
                                               ws_array(ws2, off, cnt, np.int32))
 
 
+def test_whole_calls_on_a_reused_garbage_workspace():
+    """llsa_forward zeroes the selection's pick counters itself (in its pool
+    launch): a workspace filled with 0xFF bytes, then reused by a second
+    forward + backward, gives bit for bit the results of a fresh one, and the
+    key->query lists stay the exact transpose of the index lists."""
+    import torch
+    import sparse_attention_diffusion_order_amd as lib
+    w = small("reuse", 1, 2, 64, "bf16", 2, 4)
+    inp = synth.make_inputs(w)
+    q, k, v, do = (to_device(inp[n_], "bf16") for n_ in ("q", "k", "v", "do"))
+    out0, lse0, ws0 = lib.forward(q, k, v, w.topk, w.levels)
+    ref = (out0,) + lib.backward(q, k, v, out0, lse0, do, w.topk, w.levels, ws0)
+    ws = torch.full_like(ws0, 255)
+    G = w.B * w.H
+    lay = lib.llsa_workspace_layout_lk(w.B, w.H, w.N, w.d, BS, [w.topk] * w.levels, w.levels,
+                                       lib.BF16)
+    for _ in range(2):
+        out, lse, _ws = lib.forward(q, k, v, w.topk, w.levels, workspace=ws)
+        got = (out,) + lib.backward(q, k, v, out, lse, do, w.topk, w.levels, ws)
+        torch.cuda.synchronize()
+        for a_, b_ in zip(got, ref):
+            assert torch.equal(a_.view(torch.int16), b_.view(torch.int16))
+        for l in range(w.levels):
+            n = w.N // BS ** (l + 1)
+            idx = ws_array(ws, lay["idx"][l], G * n * w.topk, np.int32).reshape(G, n, w.topk)
+            rp = ws_array(ws, lay["rowptr"][l], G * (n + 1), np.int32).reshape(G, n + 1)
+            col = ws_array(ws, lay["col"][l], G * n * w.topk, np.int32).reshape(G, n * w.topk)
+            want_rp, want_col = oracle.transpose(idx)
+            np.testing.assert_array_equal(rp, want_rp)
+            np.testing.assert_array_equal(col, want_col)
+
+
 # ------------------------------------------------------- full-size workloads
 
 def _needed_qblocks(w, idx, kblocks):
