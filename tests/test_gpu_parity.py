@@ -179,6 +179,9 @@ _PER_LEVEL = [
     (_grid("grid64_bf16_l2_k8x4", "bf16", 2, (8, 4), 64), oracle.SIZE_BIAS),
     (_grid("grid32_f32_l2_k4x2", "f32", 2, (4, 2), 32), oracle.SIZE_BIAS),
     (_grid("grid64_bf16_l2_k2x16", "bf16", 2, (2, 16), 64), 0),         # fewer fine picks
+    # every coarsest block picked: the fused two-level selection with 1024
+    # candidates per fine row (its largest LDS tile)
+    (_grid("grid128_bf16_l2_k16x64", "bf16", 2, (16, 64), 128, H=1), 0),
 ]
 
 
