@@ -305,6 +305,9 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
     // per-wave Q and dO tiles; after the last tile the same memory holds the
     // four waves' partial sums for the cross-wave reduction
     __shared__ __attribute__((aligned(16))) unsigned short smem[4][2][TILE<D>];
+    // lse and delta of each wave's 64 queries (its four blocks are consecutive),
+    // loaded once, so no step waits on a global load for them
+    __shared__ __attribute__((aligned(16))) float rowst[4][2][4 * BS];
     float* red = (float*)&smem[0][0][0];  // [wave][dtile][r][lane], one kind at a time
     static_assert(sizeof(smem) >= 4 * ND * 4 * 64 * sizeof(float), "reduction buffer");
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -327,6 +330,11 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
 #pragma unroll
         for (int v = 0; v < NI; ++v) xd[v] = ld8(dout + a + (long)TS::RPI * v * D);
     };
+    {
+        const long t0 = (long)gh * g.N + (long)(16 * a2 + 4 * wv) * BS + lane;
+        rowst[wv][0][lane] = lse[t0];
+        rowst[wv][1][lane] = w.delta[t0];
+    }
     for (int l = 2; l <= g.L; ++l) {
         const int al = a2 >> (4 * (l - 2));
         const int Kl = g.Kl[l];
@@ -351,7 +359,6 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
             load_rows(xq, xd, row_addr(0));
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int i = 16 * a2 + 4 * wv + u;
                 put_rows<D>(lq, xq, lane);
                 put_rows<D>(ld, xd, lane);
                 load_rows(xq, xd, row_addr(min(u + 1, 3)));
@@ -361,9 +368,8 @@ __global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __r
                 operand_rows<D, TS::ROW_T>(ld, ad, lane);
                 f32x4 s = scores<D>(aq, bk);  // S[query][entry]
                 f32x4 dp = scores<D>(ad, bv);
-                const long tq = (long)gh * g.N + (long)i * BS + 4 * gq;
-                const float4 l4 = *(const float4*)(lse + tq);
-                const float4 d4 = *(const float4*)(w.delta + tq);
+                const float4 l4 = *(const float4*)&rowst[wv][0][u * BS + 4 * gq];
+                const float4 d4 = *(const float4*)&rowst[wv][1][u * BS + 4 * gq];
                 const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, dr[4] = {d4.x, d4.y, d4.z, d4.w};
                 bf16x4 pP, pS;
 #pragma unroll
