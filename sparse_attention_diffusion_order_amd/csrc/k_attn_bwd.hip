@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void enrich_bwd_bf16(const unsigned short* __restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ? 2 : 1))) void enrich_bwd_bf16(const unsigned short* __restrict__ q,
                                                        const float* __restrict__ lse,
                                                        const unsigned short* __restrict__ dout,
                                                        Geo g, Ws w)
