@@ -227,6 +227,36 @@ def test_all_blocks_no_enrichment_equals_dense(dtype):
     assert_close(gpu["lse"], lse, tol["out_max"], tol["out_mean"], "lse")
 
 
+@pytest.mark.parametrize("w", [small("peak_f32", 1, 2, 32, "f32", 2, 2),
+                               small("peak_bf16", 1, 2, 64, "bf16", 2, 4)],
+                         ids=lambda w: w.name)
+def test_peaked_logits(w):
+    """Q and K scaled by 4 (exactly: a power of two), so logits spread over
+    about +-50 and most softmax weights underflow: the online softmax's
+    running maximum moves far more often than on unit-scale inputs.  Out and
+    lse keep their tolerances (out is still a convex combination of V rows).
+    The gradients scale with Q and K, and the bf16 path's error (P and dS are
+    rounded to bf16 for the MFMAs, a relative error) scales with them: the
+    bound is 4x the unit-scale one (bf16 dq measured 0.104 here)."""
+    inp = synth.make_inputs(w)
+    for n_ in ("q", "k"):
+        inp[n_], inp[n_ + "64"] = synth._cast(inp[n_ + "64"] * 4.0, w.dtype)
+        assert np.array_equal(inp[n_ + "64"] / 4.0, synth.make_inputs(w)[n_ + "64"])
+    gpu = gpu_run(w, inp)
+    z = oracle_inputs(w, inp)
+    tol = TOL[w.dtype]
+    qp, kp, vp = (oracle.pool(z[n_], BS, w.levels) for n_ in ("q", "k", "v"))
+    check_selection(w, gpu, (qp, kp), exact=(w.dtype == "f32"))
+    idx = gpu["idx"]
+    scale = 1.0 / np.sqrt(w.d)
+    o, lse = oracle.forward(z["q"], z["k"], z["v"], kp, vp, idx, BS, scale)
+    assert_close(gpu["out"], o, tol["out_max"], tol["out_mean"], "out")
+    assert_close(gpu["lse"], lse, tol["out_max"], tol["out_mean"], "lse")
+    dq, dk, dv = oracle.backward(z["q"], z["k"], z["v"], kp, vp, idx, o, lse, z["do"], BS, scale)
+    for n_, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(gpu[n_], ref, 4.0 * tol["grad_max"], what=n_)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_zero_query_ties_resolve_to_lowest_blocks(dtype):
     w = small("zeroq", 1, 2, 64, dtype, 2, 4)
