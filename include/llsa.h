@@ -179,9 +179,11 @@ int llsa_backward_lk(const void* q, const void* k, const void* v, const void* ou
                      int dtype, unsigned flags, void* workspace, size_t ws_bytes, void* stream);
 
 /* Stages of llsa_forward / llsa_backward, for per-kernel timing and tests.
- * llsa_forward == parts POOL, SELECT, ATTN in that order; llsa_backward ==
- * parts TRANSPOSE, DQ, ENRICH, DKDV in that order (ENRICH: gradients of the
- * pooled tokens, needed by DKDV).  Each part reads what the parts before it
+ * llsa_forward gives the results of parts POOL, SELECT, ATTN in that order;
+ * llsa_backward those of parts TRANSPOSE, DQ, ENRICH, DKDV in that order
+ * (ENRICH: gradients of the pooled tokens, needed by DKDV).  The full calls
+ * may merge launches (the bf16 backward runs TRANSPOSE's first levels inside
+ * DQ's launch; the forward's pool zeroes SELECT's counters).  Each part reads what the parts before it
  * left in the workspace (SELECT also records how often each key block was
  * chosen, which TRANSPOSE uses); any part may be repeated.  Same arguments
  * and errors as the full calls; an unknown part number gives

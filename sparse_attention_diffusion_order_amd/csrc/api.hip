@@ -343,7 +343,18 @@ int llsa_backward_lk(const void* q, const void* k, const void* v, const void* ou
     int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
                      stream, &p);
     if (rc) return rc;
-    for (int part : {LLSA_PART_TRANSPOSE, LLSA_PART_DQ, LLSA_PART_ENRICH, LLSA_PART_DKDV}) {
+    if (dtype == LLSA_BF16) {
+        // dQ carries the first transpose launch's workgroups (one launch for
+        // both); then the finer levels' transposes, if any
+        rc = hip_rc(launch_attn_dq_transpose(q, k, v, out, lse, dout, dq, p.geo, p.ws, p.st));
+        if (rc) return rc;
+    } else {
+        for (int part : {LLSA_PART_TRANSPOSE, LLSA_PART_DQ}) {
+            rc = run_backward_part(part, q, k, v, out, lse, dout, dq, dk, dv, dtype, p);
+            if (rc) return rc;
+        }
+    }
+    for (int part : {LLSA_PART_ENRICH, LLSA_PART_DKDV}) {
         rc = run_backward_part(part, q, k, v, out, lse, dout, dq, dk, dv, dtype, p);
         if (rc) return rc;
     }

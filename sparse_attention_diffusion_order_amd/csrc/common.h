@@ -279,6 +279,21 @@ hipError_t launch_select(const Geo& g, const Ws& w, bool zero_counts, hipStream_
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                            int dtype, const Geo& g, const Ws& w, hipStream_t st);
 hipError_t launch_transpose(const Geo& g, const Ws& w, hipStream_t st);
+// The first transpose launch: the two coarsest levels together (pair) when
+// the coarsest level has at most 1024 blocks, else the coarsest alone -- its
+// level argument, pair flag and workgroup count; and the launches of the
+// levels it does not build.
+struct TrFirst {
+    int l, pair, wgs;
+};
+TrFirst transpose_first(const Geo& g);
+hipError_t launch_transpose_after(const Geo& g, const Ws& w, const TrFirst& f, hipStream_t st);
+// bf16 dQ with the first transpose launch's workgroups in front of its own
+// (both read only the forward's results and write disjoint workspace
+// regions), so the latency-bound transpose overlaps dQ in one launch.
+hipError_t launch_attn_dq_transpose(const void* q, const void* k, const void* v, const void* out,
+                                    const float* lse, const void* dout, void* dq, const Geo& g,
+                                    const Ws& w, hipStream_t st);
 hipError_t launch_attn_dq(const void* q, const void* k, const void* v, const void* out,
                           const float* lse, const void* dout, void* dq, int dtype, const Geo& g,
                           const Ws& w, hipStream_t st);

@@ -31,6 +31,7 @@
 // explicit pooled tokens at every level.
 // No floating-point atomics anywhere: results are bit-identical run to run.
 #include "common.h"
+#include "transpose.h"
 
 namespace llsa {
 namespace {
@@ -142,14 +143,16 @@ struct DqLds {
 };
 
 // at least two waves per SIMD at d = 128 (d = 64 has three without a bound)
+// One workgroup of the dQ pass: workgroup bid of nb (XCD-aware order).
 template <int ECAP, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ? 2 : 1))) void dq_bf16(const unsigned short* __restrict__ q,
-                                               const unsigned short* __restrict__ k,
-                                               const unsigned short* __restrict__ v,
-                                               const unsigned short* __restrict__ o,
-                                               const float* __restrict__ lse,
-                                               const unsigned short* __restrict__ dout,
-                                               unsigned short* __restrict__ dq, Geo g, Ws w)
+__device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
+                                         const unsigned short* __restrict__ k,
+                                         const unsigned short* __restrict__ v,
+                                         const unsigned short* __restrict__ o,
+                                         const float* __restrict__ lse,
+                                         const unsigned short* __restrict__ dout,
+                                         unsigned short* __restrict__ dq, const Geo& g,
+                                         const Ws& w, int bid, int nb)
 {
     using Lay = DqLds<ECAP, D>;
     using TS = TileShape<D>;
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
     __shared__ __attribute__((aligned(16))) unsigned short smem[4][Lay::PER_WAVE];
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, nq = lane & 15;
-    const long qblk = (long)xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
+    const long qblk = (long)xcd_block(bid, nb) * 4 + wv;
     if (qblk >= (long)g.G * g.n[1]) return;
     const int gh = (int)(qblk / g.n[1]), i = (int)(qblk % g.n[1]);
     const float c = g.scale * LOG2E;
@@ -292,6 +295,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
         for (int r = 0; r < 4; ++r) r4[r] = f2bf(acc[d][r] * g.scale);
         *(u16x4*)(dq + obase + 16 * d) = r4;
     }
+}
+
+template <int ECAP, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ? 2 : 1))) void dq_bf16(const unsigned short* __restrict__ q,
+                                               const unsigned short* __restrict__ k,
+                                               const unsigned short* __restrict__ v,
+                                               const unsigned short* __restrict__ o,
+                                               const float* __restrict__ lse,
+                                               const unsigned short* __restrict__ dout,
+                                               unsigned short* __restrict__ dq, Geo g, Ws w)
+{
+    dq_block<ECAP, D>(q, k, v, o, lse, dout, dq, g, w, blockIdx.x, gridDim.x);
+}
+
+// The dQ pass with the first transpose launch in front: workgroups below
+// tr_pad (tr_wgs rounded up to a multiple of 8, so that the dQ workgroups keep
+// their XCD placement) build the transpose's first levels, the rest run dQ.
+// The two parts read only the forward's results and write disjoint workspace
+// regions, so the latency-bound transpose overlaps dQ.
+template <int ECAP, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ? 2 : 1))) void dq_tr_bf16(const unsigned short* __restrict__ q,
+                                               const unsigned short* __restrict__ k,
+                                               const unsigned short* __restrict__ v,
+                                               const unsigned short* __restrict__ o,
+                                               const float* __restrict__ lse,
+                                               const unsigned short* __restrict__ dout,
+                                               unsigned short* __restrict__ dq, Geo g, Ws w,
+                                               TrFirst tr, int tr_pad)
+{
+    const int b = blockIdx.x;
+    if (b < tr_pad) {
+        if (b < tr.wgs) transpose_block(g, w, tr.l, tr.pair, b);
+        return;
+    }
+    dq_block<ECAP, D>(q, k, v, o, lse, dout, dq, g, w, b - tr_pad, (int)gridDim.x - tr_pad);
 }
 
 template <int D>
@@ -847,6 +885,30 @@ hipError_t launch_attn_dq_d(const void* q, const void* k, const void* v, const v
 }
 
 template <int D>
+hipError_t launch_attn_dq_tr_d(const void* q, const void* k, const void* v, const void* out,
+                               const float* lse, const void* dout, void* dq, const Geo& g,
+                               const Ws& w, hipStream_t st)
+{
+    if (g.n_pooled() > 64) {
+        // the large-entry dQ variant has no registers to spare at d = 128:
+        // two launches
+        hipError_t e = launch_transpose(g, w, st);
+        if (e != hipSuccess) return e;
+        return launch_attn_dq_d<D>(q, k, v, out, lse, dout, dq, LLSA_BF16, g, w, st);
+    }
+    const TrFirst tr = transpose_first(g);
+    const int tr_pad = (tr.wgs + 7) & ~7;
+    const long nblk = (long)g.G * g.n[1];
+    hipLaunchKernelGGL((dq_tr_bf16<64, D>), dim3((unsigned)(tr_pad + (nblk + 3) / 4)), dim3(256), 0, st,
+                       (const unsigned short*)q, (const unsigned short*)k,
+                       (const unsigned short*)v, (const unsigned short*)out, lse,
+                       (const unsigned short*)dout, (unsigned short*)dq, g, w, tr, tr_pad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_transpose_after(g, w, tr, st);
+}
+
+template <int D>
 hipError_t launch_attn_enrich_d(const void* q, const float* lse, const void* dout, int dtype,
                                 const Geo& g, const Ws& w, hipStream_t st)
 {
@@ -902,6 +964,14 @@ hipError_t launch_attn_dq(const void* q, const void* k, const void* v, const voi
 {
     return g.d == D128 ? launch_attn_dq_d<D128>(q, k, v, out, lse, dout, dq, dtype, g, w, st)
                        : launch_attn_dq_d<D64>(q, k, v, out, lse, dout, dq, dtype, g, w, st);
+}
+
+hipError_t launch_attn_dq_transpose(const void* q, const void* k, const void* v, const void* out,
+                                    const float* lse, const void* dout, void* dq, const Geo& g,
+                                    const Ws& w, hipStream_t st)
+{
+    return g.d == D128 ? launch_attn_dq_tr_d<D128>(q, k, v, out, lse, dout, dq, g, w, st)
+                       : launch_attn_dq_tr_d<D64>(q, k, v, out, lse, dout, dq, g, w, st);
 }
 
 // Gradients of the enriching pooled tokens (bf16: levels >= 2, level 1 being
