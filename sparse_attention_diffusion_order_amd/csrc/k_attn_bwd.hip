@@ -889,9 +889,10 @@ hipError_t launch_attn_dq_tr_d(const void* q, const void* k, const void* v, cons
                                const float* lse, const void* dout, void* dq, const Geo& g,
                                const Ws& w, hipStream_t st)
 {
-    if (g.n_pooled() > 64) {
-        // the large-entry dQ variant has no registers to spare at d = 128:
-        // two launches
+    if (D == D128 || g.n_pooled() > 64) {
+        // two launches at d = 128: there only two workgroups fit a CU, and the
+        // transpose's long, mostly idle workgroups would hold dQ's slots (and
+        // the large-entry variant has no registers to spare)
         hipError_t e = launch_transpose(g, w, st);
         if (e != hipSuccess) return e;
         return launch_attn_dq_d<D>(q, k, v, out, lse, dout, dq, LLSA_BF16, g, w, st);
