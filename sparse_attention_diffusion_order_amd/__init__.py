@@ -109,10 +109,15 @@ def exported_names():
 
 
 def _ptr(x):
+    """Device address of a tensor (or a raw integer address, passed as is).
+    A tensor that is not in GPU memory is refused: its host address would
+    reach the kernels."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not getattr(x, "is_cuda", False):
+        raise ValueError("libllsa takes device memory; got a tensor on %s" % x.device)
     return x.data_ptr()
 
 
@@ -238,15 +243,37 @@ def _dtype_code(t) -> int:
     raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
 
 
+def _check_tensors(named, shape, dtype, device):
+    """every tensor contiguous, on `device` (a GPU), with `shape` and `dtype`"""
+    for name, t in named:
+        if not getattr(t, "is_cuda", False) or t.device != device:
+            raise ValueError("%s must be on %s (got %s)" % (name, device, t.device))
+        if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must be %s %s, got %s %s" % (name, tuple(shape), dtype,
+                                                             tuple(t.shape), t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def _norm_topk(topk, levels):
+    """an int (every level) or one value per level, as stored in the workspace record"""
+    return int(topk) if isinstance(topk, int) else tuple(int(x) for x in topk)
+
+
 def forward(q, k, v, topk, levels: int, flags: int = 0, workspace=None, stream=None):
     """Returns (out, lse, workspace); the workspace feeds `backward`.  topk: an
-    int for every level, or one value per level (level 1 first)."""
+    int for every level, or one value per level (level 1 first).  The call
+    records its shape, dtype, top-k, levels and flags on the returned
+    workspace tensor; `backward` reuses and checks them."""
     import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
     dt = _dtype_code(q)
-    for t in (q, k, v):
-        if not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("q, k, v must be contiguous tensors of one shape and dtype")
+    if not q.is_cuda:
+        raise ValueError("q, k, v must be on a GPU (got %s)" % q.device)
+    _check_tensors((("q", q), ("k", k), ("v", v)), q.shape, q.dtype, q.device)
+    topk = _norm_topk(topk, levels)
     per_level = not isinstance(topk, int)
     nbytes = (llsa_workspace_bytes_lk if per_level else llsa_workspace_bytes)(
         B, H, N, d, 16, topk, levels, dt)
@@ -254,22 +281,53 @@ def forward(q, k, v, topk, levels: int, flags: int = 0, workspace=None, stream=N
         raise LlsaError(-2, "llsa_workspace_bytes")
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    elif (not workspace.is_cuda or workspace.device != q.device or workspace.dtype != torch.uint8
+          or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % q.device)
     out = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     (llsa_forward_lk if per_level else llsa_forward)(
         q, k, v, out, lse, B, H, N, d, 16, topk, levels, dt, flags, workspace,
         workspace.numel(), stream)
+    workspace._llsa_forward = {"shape": (B, H, N, d), "dtype": q.dtype, "topk": topk,
+                               "levels": int(levels), "flags": int(flags)}
     return out, lse, workspace
 
 
-def backward(q, k, v, out, lse, dout, topk, levels: int, workspace, flags: int = 0,
+def backward(q, k, v, out, lse, dout, topk=None, levels=None, workspace=None, flags=None,
              stream=None):
-    """Returns (dq, dk, dv); `workspace` must come from `forward`."""
+    """Returns (dq, dk, dv).  `workspace` must come from `forward` on the same
+    q, k, v; topk, levels and flags default to the forward's and, if given,
+    must equal them (a mismatch raises ValueError: the index lists in the
+    workspace are laid out for the forward's values)."""
     import torch
+    if workspace is None:
+        raise ValueError("backward needs the workspace returned by forward")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
     dt = _dtype_code(q)
-    if not dout.is_contiguous() or dout.shape != q.shape or dout.dtype != q.dtype:
-        raise ValueError("dout must be contiguous with the shape and dtype of q")
+    _check_tensors((("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)), q.shape,
+                   q.dtype, q.device)
+    _check_tensors((("lse", lse),), (B, H, N), torch.float32, q.device)
+    rec = getattr(workspace, "_llsa_forward", None)
+    given = {"topk": None if topk is None else _norm_topk(topk, levels), "levels": levels,
+             "flags": flags}
+    if rec is not None:
+        if rec["shape"] != (B, H, N, d) or rec["dtype"] != q.dtype:
+            raise ValueError("workspace holds a forward of shape %s %s, not %s %s"
+                             % (rec["shape"], rec["dtype"], (B, H, N, d), q.dtype))
+        for key, val in given.items():
+            if val is not None and val != rec[key]:
+                raise ValueError("%s=%r differs from the forward's %r" % (key, val, rec[key]))
+        topk, levels, flags = rec["topk"], rec["levels"], rec["flags"]
+    elif topk is None or levels is None:
+        raise ValueError("topk and levels are needed for a workspace that forward() did not "
+                         "return")
+    flags = 0 if flags is None else flags
+    if (not workspace.is_cuda or workspace.device != q.device or workspace.dtype != torch.uint8
+            or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % q.device)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     (llsa_backward if isinstance(topk, int) else llsa_backward_lk)(
         q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, 16, topk, levels, dt, flags,

@@ -203,6 +203,16 @@ __device__ __forceinline__ void lds_fence()
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// An index read from the workspace (a block number, a list position or a
+// slot), forced into [0, n) before it forms an address.  The backward and the
+// single stages trust the workspace to hold what the forward of the same
+// shape, top-k and flags wrote there; with any other contents the results
+// are wrong, but every access stays inside the buffers the call was given.
+__device__ __forceinline__ int clampi(int x, int n)
+{
+    return (int)min((unsigned)x, (unsigned)(n - 1));
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on
 // XCD b % 8).  Renumber them so that consecutive logical workgroups -- which
 // work on neighbouring query or key blocks and gather the same candidate

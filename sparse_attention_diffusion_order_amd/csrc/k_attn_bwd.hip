@@ -173,7 +173,7 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
         bd[u] = ld8(dout + rowq + 32 * u + 8 * gq);
     }
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
-    const int myj = lane < g.K ? sel[lane] : 0;
+    const int myj = lane < g.K ? clampi(sel[lane], g.n[1]) : 0;
     float Dq;
     {
         float s = 0.f;
@@ -198,7 +198,8 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
         for (int s0 = 0; s0 < Kl; s0 += 64)
             if (s0 + lane < Kl)
                 ent[g.eoff[l] + s0 + lane] =
-                    (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * Kl + s0 + lane]);
+                    (int)(w.prow[l - 1] + (long)gh * g.n[l] +
+                          clampi(w.idx[l - 1][a * Kl + s0 + lane], g.n[l]));
     }
     lds_fence();
 
@@ -257,7 +258,10 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
         operand_rows<D, TS::ROW_T>(lb, kb, lane);
         operand_rows<D, TS::ROW_A>(lva, va, lane);
         operand_rows<D, TS::ROW_A>(lvb, vb, lane);
-        if (p < NF && g.K > 1) {
+        // full pairs of fine tiles run unmasked; with an odd top-k the last
+        // fine "pair" holds the lone last tile twice (the clamped load), so
+        // it takes the masked path with its second tile empty
+        if (p < NF - (g.K & 1)) {
             dq_pair<false, D>(acc, bq, bd, nl2, Dq, ka, kb, va, vb, la, lb, BS, BS, c, lane);
         } else {
             const int e0 = p < NF ? 0 : BS * 2 * (p - NF);
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
 #pragma unroll
             for (int u = 0; u < NI; ++u) bk[u] = bv[u] = bf16x8{};
             if (ev) {
-                long off = ((long)gh * g.n[l] + sel[e0 + nq]) * D;
+                long off = ((long)gh * g.n[l] + clampi(sel[e0 + nq], g.n[l])) * D;
 #pragma unroll
                 for (int u = 0; u < NI; ++u) {
                     bk[u] = ld8f(w.kbar[l - 1] + off + 32 * u + 8 * gq);
@@ -468,7 +472,8 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
     const int span = 1 << (4 * (l - 2));  // level-2 blocks per level-l block
     const float* part = w.part[l - 1] + (long)gh * g.n[2] * Kl * 2 * D + dim;
     float sk[NC] = {}, sv[NC] = {};
-    const int beg = uniform(rp[j]), end = uniform(rp[j + 1]);
+    const int tot = g.n[l] * Kl;  // list entries of the head
+    const int beg = uniform(clampi(rp[j], tot + 1)), end = uniform(max(beg, clampi(rp[j + 1], tot + 1)));
     // list entries in batches of 64: lane e holds entry beg + e (row offset
     // into the partials).  The batch's (entry, level-2 block) rows are summed
     // in order, eight loads in flight at a time.
@@ -476,7 +481,7 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
     for (int e0 = beg; e0 < end; e0 += 64) {
         const int ne = min(64, end - e0);
         int off = 0;  // in rows of 2*D floats
-        if (lane < ne) off = cl[e0 + lane] * span * Kl + sl[e0 + lane];
+        if (lane < ne) off = clampi(cl[e0 + lane], g.n[l]) * span * Kl + clampi(sl[e0 + lane], Kl);
         const int nrow = ne * span;
         for (int q0 = 0; q0 < nrow; q0 += 8) {
             float vk[8][NC], vv[8][NC];
@@ -556,7 +561,8 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     const int* rp = w.rowptr[0] + (long)gh * (g.n[1] + 1);
     const int* list = w.col[0] + (long)gh * g.n[1] * g.K;
     const unsigned char* slots = w.slot[0] + (long)gh * g.n[1] * g.K;
-    const int beg = uniform(rp[j]), end = uniform(rp[j + 1]);
+    const int tot = g.n[1] * g.K;  // list entries of the head
+    const int beg = uniform(clampi(rp[j], tot + 1)), end = uniform(max(beg, clampi(rp[j + 1], tot + 1)));
     const int rr = (lane & 15) >> 2, xx = lane & 3;
     f32x4 accK[ND] = {}, accV[ND] = {};
     // live == false (the padding step of an odd-length chunk): the MFMAs run
@@ -642,8 +648,8 @@ __global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict
     QBlock<D> A, B;
     for (int cb = beg; cb < end; cb += 64) {
         const int n = min(64, end - cb);
-        myi = lane < n ? list[cb + lane] : 0;
-        mys = lane < n ? (int)slots[cb + lane] : 0;
+        myi = lane < n ? clampi(list[cb + lane], g.n[1]) : 0;
+        mys = lane < n ? clampi(slots[cb + lane], g.K) : 0;
         fetch(A, 0);
         for (int t = 0; t < n; t += 2) {
             fetch(B, min(t + 1, n - 1));
@@ -710,7 +716,7 @@ __device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const 
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + t / BS) * g.K;
     for (int s = 0; s < g.K; ++s)
         for (int r = 0; r < BS; ++r) {
-            long row = ((long)gh * g.N + (long)sel[s] * BS + r) * D;
+            long row = ((long)gh * g.N + (long)clampi(sel[s], g.n[1]) * BS + r) * D;
             f(k + row, v + row, 0.f);
         }
     // enriching levels l0..L; a level-lv token's logit gets lb2 * lv * ln 2
@@ -719,7 +725,7 @@ __device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const 
         const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.Kl[lv];
         const float bias = g.lb2 * (float)lv * LN2;
         for (int s = 0; s < g.Kl[lv]; ++s) {
-            long row = ((long)gh * g.n[lv] + sl[s]) * D;
+            long row = ((long)gh * g.n[lv] + clampi(sl[s], g.n[lv])) * D;
             f(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, bias);
         }
     }
@@ -783,8 +789,10 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
     const float bias = g.lb2 * (float)l * LN2;  // size bias of a level-l token
 #pragma unroll
     for (int c = 0; c < NC; ++c) sk[c] = sv[c] = 0.f;
-    for (int e = rp[j]; e < rp[j + 1]; ++e) {
-        const long a = cl[e];
+    const int tot = g.n[l] * g.Kl[l];
+    const int beg = clampi(rp[j], tot + 1), end = max(beg, clampi(rp[j + 1], tot + 1));
+    for (int e = beg; e < end; ++e) {
+        const long a = clampi(cl[e], g.n[l]);
         for (long t = a * span; t < (a + 1) * span; ++t) {
             const long tg = (long)gh * g.N + t;
             float qc[NC], dc[NC];
@@ -831,9 +839,11 @@ __global__ __launch_bounds__(256) void dkdv_f32(const float* __restrict__ q,
     for (int c = 0; c < NC; ++c) ak[c] = av[c] = 0.f;
     const int* rp = w.rowptr[0] + (long)gh * (g.n[1] + 1);
     const int* cl = w.col[0] + (long)gh * g.n[1] * g.K;
-    for (int e = rp[j]; e < rp[j + 1]; ++e)
+    const int tot = g.n[1] * g.K;
+    const int beg = clampi(rp[j], tot + 1), end = max(beg, clampi(rp[j + 1], tot + 1));
+    for (int e = beg; e < end; ++e)
         for (int r = 0; r < BS; ++r) {
-            const long tg = (long)gh * g.N + (long)cl[e] * BS + r;
+            const long tg = (long)gh * g.N + (long)clampi(cl[e], g.n[1]) * BS + r;
             float qc[NC], dc[NC];
             lane_channels<D>(qc, q + tg * D, lane);
             lane_channels<D>(dc, dout + tg * D, lane);

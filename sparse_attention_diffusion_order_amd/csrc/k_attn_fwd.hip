@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
     for (int u = 0; u < NI; ++u) bq[u] = ld_bf16x8(q + qbase + nq * D + 32 * u + 8 * gq);
     // the query block's K fine blocks, one per lane (K <= 64)
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
-    const int myj = lane < g.K ? sel[lane] : 0;
+    const int myj = lane < g.K ? clampi(sel[lane], g.n[1]) : 0;
     // pooled entries e = eoff[l] + slot of the enriching levels l0..L: their
     // rows in the bf16 pooled arrays
     const int E = g.n_pooled();
@@ -180,7 +180,8 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
         for (int s0 = 0; s0 < Kl; s0 += 64)
             if (s0 + lane < Kl)
                 ent[g.eoff[l] + s0 + lane] =
-                    (int)(w.prow[l - 1] + (long)gh * g.n[l] + w.idx[l - 1][a * Kl + s0 + lane]);
+                    (int)(w.prow[l - 1] + (long)gh * g.n[l] +
+                          clampi(w.idx[l - 1][a * Kl + s0 + lane], g.n[l]));
     }
     lds_fence();
 
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
     }
     // the 4 pick lists, lane 16 b + s holds pick s of block i0 + b
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i0) * K;
-    const int my = (nq < K) ? sel[gq * K + nq] : INT_MAX;
+    const int my = (nq < K) ? clampi(sel[gq * K + nq], g.n[1]) : INT_MAX;
     L.arr[lane] = my;
     lds_fence();
     // union: first occurrences in lane order, their rank among distinct picks,
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
                     const int l = tile_level(t), Kl = g.Kl[l];
                     const long a = (long)gh * g.n[l] + (i0 >> (4 * (l - 1)));
                     row = (int)(w.prow[l - 1] + (long)gh * g.n[l] +
-                                w.idx[l - 1][a * Kl + min(lane, Kl - 1)]);
+                                clampi(w.idx[l - 1][a * Kl + min(lane, Kl - 1)], g.n[l]));
                 }
                 L.pent[t * BS + lane] = row;
             }
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + t / BS) * g.K;
     for (int s = 0; s < g.K; ++s)
         for (int r = 0; r < BS; ++r) {
-            const long row = ((long)gh * g.N + (long)sel[s] * BS + r) * D;
+            const long row = ((long)gh * g.N + (long)clampi(sel[s], g.n[1]) * BS + r) * D;
             visit(k + row, v + row, 0.f);
         }
     for (int lv = g.l0; lv <= g.L; ++lv) {  // pooled tokens of the enriching levels
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
         const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.Kl[lv];
         const float bias = g.lb2 * (float)lv * LN2;
         for (int s = 0; s < g.Kl[lv]; ++s) {
-            const long row = ((long)gh * g.n[lv] + sl[s]) * D;
+            const long row = ((long)gh * g.n[lv] + clampi(sl[s], g.n[lv])) * D;
             visit(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, bias);
         }
     }

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
     for (int c = threadIdx.x; c < M; c += blockDim.x) {
         if (parent) {
             const int* pr = parent + ((long)gh * (n_l / BS) + grp) * (M / BS);  // parent row: M/16 picks
-            cand[c] = BS * pr[c / BS] + (c % BS);
+            cand[c] = BS * clampi(pr[c / BS], n_l / BS) + (c % BS);
         } else {
             cand[c] = c;
         }
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
     for (int c = threadIdx.x; c < M; c += blockDim.x) {
         if (parent) {
             const int* pr = parent + ((long)gh * (n_l / BS) + grp) * (M / BS);  // parent row: M/16 picks
-            cand[c] = BS * pr[c / BS] + (c % BS);
+            cand[c] = BS * clampi(pr[c / BS], n_l / BS) + (c % BS);
         } else {
             cand[c] = c;
         }

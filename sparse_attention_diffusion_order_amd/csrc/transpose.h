@@ -11,9 +11,10 @@ namespace {
 struct Cands {
     const int* plist;  // parent level's list of block p (nullptr at the coarsest level)
     int n;             // number of candidates
+    int np;            // blocks of the parent level (bound of a list entry)
     __device__ __forceinline__ int row(int c) const
     {
-        return plist ? BS * plist[c >> 4] + (c & 15) : c;
+        return plist ? BS * clampi(plist[c >> 4], np) + (c & 15) : c;
     }
 };
 
@@ -25,8 +26,11 @@ __device__ __forceinline__ Cands make_cands(const Geo& g, const Ws& w, int l, in
         cs.n = g.n[l];
     } else {
         const int* rp = w.rowptr[l] + (long)gh * (g.n[l + 1] + 1);
-        cs.plist = w.col[l] + (long)gh * g.n[l + 1] * g.Kl[l + 1] + rp[grp];
-        cs.n = BS * (rp[grp + 1] - rp[grp]);
+        const int tot = g.n[l + 1] * g.Kl[l + 1];
+        const int b = clampi(rp[grp], tot + 1), e = max(b, clampi(rp[grp + 1], tot + 1));
+        cs.plist = w.col[l] + (long)gh * tot + b;
+        cs.n = BS * (e - b);
+        cs.np = g.n[l + 1];
     }
     return cs;
 }
@@ -139,6 +143,7 @@ __device__ __forceinline__ void transpose_block(const Geo& g, const Ws& w, int l
         }
         cs.plist = pickers;
         cs.n = BS * total;
+        cs.np = g.n[g.L];
     } else {
         cs = make_cands(g, w, l, gh, grp);
     }
@@ -221,7 +226,7 @@ __device__ __forceinline__ void transpose_block(const Geo& g, const Ws& w, int l
             // pos < n K whenever the counts match the index lists (both come
             // from the same selection pass); the test only keeps a workspace
             // that was not filled by one from being written out of bounds
-            if (pos < n * K) {
+            if ((unsigned)pos < (unsigned)(n * K)) {
                 col[pos] = i;
                 slots[pos] = (unsigned char)(first + __popc(m & ((1u << b) - 1u)));
             }

@@ -11,6 +11,9 @@ the method's contract:
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 import oracle
@@ -98,6 +101,55 @@ def oracle_inputs(w, inp):
     return z
 
 
+def host_workers(limit: int = 16) -> int:
+    """CPU threads for oracle work: the cores this process may use, at most
+    `limit` (a GPU machine gives one GPU's process a share of 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(limit, n))
+
+
+def per_head(fn, G: int, workers: int = 0):
+    """[fn(h) for h in range(G)], run in a thread pool.  The oracle's C
+    routines release the GIL (ctypes), so heads run in parallel on the host
+    cores; each head's arithmetic is the oracle's own, unchanged."""
+    workers = workers or host_workers()
+    if workers == 1 or G == 1:
+        return [fn(h) for h in range(G)]
+    with ThreadPoolExecutor(max_workers=min(workers, G)) as ex:
+        return list(ex.map(fn, range(G)))
+
+
+def oracle_values(w, z, kp, vp, idx, flags=0, backward=True):
+    """The oracle's out, lse (and dq, dk, dv) for every head and token, on the
+    given index lists, one head per host thread."""
+    scale = 1.0 / np.sqrt(w.d)
+
+    def head(h):
+        sl = slice(h, h + 1)
+        q, k, v = (z[n][sl] for n in ("q", "k", "v"))
+        kph, vph, ih = [x[sl] for x in kp], [x[sl] for x in vp], [x[sl] for x in idx]
+        o, lse = oracle.forward(q, k, v, kph, vph, ih, BS, scale, flags)
+        if not backward:
+            return o, lse
+        return (o, lse) + oracle.backward(q, k, v, kph, vph, ih, o, lse, z["do"][sl], BS,
+                                          scale, flags)
+
+    parts = per_head(head, w.G)
+    return [np.concatenate([p_[i] for p_ in parts]) for i in range(len(parts[0]))]
+
+
+def grad_tol(ref, base: float) -> float:
+    """Max-abs bound of a bf16-path gradient: the stated 5e-2 (for unit-scale
+    inputs), or 2^-6 of the tensor's largest magnitude when that is larger --
+    eight bf16 roundings (2^-9 each) of the largest value -- since every
+    rounding on the bf16 path (the P and dS operands, lse, the stored result)
+    is relative to the values it rounds."""
+    return max(base, float(np.abs(ref).max()) * 2.0 ** -6)
+
+
 def check_selection(w, gpu, orc_pyr, exact: bool):
     """Level-by-level comparison; returns the number of rows that differ."""
     qp, kp = orc_pyr
@@ -105,7 +157,16 @@ def check_selection(w, gpu, orc_pyr, exact: bool):
     diffs = 0
     for l in range(w.levels, 0, -1):
         parent = None if l == w.levels else gpu["idx"][l]
-        want, gap = oracle.select_level(qp[l - 1], kp[l - 1], parent, level_k(w, l), BS, scale)
+
+        def head(h, l=l, parent=parent):
+            sl = slice(h, h + 1)
+            return oracle.select_level(qp[l - 1][sl], kp[l - 1][sl],
+                                       None if parent is None else parent[sl], level_k(w, l), BS,
+                                       scale)
+
+        parts = per_head(head, w.G)
+        want = np.concatenate([p_[0] for p_ in parts])
+        gap = np.concatenate([p_[1] for p_ in parts])
         got = gpu["idx"][l - 1]
         bad = np.any(got != want, axis=2)
         if exact:

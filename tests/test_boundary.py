@@ -166,3 +166,23 @@ def test_layout_consistent(B, H, N, K, Lv):
     for (a, sa), (b, _) in zip(spans, spans[1:]):
         assert a % 256 == 0 and a + sa <= b  # aligned and disjoint
     assert spans[-1][0] + spans[-1][1] <= lay["total"]
+
+
+def test_binding_refuses_host_tensors_and_mismatched_backward():
+    """The Python helpers check device, shape, dtype and contiguity before any
+    library call (a host tensor's address must never reach a kernel), and the
+    backward refuses top-k, levels or flags other than the forward's."""
+    import torch
+    q = torch.zeros(1, 2, 256, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        L.forward(q, q, q, 4, 1)
+    with pytest.raises(ValueError):
+        L.llsa_zorder(q, q, 2, 16, 128)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    ws._llsa_forward = {"shape": (1, 2, 256, 64), "dtype": torch.bfloat16, "topk": 4,
+                        "levels": 1, "flags": 0}
+    lse = torch.zeros(1, 2, 256)
+    with pytest.raises(ValueError):  # host tensors
+        L.backward(q, q, q, q, lse, q, workspace=ws)
+    with pytest.raises(ValueError):  # no workspace
+        L.backward(q, q, q, q, lse, q, 4, 1)
