@@ -220,33 +220,100 @@ def summarize_counters(db, out, cmd, workload):
         f.write("\n")
 
 
-def cpu_baseline(w, inp, min_s=10.0):
-    """The oracle (plain fp64 C, one thread) on a bounded sample of the same
-    workload: whole heads (pool, selection, forward, backward), one after the
-    other, until at least min_s seconds of CPU work have run."""
-    import oracle
-    G, N, d = w.G, w.N, w.d
-    head = lambda a, h: a.reshape(G, N, d)[h:h + 1]
-    done, dt = 0, 0.0
-    while done < G and dt < min_s:
-        q, k, v = (oracle.grid_order(head(inp[n + "64"], done), w.frames, w.rows, w.side)
-                   for n in ("q", "k", "v"))
-        do = head(inp["do64"], done)
-        t0 = time.perf_counter()
-        oracle.run(q, k, v, 16, w.levels, w.topk, dout=do)
-        dt += time.perf_counter() - t0
-        done += 1
-    f = flops(w)["fwdbwd"] * done / G
-    model = ""
+def _host_threads(limit=16):
+    """host threads for the oracle: the cores this process may use, at most
+    `limit` (the share of one GPU's process on the GPU machine)"""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(limit, n))
+
+
+def _cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
-            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+            return next((ln.split(":", 1)[1].strip() for ln in fh
+                         if ln.startswith("model name")), "")
     except OSError:
-        pass
-    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 3), "cpu_model": model, "host_cpus": os.cpu_count(),
-            "sample": "heads 0..%d of %d (%d/%d of the workload): pool, selection, forward "
-                      "and backward, fp64 C oracle, single thread" % (done - 1, G, done, G)}
+        return ""
+
+
+def oracle_workload(w, inp, threads, heads=None):
+    """The oracle (plain fp64 C, unchanged) over whole heads of the workload:
+    grid order, pool and selection per head, then the forward in query-block
+    chunks, then the backward per head, each phase on a pool of `threads`
+    host threads (the C routines release the GIL).  Returns seconds per
+    phase and the number of heads."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    G, N, d = w.G, w.N, w.d
+    heads = list(range(G)) if heads is None else list(heads)
+    scale = 1.0 / np.sqrt(d)
+    st = {}
+
+    def prep(h):
+        x = {n: oracle.grid_order(inp[n + "64"].reshape(G, N, d)[h:h + 1], w.frames, w.rows,
+                                  w.side) for n in ("q", "k", "v")}
+        x["do"] = inp["do64"].reshape(G, N, d)[h:h + 1]
+        return x
+
+    ins = {h: prep(h) for h in heads}  # input staging: not timed
+    n1 = N // 16
+    chunks = max(1, -(-threads // len(heads)))
+    bounds = [(c * n1 // chunks, (c + 1) * n1 // chunks) for c in range(chunks)]
+    t = {}
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        def sel(h):
+            x = ins[h]
+            qp, kp, vp = (oracle.pool(x[n], 16, w.levels) for n in ("q", "k", "v"))
+            idx, _ = oracle.select(qp, kp, w.topk, 16, scale)
+            st[h] = dict(kp=kp, vp=vp, idx=idx, out=np.zeros((1, N, d)), lse=np.zeros((1, N)))
+
+        def fwd(task):
+            h, (a, b) = task
+            x, s_ = ins[h], st[h]
+            oracle.forward(x["q"], x["k"], x["v"], s_["kp"], s_["vp"], s_["idx"], 16, scale,
+                           qblocks=np.arange(a, b), out=s_["out"], lse=s_["lse"])
+
+        def bwd(h):
+            x, s_ = ins[h], st[h]
+            oracle.backward(x["q"], x["k"], x["v"], s_["kp"], s_["vp"], s_["idx"], s_["out"],
+                            s_["lse"], x["do"], 16, scale)
+
+        t0 = time.perf_counter()
+        list(ex.map(sel, heads))
+        t1 = time.perf_counter()
+        list(ex.map(fwd, [(h, ab) for h in heads for ab in bounds]))
+        t2 = time.perf_counter()
+        list(ex.map(bwd, heads))
+        t3 = time.perf_counter()
+    t = {"select_s": t1 - t0, "fwd_s": t2 - t1, "bwd_s": t3 - t2, "total_s": t3 - t0}
+    return t, len(heads), chunks
+
+
+def cpu_baseline(w, inp):
+    """The oracle timed on the host's cores (a baseline, not the target):
+    the whole workload (every head: pool, selection, forward, backward) on
+    all threads this process may use (at most 16), and one head on a single
+    thread.  TFLOP/s by the same FLOP convention as the GPU figures."""
+    threads = _host_threads()
+    f = flops(w)
+    tm, nh, chunks = oracle_workload(w, inp, threads)
+    t1, _, _ = oracle_workload(w, inp, 1, heads=[0])
+    return {"value": round(f["fwdbwd"] / tm["total_s"] / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "seconds": round(tm["total_s"], 3),
+            "phases_s": {k_: round(v_, 3) for k_, v_ in tm.items() if k_ != "total_s"},
+            "fwd_ms": round((tm["select_s"] + tm["fwd_s"]) * 1e3, 1),
+            "fwdbwd_ms": round(tm["total_s"] * 1e3, 1),
+            "one_thread": {"value": round(f["fwdbwd"] / w.G / t1["total_s"] / 1e12, 6),
+                           "seconds": round(t1["total_s"], 3), "sample": "head 0"},
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": "the whole workload (%d heads): per head pool + selection, then the "
+                      "forward in %d query-block chunks per head, then the backward one head "
+                      "per thread (%d busy), on a pool of %d threads; fp64 C oracle"
+                      % (nh, chunks, min(nh, threads), threads)}
 
 
 def dense_reference(w, q, k, v, do, reps=3):
@@ -308,6 +375,9 @@ def main():
                          "WRITE_SIZE databases to --out and exit (no GPU)")
     ap.add_argument("--summarize-counters", metavar="DB",
                     help="per-kernel averages of one rocprofv3 --pmc pass")
+    ap.add_argument("--oracle-only", action="store_true",
+                    help="time only the CPU oracle on the workload (all threads and one "
+                         "thread on one head) and print its JSON line; no GPU")
     ap.add_argument("--out")
     ap.add_argument("--cmd", default="", help="the profiling command, recorded in the summary")
     ap.add_argument("--bench-json", help="bench output of the profiled run (trace summary)")
@@ -321,6 +391,16 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.out, args.cmd,
                       args.workload)
+        return
+    if args.oracle_only:
+        w = synth.WORKLOADS[args.workload]
+        print("[bench] workload %s: generating inputs" % w.name, file=sys.stderr, flush=True)
+        inp = synth.make_inputs(w)
+        print("[bench] CPU oracle", file=sys.stderr, flush=True)
+        rec = {"workload": w.name, "gflop": {k_: round(v_ / 1e9, 3)
+                                             for k_, v_ in flops(w).items() if k_ != "n_kv"}}
+        rec.update(cpu_baseline(w, inp))
+        print(json.dumps(rec), flush=True)
         return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the hot path shards over heads "
@@ -457,7 +537,14 @@ def main():
     # roofline of the longest single-kernel stage (attention fwd, dq or dkdv)
     peak_mfma = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     abytes = algo_bytes(w)
-    kflops = {"attn_fwd": f["attn_fwd"], "dq": 2.0 * f["attn_fwd"], "dkdv": 2.0 * f["attn_fwd"]}
+    # FLOPs per kernel: the backward's five products (S recomputed, dP, dQ,
+    # dK, dV; 0.5 x the forward's FLOPs each) counted once, S and dP split
+    # between the two kernels that both compute them: dq 1.0 x, dkdv 1.5 x
+    # (sum 2.5 x).  kflops_exec: what each kernel executes, recomputation
+    # included (dq: S, dP, dQ = 1.5 x; dkdv: S, dP, dK, dV = 2.0 x).
+    kflops = {"attn_fwd": f["attn_fwd"], "dq": 1.0 * f["attn_fwd"], "dkdv": 1.5 * f["attn_fwd"]}
+    kflops_exec = {"attn_fwd": f["attn_fwd"], "dq": 1.5 * f["attn_fwd"],
+                   "dkdv": 2.0 * f["attn_fwd"]}
     kname = max(("attn_fwd", "dq", "dkdv"), key=lambda s: stage_ms[s])
     kms = stage_ms[kname]
     achieved = abytes[kname] / (kms * 1e-3) / 1e9
@@ -467,7 +554,8 @@ def main():
                 "traffic": traffic,
                 "algo_bytes_per_launch": abytes[kname], "avg_launch_ms": round(kms, 5),
                 "mfma_tflops": round(kflops[kname] / (kms * 1e-3) / 1e12, 2),
-                "mfma_frac": round(kflops[kname] / (kms * 1e-3) / 1e12 / peak_mfma, 4)}
+                "mfma_frac": round(kflops[kname] / (kms * 1e-3) / 1e12 / peak_mfma, 4),
+                "mfma_tflops_incl_recompute": round(kflops_exec[kname] / (kms * 1e-3) / 1e12, 2)}
 
     res = {
         "metric": metric(w), "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -496,6 +584,7 @@ def main():
         # min(MFMA peak, intensity x HBM peak) with intensity = FLOP / unique bytes
         "attained_vs_roofline": {
             k_: {"tflops": round(kflops[k_] / (stage_ms[k_] * 1e-3) / 1e12, 2),
+                 "tflops_incl_recompute": round(kflops_exec[k_] / (stage_ms[k_] * 1e-3) / 1e12, 2),
                  "roof_tflops": round(min(peak_mfma, kflops[k_] / abytes[k_] * HBM_PEAK_GBS / 1e3), 1),
                  "frac": round(kflops[k_] / (stage_ms[k_] * 1e-3) / 1e12 /
                                min(peak_mfma, kflops[k_] / abytes[k_] * HBM_PEAK_GBS / 1e3), 4)}
