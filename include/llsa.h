@@ -26,8 +26,13 @@
  *   caller; the library never allocates, frees or keeps them.
  *   stream: a hipStream_t (NULL = the default stream).  Calls only enqueue
  *   work on that stream and return; nothing synchronises the host.
- *   The library holds no mutable global state: concurrent calls with
- *   distinct workspaces are safe.
+ *   Apart from llsa_forward_noalloc's static scratch (see there), the library
+ *   holds no mutable global state: concurrent calls with distinct workspaces
+ *   are safe.
+ *   A workspace is trusted to hold what the forward of the same shape, dtype,
+ *   top-k and flags left there: with other contents the results are wrong,
+ *   but every index read from it is clamped to its range before it forms an
+ *   address, so no access leaves the buffers the call was given.
  *   All argument validation happens before any HIP call, so every error code
  *   except LLSA_ERR_HIP can be observed without a GPU.
  */
@@ -68,6 +73,8 @@ extern "C" {
 #define LLSA_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than
                                      llsa_workspace_bytes() */
 #define LLSA_ERR_HIP (-5)         /* a HIP launch or runtime call failed */
+#define LLSA_ERR_SCRATCH (-6)     /* llsa_forward_noalloc: the shape needs more
+                                     than LLSA_NOALLOC_SCRATCH_BYTES */
 
 #define LLSA_MAX_LEVELS 6
 
@@ -204,6 +211,28 @@ int llsa_backward_part(int part, const void* q, const void* k, const void* v,
                        void* dk, void* dv, int B, int H, int N, int d, int block_size,
                        int topk, int levels, int dtype, unsigned flags, void* workspace,
                        size_t ws_bytes, void* stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, results and errors are llsa_forward's (outputs
+ * identical bit for bit), without the workspace: the pyramid, index lists and
+ * pick counters live in a static scratch array of LLSA_NOALLOC_SCRATCH_BYTES
+ * in each GPU's memory, reserved when the library is loaded on that GPU and
+ * held until the process ends.  The call itself allocates nothing.
+ *   - Shapes whose forward state exceeds the array are refused with
+ *     LLSA_ERR_SCRATCH before any launch (at d = 64: up to about 2^17 tokens
+ *     times 6 heads at 2 levels, e.g. 256x256 with 6 heads, fits).
+ *   - Every call on one GPU uses that GPU's one array, which keeps the last
+ *     call's contents (each call rewrites what it reads).  Calls that overlap
+ *     in time on one GPU -- other streams, other host threads, other
+ *     processes' streams do not share it -- race and give wrong results;
+ *     calls ordered on one stream are safe.
+ *   - There is no matching backward: the next call overwrites the index
+ *     lists.  Training keeps using llsa_forward / llsa_backward. */
+#define LLSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int llsa_forward_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int H, int N, int d, int block_size, int topk, int levels,
+                         int dtype, unsigned flags, void* stream);
 
 /* Static description of an error code (never NULL). */
 const char* llsa_strerror(int code);

@@ -22,7 +22,7 @@ __all__ = [
     "llsa_forward",
     "llsa_backward", "llsa_forward_part", "llsa_backward_part", "llsa_strerror",
     "llsa_workspace_bytes_lk", "llsa_workspace_layout_lk", "llsa_forward_lk", "llsa_backward_lk",
-    "forward", "backward", "zorder", "grid_order",
+    "llsa_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "forward", "backward", "zorder", "grid_order",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +36,7 @@ SIZE_BIAS = 4
 PART_POOL, PART_SELECT, PART_ATTN = 0, 1, 2
 PART_TRANSPOSE, PART_DQ, PART_DKDV, PART_ENRICH = 3, 4, 5, 6
 MAX_LEVELS = 6
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LLSA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -95,6 +96,8 @@ def load():
     lib.llsa_forward_lk.restype = I
     lib.llsa_backward_lk.argtypes = [P] * 9 + lk + [U, P, S, P]
     lib.llsa_backward_lk.restype = I
+    lib.llsa_forward_noalloc.argtypes = [P] * 5 + shape + [U, P]
+    lib.llsa_forward_noalloc.restype = I
     lib.llsa_strerror.argtypes = [I]
     lib.llsa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -212,6 +215,13 @@ def llsa_backward(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, block_size, t
                                 _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, block_size, topk,
                                 levels, dtype, flags, _ptr(workspace), ws_bytes,
                                 _stream(stream)), "llsa_backward")
+
+
+def llsa_forward_noalloc(q, k, v, out, lse, B, H, N, d, block_size, topk, levels, dtype, flags,
+                         stream=None):
+    _check(load().llsa_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N,
+                                       d, block_size, topk, levels, dtype, flags,
+                                       _stream(stream)), "llsa_forward_noalloc")
 
 
 def llsa_forward_part(part, q, k, v, out, lse, B, H, N, d, block_size, topk, levels, dtype,

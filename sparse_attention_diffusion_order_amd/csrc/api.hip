@@ -4,6 +4,8 @@
 // reported identically on a host without a GPU.
 #include <string.h>
 
+#include <atomic>
+
 #include "common.h"
 
 using namespace llsa;
@@ -50,14 +52,17 @@ struct Layout {
     size_t slot[MAX_L];
     size_t part[MAX_L];
     size_t dbar[MAX_L];
+    bool fwd_only;  // only the forward's parts (no backward state)
 };
 
 // Workspace: pyramid (float32), index lists, key->query CSR lists, delta,
 // enrichment gradient partials and sums.  Sizes are O(B*H*N*d): no part of
-// it grows with the square of the block count.
-void make_layout(int G, int N, int D, const int* ks, int L, Layout* lay)
+// it grows with the square of the block count.  fwd_only: the parts the
+// forward uses (pyramid, index lists, bf16 pooled copies, pick counts).
+void make_layout(int G, int N, int D, const int* ks, int L, Layout* lay, bool fwd_only = false)
 {
     memset(lay, 0, sizeof(*lay));
+    lay->fwd_only = fwd_only;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -74,7 +79,7 @@ void make_layout(int G, int N, int D, const int* ks, int L, Layout* lay)
         lay->pub.vbar[l - 1] = take(pyr);
         lay->pub.idx[l - 1] = take((size_t)G * n[l] * ks[l - 1] * sizeof(int));
     }
-    for (int l = 1; l <= L; ++l) {
+    for (int l = 1; l <= L && !fwd_only; ++l) {
         lay->pub.rowptr[l - 1] = take((size_t)G * (n[l] + 1) * sizeof(int));
         lay->pub.col[l - 1] = take((size_t)G * n[l] * ks[l - 1] * sizeof(int));
     }
@@ -82,13 +87,17 @@ void make_layout(int G, int N, int D, const int* ks, int L, Layout* lay)
     for (int l = 1; l <= L; ++l) prows += (size_t)G * n[l];
     lay->kb16 = take(prows * D * 2);
     lay->vb16 = take(prows * D * 2);
-    lay->pub.delta = take((size_t)G * N * sizeof(float));
-    lay->pe1 = take((size_t)G * n[1] * ks[0] * 2 * BS * sizeof(float));
-    for (int l = 1; l <= L; ++l) lay->slot[l - 1] = take((size_t)G * n[l] * ks[l - 1]);
     size_t blocks = 0;
     for (int l = 1; l <= L; ++l)
         blocks += (size_t)G * (n[l] + (n[l] + 15) / 16);
     lay->cnt = take(blocks * sizeof(int));
+    if (fwd_only) {
+        lay->pub.total = off;
+        return;
+    }
+    lay->pub.delta = take((size_t)G * N * sizeof(float));
+    lay->pe1 = take((size_t)G * n[1] * ks[0] * 2 * BS * sizeof(float));
+    for (int l = 1; l <= L; ++l) lay->slot[l - 1] = take((size_t)G * n[l] * ks[l - 1]);
     for (int l = 1; l <= L; ++l) {
         lay->dbar[l - 1] = take((size_t)G * n[l] * 2 * D * sizeof(float));
         if (l >= 2) lay->part[l - 1] = take((size_t)G * n[2] * ks[l - 1] * 2 * D * sizeof(float));
@@ -121,23 +130,29 @@ void make_geo(int B, int H, int N, int d, const int* ks, int levels, unsigned fl
     g->eoff[levels + 1] = e;
 }
 
+// Pointers into the workspace at `base` (the backward's parts stay null in a
+// forward-only layout).
 void make_ws(void* base, const Layout& lay, int L, Ws* w)
 {
     memset(w, 0, sizeof(*w));
     char* b = (char*)base;
+    const bool bwd = !lay.fwd_only;
     for (int l = 1; l <= L; ++l) {
         w->qbar[l - 1] = (float*)(b + lay.pub.qbar[l - 1]);
         w->kbar[l - 1] = (float*)(b + lay.pub.kbar[l - 1]);
         w->vbar[l - 1] = (float*)(b + lay.pub.vbar[l - 1]);
         w->idx[l - 1] = (int*)(b + lay.pub.idx[l - 1]);
+        if (!bwd) continue;
         w->rowptr[l - 1] = (int*)(b + lay.pub.rowptr[l - 1]);
         w->col[l - 1] = (int*)(b + lay.pub.col[l - 1]);
         w->slot[l - 1] = (unsigned char*)(b + lay.slot[l - 1]);
         w->dbar[l - 1] = (float*)(b + lay.dbar[l - 1]);
         if (l >= 2) w->part[l - 1] = (float*)(b + lay.part[l - 1]);
     }
-    w->delta = (float*)(b + lay.pub.delta);
-    w->pe1 = (float*)(b + lay.pe1);
+    if (bwd) {
+        w->delta = (float*)(b + lay.pub.delta);
+        w->pe1 = (float*)(b + lay.pe1);
+    }
     w->cnt_all = (int*)(b + lay.cnt);
     w->kb16 = (unsigned short*)(b + lay.kb16);
     w->vb16 = (unsigned short*)(b + lay.vb16);
@@ -150,12 +165,13 @@ struct Prep {
 };
 
 int prepare(int B, int H, int N, int d, int block_size, const int* ks, int levels, int dtype,
-            unsigned flags, void* workspace, size_t ws_bytes, void* stream, Prep* p)
+            unsigned flags, void* workspace, size_t ws_bytes, void* stream, Prep* p,
+            bool fwd_only = false)
 {
     int rc = validate(B, H, N, d, block_size, ks, levels, dtype, flags);
     if (rc) return rc;
     Layout lay;
-    make_layout(B * H, N, d, ks, levels, &lay);
+    make_layout(B * H, N, d, ks, levels, &lay, fwd_only);
     if (!workspace || ws_bytes < lay.pub.total) return LLSA_ERR_WORKSPACE;
     make_geo(B, H, N, d, ks, levels, flags, &p->geo);
     make_ws(workspace, lay, levels, &p->ws);
@@ -205,6 +221,32 @@ int run_backward_part(int part, const void* q, const void* k, const void* v, con
         return hip_rc(launch_attn_dkdv(q, k, v, lse, dout, dk, dv, dtype, p.geo, p.ws, p.st));
     default: return LLSA_ERR_UNSUPPORTED;
     }
+}
+
+// The scratch of llsa_forward_noalloc: one array in each GPU's memory,
+// reserved when the library's code object is loaded on that GPU and held
+// until the process ends.  In host code `scratch` only names the array;
+// its device address on the current GPU comes from hipGetSymbolAddress,
+// looked up once per device and kept in noalloc_base.
+static __device__ __align__(256) unsigned char scratch[LLSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> noalloc_base[MAX_DEVICES];
+
+// Device address of the current GPU's scratch (set up on the first call on
+// that GPU, with it current).
+int noalloc_scratch(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return LLSA_ERR_HIP;
+    void* ptr = noalloc_base[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return LLSA_ERR_HIP;
+        noalloc_base[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return LLSA_OK;
 }
 
 // the same top-k at every level, as an array (levels outside 1..MAX_L are
@@ -320,6 +362,32 @@ int llsa_forward(const void* q, const void* k, const void* v, void* out, float* 
                            stream);
 }
 
+int llsa_forward_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int H, int N, int d, int block_size, int topk, int levels,
+                         int dtype, unsigned flags, void* stream)
+{
+    if (!q || !k || !v || !out || !lse) return LLSA_ERR_NULL;
+    const UniformK ks(topk, levels);
+    int rc = validate(B, H, N, d, block_size, ks.ks, levels, dtype, flags);
+    if (rc) return rc;
+    Layout lay;
+    make_layout(B * H, N, d, ks.ks, levels, &lay, true);
+    if (lay.pub.total > (size_t)LLSA_NOALLOC_SCRATCH_BYTES) return LLSA_ERR_SCRATCH;
+    void* base = nullptr;
+    rc = noalloc_scratch(&base);
+    if (rc) return rc;
+    Prep p;
+    rc = prepare(B, H, N, d, block_size, ks.ks, levels, dtype, flags, base,
+                 (size_t)LLSA_NOALLOC_SCRATCH_BYTES, stream, &p, true);
+    if (rc) return rc;
+    // the pool launch zeroes the pick counters left by the previous call
+    rc = hip_rc(launch_pool(q, k, v, dtype, p.geo, p.ws, true, p.st));
+    if (rc) return rc;
+    rc = hip_rc(launch_select(p.geo, p.ws, false, p.st));
+    if (rc) return rc;
+    return run_forward_part(LLSA_PART_ATTN, q, k, v, out, lse, dtype, p);
+}
+
 int llsa_backward_part(int part, const void* q, const void* k, const void* v, const void* out,
                        const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
                        int H, int N, int d, int block_size, int topk, int levels, int dtype,
@@ -386,6 +454,9 @@ const char* llsa_strerror(int code)
                "levels<=6, at most 4096 coarsest blocks, topk<=64, B*H*N<2^31";
     case LLSA_ERR_WORKSPACE: return "workspace missing or smaller than llsa_workspace_bytes()";
     case LLSA_ERR_HIP: return "HIP launch or runtime error";
+    case LLSA_ERR_SCRATCH:
+        return "llsa_forward_noalloc: this shape's forward state exceeds the static scratch "
+               "of LLSA_NOALLOC_SCRATCH_BYTES (64 MiB); use llsa_forward with a workspace";
     default: return "unknown error code";
     }
 }

@@ -186,3 +186,17 @@ def test_binding_refuses_host_tensors_and_mismatched_backward():
         L.backward(q, q, q, q, lse, q, workspace=ws)
     with pytest.raises(ValueError):  # no workspace
         L.backward(q, q, q, q, lse, q, 4, 1)
+
+
+def test_noalloc_forward_refuses_oversized_shapes_before_any_launch():
+    """The allocation-free forward checks its arguments, then whether the
+    shape's forward state fits the static scratch, before any HIP call."""
+    lib = L.load()
+    args = (BAD, BAD, BAD, BAD, BAD)
+    # 512^2 tokens, 6 heads, 3 levels: about 120 MB of forward state
+    assert lib.llsa_forward_noalloc(*args, 1, 6, 262144, 64, 16, 16, 3, L.BF16, 0, None) == -6
+    assert lib.llsa_forward_noalloc(None, BAD, BAD, BAD, BAD, 1, 6, 4096, 64, 16, 16, 1,
+                                    L.BF16, 0, None) == -1
+    assert lib.llsa_forward_noalloc(*args, 1, 6, 4008, 64, 16, 16, 1, L.BF16, 0, None) == -2
+    assert lib.llsa_forward_noalloc(*args, 1, 6, 4096, 96, 16, 16, 1, L.BF16, 0, None) == -3
+    assert "scratch" in L.llsa_strerror(-6)
