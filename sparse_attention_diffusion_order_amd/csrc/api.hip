@@ -207,6 +207,22 @@ int run_forward_part(int part, const void* q, const void* k, const void* v, void
     }
 }
 
+// The whole forward.  The pool launch zeroes the pick counters the selection
+// adds to (one launch fewer than the selection part on its own, which zeroes
+// them itself); where the shape allows, selection and attention run in one
+// launch (same results, bit for bit, as the parts in order).
+int run_forward(const void* q, const void* k, const void* v, void* out, float* lse, int dtype,
+                const Prep& p)
+{
+    int rc = hip_rc(launch_pool(q, k, v, dtype, p.geo, p.ws, true, p.st));
+    if (rc) return rc;
+    if (select_attn_fits(p.geo, dtype))
+        return hip_rc(launch_select_attn(q, k, v, out, lse, p.geo, p.ws, p.st));
+    rc = hip_rc(launch_select(p.geo, p.ws, false, p.st));
+    if (rc) return rc;
+    return run_forward_part(LLSA_PART_ATTN, q, k, v, out, lse, dtype, p);
+}
+
 int run_backward_part(int part, const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
                       int dtype, const Prep& p)
@@ -344,13 +360,7 @@ int llsa_forward_lk(const void* q, const void* k, const void* v, void* out, floa
     int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
                      stream, &p);
     if (rc) return rc;
-    // pool zeroes the pick counters the selection adds to (one launch fewer
-    // than the selection part on its own, which zeroes them itself)
-    rc = hip_rc(launch_pool(q, k, v, dtype, p.geo, p.ws, true, p.st));
-    if (rc) return rc;
-    rc = hip_rc(launch_select(p.geo, p.ws, false, p.st));
-    if (rc) return rc;
-    return run_forward_part(LLSA_PART_ATTN, q, k, v, out, lse, dtype, p);
+    return run_forward(q, k, v, out, lse, dtype, p);
 }
 
 int llsa_forward(const void* q, const void* k, const void* v, void* out, float* lse, int B,
@@ -381,11 +391,7 @@ int llsa_forward_noalloc(const void* q, const void* k, const void* v, void* out,
                  (size_t)LLSA_NOALLOC_SCRATCH_BYTES, stream, &p, true);
     if (rc) return rc;
     // the pool launch zeroes the pick counters left by the previous call
-    rc = hip_rc(launch_pool(q, k, v, dtype, p.geo, p.ws, true, p.st));
-    if (rc) return rc;
-    rc = hip_rc(launch_select(p.geo, p.ws, false, p.st));
-    if (rc) return rc;
-    return run_forward_part(LLSA_PART_ATTN, q, k, v, out, lse, dtype, p);
+    return run_forward(q, k, v, out, lse, dtype, p);
 }
 
 int llsa_backward_part(int part, const void* q, const void* k, const void* v, const void* out,
