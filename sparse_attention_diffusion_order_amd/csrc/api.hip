@@ -209,15 +209,12 @@ int run_forward_part(int part, const void* q, const void* k, const void* v, void
 
 // The whole forward.  The pool launch zeroes the pick counters the selection
 // adds to (one launch fewer than the selection part on its own, which zeroes
-// them itself); where the shape allows, selection and attention run in one
-// launch (same results, bit for bit, as the parts in order).
+// them itself).
 int run_forward(const void* q, const void* k, const void* v, void* out, float* lse, int dtype,
                 const Prep& p)
 {
     int rc = hip_rc(launch_pool(q, k, v, dtype, p.geo, p.ws, true, p.st));
     if (rc) return rc;
-    if (select_attn_fits(p.geo, dtype))
-        return hip_rc(launch_select_attn(q, k, v, out, lse, p.geo, p.ws, p.st));
     rc = hip_rc(launch_select(p.geo, p.ws, false, p.st));
     if (rc) return rc;
     return run_forward_part(LLSA_PART_ATTN, q, k, v, out, lse, dtype, p);

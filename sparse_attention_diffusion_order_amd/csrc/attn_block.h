@@ -1,7 +1,6 @@
 // attn_block.h -- the sparse attention forward of one query block by one
-// wave (bf16, MFMA), used by the forward's one-block kernel (k_attn_fwd.hip)
-// and by the selection launch that runs the forward of the query blocks it
-// has just chosen for (k_select.hip).
+// wave (bf16, MFMA): the body of the forward's one-block kernel
+// (k_attn_fwd.hip), callable from any launch that owns a wave's LDS.
 //
 // LLSA README, usage: a drop-in for non-causal scaled-dot-product attention;
 // skill summary, "Core Technique" 2: the key/value set of a query is enriched

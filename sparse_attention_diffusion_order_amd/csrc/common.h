@@ -286,12 +286,6 @@ hipError_t launch_zorder(const void* src, void* dst, long long outer, int side, 
 hipError_t launch_pool(const void* q, const void* k, const void* v, int dtype, const Geo& g,
                        const Ws& w, bool zero_counts, hipStream_t st);
 hipError_t launch_select(const Geo& g, const Ws& w, bool zero_counts, hipStream_t st);
-// Selection of the two levels and the attention forward in one launch (two
-// levels, bf16, d = 64, top-k <= 16 at level 2 and at most 64 pooled entries
-// per query block); select_attn_fits says whether the shape qualifies.
-bool select_attn_fits(const Geo& g, int dtype);
-hipError_t launch_select_attn(const void* q, const void* k, const void* v, void* out, float* lse,
-                              const Geo& g, const Ws& w, hipStream_t st);
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                            int dtype, const Geo& g, const Ws& w, hipStream_t st);
 hipError_t launch_transpose(const Geo& g, const Ws& w, hipStream_t st);

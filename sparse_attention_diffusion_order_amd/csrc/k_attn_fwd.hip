@@ -374,10 +374,6 @@ hipError_t launch_attn_fwd_d(const void* q, const void* k, const void* v, void* 
         // list fit one 16-entry tile
         bool fits = D == D64 && g.K <= BS && g.n[1] % 4 == 0;
         for (int l = g.l0; l <= g.L; ++l) fits = fits && g.Kl[l] <= BS;
-        // where llsa_forward runs selection and attention in one launch (the
-        // one-block body), the attention part runs the same body, so that the
-        // parts in order give llsa_forward's results bit for bit
-        fits = fits && !select_attn_fits(g, dtype);
         if (fits) {
             hipLaunchKernelGGL(attn_fwd_u4, dim3((unsigned)((nblk + 15) / 16)), dim3(256), 0, st,
                                (const unsigned short*)q, (const unsigned short*)k,

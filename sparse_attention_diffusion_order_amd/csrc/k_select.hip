@@ -24,7 +24,7 @@
 // per key block and per 16 key blocks (see flush_counts), which the sparse
 // transpose uses.  When both fit, the two coarsest levels run in one launch
 // (select_top2).
-#include "attn_block.h"
+#include "common.h"
 
 namespace llsa {
 namespace {
@@ -469,38 +469,6 @@ __global__ __launch_bounds__(256) void select_top2(const float* __restrict__ qto
                            blockIdx.x / nL, blockIdx.x % nL);
 }
 
-// Selection and forward in one launch (two levels, d = 64): workgroup p first
-// chooses, as select_top2 does, the top K_2 of level-2 row p and the top K_1
-// of its 16 children, rows 16p .. 16p+15; then its four waves run the
-// attention forward of exactly those 16 query blocks (four each, the
-// one-block kernel's body), whose picks it has just written.  The
-// selection's latency chains of some workgroups overlap the attention of
-// others, and the level-1 picks are read back from the L2 the launch has just
-// written.  Workgroups go to the XCDs in the XCD-aware order, so that
-// neighbouring level-2 blocks -- which pick similar key blocks -- share an L2.
-template <int KPL, int KPG, int ECAP>
-__global__ __launch_bounds__(256) void select_attn_top2(const unsigned short* __restrict__ q,
-                                                        const unsigned short* __restrict__ k,
-                                                        const unsigned short* __restrict__ v,
-                                                        unsigned short* __restrict__ out,
-                                                        float* __restrict__ lse, Geo g, Ws w)
-{
-    extern __shared__ __attribute__((aligned(16))) float smem[];
-    const int nL = g.n[2];
-    const int b = xcd_block(blockIdx.x, gridDim.x);
-    const int gh = b / nL, p = b % nL;
-    top2_rows<KPL, KPG, D64>(w.qbar[1], w.kbar[1], w.qbar[0], w.kbar[0], w.idx[1], w.idx[0],
-                             Counts{w.cnt[0], w.c16[0]}, nL, g.Kl[2], g.Kl[1], g.scale, smem,
-                             gh, p);
-    // the picks (global) are visible to the workgroup, and the selection's
-    // LDS is free for the attention's
-    __syncthreads();
-    const int wv = uniform(threadIdx.x >> 6);
-    unsigned short* sm = (unsigned short*)smem + wv * FwdLds<ECAP, D64>::PER_WAVE;
-    const long q0 = (long)gh * g.n[1] + BS * p + 4 * wv;
-    for (int t = 0; t < 4; ++t) fwd_block<ECAP, D64>(q, k, v, out, lse, g, w, q0 + t, sm);
-}
-
 template <int KPG, int D>
 hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, int* idx,
                        Counts cnt, int G, int n_l, int K, int M, float scale, hipStream_t st)
@@ -532,27 +500,6 @@ hipError_t launch_top2(const Geo& g, const Ws& w, hipStream_t st)
                        w.qbar[L - 1], w.kbar[L - 1], w.qbar[L - 2], w.kbar[L - 2], w.idx[L - 1],
                        w.idx[L - 2], Counts{w.cnt[L - 2], w.c16[L - 2]}, nL, g.Kl[L],
                        g.Kl[L - 1], g.scale);
-    return hipGetLastError();
-}
-
-template <int KPL, int KPG>
-hipError_t launch_sel_attn(const void* q, const void* k, const void* v, void* out, float* lse,
-                           const Geo& g, const Ws& w, hipStream_t st)
-{
-    constexpr int ECAP = 64;
-    const int nL = g.n[2], M = BS * g.Kl[2];
-    const size_t sel_lds = (size_t)(BS * M + 2 * M + nL + g.Kl[2]) * sizeof(float);
-    const size_t att_lds = 4 * FwdLds<ECAP, D64>::PER_WAVE * sizeof(unsigned short);
-    const size_t lds = sel_lds > att_lds ? sel_lds : att_lds;
-    auto kern = select_attn_top2<KPL, KPG, ECAP>;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(kern, dim3(g.G * nL), dim3(256), lds, st, (const unsigned short*)q,
-                       (const unsigned short*)k, (const unsigned short*)v, (unsigned short*)out,
-                       lse, g, w);
     return hipGetLastError();
 }
 
@@ -627,26 +574,6 @@ hipError_t launch_select_d(const Geo& g, const Ws& w, bool zero_counts, hipStrea
 }
 
 }  // namespace
-
-bool select_attn_fits(const Geo& g, int dtype)
-{
-    if (dtype != LLSA_BF16 || g.d != D64 || g.L != 2 || g.n[2] > 1024 || g.Kl[2] > 16)
-        return false;
-    return g.n_pooled() <= 64;  // the one-block body's pooled-entry table (ECAP 64)
-}
-
-hipError_t launch_select_attn(const void* q, const void* k, const void* v, void* out, float* lse,
-                              const Geo& g, const Ws& w, hipStream_t st)
-{
-    const int M = BS * g.Kl[2];
-    const bool small = g.n[2] <= 256;
-    auto f = M <= 16 ? (small ? launch_sel_attn<4, 1> : launch_sel_attn<16, 1>)
-           : M <= 32 ? (small ? launch_sel_attn<4, 2> : launch_sel_attn<16, 2>)
-           : M <= 64 ? (small ? launch_sel_attn<4, 4> : launch_sel_attn<16, 4>)
-           : M <= 128 ? (small ? launch_sel_attn<4, 8> : launch_sel_attn<16, 8>)
-           : (small ? launch_sel_attn<4, 16> : launch_sel_attn<16, 16>);
-    return f(q, k, v, out, lse, g, w, st);
-}
 
 hipError_t launch_select(const Geo& g, const Ws& w, bool zero_counts, hipStream_t st)
 {
