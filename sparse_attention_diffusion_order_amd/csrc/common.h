@@ -38,6 +38,7 @@ struct Geo {
     unsigned flags;
     int l0;                // first level whose pooled tokens enrich (L + 1: none)
     float lb2;             // logit bias of a level-l pooled token: l * lb2 (log2 units)
+    int xcd_chunk;         // workgroups per XCD chunk of the attention launches (xcd_block)
     __host__ __device__ int n_pooled() const { return l0 <= L ? eoff[L + 1] : 0; }
     // level of pooled entry e (0 <= e < n_pooled())
     __host__ __device__ int entry_level(int e) const
@@ -216,12 +217,22 @@ __device__ __forceinline__ int clampi(int x, int n)
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on
 // XCD b % 8).  Renumber them so that consecutive logical workgroups -- which
 // work on neighbouring query or key blocks and gather the same candidate
-// blocks -- run on the same XCD and share its L2.
-__device__ __forceinline__ int xcd_block(int b, int nb)
+// blocks -- run on the same XCD and share its L2: the r-th workgroup an XCD
+// receives takes logical index (r / S) 8S + xcd S + r % S, i.e. the eight
+// XCDs work through eight neighbouring chunks of S workgroups at a time.
+// S = 0 means S = nb / 8: each XCD owns one contiguous eighth of the launch.
+// A small S (Geo::xcd_chunk, chosen on the host) keeps the launch's front
+// narrow, so that the tensors the workgroups in flight gather stay within the
+// 256 MB MALL.  Workgroups past the last full round of 8S keep their index.
+__device__ __forceinline__ int xcd_block(int b, int nb, int S)
 {
-    const int full = nb & ~7;
+    if (S <= 0) S = nb >> 3;
+    if (S == 0) return b;
+    const int span = 8 * S;
+    const int full = nb / span * span;
     if (b >= full) return b;
-    return (b & 7) * (full >> 3) + (b >> 3);
+    const int r = b >> 3;
+    return (r / S) * span + (b & 7) * S + r % S;
 }
 
 // A 16-row bf16 tile of D channels loaded by one wave in 16-byte chunks: a

@@ -160,7 +160,7 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
     __shared__ __attribute__((aligned(16))) unsigned short smem[4][Lay::PER_WAVE];
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, nq = lane & 15;
-    const long qblk = (long)xcd_block(bid, nb) * 4 + wv;
+    const long qblk = (long)xcd_block(bid, nb, g.xcd_chunk) * 4 + wv;
     if (qblk >= (long)g.G * g.n[1]) return;
     const int gh = (int)(qblk / g.n[1]), i = (int)(qblk % g.n[1]);
     const float c = g.scale * LOG2E;
@@ -530,22 +530,32 @@ struct QBlock {
               // level-1 pooled P (lanes 32..47) and dS (48..63) of row lane % 16
 };
 
-template <int D>
-__global__ __launch_bounds__(64) void dkdv_bf16(const unsigned short* __restrict__ q,
-                                                const unsigned short* __restrict__ k,
-                                                const unsigned short* __restrict__ v,
-                                                const float* __restrict__ lse,
-                                                const unsigned short* __restrict__ dout,
-                                                unsigned short* __restrict__ dk,
-                                                unsigned short* __restrict__ dv, Geo g, Ws w)
+// Waves per workgroup of the dk/dv pass: WPG consecutive (sibling) key
+// blocks, one independent wave each (no barriers), share a CU and so its L1
+// and the timing of their overlapping query-block fetches.
+constexpr int DKDV_WPG = 1;
+
+template <int D, int WPG>
+__global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __restrict__ q,
+                                                      const unsigned short* __restrict__ k,
+                                                      const unsigned short* __restrict__ v,
+                                                      const float* __restrict__ lse,
+                                                      const unsigned short* __restrict__ dout,
+                                                      unsigned short* __restrict__ dk,
+                                                      unsigned short* __restrict__ dv, Geo g,
+                                                      Ws w)
 {
     using TS = TileShape<D>;
     constexpr int NI = TS::NI, ND = D / 16;
-    __shared__ __attribute__((aligned(16))) unsigned short lq[TILE<D>], ld[TILE<D>];
-    __shared__ __attribute__((aligned(16))) float aux[4 * BS];
-    const int lane = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) unsigned short lqs[WPG][TILE<D>], lds_[WPG][TILE<D>];
+    __shared__ __attribute__((aligned(16))) float auxs[WPG][4 * BS];
+    const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
+    unsigned short* lq = lqs[wv];
+    unsigned short* ld = lds_[wv];
+    float* aux = auxs[wv];
     const int gq = lane >> 4, nq = lane & 15;
-    const long kblk = xcd_block(blockIdx.x, gridDim.x);
+    const long kblk = (long)xcd_block(blockIdx.x, gridDim.x, g.xcd_chunk) * WPG + wv;
+    if (kblk >= (long)g.G * g.n[1]) return;
     const int gh = (int)(kblk / g.n[1]), j = (int)(kblk % g.n[1]);
     const bool enrich1 = g.l0 == 1;  // level-1 pooled tokens enrich
     const float c = g.scale * LOG2E;
@@ -954,7 +964,8 @@ hipError_t launch_attn_dkdv_d(const void* q, const void* k, const void* v, const
 {
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
-        hipLaunchKernelGGL(dkdv_bf16<D>, dim3((unsigned)nblk), dim3(64), 0, st,
+        hipLaunchKernelGGL((dkdv_bf16<D, DKDV_WPG>), dim3((unsigned)((nblk + DKDV_WPG - 1) / DKDV_WPG)),
+                           dim3(64 * DKDV_WPG), 0, st,
                            (const unsigned short*)q, (const unsigned short*)k,
                            (const unsigned short*)v, lse, (const unsigned short*)dout,
                            (unsigned short*)dk, (unsigned short*)dv, g, w);

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const unsigned short* __res
 {
     __shared__ __attribute__((aligned(16))) unsigned short smem[4][FwdLds<ECAP, D>::PER_WAVE];
     const int wv = uniform(threadIdx.x >> 6);
-    const long qblk = (long)xcd_block(blockIdx.x, gridDim.x) * 4 + wv;  // over G * n1
+    const long qblk = (long)xcd_block(blockIdx.x, gridDim.x, g.xcd_chunk) * 4 + wv;  // over G * n1
     if (qblk >= (long)g.G * g.n[1]) return;
     fwd_block<ECAP, D>(q, k, v, out, lse, g, w, qblk, smem[wv]);
 }
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
     const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
     const int gq = lane >> 4, nq = lane & 15;
     const int rr = (lane & 15) >> 2, xx = lane & 3;
-    const long qb0 = ((long)xcd_block(blockIdx.x, gridDim.x) * 4 + wv) * 4;  // over G * n1
+    const long qb0 = ((long)xcd_block(blockIdx.x, gridDim.x, g.xcd_chunk) * 4 + wv) * 4;  // over G * n1
     if (qb0 >= (long)g.G * g.n[1]) return;
     const int gh = (int)(qb0 / g.n[1]), i0 = (int)(qb0 % g.n[1]);
     U4Lds& L = sm[wv];
