@@ -75,7 +75,33 @@ def _p(a):
 
 
 def level_sizes(N: int, bs: int, L: int):
-    return [N // bs ** l for l in range(1, L + 1)]
+    """blocks per level: ceil(N / bs^l) (the last block of a level may be partial)"""
+    return [-(-N // bs ** l) for l in range(1, L + 1)]
+
+
+def min_candidates(N: int, bs: int, L: int, K):
+    """The fewest candidates any row of each level has (level 1 first): every
+    block at the coarsest level; below it the existing children of the
+    parent's picks, at worst bs (K_{l+1} - 1) full parents and the partial last
+    one."""
+    ks = level_topk(K, L)
+    n = level_sizes(N, bs, L)
+    out = []
+    for l in range(1, L + 1):
+        if l == L:
+            out.append(n[l - 1])
+        else:
+            last = n[l - 1] - bs * (n[l] - 1)  # children of the last parent block
+            out.append(bs * (ks[l] - 1) + last)
+    return out
+
+
+def check_topk(N: int, bs: int, L: int, K):
+    """Raise ValueError unless every row has at least as many candidates as picks."""
+    for l, (k, m) in enumerate(zip(level_topk(K, L), min_candidates(N, bs, L, K)), 1):
+        if k > m:
+            raise ValueError("level %d: top-k %d exceeds the %d candidates a row may have"
+                             % (l, k, m))
 
 
 def _flat_levels(levels):
@@ -151,7 +177,7 @@ def select_level(qbar, kbar, parent, K: int, bs: int, scale: float):
     par = None if parent is None else _i32(parent)
     Kp = 0 if par is None else par.shape[2]
     if par is not None:
-        assert par.shape[:2] == (G, n // bs)
+        assert par.shape[:2] == (G, -(-n // bs))
     idx = np.zeros((G, n, K), np.int32)
     gap = np.zeros((G, n))
     _load().orc_select_level(_p(qbar), _p(kbar), _p(par), G, n, d, bs, K, Kp, scale,
@@ -159,13 +185,15 @@ def select_level(qbar, kbar, parent, K: int, bs: int, scale: float):
     return idx, gap
 
 
-def select(qpyr, kpyr, K, bs: int, scale: float):
-    """All levels; K an int or one value per level (level 1 first).  Returns
-    (idx list per level 1..L, gap list per level)."""
+def select(qpyr, kpyr, K, bs: int, scale: float, N=None):
+    """All levels; K an int or one value per level (level 1 first); N: the
+    token count (default: level 1's blocks times bs).  Returns (idx list per
+    level 1..L, gap list per level)."""
     G, n1, d = qpyr[0].shape
     L = len(qpyr)
-    N = n1 * bs
+    N = n1 * bs if N is None else N
     ks = level_topk(K, L)
+    check_topk(N, bs, L, ks)
     sizes = level_sizes(N, bs, L)
     idx = np.zeros(G * sum(n * k for n, k in zip(sizes, ks)), np.int32)
     gap = np.zeros(G * sum(sizes))
@@ -226,12 +254,12 @@ def run(q, k, v, bs: int, L: int, K, flags: int = 0, dout=None, scale=None,
     `idx` is given; K an int or one value per level), forward and, with `dout`,
     backward.  Returns a dict."""
     q, k, v = _f64(q), _f64(k), _f64(v)
-    d = q.shape[2]
+    N, d = q.shape[1], q.shape[2]
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     qp, kp, vp = pool(q, bs, L), pool(k, bs, L), pool(v, bs, L)
     gap = None
     if idx is None:
-        idx, gap = select(qp, kp, K, bs, scale)
+        idx, gap = select(qp, kp, K, bs, scale, N=N)
     res = {"qpyr": qp, "kpyr": kp, "vpyr": vp, "idx": idx, "gap": gap, "scale": scale}
     if dout is None:
         res["out"], res["lse"] = forward(q, k, v, kp, vp, idx, bs, scale, flags, qblocks)

@@ -20,11 +20,27 @@ static int64_t ipow(int64_t b, int e)
     return r;
 }
 
+/* Blocks of level l: the sequence of N tokens is covered by ceil(N / bs^l)
+ * blocks of bs^l consecutive tokens; when bs^l does not divide N the last
+ * block is partial (it covers the tokens that remain). */
+static int64_t nblk(int64_t N, int64_t bs, int l)
+{
+    const int64_t span = ipow(bs, l);
+    return (N + span - 1) / span;
+}
+
+/* tokens covered by block j of level l */
+static int64_t blk_tokens(int64_t N, int64_t bs, int l, int64_t j)
+{
+    const int64_t span = ipow(bs, l), rest = N - j * span;
+    return rest < span ? rest : span;
+}
+
 /* offset (in rows of width `w`) of level l (1-based) inside a pyramid */
 static int64_t lvl_off(int64_t G, int64_t N, int64_t bs, int l, int64_t w)
 {
     int64_t off = 0;
-    for (int m = 1; m < l; ++m) off += G * (N / ipow(bs, m)) * w;
+    for (int m = 1; m < l; ++m) off += G * nblk(N, bs, m) * w;
     return off;
 }
 
@@ -33,7 +49,7 @@ static int64_t lvl_off(int64_t G, int64_t N, int64_t bs, int l, int64_t w)
 static int64_t idx_off(int64_t G, int64_t N, int64_t bs, int l, const int64_t* K)
 {
     int64_t off = 0;
-    for (int m = 1; m < l; ++m) off += G * (N / ipow(bs, m)) * K[m - 1];
+    for (int m = 1; m < l; ++m) off += G * nblk(N, bs, m) * K[m - 1];
     return off;
 }
 
@@ -119,21 +135,29 @@ void orc_grid_order(const double* src, double* dst, int64_t outer, int64_t T, in
 
 /* ------------------------------------------------------------------ pool */
 
-/* [P2] hierarchical compression: level l = block means of level l-1. */
+/* [P2] hierarchical compression: level l = block means of level l-1.  A
+ * block's pooled token is the mean of the tokens it covers: each of its (up
+ * to bs) children enters with the number of tokens that child covers, so a
+ * partial last block averages only its own tokens.  (With every block full
+ * the weights are equal powers of bs, and the result is the plain mean of the
+ * bs children.) */
 void orc_pool(const double* x, int64_t G, int64_t N, int64_t d, int64_t bs,
               int L, double* pyr)
 {
     for (int l = 1; l <= L; ++l) {
-        int64_t n_prev = N / ipow(bs, l - 1), n_l = N / ipow(bs, l);
+        int64_t n_prev = l == 1 ? N : nblk(N, bs, l - 1), n_l = nblk(N, bs, l);
         const double* src = (l == 1) ? x : pyr + lvl_off(G, N, bs, l - 1, d);
         double* dst = pyr + lvl_off(G, N, bs, l, d);
         for (int64_t g = 0; g < G; ++g)
             for (int64_t i = 0; i < n_l; ++i)
                 for (int64_t c = 0; c < d; ++c) {
-                    double s = 0.0;
-                    for (int64_t r = 0; r < bs; ++r)
-                        s += src[(g * n_prev + bs * i + r) * d + c];
-                    dst[(g * n_l + i) * d + c] = s / (double)bs;
+                    double s = 0.0, w = 0.0;
+                    for (int64_t r = 0; r < bs && bs * i + r < n_prev; ++r) {
+                        const double wr = l == 1 ? 1.0 : (double)blk_tokens(N, bs, l - 1, bs * i + r);
+                        s += wr * src[(g * n_prev + bs * i + r) * d + c];
+                        w += wr;
+                    }
+                    dst[(g * n_l + i) * d + c] = s / w;
                 }
     }
 }
@@ -175,17 +199,21 @@ void orc_select_level(const double* qbar, const double* kbar,
             if (!parent) {
                 for (int64_t j = 0; j < n_l; ++j) c[nc++].j = (int32_t)j;
             } else {
-                const int32_t* pr = parent + (g * (n_l / bs) + i / bs) * Kp;
+                /* the children of the parent's picks that exist (the last
+                 * parent block may have fewer than bs children) */
+                const int32_t* pr = parent + (g * ((n_l + bs - 1) / bs) + i / bs) * Kp;
                 for (int64_t p = 0; p < Kp; ++p)
                     for (int64_t r = 0; r < bs; ++r)
-                        c[nc++].j = (int32_t)(bs * pr[p] + r);
+                        if (bs * pr[p] + r < n_l) c[nc++].j = (int32_t)(bs * pr[p] + r);
             }
             const double* qi = qbar + (g * n_l + i) * d;
             for (int64_t e = 0; e < nc; ++e)
                 c[e].score = scale * dot(qi, kbar + (g * n_l + c[e].j) * d, d);
             qsort(c, (size_t)nc, sizeof(cand_t), cand_cmp);
+            /* the callers guarantee nc >= K (a row never has fewer candidates
+             * than picks); -1 would mark a missing pick */
             int32_t* row = idx + (g * n_l + i) * K;
-            for (int64_t e = 0; e < K; ++e) row[e] = c[e].j;
+            for (int64_t e = 0; e < K; ++e) row[e] = e < nc ? c[e].j : -1;
             qsort(row, (size_t)K, sizeof(int32_t), int_cmp);
             if (gap) gap[g * n_l + i] = (nc > K) ? c[K - 1].score - c[K].score : INFINITY;
         }
@@ -197,7 +225,7 @@ void orc_select(const double* qpyr, const double* kpyr, int64_t G, int64_t N,
                 int32_t* idx, double* gap)
 {
     for (int l = L; l >= 1; --l) {
-        int64_t n_l = N / ipow(bs, l);
+        int64_t n_l = nblk(N, bs, l);
         const int32_t* parent = (l == L) ? NULL : idx + idx_off(G, N, bs, l + 1, K);
         orc_select_level(qpyr + lvl_off(G, N, bs, l, d), kpyr + lvl_off(G, N, bs, l, d),
                          parent, G, n_l, d, bs, K[l - 1], l == L ? 0 : K[l], scale,
@@ -230,10 +258,10 @@ static int64_t kv_set(const double* k, const double* v, const double* kpyr,
                       const double** val, int* tag, int64_t* ref)
 {
     int64_t ne = 0;
-    int64_t n1 = N / bs;
+    int64_t n1 = nblk(N, bs, 1);
     const int32_t* sel1 = idx + (g * n1 + t / bs) * K[0];
     for (int64_t p = 0; p < K[0]; ++p)
-        for (int64_t r = 0; r < bs; ++r) {
+        for (int64_t r = 0; r < bs && bs * sel1[p] + r < N; ++r) {
             int64_t u = bs * sel1[p] + r;
             key[ne] = k + (g * N + u) * d;
             val[ne] = v + (g * N + u) * d;
@@ -243,7 +271,7 @@ static int64_t kv_set(const double* k, const double* v, const double* kpyr,
         }
     if (!(flags & ORC_NO_ENRICH))
         for (int l = (flags & ORC_ENRICH_COARSE) ? 2 : 1; l <= L; ++l) {
-            int64_t n_l = N / ipow(bs, l), a = t / ipow(bs, l);
+            int64_t n_l = nblk(N, bs, l), a = t / ipow(bs, l);
             const int32_t* sel = idx + idx_off(G, N, bs, l, K) + (g * n_l + a) * K[l - 1];
             for (int64_t p = 0; p < K[l - 1]; ++p) {
                 int64_t j = sel[p];
@@ -265,7 +293,7 @@ void orc_forward(const double* q, const double* k, const double* v,
                  double scale, unsigned flags, const int64_t* qblocks,
                  int64_t nq, double* out, double* lse)
 {
-    int64_t n1 = N / bs, maxe = bs * K[0];
+    int64_t n1 = nblk(N, bs, 1), maxe = bs * K[0];
     for (int l = 1; l <= L; ++l) maxe += K[l - 1];
     const double** key = (const double**)malloc((size_t)maxe * sizeof(double*));
     const double** val = (const double**)malloc((size_t)maxe * sizeof(double*));
@@ -276,7 +304,7 @@ void orc_forward(const double* q, const double* k, const double* v,
     for (int64_t g = 0; g < G; ++g)
         for (int64_t b = 0; b < nb; ++b) {
             int64_t i = qblocks ? qblocks[b] : b;
-            for (int64_t t = bs * i; t < bs * (i + 1); ++t) {
+            for (int64_t t = bs * i; t < bs * (i + 1) && t < N; ++t) {
                 int64_t ne = kv_set(k, v, kpyr, vpyr, idx, g, t, G, N, d, bs, L, K,
                                     flags, key, val, tag, ref);
                 const double* qt = q + (g * N + t) * d;
@@ -309,7 +337,7 @@ void orc_backward(const double* q, const double* k, const double* v,
                   int64_t nq, const int64_t* kblocks, int64_t nk, double* dq,
                   double* dk, double* dv)
 {
-    int64_t n1 = N / bs, maxe = bs * K[0];
+    int64_t n1 = nblk(N, bs, 1), maxe = bs * K[0];
     for (int l = 1; l <= L; ++l) maxe += K[l - 1];
     const double** key = (const double**)malloc((size_t)maxe * sizeof(double*));
     const double** val = (const double**)malloc((size_t)maxe * sizeof(double*));
@@ -339,7 +367,7 @@ void orc_backward(const double* q, const double* k, const double* v,
         memset(dvp, 0, (size_t)(pyr_rows * d) * sizeof(double));
         for (int64_t b = 0; b < n1; ++b)
             if (want_k[b])
-                for (int64_t x = bs * b; x < bs * (b + 1); ++x)
+                for (int64_t x = bs * b; x < bs * (b + 1) && x < N; ++x)
                     for (int64_t c = 0; c < d; ++c) {
                         dk[(g * N + x) * d + c] = 0.0;
                         dv[(g * N + x) * d + c] = 0.0;
@@ -352,14 +380,14 @@ void orc_backward(const double* q, const double* k, const double* v,
             for (int64_t p = 0; p < K[0] && !need; ++p) need = want_k[sel1[p]];
             if (!(flags & ORC_NO_ENRICH))
                 for (int l = 1; l <= L && !need; ++l) {
-                    int64_t n_l = N / ipow(bs, l), a = (bs * i) / ipow(bs, l);
+                    int64_t n_l = nblk(N, bs, l), a = (bs * i) / ipow(bs, l);
                     const int32_t* sel = idx + idx_off(G, N, bs, l, K) + (g * n_l + a) * K[l - 1];
                     for (int64_t p = 0; p < K[l - 1] && !need; ++p)
                         need = want_p[lvl_off(1, N, bs, l, 1) + sel[p]];
                 }
             if (!need) continue;
 
-            for (int64_t t = bs * i; t < bs * (i + 1); ++t) {
+            for (int64_t t = bs * i; t < bs * (i + 1) && t < N; ++t) {
                 int64_t ne = kv_set(k, v, kpyr, vpyr, idx, g, t, G, N, d, bs, L, K,
                                     flags, key, val, tag, ref);
                 const double* qt = q + (g * N + t) * d;
@@ -394,14 +422,15 @@ void orc_backward(const double* q, const double* k, const double* v,
             }
         }
 
-        /* a level-l pooled token is the mean of bs^l tokens: each of them
-         * receives 1/bs^l of its gradient */
+        /* a level-l pooled token is the mean of the tokens it covers (bs^l,
+         * fewer in a partial last block): each of them receives that fraction
+         * of its gradient */
         for (int64_t b = 0; b < n1; ++b)
             if (want_k[b])
-                for (int64_t x = bs * b; x < bs * (b + 1); ++x)
+                for (int64_t x = bs * b; x < bs * (b + 1) && x < N; ++x)
                     for (int l = 1; l <= L; ++l) {
                         int64_t row = lvl_off(1, N, bs, l, 1) + x / ipow(bs, l);
-                        double w = 1.0 / (double)ipow(bs, l);
+                        double w = 1.0 / (double)blk_tokens(N, bs, l, x / ipow(bs, l));
                         for (int64_t c = 0; c < d; ++c) {
                             dk[(g * N + x) * d + c] += w * dkp[row * d + c];
                             dv[(g * N + x) * d + c] += w * dvp[row * d + c];

@@ -21,7 +21,10 @@
  *   G = B*H independent heads, N tokens, d channels, bs = block size,
  *   L = number of pooling levels, K[l-1] = top-k of level l (all equal in the
  *   README's usage; a per-level K is an extension),
- *   n_l = N / bs^l blocks at level l (l = 1..L).
+ *   n_l = ceil(N / bs^l) blocks at level l (l = 1..L): block j covers tokens
+ *   j*bs^l .. min((j+1)*bs^l, N) - 1, so when bs^l does not divide N the last
+ *   block of a level is partial (padding to a multiple of bs^L, with the
+ *   padded tokens never attended).
  *   token tensors  : [G][N][d]            double
  *   pyramid        : level l (1..L) stored at offset G*d*sum_{l'<l} n_{l'},
  *                    each level [G][n_l][d]
@@ -72,15 +75,17 @@ void orc_grid_order(const double* src, double* dst, int64_t outer, int64_t T, in
                     int64_t W, int64_t inner, int inverse);
 
 /* Block mean-pool pyramid of x [G][N][d]: level l token i is the mean of the
- * bs level-(l-1) tokens bs*i .. bs*i+bs-1 ([P2] hierarchical compression,
- * [P3] block-wise representation). */
+ * tokens block i covers, computed from its (up to bs) level-(l-1) children
+ * weighted by the tokens each covers ([P2] hierarchical compression, [P3]
+ * block-wise representation). */
 void orc_pool(const double* x, int64_t G, int64_t N, int64_t d, int64_t bs,
               int L, double* pyr);
 
 /* Top-K selection at one level ([P2] hierarchical Top-K).
  * parent == NULL: coarsest level, candidates are all n_l blocks.
- * otherwise parent is [G][n_l/bs][Kp] (ascending) and the candidates of row i
- * are the bs*Kp children bs*c + r of the parent row i/bs.
+ * otherwise parent is [G][ceil(n_l/bs)][Kp] (ascending) and the candidates of
+ * row i are the existing children bs*c + r < n_l of the parent row i/bs.
+ * Precondition: every row has at least K candidates.
  * Score = scale * <qbar_l[i], kbar_l[j]>; order = score descending, then
  * block index ascending; the first K are kept and stored ascending.
  * gap[i] = score of K-th kept - score of best rejected (+inf if none). */
@@ -113,7 +118,8 @@ void orc_forward(const double* q, const double* k, const double* v,
  * dq is written for the query blocks in qblocks (NULL = all); dk, dv are
  * written for the key blocks in kblocks (NULL = all); the rest is untouched.
  * Selection is piecewise constant: no gradient flows through the scores.
- * Pooled tokens pass their gradient to the tokens they average (mean rule). */
+ * A pooled token passes 1/count of its gradient to each of the count tokens it
+ * averages (mean rule). */
 void orc_backward(const double* q, const double* k, const double* v,
                   const double* kpyr, const double* vpyr, const int32_t* idx,
                   const double* o, const double* lse, const double* dout,
