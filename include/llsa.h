@@ -17,6 +17,16 @@
  *   - the backward pass turns the query->key block lists into key->query
  *     lists (a sparse index transpose) instead of building a dense mask.
  *
+ * Token counts (README usage: the power-of-two limit is to be lifted).  N
+ *   is any multiple of 16.  Level l has n_l = ceil(N / 16^l) blocks; when 16^l
+ *   does not divide N the last one is partial, as if the sequence were padded
+ *   to a multiple of 16^levels with tokens that are never attended: its pooled
+ *   token is the mean of the tokens it covers (and passes 1/count of its
+ *   gradient to each), and a level's candidates are the blocks that exist.  A
+ *   row of the coarsest level chooses among n_L blocks; below it among the
+ *   existing children of its parent's picks -- at worst 16 (topk_{l+1} - 1)
+ *   full parents and the partial last one -- and top-k may not exceed that.
+ *
  * Conventions shared by all entry points
  *   Tensors q, k, v, out, dout, dq, dk, dv: contiguous [B][H][N][d] in the
  *   element type `dtype` (LLSA_F32 or LLSA_BF16), tokens already in Z-order
@@ -62,10 +72,12 @@ extern "C" {
 /* error codes */
 #define LLSA_OK 0
 #define LLSA_ERR_NULL (-1)        /* a required pointer is NULL */
-#define LLSA_ERR_SHAPE (-2)       /* levels < 1, 16^levels does not divide N,
-                                     topk < 1 or topk > N / 16^levels,
+#define LLSA_ERR_SHAPE (-2)       /* levels < 1, N not a multiple of 16,
+                                     a top-k < 1 or above the candidates a row
+                                     of its level may have (see below),
                                      B or H < 1 (N and topk need not be
-                                     powers of two) */
+                                     powers of two, nor N a multiple of
+                                     16^levels) */
 #define LLSA_ERR_UNSUPPORTED (-3) /* d not 64 or 128, block_size != 16, unknown dtype
                                      or flags, levels > LLSA_MAX_LEVELS,
                                      coarsest block count > 4096, topk > 64,
@@ -167,8 +179,9 @@ int llsa_backward(const void* q, const void* k, const void* v, const void* out,
  * same with a different count at each level).  topk: HOST array of `levels`
  * ints, topk[l-1] the picks of every level-l row, level 1 (the fine blocks)
  * first; read during the call only.  Level l < levels chooses among the
- * 16*topk[l] children of its parent's picks, so 1 <= topk[l-1] <=
- * 16*topk[l]; the coarsest level among N/16^levels blocks.  Every other
+ * (up to) 16*topk[l] children of its parent's picks, so 1 <= topk[l-1] <=
+ * 16*(topk[l] - 1) + the children of the level's partial last parent (16 when
+ * 16^(l+1) divides N); the coarsest level among ceil(N/16^levels) blocks.  Every other
  * argument, the layout and the errors are those of the uniform calls (a NULL
  * topk gives LLSA_ERR_NULL); with equal values the results are identical to
  * them.  The workspace must be sized by llsa_workspace_bytes_lk with the same

@@ -28,14 +28,19 @@ int validate(int B, int H, int N, int d, int block_size, const int* ks, int leve
         return LLSA_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || N < BS || levels < 1) return LLSA_ERR_SHAPE;
     if (levels > MAX_L) return LLSA_ERR_UNSUPPORTED;
-    long long span = 1;
-    for (int l = 0; l < levels; ++l) span *= BS;
-    if (span > N || N % span) return LLSA_ERR_SHAPE;
-    long long nL = N / span;
-    // level l chooses among n_L blocks (coarsest) or the 16 K_{l+1} children
-    // of its parent's picks
+    if (N % BS) return LLSA_ERR_SHAPE;  // whole level-1 blocks
+    // level l has ceil(N / 16^l) blocks, the last one partial when 16^l does
+    // not divide N
+    long long n[MAX_L + 2];
+    n[0] = N;
+    for (int l = 1; l <= levels; ++l) n[l] = (n[l - 1] + BS - 1) / BS;
+    const long long nL = n[levels];
+    // level l chooses among the n_L blocks (coarsest) or the existing
+    // children of its parent's K_{l+1} picks: at worst 16 (K_{l+1} - 1) full
+    // parents and the last, partial one
     for (int l = levels; l >= 1; --l) {
-        const long long cands = l == levels ? nL : (long long)BS * ks[l];
+        const long long cands =
+            l == levels ? nL : (long long)BS * (ks[l] - 1) + (n[l] - BS * (n[l + 1] - 1));
         if (ks[l - 1] < 1 || ks[l - 1] > cands) return LLSA_ERR_SHAPE;
     }
     for (int l = 0; l < levels; ++l)
@@ -71,7 +76,7 @@ void make_layout(int G, int N, int D, const int* ks, int L, Layout* lay, bool fw
     };
     long long n[MAX_L + 1];
     n[0] = N;
-    for (int l = 1; l <= L; ++l) n[l] = n[l - 1] / BS;
+    for (int l = 1; l <= L; ++l) n[l] = (n[l - 1] + BS - 1) / BS;
     for (int l = 1; l <= L; ++l) {
         size_t pyr = (size_t)G * n[l] * D * sizeof(float);
         lay->pub.qbar[l - 1] = take(pyr);
@@ -116,7 +121,7 @@ void make_geo(int B, int H, int N, int d, const int* ks, int levels, unsigned fl
     g->L = levels;
     g->n[0] = N;
     for (int l = 1; l <= levels; ++l) {
-        g->n[l] = g->n[l - 1] / BS;
+        g->n[l] = (g->n[l - 1] + BS - 1) / BS;  // the last block may be partial
         g->Kl[l] = ks[l - 1];
     }
     g->scale = 1.0f / sqrtf((float)d);  // SDPA's default scale
@@ -458,10 +463,11 @@ const char* llsa_strerror(int code)
     case LLSA_OK: return "ok";
     case LLSA_ERR_NULL: return "a required pointer is NULL";
     case LLSA_ERR_SHAPE:
-        return "bad shape: 16^levels must divide N; B, H, levels >= 1; every top-k >= 1 and "
-               "at most its level's candidates (N/16^levels at the coarsest level, 16 times "
-               "the parent level's top-k below it); grid order: sides in [1, 2^15], at most "
-               "2^30 cells, inner_bytes a positive multiple of 4";
+        return "bad shape: N a multiple of 16; B, H, levels >= 1; every top-k >= 1 and "
+               "at most the candidates a row of its level may have (ceil(N/16^levels) at the "
+               "coarsest level; below it 16 (parent top-k - 1) plus the children of the "
+               "partial last parent); grid order: sides in [1, 2^15], at most 2^30 cells, "
+               "inner_bytes a positive multiple of 4";
     case LLSA_ERR_UNSUPPORTED:
         return "unsupported: needs d=64 or 128, block_size=16, dtype f32/bf16, known flags, "
                "levels<=6, at most 4096 coarsest blocks, topk<=64, B*H*N<2^31";

@@ -28,7 +28,10 @@ struct Geo {
     int N;                 // tokens per head
     int K;                 // top-k of level 1 (the fine blocks), == Kl[1]
     int L;                 // pooling levels
-    int n[MAX_L + 1];      // n[l] = N / 16^l blocks at level l (n[0] = N)
+    int n[MAX_L + 1];      // n[l] = ceil(N / 16^l) blocks at level l (n[0] = N); N is a
+                           // multiple of 16, and the last block of a level l >= 2
+                           // covers the tokens that remain (fewer than 16^l when
+                           // 16^l does not divide N)
     int d;                 // head dimension (64 or 128)
     int Kl[MAX_L + 2];     // Kl[l]: picks per level-l row, l = 1..L
     // pooled entries of a query block: those of level l (l0 <= l <= L) are
@@ -40,6 +43,12 @@ struct Geo {
     float lb2;             // logit bias of a level-l pooled token: l * lb2 (log2 units)
     int xcd_chunk;         // workgroups per XCD chunk of the attention launches (xcd_block)
     __host__ __device__ int n_pooled() const { return l0 <= L ? eoff[L + 1] : 0; }
+    // tokens covered by block j of level l (16^l but for a partial last block)
+    __host__ __device__ int tokens(int l, int j) const
+    {
+        const long span = 1l << (4 * l), rest = (long)N - (long)j * span;
+        return (int)(rest < span ? rest : span);
+    }
     // level of pooled entry e (0 <= e < n_pooled())
     __host__ __device__ int entry_level(int e) const
     {

@@ -362,8 +362,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
     unsigned short* ld = smem[wv][1];
     // this wave's four query blocks i = 16 a2 + 4 wv + u (u < 4); load v of
     // a block covers its row sr + RPI v
+    // query blocks past the last level-1 block (under a partial last level-2
+    // block) do not exist: their rows are read from the last block instead
+    // and their weights are 0
     auto row_addr = [&](int u) {
-        const int i = 16 * a2 + 4 * wv + u;
+        const int i = min(16 * a2 + 4 * wv + u, g.n[1] - 1);
         return ((long)gh * g.N + (long)i * BS + sr) * D + sc;
     };
     auto load_rows = [&](bf16x8 (&xq)[NI], bf16x8 (&xd)[NI], long a) {
@@ -373,7 +376,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
         for (int v = 0; v < NI; ++v) xd[v] = ld8(dout + a + (long)TS::RPI * v * D);
     };
     {
-        const long t0 = (long)gh * g.N + (long)(16 * a2 + 4 * wv) * BS + lane;
+        const int i = min(16 * a2 + 4 * wv + (lane >> 4), g.n[1] - 1);
+        const long t0 = (long)gh * g.N + (long)i * BS + (lane & 15);
         rowst[wv][0][lane] = lse[t0];
         rowst[wv][1][lane] = w.delta[t0];
     }
@@ -413,10 +417,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
                 const float4 l4 = *(const float4*)&rowst[wv][0][u * BS + 4 * gq];
                 const float4 d4 = *(const float4*)&rowst[wv][1][u * BS + 4 * gq];
                 const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, dr[4] = {d4.x, d4.y, d4.z, d4.w};
+                const bool live = 16 * a2 + 4 * wv + u < g.n[1];
                 bf16x4 pP, pS;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float P = ev ? fast_exp2(s[r] * c - lr[r] * LOG2E + lb) : 0.f;
+                    float P = (ev && live) ? fast_exp2(s[r] * c - lr[r] * LOG2E + lb) : 0.f;
                     pP[r] = (bf16)P;
                     pS[r] = (bf16)(P * (dp[r] - dr[r]));
                 }
@@ -481,15 +486,23 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
     for (int e0 = beg; e0 < end; e0 += 64) {
         const int ne = min(64, end - e0);
         int off = 0;  // in rows of 2*D floats
-        if (lane < ne) off = clampi(cl[e0 + lane], g.n[l]) * span * Kl + clampi(sl[e0 + lane], Kl);
+        int blk2 = 0;  // the entry's first level-2 block
+        if (lane < ne) {
+            const int a = clampi(cl[e0 + lane], g.n[l]);
+            blk2 = a * span;
+            off = a * span * Kl + clampi(sl[e0 + lane], Kl);
+        }
         const int nrow = ne * span;
         for (int q0 = 0; q0 < nrow; q0 += 8) {
             float vk[8][NC], vv[8][NC];
+            bool ok[8];  // level-2 blocks past the last one (partial level-l block) do not exist
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int qq = min(q0 + u, nrow - 1);
                 const int e = qq / span, a2 = qq % span;
-                const long o = ((long)__builtin_amdgcn_readlane(off, e) + (long)a2 * Kl) * 2 * D;
+                ok[u] = q0 + u < nrow && __builtin_amdgcn_readlane(blk2, e) + a2 < g.n[2];
+                const int a2c = ok[u] ? a2 : 0;
+                const long o = ((long)__builtin_amdgcn_readlane(off, e) + (long)a2c * Kl) * 2 * D;
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     vk[u][c] = part[o + 64 * c];
@@ -498,7 +511,7 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (q0 + u < nrow)
+                if (ok[u])
 #pragma unroll
                     for (int c = 0; c < NC; ++c) {
                         sk[c] += vk[u][c];
@@ -680,7 +693,7 @@ __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __re
         }
         for (int l = max(2, g.l0); l <= g.L; ++l) {
             const int a = j >> (4 * (l - 1));
-            const float wgt = 1.0f / (float)(1 << (4 * l));
+            const float wgt = 1.0f / (float)g.tokens(l, a);  // the mean's share of each token
             const float* db = w.dbar[l - 1] + ((long)gh * g.n[l] + a) * 2 * D + 16 * d + 4 * gq;
             const float4 gk = *(const float4*)db, gv = *(const float4*)(db + D);
             xk[0] += gk.x * wgt; xk[1] += gk.y * wgt; xk[2] += gk.z * wgt; xk[3] += gk.w * wgt;
@@ -803,7 +816,7 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
     const int beg = clampi(rp[j], tot + 1), end = max(beg, clampi(rp[j + 1], tot + 1));
     for (int e = beg; e < end; ++e) {
         const long a = clampi(cl[e], g.n[l]);
-        for (long t = a * span; t < (a + 1) * span; ++t) {
+        for (long t = a * span; t < (a + 1) * span && t < g.N; ++t) {
             const long tg = (long)gh * g.N + t;
             float qc[NC], dc[NC];
             lane_channels<D>(qc, q + tg * D, lane);
@@ -868,7 +881,7 @@ __global__ __launch_bounds__(256) void dkdv_f32(const float* __restrict__ q,
             }
         }
     for (int l = g.l0; l <= g.L; ++l) {
-        const float wgt = 1.0f / (float)(1 << (4 * l));
+        const float wgt = 1.0f / (float)g.tokens(l, x >> (4 * l));  // the mean's share
         const float* db = w.dbar[l - 1] + ((long)gh * g.n[l] + (x >> (4 * l))) * 2 * D;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {

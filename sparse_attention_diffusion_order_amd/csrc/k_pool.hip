@@ -2,8 +2,10 @@
 //
 // LLSA skill summary, "Core Technique" 1 (hierarchical compression) and the
 // arXiv abstract (block-wise representation of tokens): the level-l token i
-// is the mean of the 16 level-(l-1) tokens 16i .. 16i+15.  Levels are
-// computed recursively, in float32.
+// is the mean of the tokens block i covers -- its 16 level-(l-1) children
+// 16i .. 16i+15, fewer for the partial last block of a level when 16^l does
+// not divide N (the children then weighted by the tokens each covers).
+// Levels are computed recursively, in float32.
 //
 // pool_l12: one workgroup per 256 consecutive tokens of one head and one
 // tensor.  Thread (blk, sub) sums the 16 tokens of level-1 block blk over the
@@ -105,14 +107,18 @@ __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T
         }
         __syncthreads();
         if (threadIdx.x < D) {
+            // the mean of the tokens of the level-2 block: its level-1 blocks
+            // (whole blocks of 16 tokens; a partial last level-2 block has
+            // fewer of them, and the others hold zeros)
             float a = 0.f;
 #pragma unroll
             for (int b = 0; b < 16; ++b) a += m1[b][threadIdx.x];
+            const int live1 = min(16, n1 - b0);
+            const float mean = a / (float)live1;
             const long row = (long)gh * g.n[2] + b0 / 16;
-            lv2[row * D + threadIdx.x] = a * (1.0f / BS);
+            lv2[row * D + threadIdx.x] = mean;
             if (tensor)
-                (tensor == 1 ? w.kb16 : w.vb16)[(w.prow[1] + row) * D + threadIdx.x] =
-                    f2bf(a * (1.0f / BS));
+                (tensor == 1 ? w.kb16 : w.vb16)[(w.prow[1] + row) * D + threadIdx.x] = f2bf(mean);
         }
     }
 }
@@ -128,11 +134,20 @@ __global__ __launch_bounds__(256) void pool_up(Geo g, Ws w, int l)
     if (id >= total) return;
     long row = id / D;
     int c = (int)(id % D);
-    float a = 0.f;
-    for (int t = 0; t < BS; ++t) a += src[(row * BS + t) * D + c];
-    dst[id] = a * (1.0f / BS);
-    if (tensor)
-        (tensor == 1 ? w.kb16 : w.vb16)[(w.prow[l - 1] + row) * D + c] = f2bf(a * (1.0f / BS));
+    // the mean of the tokens the block covers: its existing children, each
+    // weighted by the tokens it covers (all 16^(l-1) unless it is the partial
+    // last one; equal power-of-two weights give the plain mean exactly)
+    const int gh = (int)(row / g.n[l]), i = (int)(row % g.n[l]);
+    const int np = g.n[l - 1];
+    float a = 0.f, wsum = 0.f;
+    for (int t = 0; t < BS && BS * i + t < np; ++t) {
+        const float wt = (float)g.tokens(l - 1, BS * i + t);
+        a += wt * src[((long)gh * np + BS * i + t) * D + c];
+        wsum += wt;
+    }
+    const float mean = a / wsum;
+    dst[id] = mean;
+    if (tensor) (tensor == 1 ? w.kb16 : w.vb16)[(w.prow[l - 1] + row) * D + c] = f2bf(mean);
 }
 
 template <int D>

@@ -139,17 +139,18 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
     int* cand = (int*)(sc + R * M);   // [M]
     int* pc = cand + M;               // [M] picks per candidate
 
-    const int groups_per_head = parent ? n_l / BS : (n_l + R - 1) / R;
+    const int np = (n_l + BS - 1) / BS;  // parent-level blocks
+    const int groups_per_head = parent ? np : (n_l + R - 1) / R;
     const int gh = blockIdx.x / groups_per_head;
     const int grp = blockIdx.x % groups_per_head;
     const int row0 = grp * (parent ? BS : R);
-    const int rows = parent ? BS : min(R, n_l - row0);
+    const int rows = min(parent ? BS : R, n_l - row0);
 
     // candidate list (ascending)
     for (int c = threadIdx.x; c < M; c += blockDim.x) {
         if (parent) {
-            const int* pr = parent + ((long)gh * (n_l / BS) + grp) * (M / BS);  // parent row: M/16 picks
-            cand[c] = BS * clampi(pr[c / BS], n_l / BS) + (c % BS);
+            const int* pr = parent + ((long)gh * np + grp) * (M / BS);  // parent row: M/16 picks
+            cand[c] = BS * clampi(pr[c / BS], np) + (c % BS);  // may lie past n_l
         } else {
             cand[c] = c;
         }
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
     const int sub = threadIdx.x & 3;
     for (int c0 = 0; c0 < M; c0 += 64) {
         const int c = c0 + (threadIdx.x >> 2);
-        const bool ok = c < M;
+        const bool ok = c < M && cand[min(c, M - 1)] < n_l;  // children that exist
         float4 kv[NV];
         if (ok) {
             const float4* kr = (const float4*)(kbar + ((long)gh * n_l + cand[c]) * D + (D / 4) * sub);
@@ -189,7 +190,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
             }
             a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false));
             a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false));
-            if (ok && sub == 0) sc[r * M + c] = a * scale + 0.0f;  // + 0 turns -0 into +0
+            if (sub == 0 && c < M)  // + 0 turns -0 into +0; no child: never chosen
+                sc[r * M + c] = ok ? a * scale + 0.0f : -INFINITY;
         }
     }
     __syncthreads();
@@ -297,7 +299,7 @@ __device__ __forceinline__ void load_query_operand(float (&qa)[D / 4], const flo
 template <int KPG, int D>
 __device__ __forceinline__ void score_select16(const float (&qa)[D / 4], const float* kh, int* out,
                                                int rows, int M, int K, float scale, float* sc,
-                                               const int* cand, int* pc, Counts cnt)
+                                               const int* cand, int* pc, Counts cnt, int n_l)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
@@ -305,7 +307,7 @@ __device__ __forceinline__ void score_select16(const float (&qa)[D / 4], const f
     const int tiles = (M + BS - 1) / BS;
     kh += CG * g;
     auto load_tile = [&](float (&kb)[CG], int tile) {
-        const int c = cand[min(tile * BS + n, M - 1)];
+        const int c = min(cand[min(tile * BS + n, M - 1)], n_l - 1);
         const float4* kr = (const float4*)(kh + (long)c * D);
 #pragma unroll
         for (int t = 0; t < CG / 4; ++t) {
@@ -322,9 +324,13 @@ __device__ __forceinline__ void score_select16(const float (&qa)[D / 4], const f
         for (int k = 0; k < CG; ++k)
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[k], kb[k], acc, 0, 0, 0);
         const int col = tile * BS + n;
+        // candidates past the level's last block (children the partial last
+        // parent does not have) score -inf: never chosen
+        const bool exists = col < M && cand[min(col, M - 1)] < n_l;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            if (4 * g + r < rows && col < M) sc[(4 * g + r) * M + col] = acc[r] * scale + 0.0f;
+            if (4 * g + r < rows && col < M)
+                sc[(4 * g + r) * M + col] = exists ? acc[r] * scale + 0.0f : -INFINITY;
 #pragma unroll
         for (int k = 0; k < CG; ++k) kb[k] = kn[k];
     }
@@ -354,10 +360,11 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
     const int grp = blockIdx.x % groups_per_head;
     const int row0 = grp * R;
     const int rows = min(R, n_l - row0);
+    const int np = (n_l + BS - 1) / BS;  // parent-level blocks
     for (int c = threadIdx.x; c < M; c += blockDim.x) {
         if (parent) {
-            const int* pr = parent + ((long)gh * (n_l / BS) + grp) * (M / BS);  // parent row: M/16 picks
-            cand[c] = BS * clampi(pr[c / BS], n_l / BS) + (c % BS);
+            const int* pr = parent + ((long)gh * np + grp) * (M / BS);  // parent row: M/16 picks
+            cand[c] = BS * clampi(pr[c / BS], np) + (c % BS);  // may lie past n_l
         } else {
             cand[c] = c;
         }
@@ -368,7 +375,7 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
     __syncthreads();
     score_select16<KPG, D>(qa, kbar + (long)gh * n_l * D, idx + ((long)gh * n_l + row0) * K, rows,
                            M, K, scale, sc, cand, pc,
-                           {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)});
+                           {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)}, n_l);
 }
 
 // The two coarsest levels in one launch.  Workgroup p (of a head) first
@@ -389,8 +396,8 @@ __device__ __forceinline__ void top2_rows(const float* __restrict__ qtop,
                                           const float* __restrict__ qbar,
                                           const float* __restrict__ kbar,
                                           int* __restrict__ idx_top, int* __restrict__ idx,
-                                          Counts cnt, int nL, int Ktop, int K, float scale,
-                                          float* smem, int gh, int p)
+                                          Counts cnt, int nL, int n_l, int Ktop, int K,
+                                          float scale, float* smem, int gh, int p)
 {
     const int M = BS * Ktop;          // candidates of a level-(L-1) row
     float* sc = smem;                 // [16][M]
@@ -398,7 +405,6 @@ __device__ __forceinline__ void top2_rows(const float* __restrict__ qtop,
     int* pc = cand + M;               // [M]
     float* st = (float*)(pc + M);     // [nL] scores of row p
     int* picks = (int*)(st + nL);     // [Ktop]
-    const int n_l = BS * nL;
     for (int c = threadIdx.x; c < M; c += blockDim.x) pc[c] = 0;
     // row p's scores: eight lanes per candidate, lane u reading 16-byte
     // pieces u, u + 8, ... of the rows (query row p and key rows), so each
@@ -445,13 +451,15 @@ __device__ __forceinline__ void top2_rows(const float* __restrict__ qtop,
     __syncthreads();
     // the children's query operand (loaded only now: phase-A registers are
     // free again, and its latency overlaps the first key tile's)
+    // the children rows 16p .. (fewer under the partial last block)
+    const int rows = min(BS, n_l - BS * p);
     float qa[D / 4];
-    load_query_operand<D>(qa, qbar, (long)gh * n_l + BS * p, BS);
+    load_query_operand<D>(qa, qbar, (long)gh * n_l + BS * p, rows);
     for (int c = threadIdx.x; c < M; c += blockDim.x) cand[c] = BS * picks[c / BS] + (c % BS);
     __syncthreads();
-    score_select16<KPG, D>(qa, kbar + (long)gh * n_l * D, idx + ((long)gh * n_l + BS * p) * K, BS,
-                           M, K, scale, sc, cand, pc,
-                           {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)});
+    score_select16<KPG, D>(qa, kbar + (long)gh * n_l * D, idx + ((long)gh * n_l + BS * p) * K,
+                           rows, M, K, scale, sc, cand, pc,
+                           {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)}, n_l);
 }
 
 template <int KPL, int KPG, int D>
@@ -461,12 +469,12 @@ __global__ __launch_bounds__(256) void select_top2(const float* __restrict__ qto
                                                    const float* __restrict__ kbar,
                                                    int* __restrict__ idx_top,
                                                    int* __restrict__ idx, Counts cnt,
-                                                   int nL, int Ktop, int K,
+                                                   int nL, int n_l, int Ktop, int K,
                                                    float scale)
 {
     extern __shared__ float smem[];
-    top2_rows<KPL, KPG, D>(qtop, ktop, qbar, kbar, idx_top, idx, cnt, nL, Ktop, K, scale, smem,
-                           blockIdx.x / nL, blockIdx.x % nL);
+    top2_rows<KPL, KPG, D>(qtop, ktop, qbar, kbar, idx_top, idx, cnt, nL, n_l, Ktop, K, scale,
+                           smem, blockIdx.x / nL, blockIdx.x % nL);
 }
 
 template <int KPG, int D>
@@ -498,8 +506,8 @@ hipError_t launch_top2(const Geo& g, const Ws& w, hipStream_t st)
     }
     hipLaunchKernelGGL((select_top2<KPL, KPG, D>), dim3(g.G * nL), dim3(256), lds, st,
                        w.qbar[L - 1], w.kbar[L - 1], w.qbar[L - 2], w.kbar[L - 2], w.idx[L - 1],
-                       w.idx[L - 2], Counts{w.cnt[L - 2], w.c16[L - 2]}, nL, g.Kl[L],
-                       g.Kl[L - 1], g.scale);
+                       w.idx[L - 2], Counts{w.cnt[L - 2], w.c16[L - 2]}, nL, g.n[L - 1],
+                       g.Kl[L], g.Kl[L - 1], g.scale);
     return hipGetLastError();
 }
 

@@ -156,7 +156,9 @@ __device__ __forceinline__ void transpose_block(const Geo& g, const Ws& w, int l
         cm = 0;
         if (c < cs.n) {
             ci = cs.row(c);
-            cm = hit_mask(I + (long)ci * K, K, grp, &cfirst);
+            // a child past the level's last block (the parent may be the
+            // partial last block) does not exist and chose nothing
+            if (ci < n) cm = hit_mask(I + (long)ci * K, K, grp, &cfirst);
         }
     };
     probe(0);

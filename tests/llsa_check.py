@@ -71,7 +71,7 @@ def gpu_run(w, inp, flags=0, backward=True, q64=None):
     res["idx"], res["qbar"], res["kbar"], res["vbar"] = [], [], [], []
     res["rowptr"], res["col"] = [], []
     for l in range(1, w.levels + 1):
-        n = N // BS ** l
+        n = -(-N // BS ** l)  # the last block of a level may be partial
         K = level_k(w, l)
         res["idx"].append(ws_array(ws, lay["idx"][l - 1], G * n * K, np.int32)
                           .reshape(G, n, K))
@@ -177,7 +177,7 @@ def check_selection(w, gpu, orc_pyr, exact: bool):
         # every GPU row is a valid selection: ascending, distinct, children of parent
         assert np.all(np.diff(got, axis=2) > 0)
         if parent is not None:
-            par = np.repeat(parent, BS, axis=1)
+            par = np.repeat(parent, BS, axis=1)[:, :got.shape[1]]
             assert np.all(np.any((got[..., :, None] // BS) == par[..., None, :], axis=3))
         diffs += int(bad.sum())
     return diffs

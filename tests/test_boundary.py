@@ -2,8 +2,9 @@
 
 The library must load, export every function declared in include/llsa.h, and
 reject bad arguments before any HIP call.  The README's usage notes limit the
-token count and top-k to powers of two; this library accepts any N that
-16^levels divides and any topk up to the coarsest block count.
+token count and top-k to powers of two; this library accepts any N that 16
+divides (a partial last block at the coarser levels) and any top-k up to the
+candidates a row of its level may have.
 """
 import ctypes
 import os
@@ -200,3 +201,24 @@ def test_noalloc_forward_refuses_oversized_shapes_before_any_launch():
     assert lib.llsa_forward_noalloc(*args, 1, 6, 4008, 64, 16, 16, 1, L.BF16, 0, None) == -2
     assert lib.llsa_forward_noalloc(*args, 1, 6, 4096, 96, 16, 16, 1, L.BF16, 0, None) == -3
     assert "scratch" in L.llsa_strerror(-6)
+
+
+@pytest.mark.parametrize("N,K,Lv,ok", [
+    (336, (4, 2), 2, True),     # 21 level-1 blocks, level-2 blocks of 16 and 5
+    (336, (21, 2), 2, True),    # a level-1 row may have 16 + 5 = 21 candidates
+    (336, (22, 2), 2, False),
+    (336, (4, 3), 2, False),    # only 2 level-2 blocks
+    (336, (5, 1), 2, True),     # a row under the partial block has 5 candidates
+    (336, (6, 1), 2, False),
+    (10000, (16, 16), 2, True), # 100 x 100: 625 level-1 and 40 level-2 blocks
+    (4800, (8, 4, 2), 3, True), # 300 / 19 / 2 blocks
+    (4808, (4, 2), 2, False),   # not a multiple of 16
+])
+def test_token_counts_that_16_to_the_levels_does_not_divide(N, K, Lv, ok):
+    nb = L.llsa_workspace_bytes_lk(1, 2, N, 64, 16, list(K), Lv, L.BF16)
+    assert (nb > 0) == ok
+    lib = L.load()
+    arr = (ctypes.c_int * Lv)(*K)
+    rc = lib.llsa_forward_lk(BAD, BAD, BAD, BAD, BAD, 1, 2, N, 64, 16, arr, Lv, L.BF16, 0, BAD, 0,
+                             None)
+    assert rc == (-4 if ok else -2)  # a valid shape then fails on the missing workspace

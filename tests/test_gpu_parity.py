@@ -198,6 +198,29 @@ def test_top_k_per_level(w, flags):
     _full_check(w, flags=flags)
 
 
+# token counts that 16^levels does not divide (a multiple of 16): partial
+# last blocks at the coarser levels, whose pooled tokens average fewer tokens,
+# and rows whose parent is such a block, which have fewer candidates
+_PADDED = [
+    (_grid("grid16x21_bf16_l2_k4x2", "bf16", 2, (4, 2), 21, height=16), 0),      # N = 336
+    (_grid("grid16x21_f32_l2_k4x2", "f32", 2, (4, 2), 21, height=16), 0),
+    (_grid("grid16x21_bf16_l2_k5x1", "bf16", 2, (5, 1), 21, height=16), 0),      # 5 candidates
+    (_grid("grid16x21_bf16_l2_k21x2", "bf16", 2, (21, 2), 21, height=16, H=1), 0),  # every block
+    (_grid("grid16x21_bf16_l2_k4x2", "bf16", 2, (4, 2), 21, height=16), oracle.SIZE_BIAS),
+    (_grid("grid16x21_bf16_l2_k4x2", "bf16", 2, (4, 2), 21, height=16), oracle.ENRICH_COARSE),
+    (_grid("rect100x100_bf16_l2_k16", "bf16", 2, 16, 100, height=100), 0),       # N = 10000
+    (_grid("rect60x80_bf16_l3_k8x4x2", "bf16", 3, (8, 4, 2), 80, height=60), 0),  # N = 4800
+    (_grid("rect60x80_f32_l3_k8x4x2", "f32", 3, (8, 4, 2), 80, height=60, H=1), 0),
+    (_grid("rect100x100_bf16_l2_k16_d128", "bf16", 2, 16, 100, height=100, d=128), 0),
+    (_grid("rect100x100_bf16_l2_k16", "bf16", 2, 16, 100, height=100), oracle.NO_ENRICH),
+]
+
+
+@pytest.mark.parametrize("w,flags", _PADDED, ids=["%s_f%d" % (w.name, f) for w, f in _PADDED])
+def test_token_counts_beyond_16_to_the_levels(w, flags):
+    _full_check(w, flags=flags)
+
+
 # head dimension 128 (the one-block bf16 kernels and the fp32 kernels)
 _D128 = [
     (_grid("grid32_f32_l1_k8_d128", "f32", 1, 8, 32, H=1, d=128), 0),
@@ -461,6 +484,9 @@ _FULL = [synth.WORKLOADS[n] for n in (
     # the deepest pyramids N <= 2^23 allows: 4 and 5 levels down to one block
     _grid("grid256_bf16_l4_k1", "bf16", 4, 1, 256, H=1),
     _grid("grid1024_bf16_l5_k1", "bf16", 5, 1, 1024, H=1),
+    # 200 x 200 (N = 40000): 2500 level-1 and 157 level-2 blocks, the last
+    # of which covers 4 level-1 blocks
+    _grid("rect200x200_bf16_l2_k16", "bf16", 2, 16, 200, height=200, H=6, sigma=4.0),
 ]
 
 
