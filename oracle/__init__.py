@@ -18,6 +18,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 NO_ENRICH = 1
 ENRICH_COARSE = 2
 SIZE_BIAS = 4
+ENRICH_COMPLEMENT = 8
 
 _lib = None
 

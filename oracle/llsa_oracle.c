@@ -272,17 +272,56 @@ static int64_t kv_set(const double* k, const double* v, const double* kpyr,
     if (!(flags & ORC_NO_ENRICH))
         for (int l = (flags & ORC_ENRICH_COARSE) ? 2 : 1; l <= L; ++l) {
             int64_t n_l = nblk(N, bs, l), a = t / ipow(bs, l);
+            const double* kl = kpyr + lvl_off(G, N, bs, l, d);
+            const double* vl = vpyr + lvl_off(G, N, bs, l, d);
             const int32_t* sel = idx + idx_off(G, N, bs, l, K) + (g * n_l + a) * K[l - 1];
-            for (int64_t p = 0; p < K[l - 1]; ++p) {
-                int64_t j = sel[p];
-                key[ne] = kpyr + lvl_off(G, N, bs, l, d) + (g * n_l + j) * d;
-                val[ne] = vpyr + lvl_off(G, N, bs, l, d) + (g * n_l + j) * d;
+            if (!(flags & ORC_ENRICH_COMPLEMENT)) {
+                /* the pooled tokens of the blocks the ancestor picked */
+                for (int64_t p = 0; p < K[l - 1]; ++p) {
+                    int64_t j = sel[p];
+                    key[ne] = kl + (g * n_l + j) * d;
+                    val[ne] = vl + (g * n_l + j) * d;
+                    tag[ne] = l;
+                    ref[ne] = j;
+                    ++ne;
+                }
+                continue;
+            }
+            /* the pooled tokens of the ancestor's candidates that it did not
+             * pick: every block at the coarsest level, below it the existing
+             * children of the parent's picks; ascending */
+            int64_t nc = n_l, Kp = 0;
+            const int32_t* par = NULL;
+            if (l < L) {
+                int64_t n_p = nblk(N, bs, l + 1);
+                Kp = K[l];
+                par = idx + idx_off(G, N, bs, l + 1, K) + (g * n_p + a / bs) * Kp;
+                nc = bs * Kp;
+            }
+            for (int64_t c = 0; c < nc; ++c) {
+                const int64_t j = par ? bs * par[c / bs] + c % bs : c;
+                if (j >= n_l) continue;  /* the partial last parent has fewer children */
+                int picked = 0;
+                for (int64_t p = 0; p < K[l - 1]; ++p) picked |= sel[p] == j;
+                if (picked) continue;
+                key[ne] = kl + (g * n_l + j) * d;
+                val[ne] = vl + (g * n_l + j) * d;
                 tag[ne] = l;
                 ref[ne] = j;
                 ++ne;
             }
         }
     return ne;
+}
+
+/* Entries a token's key/value set may hold: the fine tokens, then per level
+ * the picks, or with ORC_ENRICH_COMPLEMENT the candidates. */
+static int64_t max_entries(int64_t N, int64_t bs, int L, const int64_t* K, unsigned flags)
+{
+    int64_t m = bs * K[0];
+    for (int l = 1; l <= L; ++l)
+        m += (flags & ORC_ENRICH_COMPLEMENT) ? (l == L ? nblk(N, bs, l) : bs * K[l]) : K[l - 1];
+    return m;
 }
 
 /* ------------------------------------------------------------- forward */
@@ -293,8 +332,7 @@ void orc_forward(const double* q, const double* k, const double* v,
                  double scale, unsigned flags, const int64_t* qblocks,
                  int64_t nq, double* out, double* lse)
 {
-    int64_t n1 = nblk(N, bs, 1), maxe = bs * K[0];
-    for (int l = 1; l <= L; ++l) maxe += K[l - 1];
+    int64_t n1 = nblk(N, bs, 1), maxe = max_entries(N, bs, L, K, flags);
     const double** key = (const double**)malloc((size_t)maxe * sizeof(double*));
     const double** val = (const double**)malloc((size_t)maxe * sizeof(double*));
     int* tag = (int*)malloc((size_t)maxe * sizeof(int));
@@ -337,8 +375,7 @@ void orc_backward(const double* q, const double* k, const double* v,
                   int64_t nq, const int64_t* kblocks, int64_t nk, double* dq,
                   double* dk, double* dv)
 {
-    int64_t n1 = nblk(N, bs, 1), maxe = bs * K[0];
-    for (int l = 1; l <= L; ++l) maxe += K[l - 1];
+    int64_t n1 = nblk(N, bs, 1), maxe = max_entries(N, bs, L, K, flags);
     const double** key = (const double**)malloc((size_t)maxe * sizeof(double*));
     const double** val = (const double**)malloc((size_t)maxe * sizeof(double*));
     int* tag = (int*)malloc((size_t)maxe * sizeof(int));
@@ -374,17 +411,16 @@ void orc_backward(const double* q, const double* k, const double* v,
                     }
 
         for (int64_t i = 0; i < n1; ++i) {
-            /* skip query blocks that contribute to no requested output */
+            /* skip query blocks that contribute to no requested output (all
+             * tokens of block i share one key/value set) */
             int need = want_q[i];
-            const int32_t* sel1 = idx + (g * n1 + i) * K[0];
-            for (int64_t p = 0; p < K[0] && !need; ++p) need = want_k[sel1[p]];
-            if (!(flags & ORC_NO_ENRICH))
-                for (int l = 1; l <= L && !need; ++l) {
-                    int64_t n_l = nblk(N, bs, l), a = (bs * i) / ipow(bs, l);
-                    const int32_t* sel = idx + idx_off(G, N, bs, l, K) + (g * n_l + a) * K[l - 1];
-                    for (int64_t p = 0; p < K[l - 1] && !need; ++p)
-                        need = want_p[lvl_off(1, N, bs, l, 1) + sel[p]];
-                }
+            if (!need) {
+                int64_t ne = kv_set(k, v, kpyr, vpyr, idx, g, bs * i, G, N, d, bs, L, K, flags,
+                                    key, val, tag, ref);
+                for (int64_t e = 0; e < ne && !need; ++e)
+                    need = tag[e] == 0 ? want_k[ref[e] / bs]
+                                       : want_p[lvl_off(1, N, bs, tag[e], 1) + ref[e]];
+            }
             if (!need) continue;
 
             for (int64_t t = bs * i; t < bs * (i + 1) && t < N; ++t) {

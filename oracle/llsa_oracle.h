@@ -50,6 +50,8 @@ extern "C" {
 #define ORC_NO_ENRICH 1u     /* fine tokens only */
 #define ORC_ENRICH_COARSE 2u /* pooled tokens of levels 2..L only */
 #define ORC_SIZE_BIAS 4u     /* a level-l pooled logit gets + ln bs^l */
+#define ORC_ENRICH_COMPLEMENT 8u /* the pooled tokens of the candidates a level did
+                                    NOT pick, instead of those it picked */
 
 /* Morton (Z-order) position of raster cell (y, x) on a side x side grid,
  * side a power of two: bits of y and x interleaved, the y bit above the x
@@ -104,7 +106,11 @@ void orc_select(const double* qpyr, const double* kpyr, int64_t G, int64_t N,
  * For token t with query block i = t/bs and level-l ancestor a_l = t/bs^l the
  * key/value set is the bs*K[0] tokens of the blocks idx_1[i] plus (unless
  * ORC_NO_ENRICH) the pooled pairs (kbar_l[j], vbar_l[j]) for l = 1..L and
- * j in idx_l[a_l].  One softmax over that set with the given scale;
+ * j in idx_l[a_l] -- or, with ORC_ENRICH_COMPLEMENT, for j among the
+ * candidates of a_l that it did not pick (every level-L block; below L the
+ * existing children of the parent's picks).  The fine tokens and the
+ * complement's pooled tokens then cover every key token exactly once, each
+ * pooled token standing for the tokens it averages.  One softmax over that set with the given scale;
  * lse = m + ln(sum exp(z - m)).
  * qblocks: optional list of query blocks to compute (NULL = all of them, in
  * which case nq is ignored); rows not listed are left untouched. */

@@ -70,7 +70,7 @@ int main(void)
             double* dq = malloc(G * N * d * sizeof(double));
             double* dk = malloc(G * N * d * sizeof(double));
             double* dv = malloc(G * N * d * sizeof(double));
-            for (unsigned flags = 0; flags < 8; ++flags) {
+            for (unsigned flags = 0; flags < 16; ++flags) {
                 orc_forward(q, k, v, kp, vp, idx, G, N, d, bs, L, K, 0.3, flags, NULL, 0, o, lse);
                 orc_backward(q, k, v, kp, vp, idx, o, lse, dout, G, N, d, bs, L, K, 0.3, flags,
                              NULL, 0, NULL, 0, dq, dk, dv);
