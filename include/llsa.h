@@ -67,7 +67,14 @@ extern "C" {
 #define LLSA_ENRICH_COARSE 2u /* pooled tokens of levels 2..levels only */
 #define LLSA_SIZE_BIAS 4u     /* a level-l pooled token, the mean of 16^l tokens,
                                  counts as 16^l copies (logit + ln 16^l) */
-#define LLSA_KNOWN_FLAGS 7u
+#define LLSA_ENRICH_COMPLEMENT 8u /* the pooled tokens of the candidates each level did
+                                     NOT pick (every coarsest block not picked; below
+                                     it the parent's picks' children not picked):
+                                     with the fine tokens they cover every key token
+                                     once.  At most 2048 such entries per query block
+                                     (sum over the enriching levels of the candidate
+                                     counts), else LLSA_ERR_UNSUPPORTED */
+#define LLSA_KNOWN_FLAGS 15u
 
 /* error codes */
 #define LLSA_OK 0

@@ -46,6 +46,14 @@ int validate(int B, int H, int N, int d, int block_size, const int* ks, int leve
     for (int l = 0; l < levels; ++l)
         if (ks[l] > 64) return LLSA_ERR_UNSUPPORTED;
     if (nL > 4096) return LLSA_ERR_UNSUPPORTED;
+    if ((flags & LLSA_ENRICH_COMPLEMENT) && !(flags & LLSA_NO_ENRICH)) {
+        // the complement's entries per query block: the candidates of the
+        // enriching levels, at most 2048 (the entry table of the kernels)
+        long long m = 0;
+        for (int l = (flags & LLSA_ENRICH_COARSE) ? 2 : 1; l <= levels; ++l)
+            m += l == levels ? nL : (long long)BS * ks[l];
+        if (m > 2048) return LLSA_ERR_UNSUPPORTED;
+    }
     if ((long long)B * H * N >= (1ll << 31)) return LLSA_ERR_UNSUPPORTED;
     if (N > (1 << 23)) return LLSA_ERR_UNSUPPORTED;  // one head's tensor < 2 GiB (buffer offsets)
     return LLSA_OK;
@@ -128,6 +136,7 @@ void make_geo(int B, int H, int N, int d, const int* ks, int levels, unsigned fl
     g->flags = flags;
     g->l0 = (flags & LLSA_NO_ENRICH) ? levels + 1 : (flags & LLSA_ENRICH_COARSE) ? 2 : 1;
     g->lb2 = (flags & LLSA_SIZE_BIAS) ? 4.0f : 0.0f;  // log2(16^l) = 4 l
+    g->cmp = (flags & LLSA_ENRICH_COMPLEMENT) != 0;
     // The attention launches gather key/value (forward, dQ) or query/dO
     // (dK/dV) rows of every head.  While those of all heads fit well inside
     // the 256 MB MALL, each XCD takes one contiguous eighth of the launch

@@ -110,6 +110,7 @@ __device__ __forceinline__ void attend_pair(Online<D>& st, const bf16x8 (&bq)[Ti
 }
 
 constexpr int MAX_E = MAX_L * 64;  // pooled entries per query block (L * K)
+constexpr int CMP_E = 2048;        // the complement's entries per query block, at most
 
 // Per-wave LDS: two value tiles (160-byte rows), two key tiles (144-byte
 // rows) and the table of pooled-entry rows (ECAP ints).  With ECAP = 64 a
@@ -146,19 +147,10 @@ __device__ __forceinline__ void fwd_block(const unsigned short* __restrict__ q,
     // the query block's K fine blocks, one per lane (K <= 64)
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
     const int myj = lane < g.K ? clampi(sel[lane], g.n[1]) : 0;
-    // pooled entries e = eoff[l] + slot of the enriching levels l0..L: their
-    // rows in the bf16 pooled arrays
-    const int E = g.n_pooled();
+    // the pooled entries of the enriching levels: rows in the bf16 pooled
+    // arrays, with their level (fill_entries)
     int* ent = (int*)(sm + 2 * Lay::V_TILE + 2 * Lay::K_TILE);
-    for (int l = g.l0; l <= g.L; ++l) {
-        const int Kl = g.Kl[l];
-        const long a = (long)gh * g.n[l] + (i >> (4 * (l - 1)));
-        for (int s0 = 0; s0 < Kl; s0 += 64)
-            if (s0 + lane < Kl)
-                ent[g.eoff[l] + s0 + lane] =
-                    (int)(w.prow[l - 1] + (long)gh * g.n[l] +
-                          clampi(w.idx[l - 1][a * Kl + s0 + lane], g.n[l]));
-    }
+    const int E = fill_entries(g, w, gh, i, ent, lane);
     lds_fence();
 
     Online<D> st;
@@ -232,7 +224,7 @@ __device__ __forceinline__ void fwd_block(const unsigned short* __restrict__ q,
         // fine tile) or in the pooled copies; rows past the last entry
         // repeat a valid one (they are masked)
         if (t < NFT) return hbase + ((long)jlast * BS + r) * D;
-        return (long)ent[min(BS * (t - NFT) + r, E - 1)] * D;
+        return (long)(ent[min(BS * (t - NFT) + r, E - 1)] & ENT_ROW) * D;
     };
     for (int t = 0; t < NT; t += 2) {
         const int tb = min(t + 1, NT - 1);
@@ -266,8 +258,10 @@ __device__ __forceinline__ void fwd_block(const unsigned short* __restrict__ q,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int ea = BS * (t - NFT) + 4 * gq + r, eb = ea + BS;
-            ba[r] = t < NFT ? 0.f : g.lb2 * (float)g.entry_level(ea);
-            bb[r] = t + 1 < NFT ? 0.f : g.lb2 * (float)g.entry_level(eb);
+            ba[r] = (t < NFT || g.lb2 == 0.f) ? 0.f
+                    : g.lb2 * (float)ent_level(ent[max(0, min(ea, E - 1))]);
+            bb[r] = (t + 1 < NFT || g.lb2 == 0.f) ? 0.f
+                    : g.lb2 * (float)ent_level(ent[max(0, min(eb, E - 1))]);
         }
         attend_pair<true, D>(st, bq, ka, kb, la, lb, na, nb, c, lane, ba, bb);
     }

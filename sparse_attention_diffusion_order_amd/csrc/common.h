@@ -42,7 +42,17 @@ struct Geo {
     int l0;                // first level whose pooled tokens enrich (L + 1: none)
     float lb2;             // logit bias of a level-l pooled token: l * lb2 (log2 units)
     int xcd_chunk;         // workgroups per XCD chunk of the attention launches (xcd_block)
+    bool cmp;              // LLSA_ENRICH_COMPLEMENT: the unpicked candidates enrich
+    // pooled entries per query block: the picks of the enriching levels (their
+    // number), or with the complement at most the candidates of those levels
     __host__ __device__ int n_pooled() const { return l0 <= L ? eoff[L + 1] : 0; }
+    __host__ __device__ int max_pooled() const
+    {
+        if (!cmp || l0 > L) return n_pooled();
+        int m = 0;
+        for (int l = l0; l <= L; ++l) m += l == L ? n[L] : BS * Kl[l + 1];
+        return m;
+    }
     // tokens covered by block j of level l (16^l but for a partial last block)
     __host__ __device__ int tokens(int l, int j) const
     {
@@ -292,6 +302,81 @@ __device__ __forceinline__ f32x4 scores(const bf16x8 (&a)[TileShape<D>::NI],
 #pragma unroll
     for (int u = 0; u < TileShape<D>::NI; ++u) s = mfma32(a[u], b[u], s);
     return s;
+}
+
+// An entry of a query block's pooled-entry table (LDS): the row of the
+// pooled token in the bf16 pooled arrays, with its level in bits 28..30
+// (rows stay below 2^28: B*H*N < 2^31 tokens give fewer than 2^27 blocks).
+constexpr int ENT_ROW = (1 << 28) - 1;
+__device__ __forceinline__ int ent_level(int e) { return e >> 28; }
+
+// Fill the pooled-entry table of query block i (head gh) and return the
+// number of entries (the same in every lane of the wave).  Default: the
+// picks of its ancestor at every enriching level l0..L, level by level.
+// LLSA_ENRICH_COMPLEMENT: at every enriching level the ancestor's candidates
+// it did not pick -- all blocks at the coarsest level, below it the existing
+// children of the parent's picks -- in ascending order, compacted by ballot.
+__device__ __forceinline__ int fill_entries(const Geo& g, const Ws& w, int gh, int i, int* ent,
+                                            int lane)
+{
+    int E = 0;
+    for (int l = g.l0; l <= g.L; ++l) {
+        const int Kl = g.Kl[l], nl = g.n[l];
+        const int a = i >> (4 * (l - 1));
+        const int* sel = w.idx[l - 1] + ((long)gh * nl + a) * Kl;
+        const long row0 = w.prow[l - 1] + (long)gh * nl;
+        if (!g.cmp) {
+            for (int s0 = 0; s0 < Kl; s0 += 64)
+                if (s0 + lane < Kl)
+                    ent[E + s0 + lane] = (int)(row0 + clampi(sel[s0 + lane], nl)) | (l << 28);
+            E += Kl;
+            continue;
+        }
+        // the ancestor's picks, one per lane (Kl <= 64)
+        const int mine = lane < Kl ? clampi(sel[lane], nl) : -1;
+        const int M = l == g.L ? nl : BS * g.Kl[l + 1];
+        const int* par = l == g.L ? nullptr
+                                  : w.idx[l] + ((long)gh * g.n[l + 1] + (a >> 4)) * g.Kl[l + 1];
+        const unsigned long long below = (1ull << lane) - 1ull;
+        for (int c0 = 0; c0 < M; c0 += 64) {
+            const int c = c0 + lane;
+            int j = nl;
+            if (c < M) j = par ? BS * clampi(par[c >> 4], g.n[l + 1]) + (c & 15) : c;
+            bool keep = j < nl;  // past the level's last block: no such child
+            for (int p = 0; p < Kl; ++p) keep = keep && j != __builtin_amdgcn_readlane(mine, p);
+            const unsigned long long bal = __ballot(keep);
+            if (keep) ent[E + __popcll(bal & below)] = (int)(row0 + j) | (l << 28);
+            E += __popcll(bal);
+        }
+    }
+    return E;
+}
+
+// Visit the pooled entries of query block i (head gh), level by level, in
+// the order fill_entries lists them: f(level, block) (uniform in the wave;
+// the fp32 kernels).
+template <typename F>
+__device__ __forceinline__ void for_each_pooled(const Geo& g, const Ws& w, int gh, int i, F f)
+{
+    for (int l = g.l0; l <= g.L; ++l) {
+        const int Kl = g.Kl[l], nl = g.n[l];
+        const int a = i >> (4 * (l - 1));
+        const int* sel = w.idx[l - 1] + ((long)gh * nl + a) * Kl;
+        if (!g.cmp) {
+            for (int s = 0; s < Kl; ++s) f(l, clampi(sel[s], nl));
+            continue;
+        }
+        const int M = l == g.L ? nl : BS * g.Kl[l + 1];
+        const int* par = l == g.L ? nullptr
+                                  : w.idx[l] + ((long)gh * g.n[l + 1] + (a >> 4)) * g.Kl[l + 1];
+        for (int c = 0; c < M; ++c) {
+            const int j = par ? BS * clampi(par[c >> 4], g.n[l + 1]) + (c & 15) : c;
+            if (j >= nl) continue;
+            bool picked = false;
+            for (int s = 0; s < Kl; ++s) picked = picked || sel[s] == j;
+            if (!picked) f(l, j);
+        }
+    }
 }
 
 // ------------------------------------------------------------ launchers

@@ -132,6 +132,7 @@ __device__ __forceinline__ void dq_pair(f32x4 (&acc)[D / 16], const bf16x8 (&bq)
 }
 
 constexpr int MAX_E = MAX_L * 64;  // pooled entries per query block (sum of the levels' K)
+constexpr int CMP_E = 2048;        // the complement's entries per query block, at most
 
 // Per-wave LDS of dq: two key tiles (160-byte rows, read as operands and
 // transposed), two value tiles (144-byte rows) and the pooled-entry table.
@@ -188,19 +189,10 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
     const long tok = (long)gh * g.N + (long)i * BS + nq;
     if (gq == 0) w.delta[tok] = Dq;
     const float nl2 = -lse[tok] * LOG2E;
-    // pooled entries e = (l - l0) * K + slot of the enriching levels l0..L:
-    // their rows in the bf16 pooled arrays
-    const int E = g.n_pooled();
+    // the pooled entries of the enriching levels: rows in the bf16 pooled
+    // arrays, with their level (fill_entries)
     int* ent = (int*)(smem[wv] + 2 * Lay::K_TILE + 2 * Lay::V_TILE);
-    for (int l = g.l0; l <= g.L; ++l) {
-        const int Kl = g.Kl[l];
-        const long a = (long)gh * g.n[l] + (i >> (4 * (l - 1)));
-        for (int s0 = 0; s0 < Kl; s0 += 64)
-            if (s0 + lane < Kl)
-                ent[g.eoff[l] + s0 + lane] =
-                    (int)(w.prow[l - 1] + (long)gh * g.n[l] +
-                          clampi(w.idx[l - 1][a * Kl + s0 + lane], g.n[l]));
-    }
+    const int E = fill_entries(g, w, gh, i, ent, lane);
     lds_fence();
 
     f32x4 acc[D / 16] = {};
@@ -231,8 +223,8 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
             const int t = 2 * (p - NF);
 #pragma unroll
             for (int u = 0; u < NI; ++u) {
-                ka[u] = (long)ent[min(BS * t + sr + TS::RPI * u, E - 1)] * D + sc;
-                kb[u] = (long)ent[min(BS * t + BS + sr + TS::RPI * u, E - 1)] * D + sc;
+                ka[u] = (long)(ent[min(BS * t + sr + TS::RPI * u, E - 1)] & ENT_ROW) * D + sc;
+                kb[u] = (long)(ent[min(BS * t + BS + sr + TS::RPI * u, E - 1)] & ENT_ROW) * D + sc;
             }
             kp = w.kb16;
             vp = w.vb16;
@@ -268,14 +260,17 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
             const int na = p < NF ? BS : max(0, min(BS, E - e0));
             const int nb = p < NF ? 0 : max(0, min(BS, E - e0 - BS));
             const bool pooled = p >= NF;
-            float* pe = (pooled && g.l0 == 1 && e0 < g.K)
+            // the level-1 picks' pooled entries (the first K, by default)
+            // keep their P and dS for the key-major pass
+            float* pe = (pooled && g.l0 == 1 && !g.cmp && e0 < g.K)
                             ? w.pe1 + ((long)gh * g.n[1] + i) * g.K * 2 * BS : nullptr;
             float ba[4], bb[4];  // pooled rows: the logit bias of the entry's level
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int ea = e0 + 4 * gq + r;
-                ba[r] = pooled ? g.lb2 * (float)g.entry_level(ea) : 0.f;
-                bb[r] = pooled ? g.lb2 * (float)g.entry_level(ea + BS) : 0.f;
+                const bool bias = pooled && g.lb2 != 0.f;
+                ba[r] = bias ? g.lb2 * (float)ent_level(ent[max(0, min(ea, E - 1))]) : 0.f;
+                bb[r] = bias ? g.lb2 * (float)ent_level(ent[max(0, min(ea + BS, E - 1))]) : 0.f;
             }
             dq_pair<true, D>(acc, bq, bd, nl2, Dq, ka, kb, va, vb, la, lb, na, nb, c, lane, pe,
                              e0, g.K, ba, bb);
@@ -570,7 +565,7 @@ __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __re
     const long kblk = (long)xcd_block(blockIdx.x, gridDim.x, g.xcd_chunk) * WPG + wv;
     if (kblk >= (long)g.G * g.n[1]) return;
     const int gh = (int)(kblk / g.n[1]), j = (int)(kblk % g.n[1]);
-    const bool enrich1 = g.l0 == 1;  // level-1 pooled tokens enrich
+    const bool enrich1 = g.l0 == 1 && !g.cmp;  // level-1 picks' pooled tokens enrich
     const float c = g.scale * LOG2E;
     const long hbase = (long)gh * g.N * D;
     const long tbase = (long)gh * g.N;
@@ -691,7 +686,9 @@ __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __re
             xk[r] = accK[d][r] * g.scale;
             xv[r] = accV[d][r];
         }
-        for (int l = max(2, g.l0); l <= g.L; ++l) {
+        // pooled-token gradients of levels >= 2 (every enriching level with
+        // the complement, whose level-1 gradients also come from dbar)
+        for (int l = g.cmp ? g.l0 : max(2, g.l0); l <= g.L; ++l) {
             const int a = j >> (4 * (l - 1));
             const float wgt = 1.0f / (float)g.tokens(l, a);  // the mean's share of each token
             const float* db = w.dbar[l - 1] + ((long)gh * g.n[l] + a) * 2 * D + 16 * d + 4 * gq;
@@ -708,6 +705,188 @@ __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __re
         *(u16x4*)(dk + obase + 16 * d) = ok;
         *(u16x4*)(dv + obase + 16 * d) = ov;
     }
+}
+
+// ------------------------------------------- complement pooled-token gradients
+//
+// With LLSA_ENRICH_COMPLEMENT the pooled token j of level l is attended by
+// the query blocks under every level-l block a whose candidates hold j and
+// that did not pick it: every level-L block when l = L, below it the existing
+// children of the level-(l+1) blocks that picked j's parent (that level's
+// key->query list of the parent).  A workgroup takes 16 sibling pooled keys
+// 16p .. 16p+15 (they share these attendees), its four waves split the query
+// tiles (16 tokens each), and per tile
+//   S = Q Kbar^T, dP = dO Vbar^T (16x16x32 MFMA), P = exp(s S + bias - lse)
+//   with P = 0 in the columns of the keys the attendee picked,
+//   dS = P (dP - D), dVbar^T += dO^T P, dKbar^T += Q^T dS (16x16x16 MFMA).
+// The waves' sums are reduced in LDS in a fixed order.  At the coarsest level
+// the attendees are split further into `chunks` workgroups per group, whose
+// partial sums (in the level-1 pooled P/dS buffer, unused by this variant)
+// cmp_sum adds in chunk order; otherwise the sums go straight to dbar.
+template <int D>
+__global__ __launch_bounds__(256) void cmp_grad_bf16(const unsigned short* __restrict__ q,
+                                                     const float* __restrict__ lse,
+                                                     const unsigned short* __restrict__ dout,
+                                                     Geo g, Ws w, int l, int chunks)
+{
+    using TS = TileShape<D>;
+    constexpr int NI = TS::NI, ND = D / 16;
+    __shared__ __attribute__((aligned(16))) unsigned short tiles[4][2][TILE<D>];
+    __shared__ __attribute__((aligned(16))) float auxs[4][2 * BS];
+    float* red = (float*)&tiles[0][0][0];  // the cross-wave sums, after the last tile
+    static_assert(sizeof(tiles) >= 4 * ND * 4 * 64 * sizeof(float), "reduction buffer");
+    const int lane = threadIdx.x & 63, wv = uniform(threadIdx.x >> 6);
+    const int gq = lane >> 4, nq = lane & 15;
+    const int rr = (lane & 15) >> 2, xx = lane & 3;
+    const int nl = g.n[l], groups = (nl + BS - 1) / BS;
+    const int bid = blockIdx.x;
+    const int gh = bid / (groups * chunks), p = (bid / chunks) % groups, ck = bid % chunks;
+    const float c = g.scale * LOG2E;
+    const float lb = g.lb2 * (float)l;  // size bias of a level-l pooled token (log2)
+    // the 16 pooled keys (rows past the level's last block: the last row,
+    // their columns masked)
+    const bool col_ok = BS * p + nq < nl;
+    const long krow = w.prow[l - 1] + (long)gh * nl + min(BS * p + nq, nl - 1);
+    bf16x8 bk[NI], bv[NI];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+        bk[u] = *(const bf16x8*)(w.kb16 + krow * D + 32 * u + 8 * gq);
+        bv[u] = *(const bf16x8*)(w.vb16 + krow * D + 32 * u + 8 * gq);
+    }
+    // attendees of the group and their query tiles: tile z of the workgroup
+    // is tile z % tpa of attendee z / tpa
+    const int tpa = 1 << (4 * (l - 1));  // level-1 blocks under a level-l block
+    int na, a0 = 0;
+    const int* plist = nullptr;  // l < L: the parent level's key->query list of p
+    if (l == g.L) {
+        const int per = (nl + chunks - 1) / chunks;
+        a0 = ck * per;
+        na = max(0, min(per, nl - a0));
+    } else {
+        const int np = g.n[l + 1], kp = g.Kl[l + 1];
+        const int* rp = w.rowptr[l] + (long)gh * (np + 1);
+        const int tot = np * kp;
+        const int b = clampi(rp[p], tot + 1), e = max(b, clampi(rp[p + 1], tot + 1));
+        plist = w.col[l] + (long)gh * tot + b;
+        na = BS * (e - b);
+    }
+    const int Kl = g.Kl[l];
+    const int* Il = w.idx[l - 1] + (long)gh * nl * Kl;
+    const long hbase = (long)gh * g.N * D;
+    const unsigned head_bytes = (unsigned)g.N * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + hbase, head_bytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + hbase, head_bytes);
+    const int sr = lane / TS::LPR, scol = (lane % TS::LPR) * 8;
+    const int voff = (sr * D + scol) * 2;
+    unsigned short* lq = tiles[wv][0];
+    unsigned short* ld = tiles[wv][1];
+    float* aux = auxs[wv];
+    f32x4 accK[ND] = {}, accV[ND] = {};
+    const long ntile = (long)na * tpa;
+    for (long z = wv; z < ntile; z += 4) {
+        const int k = (int)(z / tpa), t = (int)(z % tpa);
+        const int a = l == g.L ? a0 + k : BS * clampi(plist[k >> 4], g.n[l + 1]) + (k & 15);
+        const int qb = a * tpa + t;  // the tile's level-1 query block
+        if (a >= nl || qb >= g.n[1]) continue;  // no such child / block (partial parent)
+        // the keys of the group this attendee picked (excluded)
+        int first;
+        const unsigned picked = hit_mask(Il + (long)clampi(a, nl) * Kl, Kl, p, &first);
+        const bool live = col_ok && !((picked >> nq) & 1u);
+        const int so = qb * (BS * D * 2);
+        bf16x8 xq[NI], xd[NI];
+#pragma unroll
+        for (int u = 0; u < NI; ++u) xq[u] = bload8(rq, voff + 1024 * u, so);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) xd[u] = bload8(rdo, voff + 1024 * u, so);
+        const long trow = (long)gh * g.N + (long)qb * BS;
+        const float rowv = lane < BS ? -LOG2E * lse[trow + lane]
+                                     : lane < 2 * BS ? w.delta[trow + lane - BS] : 0.f;
+        put_rows<D>(lq, xq, lane);
+        put_rows<D>(ld, xd, lane);
+        if (lane < 2 * BS) aux[lane] = rowv;
+        lds_fence();
+        const float4 l4 = *(const float4*)(aux + 4 * gq);
+        const float4 e4 = *(const float4*)(aux + BS + 4 * gq);
+        bf16x8 aq[NI], ad[NI];
+        operand_rows<D, TS::ROW_T>(lq, aq, lane);
+        operand_rows<D, TS::ROW_T>(ld, ad, lane);
+        const f32x4 sc = scores<D>(aq, bk);   // S[query][key]
+        const f32x4 dp = scores<D>(ad, bv);  // dP[query][key]
+        const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, dr[4] = {e4.x, e4.y, e4.z, e4.w};
+        bf16x4 bp, bs;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pr = live ? fast_exp2(fmaf(sc[r], c, lr[r] + lb)) : 0.f;
+            bp[r] = (bf16)pr;
+            bs[r] = (bf16)(pr * (dp[r] - dr[r]));
+        }
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+            const int off = (4 * gq + rr) * TS::ROW_T + 16 * d + 4 * xx;
+            accV[d] = mfma16(lds_read_tr(ld + off), bp, accV[d]);
+            accK[d] = mfma16(lds_read_tr(lq + off), bs, accK[d]);
+        }
+        wave_lds_sync();  // this tile's LDS reads are done before the next writes
+    }
+    // the four waves' sums in a fixed order, dK then dV
+    const int groups_all = g.G * groups;
+    for (int kind = 0; kind < 2; ++kind) {
+        __syncthreads();
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[((wv * ND + d) * 4 + r) * 64 + lane] = kind == 0 ? accK[d][r] : accV[d][r];
+        __syncthreads();
+        for (int x = threadIdx.x; x < ND * 4 * 64; x += blockDim.x) {
+            const float sum = red[x] + red[ND * 256 + x] + red[2 * ND * 256 + x] +
+                              red[3 * ND * 256 + x];
+            const int d = x >> 8, r = (x >> 6) & 3, ln = x & 63;
+            const int key = ln & 15, dim = 16 * d + 4 * (ln >> 4) + r;
+            const float val = kind == 0 ? sum * g.scale : sum;
+            if (chunks == 1) {
+                if (BS * p + key < nl)
+                    w.dbar[l - 1][(((long)gh * nl + BS * p + key) * 2 + kind) * D + dim] = val;
+            } else {  // partial of chunk ck: [chunk][group][key][kind][dim]
+                w.pe1[((((long)ck * groups_all + (long)gh * groups + p) * BS + key) * 2 + kind) *
+                          D + dim] = val;
+            }
+        }
+    }
+}
+
+// The coarsest level's complement gradients: the chunks' partial sums, added
+// in chunk order.  One thread per (key, kind, channel).
+template <int D>
+__global__ __launch_bounds__(256) void cmp_sum(Geo g, Ws w, int chunks)
+{
+    const int l = g.L, nl = g.n[l], groups = (nl + BS - 1) / BS;
+    const long groups_all = (long)g.G * groups;
+    const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= groups_all * BS * 2 * D) return;
+    const long gk = id / (2 * D);  // (head, group, key)
+    const int rest = (int)(id % (2 * D));
+    const long gg = gk / BS;
+    const int key = (int)(gk % BS);
+    const int gh = (int)(gg / groups), p = (int)(gg % groups);
+    if (BS * p + key >= nl) return;
+    float s = 0.f;
+    for (int ck = 0; ck < chunks; ++ck) s += w.pe1[(((long)ck * groups_all + gg) * BS + key) * 2 * D + rest];
+    w.dbar[l - 1][((long)gh * nl + BS * p + key) * 2 * D + rest] = s;
+}
+
+// Workgroups per group for the coarsest level's complement gradients: about
+// 256 query tiles each, bounded by the partial buffer (the level-1 pooled
+// P/dS array, G * n1 * K * 32 floats).
+int cmp_chunks(const Geo& g, int D)
+{
+    const int nl = g.n[g.L], groups = (nl + BS - 1) / BS;
+    const long tiles = (long)nl << (4 * (g.L - 1));
+    long want = (tiles + 255) / 256;
+    const long cap = ((long)g.G * g.n[1] * g.K * 2 * BS) / ((long)g.G * groups * BS * 2 * D);
+    want = want < cap ? want : cap;
+    want = want < nl ? want : nl;
+    return want < 1 ? 1 : (int)want;
 }
 
 // ------------------------------------------------------------ fp32 path
@@ -743,15 +922,10 @@ __device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const 
             f(k + row, v + row, 0.f);
         }
     // enriching levels l0..L; a level-lv token's logit gets lb2 * lv * ln 2
-    for (int lv = g.l0; lv <= g.L; ++lv) {
-        const int a = t >> (4 * lv);
-        const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.Kl[lv];
-        const float bias = g.lb2 * (float)lv * LN2;
-        for (int s = 0; s < g.Kl[lv]; ++s) {
-            long row = ((long)gh * g.n[lv] + clampi(sl[s], g.n[lv])) * D;
-            f(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, bias);
-        }
-    }
+    for_each_pooled(g, w, gh, t / BS, [&](int lv, int j) {
+        const long row = ((long)gh * g.n[lv] + j) * D;
+        f(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, g.lb2 * (float)lv * LN2);
+    });
 }
 
 // dq and delta: one wave per query token
@@ -812,10 +986,40 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
     const float bias = g.lb2 * (float)l * LN2;  // size bias of a level-l token
 #pragma unroll
     for (int c = 0; c < NC; ++c) sk[c] = sv[c] = 0.f;
+    // the level-l blocks whose tokens attend j: those that picked it (its
+    // key->query list), or with the complement those among whose candidates
+    // it is and that did not pick it -- every level-L block, below L the
+    // children of the level-(l+1) blocks that picked j's parent
     const int tot = g.n[l] * g.Kl[l];
-    const int beg = clampi(rp[j], tot + 1), end = max(beg, clampi(rp[j + 1], tot + 1));
+    int beg = clampi(rp[j], tot + 1), end = max(beg, clampi(rp[j + 1], tot + 1));
+    const int* pl = nullptr;  // the parent level's key->query list of j's parent
+    if (g.cmp) {
+        if (l == g.L) {
+            beg = 0;
+            end = g.n[l];
+        } else {
+            const int np = g.n[l + 1], kp = g.Kl[l + 1], ptot = np * kp;
+            const int* prp = w.rowptr[l] + (long)gh * (np + 1);
+            const int pb = clampi(prp[j >> 4], ptot + 1);
+            const int pe = max(pb, clampi(prp[(j >> 4) + 1], ptot + 1));
+            pl = w.col[l] + (long)gh * ptot + pb;
+            beg = 0;
+            end = BS * (pe - pb);
+        }
+    }
+    const int Kl = g.Kl[l];
     for (int e = beg; e < end; ++e) {
-        const long a = clampi(cl[e], g.n[l]);
+        long a;
+        if (!g.cmp) {
+            a = clampi(cl[e], g.n[l]);
+        } else {
+            a = l == g.L ? e : BS * clampi(pl[e >> 4], g.n[l + 1]) + (e & 15);
+            if (a >= g.n[l]) continue;
+            const int* sel = w.idx[l - 1] + ((long)gh * g.n[l] + a) * Kl;
+            bool picked = false;
+            for (int s = 0; s < Kl; ++s) picked = picked || sel[s] == j;
+            if (picked) continue;
+        }
         for (long t = a * span; t < (a + 1) * span && t < g.N; ++t) {
             const long tg = (long)gh * g.N + t;
             float qc[NC], dc[NC];
@@ -903,7 +1107,8 @@ hipError_t launch_attn_dq_d(const void* q, const void* k, const void* v, const v
 {
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
-        auto kern = (g.n_pooled() <= 64) ? dq_bf16<64, D> : dq_bf16<MAX_E, D>;
+        const int me = g.max_pooled();
+        auto kern = me <= 64 ? dq_bf16<64, D> : me <= MAX_E ? dq_bf16<MAX_E, D> : dq_bf16<CMP_E, D>;
         hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
                            (const unsigned short*)q, (const unsigned short*)k,
                            (const unsigned short*)v, (const unsigned short*)out, lse,
@@ -922,7 +1127,7 @@ hipError_t launch_attn_dq_tr_d(const void* q, const void* k, const void* v, cons
                                const float* lse, const void* dout, void* dq, const Geo& g,
                                const Ws& w, hipStream_t st)
 {
-    if (D == D128 || g.n_pooled() > 64) {
+    if (D == D128 || g.max_pooled() > 64) {
         // two launches at d = 128: there only two workgroups fit a CU, and the
         // transpose's long, mostly idle workgroups would hold dQ's slots (and
         // the large-entry variant has no registers to spare)
@@ -947,6 +1152,24 @@ hipError_t launch_attn_enrich_d(const void* q, const float* lse, const void* dou
                                 const Geo& g, const Ws& w, hipStream_t st)
 {
     if (g.l0 > g.L) return hipSuccess;
+    if (dtype == LLSA_BF16 && g.cmp) {  // the complement's pooled tokens, every enriching level
+        hipError_t e = hipSuccess;
+        for (int l = g.l0; l <= g.L && e == hipSuccess; ++l) {
+            const int groups = (g.n[l] + BS - 1) / BS;
+            const int chunks = l == g.L ? cmp_chunks(g, D) : 1;
+            hipLaunchKernelGGL(cmp_grad_bf16<D>, dim3((unsigned)(g.G * groups * chunks)), dim3(256),
+                               0, st, (const unsigned short*)q, lse, (const unsigned short*)dout, g,
+                               w, l, chunks);
+            e = hipGetLastError();
+            if (e == hipSuccess && chunks > 1) {
+                const long n = (long)g.G * groups * BS * 2 * D;
+                hipLaunchKernelGGL(cmp_sum<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g,
+                                   w, chunks);
+                e = hipGetLastError();
+            }
+        }
+        return e;
+    }
     if (dtype == LLSA_BF16) {
         if (g.L < 2) return hipSuccess;
         hipLaunchKernelGGL(enrich_bwd_bf16<D>, dim3(g.G * g.n[2]), dim3(256), 0, st,

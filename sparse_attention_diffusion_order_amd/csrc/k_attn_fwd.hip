@@ -350,15 +350,11 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
             const long row = ((long)gh * g.N + (long)clampi(sel[s], g.n[1]) * BS + r) * D;
             visit(k + row, v + row, 0.f);
         }
-    for (int lv = g.l0; lv <= g.L; ++lv) {  // pooled tokens of the enriching levels
-        const int a = t >> (4 * lv);
-        const int* sl = w.idx[lv - 1] + ((long)gh * g.n[lv] + a) * g.Kl[lv];
-        const float bias = g.lb2 * (float)lv * LN2;
-        for (int s = 0; s < g.Kl[lv]; ++s) {
-            const long row = ((long)gh * g.n[lv] + clampi(sl[s], g.n[lv])) * D;
-            visit(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, bias);
-        }
-    }
+    // pooled tokens of the enriching levels
+    for_each_pooled(g, w, gh, t / BS, [&](int lv, int j) {
+        const long row = ((long)gh * g.n[lv] + j) * D;
+        visit(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, g.lb2 * (float)lv * LN2);
+    });
 #pragma unroll
     for (int c = 0; c < NC; ++c) out[tg * D + lane + 64 * c] = o[c] / l;
     if (lane == 0) lse[tg] = m + logf(l);
@@ -372,14 +368,16 @@ hipError_t launch_attn_fwd_d(const void* q, const void* k, const void* v, void* 
         long nblk = (long)g.G * g.n[1];
         // the four-block kernel (d = 64): every fine list and every pooled
         // list fit one 16-entry tile
-        bool fits = D == D64 && g.K <= BS && g.n[1] % 4 == 0;
+        bool fits = D == D64 && g.K <= BS && g.n[1] % 4 == 0 && !g.cmp;
         for (int l = g.l0; l <= g.L; ++l) fits = fits && g.Kl[l] <= BS;
         if (fits) {
             hipLaunchKernelGGL(attn_fwd_u4, dim3((unsigned)((nblk + 15) / 16)), dim3(256), 0, st,
                                (const unsigned short*)q, (const unsigned short*)k,
                                (const unsigned short*)v, (unsigned short*)out, lse, g, w);
         } else {
-            auto kern = (g.n_pooled() <= 64) ? attn_fwd_bf16<64, D> : attn_fwd_bf16<MAX_E, D>;
+            const int me = g.max_pooled();
+            auto kern = me <= 64 ? attn_fwd_bf16<64, D>
+                      : me <= MAX_E ? attn_fwd_bf16<MAX_E, D> : attn_fwd_bf16<CMP_E, D>;
             hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + 3) / 4)), dim3(256), 0, st,
                                (const unsigned short*)q, (const unsigned short*)k,
                                (const unsigned short*)v, (unsigned short*)out, lse, g, w);

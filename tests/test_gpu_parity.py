@@ -221,6 +221,46 @@ def test_token_counts_beyond_16_to_the_levels(w, flags):
     _full_check(w, flags=flags)
 
 
+# the complement variant: the pooled tokens of the candidates a level did
+# not pick (oracle.ENRICH_COMPLEMENT), alone and with the other flags
+_CMP = oracle.ENRICH_COMPLEMENT
+_COMPLEMENT = [
+    (SMALL[0], _CMP), (SMALL[0], _CMP | _SIZE),                        # fp32, one level
+    (SMALL[1], _CMP), (SMALL[1], _CMP | _SIZE | _COARSE),              # fp32, two levels
+    (SMALL[4], _CMP), (SMALL[4], _CMP | _SIZE), (SMALL[4], _CMP | _COARSE),
+    (SMALL[5], _CMP),                                                  # three levels, topk 1
+    (synth.WORKLOADS["grid64_bf16_l1_k16"], _CMP),                     # 240 entries per block
+    (_grid("grid16x21_bf16_l2_k4x2", "bf16", 2, (4, 2), 21, height=16), _CMP),  # padded
+    (_grid("rect60x80_bf16_l3_k8x4x2", "bf16", 3, (8, 4, 2), 80, height=60), _CMP | _SIZE),
+    (_grid("grid64_bf16_l2_k4_d128", "bf16", 2, 4, 64, d=128), _CMP),
+    (synth.WORKLOADS["grid128_bf16_l2_k16"], _CMP),
+]
+
+
+@pytest.mark.parametrize("w,flags", _COMPLEMENT,
+                         ids=["%s_f%d" % (w.name, f) for w, f in _COMPLEMENT])
+def test_complement_enrichment(w, flags):
+    _full_check(w, flags=flags)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_complement_with_zero_queries_averages_every_token(dtype):
+    """Q = 0 with the complement and size-weighted logits: the fine tokens and
+    the unpicked candidates' pooled tokens cover every key token once, so
+    every output is the mean of all N values and lse = ln N (a closed form,
+    independent of the oracle)."""
+    w = small("zeroq_cmp", 1, 2, 64, dtype, 2, 4)
+    inp = synth.make_inputs(w)
+    inp["q"] = np.zeros_like(inp["q"])
+    inp["q64"] = np.zeros_like(inp["q64"])
+    gpu = gpu_run(w, inp, flags=_CMP | _SIZE, backward=False)
+    z = oracle_inputs(w, inp)
+    want = np.broadcast_to(z["v"].mean(axis=1, keepdims=True), z["v"].shape)
+    tol = TOL[dtype]
+    assert_close(gpu["out"], want, tol["out_max"], tol["out_mean"], "out")
+    assert_close(gpu["lse"], np.full_like(gpu["lse"], np.log(w.N)), tol["out_max"], what="lse")
+
+
 # head dimension 128 (the one-block bf16 kernels and the fp32 kernels)
 _D128 = [
     (_grid("grid32_f32_l1_k8_d128", "f32", 1, 8, 32, H=1, d=128), 0),
@@ -495,6 +535,13 @@ def test_full_size(w):
     """Full-size workloads: pyramid, selection, transposes, out, lse and
     every gradient against the oracle, element by element, all heads."""
     _full_check(w)
+
+
+@pytest.mark.parametrize("w", [synth.WORKLOADS["grid256_bf16_l2_k16"]], ids=lambda w: w.name)
+def test_full_size_complement(w):
+    """The complement variant at 256 x 256 (496 pooled entries per query
+    block), element by element, all heads."""
+    _full_check(w, flags=oracle.ENRICH_COMPLEMENT)
 
 
 # the largest N the boundary accepts (2^23 tokens, 1 GiB per head and
