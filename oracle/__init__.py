@@ -19,6 +19,7 @@ NO_ENRICH = 1
 ENRICH_COARSE = 2
 SIZE_BIAS = 4
 ENRICH_COMPLEMENT = 8
+CAUSAL = 16
 
 _lib = None
 
@@ -49,8 +50,8 @@ def _load():
         lib.orc_grid_index.restype = I
         lib.orc_grid_order.argtypes = [P, P, I, I, I, I, I, ctypes.c_int]
         lib.orc_pool.argtypes = [P, I, I, I, I, ctypes.c_int, P]
-        lib.orc_select_level.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P]
-        lib.orc_select.argtypes = [P, P, I, I, I, I, ctypes.c_int, P, D, P, P]
+        lib.orc_select_level.argtypes = [P, P, P, I, I, I, I, I, I, D, ctypes.c_int, P, P]
+        lib.orc_select.argtypes = [P, P, I, I, I, I, ctypes.c_int, P, D, ctypes.c_int, P, P]
         lib.orc_forward.argtypes = [P, P, P, P, P, P, I, I, I, I, ctypes.c_int, P, D,
                                     ctypes.c_uint, P, I, P, P]
         lib.orc_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, ctypes.c_int,
@@ -170,9 +171,10 @@ def _ks(idx):
     return np.ascontiguousarray([x.shape[2] for x in idx], dtype=np.int64)
 
 
-def select_level(qbar, kbar, parent, K: int, bs: int, scale: float):
+def select_level(qbar, kbar, parent, K: int, bs: int, scale: float, causal: bool = False):
     """One level of Top-K; returns (idx [G, n, K] int32, gap [G, n]).  The
-    parent rows may hold another count of picks than K."""
+    parent rows may hold another count of picks than K.  causal: each row
+    keeps itself and its best K-1 earlier candidates (-1 in unused slots)."""
     qbar, kbar = _f64(qbar), _f64(kbar)
     G, n, d = qbar.shape
     par = None if parent is None else _i32(parent)
@@ -182,11 +184,11 @@ def select_level(qbar, kbar, parent, K: int, bs: int, scale: float):
     idx = np.zeros((G, n, K), np.int32)
     gap = np.zeros((G, n))
     _load().orc_select_level(_p(qbar), _p(kbar), _p(par), G, n, d, bs, K, Kp, scale,
-                             _p(idx), _p(gap))
+                             int(causal), _p(idx), _p(gap))
     return idx, gap
 
 
-def select(qpyr, kpyr, K, bs: int, scale: float, N=None):
+def select(qpyr, kpyr, K, bs: int, scale: float, N=None, causal: bool = False):
     """All levels; K an int or one value per level (level 1 first); N: the
     token count (default: level 1's blocks times bs).  Returns (idx list per
     level 1..L, gap list per level)."""
@@ -194,13 +196,14 @@ def select(qpyr, kpyr, K, bs: int, scale: float, N=None):
     L = len(qpyr)
     N = n1 * bs if N is None else N
     ks = level_topk(K, L)
-    check_topk(N, bs, L, ks)
+    if not causal:  # causal rows may keep fewer picks (-1 in the slots left)
+        check_topk(N, bs, L, ks)
     sizes = level_sizes(N, bs, L)
     idx = np.zeros(G * sum(n * k for n, k in zip(sizes, ks)), np.int32)
     gap = np.zeros(G * sum(sizes))
     ka = np.ascontiguousarray(ks, dtype=np.int64)
     _load().orc_select(_p(_flat_levels(qpyr)), _p(_flat_levels(kpyr)), G, N, d, bs, L, _p(ka),
-                       scale, _p(idx), _p(gap))
+                       scale, int(causal), _p(idx), _p(gap))
     out, off = [], 0
     for n, k in zip(sizes, ks):
         out.append(idx[off:off + G * n * k].reshape(G, n, k))
@@ -260,7 +263,7 @@ def run(q, k, v, bs: int, L: int, K, flags: int = 0, dout=None, scale=None,
     qp, kp, vp = pool(q, bs, L), pool(k, bs, L), pool(v, bs, L)
     gap = None
     if idx is None:
-        idx, gap = select(qp, kp, K, bs, scale, N=N)
+        idx, gap = select(qp, kp, K, bs, scale, N=N, causal=bool(flags & CAUSAL))
     res = {"qpyr": qp, "kpyr": kp, "vpyr": vp, "idx": idx, "gap": gap, "scale": scale}
     if dout is None:
         res["out"], res["lse"] = forward(q, k, v, kp, vp, idx, bs, scale, flags, qblocks)

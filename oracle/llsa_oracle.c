@@ -187,24 +187,45 @@ static int int_cmp(const void* a, const void* b)
 
 void orc_select_level(const double* qbar, const double* kbar,
                       const int32_t* parent, int64_t G, int64_t n_l, int64_t d,
-                      int64_t bs, int64_t K, int64_t Kp, double scale, int32_t* idx,
-                      double* gap)
+                      int64_t bs, int64_t K, int64_t Kp, double scale, int causal,
+                      int32_t* idx, double* gap)
 {
     int64_t maxc = parent ? bs * Kp : n_l;
     cand_t* c = (cand_t*)malloc((size_t)maxc * sizeof(cand_t));
     for (int64_t g = 0; g < G; ++g)
         for (int64_t i = 0; i < n_l; ++i) {
-            /* candidate blocks of row i */
+            /* candidate blocks of row i (causal: only blocks before it; the
+             * block itself is chosen apart, below) */
             int64_t nc = 0;
             if (!parent) {
-                for (int64_t j = 0; j < n_l; ++j) c[nc++].j = (int32_t)j;
+                for (int64_t j = 0; j < (causal ? i : n_l); ++j) c[nc++].j = (int32_t)j;
             } else {
                 /* the children of the parent's picks that exist (the last
                  * parent block may have fewer than bs children) */
                 const int32_t* pr = parent + (g * ((n_l + bs - 1) / bs) + i / bs) * Kp;
                 for (int64_t p = 0; p < Kp; ++p)
-                    for (int64_t r = 0; r < bs; ++r)
-                        if (bs * pr[p] + r < n_l) c[nc++].j = (int32_t)(bs * pr[p] + r);
+                    for (int64_t r = 0; r < bs; ++r) {
+                        const int64_t j = bs * (int64_t)pr[p] + r;
+                        if (pr[p] < 0 || j >= n_l || (causal && j >= i)) continue;
+                        c[nc++].j = (int32_t)j;
+                    }
+            }
+            if (causal) {
+                /* the block itself, then the best K-1 earlier candidates (all
+                 * of them if fewer); unused slots hold -1 after the picks */
+                for (int64_t e = 0; e < nc; ++e)
+                    c[e].score = scale * dot(qbar + (g * n_l + i) * d,
+                                             kbar + (g * n_l + c[e].j) * d, d);
+                qsort(c, (size_t)nc, sizeof(cand_t), cand_cmp);
+                int32_t* row = idx + (g * n_l + i) * K;
+                const int64_t take = nc < K - 1 ? nc : K - 1;
+                for (int64_t e = 0; e < take; ++e) row[e] = c[e].j;
+                row[take] = (int32_t)i;
+                qsort(row, (size_t)(take + 1), sizeof(int32_t), int_cmp);
+                for (int64_t e = take + 1; e < K; ++e) row[e] = -1;
+                if (gap) gap[g * n_l + i] = nc > K - 1 && K > 1 ? c[K - 2].score - c[K - 1].score
+                                                                : INFINITY;
+                continue;
             }
             const double* qi = qbar + (g * n_l + i) * d;
             for (int64_t e = 0; e < nc; ++e)
@@ -221,14 +242,14 @@ void orc_select_level(const double* qbar, const double* kbar,
 }
 
 void orc_select(const double* qpyr, const double* kpyr, int64_t G, int64_t N,
-                int64_t d, int64_t bs, int L, const int64_t* K, double scale,
+                int64_t d, int64_t bs, int L, const int64_t* K, double scale, int causal,
                 int32_t* idx, double* gap)
 {
     for (int l = L; l >= 1; --l) {
         int64_t n_l = nblk(N, bs, l);
         const int32_t* parent = (l == L) ? NULL : idx + idx_off(G, N, bs, l + 1, K);
         orc_select_level(qpyr + lvl_off(G, N, bs, l, d), kpyr + lvl_off(G, N, bs, l, d),
-                         parent, G, n_l, d, bs, K[l - 1], l == L ? 0 : K[l], scale,
+                         parent, G, n_l, d, bs, K[l - 1], l == L ? 0 : K[l], scale, causal,
                          idx + idx_off(G, N, bs, l, K),
                          gap ? gap + lvl_off(G, N, bs, l, 1) : NULL);
     }
@@ -259,10 +280,12 @@ static int64_t kv_set(const double* k, const double* v, const double* kpyr,
 {
     int64_t ne = 0;
     int64_t n1 = nblk(N, bs, 1);
+    const int causal = (flags & ORC_CAUSAL) != 0;
     const int32_t* sel1 = idx + (g * n1 + t / bs) * K[0];
     for (int64_t p = 0; p < K[0]; ++p)
-        for (int64_t r = 0; r < bs && bs * sel1[p] + r < N; ++r) {
+        for (int64_t r = 0; sel1[p] >= 0 && r < bs && bs * sel1[p] + r < N; ++r) {
             int64_t u = bs * sel1[p] + r;
+            if (causal && u > t) break;  /* the diagonal block: keys up to t */
             key[ne] = k + (g * N + u) * d;
             val[ne] = v + (g * N + u) * d;
             tag[ne] = 0;
@@ -276,9 +299,11 @@ static int64_t kv_set(const double* k, const double* v, const double* kpyr,
             const double* vl = vpyr + lvl_off(G, N, bs, l, d);
             const int32_t* sel = idx + idx_off(G, N, bs, l, K) + (g * n_l + a) * K[l - 1];
             if (!(flags & ORC_ENRICH_COMPLEMENT)) {
-                /* the pooled tokens of the blocks the ancestor picked */
+                /* the pooled tokens of the blocks the ancestor picked (causal:
+                 * not its own block, whose mean holds tokens after t) */
                 for (int64_t p = 0; p < K[l - 1]; ++p) {
                     int64_t j = sel[p];
+                    if (j < 0 || (causal && j == a)) continue;
                     key[ne] = kl + (g * n_l + j) * d;
                     val[ne] = vl + (g * n_l + j) * d;
                     tag[ne] = l;
@@ -491,13 +516,14 @@ void orc_transpose(const int32_t* idx, int64_t G, int64_t n, int64_t K,
         int32_t* cl = col + g * n * K;
         const int32_t* I = idx + g * n * K;
         for (int64_t j = 0; j <= n; ++j) rp[j] = 0;
-        for (int64_t e = 0; e < n * K; ++e) rp[I[e] + 1] += 1;
+        for (int64_t e = 0; e < n * K; ++e)
+            if (I[e] >= 0) rp[I[e] + 1] += 1;  /* -1: an unused slot */
         for (int64_t j = 0; j < n; ++j) rp[j + 1] += rp[j];
         for (int64_t j = 0; j < n; ++j) fill[j] = 0;
         for (int64_t i = 0; i < n; ++i)
             for (int64_t p = 0; p < K; ++p) {
                 int32_t j = I[i * K + p];
-                cl[rp[j] + fill[j]++] = (int32_t)i;
+                if (j >= 0) cl[rp[j] + fill[j]++] = (int32_t)i;
             }
     }
     free(fill);

@@ -52,6 +52,8 @@ extern "C" {
 #define ORC_SIZE_BIAS 4u     /* a level-l pooled logit gets + ln bs^l */
 #define ORC_ENRICH_COMPLEMENT 8u /* the pooled tokens of the candidates a level did
                                     NOT pick, instead of those it picked */
+#define ORC_CAUSAL 16u       /* token t attends keys u <= t (selection: see
+                                orc_select_level; not with the complement) */
 
 /* Morton (Z-order) position of raster cell (y, x) on a side x side grid,
  * side a power of two: bits of y and x interleaved, the y bit above the x
@@ -90,16 +92,20 @@ void orc_pool(const double* x, int64_t G, int64_t N, int64_t d, int64_t bs,
  * Precondition: every row has at least K candidates.
  * Score = scale * <qbar_l[i], kbar_l[j]>; order = score descending, then
  * block index ascending; the first K are kept and stored ascending.
- * gap[i] = score of K-th kept - score of best rejected (+inf if none). */
+ * gap[i] = score of K-th kept - score of best rejected (+inf if none).
+ * causal != 0: the candidates are the blocks j < i among those above (parent
+ * entries -1 are unused slots); row i keeps itself and the best K-1 of them
+ * (all if fewer), ascending, then -1 in the slots left; gap is that of the
+ * K-1 earlier picks. */
 void orc_select_level(const double* qbar, const double* kbar,
                       const int32_t* parent, int64_t G, int64_t n_l, int64_t d,
-                      int64_t bs, int64_t K, int64_t Kp, double scale, int32_t* idx,
-                      double* gap);
+                      int64_t bs, int64_t K, int64_t Kp, double scale, int causal,
+                      int32_t* idx, double* gap);
 
 /* All levels, coarsest first (idx, gap in pyramid layouts); K[l-1] picks at
  * level l. */
 void orc_select(const double* qpyr, const double* kpyr, int64_t G, int64_t N,
-                int64_t d, int64_t bs, int L, const int64_t* K, double scale,
+                int64_t d, int64_t bs, int L, const int64_t* K, double scale, int causal,
                 int32_t* idx, double* gap);
 
 /* Sparse attention forward with hierarchical KV enrichment.
@@ -110,7 +116,9 @@ void orc_select(const double* qpyr, const double* kpyr, int64_t G, int64_t N,
  * candidates of a_l that it did not pick (every level-L block; below L the
  * existing children of the parent's picks).  The fine tokens and the
  * complement's pooled tokens then cover every key token exactly once, each
- * pooled token standing for the tokens it averages.  One softmax over that set with the given scale;
+ * pooled token standing for the tokens it averages.  ORC_CAUSAL: of the
+ * diagonal block (the query's own) only the keys u <= t, and no pooled token
+ * of an ancestor's own block; -1 picks are skipped.  One softmax over that set with the given scale;
  * lse = m + ln(sum exp(z - m)).
  * qblocks: optional list of query blocks to compute (NULL = all of them, in
  * which case nq is ignored); rows not listed are left untouched. */
@@ -136,7 +144,8 @@ void orc_backward(const double* q, const double* k, const double* v,
 
 /* Sparse index transpose of one level ([P2] technique 3): for the index lists
  * idx [G][n][K], col/rowptr hold, per head, T[j] = ascending {i : j in idx[i]}
- * in CSR form: rowptr [G][n+1] (per-head offsets from 0), col [G][n*K]. */
+ * in CSR form: rowptr [G][n+1] (per-head offsets from 0), col [G][n*K];
+ * entries -1 (unused slots) are skipped. */
 void orc_transpose(const int32_t* idx, int64_t G, int64_t n, int64_t K,
                    int32_t* rowptr, int32_t* col);
 

@@ -64,12 +64,26 @@ int main(void)
             orc_pool(v, G, N, d, bs, L, vp);
             int32_t* idx = malloc(G * irows * sizeof(int32_t));
             double* gap = malloc(G * rows * sizeof(double));
-            orc_select(qp, kp, G, N, d, bs, L, K, 1.0 / sqrt((double)d), idx, gap);
+            orc_select(qp, kp, G, N, d, bs, L, K, 1.0 / sqrt((double)d), 0, idx, gap);
             double* o = malloc(G * N * d * sizeof(double));
             double* lse = malloc(G * N * sizeof(double));
             double* dq = malloc(G * N * d * sizeof(double));
             double* dk = malloc(G * N * d * sizeof(double));
             double* dv = malloc(G * N * d * sizeof(double));
+            /* a causal selection too (rows with fewer picks hold -1) */
+            int32_t* cidx = malloc(G * irows * sizeof(int32_t));
+            orc_select(qp, kp, G, N, d, bs, L, K, 1.0 / sqrt((double)d), 1, cidx, gap);
+            orc_forward(q, k, v, kp, vp, cidx, G, N, d, bs, L, K, 0.3, 16u, NULL, 0, o, lse);
+            orc_backward(q, k, v, kp, vp, cidx, o, lse, dout, G, N, d, bs, L, K, 0.3, 16u,
+                         NULL, 0, NULL, 0, dq, dk, dv);
+            {
+                const int64_t n1c = (N + bs - 1) / bs;
+                int32_t* rpc = malloc(G * (n1c + 1) * sizeof(int32_t));
+                int32_t* colc = malloc(G * n1c * K[0] * sizeof(int32_t));
+                orc_transpose(cidx, G, n1c, K[0], rpc, colc);
+                free(rpc); free(colc);
+            }
+            free(cidx);
             for (unsigned flags = 0; flags < 16; ++flags) {
                 orc_forward(q, k, v, kp, vp, idx, G, N, d, bs, L, K, 0.3, flags, NULL, 0, o, lse);
                 orc_backward(q, k, v, kp, vp, idx, o, lse, dout, G, N, d, bs, L, K, 0.3, flags,
@@ -84,7 +98,7 @@ int main(void)
             int32_t* col = malloc(G * n1 * K[0] * sizeof(int32_t));
             orc_transpose(idx, G, n1, K[0], rp, col);
             double* lvl = malloc(G * n1 * sizeof(double));
-            orc_select_level(qp, kp, NULL, G, n1, d, bs, K[0], 0, 0.3, idx, lvl);
+            orc_select_level(qp, kp, NULL, G, n1, d, bs, K[0], 0, 0.3, 0, idx, lvl);
             free(q); free(k); free(v); free(dout); free(qp); free(kp); free(vp); free(idx);
             free(gap); free(o); free(lse); free(dq); free(dk); free(dv); free(rp); free(col);
             free(lvl);
