@@ -11,7 +11,8 @@
  *   - Top-K key blocks are chosen per query block: densely at the coarsest
  *     level, and at every finer level only among the children of the blocks
  *     chosen one level up;
- *   - non-causal attention runs over the tokens of the chosen level-1 blocks,
+ *   - attention (non-causal; causal with LLSA_CAUSAL) runs over the tokens of
+ *     the chosen level-1 blocks,
  *     enriched with the pooled key/value tokens of the blocks chosen at every
  *     level;
  *   - the backward pass turns the query->key block lists into key->query
@@ -74,7 +75,19 @@ extern "C" {
                                      once.  At most 2048 such entries per query block
                                      (sum over the enriching levels of the candidate
                                      counts), else LLSA_ERR_UNSUPPORTED */
-#define LLSA_KNOWN_FLAGS 15u
+#define LLSA_CAUSAL 16u       /* causal attention (the README's usage note names the
+                                 non-causal form only; this is the reading taken):
+                                 token t attends keys u <= t.  At every level a
+                                 query block keeps its own block and its best
+                                 topk - 1 earlier candidates (all of them when
+                                 fewer), the valid picks first, ascending, then -1
+                                 in the slots left; the query's own fine block is
+                                 masked to keys u <= t, and the pooled token of an
+                                 ancestor's own block (its mean holds later tokens)
+                                 does not enrich.  topk is limited as without
+                                 the flag.  Not with LLSA_ENRICH_COMPLEMENT
+                                 (LLSA_ERR_UNSUPPORTED) */
+#define LLSA_KNOWN_FLAGS 31u
 
 /* error codes */
 #define LLSA_OK 0
@@ -102,7 +115,8 @@ extern "C" {
  *   qbar/kbar/vbar[l-1] : float32 [B*H][N/16^l][d]   block means (pyramid)
  *   idx[l-1]            : int32   [B*H][N/16^l][topk] chosen blocks of each
  *                         (topk: that level's count with the _lk calls)
- *                         level-l query block, ascending
+ *                         level-l query block, ascending (LLSA_CAUSAL: -1 in
+ *                         the unused slots after the picks)
  *   rowptr[l-1]         : int32   [B*H][N/16^l + 1]  key->query lists (CSR,
  *   col[l-1]            : int32   [B*H][N/16^l*topk]  offsets per head from 0,
  *                         each list ascending); written by llsa_backward

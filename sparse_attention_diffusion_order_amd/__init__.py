@@ -16,7 +16,7 @@ import os
 import re
 
 __all__ = [
-    "LlsaError", "F32", "BF16", "NO_ENRICH", "ENRICH_COARSE", "SIZE_BIAS", "ENRICH_COMPLEMENT", "PART_POOL", "PART_SELECT", "PART_ATTN",
+    "LlsaError", "F32", "BF16", "NO_ENRICH", "ENRICH_COARSE", "SIZE_BIAS", "ENRICH_COMPLEMENT", "CAUSAL", "PART_POOL", "PART_SELECT", "PART_ATTN",
     "PART_TRANSPOSE", "PART_DQ", "PART_ENRICH", "PART_DKDV", "library_path", "load", "exported_names",
     "llsa_workspace_bytes", "llsa_workspace_layout", "llsa_zorder", "llsa_grid_order",
     "llsa_forward",
@@ -34,6 +34,7 @@ NO_ENRICH = 1
 ENRICH_COARSE = 2
 SIZE_BIAS = 4
 ENRICH_COMPLEMENT = 8
+CAUSAL = 16
 PART_POOL, PART_SELECT, PART_ATTN = 0, 1, 2
 PART_TRANSPOSE, PART_DQ, PART_DKDV, PART_ENRICH = 3, 4, 5, 6
 MAX_LEVELS = 6

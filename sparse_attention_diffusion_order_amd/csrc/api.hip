@@ -38,11 +38,16 @@ int validate(int B, int H, int N, int d, int block_size, const int* ks, int leve
     // level l chooses among the n_L blocks (coarsest) or the existing
     // children of its parent's K_{l+1} picks: at worst 16 (K_{l+1} - 1) full
     // parents and the last, partial one
+    // (the same limit holds for causal rows, which keep fewer picks where
+    // they have fewer earlier candidates: the workspace size depends on the
+    // shape and top-k only)
     for (int l = levels; l >= 1; --l) {
         const long long cands =
             l == levels ? nL : (long long)BS * (ks[l] - 1) + (n[l] - BS * (n[l + 1] - 1));
         if (ks[l - 1] < 1 || ks[l - 1] > cands) return LLSA_ERR_SHAPE;
     }
+    // the complement is defined for the non-causal selection only
+    if ((flags & LLSA_CAUSAL) && (flags & LLSA_ENRICH_COMPLEMENT)) return LLSA_ERR_UNSUPPORTED;
     for (int l = 0; l < levels; ++l)
         if (ks[l] > 64) return LLSA_ERR_UNSUPPORTED;
     if (nL > 4096) return LLSA_ERR_UNSUPPORTED;
@@ -137,6 +142,7 @@ void make_geo(int B, int H, int N, int d, const int* ks, int levels, unsigned fl
     g->l0 = (flags & LLSA_NO_ENRICH) ? levels + 1 : (flags & LLSA_ENRICH_COARSE) ? 2 : 1;
     g->lb2 = (flags & LLSA_SIZE_BIAS) ? 4.0f : 0.0f;  // log2(16^l) = 4 l
     g->cmp = (flags & LLSA_ENRICH_COMPLEMENT) != 0;
+    g->causal = (flags & LLSA_CAUSAL) != 0;
     // The attention launches gather key/value (forward, dQ) or query/dO
     // (dK/dV) rows of every head.  While those of all heads fit well inside
     // the 256 MB MALL, each XCD takes one contiguous eighth of the launch
@@ -479,7 +485,8 @@ const char* llsa_strerror(int code)
                "inner_bytes a positive multiple of 4";
     case LLSA_ERR_UNSUPPORTED:
         return "unsupported: needs d=64 or 128, block_size=16, dtype f32/bf16, known flags, "
-               "levels<=6, at most 4096 coarsest blocks, topk<=64, B*H*N<2^31";
+               "levels<=6, at most 4096 coarsest blocks, topk<=64, B*H*N<2^31, "
+               "at most 2048 complement entries, no complement with causal";
     case LLSA_ERR_WORKSPACE: return "workspace missing or smaller than llsa_workspace_bytes()";
     case LLSA_ERR_HIP: return "HIP launch or runtime error";
     case LLSA_ERR_SCRATCH:

@@ -144,9 +144,13 @@ __device__ __forceinline__ void fwd_block(const unsigned short* __restrict__ q,
     bf16x8 bq[NI];  // B operand of S^T: query row lane%16, channels 32u + 8(lane/16) ..
 #pragma unroll
     for (int u = 0; u < NI; ++u) bq[u] = ld_bf16x8(q + qbase + nq * D + 32 * u + 8 * gq);
-    // the query block's K fine blocks, one per lane (K <= 64)
+    // the query block's K fine blocks, one per lane (K <= 64).  Causal: the
+    // KF valid picks come first, the last of them the block itself (the
+    // diagonal tile, masked to keys u <= t), then -1.
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
-    const int myj = lane < g.K ? clampi(sel[lane], g.n[1]) : 0;
+    const int rawj = lane < g.K ? sel[lane] : -1;
+    const int myj = lane < g.K ? clampi(rawj, g.n[1]) : 0;
+    const int KF = g.causal ? max(1, (int)__popcll(__ballot(rawj >= 0))) : g.K;
     // the pooled entries of the enriching levels: rows in the bf16 pooled
     // arrays, with their level (fill_entries)
     int* ent = (int*)(sm + 2 * Lay::V_TILE + 2 * Lay::K_TILE);
@@ -174,7 +178,7 @@ __device__ __forceinline__ void fwd_block(const unsigned short* __restrict__ q,
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + hbase, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + hbase, head_bytes);
     const int voff = (vr * D + vc) * 2;
-    const int NF = g.K / 2;  // full fine pairs
+    const int NF = (g.causal ? KF - 1 : g.K) / 2;  // full (unmasked) fine pairs
     auto load_fine = [&](FinePair<D>& f, int p) {
         const int sa = __builtin_amdgcn_readlane(myj, 2 * p) * (BS * D * 2);
         const int sb = __builtin_amdgcn_readlane(myj, 2 * p + 1) * (BS * D * 2);
@@ -214,18 +218,21 @@ __device__ __forceinline__ void fwd_block(const unsigned short* __restrict__ q,
         }
         if (p < NF) step_fine(A);  // odd number of pairs: the last one is in A
     }
-    // masked tail: tile t < NFT is the lone fine tile (K odd), then the
-    // pooled tiles; pairs of tiles, rows read through per-lane pointers
-    const int NFT = g.K & 1;
+    // masked tail: tiles t < NFT are the fine tiles left (the lone one of an
+    // odd count, and when causal the diagonal one, last), then the pooled
+    // tiles; pairs of tiles, rows read through per-lane pointers
+    const int NFT = KF - 2 * NF;
     const int NT = NFT + (E + BS - 1) / BS;
-    const int jlast = __builtin_amdgcn_readlane(myj, g.K - 1);
     auto tail_off = [&](int t, int r) -> long {
-        // element offset of row r (0..15) of tail tile t in k / v (the lone
-        // fine tile) or in the pooled copies; rows past the last entry
-        // repeat a valid one (they are masked)
-        if (t < NFT) return hbase + ((long)jlast * BS + r) * D;
+        // element offset of row r (0..15) of tail tile t in k / v (a fine
+        // tile) or in the pooled copies; rows past the last entry repeat a
+        // valid one (they are masked)
+        if (t < NFT) return hbase + ((long)__builtin_amdgcn_readlane(myj, 2 * NF + t) * BS + r) * D;
         return (long)(ent[min(BS * (t - NFT) + r, E - 1)] & ENT_ROW) * D;
     };
+    // valid rows of fine tail tile t: all 16, or for the causal diagonal
+    // tile those at or before this lane's query row (a per-lane count)
+    auto fine_rows = [&](int t) { return (g.causal && t == NFT - 1) ? nq + 1 : BS; };
     for (int t = 0; t < NT; t += 2) {
         const int tb = min(t + 1, NT - 1);
         const bool fa = t < NFT, fb = tb < NFT;
@@ -252,8 +259,9 @@ __device__ __forceinline__ void fwd_block(const unsigned short* __restrict__ q,
         stage(f, ka, kb);
         // valid entries of the two tiles, and each row's logit bias (that
         // of the level of pooled entry e)
-        const int na = t < NFT ? BS : max(0, min(BS, E - BS * (t - NFT)));
-        const int nb = t + 1 >= NT ? 0 : (t + 1 < NFT ? BS : max(0, min(BS, E - BS * (t + 1 - NFT))));
+        const int na = t < NFT ? fine_rows(t) : max(0, min(BS, E - BS * (t - NFT)));
+        const int nb = t + 1 >= NT ? 0
+                     : (t + 1 < NFT ? fine_rows(t + 1) : max(0, min(BS, E - BS * (t + 1 - NFT))));
         float ba[4], bb[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {

@@ -43,6 +43,7 @@ struct Geo {
     float lb2;             // logit bias of a level-l pooled token: l * lb2 (log2 units)
     int xcd_chunk;         // workgroups per XCD chunk of the attention launches (xcd_block)
     bool cmp;              // LLSA_ENRICH_COMPLEMENT: the unpicked candidates enrich
+    bool causal;           // LLSA_CAUSAL: token t attends keys u <= t
     // pooled entries per query block: the picks of the enriching levels (their
     // number), or with the complement at most the candidates of those levels
     __host__ __device__ int n_pooled() const { return l0 <= L ? eoff[L + 1] : 0; }
@@ -313,6 +314,9 @@ __device__ __forceinline__ int ent_level(int e) { return e >> 28; }
 // Fill the pooled-entry table of query block i (head gh) and return the
 // number of entries (the same in every lane of the wave).  Default: the
 // picks of its ancestor at every enriching level l0..L, level by level.
+// LLSA_CAUSAL: of those only the picks before the ancestor itself (its own
+// block's mean holds later tokens; unused slots hold -1), compacted by
+// ballot -- the level-1 entries then keep the positions of their picks.
 // LLSA_ENRICH_COMPLEMENT: at every enriching level the ancestor's candidates
 // it did not pick -- all blocks at the coarsest level, below it the existing
 // children of the parent's picks -- in ascending order, compacted by ballot.
@@ -320,11 +324,20 @@ __device__ __forceinline__ int fill_entries(const Geo& g, const Ws& w, int gh, i
                                             int lane)
 {
     int E = 0;
+    const unsigned long long below = (1ull << lane) - 1ull;
     for (int l = g.l0; l <= g.L; ++l) {
         const int Kl = g.Kl[l], nl = g.n[l];
         const int a = i >> (4 * (l - 1));
         const int* sel = w.idx[l - 1] + ((long)gh * nl + a) * Kl;
         const long row0 = w.prow[l - 1] + (long)gh * nl;
+        if (g.causal) {  // Kl <= 64: one pick per lane
+            const int j = lane < Kl ? sel[lane] : -1;
+            const bool keep = j >= 0 && j != a;
+            const unsigned long long bal = __ballot(keep);
+            if (keep) ent[E + __popcll(bal & below)] = (int)(row0 + clampi(j, nl)) | (l << 28);
+            E += __popcll(bal);
+            continue;
+        }
         if (!g.cmp) {
             for (int s0 = 0; s0 < Kl; s0 += 64)
                 if (s0 + lane < Kl)
@@ -337,7 +350,6 @@ __device__ __forceinline__ int fill_entries(const Geo& g, const Ws& w, int gh, i
         const int M = l == g.L ? nl : BS * g.Kl[l + 1];
         const int* par = l == g.L ? nullptr
                                   : w.idx[l] + ((long)gh * g.n[l + 1] + (a >> 4)) * g.Kl[l + 1];
-        const unsigned long long below = (1ull << lane) - 1ull;
         for (int c0 = 0; c0 < M; c0 += 64) {
             const int c = c0 + lane;
             int j = nl;
@@ -363,7 +375,8 @@ __device__ __forceinline__ void for_each_pooled(const Geo& g, const Ws& w, int g
         const int a = i >> (4 * (l - 1));
         const int* sel = w.idx[l - 1] + ((long)gh * nl + a) * Kl;
         if (!g.cmp) {
-            for (int s = 0; s < Kl; ++s) f(l, clampi(sel[s], nl));
+            for (int s = 0; s < Kl; ++s)
+                if (!g.causal || (sel[s] >= 0 && sel[s] != a)) f(l, clampi(sel[s], nl));
             continue;
         }
         const int M = l == g.L ? nl : BS * g.Kl[l + 1];

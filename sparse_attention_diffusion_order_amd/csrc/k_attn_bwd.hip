@@ -29,6 +29,10 @@
 //               The epilogue adds the pooled-level gradients of levels >= 2.
 // fp32 path: plain VALU kernels, one wave per row (lane = channel), with
 // explicit pooled tokens at every level.
+// LLSA_CAUSAL: the key/value set of the forward (the diagonal fine block
+// masked to keys u <= t, no pooled token of an ancestor's own block, unused
+// slots -1 skipped), so a key block's own query block sees it masked and does
+// not count its level-1 pooled token.
 // No floating-point atomics anywhere: results are bit-identical run to run.
 #include "common.h"
 #include "transpose.h"
@@ -174,7 +178,13 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
         bd[u] = ld8(dout + rowq + 32 * u + 8 * gq);
     }
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + i) * g.K;
-    const int myj = lane < g.K ? clampi(sel[lane], g.n[1]) : 0;
+    const int rawj = lane < g.K ? sel[lane] : -1;
+    const int myj = lane < g.K ? clampi(rawj, g.n[1]) : 0;
+    // fine tiles: K, or when causal the KF valid picks, the last of them the
+    // diagonal tile; E1: the level-1 pooled entries (the picks but, when
+    // causal, the block itself and the unused slots), at the picks' positions
+    const int KF = g.causal ? max(1, (int)__popcll(__ballot(rawj >= 0))) : g.K;
+    const int E1 = g.causal ? (int)__popcll(__ballot(rawj >= 0 && rawj != i)) : g.K;
     float Dq;
     {
         float s = 0.f;
@@ -202,7 +212,8 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
     unsigned short* lvb = lva + Lay::V_TILE;
     // one pipeline over NF fine pairs then the pooled pairs, next pair in
     // flight; unconditional (clamped) loads keep the wait counts exact
-    const int NF = (g.K + 1) / 2;
+    const int NF = (KF + 1) / 2;
+    const int NFU = (g.causal ? KF - 1 : g.K) / 2;  // fine pairs without a mask
     const int NT = (E + BS - 1) / BS;
     const int NP = NF + (NT + 1) / 2;
     const int sr = lane / TS::LPR, sc = (lane % TS::LPR) * 8;
@@ -210,8 +221,8 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
         long ka[NI], kb[NI];  // element offsets of row sr + RPI u of tiles a and b
         const unsigned short *kp, *vp;
         if (p < NF) {
-            const int ja = __builtin_amdgcn_readlane(myj, min(2 * p, g.K - 1));
-            const int jb = __builtin_amdgcn_readlane(myj, min(2 * p + 1, g.K - 1));
+            const int ja = __builtin_amdgcn_readlane(myj, min(2 * p, KF - 1));
+            const int jb = __builtin_amdgcn_readlane(myj, min(2 * p + 1, KF - 1));
 #pragma unroll
             for (int u = 0; u < NI; ++u) {
                 ka[u] = hbase + ((long)ja * BS + sr + TS::RPI * u) * D + sc;
@@ -250,19 +261,24 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
         operand_rows<D, TS::ROW_T>(lb, kb, lane);
         operand_rows<D, TS::ROW_A>(lva, va, lane);
         operand_rows<D, TS::ROW_A>(lvb, vb, lane);
-        // full pairs of fine tiles run unmasked; with an odd top-k the last
+        // full pairs of fine tiles run unmasked; with an odd count the last
         // fine "pair" holds the lone last tile twice (the clamped load), so
-        // it takes the masked path with its second tile empty
-        if (p < NF - (g.K & 1)) {
+        // it takes the masked path with its second tile empty; the causal
+        // diagonal tile (the last fine one) is masked to the keys at or
+        // before each query row
+        if (p < NFU) {
             dq_pair<false, D>(acc, bq, bd, nl2, Dq, ka, kb, va, vb, la, lb, BS, BS, c, lane);
         } else {
+            auto fine_rows = [&](int t) {
+                return t >= KF ? 0 : (g.causal && t == KF - 1) ? nq + 1 : BS;
+            };
             const int e0 = p < NF ? 0 : BS * 2 * (p - NF);
-            const int na = p < NF ? BS : max(0, min(BS, E - e0));
-            const int nb = p < NF ? 0 : max(0, min(BS, E - e0 - BS));
+            const int na = p < NF ? fine_rows(2 * p) : max(0, min(BS, E - e0));
+            const int nb = p < NF ? fine_rows(2 * p + 1) : max(0, min(BS, E - e0 - BS));
             const bool pooled = p >= NF;
-            // the level-1 picks' pooled entries (the first K, by default)
-            // keep their P and dS for the key-major pass
-            float* pe = (pooled && g.l0 == 1 && !g.cmp && e0 < g.K)
+            // the level-1 picks' pooled entries (the first E1) keep their P
+            // and dS for the key-major pass, at their picks' positions
+            float* pe = (pooled && g.l0 == 1 && !g.cmp && e0 < E1)
                             ? w.pe1 + ((long)gh * g.n[1] + i) * g.K * 2 * BS : nullptr;
             float ba[4], bb[4];  // pooled rows: the logit bias of the entry's level
 #pragma unroll
@@ -273,7 +289,7 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
                 bb[r] = bias ? g.lb2 * (float)ent_level(ent[max(0, min(ea + BS, E - 1))]) : 0.f;
             }
             dq_pair<true, D>(acc, bq, bd, nl2, Dq, ka, kb, va, vb, la, lb, na, nb, c, lane, pe,
-                             e0, g.K, ba, bb);
+                             e0, E1, ba, bb);
         }
     };
     DqPair<D> A, B;
@@ -382,7 +398,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
         const int* sel = w.idx[l - 1] + ((long)gh * g.n[l] + al) * Kl;
         const float lb = g.lb2 * (float)l;  // size bias of a level-l token (log2)
         for (int e0 = 0; e0 < Kl; e0 += BS) {
-            const bool ev = e0 + nq < Kl;
+            // a live entry: causal rows skip unused slots (-1) and the
+            // ancestor's own block (their partials are written as zeros)
+            const int sj = e0 + nq < Kl ? sel[e0 + nq] : -1;
+            const bool ev = e0 + nq < Kl && (!g.causal || (sj >= 0 && sj != al));
             bf16x8 bk[NI], bv[NI];  // entry rows lane%16, channels 32u + 8(lane/16) ..
 #pragma unroll
             for (int u = 0; u < NI; ++u) bk[u] = bv[u] = bf16x8{};
@@ -536,6 +555,7 @@ struct QBlock {
     bf16x8 q[D / 32], d[D / 32];  // load u: row sr + RPI u, channels sc .. sc+7
     float x;  // lane < 16: lse of row lane; < 32: delta of row lane - 16; else the
               // level-1 pooled P (lanes 32..47) and dS (48..63) of row lane % 16
+    bool diag;  // causal and the query block is the key block itself
 };
 
 // Waves per workgroup of the dk/dv pass: WPG consecutive (sibling) key
@@ -613,6 +633,8 @@ __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __re
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float p = fast_exp2(fmaf(s[r], c, lr[r]));
+            // the causal diagonal block: key nq is seen by queries at or after it
+            if (f.diag && nq > 4 * gq + r) p = 0.f;
             float ds = p * (dp[r] - dr[r]);
             if (enrich1) {
                 p = fmaf(pr[r], 1.0f / BS, p);
@@ -654,8 +676,11 @@ __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __re
         for (int u = 0; u < NI; ++u) f.q[u] = bload8(rq, voff + 1024 * u, so);
 #pragma unroll
         for (int u = 0; u < NI; ++u) f.d[u] = bload8(rdo, voff + 1024 * u, so);
-        const __amdgpu_buffer_rsrc_t rpe =
-            make_rsrc(w.pe1 + (((long)gh * g.n[1] + i) * g.K + sl) * 2 * BS, 2 * BS * 4);
+        // (the causal diagonal block does not see block j's pooled token:
+        // an empty resource reads 0)
+        f.diag = g.causal && i == j;
+        const __amdgpu_buffer_rsrc_t rpe = make_rsrc(
+            w.pe1 + (((long)gh * g.n[1] + i) * g.K + sl) * 2 * BS, f.diag ? 0u : 2 * BS * 4);
         f.x = bloadf(rlse, off_lse, i * BS * 4) + bloadf(rdel, off_del, i * BS * 4) +
               bloadf(rpe, off_pe, 0);
     };
@@ -916,11 +941,14 @@ __device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const 
                                                const float* v, int gh, int t, F f)
 {
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + t / BS) * g.K;
-    for (int s = 0; s < g.K; ++s)
-        for (int r = 0; r < BS; ++r) {
+    for (int s = 0; s < g.K; ++s) {
+        if (g.causal && sel[s] < 0) continue;  // an unused slot
+        const bool diag = g.causal && sel[s] == t / BS;
+        for (int r = 0; r < (diag ? t % BS + 1 : BS); ++r) {  // diagonal: keys up to t
             long row = ((long)gh * g.N + (long)clampi(sel[s], g.n[1]) * BS + r) * D;
             f(k + row, v + row, 0.f);
         }
+    }
     // enriching levels l0..L; a level-lv token's logit gets lb2 * lv * ln 2
     for_each_pooled(g, w, gh, t / BS, [&](int lv, int j) {
         const long row = ((long)gh * g.n[lv] + j) * D;
@@ -1012,6 +1040,7 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
         long a;
         if (!g.cmp) {
             a = clampi(cl[e], g.n[l]);
+            if (g.causal && a == j) continue;  // its own block's mean: not seen
         } else {
             a = l == g.L ? e : BS * clampi(pl[e >> 4], g.n[l + 1]) + (e & 15);
             if (a >= g.n[l]) continue;
@@ -1069,7 +1098,8 @@ __global__ __launch_bounds__(256) void dkdv_f32(const float* __restrict__ q,
     const int tot = g.n[1] * g.K;
     const int beg = clampi(rp[j], tot + 1), end = max(beg, clampi(rp[j + 1], tot + 1));
     for (int e = beg; e < end; ++e)
-        for (int r = 0; r < BS; ++r) {
+        // the causal diagonal block: the queries at or after key x
+        for (int r = (g.causal && cl[e] == j) ? x % BS : 0; r < BS; ++r) {
             const long tg = (long)gh * g.N + (long)clampi(cl[e], g.n[1]) * BS + r;
             float qc[NC], dc[NC];
             lane_channels<D>(qc, q + tg * D, lane);

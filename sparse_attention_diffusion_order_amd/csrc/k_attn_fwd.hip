@@ -12,7 +12,10 @@
 //     LLSA_ENRICH_COARSE, none with LLSA_NO_ENRICH.
 // One softmax over the whole set, scale 1/sqrt(d); lse in natural log.  With
 // LLSA_SIZE_BIAS a level-l pooled logit gets + ln 16^l, as if the token stood
-// for its 16^l keys.
+// for its 16^l keys.  LLSA_CAUSAL (a reading; the README's usage names the
+// non-causal form only): idx_1[i] holds block i itself (last of its valid
+// picks), masked to keys u <= t, and the pooled token of an ancestor's own
+// block is left out; unused slots (-1) are skipped.
 //
 // The pooled entries of the enriching levels (the sum of their top-k) form
 // extra tiles of 16, read from the bf16 copy of the pyramid that the pool
@@ -345,11 +348,14 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
         for (int c = 0; c < NC; ++c) o[c] = fmaf(p, vr[lane + 64 * c], o[c]);
     };
     const int* sel = w.idx[0] + ((long)gh * g.n[1] + t / BS) * g.K;
-    for (int s = 0; s < g.K; ++s)
-        for (int r = 0; r < BS; ++r) {
+    for (int s = 0; s < g.K; ++s) {
+        if (g.causal && sel[s] < 0) continue;  // an unused slot
+        const bool diag = g.causal && sel[s] == t / BS;
+        for (int r = 0; r < (diag ? t % BS + 1 : BS); ++r) {  // diagonal: keys up to t
             const long row = ((long)gh * g.N + (long)clampi(sel[s], g.n[1]) * BS + r) * D;
             visit(k + row, v + row, 0.f);
         }
+    }
     // pooled tokens of the enriching levels
     for_each_pooled(g, w, gh, t / BS, [&](int lv, int j) {
         const long row = ((long)gh * g.n[lv] + j) * D;
@@ -368,7 +374,7 @@ hipError_t launch_attn_fwd_d(const void* q, const void* k, const void* v, void* 
         long nblk = (long)g.G * g.n[1];
         // the four-block kernel (d = 64): every fine list and every pooled
         // list fit one 16-entry tile
-        bool fits = D == D64 && g.K <= BS && g.n[1] % 4 == 0 && !g.cmp;
+        bool fits = D == D64 && g.K <= BS && g.n[1] % 4 == 0 && !g.cmp && !g.causal;
         for (int l = g.l0; l <= g.L; ++l) fits = fits && g.Kl[l] <= BS;
         if (fits) {
             hipLaunchKernelGGL(attn_fwd_u4, dim3((unsigned)((nblk + 15) / 16)), dim3(256), 0, st,

@@ -24,6 +24,13 @@
 // per key block and per 16 key blocks (see flush_counts), which the sparse
 // transpose uses.  When both fit, the two coarsest levels run in one launch
 // (select_top2).
+//
+// LLSA_CAUSAL (a reading: the README's usage names the non-causal form only):
+// a row's own block scores +inf and the candidates after it -inf, so the
+// top-K holds the block itself and its best K-1 earlier candidates.  A row
+// keeps only candidates with a finite or +inf score: when it has fewer than
+// K, the slots after its picks hold -1, and the children of a -1 parent slot
+// are no candidates.
 #include "common.h"
 
 namespace llsa {
@@ -43,6 +50,24 @@ __device__ __forceinline__ unsigned order_key(float f)
 {
     unsigned u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// order_key(-inf): keys at or below it belong to no candidate (no such
+// child, or a causal row's later blocks)
+constexpr unsigned KEY_NONE = 0x007FFFFFu;
+
+// Block number of candidate c of a row below the coarsest level: child c % 16
+// of parent pick pr; an unused parent slot (pr < 0) has no children (INT_MAX,
+// past every level's last block)
+__device__ __forceinline__ int child_of(int pr, int c, int np)
+{
+    return pr < 0 ? INT_MAX : BS * clampi(pr, np) + (c % BS);
+}
+
+// Causal score of candidate block j in row `row` (row < 0: not causal)
+__device__ __forceinline__ float causal_score(float s, int j, int row)
+{
+    return row < 0 ? s : j == row ? INFINITY : j > row ? -INFINITY : s;
 }
 
 // Pick counts of one head below the coarsest level: per key block and per
@@ -73,18 +98,28 @@ __device__ __forceinline__ void flush_counts(const int* pc, const int* cand, int
 // (LDS) to add to, or nullptr; lout: an LDS copy of the output, or nullptr.
 template <int KPL>
 __device__ __forceinline__ void select_rows(const float* sc, const int* cand, int* out, int rows,
-                                            int M, int K, int* pc, int* lout = nullptr)
+                                            int M, int Kq, int* pc, int* lout = nullptr)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const unsigned long long below = (1ull << lane) - 1ull;
     for (int r = wv; r < rows; r += blockDim.x / 64) {
         unsigned key[KPL];
         bool ok[KPL];
+        int nvalid = 0;
 #pragma unroll
         for (int s = 0; s < KPL; ++s) {
             int p = s * 64 + lane;
             ok[s] = p < M;
             key[s] = ok[s] ? order_key(sc[r * M + p]) : 0u;
+            nvalid += __popcll(__ballot(key[s] > KEY_NONE));
+        }
+        // the picks this row can make (K, but for a causal row with fewer
+        // candidates); -1 in the slots after them
+        const int K = min(Kq, nvalid);
+        int* orow = out + (long)r * Kq;
+        for (int p = K + lane; p < Kq; p += 64) {
+            orow[p] = -1;
+            if (lout) lout[r * Kq + p] = -1;
         }
         // MSB-first search for a threshold T with #(key >= T) >= K.  It ends
         // at the K-th largest key, or earlier as soon as exactly K keys are
@@ -106,7 +141,6 @@ __device__ __forceinline__ void select_rows(const float* sc, const int* cand, in
         for (int s = 0; s < KPL; ++s) gt += __popcll(__ballot(ok[s] && key[s] > T));
         int need = K - gt;  // ties at T: lowest candidate positions win
         int eq_before = 0, out_before = 0;
-        int* orow = out + (long)r * K;
 #pragma unroll
         for (int s = 0; s < KPL; ++s) {
             bool eq = ok[s] && key[s] == T;
@@ -117,7 +151,7 @@ __device__ __forceinline__ void select_rows(const float* sc, const int* cand, in
                 const int pos = out_before + __popcll(bt & below);
                 const int blk = cand ? cand[s * 64 + lane] : s * 64 + lane;
                 orow[pos] = blk;
-                if (lout) lout[r * K + pos] = blk;
+                if (lout) lout[r * Kq + pos] = blk;
                 if (pc) atomicAdd(pc + s * 64 + lane, 1);
             }
             eq_before += __popcll(beq);
@@ -131,7 +165,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
                                                      const float* __restrict__ kbar,
                                                      const int* __restrict__ parent,
                                                      int* __restrict__ idx, Counts cnt,
-                                                     int n_l, int K, int R, int M, float scale)
+                                                     int n_l, int K, int R, int M, float scale,
+                                                     int causal)
 {
     extern __shared__ float smem[];
     float* qs = smem;                 // [R][D]
@@ -150,7 +185,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
     for (int c = threadIdx.x; c < M; c += blockDim.x) {
         if (parent) {
             const int* pr = parent + ((long)gh * np + grp) * (M / BS);  // parent row: M/16 picks
-            cand[c] = BS * clampi(pr[c / BS], np) + (c % BS);  // may lie past n_l
+            cand[c] = child_of(pr[c / BS], c, np);  // may lie past n_l
         } else {
             cand[c] = c;
         }
@@ -191,7 +226,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
             a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false));
             a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false));
             if (sub == 0 && c < M)  // + 0 turns -0 into +0; no child: never chosen
-                sc[r * M + c] = ok ? a * scale + 0.0f : -INFINITY;
+                sc[r * M + c] = ok ? causal_score(a * scale + 0.0f, cand[c], causal ? row0 + r : -1)
+                                   : -INFINITY;
         }
     }
     __syncthreads();
@@ -218,19 +254,27 @@ __device__ __forceinline__ int row16_sum(int x)
 // and the four rows of a wave advance together.
 template <int KPG>
 __device__ __forceinline__ void select_rows16(const float* sc, const int* cand, int* out,
-                                              int rows, int M, int K, int* pc)
+                                              int rows, int M, int Kq, int* pc)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
     const int r = 4 * wv + g;
     const bool live = r < rows;
     unsigned key[KPG];
+    int nvalid = 0;
 #pragma unroll
     for (int s = 0; s < KPG; ++s) {
         const int c = BS * s + n;
         // invalid candidates get key 0, below every finite score's key
         key[s] = (live && c < M) ? order_key(sc[r * M + c]) : 0u;
+        nvalid += key[s] > KEY_NONE ? 1 : 0;
     }
+    // the picks this row can make (K, but for a causal row with fewer
+    // candidates); -1 in the slots after them
+    const int K = min(Kq, row16_sum(nvalid));
+    int* orow = out + (long)r * Kq;
+    if (live)
+        for (int p = K + n; p < Kq; p += 16) orow[p] = -1;
     // per-row threshold search, stopped per row as soon as exactly K keys
     // are >= T (see select_rows)
     unsigned T = 0;
@@ -254,7 +298,6 @@ __device__ __forceinline__ void select_rows16(const float* sc, const int* cand, 
     const unsigned below = (1u << n) - 1u;
     const int sh = 16 * (g & 1);
     int eq_before = 0, out_before = 0;
-    int* orow = out + (long)r * K;
 #pragma unroll
     for (int s = 0; s < KPG; ++s) {
         const bool eq = live && key[s] == T;
@@ -295,11 +338,13 @@ __device__ __forceinline__ void load_query_operand(float (&qa)[D / 4], const flo
 // k-slot, so every lane reads whole 64-byte pieces of the rows.  The channel sum order is
 // fixed by the instruction sequence.  Then the top-K of the `rows` rows
 // (select_rows16) and the pick counts.  On entry cand and pc (LDS, M each)
-// are filled and zeroed and a barrier has passed; kh = the head's key rows.
+// are filled and zeroed and a barrier has passed; kh = the head's key rows;
+// crow0: the level row of output row 0 when causal, else -1.
 template <int KPG, int D>
 __device__ __forceinline__ void score_select16(const float (&qa)[D / 4], const float* kh, int* out,
                                                int rows, int M, int K, float scale, float* sc,
-                                               const int* cand, int* pc, Counts cnt, int n_l)
+                                               const int* cand, int* pc, Counts cnt, int n_l,
+                                               int crow0)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int g = lane >> 4, n = lane & 15;
@@ -326,11 +371,14 @@ __device__ __forceinline__ void score_select16(const float (&qa)[D / 4], const f
         const int col = tile * BS + n;
         // candidates past the level's last block (children the partial last
         // parent does not have) score -inf: never chosen
-        const bool exists = col < M && cand[min(col, M - 1)] < n_l;
+        const int cj = cand[min(col, M - 1)];
+        const bool exists = col < M && cj < n_l;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (4 * g + r < rows && col < M)
-                sc[(4 * g + r) * M + col] = exists ? acc[r] * scale + 0.0f : -INFINITY;
+                sc[(4 * g + r) * M + col] =
+                    exists ? causal_score(acc[r] * scale + 0.0f, cj, crow0 < 0 ? -1 : crow0 + 4 * g + r)
+                           : -INFINITY;
 #pragma unroll
         for (int k = 0; k < CG; ++k) kb[k] = kn[k];
     }
@@ -346,7 +394,7 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
                                                    const float* __restrict__ kbar,
                                                    const int* __restrict__ parent,
                                                    int* __restrict__ idx, Counts cnt,
-                                                   int n_l, int K, int M, float scale)
+                                                   int n_l, int K, int M, float scale, int causal)
 {
     extern __shared__ float smem[];
     float* sc = smem;                 // [16][M]
@@ -364,7 +412,7 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
     for (int c = threadIdx.x; c < M; c += blockDim.x) {
         if (parent) {
             const int* pr = parent + ((long)gh * np + grp) * (M / BS);  // parent row: M/16 picks
-            cand[c] = BS * clampi(pr[c / BS], np) + (c % BS);  // may lie past n_l
+            cand[c] = child_of(pr[c / BS], c, np);  // may lie past n_l
         } else {
             cand[c] = c;
         }
@@ -375,7 +423,8 @@ __global__ __launch_bounds__(256) void select_mfma(const float* __restrict__ qba
     __syncthreads();
     score_select16<KPG, D>(qa, kbar + (long)gh * n_l * D, idx + ((long)gh * n_l + row0) * K, rows,
                            M, K, scale, sc, cand, pc,
-                           {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)}, n_l);
+                           {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)}, n_l,
+                           causal ? row0 : -1);
 }
 
 // The two coarsest levels in one launch.  Workgroup p (of a head) first
@@ -397,7 +446,7 @@ __device__ __forceinline__ void top2_rows(const float* __restrict__ qtop,
                                           const float* __restrict__ kbar,
                                           int* __restrict__ idx_top, int* __restrict__ idx,
                                           Counts cnt, int nL, int n_l, int Ktop, int K,
-                                          float scale, float* smem, int gh, int p)
+                                          float scale, float* smem, int gh, int p, int causal)
 {
     const int M = BS * Ktop;          // candidates of a level-(L-1) row
     float* sc = smem;                 // [16][M]
@@ -441,7 +490,8 @@ __device__ __forceinline__ void top2_rows(const float* __restrict__ qtop,
             x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
             x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
             const int c = c0 + 32 * a + rg;
-            if (u == 0 && c < nL) st[c] = x * scale + 0.0f;  // + 0 turns -0 into +0
+            if (u == 0 && c < nL)  // + 0 turns -0 into +0
+                st[c] = causal_score(x * scale + 0.0f, c, causal ? p : -1);
         }
     }
     __syncthreads();
@@ -455,11 +505,12 @@ __device__ __forceinline__ void top2_rows(const float* __restrict__ qtop,
     const int rows = min(BS, n_l - BS * p);
     float qa[D / 4];
     load_query_operand<D>(qa, qbar, (long)gh * n_l + BS * p, rows);
-    for (int c = threadIdx.x; c < M; c += blockDim.x) cand[c] = BS * picks[c / BS] + (c % BS);
+    for (int c = threadIdx.x; c < M; c += blockDim.x) cand[c] = child_of(picks[c / BS], c, nL);
     __syncthreads();
     score_select16<KPG, D>(qa, kbar + (long)gh * n_l * D, idx + ((long)gh * n_l + BS * p) * K,
                            rows, M, K, scale, sc, cand, pc,
-                           {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)}, n_l);
+                           {cnt.c1 + (long)gh * n_l, cnt.c16 + (long)gh * ((n_l + 15) / 16)}, n_l,
+                           causal ? BS * p : -1);
 }
 
 template <int KPL, int KPG, int D>
@@ -470,16 +521,17 @@ __global__ __launch_bounds__(256) void select_top2(const float* __restrict__ qto
                                                    int* __restrict__ idx_top,
                                                    int* __restrict__ idx, Counts cnt,
                                                    int nL, int n_l, int Ktop, int K,
-                                                   float scale)
+                                                   float scale, int causal)
 {
     extern __shared__ float smem[];
     top2_rows<KPL, KPG, D>(qtop, ktop, qbar, kbar, idx_top, idx, cnt, nL, n_l, Ktop, K, scale,
-                           smem, blockIdx.x / nL, blockIdx.x % nL);
+                           smem, blockIdx.x / nL, blockIdx.x % nL, causal);
 }
 
 template <int KPG, int D>
 hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, int* idx,
-                       Counts cnt, int G, int n_l, int K, int M, float scale, hipStream_t st)
+                       Counts cnt, int G, int n_l, int K, int M, float scale, int causal,
+                       hipStream_t st)
 {
     const int groups = (n_l + (parent ? BS : 4) - 1) / (parent ? BS : 4);
     const size_t lds = (size_t)BS * M * sizeof(float) + 2 * (size_t)M * sizeof(int);
@@ -489,7 +541,7 @@ hipError_t launch_mfma(const float* qbar, const float* kbar, const int* parent, 
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((select_mfma<KPG, D>), dim3(G * groups), dim3(256), lds, st, qbar, kbar, parent,
-                       idx, cnt, n_l, K, M, scale);
+                       idx, cnt, n_l, K, M, scale, causal);
     return hipGetLastError();
 }
 
@@ -507,7 +559,7 @@ hipError_t launch_top2(const Geo& g, const Ws& w, hipStream_t st)
     hipLaunchKernelGGL((select_top2<KPL, KPG, D>), dim3(g.G * nL), dim3(256), lds, st,
                        w.qbar[L - 1], w.kbar[L - 1], w.qbar[L - 2], w.kbar[L - 2], w.idx[L - 1],
                        w.idx[L - 2], Counts{w.cnt[L - 2], w.c16[L - 2]}, nL, g.n[L - 1],
-                       g.Kl[L], g.Kl[L - 1], g.scale);
+                       g.Kl[L], g.Kl[L - 1], g.scale, (int)g.causal);
     return hipGetLastError();
 }
 
@@ -526,7 +578,7 @@ hipError_t launch_top2_k(const Geo& g, const Ws& w, hipStream_t st)
 // the dense n_L x n_L scoring spreads over many CUs.
 template <int KPL, int D>
 hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, Counts cnt, int G, int n_l,
-                       int K, float scale, hipStream_t st)
+                       int K, float scale, int causal, hipStream_t st)
 {
     const int M = n_l;
     int R = max(1, min(min(16, n_l / 64), 8192 / M));
@@ -538,7 +590,7 @@ hipError_t launch_wide(const float* qbar, const float* kbar, int* idx, Counts cn
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((select_kernel<KPL, D>), dim3(G * groups), dim3(256), lds, st, qbar, kbar,
-                       nullptr, idx, cnt, n_l, K, R, M, scale);
+                       nullptr, idx, cnt, n_l, K, R, M, scale, causal);
     return hipGetLastError();
 }
 
@@ -571,10 +623,10 @@ hipError_t launch_select_d(const Geo& g, const Ws& w, bool zero_counts, hipStrea
                    : M <= 64 ? launch_mfma<4, D> : M <= 128 ? launch_mfma<8, D>
                    : M <= 256 ? launch_mfma<16, D> : M <= 512 ? launch_mfma<32, D>
                    : launch_mfma<64, D>;
-            e = f(qb, kb, parent, out, cnt, g.G, g.n[l], K, M, g.scale, st);
+            e = f(qb, kb, parent, out, cnt, g.G, g.n[l], K, M, g.scale, (int)g.causal, st);
         } else {
             auto f = M <= 2048 ? launch_wide<32, D> : launch_wide<64, D>;
-            e = f(qb, kb, out, cnt, g.G, g.n[l], K, g.scale, st);
+            e = f(qb, kb, out, cnt, g.G, g.n[l], K, g.scale, (int)g.causal, st);
         }
         if (e != hipSuccess) return e;
     }

@@ -38,12 +38,13 @@ __device__ __forceinline__ Cands make_cands(const Geo& g, const Ws& w, int l, in
 // 16-bit mask of which of the bins 16*grp .. 16*grp+15 query block i selected,
 // and in *first the number of its entries below bin 16*grp.  The list is
 // ascending, so the hits form one run starting at *first: the hit in bin b
-// sits at position *first + popcount(mask & ((1 << b) - 1)).
+// sits at position *first + popcount(mask & ((1 << b) - 1)).  Unused slots
+// (-1, after the picks of a causal row) are neither hits nor below.
 __device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp, int* first)
 {
     unsigned m = 0;
     int below = 0;
-    const int lo = BS * grp;
+    const unsigned lo = BS * grp;
     if ((K & 3) == 0) {
         for (int e = 0; e < K; e += 4) {
             const int4 j4 = *(const int4*)(I + e);
@@ -51,13 +52,14 @@ __device__ __forceinline__ unsigned hit_mask(const int* I, int K, int grp, int* 
             m |= ((j4.y >> 4) == grp) ? 1u << (j4.y & 15) : 0u;
             m |= ((j4.z >> 4) == grp) ? 1u << (j4.z & 15) : 0u;
             m |= ((j4.w >> 4) == grp) ? 1u << (j4.w & 15) : 0u;
-            below += (j4.x < lo) + (j4.y < lo) + (j4.z < lo) + (j4.w < lo);
+            below += ((unsigned)j4.x < lo) + ((unsigned)j4.y < lo) + ((unsigned)j4.z < lo) +
+                     ((unsigned)j4.w < lo);
         }
     } else {
         for (int e = 0; e < K; ++e) {
             const int j = I[e];
             m |= ((j >> 4) == grp) ? 1u << (j & 15) : 0u;
-            below += j < lo;
+            below += (unsigned)j < lo;
         }
     }
     *first = below;

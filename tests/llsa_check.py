@@ -150,8 +150,10 @@ def grad_tol(ref, base: float) -> float:
     return max(base, float(np.abs(ref).max()) * 2.0 ** -6)
 
 
-def check_selection(w, gpu, orc_pyr, exact: bool):
-    """Level-by-level comparison; returns the number of rows that differ."""
+def check_selection(w, gpu, orc_pyr, exact: bool, causal: bool = False):
+    """Level-by-level comparison; returns the number of rows that differ.
+    causal: the causal selection (the row's own block plus its best K-1
+    earlier candidates, -1 in the slots left)."""
     qp, kp = orc_pyr
     scale = 1.0 / np.sqrt(w.d)
     diffs = 0
@@ -162,7 +164,7 @@ def check_selection(w, gpu, orc_pyr, exact: bool):
             sl = slice(h, h + 1)
             return oracle.select_level(qp[l - 1][sl], kp[l - 1][sl],
                                        None if parent is None else parent[sl], level_k(w, l), BS,
-                                       scale)
+                                       scale, causal=causal)
 
         parts = per_head(head, w.G)
         want = np.concatenate([p_[0] for p_ in parts])
@@ -174,20 +176,36 @@ def check_selection(w, gpu, orc_pyr, exact: bool):
         else:
             assert np.all(gap[bad] < GAP), \
                 "level %d: mismatch in rows with gap >= %g: %s" % (l, GAP, gap[bad][gap[bad] >= GAP][:5])
-        # every GPU row is a valid selection: ascending, distinct, children of parent
-        assert np.all(np.diff(got, axis=2) > 0)
+        # every GPU row is a valid selection: ascending, distinct, children of
+        # the parent's picks (causal: the valid picks first, the row itself
+        # among them and none after it, then -1)
+        valid = got >= 0
+        if causal:
+            assert np.all(valid[..., :1]) and np.all(valid[..., :-1] | ~valid[..., 1:])
+            rows = np.arange(got.shape[1])[None, :, None]
+            assert np.all(np.any(got == rows, axis=2)) and np.all(~valid | (got <= rows))
+            pairs = valid[..., 1:]
+            assert np.all(np.diff(got, axis=2)[pairs] > 0)
+        else:
+            assert np.all(valid) and np.all(np.diff(got, axis=2) > 0)
         if parent is not None:
             par = np.repeat(parent, BS, axis=1)[:, :got.shape[1]]
-            assert np.all(np.any((got[..., :, None] // BS) == par[..., None, :], axis=3))
+            par = np.where(par >= 0, par, -2)  # an unused parent slot has no children
+            hit = np.any((got[..., :, None] // BS) == par[..., None, :], axis=3)
+            assert np.all(hit | ~valid)
         diffs += int(bad.sum())
     return diffs
 
 
 def check_transpose(gpu, w):
+    """The key->query lists, exactly: rowptr, and col up to rowptr[n] (causal
+    rows hold fewer than K picks, so the n K slots of a head end in unused
+    ones, which the library leaves untouched)."""
     for l in range(w.levels):
         rp, col = oracle.transpose(gpu["idx"][l])
         np.testing.assert_array_equal(gpu["rowptr"][l], rp)
-        np.testing.assert_array_equal(gpu["col"][l], col)
+        for h in range(rp.shape[0]):
+            np.testing.assert_array_equal(gpu["col"][l][h, :rp[h, -1]], col[h, :rp[h, -1]])
 
 
 def assert_close(got, want, max_abs, mean_abs=None, what=""):
@@ -197,3 +215,26 @@ def assert_close(got, want, max_abs, mean_abs=None, what=""):
     if mean_abs is not None:
         assert err.mean() <= mean_abs, "%s: mean-abs %.3g > %.3g" % (what, err.mean(), mean_abs)
     return float(err.max()), float(err.mean())
+
+
+def full_check(w, flags=0, inp=None):
+    """Every stage of the HIP path against the oracle, for every head, block
+    and token: pyramid, selection (gap rule on bf16, exact on fp32),
+    transposes (exact), out and lse, and the gradients."""
+    inp = synth.make_inputs(w) if inp is None else inp
+    gpu = gpu_run(w, inp, flags=flags)
+    z = oracle_inputs(w, inp)
+    tol = TOL[w.dtype]
+    qp, kp, vp = (oracle.pool(z[n], BS, w.levels) for n in ("q", "k", "v"))
+    for l in range(w.levels):  # pyramid: fp32 sums of exact inputs
+        for name, ref in (("qbar", qp), ("kbar", kp), ("vbar", vp)):
+            assert_close(gpu[name][l], ref[l], 2e-6, what="%s level %d" % (name, l + 1))
+    check_selection(w, gpu, (qp, kp), exact=(w.dtype == "f32"),
+                    causal=bool(flags & oracle.CAUSAL))
+    check_transpose(gpu, w)
+    o, lse, dq, dk, dv = oracle_values(w, z, kp, vp, gpu["idx"], flags)
+    assert_close(gpu["out"], o, tol["out_max"], tol["out_mean"], "out")
+    assert_close(gpu["lse"], lse, tol["out_max"], tol["out_mean"], "lse")
+    for n_, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(gpu[n_], ref, tol["grad_max"], what=n_)
+    return gpu

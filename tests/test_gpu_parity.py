@@ -11,8 +11,8 @@ import pytest
 
 import oracle
 import synth
-from llsa_check import (BS, TOL, assert_close, check_selection, check_transpose, gpu_run,
-                        grad_tol, oracle_inputs, oracle_values, to_device, ws_array)
+from llsa_check import (BS, TOL, assert_close, check_selection, check_transpose, full_check,
+                        gpu_run, grad_tol, oracle_inputs, oracle_values, to_device, ws_array)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,26 +35,7 @@ SMALL = [
 ]
 
 
-def _full_check(w, flags=0, inp=None):
-    """Every stage of the HIP path against the oracle, for every head, block
-    and token: pyramid, selection (gap rule on bf16, exact on fp32),
-    transposes (exact), out and lse, and the gradients."""
-    inp = synth.make_inputs(w) if inp is None else inp
-    gpu = gpu_run(w, inp, flags=flags)
-    z = oracle_inputs(w, inp)
-    tol = TOL[w.dtype]
-    qp, kp, vp = (oracle.pool(z[n], BS, w.levels) for n in ("q", "k", "v"))
-    for l in range(w.levels):  # pyramid: fp32 sums of exact inputs
-        for name, ref in (("qbar", qp), ("kbar", kp), ("vbar", vp)):
-            assert_close(gpu[name][l], ref[l], 2e-6, what="%s level %d" % (name, l + 1))
-    check_selection(w, gpu, (qp, kp), exact=(w.dtype == "f32"))
-    check_transpose(gpu, w)
-    o, lse, dq, dk, dv = oracle_values(w, z, kp, vp, gpu["idx"], flags)
-    assert_close(gpu["out"], o, tol["out_max"], tol["out_mean"], "out")
-    assert_close(gpu["lse"], lse, tol["out_max"], tol["out_mean"], "lse")
-    for n_, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
-        assert_close(gpu[n_], ref, tol["grad_max"], what=n_)
-    return gpu
+_full_check = full_check
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
