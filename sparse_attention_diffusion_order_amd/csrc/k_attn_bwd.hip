@@ -563,7 +563,9 @@ struct QBlock {
 // and the timing of their overlapping query-block fetches.
 constexpr int DKDV_WPG = 1;
 
-template <int D, int WPG>
+// CAUSAL: LLSA_CAUSAL (its own instance, so that the default one carries no
+// mask code)
+template <int D, int WPG, bool CAUSAL>
 __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __restrict__ q,
                                                       const unsigned short* __restrict__ k,
                                                       const unsigned short* __restrict__ v,
@@ -634,7 +636,7 @@ __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __re
         for (int r = 0; r < 4; ++r) {
             float p = fast_exp2(fmaf(s[r], c, lr[r]));
             // the causal diagonal block: key nq is seen by queries at or after it
-            if (f.diag && nq > 4 * gq + r) p = 0.f;
+            if (CAUSAL && f.diag && nq > 4 * gq + r) p = 0.f;
             float ds = p * (dp[r] - dr[r]);
             if (enrich1) {
                 p = fmaf(pr[r], 1.0f / BS, p);
@@ -678,7 +680,7 @@ __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __re
         for (int u = 0; u < NI; ++u) f.d[u] = bload8(rdo, voff + 1024 * u, so);
         // (the causal diagonal block does not see block j's pooled token:
         // an empty resource reads 0)
-        f.diag = g.causal && i == j;
+        f.diag = CAUSAL && i == j;
         const __amdgpu_buffer_rsrc_t rpe = make_rsrc(
             w.pe1 + (((long)gh * g.n[1] + i) * g.K + sl) * 2 * BS, f.diag ? 0u : 2 * BS * 4);
         f.x = bloadf(rlse, off_lse, i * BS * 4) + bloadf(rdel, off_del, i * BS * 4) +
@@ -1230,7 +1232,8 @@ hipError_t launch_attn_dkdv_d(const void* q, const void* k, const void* v, const
 {
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
-        hipLaunchKernelGGL((dkdv_bf16<D, DKDV_WPG>), dim3((unsigned)((nblk + DKDV_WPG - 1) / DKDV_WPG)),
+        auto kern = g.causal ? dkdv_bf16<D, DKDV_WPG, true> : dkdv_bf16<D, DKDV_WPG, false>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + DKDV_WPG - 1) / DKDV_WPG)),
                            dim3(64 * DKDV_WPG), 0, st,
                            (const unsigned short*)q, (const unsigned short*)k,
                            (const unsigned short*)v, lse, (const unsigned short*)dout,
