@@ -361,6 +361,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--flags", type=int, default=0,
+                    help="llsa flags of the timed calls (e.g. 16: causal); the headline uses 0. "
+                         "With other flags FLOPs are still counted as for flags 0, and the "
+                         "measured-traffic and CPU-baseline fields are left out")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-dist", action="store_true",
@@ -433,7 +437,7 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     row_bytes = d * q_r.element_size()
-    shape = (B, H, N, d, 16, K, L, dcode, 0, ws, ws_bytes, sh)
+    shape = (B, H, N, d, 16, K, L, dcode, args.flags, ws, ws_bytes, sh)
 
     stages = ["zorder", "pool", "select", "attn_fwd", "transpose", "dq", "enrich", "dkdv"]
 
@@ -548,7 +552,8 @@ def main():
     kname = max(("attn_fwd", "dq", "dkdv"), key=lambda s: stage_ms[s])
     kms = stage_ms[kname]
     achieved = abytes[kname] / (kms * 1e-3) / 1e9
-    traffic = load_traffic(kname, w)
+    # (the committed counter summaries were taken with flags 0)
+    traffic = load_traffic(kname, w) if not args.flags else None
     roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
@@ -564,7 +569,10 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "block_size": 16,
                    "topk": K, "levels": L, "grid": grid_name(w),
-                   "sigma_px": w.sigma, "seed": w.seed},
+                   "sigma_px": w.sigma, "seed": w.seed,
+                   **({"flags": args.flags,
+                       "flops_counted_as": "flags 0 (the work of the default, non-causal path)"}
+                      if args.flags else {})},
         "fwd_ms": round(fwd_ms, 5), "fwd_tflops": round(f["fwd"] / (fwd_ms * 1e-3) / 1e12, 3),
         "fwdbwd_ms": round(fwdbwd_ms, 5),
         "fwdbwd_tflops": round(f["fwdbwd"] / (fwdbwd_ms * 1e-3) / 1e12, 3),
@@ -577,7 +585,8 @@ def main():
         # measured HBM bytes per launch (committed rocprofv3 FETCH_SIZE +
         # WRITE_SIZE summary of the current kernel sources), where available
         "stage_hbm_mb": {k_: round(t_ / 1e6, 1) for k_, t_ in
-                         ((k_, load_traffic(k_, w)) for k_ in stages) if t_ is not None},
+                         ((k_, load_traffic(k_, w) if not args.flags else None)
+                          for k_ in stages) if t_ is not None},
         "roofline": roofline,
         "timing": timing,
         # each attention kernel against its own algorithmic roofline,
@@ -615,7 +624,7 @@ def main():
         torch.cuda.synchronize()
         res["calib_copy_bytes"] = nb
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.flags:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(res), flush=True)

@@ -36,6 +36,8 @@ def test_noalloc_forward_matches_forward_twice():
     _noalloc_vs_forward(W("small_l3", 1, 2, 128, 64, "bf16", 3, 2, 2.0))
     # fp32 and an enrichment variant on the same scratch
     _noalloc_vs_forward(W("small_f32", 1, 2, 32, 64, "f32", 2, 2, 2.0), flags=4)
+    # causal rows (unused slots -1 in the scratch's index lists)
+    _noalloc_vs_forward(W("small_causal", 1, 2, 64, 64, "bf16", 2, 4, 2.0), flags=16)
 
 
 def test_noalloc_forward_refuses_a_shape_beyond_the_scratch():
