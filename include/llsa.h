@@ -183,6 +183,23 @@ int llsa_forward(const void* q, const void* k, const void* v, void* out, float* 
                  int dtype, unsigned flags, void* workspace, size_t ws_bytes,
                  void* stream);
 
+/* llsa_forward on raster-order inputs, the grid order folded into the
+ * pooling pass (README, reordering of non-sequential data, then usage):
+ * q_raster, k_raster, v_raster are [B][H][frames*height*width][d] in raster
+ * order (frame, row, column).  The call writes their grid-ordered copies to
+ * q, k, v -- the bytes llsa_grid_order would write, and what llsa_backward
+ * takes -- while it pools them, so each input is read once, then selects and
+ * attends exactly as llsa_forward on q, k, v (out, lse in grid order; the
+ * same results bit for bit).  N = frames*height*width.  The raster buffers
+ * must not overlap q, k, v.  Grid sides as for llsa_grid_order, and the
+ * shape, top-k, flags and workspace as for llsa_forward.  Errors: those of
+ * llsa_grid_order and llsa_forward. */
+int llsa_forward_grid(const void* q_raster, const void* k_raster, const void* v_raster,
+                      void* q, void* k, void* v, void* out, float* lse, int B, int H,
+                      int frames, int height, int width, int d, int block_size, int topk,
+                      int levels, int dtype, unsigned flags, void* workspace,
+                      size_t ws_bytes, void* stream);
+
 /* LLSA backward (skill summary, "Core Technique" 3): given dout, writes dq,
  * dk, dv ([B][H][N][d], dtype).  Reuses the forward's pyramid and index lists
  * from the workspace (no re-selection; selection passes no gradient), builds

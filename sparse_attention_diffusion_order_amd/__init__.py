@@ -22,7 +22,8 @@ __all__ = [
     "llsa_forward",
     "llsa_backward", "llsa_forward_part", "llsa_backward_part", "llsa_strerror",
     "llsa_workspace_bytes_lk", "llsa_workspace_layout_lk", "llsa_forward_lk", "llsa_backward_lk",
-    "llsa_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "forward", "backward", "zorder", "grid_order",
+    "llsa_forward_noalloc", "llsa_forward_grid", "NOALLOC_SCRATCH_BYTES", "forward", "forward_grid",
+    "backward", "zorder", "grid_order",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -100,6 +101,8 @@ def load():
     lib.llsa_backward_lk.restype = I
     lib.llsa_forward_noalloc.argtypes = [P] * 5 + shape + [U, P]
     lib.llsa_forward_noalloc.restype = I
+    lib.llsa_forward_grid.argtypes = [P] * 8 + [I] * 10 + [U, P, S, P]
+    lib.llsa_forward_grid.restype = I
     lib.llsa_strerror.argtypes = [I]
     lib.llsa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -226,6 +229,16 @@ def llsa_forward_noalloc(q, k, v, out, lse, B, H, N, d, block_size, topk, levels
                                        _stream(stream)), "llsa_forward_noalloc")
 
 
+def llsa_forward_grid(q_raster, k_raster, v_raster, q, k, v, out, lse, B, H, frames, height,
+                      width, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
+                      stream=None):
+    _check(load().llsa_forward_grid(_ptr(q_raster), _ptr(k_raster), _ptr(v_raster), _ptr(q),
+                                    _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, frames, height,
+                                    width, d, block_size, topk, levels, dtype, flags,
+                                    _ptr(workspace), ws_bytes, _stream(stream)),
+           "llsa_forward_grid")
+
+
 def llsa_forward_part(part, q, k, v, out, lse, B, H, N, d, block_size, topk, levels, dtype,
                       flags, workspace, ws_bytes, stream=None):
     _check(load().llsa_forward_part(part, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B,
@@ -304,6 +317,42 @@ def forward(q, k, v, topk, levels: int, flags: int = 0, workspace=None, stream=N
     workspace._llsa_forward = {"shape": (B, H, N, d), "dtype": q.dtype, "topk": topk,
                                "levels": int(levels), "flags": int(flags)}
     return out, lse, workspace
+
+
+def forward_grid(q_raster, k_raster, v_raster, frames: int, height: int, width: int, topk: int,
+                 levels: int, flags: int = 0, workspace=None, stream=None):
+    """The forward on raster-order q, k, v [B, H, frames*height*width, d]:
+    returns (q, k, v, out, lse, workspace) with q, k, v the grid-ordered
+    copies (written by the pooling pass) that `backward` takes, and out, lse
+    in grid order -- the results of grid_order and forward, bit for bit."""
+    import torch
+    if q_raster.dim() != 4:
+        raise ValueError("q_raster must be [B, H, N, d]")
+    B, H, N, d = q_raster.shape
+    if N != frames * height * width:
+        raise ValueError("N must equal frames*height*width")
+    dt = _dtype_code(q_raster)
+    if not q_raster.is_cuda:
+        raise ValueError("q, k, v must be on a GPU (got %s)" % q_raster.device)
+    _check_tensors((("q_raster", q_raster), ("k_raster", k_raster), ("v_raster", v_raster)),
+                   q_raster.shape, q_raster.dtype, q_raster.device)
+    if not isinstance(topk, int):
+        raise ValueError("forward_grid takes one top-k for every level")
+    nbytes = llsa_workspace_bytes(B, H, N, d, 16, topk, levels, dt)
+    if nbytes == 0:
+        raise LlsaError(-2, "llsa_workspace_bytes")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q_raster.device)
+    elif (not workspace.is_cuda or workspace.device != q_raster.device
+          or workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % q_raster.device)
+    q, k, v, out = (torch.empty_like(q_raster) for _ in range(4))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q_raster.device)
+    llsa_forward_grid(q_raster, k_raster, v_raster, q, k, v, out, lse, B, H, frames, height,
+                      width, d, 16, topk, levels, dt, flags, workspace, workspace.numel(), stream)
+    workspace._llsa_forward = {"shape": (B, H, N, d), "dtype": q.dtype, "topk": topk,
+                               "levels": int(levels), "flags": int(flags)}
+    return q, k, v, out, lse, workspace
 
 
 def backward(q, k, v, out, lse, dout, topk=None, levels=None, workspace=None, flags=None,

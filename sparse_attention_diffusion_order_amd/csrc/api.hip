@@ -390,6 +390,31 @@ int llsa_forward_lk(const void* q, const void* k, const void* v, void* out, floa
     return run_forward(q, k, v, out, lse, dtype, p);
 }
 
+int llsa_forward_grid(const void* q_raster, const void* k_raster, const void* v_raster,
+                      void* q, void* k, void* v, void* out, float* lse, int B, int H,
+                      int frames, int height, int width, int d, int block_size, int topk,
+                      int levels, int dtype, unsigned flags, void* workspace,
+                      size_t ws_bytes, void* stream)
+{
+    if (!q_raster || !k_raster || !v_raster || !q || !k || !v || !out || !lse)
+        return LLSA_ERR_NULL;
+    const int lim = 1 << 15;
+    if (frames < 1 || height < 1 || width < 1 || frames > lim || height > lim || width > lim ||
+        (long long)frames * height * width > (1ll << 30))
+        return LLSA_ERR_SHAPE;
+    const int N = (int)((long long)frames * height * width);  // <= 2^30; validate caps it
+    Prep p;
+    int rc = prepare(B, H, N, d, block_size, UniformK(topk, levels).ks, levels, dtype, flags,
+                     workspace, ws_bytes, stream, &p);
+    if (rc) return rc;
+    rc = hip_rc(launch_pool_gather(q_raster, k_raster, v_raster, q, k, v,
+                                   make_grid_geo(frames, height, width), dtype, p.geo, p.ws, p.st));
+    if (rc) return rc;
+    rc = hip_rc(launch_select(p.geo, p.ws, false, p.st));
+    if (rc) return rc;
+    return run_forward_part(LLSA_PART_ATTN, q, k, v, out, lse, dtype, p);
+}
+
 int llsa_forward(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                  int H, int N, int d, int block_size, int topk, int levels, int dtype,
                  unsigned flags, void* workspace, size_t ws_bytes, void* stream)

@@ -392,6 +392,78 @@ __device__ __forceinline__ void for_each_pooled(const Geo& g, const Ws& w, int g
     }
 }
 
+// ------------------------------------------------------------ grid order
+
+__device__ __forceinline__ unsigned gather_bits(unsigned x)  // inverse of spread_bits
+{
+    x &= 0x55555555u;
+    x = (x | (x >> 1)) & 0x33333333u;
+    x = (x | (x >> 2)) & 0x0f0f0f0fu;
+    x = (x | (x >> 4)) & 0x00ff00ffu;
+    x = (x | (x >> 8)) & 0x0000ffffu;
+    return x;
+}
+
+__device__ __forceinline__ unsigned gather3(unsigned x)  // inverse of spread3
+{
+    x &= 0x09249249u;
+    x = (x | (x >> 2)) & 0x030c30c3u;
+    x = (x | (x >> 4)) & 0x0300f00fu;
+    x = (x | (x >> 8)) & 0xff0000ffu;
+    x = (x | (x >> 16)) & 0x000003ffu;
+    return x;
+}
+
+// Grid order of frames x height x width cells (LLSA README, reordering of
+// non-sequential data, extended to rectangles and video): tiles of S x S
+// (S^3 for video) cells in raster order, S the largest power of two dividing
+// every side; Morton order inside a tile with the frame bit above the row bit
+// above the column bit.  A square power-of-two image is one tile.
+struct GridGeo {
+    unsigned H, W;        // rows, columns
+    unsigned tw, th;      // tiles per row, tile rows per frame slab
+    int s_log2;           // log2 S
+    int video;            // 3-D tiles
+};
+
+
+inline GridGeo make_grid_geo(int frames, int height, int width)
+{
+    auto p2 = [](int v) { return v & -v; };
+    int S = p2(height) < p2(width) ? p2(height) : p2(width);
+    const int video = frames > 1;
+    if (video && p2(frames) < S) S = p2(frames);
+    GridGeo gg;
+    gg.H = (unsigned)height;
+    gg.W = (unsigned)width;
+    gg.tw = (unsigned)(width / S);
+    gg.th = (unsigned)(height / S);
+    gg.s_log2 = __builtin_ctz((unsigned)S);
+    gg.video = video;
+    return gg;
+}
+
+// The raster cell (frame, row, column flattened) of grid-order position p.
+__device__ __forceinline__ unsigned grid_source(unsigned p, const GridGeo& gg)
+{
+    const int tb = (gg.video ? 3 : 2) * gg.s_log2;  // bits of a position inside a tile
+    const unsigned code = p & ((1u << tb) - 1u), tile = p >> tb;
+    unsigned yy, xx, tt = 0;
+    if (gg.video) {
+        xx = gather3(code);
+        yy = gather3(code >> 1);
+        tt = gather3(code >> 2);
+    } else {
+        xx = gather_bits(code);
+        yy = gather_bits(code >> 1);
+    }
+    const unsigned tx = tile % gg.tw, rest = tile / gg.tw;
+    const unsigned ty = rest % gg.th, tz = rest / gg.th;
+    const unsigned y = (ty << gg.s_log2) | yy, x = (tx << gg.s_log2) | xx;
+    const unsigned t = (tz << gg.s_log2) | tt;  // frame (0 for an image)
+    return (t * gg.H + y) * gg.W + x;
+}
+
 // ------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 
@@ -403,6 +475,11 @@ hipError_t launch_zorder(const void* src, void* dst, long long outer, int side, 
 // select zeroes them itself (the selection part on its own)
 hipError_t launch_pool(const void* q, const void* k, const void* v, int dtype, const Geo& g,
                        const Ws& w, bool zero_counts, hipStream_t st);
+// the pool pass that also gathers raster-order q, k, v (qr, kr, vr) into q,
+// k, v in grid order; zeroes the selection's pick counters like launch_pool
+hipError_t launch_pool_gather(const void* qr, const void* kr, const void* vr, void* q, void* k,
+                              void* v, const GridGeo& gg, int dtype, const Geo& g, const Ws& w,
+                              hipStream_t st);
 hipError_t launch_select(const Geo& g, const Ws& w, bool zero_counts, hipStream_t st);
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                            int dtype, const Geo& g, const Ws& w, hipStream_t st);

@@ -7,11 +7,18 @@
 // not divide N (the children then weighted by the tokens each covers).
 // Levels are computed recursively, in float32.
 //
+// With GATHER the pass also performs the grid-order gather (LLSA README,
+// reordering of non-sequential data): q, k, v are read in raster order, each
+// token from the raster cell its grid-order position names, and the
+// grid-ordered copies are written as the pass goes -- the same bytes as
+// llsa_grid_order, and the same sums, without reading the tensors twice.
+//
 // pool_l12: one workgroup per 256 consecutive tokens of one head and one
 // tensor.  Thread (blk, sub) sums the 16 tokens of level-1 block blk over the
-// channels 4*sub .. 4*sub+3 (and 64 + 4*sub .. when d = 128), so each 64-channel
-// part of a token row is read whole by 16 adjacent lanes.  Level 2 (one block per workgroup) is the mean of the
-// 16 level-1 means, formed in LDS.  pool_up forms levels >= 3 from level l-1.
+// d/16 channels (d/16) sub .. (d/16)(sub+1) - 1, so a token row is read whole
+// by 16 adjacent lanes with one load each (8 or 16 bytes in bf16).  Level 2
+// (one block per workgroup) is the mean of the 16 level-1 means, formed in
+// LDS.  pool_up forms levels >= 3 from level l-1.
 // The pooled keys and values are also stored rounded to bf16 (the operands
 // the attention kernels feed to the MFMA).  pool_l12 also zeroes the
 // selection's pick counters when given them (llsa_forward), which saves the
@@ -21,33 +28,74 @@
 namespace llsa {
 namespace {
 
-template <typename T> struct Vec4;
-template <> struct Vec4<float> {
-    static __device__ __forceinline__ float4 load(const float* p)
+// C consecutive channels (C = 4 or 8) of one token row: load() reads them
+// raw (one 8- or 16-byte load in bf16, one or two 16-byte loads in fp32),
+// add() widens them to float and adds them to s
+template <typename T, int C> struct Row;
+template <int C> struct Row<float, C> {
+    float4 r[C / 4];
+    __device__ __forceinline__ void load(const float* p)
     {
-        return *(const float4*)p;
+#pragma unroll
+        for (int h = 0; h < C / 4; ++h) r[h] = ((const float4*)p)[h];
+    }
+    __device__ __forceinline__ void add(float (&s)[C]) const
+    {
+#pragma unroll
+        for (int h = 0; h < C / 4; ++h) {
+            s[4 * h] += r[h].x; s[4 * h + 1] += r[h].y; s[4 * h + 2] += r[h].z; s[4 * h + 3] += r[h].w;
+        }
+    }
+    __device__ __forceinline__ void store(float* p) const
+    {
+#pragma unroll
+        for (int h = 0; h < C / 4; ++h) ((float4*)p)[h] = r[h];
     }
 };
-template <> struct Vec4<unsigned short> {
-    static __device__ __forceinline__ float4 load(const unsigned short* p)
+template <int C> struct Row<unsigned short, C> {
+    unsigned u[C / 2];  // two bf16 per word, the lower channel in the low half
+    __device__ __forceinline__ void load(const unsigned short* p)
     {
-        uint2 u = *(const uint2*)p;
-        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+        if constexpr (C == 4) {
+            const uint2 x = *(const uint2*)p;
+            u[0] = x.x; u[1] = x.y;
+        } else {
+            const uint4 x = *(const uint4*)p;
+            u[0] = x.x; u[1] = x.y; u[2] = x.z; u[3] = x.w;
+        }
+    }
+    __device__ __forceinline__ void add(float (&s)[C]) const
+    {
+#pragma unroll
+        for (int h = 0; h < C / 2; ++h) {
+            s[2 * h] += __uint_as_float(u[h] << 16);
+            s[2 * h + 1] += __uint_as_float(u[h] & 0xffff0000u);
+        }
+    }
+    __device__ __forceinline__ void store(unsigned short* p) const
+    {
+        if constexpr (C == 4)
+            *(uint2*)p = make_uint2(u[0], u[1]);
+        else
+            *(uint4*)p = make_uint4(u[0], u[1], u[2], u[3]);
     }
 };
 
-__device__ __forceinline__ void put_bf16x4(unsigned short* dst, long off, float4 s)
-{
-    u16x4 o = {f2bf(s.x), f2bf(s.y), f2bf(s.z), f2bf(s.w)};
-    *(u16x4*)(dst + off) = o;
-}
+// Raster sources and grid-ordered destinations of the gathering pass.
+template <typename T>
+struct Gather {
+    T* q;
+    T* k;
+    T* v;
+    GridGeo gg;
+};
 
-template <typename T, int D>
+template <typename T, int D, bool GATHER>
 __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T* __restrict__ k,
-                                                const T* __restrict__ v, Geo g, Ws w)
+                                                const T* __restrict__ v, Geo g, Ws w,
+                                                Gather<T> gt)
 {
-    constexpr int NC = D / 64;  // 4-channel groups per thread: channels 4 sub + 64 c
+    constexpr int C = D / 16;  // channels per thread: C sub .. C sub + C - 1
     __shared__ float m1[16][D];
     if (w.cnt_all) {
         // zero the selection's pick counters (the selection pass that follows
@@ -68,43 +116,67 @@ __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T
     const int b0 = (blockIdx.x % wg_per_head) * 16;  // first level-1 block
     const int blk = threadIdx.x >> 4, sub = threadIdx.x & 15;
     const bool live = b0 + blk < n1;
-    float4 s[NC];
+    float s[C];
 #pragma unroll
-    for (int cg = 0; cg < NC; ++cg) s[cg] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < C; ++c) s[c] = 0.f;
     if (live) {
-        const T* p = x + ((long)gh * g.N + (long)(b0 + blk) * BS) * D + 4 * sub;
+        const T* p = x + ((long)gh * g.N + (long)(b0 + blk) * BS) * D + C * sub;
+        Row<T, C> r[BS];
+        if (GATHER) {
+            // token (b0 + blk) 16 + t of the head comes from the raster cell
+            // its grid position names; its grid-ordered copy goes to position.
+            // When a tile holds at least 16 cells, the block's 16 positions
+            // differ in the low four bits of the in-tile code only: x0 y0 x1
+            // y1 (image) or x0 y0 t0 x1 (video), offsets from the first cell.
+            const T* src = x + (long)gh * g.N * D + C * sub;
+            const unsigned p0 = (unsigned)(b0 + blk) * BS;
+            const GridGeo& gg = gt.gg;
+            if ((gg.video ? 3 : 2) * gg.s_log2 >= 4) {
+                const long base = grid_source(p0, gg);
 #pragma unroll
-        for (int cg = 0; cg < NC; ++cg) {
-            float4 r[BS];
+                for (int t = 0; t < BS; ++t) {
+                    const unsigned b0_ = t & 1, b1_ = (t >> 1) & 1, b2_ = (t >> 2) & 1,
+                                   b3_ = (t >> 3) & 1;
+                    const long off = gg.video
+                                         ? ((long)b2_ * gg.H + b1_) * gg.W + (b0_ | (b3_ << 1))
+                                         : (long)(b1_ | (b3_ << 1)) * gg.W + (b0_ | (b2_ << 1));
+                    r[t].load(src + (base + off) * D);
+                }
+            } else {
 #pragma unroll
-            for (int t = 0; t < BS; ++t) r[t] = Vec4<T>::load(p + (long)t * D + 64 * cg);
-#pragma unroll
-            for (int t = 0; t < BS; ++t) {
-                s[cg].x += r[t].x;
-                s[cg].y += r[t].y;
-                s[cg].z += r[t].z;
-                s[cg].w += r[t].w;
+                for (int t = 0; t < BS; ++t) r[t].load(src + (long)grid_source(p0 + t, gg) * D);
             }
+            T* dst = (tensor == 0 ? gt.q : tensor == 1 ? gt.k : gt.v) +
+                     ((long)gh * g.N + (long)(b0 + blk) * BS) * D + C * sub;
+#pragma unroll
+            for (int t = 0; t < BS; ++t) r[t].store(dst + (long)t * D);
+        } else {
+#pragma unroll
+            for (int t = 0; t < BS; ++t) r[t].load(p + (long)t * D);
         }
+#pragma unroll
+        for (int t = 0; t < BS; ++t) r[t].add(s);
         const float inv = 1.0f / BS;
         const long row = (long)gh * n1 + b0 + blk;
 #pragma unroll
-        for (int cg = 0; cg < NC; ++cg) {
-            s[cg] = make_float4(s[cg].x * inv, s[cg].y * inv, s[cg].z * inv, s[cg].w * inv);
-            *(float4*)(lv1 + row * D + 4 * sub + 64 * cg) = s[cg];
-            if (tensor)
-                put_bf16x4(tensor == 1 ? w.kb16 : w.vb16, (w.prow[0] + row) * D + 4 * sub + 64 * cg,
-                           s[cg]);
+        for (int c = 0; c < C; ++c) s[c] *= inv;
+#pragma unroll
+        for (int h = 0; h < C / 4; ++h)
+            *(float4*)(lv1 + row * D + C * sub + 4 * h) =
+                make_float4(s[4 * h], s[4 * h + 1], s[4 * h + 2], s[4 * h + 3]);
+        if (tensor) {
+            unsigned short* dst = (tensor == 1 ? w.kb16 : w.vb16) + (w.prow[0] + row) * D + C * sub;
+#pragma unroll
+            for (int h = 0; h < C / 4; ++h) {
+                const u16x4 o = {f2bf(s[4 * h]), f2bf(s[4 * h + 1]), f2bf(s[4 * h + 2]),
+                                 f2bf(s[4 * h + 3])};
+                *(u16x4*)(dst + 4 * h) = o;
+            }
         }
     }
     if (g.L >= 2) {  // b0 is a multiple of 16, so this workgroup is one level-2 block
 #pragma unroll
-        for (int cg = 0; cg < NC; ++cg) {
-            m1[blk][4 * sub + 64 * cg + 0] = s[cg].x;
-            m1[blk][4 * sub + 64 * cg + 1] = s[cg].y;
-            m1[blk][4 * sub + 64 * cg + 2] = s[cg].z;
-            m1[blk][4 * sub + 64 * cg + 3] = s[cg].w;
-        }
+        for (int c = 0; c < C; ++c) m1[blk][C * sub + c] = s[c];
         __syncthreads();
         if (threadIdx.x < D) {
             // the mean of the tokens of the level-2 block: its level-1 blocks
@@ -150,18 +222,27 @@ __global__ __launch_bounds__(256) void pool_up(Geo g, Ws w, int l)
     if (tensor) (tensor == 1 ? w.kb16 : w.vb16)[(w.prow[l - 1] + row) * D + c] = f2bf(mean);
 }
 
+// gq, gk, gv != nullptr: q, k, v are raster-order sources, gathered into gq,
+// gk, gv in grid order (GridGeo gg) by the same pass
 template <int D>
-hipError_t launch_pool_d(const void* q, const void* k, const void* v, int dtype, const Geo& g,
-                         const Ws& w, hipStream_t st)
+hipError_t launch_pool_d(const void* q, const void* k, const void* v, void* gq, void* gk,
+                         void* gv, const GridGeo& gg, int dtype, const Geo& g, const Ws& w,
+                         hipStream_t st)
 {
     dim3 grid(g.G * ((g.n[1] + 15) / 16), 3);
-    if (dtype == LLSA_BF16)
-        hipLaunchKernelGGL((pool_l12<unsigned short, D>), grid, dim3(256), 0, st,
-                           (const unsigned short*)q, (const unsigned short*)k,
-                           (const unsigned short*)v, g, w);
-    else
-        hipLaunchKernelGGL((pool_l12<float, D>), grid, dim3(256), 0, st, (const float*)q,
-                           (const float*)k, (const float*)v, g, w);
+    if (dtype == LLSA_BF16) {
+        using T = unsigned short;
+        const Gather<T> gt{(T*)gq, (T*)gk, (T*)gv, gg};
+        auto kern = gq ? pool_l12<T, D, true> : pool_l12<T, D, false>;
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const T*)q, (const T*)k, (const T*)v,
+                           g, w, gt);
+    } else {
+        using T = float;
+        const Gather<T> gt{(T*)gq, (T*)gk, (T*)gv, gg};
+        auto kern = gq ? pool_l12<T, D, true> : pool_l12<T, D, false>;
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const T*)q, (const T*)k, (const T*)v,
+                           g, w, gt);
+    }
     hipError_t e = hipGetLastError();
     for (int l = 3; l <= g.L && e == hipSuccess; ++l) {
         long total = (long)g.G * g.n[l] * D;
@@ -179,8 +260,17 @@ hipError_t launch_pool(const void* q, const void* k, const void* v, int dtype, c
 {
     Ws wz = w;
     if (!zero_counts) wz.cnt_all = nullptr;
-    return g.d == D128 ? launch_pool_d<D128>(q, k, v, dtype, g, wz, st)
-                       : launch_pool_d<D64>(q, k, v, dtype, g, wz, st);
+    const GridGeo gg{};
+    return g.d == D128 ? launch_pool_d<D128>(q, k, v, nullptr, nullptr, nullptr, gg, dtype, g, wz, st)
+                       : launch_pool_d<D64>(q, k, v, nullptr, nullptr, nullptr, gg, dtype, g, wz, st);
+}
+
+hipError_t launch_pool_gather(const void* qr, const void* kr, const void* vr, void* q, void* k,
+                              void* v, const GridGeo& gg, int dtype, const Geo& g, const Ws& w,
+                              hipStream_t st)
+{
+    return g.d == D128 ? launch_pool_d<D128>(qr, kr, vr, q, k, v, gg, dtype, g, w, st)
+                       : launch_pool_d<D64>(qr, kr, vr, q, k, v, gg, dtype, g, w, st);
 }
 
 }  // namespace llsa

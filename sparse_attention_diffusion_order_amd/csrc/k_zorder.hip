@@ -22,13 +22,13 @@ __device__ __forceinline__ unsigned spread_bits(unsigned x)  // 0bABCD -> 0b0A0B
     return x;
 }
 
-__device__ __forceinline__ unsigned gather_bits(unsigned x)  // inverse of spread_bits
+__device__ __forceinline__ unsigned spread3(unsigned x)  // bit b -> bit 3b (10 bits)
 {
-    x &= 0x55555555u;
-    x = (x | (x >> 1)) & 0x33333333u;
-    x = (x | (x >> 2)) & 0x0f0f0f0fu;
-    x = (x | (x >> 4)) & 0x00ff00ffu;
-    x = (x | (x >> 8)) & 0x0000ffffu;
+    x &= 0x000003ffu;
+    x = (x | (x << 16)) & 0xff0000ffu;
+    x = (x | (x << 8)) & 0x0300f00fu;
+    x = (x | (x << 4)) & 0x030c30c3u;
+    x = (x | (x << 2)) & 0x09249249u;
     return x;
 }
 
@@ -68,44 +68,13 @@ __global__ __launch_bounds__(256) void zorder_kernel(const V* __restrict__ src,
     }
 }
 
-__device__ __forceinline__ unsigned spread3(unsigned x)  // bit b -> bit 3b (10 bits)
-{
-    x &= 0x000003ffu;
-    x = (x | (x << 16)) & 0xff0000ffu;
-    x = (x | (x << 8)) & 0x0300f00fu;
-    x = (x | (x << 4)) & 0x030c30c3u;
-    x = (x | (x << 2)) & 0x09249249u;
-    return x;
-}
-
-__device__ __forceinline__ unsigned gather3(unsigned x)  // inverse of spread3
-{
-    x &= 0x09249249u;
-    x = (x | (x >> 2)) & 0x030c30c3u;
-    x = (x | (x >> 4)) & 0x0300f00fu;
-    x = (x | (x >> 8)) & 0xff0000ffu;
-    x = (x | (x >> 16)) & 0x000003ffu;
-    return x;
-}
-
-// Grid order of frames x height x width cells: tiles of S x S (S^3 for
-// video) cells in raster order, Morton order inside a tile with the frame bit
-// above the row bit above the column bit.  One VW-byte chunk per thread, as
-// in zorder_kernel; tile coordinates by division (any side).
-struct GridGeo {
-    unsigned H, W;        // rows, columns
-    unsigned tw, th;      // tiles per row, tile rows per frame slab
-    int s_log2;           // log2 S
-    int video;            // 3-D tiles
-};
-
 template <typename V>
 __global__ __launch_bounds__(256) void grid_kernel(const V* __restrict__ src, V* __restrict__ dst,
                                                    long long total, int cpr, unsigned n,
                                                    GridGeo gg, int inverse)
 {
     const int tb = (gg.video ? 3 : 2) * gg.s_log2;  // bits of a position inside a tile
-    const unsigned cmask = (1u << tb) - 1u, smask = (1u << gg.s_log2) - 1u;
+    const unsigned smask = (1u << gg.s_log2) - 1u;
     for (long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x; id < total;
          id += (long long)gridDim.x * blockDim.x) {
         const long long row = id / cpr;
@@ -114,21 +83,7 @@ __global__ __launch_bounds__(256) void grid_kernel(const V* __restrict__ src, V*
         const unsigned p = (unsigned)(row - o * n);  // destination cell
         unsigned s;                                  // source cell
         if (!inverse) {  // p is a grid-order position: find its raster cell
-            const unsigned code = p & cmask, tile = p >> tb;
-            unsigned yy, xx, tt = 0;
-            if (gg.video) {
-                xx = gather3(code);
-                yy = gather3(code >> 1);
-                tt = gather3(code >> 2);
-            } else {
-                xx = gather_bits(code);
-                yy = gather_bits(code >> 1);
-            }
-            const unsigned tx = tile % gg.tw, rest = tile / gg.tw;
-            const unsigned ty = rest % gg.th, tz = rest / gg.th;
-            const unsigned y = (ty << gg.s_log2) | yy, x = (tx << gg.s_log2) | xx;
-            const unsigned t = (tz << gg.s_log2) | tt;  // frame (0 for an image)
-            s = (t * gg.H + y) * gg.W + x;
+            s = grid_source(p, gg);
         } else {  // p is a raster cell: find its grid-order position
             const unsigned x = p % gg.W, r = p / gg.W;
             const unsigned y = r % gg.H, t = r / gg.H;
@@ -148,19 +103,9 @@ __global__ __launch_bounds__(256) void grid_kernel(const V* __restrict__ src, V*
 hipError_t launch_grid_order(const void* src, void* dst, long long outer, int frames, int height,
                              int width, int inner_bytes, int inverse, hipStream_t st)
 {
-    auto p2 = [](int v) { return v & -v; };
-    int S = min(p2(height), p2(width));
-    const int video = frames > 1;
-    if (video) S = min(S, p2(frames));
-    if (!video && height == width && S == width)  // a square power-of-two image: one tile
+    if (frames == 1 && height == width && (width & (width - 1)) == 0)  // one square tile
         return launch_zorder(src, dst, outer, width, inner_bytes, inverse, st);
-    GridGeo gg;
-    gg.H = (unsigned)height;
-    gg.W = (unsigned)width;
-    gg.tw = (unsigned)(width / S);
-    gg.th = (unsigned)(height / S);
-    gg.s_log2 = __builtin_ctz((unsigned)S);
-    gg.video = video;
+    const GridGeo gg = make_grid_geo(frames, height, width);
     const int vw = (inner_bytes % 16 == 0) ? 16 : (inner_bytes % 8 == 0) ? 8 : 4;
     const int cpr = inner_bytes / vw;
     const unsigned n = (unsigned)frames * (unsigned)height * (unsigned)width;

@@ -225,3 +225,30 @@ def test_token_counts_that_16_to_the_levels_does_not_divide(N, K, Lv, ok):
     rc = lib.llsa_forward_lk(BAD, BAD, BAD, BAD, BAD, 1, 2, N, 64, 16, arr, Lv, L.BF16, 0, BAD, 0,
                              None)
     assert rc == (-4 if ok else -2)  # a valid shape then fails on the missing workspace
+
+
+def _fwd_grid(**kw):
+    a = dict(ptrs=[BAD] * 8, B=1, H=2, frames=1, height=64, width=64, d=64, block_size=16,
+             topk=16, levels=2, dtype=L.BF16, flags=0, workspace=BAD, ws_bytes=1 << 40)
+    a.update(kw)
+    return L.load().llsa_forward_grid(*a["ptrs"], a["B"], a["H"], a["frames"], a["height"],
+                                      a["width"], a["d"], a["block_size"], a["topk"],
+                                      a["levels"], a["dtype"], a["flags"], a["workspace"],
+                                      a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptrs=[None] + [BAD] * 7), -1), (dict(ptrs=[BAD] * 5 + [None] + [BAD] * 2), -1),
+    (dict(ptrs=[BAD] * 7 + [None]), -1),
+    (dict(height=0), -2), (dict(width=1 << 16), -2), (dict(frames=-1), -2),
+    (dict(height=3, width=5), -2),            # N = 15: not a multiple of 16
+    (dict(height=16, width=21, topk=2), -4),  # N = 336: valid, no workspace given
+    (dict(height=16, width=21), -2),          # top-16 of two level-2 blocks
+    (dict(frames=4, height=32, width=32), -4),
+    (dict(d=96), -3), (dict(flags=32), -3), (dict(topk=0), -2),
+    (dict(workspace=None), -4), (dict(ws_bytes=100), -4),
+])
+def test_forward_grid_validation(kw, code):
+    if code == -4 and "workspace" not in kw and "ws_bytes" not in kw:
+        kw = dict(kw, workspace=None)
+    assert _fwd_grid(**kw) == code
