@@ -250,7 +250,10 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
 #pragma unroll
         for (int u = 0; u < NI; ++u) f.vrb[u] = ld8(vp + kb[u]);
     };
-    auto step = [&](const DqPair<D>& f, int p) {
+    // SINGLE: one register set (d = 128, where two sets spill): the next
+    // pair is loaded into it as soon as the current one is staged
+    constexpr bool SINGLE = D == D128;
+    auto step = [&](DqPair<D>& f, int p) {
         put_rows<D>(la, f.kra, lane);
         put_rows<D>(lb, f.krb, lane);
         stage_rows<D, TS::ROW_A>(lva, f.vra, lane);
@@ -261,6 +264,7 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
         operand_rows<D, TS::ROW_T>(lb, kb, lane);
         operand_rows<D, TS::ROW_A>(lva, va, lane);
         operand_rows<D, TS::ROW_A>(lvb, vb, lane);
+        if (SINGLE) load_pair(f, min(p + 1, NP - 1));
         // full pairs of fine tiles run unmasked; with an odd count the last
         // fine "pair" holds the lone last tile twice (the clamped load), so
         // it takes the masked path with its second tile empty; the causal
@@ -292,15 +296,21 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
                              e0, E1, ba, bb);
         }
     };
-    DqPair<D> A, B;
-    load_pair(A, 0);
-    for (int p = 0;; p += 2) {
-        load_pair(B, min(p + 1, NP - 1));
-        step(A, p);
-        if (p + 1 >= NP) break;
-        load_pair(A, min(p + 2, NP - 1));
-        step(B, p + 1);
-        if (p + 2 >= NP) break;
+    if (SINGLE) {
+        DqPair<D> A;
+        load_pair(A, 0);
+        for (int p = 0; p < NP; ++p) step(A, p);
+    } else {
+        DqPair<D> A, B;
+        load_pair(A, 0);
+        for (int p = 0;; p += 2) {
+            load_pair(B, min(p + 1, NP - 1));
+            step(A, p);
+            if (p + 1 >= NP) break;
+            load_pair(A, min(p + 2, NP - 1));
+            step(B, p + 1);
+            if (p + 2 >= NP) break;
+        }
     }
     const long obase = rowq + 4 * gq;
 #pragma unroll
