@@ -48,15 +48,22 @@ def ws_array(ws, off, count, np_dtype):
 
 
 def gpu_run(w, inp, flags=0, backward=True, q64=None):
-    """HIP path on raster-order inputs: grid-order gather, forward, backward.
+    """HIP path on raster-order inputs: grid-order gather and forward
+    (llsa_forward_grid; llsa_grid_order and llsa_forward_lk for a top-k per
+    level), backward.
     Returns numpy float64 results in Z-order plus workspace contents."""
     import torch
     import sparse_attention_diffusion_order_amd as lib
     B, H, N, d = w.B, w.H, w.N, w.d
     dt = lib.BF16 if w.dtype == "bf16" else lib.F32
     q_r, k_r, v_r = (to_device(inp[n], w.dtype) for n in ("q", "k", "v"))
-    q, k, v = (lib.grid_order(x, w.frames, w.rows, w.side) for x in (q_r, k_r, v_r))
-    out, lse, ws = lib.forward(q, k, v, w.topk, w.levels, flags)
+    if isinstance(w.topk, int):
+        # the forward with the grid order folded into its pooling pass
+        q, k, v, out, lse, ws = lib.forward_grid(q_r, k_r, v_r, w.frames, w.rows, w.side,
+                                                 w.topk, w.levels, flags)
+    else:
+        q, k, v = (lib.grid_order(x, w.frames, w.rows, w.side) for x in (q_r, k_r, v_r))
+        out, lse, ws = lib.forward(q, k, v, w.topk, w.levels, flags)
     res = {"q": q, "k": k, "v": v, "out_t": out, "lse_t": lse, "ws": ws}
     if backward:
         do = to_device(inp["do"], w.dtype)
