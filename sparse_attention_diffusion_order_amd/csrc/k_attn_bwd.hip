@@ -574,8 +574,10 @@ struct QBlock {
 constexpr int DKDV_WPG = 1;
 
 // CAUSAL: LLSA_CAUSAL (its own instance, so that the default one carries no
-// mask code)
-template <int D, int WPG, bool CAUSAL>
+// mask code).  ENRICH1: level 1's pooled tokens enrich (a compile-time
+// switch: as a run-time one the compiler branches around the pooled terms of
+// every row, each branch waiting on all outstanding LDS reads).
+template <int D, int WPG, bool CAUSAL, bool ENRICH1>
 __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __restrict__ q,
                                                       const unsigned short* __restrict__ k,
                                                       const unsigned short* __restrict__ v,
@@ -597,7 +599,7 @@ __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __re
     const long kblk = (long)xcd_block(blockIdx.x, gridDim.x, g.xcd_chunk) * WPG + wv;
     if (kblk >= (long)g.G * g.n[1]) return;
     const int gh = (int)(kblk / g.n[1]), j = (int)(kblk % g.n[1]);
-    const bool enrich1 = g.l0 == 1 && !g.cmp;  // level-1 picks' pooled tokens enrich
+    constexpr bool enrich1 = ENRICH1;  // level-1 picks' pooled tokens enrich
     const float c = g.scale * LOG2E;
     const long hbase = (long)gh * g.N * D;
     const long tbase = (long)gh * g.N;
@@ -1242,7 +1244,9 @@ hipError_t launch_attn_dkdv_d(const void* q, const void* k, const void* v, const
 {
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
-        auto kern = g.causal ? dkdv_bf16<D, DKDV_WPG, true> : dkdv_bf16<D, DKDV_WPG, false>;
+        const bool e1 = g.l0 == 1 && !g.cmp;  // level-1 picks' pooled tokens enrich
+        auto kern = g.causal ? (e1 ? dkdv_bf16<D, DKDV_WPG, true, true> : dkdv_bf16<D, DKDV_WPG, true, false>)
+                             : (e1 ? dkdv_bf16<D, DKDV_WPG, false, true> : dkdv_bf16<D, DKDV_WPG, false, false>);
         hipLaunchKernelGGL(kern, dim3((unsigned)((nblk + DKDV_WPG - 1) / DKDV_WPG)),
                            dim3(64 * DKDV_WPG), 0, st,
                            (const unsigned short*)q, (const unsigned short*)k,
