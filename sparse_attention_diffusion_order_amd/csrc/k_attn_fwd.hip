@@ -373,8 +373,13 @@ hipError_t launch_attn_fwd_d(const void* q, const void* k, const void* v, void* 
     if (dtype == LLSA_BF16) {
         long nblk = (long)g.G * g.n[1];
         // the four-block kernel (d = 64): every fine list and every pooled
-        // list fit one 16-entry tile
-        bool fits = D == D64 && g.K <= BS && g.n[1] % 4 == 0 && !g.cmp && !g.causal;
+        // list fit one 16-entry tile, and the launch fills the chip at least
+        // twice over at its 2 waves per SIMD (2048 waves a round); with fewer
+        // query blocks the one-block kernel's 4 waves per SIMD win (measured:
+        // 64^2 x 12 heads 15.6 against 28.0 us, 128^2 x 12 heads 51.7
+        // against 60.9 us; 256^2 x 6 heads 105 against 97 us)
+        bool fits = D == D64 && g.K <= BS && g.n[1] % 4 == 0 && !g.cmp && !g.causal &&
+                    nblk / 4 >= 2 * 2048;
         for (int l = g.l0; l <= g.L; ++l) fits = fits && g.Kl[l] <= BS;
         if (fits) {
             hipLaunchKernelGGL(attn_fwd_u4, dim3((unsigned)((nblk + 15) / 16)), dim3(256), 0, st,
