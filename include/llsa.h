@@ -91,7 +91,10 @@ extern "C" {
 
 /* error codes */
 #define LLSA_OK 0
-#define LLSA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define LLSA_ERR_NULL (-1)        /* a required pointer is NULL, or a tensor
+                                     pointer (q, k, v, out, dout, dq, dk, dv,
+                                     the raster inputs) not 16-byte aligned,
+                                     or lse not 4-byte aligned */
 #define LLSA_ERR_SHAPE (-2)       /* levels < 1, N not a multiple of 16,
                                      a top-k < 1 or above the candidates a row
                                      of its level may have (see below),
@@ -102,8 +105,8 @@ extern "C" {
                                      or flags, levels > LLSA_MAX_LEVELS,
                                      coarsest block count > 4096, topk > 64,
                                      N > 2^23, or B*H*N >= 2^31 */
-#define LLSA_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than
-                                     llsa_workspace_bytes() */
+#define LLSA_ERR_WORKSPACE (-4)   /* workspace NULL, not 16-byte aligned, or
+                                     smaller than llsa_workspace_bytes() */
 #define LLSA_ERR_HIP (-5)         /* a HIP launch or runtime call failed */
 #define LLSA_ERR_SCRATCH (-6)     /* llsa_forward_noalloc: the shape needs more
                                      than LLSA_NOALLOC_SCRATCH_BYTES */

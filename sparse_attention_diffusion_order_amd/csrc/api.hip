@@ -2,6 +2,7 @@
 //
 // Every check happens before the first HIP call, so argument errors are
 // reported identically on a host without a GPU.
+#include <stdint.h>
 #include <string.h>
 
 #include <atomic>
@@ -194,6 +195,18 @@ struct Prep {
     hipStream_t st;
 };
 
+// Tensor arguments: the kernels move rows of q, k, v, out, dout and the
+// gradients (and workspace regions) in 16-byte pieces, lse in 4-byte ones.
+bool bad16(const void* p) { return !p || ((uintptr_t)p & 15u); }
+
+template <typename... P>
+bool any_bad16(P... p)
+{
+    return (bad16(p) || ...);
+}
+
+bool bad_lse(const float* p) { return !p || ((uintptr_t)p & 3u); }
+
 int prepare(int B, int H, int N, int d, int block_size, const int* ks, int levels, int dtype,
             unsigned flags, void* workspace, size_t ws_bytes, void* stream, Prep* p,
             bool fwd_only = false)
@@ -202,7 +215,7 @@ int prepare(int B, int H, int N, int d, int block_size, const int* ks, int level
     if (rc) return rc;
     Layout lay;
     make_layout(B * H, N, d, ks, levels, &lay, fwd_only);
-    if (!workspace || ws_bytes < lay.pub.total) return LLSA_ERR_WORKSPACE;
+    if (bad16(workspace) || ws_bytes < lay.pub.total) return LLSA_ERR_WORKSPACE;
     make_geo(B, H, N, d, ks, levels, flags, dtype, &p->geo);
     make_ws(workspace, lay, levels, &p->ws);
     // per-level block rows of the bf16 pyramid copies; the choice counts
@@ -370,7 +383,7 @@ int llsa_forward_part(int part, const void* q, const void* k, const void* v, voi
                       int levels, int dtype, unsigned flags, void* workspace, size_t ws_bytes,
                       void* stream)
 {
-    if (!q || !k || !v || !out || !lse) return LLSA_ERR_NULL;
+    if (any_bad16(q, k, v, out) || bad_lse(lse)) return LLSA_ERR_NULL;
     Prep p;
     int rc = prepare(B, H, N, d, block_size, UniformK(topk, levels).ks, levels, dtype, flags,
                      workspace, ws_bytes, stream, &p);
@@ -382,7 +395,7 @@ int llsa_forward_lk(const void* q, const void* k, const void* v, void* out, floa
                     int H, int N, int d, int block_size, const int* topk, int levels, int dtype,
                     unsigned flags, void* workspace, size_t ws_bytes, void* stream)
 {
-    if (!q || !k || !v || !out || !lse) return LLSA_ERR_NULL;
+    if (any_bad16(q, k, v, out) || bad_lse(lse)) return LLSA_ERR_NULL;
     Prep p;
     int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
                      stream, &p);
@@ -396,7 +409,7 @@ int llsa_forward_grid(const void* q_raster, const void* k_raster, const void* v_
                       int levels, int dtype, unsigned flags, void* workspace,
                       size_t ws_bytes, void* stream)
 {
-    if (!q_raster || !k_raster || !v_raster || !q || !k || !v || !out || !lse)
+    if (any_bad16(q_raster, k_raster, v_raster, q, k, v, out) || bad_lse(lse))
         return LLSA_ERR_NULL;
     const int lim = 1 << 15;
     if (frames < 1 || height < 1 || width < 1 || frames > lim || height > lim || width > lim ||
@@ -428,7 +441,7 @@ int llsa_forward_noalloc(const void* q, const void* k, const void* v, void* out,
                          int B, int H, int N, int d, int block_size, int topk, int levels,
                          int dtype, unsigned flags, void* stream)
 {
-    if (!q || !k || !v || !out || !lse) return LLSA_ERR_NULL;
+    if (any_bad16(q, k, v, out) || bad_lse(lse)) return LLSA_ERR_NULL;
     const UniformK ks(topk, levels);
     int rc = validate(B, H, N, d, block_size, ks.ks, levels, dtype, flags);
     if (rc) return rc;
@@ -451,7 +464,7 @@ int llsa_backward_part(int part, const void* q, const void* k, const void* v, co
                        int H, int N, int d, int block_size, int topk, int levels, int dtype,
                        unsigned flags, void* workspace, size_t ws_bytes, void* stream)
 {
-    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return LLSA_ERR_NULL;
+    if (any_bad16(q, k, v, out, dout, dq, dk, dv) || bad_lse(lse)) return LLSA_ERR_NULL;
     Prep p;
     int rc = prepare(B, H, N, d, block_size, UniformK(topk, levels).ks, levels, dtype, flags,
                      workspace, ws_bytes, stream, &p);
@@ -464,7 +477,7 @@ int llsa_backward_lk(const void* q, const void* k, const void* v, const void* ou
                      int H, int N, int d, int block_size, const int* topk, int levels,
                      int dtype, unsigned flags, void* workspace, size_t ws_bytes, void* stream)
 {
-    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return LLSA_ERR_NULL;
+    if (any_bad16(q, k, v, out, dout, dq, dk, dv) || bad_lse(lse)) return LLSA_ERR_NULL;
     Prep p;
     int rc = prepare(B, H, N, d, block_size, topk, levels, dtype, flags, workspace, ws_bytes,
                      stream, &p);
@@ -501,7 +514,7 @@ const char* llsa_strerror(int code)
 {
     switch (code) {
     case LLSA_OK: return "ok";
-    case LLSA_ERR_NULL: return "a required pointer is NULL";
+    case LLSA_ERR_NULL: return "a required pointer is NULL or misaligned";
     case LLSA_ERR_SHAPE:
         return "bad shape: N a multiple of 16; B, H, levels >= 1; every top-k >= 1 and "
                "at most the candidates a row of its level may have (ceil(N/16^levels) at the "

@@ -392,6 +392,122 @@ __device__ __forceinline__ void for_each_pooled(const Geo& g, const Ws& w, int g
     }
 }
 
+// ------------------------------------------------------------ fp32 row batches
+//
+// The fp32 kernels hold one row per wave (a token's query, a key, or a pooled
+// token) and visit the rows it meets 16 at a time.  Lane layout: lane =
+// r + 16 cg holds batch row r's channels CH cg .. CH cg + CH - 1 (CH = D/4)
+// and the same slice of the wave's own row.  A dot product is CH fmas in the
+// lane and a sum over the four channel groups (sum_x4, the same value in all
+// four lanes of the row); a row-weighted sum of rows (o, dq, dk, dv, pooled
+// gradients) accumulates per lane and is summed over the 16 rows once, at
+// the end (row16_sum).  A batch's loads are all in flight together.
+//
+// A batch: lane r + 16 cg holds row r's key and value pointers and logit
+// bias; rows at or past n hold row 0's (valid memory; the caller masks them).
+
+struct RowBatch {
+    const float* k;
+    const float* v;
+    float bias;
+    int n;  // rows in the batch (wave-uniform)
+};
+
+// Collects rows one at a time and hands every full batch, and at finish()
+// the last partial one, to `flush`.
+template <typename F>
+struct RowBatcher {
+    RowBatch b;
+    int row;  // lane % 16
+    F& flush;
+    __device__ RowBatcher(int lane, F& f) : b{nullptr, nullptr, 0.f, 0}, row(lane & 15), flush(f) {}
+    __device__ void push(const float* k, const float* v, float bias)
+    {
+        if (b.n == 0 || row == b.n) {
+            b.k = k;
+            b.v = v;
+            b.bias = bias;
+        }
+        if (++b.n == BS) {
+            flush(b);
+            b.n = 0;
+        }
+    }
+    __device__ void finish()
+    {
+        if (b.n > 0) flush(b);
+        b.n = 0;
+    }
+};
+
+// channels D/4 cg .. D/4 cg + D/4 - 1 of a row (16-byte loads)
+template <int D>
+__device__ __forceinline__ void load_slice(float (&x)[D / 4], const float* row, int lane)
+{
+    const float4* p = (const float4*)(row + (D / 4) * (lane >> 4));
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+        const float4 t = p[u];
+        x[4 * u] = t.x;
+        x[4 * u + 1] = t.y;
+        x[4 * u + 2] = t.z;
+        x[4 * u + 3] = t.w;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ float slice_dot(const float (&a)[D / 4], const float (&b)[D / 4])
+{
+    float part = a[0] * b[0];
+#pragma unroll
+    for (int c = 1; c < D / 4; ++c) part = fmaf(a[c], b[c], part);
+    return sum_x4(part);
+}
+
+// Sum / max over the 16 lanes of each DPP row (every lane gets the result).
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp_f<0xB1>(x);   // quad_perm 1,0,3,2
+    x += dpp_f<0x4E>(x);   // quad_perm 2,3,0,1
+    x += dpp_f<0x124>(x);  // row_ror 4
+    x += dpp_f<0x128>(x);  // row_ror 8
+    return x;
+}
+
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x124>(x));
+    x = fmaxf(x, dpp_f<0x128>(x));
+    return x;
+}
+
+// A query token's key/value set as batches: each fine block of its level-1
+// list (its 16 rows; under LLSA_CAUSAL unused slots skipped and the diagonal
+// block cut to the keys at or before t), then the pooled tokens of the
+// enriching levels (a level-lv token's logit gets lb2 * lv * ln 2).
+template <int D, typename F>
+__device__ __forceinline__ void for_each_batch(const Geo& g, const Ws& w, const float* k,
+                                               const float* v, int gh, int t, int lane, F& run)
+{
+    const int* sel = w.idx[0] + ((long)gh * g.n[1] + t / BS) * g.K;
+    for (int s = 0; s < g.K; ++s) {
+        const int j = sel[s];
+        if (g.causal && j < 0) continue;  // an unused slot
+        const int cnt = (g.causal && j == t / BS) ? t % BS + 1 : BS;
+        const long row =
+            ((long)gh * g.N + (long)clampi(j, g.n[1]) * BS + min(lane & 15, cnt - 1)) * D;
+        run(RowBatch{k + row, v + row, 0.f, cnt});
+    }
+    RowBatcher<F> bat(lane, run);
+    for_each_pooled(g, w, gh, t / BS, [&](int lv, int j) {
+        const long row = ((long)gh * g.n[lv] + j) * D;
+        bat.push(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, g.lb2 * (float)lv * LN2);
+    });
+    bat.finish();
+}
+
 // ------------------------------------------------------------ grid order
 
 __device__ __forceinline__ unsigned gather_bits(unsigned x)  // inverse of spread_bits

@@ -930,44 +930,27 @@ int cmp_chunks(const Geo& g, int D)
 
 // ------------------------------------------------------------ fp32 path
 
-// One wave per row, lane = channels lane + 64 c: every dot product is a wave
-// sum.
+// One wave per row (a query token, a key token, or a pooled token); the rows
+// it meets are visited 16 at a time with lane = row r + 16 channel group
+// (RowBatch and its helpers): dot products are CH = D/4 fmas and a sum over
+// the four channel groups, and row-weighted sums are reduced over the 16
+// rows once, at the end.
 
-// <a, row> over the D channels, a held as the lane's channels
+// a wave's per-lane partial sums of CH channels, reduced over the 16 rows,
+// stored by lanes 0, 16, 32, 48 (each its channel group), times `scale`
 template <int D>
-__device__ __forceinline__ float row_dot(const float (&a)[D / 64], const float* row, int lane)
+__device__ __forceinline__ void store_slice(float* row, float (&x)[D / 4], int lane,
+                                            float scale = 1.f)
 {
-    float part = a[0] * row[lane];
+    constexpr int CH = D / 4;
 #pragma unroll
-    for (int c = 1; c < D / 64; ++c) part = fmaf(a[c], row[lane + 64 * c], part);
-    return wave_sum(part);
-}
-
-template <int D>
-__device__ __forceinline__ void lane_channels(float (&x)[D / 64], const float* row, int lane)
-{
+    for (int c = 0; c < CH; ++c) x[c] = row16_sum(x[c]) * scale;
+    if ((lane & 15) == 0) {
+        float4* dst = (float4*)(row + CH * (lane >> 4));
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) x[c] = row[lane + 64 * c];
-}
-
-template <int D, typename F>
-__device__ __forceinline__ void for_each_entry(const Geo& g, const Ws& w, const float* k,
-                                               const float* v, int gh, int t, F f)
-{
-    const int* sel = w.idx[0] + ((long)gh * g.n[1] + t / BS) * g.K;
-    for (int s = 0; s < g.K; ++s) {
-        if (g.causal && sel[s] < 0) continue;  // an unused slot
-        const bool diag = g.causal && sel[s] == t / BS;
-        for (int r = 0; r < (diag ? t % BS + 1 : BS); ++r) {  // diagonal: keys up to t
-            long row = ((long)gh * g.N + (long)clampi(sel[s], g.n[1]) * BS + r) * D;
-            f(k + row, v + row, 0.f);
-        }
+        for (int u = 0; u < CH / 4; ++u)
+            dst[u] = float4{x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]};
     }
-    // enriching levels l0..L; a level-lv token's logit gets lb2 * lv * ln 2
-    for_each_pooled(g, w, gh, t / BS, [&](int lv, int j) {
-        const long row = ((long)gh * g.n[lv] + j) * D;
-        f(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, g.lb2 * (float)lv * LN2);
-    });
 }
 
 // dq and delta: one wave per query token
@@ -980,31 +963,54 @@ __global__ __launch_bounds__(256) void dq_f32(const float* __restrict__ q,
                                               const float* __restrict__ dout,
                                               float* __restrict__ dq, Geo g, Ws w)
 {
-    constexpr int NC = D / 64;
+    constexpr int CH = D / 4;
     const long tg = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (tg >= (long)g.G * g.N) return;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, r = lane & 15;
     const int gh = (int)(tg / g.N), t = (int)(tg % g.N);
-    float qc[NC], dc[NC], acc[NC];
-    lane_channels<D>(qc, q + tg * D, lane);
-    lane_channels<D>(dc, dout + tg * D, lane);
-    const float Dt = row_dot<D>(dc, o + tg * D, lane);
+    float qc[CH], dc[CH], acc[CH];
+    load_slice<D>(qc, q + tg * D, lane);
+    load_slice<D>(dc, dout + tg * D, lane);
+    load_slice<D>(acc, o + tg * D, lane);  // o, for delta
+    const float Dt = slice_dot<D>(dc, acc);
     if (lane == 0) w.delta[tg] = Dt;
     const float lt = lse[tg];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = 0.f;
-    for_each_entry<D>(g, w, k, v, gh, t, [&](const float* kr, const float* vr, float bias) {
-        float kc[NC];
-        lane_channels<D>(kc, kr, lane);
-        const float z = row_dot<D>(qc, kr, lane);
-        const float dp = row_dot<D>(dc, vr, lane);
-        const float P = expf(z * g.scale + bias - lt);
-        const float ds = P * (dp - Dt) * g.scale;
+    for (int c = 0; c < CH; ++c) acc[c] = 0.f;
+    auto run = [&](const RowBatch& bt) {
+        float kx[CH], vx[CH];
+        load_slice<D>(kx, bt.k, lane);
+        load_slice<D>(vx, bt.v, lane);
+        const float z = slice_dot<D>(qc, kx);
+        const float dp = slice_dot<D>(dc, vx);
+        const float P = r < bt.n ? expf(z * g.scale + bt.bias - lt) : 0.f;
+        const float ds = P * (dp - Dt);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc[c] = fmaf(ds, kc[c], acc[c]);
-    });
-#pragma unroll
-    for (int c = 0; c < NC; ++c) dq[tg * D + lane + 64 * c] = acc[c];
+        for (int c = 0; c < CH; ++c) acc[c] = fmaf(ds, kx[c], acc[c]);
+    };
+    for_each_batch<D>(g, w, k, v, gh, t, lane, run);
+    store_slice<D>(dq + tg * D, acc, lane, g.scale);
+}
+
+// The query tokens tok0 + r of a 16-row batch (rows at or past n repeat the
+// last one): this lane's channel slice of row r's q and dO, and row r's lse
+// and delta.
+template <int D>
+struct QRow {
+    float q[D / 4], d[D / 4];
+    float lse, delta;
+};
+
+template <int D>
+__device__ __forceinline__ void load_qrow(QRow<D>& x, const float* q, const float* dout,
+                                          const float* lse, const float* delta, long tok0,
+                                          int n, int lane)
+{
+    const long t = tok0 + min(lane & 15, n - 1);
+    load_slice<D>(x.q, q + t * D, lane);
+    load_slice<D>(x.d, dout + t * D, lane);
+    x.lse = lse[t];
+    x.delta = delta[t];
 }
 
 // pooled-token gradients, every level: one wave per level-l block
@@ -1014,20 +1020,20 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
                                                   const float* __restrict__ dout, Geo g, Ws w,
                                                   int l)
 {
-    constexpr int NC = D / 64;
+    constexpr int CH = D / 4;
     const long blk = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (blk >= (long)g.G * g.n[l]) return;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, r = lane & 15;
     const int gh = (int)(blk / g.n[l]), j = (int)(blk % g.n[l]);
-    float kb[NC], vb[NC], sk[NC], sv[NC];
-    lane_channels<D>(kb, w.kbar[l - 1] + blk * D, lane);
-    lane_channels<D>(vb, w.vbar[l - 1] + blk * D, lane);
+    float kb[CH], vb[CH], sk[CH], sv[CH];
+    load_slice<D>(kb, w.kbar[l - 1] + blk * D, lane);
+    load_slice<D>(vb, w.vbar[l - 1] + blk * D, lane);
     const int* rp = w.rowptr[l - 1] + (long)gh * (g.n[l] + 1);
     const int* cl = w.col[l - 1] + (long)gh * g.n[l] * g.Kl[l];
     const long span = 1l << (4 * l);
     const float bias = g.lb2 * (float)l * LN2;  // size bias of a level-l token
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sk[c] = sv[c] = 0.f;
+    for (int c = 0; c < CH; ++c) sk[c] = sv[c] = 0.f;
     // the level-l blocks whose tokens attend j: those that picked it (its
     // key->query list), or with the complement those among whose candidates
     // it is and that did not pick it -- every level-L block, below L the
@@ -1063,31 +1069,30 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
             for (int s = 0; s < Kl; ++s) picked = picked || sel[s] == j;
             if (picked) continue;
         }
-        for (long t = a * span; t < (a + 1) * span && t < g.N; ++t) {
-            const long tg = (long)gh * g.N + t;
-            float qc[NC], dc[NC];
-            lane_channels<D>(qc, q + tg * D, lane);
-            lane_channels<D>(dc, dout + tg * D, lane);
-            const float z = row_dot<D>(kb, q + tg * D, lane);
-            const float dp = row_dot<D>(vb, dout + tg * D, lane);
-            const float P = expf(z * g.scale + bias - lse[tg]);
-            const float ds = P * (dp - w.delta[tg]);
+        // the block's tokens (those before N), 16 at a time
+        const long t1 = min((a + 1) * span, (long)g.N);
+        for (long t0 = a * span; t0 < t1; t0 += BS) {
+            const int n = (int)min((long)BS, t1 - t0);
+            QRow<D> x;
+            load_qrow<D>(x, q, dout, lse, w.delta, (long)gh * g.N + t0, n, lane);
+            const float z = slice_dot<D>(kb, x.q);
+            const float dp = slice_dot<D>(vb, x.d);
+            const float P = r < n ? expf(z * g.scale + bias - x.lse) : 0.f;
+            const float ds = P * (dp - x.delta);
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                sk[c] = fmaf(ds * g.scale, qc[c], sk[c]);
-                sv[c] = fmaf(P, dc[c], sv[c]);
+            for (int c = 0; c < CH; ++c) {
+                sk[c] = fmaf(ds, x.q[c], sk[c]);
+                sv[c] = fmaf(P, x.d[c], sv[c]);
             }
         }
     }
     float* dst = w.dbar[l - 1] + blk * 2 * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        dst[lane + 64 * c] = sk[c];
-        dst[D + lane + 64 * c] = sv[c];
-    }
+    store_slice<D>(dst, sk, lane, g.scale);
+    store_slice<D>(dst + D, sv, lane);
 }
 
-// dk, dv: one wave per key token
+// dk, dv: one wave per key token, over the 16 rows of each query block of
+// its block's list
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_f32(const float* __restrict__ q,
                                                 const float* __restrict__ k,
@@ -1097,50 +1102,63 @@ __global__ __launch_bounds__(256) void dkdv_f32(const float* __restrict__ q,
                                                 float* __restrict__ dk, float* __restrict__ dv,
                                                 Geo g, Ws w)
 {
-    constexpr int NC = D / 64;
+    constexpr int CH = D / 4;
     const long xg = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (xg >= (long)g.G * g.N) return;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, r = lane & 15;
     const int gh = (int)(xg / g.N), x = (int)(xg % g.N), j = x / BS;
-    float kc[NC], vc[NC], ak[NC], av[NC];
-    lane_channels<D>(kc, k + xg * D, lane);
-    lane_channels<D>(vc, v + xg * D, lane);
+    float kc[CH], vc[CH], ak[CH], av[CH];
+    load_slice<D>(kc, k + xg * D, lane);
+    load_slice<D>(vc, v + xg * D, lane);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) ak[c] = av[c] = 0.f;
+    for (int c = 0; c < CH; ++c) ak[c] = av[c] = 0.f;
     const int* rp = w.rowptr[0] + (long)gh * (g.n[1] + 1);
     const int* cl = w.col[0] + (long)gh * g.n[1] * g.K;
     const int tot = g.n[1] * g.K;
     const int beg = clampi(rp[j], tot + 1), end = max(beg, clampi(rp[j + 1], tot + 1));
-    for (int e = beg; e < end; ++e)
+    for (int e = beg; e < end; ++e) {
+        const int i = clampi(cl[e], g.n[1]);
         // the causal diagonal block: the queries at or after key x
-        for (int r = (g.causal && cl[e] == j) ? x % BS : 0; r < BS; ++r) {
-            const long tg = (long)gh * g.N + (long)clampi(cl[e], g.n[1]) * BS + r;
-            float qc[NC], dc[NC];
-            lane_channels<D>(qc, q + tg * D, lane);
-            lane_channels<D>(dc, dout + tg * D, lane);
-            const float z = row_dot<D>(kc, q + tg * D, lane);
-            const float dp = row_dot<D>(vc, dout + tg * D, lane);
-            const float P = expf(z * g.scale - lse[tg]);
-            const float ds = P * (dp - w.delta[tg]) * g.scale;
+        const int r0 = (g.causal && cl[e] == j) ? x % BS : 0;
+        QRow<D> y;
+        load_qrow<D>(y, q, dout, lse, w.delta, (long)gh * g.N + (long)i * BS, BS, lane);
+        const float z = slice_dot<D>(kc, y.q);
+        const float dp = slice_dot<D>(vc, y.d);
+        const float P = r >= r0 ? expf(z * g.scale - y.lse) : 0.f;
+        const float ds = P * (dp - y.delta);
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                ak[c] = fmaf(ds, qc[c], ak[c]);
-                av[c] = fmaf(P, dc[c], av[c]);
-            }
-        }
-    for (int l = g.l0; l <= g.L; ++l) {
-        const float wgt = 1.0f / (float)g.tokens(l, x >> (4 * l));  // the mean's share
-        const float* db = w.dbar[l - 1] + ((long)gh * g.n[l] + (x >> (4 * l))) * 2 * D;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            ak[c] += db[lane + 64 * c] * wgt;
-            av[c] += db[D + lane + 64 * c] * wgt;
+        for (int c = 0; c < CH; ++c) {
+            ak[c] = fmaf(ds, y.q[c], ak[c]);
+            av[c] = fmaf(P, y.d[c], av[c]);
         }
     }
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        dk[xg * D + lane + 64 * c] = ak[c];
-        dv[xg * D + lane + 64 * c] = av[c];
+    for (int c = 0; c < CH; ++c) {
+        ak[c] = row16_sum(ak[c]) * g.scale;
+        av[c] = row16_sum(av[c]);
+    }
+    // the pooled-level gradients: dbar_l of the block's level-l ancestor,
+    // each token's share 1 / (its tokens)
+    for (int l = g.l0; l <= g.L; ++l) {
+        const float wgt = 1.0f / (float)g.tokens(l, x >> (4 * l));
+        float db[CH], dbv[CH];
+        const float* src = w.dbar[l - 1] + ((long)gh * g.n[l] + (x >> (4 * l))) * 2 * D;
+        load_slice<D>(db, src, lane);
+        load_slice<D>(dbv, src + D, lane);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            ak[c] += db[c] * wgt;
+            av[c] += dbv[c] * wgt;
+        }
+    }
+    if (r == 0) {
+        float4* ok = (float4*)(dk + xg * D + CH * (lane >> 4));
+        float4* ov = (float4*)(dv + xg * D + CH * (lane >> 4));
+#pragma unroll
+        for (int u = 0; u < CH / 4; ++u) {
+            ok[u] = float4{ak[4 * u], ak[4 * u + 1], ak[4 * u + 2], ak[4 * u + 3]};
+            ov[u] = float4{av[4 * u], av[4 * u + 1], av[4 * u + 2], av[4 * u + 3]};
+        }
     }
 }
 

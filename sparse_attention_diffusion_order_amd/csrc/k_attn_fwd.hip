@@ -309,8 +309,8 @@ __global__ __launch_bounds__(256) void attn_fwd_u4(const unsigned short* __restr
 
 // ------------------------------------------------------------ fp32 path
 
-// one wave per query token, lane = channels lane + 64 c: every logit is a
-// wave sum
+// one wave per query token; keys in batches of 16 (for_each_batch, lane =
+// key r + 16 channel group), the online softmax updated once per batch
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
                                                     const float* __restrict__ k,
@@ -318,51 +318,44 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
                                                     float* __restrict__ out,
                                                     float* __restrict__ lse, Geo g, Ws w)
 {
-    constexpr int NC = D / 64;
+    constexpr int CH = D / 4;
     const long tg = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (tg >= (long)g.G * g.N) return;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, r = lane & 15;
     const int gh = (int)(tg / g.N), t = (int)(tg % g.N);
-    float qc[NC], o[NC];
+    float qc[CH], o[CH];
+    load_slice<D>(qc, q + tg * D, lane);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        qc[c] = q[tg * D + lane + 64 * c];
-        o[c] = 0.f;
-    }
-    float m = -INFINITY, l = 0.f;
-    auto visit = [&](const float* kr, const float* vr, float bias) {
-        float part = qc[0] * kr[lane];
-#pragma unroll
-        for (int c = 1; c < NC; ++c) part = fmaf(qc[c], kr[lane + 64 * c], part);
-        const float z = wave_sum(part) * g.scale + bias;
-        if (z > m) {
-            const float a = expf(m - z);
+    for (int c = 0; c < CH; ++c) o[c] = 0.f;
+    float m = -INFINITY, l = 0.f;  // l, o: this lane's rows' share
+    auto run = [&](const RowBatch& bt) {
+        float kx[CH], vx[CH];
+        load_slice<D>(kx, bt.k, lane);
+        load_slice<D>(vx, bt.v, lane);
+        const float z = r < bt.n ? slice_dot<D>(qc, kx) * g.scale + bt.bias : -INFINITY;
+        const float mb = row16_max(z);
+        if (mb > m) {
+            const float a = expf(m - mb);
             l *= a;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) o[c] *= a;
-            m = z;
+            for (int c = 0; c < CH; ++c) o[c] *= a;
+            m = mb;
         }
         const float p = expf(z - m);
         l += p;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) o[c] = fmaf(p, vr[lane + 64 * c], o[c]);
+        for (int c = 0; c < CH; ++c) o[c] = fmaf(p, vx[c], o[c]);
     };
-    const int* sel = w.idx[0] + ((long)gh * g.n[1] + t / BS) * g.K;
-    for (int s = 0; s < g.K; ++s) {
-        if (g.causal && sel[s] < 0) continue;  // an unused slot
-        const bool diag = g.causal && sel[s] == t / BS;
-        for (int r = 0; r < (diag ? t % BS + 1 : BS); ++r) {  // diagonal: keys up to t
-            const long row = ((long)gh * g.N + (long)clampi(sel[s], g.n[1]) * BS + r) * D;
-            visit(k + row, v + row, 0.f);
-        }
-    }
-    // pooled tokens of the enriching levels
-    for_each_pooled(g, w, gh, t / BS, [&](int lv, int j) {
-        const long row = ((long)gh * g.n[lv] + j) * D;
-        visit(w.kbar[lv - 1] + row, w.vbar[lv - 1] + row, g.lb2 * (float)lv * LN2);
-    });
+    for_each_batch<D>(g, w, k, v, gh, t, lane, run);
+    l = row16_sum(l);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) out[tg * D + lane + 64 * c] = o[c] / l;
+    for (int c = 0; c < CH; ++c) o[c] = row16_sum(o[c]);
+    if (r == 0) {
+        float4* dst = (float4*)(out + tg * D + CH * (lane >> 4));
+#pragma unroll
+        for (int u = 0; u < CH / 4; ++u)
+            dst[u] = float4{o[4 * u] / l, o[4 * u + 1] / l, o[4 * u + 2] / l, o[4 * u + 3] / l};
+    }
     if (lane == 0) lse[tg] = m + logf(l);
 }
 

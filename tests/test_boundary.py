@@ -69,15 +69,19 @@ def bwd(**kw):
     (dict(levels=7, N=1 << 30), -3), (dict(N=131072, topk=16), -3), (dict(topk=128, N=65536, levels=2), -3),
     (dict(B=1 << 16, H=1 << 4, N=4096), -3), (dict(N=1 << 24, levels=3, topk=16), -3),
     (dict(workspace=None), -4), (dict(ws_bytes=100), -4),
+    # tensors move in 16-byte pieces, lse in 4-byte ones
+    (dict(q=BAD + 8), -1), (dict(out=BAD + 4), -1), (dict(lse=BAD + 2), -1),
+    (dict(lse=BAD + 4, workspace=None), -4), (dict(workspace=BAD + 8), -4),
 ])
 def test_forward_validation(kw, code):
     assert fwd(**kw) == code
-    if "q" not in kw and "lse" not in kw:
+    if not {"q", "lse", "out"} & kw.keys():
         assert bwd(**{k: v for k, v in kw.items()}) == code
 
 
 def test_backward_null_output():
     assert bwd(dq=None) == -1
+    assert bwd(dq=BAD + 8) == -1
 
 
 def test_zorder_validation():

@@ -298,12 +298,16 @@ def test_all_blocks_no_enrichment_equals_dense(dtype):
 def test_peaked_logits(w):
     """Q and K scaled by 4 (exactly: a power of two), so logits spread over
     about +-50 and most softmax weights underflow: the online softmax's
-    running maximum moves far more often than on unit-scale inputs.  Out and
-    lse keep their tolerances (out is still a convex combination of V rows).
-    The gradients grow with Q and K (here to about 16 in magnitude) and every
-    rounding on the bf16 path is relative to the values it rounds, so their
-    bound is grad_tol's: 5e-2, or 2^-6 of the tensor's largest magnitude when
-    that is larger (fp32: 1e-4 relative to that magnitude)."""
+    running maximum moves far more often than on unit-scale inputs.  Out
+    keeps its tolerance (it is still a convex combination of V rows).  lse
+    grows with the logits (here to about 50, where one fp32 ulp is 3.8e-6 and
+    a 64-term fp32 dot product may be off by several), so on fp32 its bound
+    is out_max relative to its largest magnitude; on bf16 the absolute 2e-2
+    already covers it.  The gradients grow with Q and K (here to about 16 in
+    magnitude) and every rounding on the bf16 path is relative to the values
+    it rounds, so their bound is grad_tol's: 5e-2, or 2^-6 of the tensor's
+    largest magnitude when that is larger (fp32: 1e-4 relative to that
+    magnitude)."""
     inp = synth.make_inputs(w)
     for n_ in ("q", "k"):
         inp[n_], inp[n_ + "64"] = synth._cast(inp[n_ + "64"] * 4.0, w.dtype)
@@ -317,7 +321,8 @@ def test_peaked_logits(w):
     scale = 1.0 / np.sqrt(w.d)
     o, lse = oracle.forward(z["q"], z["k"], z["v"], kp, vp, idx, BS, scale)
     assert_close(gpu["out"], o, tol["out_max"], tol["out_mean"], "out")
-    assert_close(gpu["lse"], lse, tol["out_max"], tol["out_mean"], "lse")
+    lse_scale = max(1.0, float(np.abs(lse).max())) if w.dtype == "f32" else 1.0
+    assert_close(gpu["lse"], lse, tol["out_max"] * lse_scale, tol["out_mean"] * lse_scale, "lse")
     dq, dk, dv = oracle.backward(z["q"], z["k"], z["v"], kp, vp, idx, o, lse, z["do"], BS, scale)
     for n_, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
         bound = (grad_tol(ref, tol["grad_max"]) if w.dtype == "bf16"
