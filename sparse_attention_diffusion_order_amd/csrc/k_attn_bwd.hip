@@ -357,7 +357,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
     dq_block<ECAP, D>(q, k, v, o, lse, dout, dq, g, w, b - tr_pad, (int)gridDim.x - tr_pad);
 }
 
-template <int D>
+// The pooled-token gradients of levels >= 2 over one level-2 block's 256
+// query tokens.  The (level, 16-entry tile) pairs of the block's lists are
+// taken NP at a time: each query block's Q and dO tiles are loaded once per
+// NP pairs (NP = 2 at d = 64 when there are two or more pairs: with three
+// levels the query rows are read once, not once per level).
+template <int D, int NP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ? 2 : 1))) void enrich_bwd_bf16(const unsigned short* __restrict__ q,
                                                        const float* __restrict__ lse,
                                                        const unsigned short* __restrict__ dout,
@@ -402,74 +407,100 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
         rowst[wv][0][lane] = lse[t0];
         rowst[wv][1][lane] = w.delta[t0];
     }
-    for (int l = 2; l <= g.L; ++l) {
-        const int al = a2 >> (4 * (l - 2));
-        const int Kl = g.Kl[l];
-        const int* sel = w.idx[l - 1] + ((long)gh * g.n[l] + al) * Kl;
-        const float lb = g.lb2 * (float)l;  // size bias of a level-l token (log2)
-        for (int e0 = 0; e0 < Kl; e0 += BS) {
+    // the pairs: level l = 2..L, entry tiles e0 = 0, 16, .. below K_l
+    int npairs = 0;
+    for (int l = 2; l <= g.L; ++l) npairs += (g.Kl[l] + BS - 1) / BS;
+    for (int p0 = 0; p0 < npairs; p0 += NP) {
+        int lv[NP], e0[NP];
+        bool on[NP];  // pair p0 + pp exists
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+            int p = min(p0 + pp, npairs - 1), l = 2;
+            for (; l < g.L && p >= (g.Kl[l] + BS - 1) / BS; ++l) p -= (g.Kl[l] + BS - 1) / BS;
+            lv[pp] = l;
+            e0[pp] = BS * p;
+            on[pp] = p0 + pp < npairs;
+        }
+        bool ev[NP];  // this lane's entry (e0 + nq) is live
+        bf16x8 bk[NP][NI], bv[NP][NI];  // entry rows lane%16, channels 32u + 8(lane/16) ..
+        float lb[NP];                   // size bias of the pair's level (log2)
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+            const int l = lv[pp], al = a2 >> (4 * (l - 2)), Kl = g.Kl[l];
+            const int* sel = w.idx[l - 1] + ((long)gh * g.n[l] + al) * Kl;
+            lb[pp] = g.lb2 * (float)l;
             // a live entry: causal rows skip unused slots (-1) and the
             // ancestor's own block (their partials are written as zeros)
-            const int sj = e0 + nq < Kl ? sel[e0 + nq] : -1;
-            const bool ev = e0 + nq < Kl && (!g.causal || (sj >= 0 && sj != al));
-            bf16x8 bk[NI], bv[NI];  // entry rows lane%16, channels 32u + 8(lane/16) ..
+            const int en = e0[pp] + nq;
+            const int sj = en < Kl ? sel[en] : -1;
+            ev[pp] = on[pp] && en < Kl && (!g.causal || (sj >= 0 && sj != al));
 #pragma unroll
-            for (int u = 0; u < NI; ++u) bk[u] = bv[u] = bf16x8{};
-            if (ev) {
-                long off = ((long)gh * g.n[l] + clampi(sel[e0 + nq], g.n[l])) * D;
+            for (int u = 0; u < NI; ++u) bk[pp][u] = bv[pp][u] = bf16x8{};
+            if (ev[pp]) {
+                long off = ((long)gh * g.n[l] + clampi(sj, g.n[l])) * D;
 #pragma unroll
                 for (int u = 0; u < NI; ++u) {
-                    bk[u] = ld8f(w.kbar[l - 1] + off + 32 * u + 8 * gq);
-                    bv[u] = ld8f(w.vbar[l - 1] + off + 32 * u + 8 * gq);
+                    bk[pp][u] = ld8f(w.kbar[l - 1] + off + 32 * u + 8 * gq);
+                    bv[pp][u] = ld8f(w.vbar[l - 1] + off + 32 * u + 8 * gq);
                 }
             }
-            f32x4 ak[ND] = {}, av[ND] = {};
-            // rows of block u + 1 are loaded while block u is computed
-            bf16x8 xq[NI], xd[NI];
-            load_rows(xq, xd, row_addr(0));
+        }
+        f32x4 ak[NP][ND] = {}, av[NP][ND] = {};
+        // rows of block u + 1 are loaded while block u is computed
+        bf16x8 xq[NI], xd[NI];
+        load_rows(xq, xd, row_addr(0));
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                put_rows<D>(lq, xq, lane);
-                put_rows<D>(ld, xd, lane);
-                load_rows(xq, xd, row_addr(min(u + 1, 3)));
-                lds_fence();
-                bf16x8 aq[NI], ad[NI];
-                operand_rows<D, TS::ROW_T>(lq, aq, lane);
-                operand_rows<D, TS::ROW_T>(ld, ad, lane);
-                f32x4 s = scores<D>(aq, bk);  // S[query][entry]
-                f32x4 dp = scores<D>(ad, bv);
-                const float4 l4 = *(const float4*)&rowst[wv][0][u * BS + 4 * gq];
-                const float4 d4 = *(const float4*)&rowst[wv][1][u * BS + 4 * gq];
-                const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, dr[4] = {d4.x, d4.y, d4.z, d4.w};
-                const bool live = 16 * a2 + 4 * wv + u < g.n[1];
+        for (int u = 0; u < 4; ++u) {
+            put_rows<D>(lq, xq, lane);
+            put_rows<D>(ld, xd, lane);
+            load_rows(xq, xd, row_addr(min(u + 1, 3)));
+            lds_fence();
+            bf16x8 aq[NI], ad[NI];
+            operand_rows<D, TS::ROW_T>(lq, aq, lane);
+            operand_rows<D, TS::ROW_T>(ld, ad, lane);
+            const float4 l4 = *(const float4*)&rowst[wv][0][u * BS + 4 * gq];
+            const float4 d4 = *(const float4*)&rowst[wv][1][u * BS + 4 * gq];
+            const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, dr[4] = {d4.x, d4.y, d4.z, d4.w};
+            const bool live = 16 * a2 + 4 * wv + u < g.n[1];
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp) {
+                if (!on[pp]) continue;  // wave-uniform
+                f32x4 s = scores<D>(aq, bk[pp]);  // S[query][entry]
+                f32x4 dp = scores<D>(ad, bv[pp]);
                 bf16x4 pP, pS;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float P = (ev && live) ? fast_exp2(s[r] * c - lr[r] * LOG2E + lb) : 0.f;
+                    float P = (ev[pp] && live) ? fast_exp2(s[r] * c - lr[r] * LOG2E + lb[pp]) : 0.f;
                     pP[r] = (bf16)P;
                     pS[r] = (bf16)(P * (dp[r] - dr[r]));
                 }
 #pragma unroll
                 for (int d = 0; d < ND; ++d) {
                     const int off = (4 * gq + rr) * TS::ROW_T + 16 * d + 4 * xx;
-                    ak[d] = mfma16(lds_read_tr(lq + off), pS, ak[d]);
-                    av[d] = mfma16(lds_read_tr(ld + off), pP, av[d]);
+                    ak[pp][d] = mfma16(lds_read_tr(lq + off), pS, ak[pp][d]);
+                    av[pp][d] = mfma16(lds_read_tr(ld + off), pP, av[pp][d]);
                 }
             }
-            // reduce the four waves in a fixed order, dk then dv
+        }
+        // reduce the four waves in a fixed order, per pair dk then dv
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+            if (!on[pp]) continue;  // workgroup-uniform
+            const int l = lv[pp], Kl = g.Kl[l];
             for (int kind = 0; kind < 2; ++kind) {
                 __syncthreads();  // tiles (or the previous kind) no longer read
 #pragma unroll
                 for (int d = 0; d < ND; ++d)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        red[((wv * ND + d) * 4 + r) * 64 + lane] = kind == 0 ? ak[d][r] : av[d][r];
+                        red[((wv * ND + d) * 4 + r) * 64 + lane] =
+                            kind == 0 ? ak[pp][d][r] : av[pp][d][r];
                 __syncthreads();
                 for (int x = threadIdx.x; x < ND * 4 * 64; x += blockDim.x) {
                     const float s = red[x] + red[ND * 256 + x] + red[2 * ND * 256 + x] +
                                     red[3 * ND * 256 + x];
                     const int d = x >> 8, r = (x >> 6) & 3, ln = x & 63;
-                    const int ent = e0 + (ln & 15), dim = 16 * d + 4 * (ln >> 4) + r;
+                    const int ent = e0[pp] + (ln & 15), dim = 16 * d + 4 * (ln >> 4) + r;
                     if (ent < Kl) {
                         float* dst = w.part[l - 1] +
                                      ((((long)gh * g.n[2] + a2) * Kl + ent) * 2 + kind) * D;
@@ -477,22 +508,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == D128 ?
                     }
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();
     }
 }
 
 // dbar_l[j] = sum over level-l query blocks a that chose j, and over the
 // level-2 blocks under a, of the partial sums at j's slot in a's list.  One
-// wave per pooled block, lane = channels lane + 64 c; list entries in
-// ascending order.
+// workgroup per pooled block, lane = channels lane + 64 c: the list's
+// (entry, level-2 block) rows, in ascending entry order, are split into four
+// contiguous quarters, each summed in order by one wave, and the four sums
+// are added in wave order.
 template <int D>
 __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
 {
     constexpr int NC = D / 64;  // channels dim + 64 c per lane
-    const long blk = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (blk >= (long)g.G * g.n[l]) return;
-    const int dim = threadIdx.x & 63;
+    __shared__ float wsum[4][2][D];
+    const long blk = blockIdx.x;
+    if (blk >= (long)g.G * g.n[l]) return;  // workgroup-uniform
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int dim = lane;
     const int gh = (int)(blk / g.n[l]), j = (int)(blk % g.n[l]);
     const int* rp = w.rowptr[l - 1] + (long)gh * (g.n[l] + 1);
     const int Kl = g.Kl[l];
@@ -503,28 +538,31 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
     float sk[NC] = {}, sv[NC] = {};
     const int tot = g.n[l] * Kl;  // list entries of the head
     const int beg = uniform(clampi(rp[j], tot + 1)), end = uniform(max(beg, clampi(rp[j + 1], tot + 1)));
-    // list entries in batches of 64: lane e holds entry beg + e (row offset
-    // into the partials).  The batch's (entry, level-2 block) rows are summed
-    // in order, eight loads in flight at a time.
-    const int lane = threadIdx.x & 63;
-    for (int e0 = beg; e0 < end; e0 += 64) {
+    // this wave's rows: a contiguous quarter of the (entry, level-2 block)
+    // rows, taken in batches of 64 entries (lane e holds entry e0 + e: the
+    // row offset into the partials), eight loads in flight at a time
+    const long nrow_all = (long)(end - beg) * span;
+    const long q_lo = nrow_all * wv / 4, q_hi = nrow_all * (wv + 1) / 4;
+    for (long qb = q_lo; qb < q_hi;) {
+        const int e0 = beg + (int)(qb / span);  // the batch's first entry
         const int ne = min(64, end - e0);
-        int off = 0;  // in rows of 2*D floats
+        int off = 0;   // in rows of 2*D floats
         int blk2 = 0;  // the entry's first level-2 block
         if (lane < ne) {
             const int a = clampi(cl[e0 + lane], g.n[l]);
             blk2 = a * span;
             off = a * span * Kl + clampi(sl[e0 + lane], Kl);
         }
-        const int nrow = ne * span;
-        for (int q0 = 0; q0 < nrow; q0 += 8) {
+        // rows qb .. qe of this batch (row q: entry q / span, block q % span)
+        const long qe = min(q_hi, (long)(e0 - beg + ne) * span);
+        for (long q0 = qb; q0 < qe; q0 += 8) {
             float vk[8][NC], vv[8][NC];
             bool ok[8];  // level-2 blocks past the last one (partial level-l block) do not exist
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int qq = min(q0 + u, nrow - 1);
-                const int e = qq / span, a2 = qq % span;
-                ok[u] = q0 + u < nrow && __builtin_amdgcn_readlane(blk2, e) + a2 < g.n[2];
+                const long qq = min(q0 + u, qe - 1);
+                const int e = (int)(qq / span) - (e0 - beg), a2 = (int)(qq % span);
+                ok[u] = q0 + u < qe && __builtin_amdgcn_readlane(blk2, e) + a2 < g.n[2];
                 const int a2c = ok[u] ? a2 : 0;
                 const long o = ((long)__builtin_amdgcn_readlane(off, e) + (long)a2c * Kl) * 2 * D;
 #pragma unroll
@@ -542,12 +580,22 @@ __global__ __launch_bounds__(256) void enrich_sum(Geo g, Ws w, int l)
                         sv[c] += vv[u][c];
                     }
         }
+        qb = qe;
     }
-    float* dst = w.dbar[l - 1] + blk * 2 * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        dst[dim + 64 * c] = sk[c];
-        dst[D + dim + 64 * c] = sv[c];
+        wsum[wv][0][dim + 64 * c] = sk[c];
+        wsum[wv][1][dim + 64 * c] = sv[c];
+    }
+    __syncthreads();
+    if (wv == 0) {
+        float* dst = w.dbar[l - 1] + blk * 2 * D;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int x = dim + 64 * c;
+            dst[x] = ((wsum[0][0][x] + wsum[1][0][x]) + wsum[2][0][x]) + wsum[3][0][x];
+            dst[D + x] = ((wsum[0][1][x] + wsum[1][1][x]) + wsum[2][1][x]) + wsum[3][1][x];
+        }
     }
 }
 
@@ -1234,13 +1282,18 @@ hipError_t launch_attn_enrich_d(const void* q, const float* lse, const void* dou
     }
     if (dtype == LLSA_BF16) {
         if (g.L < 2) return hipSuccess;
-        hipLaunchKernelGGL(enrich_bwd_bf16<D>, dim3(g.G * g.n[2]), dim3(256), 0, st,
-                           (const unsigned short*)q, lse, (const unsigned short*)dout, g, w);
+        int npairs = 0;  // (level, 16-entry tile) pairs of levels >= 2
+        for (int l = 2; l <= g.L; ++l) npairs += (g.Kl[l] + BS - 1) / BS;
+        // two pairs per pass at d = 64 (at d = 128 two pairs spill)
+        auto kern = enrich_bwd_bf16<D, 1>;
+        if constexpr (D == D64)
+            if (npairs >= 2) kern = enrich_bwd_bf16<D, 2>;
+        hipLaunchKernelGGL(kern, dim3(g.G * g.n[2]), dim3(256), 0, st, (const unsigned short*)q,
+                           lse, (const unsigned short*)dout, g, w);
         hipError_t e = hipGetLastError();
         for (int l = 2; l <= g.L && e == hipSuccess; ++l) {
-            long n = (long)g.G * g.n[l];
-            hipLaunchKernelGGL(enrich_sum<D>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, g,
-                               w, l);
+            long n = (long)g.G * g.n[l];  // one workgroup per pooled block
+            hipLaunchKernelGGL(enrich_sum<D>, dim3((unsigned)n), dim3(256), 0, st, g, w, l);
             e = hipGetLastError();
         }
         return e;
