@@ -1061,7 +1061,9 @@ __device__ __forceinline__ void load_qrow(QRow<D>& x, const float* q, const floa
     x.delta = delta[t];
 }
 
-// pooled-token gradients, every level: one wave per level-l block
+// pooled-token gradients, every level: one workgroup per level-l block,
+// its four waves taking contiguous quarters of the block's chooser list; the
+// four sums are added in wave order
 template <int D>
 __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
                                                   const float* __restrict__ lse,
@@ -1069,9 +1071,10 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
                                                   int l)
 {
     constexpr int CH = D / 4;
-    const long blk = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    if (blk >= (long)g.G * g.n[l]) return;
-    const int lane = threadIdx.x & 63, r = lane & 15;
+    __shared__ float wsum[4][2][D];
+    const long blk = blockIdx.x;
+    if (blk >= (long)g.G * g.n[l]) return;  // workgroup-uniform
+    const int lane = threadIdx.x & 63, r = lane & 15, wv = threadIdx.x >> 6;
     const int gh = (int)(blk / g.n[l]), j = (int)(blk % g.n[l]);
     float kb[CH], vb[CH], sk[CH], sv[CH];
     load_slice<D>(kb, w.kbar[l - 1] + blk * D, lane);
@@ -1104,7 +1107,9 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
         }
     }
     const int Kl = g.Kl[l];
-    for (int e = beg; e < end; ++e) {
+    const int e_lo = beg + (int)((long)(end - beg) * wv / 4);
+    const int e_hi = beg + (int)((long)(end - beg) * (wv + 1) / 4);
+    for (int e = e_lo; e < e_hi; ++e) {
         long a;
         if (!g.cmp) {
             a = clampi(cl[e], g.n[l]);
@@ -1134,9 +1139,25 @@ __global__ __launch_bounds__(256) void enrich_f32(const float* __restrict__ q,
             }
         }
     }
-    float* dst = w.dbar[l - 1] + blk * 2 * D;
-    store_slice<D>(dst, sk, lane, g.scale);
-    store_slice<D>(dst + D, sv, lane);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        sk[c] = row16_sum(sk[c]) * g.scale;
+        sv[c] = row16_sum(sv[c]);
+    }
+    if (r == 0)
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            wsum[wv][0][CH * (lane >> 4) + c] = sk[c];
+            wsum[wv][1][CH * (lane >> 4) + c] = sv[c];
+        }
+    __syncthreads();
+    if (wv == 0) {
+        float* dst = w.dbar[l - 1] + blk * 2 * D;
+        for (int x = lane; x < 2 * D; x += 64) {
+            const float* ws = &wsum[0][0][0] + x;  // kind x / D, element x % D
+            dst[x] = ((ws[0] + ws[2 * D]) + ws[4 * D]) + ws[6 * D];
+        }
+    }
 }
 
 // dk, dv: one wave per key token, over the 16 rows of each query block of
@@ -1300,9 +1321,9 @@ hipError_t launch_attn_enrich_d(const void* q, const float* lse, const void* dou
     }
     hipError_t e = hipSuccess;
     for (int l = g.l0; l <= g.L && e == hipSuccess; ++l) {
-        long n = (long)g.G * g.n[l];  // one wave per pooled block
-        hipLaunchKernelGGL(enrich_f32<D>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st,
-                           (const float*)q, lse, (const float*)dout, g, w, l);
+        long n = (long)g.G * g.n[l];  // one workgroup per pooled block
+        hipLaunchKernelGGL(enrich_f32<D>, dim3((unsigned)n), dim3(256), 0, st, (const float*)q,
+                           lse, (const float*)dout, g, w, l);
         e = hipGetLastError();
     }
     return e;
