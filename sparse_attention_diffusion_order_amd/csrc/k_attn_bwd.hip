@@ -624,9 +624,13 @@ constexpr int DKDV_WPG = 1;
 // CAUSAL: LLSA_CAUSAL (its own instance, so that the default one carries no
 // mask code).  ENRICH1: level 1's pooled tokens enrich (a compile-time
 // switch: as a run-time one the compiler branches around the pooled terms of
-// every row, each branch waiting on all outstanding LDS reads).
+// every row, each branch waiting on all outstanding LDS reads).  At most 3
+// waves per SIMD: the compiler then schedules for that occupancy (147
+// registers at d = 64); left to fit 4 (114 registers) the kernel is slower
+// (256x256: 214.7 against 204.1 us; 512x512: 861 against 804 us), as more key
+// blocks in flight per XCD spread the query blocks they gather over its L2.
 template <int D, int WPG, bool CAUSAL, bool ENRICH1>
-__global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __restrict__ q,
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(1, 3))) void dkdv_bf16(const unsigned short* __restrict__ q,
                                                       const unsigned short* __restrict__ k,
                                                       const unsigned short* __restrict__ v,
                                                       const float* __restrict__ lse,
@@ -749,19 +753,22 @@ __global__ __launch_bounds__(64 * WPG) void dkdv_bf16(const unsigned short* __re
     // two register sets alternate, each filled one step before it is used.
     // The loop body is one basic block: a conditional exit between a fetch
     // and its use would let the compiler sink the loads down to the use.
-    // Fetches past the end re-read the last block (valid memory).
+    // Fetches past the end re-read the last block (valid memory).  The loop
+    // takes the blocks in pairs; an odd count's last block, already in A,
+    // takes one step after it.
     QBlock<D> A, B;
     for (int cb = beg; cb < end; cb += 64) {
         const int n = min(64, end - cb);
         myi = lane < n ? clampi(list[cb + lane], g.n[1]) : 0;
         mys = lane < n ? clampi(slots[cb + lane], g.K) : 0;
         fetch(A, 0);
-        for (int t = 0; t < n; t += 2) {
-            fetch(B, min(t + 1, n - 1));
+        for (int t = 0; t + 1 < n; t += 2) {
+            fetch(B, t + 1);
             step(A, true);
             fetch(A, min(t + 2, n - 1));
-            step(B, t + 1 < n);
+            step(B, true);
         }
+        if (n & 1) step(A, true);
     }
     // epilogue: scale, add the pooled-level gradients (levels >= 2), store
     const long obase = kbase + nq * D + 4 * gq;
