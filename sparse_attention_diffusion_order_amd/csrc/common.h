@@ -87,7 +87,8 @@ struct Ws {
     unsigned short* vb16;    //   row (prow[l] + gh * n_l + j) holds level l, head gh, block j
     long prow[MAX_L];        // first row of each level in kb16 / vb16
     float* delta;            // [G][N]
-    float* pe1;              // [G][n1][K][2][16]: P and dS of the level-1 pooled entries
+    float* pe1;              // [G][n1][K][2][16] bf16: P and dS of the level-1 pooled
+                             // entries (the complement uses the region as fp32 partials)
     float* part[MAX_L];      // level l>=2 partial enrichment grads [G][n2][K][2][d]
     float* dbar[MAX_L];      // level l>=2 enrichment grads [G][n_l][2][d]
 };
@@ -192,6 +193,12 @@ __device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, int voff, int
 __device__ __forceinline__ float bloadf(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+// one bf16 element, widened to float (out of range: 0)
+__device__ __forceinline__ float bload_bf16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0) << 16);
 }
 
 // A per-lane buffer offset that is out of range for any resource here: the

@@ -82,15 +82,16 @@ __device__ __forceinline__ void put_rows(unsigned short* lds, const bf16x8 (&r)[
 // ba / bb (MASK only, may be null): logit bias of rows 4(lane/16) + r of
 // tiles a and b (log2 units; pooled entries under the size-weighted variant).
 // pe != nullptr: entries ea + 4(lane/16) + r (tile a) and ea + 16 + ... (tile
-// b) below K1 are level-1 pooled tokens; their P and dS are stored at
-// pe[entry][0 | 1][query] for the key-major dk/dv pass.
+// b) below K1 are level-1 pooled tokens; their P and dS are stored (bf16) at
+// pe[entry][0 | 1][query] for the key-major dk/dv pass, which adds them at
+// 1/16 weight to values it rounds to bf16 itself.
 template <bool MASK, int D>
 __device__ __forceinline__ void dq_pair(f32x4 (&acc)[D / 16], const bf16x8 (&bq)[D / 32],
                                         const bf16x8 (&bd)[D / 32], float nl2, float Dq,
                                         const bf16x8 (&ka)[D / 32], const bf16x8 (&kb)[D / 32],
                                         const bf16x8 (&va)[D / 32], const bf16x8 (&vb)[D / 32],
                                         const unsigned short* la, const unsigned short* lb,
-                                        int na, int nb, float c, int lane, float* pe = nullptr,
+                                        int na, int nb, float c, int lane, unsigned short* pe = nullptr,
                                         int ea = 0, int K1 = 0, const float* ba = nullptr,
                                         const float* bb = nullptr)
 {
@@ -115,12 +116,12 @@ __device__ __forceinline__ void dq_pair(f32x4 (&acc)[D / 16], const bf16x8 (&bq)
             const int nq = lane & 15;
             const int e_a = ea + 4 * gq + r, e_b = e_a + BS;
             if (e_a < K1) {
-                pe[e_a * 2 * BS + nq] = Pa;
-                pe[e_a * 2 * BS + BS + nq] = dSa;
+                pe[e_a * 2 * BS + nq] = f2bf(Pa);
+                pe[e_a * 2 * BS + BS + nq] = f2bf(dSa);
             }
             if (e_b < K1) {
-                pe[e_b * 2 * BS + nq] = Pb;
-                pe[e_b * 2 * BS + BS + nq] = dSb;
+                pe[e_b * 2 * BS + nq] = f2bf(Pb);
+                pe[e_b * 2 * BS + BS + nq] = f2bf(dSb);
             }
         }
         bs[r] = (bf16)dSa;
@@ -282,8 +283,9 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
             const bool pooled = p >= NF;
             // the level-1 picks' pooled entries (the first E1) keep their P
             // and dS for the key-major pass, at their picks' positions
-            float* pe = (pooled && g.l0 == 1 && !g.cmp && e0 < E1)
-                            ? w.pe1 + ((long)gh * g.n[1] + i) * g.K * 2 * BS : nullptr;
+            unsigned short* pe = (pooled && g.l0 == 1 && !g.cmp && e0 < E1)
+                                     ? (unsigned short*)w.pe1 + ((long)gh * g.n[1] + i) * g.K * 2 * BS
+                                     : nullptr;
             float ba[4], bb[4];  // pooled rows: the logit bias of the entry's level
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -733,7 +735,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(1, 3))
     const int voff = (sr * D + sc) * 2;
     const int off_lse = lane < 16 ? 4 * lane : OFF_NONE;
     const int off_del = (lane >= 16 && lane < 32) ? 4 * (lane - 16) : OFF_NONE;
-    const int off_pe = lane >= 32 ? 4 * (lane - 32) : OFF_NONE;
+    const int off_pe = lane >= 32 ? 2 * (lane - 32) : OFF_NONE;  // bf16 P (32..47), dS (48..63)
     auto fetch = [&](QBlock<D>& f, int t) {
         const int i = __builtin_amdgcn_readlane(myi, t);
         const int sl = __builtin_amdgcn_readlane(mys, t);
@@ -746,9 +748,10 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(1, 3))
         // an empty resource reads 0)
         f.diag = CAUSAL && i == j;
         const __amdgpu_buffer_rsrc_t rpe = make_rsrc(
-            w.pe1 + (((long)gh * g.n[1] + i) * g.K + sl) * 2 * BS, f.diag ? 0u : 2 * BS * 4);
+            (const unsigned short*)w.pe1 + (((long)gh * g.n[1] + i) * g.K + sl) * 2 * BS,
+            f.diag ? 0u : 2 * BS * 2);
         f.x = bloadf(rlse, off_lse, i * BS * 4) + bloadf(rdel, off_del, i * BS * 4) +
-              bloadf(rpe, off_pe, 0);
+              bload_bf16(rpe, off_pe, 0);
     };
     // two register sets alternate, each filled one step before it is used.
     // The loop body is one basic block: a conditional exit between a fetch
