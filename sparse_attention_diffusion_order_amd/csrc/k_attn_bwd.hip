@@ -191,7 +191,7 @@ __device__ __forceinline__ void dq_block(const unsigned short* __restrict__ q,
         float s = 0.f;
 #pragma unroll
         for (int u = 0; u < NI; ++u) {
-            const bf16x8 ou = ld8(o + rowq + 32 * u + 8 * gq);
+            const bf16x8 ou = ld8_once(o + rowq + 32 * u + 8 * gq);
 #pragma unroll
             for (int e = 0; e < 8; ++e) s += (float)bd[u][e] * (float)ou[e];
         }
@@ -661,8 +661,8 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(1, 3))
     bf16x8 bk[NI], bv[NI];  // the key block's rows lane%16, channels 32u + 8(lane/16) ..
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-        bk[u] = ld8(k + kbase + nq * D + 32 * u + 8 * gq);
-        bv[u] = ld8(v + kbase + nq * D + 32 * u + 8 * gq);
+        bk[u] = ld8_once(k + kbase + nq * D + 32 * u + 8 * gq);
+        bv[u] = ld8_once(v + kbase + nq * D + 32 * u + 8 * gq);
     }
     const int* rp = w.rowptr[0] + (long)gh * (g.n[1] + 1);
     const int* list = w.col[0] + (long)gh * g.n[1] * g.K;

@@ -30,7 +30,11 @@ namespace {
 
 // C consecutive channels (C = 4 or 8) of one token row: load() reads them
 // raw (one 8- or 16-byte load in bf16, one or two 16-byte loads in fp32),
-// add() widens them to float and adds them to s
+// add() widens them to float and adds them to s.  load_once() is load() with
+// the nontemporal hint, for the raster rows of the gathering pass: they are
+// read once, and streaming them keeps the caches for the grid-ordered copies
+// the selection and attention read next (256x256: forward with the gather
+// 0.185 -> 0.182 ms).
 template <typename T, int C> struct Row;
 template <int C> struct Row<float, C> {
     float4 r[C / 4];
@@ -44,6 +48,14 @@ template <int C> struct Row<float, C> {
 #pragma unroll
         for (int h = 0; h < C / 4; ++h) {
             s[4 * h] += r[h].x; s[4 * h + 1] += r[h].y; s[4 * h + 2] += r[h].z; s[4 * h + 3] += r[h].w;
+        }
+    }
+    __device__ __forceinline__ void load_once(const float* p)
+    {
+#pragma unroll
+        for (int h = 0; h < C / 4; ++h) {
+            const f32x4 x = __builtin_nontemporal_load((const f32x4*)p + h);
+            r[h] = make_float4(x[0], x[1], x[2], x[3]);
         }
     }
     __device__ __forceinline__ void store(float* p) const
@@ -63,6 +75,13 @@ template <int C> struct Row<unsigned short, C> {
             const uint4 x = *(const uint4*)p;
             u[0] = x.x; u[1] = x.y; u[2] = x.z; u[3] = x.w;
         }
+    }
+    __device__ __forceinline__ void load_once(const unsigned short* p)
+    {
+        typedef unsigned uv __attribute__((ext_vector_type(C / 2)));
+        const uv x = __builtin_nontemporal_load((const uv*)p);
+#pragma unroll
+        for (int h = 0; h < C / 2; ++h) u[h] = x[h];
     }
     __device__ __forceinline__ void add(float (&s)[C]) const
     {
@@ -140,11 +159,11 @@ __global__ __launch_bounds__(256) void pool_l12(const T* __restrict__ q, const T
                     const long off = gg.video
                                          ? ((long)b2_ * gg.H + b1_) * gg.W + (b0_ | (b3_ << 1))
                                          : (long)(b1_ | (b3_ << 1)) * gg.W + (b0_ | (b2_ << 1));
-                    r[t].load(src + (base + off) * D);
+                    r[t].load_once(src + (base + off) * D);
                 }
             } else {
 #pragma unroll
-                for (int t = 0; t < BS; ++t) r[t].load(src + (long)grid_source(p0 + t, gg) * D);
+                for (int t = 0; t < BS; ++t) r[t].load_once(src + (long)grid_source(p0 + t, gg) * D);
             }
             T* dst = (tensor == 0 ? gt.q : tensor == 1 ? gt.k : gt.v) +
                      ((long)gh * g.N + (long)(b0 + blk) * BS) * D + C * sub;
