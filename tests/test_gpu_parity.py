@@ -32,6 +32,10 @@ SMALL = [
     small("grid64_bf16_l3_k1", 1, 2, 64, "bf16", 3, 1),
     small("grid64_bf16_l1_k32", 1, 1, 64, "bf16", 1, 32),
     synth.WORKLOADS["grid64_bf16_l1_k16"],
+    # two levels with top-16 at both: at 64^2 the coarsest level has exactly
+    # 16 blocks, so every coarsest row picks all of them
+    small("grid64_bf16_l2_k16", 2, 3, 64, "bf16", 2, 16),
+    W("rect64x128_bf16_l2_k16", 1, 2, 128, 64, "bf16", 2, 16, 2.0, 0, 16, 1, 64),
 ]
 
 
